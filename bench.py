@@ -1,0 +1,177 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the whole path on synthetic, seeded inputs resident in HBM:
+  * chunked prefill of a 128k-token sequence: B=1, H=32, T=131072, dk=dv=128, bf16 q/k/v
+    (q, k unit-norm), fp32 per-channel log_alpha = -softplus(N(0,1)), fp32 beta =
+    sigmoid(N(0,1)), zero initial state, chunk 64, output o and the final state;
+  * one batched decode step: 256 sequences x 32 heads, fp32 128x128 states ~ N(0, 0.02),
+    raw bf16 activations -> width-4 short conv with cache (q, k, v) -> decode step with
+    in-kernel L2 normalisation of q and k.
+`value` is prefill tokens/s; the decode state-update GB/s is reported beside it.
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_BYTES_PER_TH = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (512) + beta (4)
+DECODE_BYTES_PER_SH = 132612         # state read+write 8*K*V + q,k,v,o (1024) + log_alpha (512) + beta
+
+
+def prefill_flops_per_th(C, K=128, V=128):
+    # chunk WY form, triangles exploited: A, P, the solve on [V|K], P U, three state products
+    return C * (3 * K + 2 * V) + 6 * K * V
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--T", type=int, default=131072)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--decode-batch", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
+                    help="tokens per head of the oracle's CPU-baseline sample (32 heads)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(args):
+    """The fp64 oracle on a bounded sample of the same prefill workload (host cores)."""
+    import numpy as np
+    from linear_attention_recurrence_kda_amd import datagen as D
+    from oracle import oracle as O
+    H, T = 32, args.cpu_sample_tokens
+    inp = D.np_kda_inputs(1, T, H, 128, 128, "bf16", seed=0)
+    threads = O.host_threads()
+    O.c_prefill(**{n: x[:, :16] for n, x in inp.items()}, nthreads=threads)   # load + warm
+    t0 = time.perf_counter()
+    O.c_prefill(**inp, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 token loop, B=1 H=32 T={T} dk=dv=128 (seed 0), {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path would shard over heads/sequences, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from linear_attention_recurrence_kda_amd import datagen as D
+    from linear_attention_recurrence_kda_amd import kda
+
+    dev = torch.device("cuda:0")
+    H, dk, dv, T, C = 32, 128, 128, args.T, args.chunk
+    x = D.torch_kda_inputs(1, T, H, dk, dv, dev, "bf16", seed=0)
+    o = torch.empty(1, T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.prefill_workspace_size(1, T, H, dk, dv, C, kda.KDA_BF16), dtype=torch.uint8, device=dev)
+
+    Bd = args.decode_batch
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    state = 0.02 * torch.randn(Bd, H, dk, dv, device=dev, generator=g)
+    dx = {n: torch.randn(Bd, 1, H * dk, device=dev, generator=g).to(torch.bfloat16) for n in ("q", "k", "v")}
+    cw = {n: (torch.rand(H * dk, 4, device=dev, generator=g) - 0.5) for n in ("q", "k", "v")}
+    cache = {n: torch.randn(Bd, 3, H * dk, device=dev, generator=g).to(torch.bfloat16) for n in ("q", "k", "v")}
+    dla = -torch.nn.functional.softplus(torch.randn(Bd, H, dk, device=dev, generator=g))
+    dbeta = torch.sigmoid(torch.randn(Bd, H, device=dev, generator=g))
+    dy = {n: torch.empty_like(dx[n]) for n in dx}
+    do = torch.empty(Bd, H, dv, dtype=torch.bfloat16, device=dev)
+
+    def prefill():
+        kda.chunk_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], chunk_size=C,
+                          out=o, final_state=fs, workspace=ws)
+
+    def decode():
+        for n in ("q", "k", "v"):
+            kda.short_conv(dx[n], cw[n], None, None, cache[n], out=dy[n])
+        kda.decode_step(dy["q"].view(Bd, H, dk), dy["k"].view(Bd, H, dk), dy["v"].view(Bd, H, dv),
+                        dla, dbeta, state, l2norm_qk=True, out=do)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        prefill()
+        e[1].record()
+        e[2].record()
+        decode()
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sorted(a.elapsed_time(b) for a, b, _, _ in ev)
+    dec_ms = sorted(c.elapsed_time(d) for _, _, c, d in ev)
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    # decode state update alone (the bandwidth-bound kernel), timed on its own
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(10, args.steps)
+    e0.record()
+    for _ in range(reps):
+        kda.decode_step(dy["q"].view(Bd, H, dk), dy["k"].view(Bd, H, dk), dy["v"].view(Bd, H, dv),
+                        dla, dbeta, state, l2norm_qk=True, out=do)
+    e1.record()
+    torch.cuda.synchronize()
+    dstep_ms = e0.elapsed_time(e1) / reps
+
+    th = T * H
+    tok_s = T / (pre_avg * 1e-3)
+    pre_gbs = PREFILL_BYTES_PER_TH * th / (pre_avg * 1e-3) / 1e9
+    pre_tflops = prefill_flops_per_th(C) * th / (pre_avg * 1e-3) / 1e12
+    dec_gbs = DECODE_BYTES_PER_SH * Bd * H / (dstep_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": "KDA prefill tokens/s at 128k (MFMA %) + decode state-update GB/s (HBM %)",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; q,k unit-norm bf16, log_alpha=-softplus(N(0,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": f"kda_prefill_T{T}_B1_H32_dk128_dv128_chunk{C} + kda_decode_B{Bd}_H32",
+                   "prefill": {"B": 1, "T": T, "H": H, "dk": dk, "dv": dv, "chunk": C},
+                   "decode": {"B": Bd, "H": H, "dk": dk, "dv": dv, "conv_width": 4}},
+        "prefill": {"ms": pre_avg, "ms_min": pre_ms[0], "tokens_per_s": tok_s,
+                    "algorithmic_GBps": pre_gbs, "hbm_frac": pre_gbs / HBM_PEAK_GBS,
+                    "model_tflops": pre_tflops, "mfma_frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "decode": {"step_ms_with_conv": dec_avg, "state_update_ms": dstep_ms,
+                   "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
+                   "tokens_per_s": Bd / (dec_avg * 1e-3),
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+                                "kernel": "decode_step_kernel"}},
+        "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_chunk_prefill (prep_kernel + scan_kernel)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) implementation of the
+ * Kimi Delta Attention (KDA) gated delta-rule recurrence.
+ *
+ * The recurrence (Kimi Linear summary page, "recurrent layers" paragraph:
+ * each step decays the state per channel, removes the old state's projection
+ * onto the current key, then writes the new key/value pair; the remio.ai page,
+ * section on KDA's recurrent memory: a per-channel forget gate on top of Gated
+ * DeltaNet's delta rule).  Per batch row b and head h the state S is a dk x dv
+ * fp32 matrix whose rows are key channels.  For each valid token t:
+ *
+ *     S'  = Diag(exp(log_alpha_t)) S
+ *     u   = beta_t (v_t - S'^T k_t)
+ *     S   = S' + k_t u^T
+ *     o_t = S^T q_t                       (no 1/sqrt(dk) scale; callers pre-scale q)
+ *
+ * Masks (Transformers issue report on Kimi Linear cached continuation:
+ * padding must advance neither the convolution state nor the recurrent
+ * state).  A position with mask == 0 behaves as alpha = 1, beta = 0: it leaves
+ * S untouched, produces o_t = 0, and its q/k/v/log_alpha/beta values are never
+ * read into the arithmetic (NaN or garbage there cannot leak).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are device pointers (HBM), dense, row-major, 16-byte
+ *     aligned, owned by the caller.  The library allocates nothing, keeps no
+ *     pointer after returning, and holds no global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it; nothing synchronises the host.
+ *   - Arguments are validated on the host before any HIP call.  A failing call
+ *     returns a negative kda_status and has no side effect.  KDA_ERR_HIP means
+ *     a launch failed; kda_last_hip_error() then gives the hipError_t value
+ *     (per calling thread).
+ *   - `dtype` is the element type of q, k, v, o (and x, y, conv_cache for the
+ *     short convolution).  log_alpha, beta, weights and states are always fp32.
+ *   - Results are bitwise deterministic for identical inputs and arguments
+ *     (no atomics, fixed reduction orders).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = -1,  /* null pointer where one is required, negative size, bad alignment */
+  KDA_ERR_UNSUPPORTED = -2,  /* well-formed but outside the supported set (head size, chunk, width) */
+  KDA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the size query returned */
+  KDA_ERR_HIP = -4           /* a HIP launch failed; see kda_last_hip_error() */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+enum {
+  /* normalise q and k per (b,t,h) to x / sqrt(sum x^2 + 1e-6) before use */
+  KDA_FLAG_L2NORM_QK = 1u,
+  /* short convolution: apply SiLU, y = z / (1 + exp(-z)) */
+  KDA_FLAG_SILU = 2u
+};
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+/* Static, human-readable name of a kda_status value (never NULL). */
+const char* kda_status_string(int status);
+
+/* hipError_t of the last KDA_ERR_HIP returned on this thread (0 if none). */
+int kda_last_hip_error(void);
+
+/*
+ * Bytes of device workspace kda_chunk_prefill needs for these arguments
+ * (0 when none is needed).  Returns 0 as well for arguments that the call
+ * itself would reject.
+ */
+size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+
+/*
+ * Chunked prefill of T tokens for B sequences and H heads (Kimi Linear
+ * summary page, paragraph on the kernels: sequences are split into chunks and
+ * the chunk's rank-1 updates are batched through a WY representation, i.e. a
+ * triangular solve).  Computes exactly the token recurrence above; `chunk` is
+ * a tuning parameter that changes rounding only.
+ *
+ *   q, k        [B,T,H,dk]   dtype
+ *   v           [B,T,H,dv]   dtype
+ *   log_alpha   [B,T,H,dk]   fp32, finite, <= 0 (per-channel log forget gate)
+ *   beta        [B,T,H]      fp32 in [0,1]
+ *   mask        [B,T]        uint8 0/1, NULL = every position valid
+ *   init_state  [B,H,dk,dv]  fp32, NULL = zeros
+ *   o           [B,T,H,dv]   dtype, written (0 at masked positions)
+ *   final_state [B,H,dk,dv]  fp32, written; may be the same pointer as init_state
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}; T >= 0
+ * (T = 0 copies init_state to final_state).  The ragged tail of the last chunk
+ * is handled as masked positions.  `flags` may hold KDA_FLAG_L2NORM_QK.
+ * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
+ * bytes of device memory (may be NULL when that size is 0).
+ */
+int kda_chunk_prefill(const void* q, const void* k, const void* v,
+                      const float* log_alpha, const float* beta, const uint8_t* mask,
+                      const float* init_state, void* o, float* final_state,
+                      int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                      unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step: a single new token per sequence, state updated in place
+ * (remio.ai page, decode section: KDA keeps a fixed-size state, so each
+ * generated token reads and rewrites that state once).
+ *
+ *   q, k        [B,H,dk]     dtype
+ *   v           [B,H,dv]     dtype
+ *   log_alpha   [B,H,dk]     fp32
+ *   beta        [B,H]        fp32
+ *   mask        [B]          uint8 0/1, NULL = all valid (0 leaves S untouched, o = 0)
+ *   state       [B,H,dk,dv]  fp32, read and written in place
+ *   o           [B,H,dv]     dtype, written
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; B, H >= 0.  `flags` may hold
+ * KDA_FLAG_L2NORM_QK.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v,
+                    const float* log_alpha, const float* beta, const uint8_t* mask,
+                    float* state, void* o, int B, int H, int dk, int dv, int dtype,
+                    unsigned flags, void* stream);
+
+/*
+ * Depthwise causal short convolution with a cache, over the compacted
+ * sequence of valid positions (Transformers issue report on Kimi Linear:
+ * padded entries must not enter the convolution window).  Per sequence b and
+ * channel c, let x~ be [the W-1 cached inputs (oldest first), then x at the
+ * valid positions in order].  At a valid position t that is the m-th valid one,
+ *     y[b,t,c] = bias[c] + sum_{j=0}^{W-1} weight[c,j] * x~[m + j]
+ * (weight[c,W-1] multiplies the current input), optionally passed through SiLU;
+ * y = 0 at masked positions.  The cache then holds the last W-1 entries of x~.
+ *
+ *   x           [B,T,D]      dtype
+ *   weight      [D,W]        fp32
+ *   bias        [D]          fp32 or NULL
+ *   mask        [B,T]        uint8 0/1 or NULL
+ *   conv_cache  [B,W-1,D]    dtype, read then overwritten; NULL = zero history, not written
+ *   y           [B,T,D]      dtype, written; must not overlap x or conv_cache
+ *
+ * Supported: W in {2, 3, 4}; D >= 1, D a multiple of 8; T >= 0.  `flags` may
+ * hold KDA_FLAG_SILU.
+ */
+int kda_short_conv(const void* x, const float* weight, const float* bias, const uint8_t* mask,
+                   void* conv_cache, void* y, int B, int T, int D, int W, int dtype,
+                   unsigned flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

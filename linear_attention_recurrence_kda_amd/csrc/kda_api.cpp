@@ -1,0 +1,108 @@
+// C ABI of libkda (declared in include/kda.h): argument validation on the
+// host, then dispatch to the gfx950 kernel launchers.  Nothing here allocates
+// or synchronises; a rejected call makes no HIP call at all.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == KDA_BF16 || dt == KDA_F32; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KDA_OK;
+  g_last_hip_error = (int)e;
+  return KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: null, negative or misaligned argument";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head size, chunk or width outside the supported set";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch failed (see kda_last_hip_error)";
+    default: return "unknown kda_status";
+  }
+}
+
+int kda_last_hip_error(void) { return g_last_hip_error; }
+
+size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return 0;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk)) return 0;
+  return kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
+}
+
+int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                      const float* beta, const uint8_t* mask, const float* init_state, void* o,
+                      float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                      unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_INVALID_ARG;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk))
+    return KDA_ERR_UNSUPPORTED;
+  const bool work = (size_t)B * H > 0;
+  if (work) {
+    if (final_state == nullptr || !aligned16(final_state)) return KDA_ERR_INVALID_ARG;
+    if (init_state != nullptr && !aligned16(init_state)) return KDA_ERR_INVALID_ARG;
+    if (T > 0) {
+      const void* req[] = {q, k, v, log_alpha, beta, o};
+      for (const void* p : req)
+        if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    }
+  }
+  const size_t need = kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return KDA_ERR_WORKSPACE;
+  if (!work) return KDA_OK;
+  kda::PrefillArgs a{q, k, v, log_alpha, beta, mask, init_state, o, final_state,
+                     B, T, H, dk, dv, chunk, dtype, (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0,
+                     workspace, workspace_bytes, stream};
+  return hip_status(kda::launch_prefill(a));
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, const uint8_t* mask, float* state, void* o, int B, int H,
+                    int dk, int dv, int dtype, unsigned flags, void* stream) {
+  if (B < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_INVALID_ARG;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if ((size_t)B * H == 0) return KDA_OK;
+  const void* req[] = {q, k, v, log_alpha, beta, state, o};
+  for (const void* p : req)
+    if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+  kda::DecodeArgs a{q, k, v, log_alpha, beta, mask, state, o, B, H, dk, dv, dtype,
+                    (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, stream};
+  return hip_status(kda::launch_decode(a));
+}
+
+int kda_short_conv(const void* x, const float* weight, const float* bias, const uint8_t* mask,
+                   void* conv_cache, void* y, int B, int T, int D, int W, int dtype, unsigned flags,
+                   void* stream) {
+  if (B < 0 || T < 0 || D <= 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)KDA_FLAG_SILU) != 0) return KDA_ERR_INVALID_ARG;
+  if (W < 2 || W > 4 || D % 8 != 0) return KDA_ERR_UNSUPPORTED;
+  if (B == 0) return KDA_OK;
+  if (weight == nullptr) return KDA_ERR_INVALID_ARG;
+  if (conv_cache != nullptr && !aligned16(conv_cache)) return KDA_ERR_INVALID_ARG;
+  if (T > 0 && (x == nullptr || y == nullptr || !aligned16(x) || !aligned16(y))) return KDA_ERR_INVALID_ARG;
+  if (T == 0) return KDA_OK;   // nothing to convolve; the cache keeps its contents
+  kda::ConvArgs a{x, weight, bias, mask, conv_cache, y, B, T, D, W, dtype,
+                  (flags & KDA_FLAG_SILU) ? 1 : 0, stream};
+  return hip_status(kda::launch_short_conv(a));
+}
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Masked depthwise causal short convolution with a conv cache (Transformers
+// issue report on Kimi Linear cached continuation: padded entries entering the
+// convolution window were one of the two causes of the state defect, so the
+// taps here run over the compacted sequence of valid positions only).
+//
+// For sequence b and channel c, x~ = [cache[b,0..W-2,c], x at the valid
+// positions of b in order]; the m-th valid position gets
+//   y = bias[c] + sum_j w[c,j] * x~[m + j]      (w[c,W-1] on the current input)
+// and masked positions get y = 0.  The new cache is the last W-1 entries of x~.
+//
+// Two launches on the caller's stream: conv_y_kernel reads the old cache,
+// conv_cache_kernel then overwrites it (stream order separates the two).
+// Each thread owns 8 consecutive channels (one 16-byte bf16 vector) and a
+// segment of tokens; its window history is found by walking back over the mask.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvSeg = 32;   // tokens per thread
+
+__device__ __forceinline__ bool conv_valid(const uint8_t* mask, int b, int T, int t) {
+  return mask == nullptr || mask[(size_t)b * T + t] != 0;
+}
+
+// History entries preceding position t_start (exclusive): hist[0] oldest ... hist[W-2] newest.
+template <int DT, int W>
+__device__ __forceinline__ void conv_history(const typename Elem<DT>::T* x, const typename Elem<DT>::T* cache,
+                                             const uint8_t* mask, int b, int T, int D, int c0, int t_start,
+                                             float (&hist)[W > 1 ? W - 1 : 1][8]) {
+  using E = Elem<DT>;
+  int t = t_start - 1;
+  int used_cache = 0;
+#pragma unroll
+  for (int s = 0; s < W - 1; ++s) {
+    while (t >= 0 && !conv_valid(mask, b, T, t)) --t;
+    if (t >= 0) {
+      E::ld8(x, ((size_t)b * T + t) * D + c0, hist[W - 2 - s]);
+      --t;
+    } else if (cache != nullptr) {
+      E::ld8(cache, ((size_t)b * (W - 1) + (W - 2 - used_cache)) * D + c0, hist[W - 2 - s]);
+      ++used_cache;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hist[W - 2 - s][i] = 0.f;
+    }
+  }
+}
+
+template <int DT, int W>
+__global__ void __launch_bounds__(kConvThreads)
+conv_y_kernel(const typename Elem<DT>::T* __restrict__ x, const float* __restrict__ w,
+              const float* __restrict__ bias, const uint8_t* __restrict__ mask,
+              const typename Elem<DT>::T* __restrict__ cache, typename Elem<DT>::T* __restrict__ y,
+              int T, int D, int silu) {
+  using E = Elem<DT>;
+  const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * 8;
+  if (c0 >= D) return;
+  const int b = blockIdx.z;
+  const int t_start = blockIdx.y * kConvSeg;
+  const int t_end = min(T, t_start + kConvSeg);
+
+  float wt[8][W], bs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < W; ++j) wt[i][j] = w[(size_t)(c0 + i) * W + j];
+    bs[i] = bias != nullptr ? bias[c0 + i] : 0.f;
+  }
+  float hist[W > 1 ? W - 1 : 1][8];
+  conv_history<DT, W>(x, cache, mask, b, T, D, c0, t_start, hist);
+
+  for (int t = t_start; t < t_end; ++t) {
+    const size_t off = ((size_t)b * T + t) * D + c0;
+    float out[8];
+    if (conv_valid(mask, b, T, t)) {
+      float xt[8];
+      E::ld8(x, off, xt);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float acc = bs[i];
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) acc += wt[i][j] * hist[j][i];
+        acc += wt[i][W - 1] * xt[i];
+        if (silu) acc = acc / (1.0f + __expf(-acc));
+        out[i] = acc;
+      }
+#pragma unroll
+      for (int j = 0; j + 1 < W - 1; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hist[j][i] = hist[j + 1][i];
+      if (W > 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hist[W > 1 ? W - 2 : 0][i] = xt[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) out[i] = 0.f;
+    }
+    E::st8(y, off, out);
+  }
+}
+
+template <int DT, int W>
+__global__ void __launch_bounds__(kConvThreads)
+conv_cache_kernel(const typename Elem<DT>::T* __restrict__ x, const uint8_t* __restrict__ mask,
+                  typename Elem<DT>::T* __restrict__ cache, int T, int D) {
+  using E = Elem<DT>;
+  const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * 8;
+  if (c0 >= D) return;
+  const int b = blockIdx.z;
+  float hist[W > 1 ? W - 1 : 1][8];
+  conv_history<DT, W>(x, cache, mask, b, T, D, c0, T, hist);   // reads the old cache first
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) E::st8(cache, ((size_t)b * (W - 1) + j) * D + c0, hist[j]);
+}
+
+template <int DT, int W>
+static hipError_t launch_conv_t(const ConvArgs& a) {
+  using T = typename Elem<DT>::T;
+  if (a.B == 0 || a.T == 0) return hipSuccess;
+  const int cblocks = (a.D / 8 + kConvThreads - 1) / kConvThreads;
+  const int segs = (a.T + kConvSeg - 1) / kConvSeg;
+  hipStream_t st = (hipStream_t)a.stream;
+  hipLaunchKernelGGL((conv_y_kernel<DT, W>), dim3(cblocks, segs, a.B), dim3(kConvThreads), 0, st,
+                     (const T*)a.x, a.weight, a.bias, a.mask, (const T*)a.cache, (T*)a.y, a.T, a.D, a.silu);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.cache == nullptr) return e;
+  hipLaunchKernelGGL((conv_cache_kernel<DT, W>), dim3(cblocks, 1, a.B), dim3(kConvThreads), 0, st,
+                     (const T*)a.x, a.mask, (T*)a.cache, a.T, a.D);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_conv_dt(const ConvArgs& a) {
+  switch (a.W) {
+    case 2: return launch_conv_t<DT, 2>(a);
+    case 3: return launch_conv_t<DT, 3>(a);
+    case 4: return launch_conv_t<DT, 4>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_short_conv(const ConvArgs& a) {
+  return a.dtype == 0 ? launch_conv_dt<0>(a) : launch_conv_dt<1>(a);
+}
+
+}  // namespace kda

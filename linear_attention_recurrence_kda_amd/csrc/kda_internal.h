@@ -1,0 +1,49 @@
+// Internal interface between the C ABI (kda_api.cpp) and the kernel launchers.
+// Every pointer here has already been validated by the ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *log_alpha, *beta;
+  const uint8_t* mask;
+  float* state;
+  void* o;
+  int B, H, dk, dv, dtype, l2norm;
+  void* stream;
+};
+
+struct ConvArgs {
+  const void* x;
+  const float *weight, *bias;
+  const uint8_t* mask;
+  void* cache;
+  void* y;
+  int B, T, D, W, dtype, silu;
+  void* stream;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *log_alpha, *beta;
+  const uint8_t* mask;
+  const float* init_state;
+  void* o;
+  float* final_state;
+  int B, T, H, dk, dv, chunk, dtype, l2norm;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_short_conv(const ConvArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+bool prefill_supported(int dk, int dv, int chunk);
+
+}  // namespace kda

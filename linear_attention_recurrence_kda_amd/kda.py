@@ -1,0 +1,202 @@
+"""Thin Python binding over libkda.so (C ABI in include/kda.h).
+
+Argument marshalling only: shapes/dtypes are checked, pointers and the current
+HIP stream are passed through, and every step of the computation runs in the
+library's gfx950 kernels.  PyTorch provides device memory and streams.  There
+is no fallback: if libkda.so is missing or the tensors are not on the GPU, the
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+KDA_FLAG_L2NORM_QK, KDA_FLAG_SILU = 1, 2
+STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
+          -3: "KDA_ERR_WORKSPACE", -4: "KDA_ERR_HIP"}
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
+           "kda_chunk_prefill_workspace_size", "kda_chunk_prefill", "kda_decode_step",
+           "kda_short_conv")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        self.status = status
+        msg = f"{fn} returned {STATUS.get(status, status)}"
+        if status == -4:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+
+
+def load():
+    """Load libkda.so (raises if it has not been built) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fp, up = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    i, u, sz = ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    lib.kda_abi_version.restype = i
+    lib.kda_abi_version.argtypes = []
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_last_hip_error.restype = i
+    lib.kda_last_hip_error.argtypes = []
+    lib.kda_chunk_prefill_workspace_size.restype = sz
+    lib.kda_chunk_prefill_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_chunk_prefill.restype = i
+    lib.kda_chunk_prefill.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp,
+                                      i, i, i, i, i, i, i, u, vp, sz, vp]
+    lib.kda_decode_step.restype = i
+    lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, i, i, i, i, i, u, vp]
+    lib.kda_short_conv.restype = i
+    lib.kda_short_conv.argtypes = [vp, fp, fp, up, vp, vp, i, i, i, i, i, u, vp]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KdaError(fn, status, load().kda_last_hip_error() if status == -4 else 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _req(t, name, dtype=None, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (libkda has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def prefill_workspace_size(B, T, H, dk, dv, chunk, dtype_code) -> int:
+    return int(load().kda_chunk_prefill_workspace_size(B, T, H, dk, dv, chunk, dtype_code))
+
+
+def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
+                  l2norm_qk=False, out=None, final_state=None, workspace=None):
+    """KDA prefill.  q,k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32), log_alpha [B,T,H,dk] fp32,
+    beta [B,T,H] fp32, mask [B,T] uint8/bool or None, initial_state [B,H,dk,dv] fp32 or None.
+    Returns (o [B,T,H,dv] in q's dtype, final_state [B,H,dk,dv] fp32)."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (B, T, H, dk))
+    _req(v, "v", q.dtype, (B, T, H, dv))
+    _req(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _req(beta, "beta", torch.float32, (B, T, H))
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        _req(mask, "mask", torch.uint8, (B, T))
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, (B, H, dk, dv))
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    _req(out, "out", q.dtype, (B, T, H, dv))
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _req(final_state, "final_state", torch.float32, (B, H, dk, dv))
+    need = prefill_workspace_size(B, T, H, dk, dv, chunk_size, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                               _ptr(initial_state), _ptr(out), _ptr(final_state),
+                               B, T, H, dk, dv, int(chunk_size), dt,
+                               KDA_FLAG_L2NORM_QK if l2norm_qk else 0,
+                               _ptr(workspace), wbytes, _stream())
+    _check("kda_chunk_prefill", st)
+    return out, final_state
+
+
+def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out=None):
+    """One decode step.  q,k [B,H,dk], v [B,H,dv], log_alpha [B,H,dk], beta [B,H],
+    state [B,H,dk,dv] fp32 updated in place, mask [B] or None.  Returns o [B,H,dv]."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (B, H, dk))
+    _req(v, "v", q.dtype, (B, H, dv))
+    _req(log_alpha, "log_alpha", torch.float32, (B, H, dk))
+    _req(beta, "beta", torch.float32, (B, H))
+    _req(state, "state", torch.float32, (B, H, dk, dv))
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        _req(mask, "mask", torch.uint8, (B,))
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _req(out, "out", q.dtype, (B, H, dv))
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                             _ptr(state), _ptr(out), B, H, dk, dv, dt,
+                             KDA_FLAG_L2NORM_QK if l2norm_qk else 0, _stream())
+    _check("kda_decode_step", st)
+    return out
+
+
+def short_conv(x, weight, bias=None, mask=None, conv_cache=None, silu=False, out=None):
+    """Masked depthwise causal conv.  x [B,T,D], weight [D,W] fp32, bias [D] or None,
+    mask [B,T] or None, conv_cache [B,W-1,D] (x's dtype, updated in place) or None.
+    Returns y [B,T,D]."""
+    import torch
+    lib = load()
+    dt = _dtype_code(x)
+    B, T, D = x.shape
+    W = weight.shape[1]
+    _req(x, "x")
+    _req(weight, "weight", torch.float32, (D, W))
+    if bias is not None:
+        _req(bias, "bias", torch.float32, (D,))
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        _req(mask, "mask", torch.uint8, (B, T))
+    if conv_cache is not None:
+        _req(conv_cache, "conv_cache", x.dtype, (B, W - 1, D))
+    if out is None:
+        out = torch.empty_like(x)
+    _req(out, "out", x.dtype, (B, T, D))
+    st = lib.kda_short_conv(_ptr(x), _ptr(weight), _ptr(bias), _ptr(mask), _ptr(conv_cache),
+                            _ptr(out), B, T, D, W, dt, KDA_FLAG_SILU if silu else 0, _stream())
+    _check("kda_short_conv", st)
+    return out

@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments with the documented status
+before making any HIP call (so no device is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_kda_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return kda.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_symbols() == sorted(kda.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert lib.kda_status_string(code).decode().startswith(kda.STATUS[code])
+    assert lib.kda_status_string(17) == b"unknown kda_status"
+    assert lib.kda_last_hip_error() == 0
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, mask=None, state=FAKE, o=FAKE,
+             B=2, H=2, dk=128, dv=128, dtype=0, flags=0)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["la"], a["beta"], a["mask"], a["state"],
+                               a["o"], a["B"], a["H"], a["dk"], a["dv"], a["dtype"], a["flags"], None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, dk=7) == UNSUPPORTED
+    assert _decode(lib, dv=256) == UNSUPPORTED
+    assert _decode(lib, dtype=5) == INVALID
+    assert _decode(lib, B=-1) == INVALID
+    assert _decode(lib, flags=8) == INVALID
+    assert _decode(lib, q=None) == INVALID
+    assert _decode(lib, state=None) == INVALID
+    assert _decode(lib, o=MISALIGNED) == INVALID
+    assert _decode(lib, B=0) == OK          # nothing to do, nothing launched
+    assert _decode(lib, H=0, q=None) == OK
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, mask=None, s0=None, o=FAKE, sT=FAKE,
+             B=1, T=64, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_prefill(a["q"], a["k"], a["v"], a["la"], a["beta"], a["mask"], a["s0"],
+                                 a["o"], a["sT"], a["B"], a["T"], a["H"], a["dk"], a["dv"],
+                                 a["chunk"], a["dtype"], a["flags"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, chunk=48) == UNSUPPORTED
+    assert _prefill(lib, chunk=0) == UNSUPPORTED
+    assert _prefill(lib, dk=100) == UNSUPPORTED
+    assert _prefill(lib, T=-3) == INVALID
+    assert _prefill(lib, dtype=2) == INVALID
+    assert _prefill(lib, flags=2) == INVALID            # SILU belongs to the short conv
+    assert _prefill(lib, v=None) == INVALID
+    assert _prefill(lib, sT=None) == INVALID
+    assert _prefill(lib, s0=MISALIGNED) == INVALID
+    assert _prefill(lib, wsb=16) == WORKSPACE
+    assert _prefill(lib, ws=None) == WORKSPACE
+    assert _prefill(lib, B=0, ws=None, wsb=0) == OK
+
+
+def test_workspace_size_query(lib):
+    f = lib.kda_chunk_prefill_workspace_size
+    assert f(1, 0, 32, 128, 128, 64, 0) == 0
+    assert f(1, 64, 32, 128, 128, 48, 0) == 0            # unsupported chunk
+    assert f(1, 64, 32, 100, 128, 64, 0) == 0            # unsupported head size
+    one = f(1, 64, 1, 128, 128, 64, 0)
+    assert one > 0 and one % 16 == 0
+    assert f(1, 65, 1, 128, 128, 64, 0) == 2 * one       # ragged tail takes a whole chunk
+    assert f(4, 4096, 32, 128, 128, 64, 0) == 4 * 32 * 64 * one
+    assert f(1, 64, 1, 128, 128, 64, 1) > one            # fp32 inputs keep residual parts
+
+
+def _conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, bias=None, mask=None, cache=FAKE, y=FAKE, B=2, T=8, D=64, W=4,
+             dtype=0, flags=0)
+    a.update(kw)
+    return lib.kda_short_conv(a["x"], a["w"], a["bias"], a["mask"], a["cache"], a["y"], a["B"],
+                              a["T"], a["D"], a["W"], a["dtype"], a["flags"], None)
+
+
+def test_conv_validation(lib):
+    assert _conv(lib, W=5) == UNSUPPORTED
+    assert _conv(lib, W=1) == UNSUPPORTED
+    assert _conv(lib, D=12) == UNSUPPORTED
+    assert _conv(lib, D=0) == INVALID
+    assert _conv(lib, flags=1) == INVALID               # L2NORM belongs to the recurrence
+    assert _conv(lib, w=None) == INVALID
+    assert _conv(lib, x=None) == INVALID
+    assert _conv(lib, cache=MISALIGNED) == INVALID
+    assert _conv(lib, T=0) == OK
+    assert _conv(lib, B=0) == OK
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.short_conv(x, torch.zeros(8, 4))
