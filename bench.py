@@ -38,26 +38,34 @@ def parse():
     ap.add_argument("--T", type=int, default=131072)
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--decode-batch", type=int, default=256)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096,
-                    help="tokens per head of the oracle's CPU-baseline sample (32 heads)")
+    ap.add_argument("--cpu-segment", type=int, default=8192,
+                    help="tokens of the oracle's CPU-baseline segment (32 heads)")
+    ap.add_argument("--cpu-repeats", type=int, default=16,
+                    help="times the segment is chained through the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
 
 def cpu_baseline(args):
-    """The fp64 oracle on a bounded sample of the same prefill workload (host cores)."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same prefill workload:
+    one seeded 32-head segment chained `cpu_repeats` times with the state carried, on
+    every host core (OpenMP over heads).  Inputs are converted to fp64 before timing."""
     import numpy as np
     from linear_attention_recurrence_kda_amd import datagen as D
     from oracle import oracle as O
-    H, T = 32, args.cpu_sample_tokens
-    inp = D.np_kda_inputs(1, T, H, 128, 128, "bf16", seed=0)
+    H, seg, reps = 32, args.cpu_segment, args.cpu_repeats
+    inp = {n: np.ascontiguousarray(x, dtype=np.float64)
+           for n, x in D.np_kda_inputs(1, seg, H, 128, 128, "bf16", seed=0).items()}
     threads = O.host_threads()
-    O.c_prefill(**{n: x[:, :16] for n, x in inp.items()}, nthreads=threads)   # load + warm
+    O.c_prefill(**{n: x[:, :16] for n, x in inp.items()}, nthreads=threads)   # load the library
+    state = None
     t0 = time.perf_counter()
-    O.c_prefill(**inp, nthreads=threads)
+    for _ in range(reps):
+        _, state = O.c_prefill(**inp, init_state=state, nthreads=threads)
     dt = time.perf_counter() - t0
-    return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 token loop, B=1 H=32 T={T} dk=dv=128 (seed 0), {dt:.2f} s wall"}
+    return {"value": seg * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 token loop, B=1 H=32 dk=dv=128: a {seg}-token segment chained "
+                      f"{reps}x ({seg * reps} tokens), {dt:.1f} s wall"}
 
 
 def main():

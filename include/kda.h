@@ -21,9 +21,11 @@
  * read into the arithmetic (NaN or garbage there cannot leak).
  *
  * Conventions for every entry point
- *   - All tensor pointers are device pointers (HBM), dense, row-major, 16-byte
- *     aligned, owned by the caller.  The library allocates nothing, keeps no
- *     pointer after returning, and holds no global state.
+ *   - All tensor pointers are device pointers (HBM), dense, row-major, owned by
+ *     the caller, and aligned to their element size; the tensors each entry
+ *     point reads with 16-byte vector accesses (listed there) must be 16-byte
+ *     aligned.  The library allocates nothing, keeps no pointer after
+ *     returning, and holds no global state.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it; nothing synchronises the host.
  *   - Arguments are validated on the host before any HIP call.  A failing call
@@ -97,8 +99,9 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  *   final_state [B,H,dk,dv]  fp32, written; may be the same pointer as init_state
  *
  * Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}; T >= 0
- * (T = 0 copies init_state to final_state).  The ragged tail of the last chunk
- * is handled as masked positions.  `flags` may hold KDA_FLAG_L2NORM_QK.
+ * (T = 0 copies init_state to final_state).  16-byte aligned: q, k,
+ * log_alpha.  The ragged tail of the last chunk is handled as masked
+ * positions.  `flags` may hold KDA_FLAG_L2NORM_QK.
  * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
  * bytes of device memory (may be NULL when that size is 0).
  */
@@ -122,7 +125,7 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
  *   o           [B,H,dv]     dtype, written
  *
  * Supported: dk, dv in {16, 32, 64, 128}; B, H >= 0.  `flags` may hold
- * KDA_FLAG_L2NORM_QK.
+ * KDA_FLAG_L2NORM_QK.  16-byte aligned: state.
  */
 int kda_decode_step(const void* q, const void* k, const void* v,
                     const float* log_alpha, const float* beta, const uint8_t* mask,
@@ -147,7 +150,7 @@ int kda_decode_step(const void* q, const void* k, const void* v,
  *   y           [B,T,D]      dtype, written; must not overlap x or conv_cache
  *
  * Supported: W in {2, 3, 4}; D >= 1, D a multiple of 8; T >= 0.  `flags` may
- * hold KDA_FLAG_SILU.
+ * hold KDA_FLAG_SILU.  16-byte aligned: x, y, conv_cache.
  */
 int kda_short_conv(const void* x, const float* weight, const float* bias, const uint8_t* mask,
                    void* conv_cache, void* y, int B, int T, int D, int W, int dtype,

@@ -12,7 +12,9 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+uintptr_t elem_bytes(int dt) { return dt == KDA_BF16 ? 2 : 4; }
 bool dtype_ok(int dt) { return dt == KDA_BF16 || dt == KDA_F32; }
 
 int hip_status(hipError_t e) {
@@ -56,12 +58,16 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
     return KDA_ERR_UNSUPPORTED;
   const bool work = (size_t)B * H > 0;
   if (work) {
-    if (final_state == nullptr || !aligned16(final_state)) return KDA_ERR_INVALID_ARG;
-    if (init_state != nullptr && !aligned16(init_state)) return KDA_ERR_INVALID_ARG;
+    if (final_state == nullptr || !aligned(final_state, 4)) return KDA_ERR_INVALID_ARG;
+    if (init_state != nullptr && !aligned(init_state, 4)) return KDA_ERR_INVALID_ARG;
     if (T > 0) {
-      const void* req[] = {q, k, v, log_alpha, beta, o};
-      for (const void* p : req)
+      // q, k, log_alpha are read with 16-byte vector loads; the rest element by element
+      const void* vec[] = {q, k, log_alpha};
+      for (const void* p : vec)
         if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+      if (v == nullptr || o == nullptr || beta == nullptr) return KDA_ERR_INVALID_ARG;
+      if (!aligned(v, elem_bytes(dtype)) || !aligned(o, elem_bytes(dtype)) || !aligned(beta, 4))
+        return KDA_ERR_INVALID_ARG;
     }
   }
   const size_t need = kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
@@ -83,7 +89,12 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
   if ((size_t)B * H == 0) return KDA_OK;
   const void* req[] = {q, k, v, log_alpha, beta, state, o};
   for (const void* p : req)
-    if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+    if (p == nullptr) return KDA_ERR_INVALID_ARG;
+  // the state is streamed with 16-byte vector accesses; the rest element by element
+  if (!aligned16(state) || !aligned(log_alpha, 4) || !aligned(beta, 4)) return KDA_ERR_INVALID_ARG;
+  const void* el[] = {q, k, v, o};
+  for (const void* p : el)
+    if (!aligned(p, elem_bytes(dtype))) return KDA_ERR_INVALID_ARG;
   kda::DecodeArgs a{q, k, v, log_alpha, beta, mask, state, o, B, H, dk, dv, dtype,
                     (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, stream};
   return hip_status(kda::launch_decode(a));

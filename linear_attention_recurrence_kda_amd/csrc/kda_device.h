@@ -26,6 +26,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 template <int DT> struct Elem;
 template <> struct Elem<0> {
   typedef uint16_t T;
+  __device__ __forceinline__ static float cvt(T x) { return bf16_bits_to_f32(x); }
   __device__ __forceinline__ static float ld(const T* p, size_t i) { return bf16_bits_to_f32(p[i]); }
   __device__ __forceinline__ static void st(T* p, size_t i, float v) { p[i] = f32_to_bf16_bits(v); }
   // 8 consecutive values starting at p[i] (i multiple of 8, 16-byte aligned)
@@ -62,6 +63,7 @@ template <> struct Elem<0> {
 };
 template <> struct Elem<1> {
   typedef float T;
+  __device__ __forceinline__ static float cvt(T x) { return x; }
   __device__ __forceinline__ static float ld(const T* p, size_t i) { return p[i]; }
   __device__ __forceinline__ static void st(T* p, size_t i, float v) { p[i] = v; }
   __device__ __forceinline__ static void ld8(const T* p, size_t i, float* out) {

@@ -62,7 +62,8 @@ def test_decode_validation(lib):
     assert _decode(lib, flags=8) == INVALID
     assert _decode(lib, q=None) == INVALID
     assert _decode(lib, state=None) == INVALID
-    assert _decode(lib, o=MISALIGNED) == INVALID
+    assert _decode(lib, state=MISALIGNED) == INVALID
+    assert _decode(lib, o=ctypes.c_void_p(0x10001)) == INVALID
     assert _decode(lib, B=0) == OK          # nothing to do, nothing launched
     assert _decode(lib, H=0, q=None) == OK
 
@@ -85,7 +86,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, flags=2) == INVALID            # SILU belongs to the short conv
     assert _prefill(lib, v=None) == INVALID
     assert _prefill(lib, sT=None) == INVALID
-    assert _prefill(lib, s0=MISALIGNED) == INVALID
+    assert _prefill(lib, s0=ctypes.c_void_p(0x10002)) == INVALID
+    assert _prefill(lib, la=MISALIGNED) == INVALID
     assert _prefill(lib, wsb=16) == WORKSPACE
     assert _prefill(lib, ws=None) == WORKSPACE
     assert _prefill(lib, B=0, ws=None, wsb=0) == OK
