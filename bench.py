@@ -25,6 +25,25 @@ PREFILL_BYTES_PER_TH = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (
 DECODE_BYTES_PER_SH = 132612         # state read+write 8*K*V + q,k,v,o (1024) + log_alpha (512) + beta
 
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on the default workload,
+# scaled by a known-size streaming kernel in the same run (factors 2.0 and 1.0 on this GPU).  A
+# figure is reported only while the kernel sources still hash to what was profiled.
+MEASURED_TRAFFIC = {
+    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "87657106a762d602", "bytes": 17.796e9},
+    "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "1752aeb7f0fd0e34", "bytes": 1.087e9},
+}
+
+
+def measured_traffic(key, default_workload):
+    import hashlib
+    ent = MEASURED_TRAFFIC[key]
+    h = hashlib.sha256()
+    for name in ent["sources"]:
+        with open(os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return ent["bytes"] if default_workload and h.hexdigest()[:16] == ent["sha"] else None
+
+
 def prefill_flops_per_th(C, K=128, V=128):
     # chunk WY form, triangles exploited: A, P, the solve on [V|K], P U, three state products
     return C * (3 * K + 2 * V) + 6 * K * V
@@ -43,6 +62,9 @@ def parse():
     ap.add_argument("--cpu-repeats", type=int, default=16,
                     help="times the segment is chained through the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size kernel "
+                         "that scales the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
     return ap.parse_args()
 
 
@@ -142,6 +164,9 @@ def main():
     dstep_ms = e0.elapsed_time(e1) / reps
 
     th = T * H
+    default_wl = (T == 131072 and C == 64 and Bd == 256)
+    pre_traffic = measured_traffic("prefill", default_wl)
+    dec_traffic = measured_traffic("decode", default_wl)
     tok_s = T / (pre_avg * 1e-3)
     pre_gbs = PREFILL_BYTES_PER_TH * th / (pre_avg * 1e-3) / 1e9
     pre_tflops = prefill_flops_per_th(C) * th / (pre_avg * 1e-3) / 1e12
@@ -170,12 +195,21 @@ def main():
                    "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
                    "tokens_per_s": Bd / (dec_avg * 1e-3),
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+                                "frac": dec_gbs / HBM_PEAK_GBS, "traffic": dec_traffic,
+                                "algorithmic_bytes": DECODE_BYTES_PER_SH * Bd * H,
                                 "kernel": "decode_step_kernel"}},
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kda_chunk_prefill (prep_kernel + scan_kernel)"},
+                     "frac": pre_gbs / HBM_PEAK_GBS, "traffic": pre_traffic,
+                     "algorithmic_bytes": PREFILL_BYTES_PER_TH * th,
+                     "kernel": "kda_chunk_prefill call (prep_kernel then scan_kernel)"},
     }
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)          # a streaming kernel (copy_ would be a DMA memcpy)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = {"read": n * 4, "write": n * 4}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(line), flush=True)
