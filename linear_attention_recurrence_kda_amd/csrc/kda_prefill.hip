@@ -114,20 +114,24 @@ prep_kernel(PrepParams p) {
   constexpr int KB = K + 8;           // bf16 row stride (16-byte aligned rows)
   constexpr int CP = C + 4;           // fp32 row stride of the C x C matrices (16 rows -> 16 bank groups)
   constexpr int NLA = C * (K / 4) / kPrepThreads;                        // float4 of log_alpha per thread
-  constexpr int NKI = (K * (C / 8) + kPrepThreads - 1) / kPrepThreads;   // (channel, 8 rows) items per thread
+  constexpr int NKI = (C * (K / 8) + kPrepThreads - 1) / kPrepThreads;   // (row, 8 channels) items per thread
   static_assert(NLA >= 1 && C * (K / 4) % kPrepThreads == 0, "log_alpha tiling");
 
-  __shared__ float s_G[C * KP];                        // G (log2), then Gam in the fast path
+  __shared__ __attribute__((aligned(16))) float s_G[C * KP];   // G (log2), then Gam in the fast path
   __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][C * KB];   // Kt hi, lo
   __shared__ __attribute__((aligned(16))) __bf16 s_ki[2][C * KB];   // Ki hi, lo
-  __shared__ __attribute__((aligned(16))) float s_A[C * CP];        // A, later M = P T'
-  __shared__ __attribute__((aligned(16))) float s_T[C * CP];
-  __shared__ __attribute__((aligned(16))) float s_P[C * CP];
+  // A (later M = P T'), T and P, carved from one buffer that first stages Kh rows
+  constexpr int kMatBytes = 3 * C * CP * 4, kKhStageBytes = C * KB * 2 * (SPLIT ? 2 : 1);
+  __shared__ __attribute__((aligned(16))) unsigned char s_mat[kMatBytes > kKhStageBytes ? kMatBytes : kKhStageBytes];
+  float* s_A = reinterpret_cast<float*>(s_mat);
+  float* s_T = s_A + C * CP;
+  float* s_P = s_T + C * CP;
   // inversion temporaries and (later) per-wave staging tiles share one buffer
   constexpr int kXSize = (RT > 1 ? RT - 1 : 1) * 16 * 17, kStageSize = 4 * 16 * 17;
   __shared__ float s_scratch[kXSize > kStageSize ? kXSize : kStageSize];
   float* s_X = s_scratch;
-  __shared__ float s_beta[C], s_qs[C], s_ks[C], s_gc[K];
+  __shared__ float s_beta[C], s_qs[C], s_ks[C];
+  __shared__ __attribute__((aligned(16))) float s_gc[K];
   __shared__ int s_valid[C];
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -150,13 +154,12 @@ prep_kernel(PrepParams p) {
     const int r = idx / (K / 4), c = (idx % (K / 4)) * 4;
     la_r[i] = *reinterpret_cast<const float4*>(p.log_alpha + grow(tsafe(r)) * dk + (c < dk ? c : 0));
   }
-  Raw k_r[NKI][8];
+  float k_r[NKI][8];
 #pragma unroll
   for (int it = 0; it < NKI; ++it) {
-    const int idx = tid + kPrepThreads * it;
-    const int c = idx % K, oct = (idx / K) % (C / 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) k_r[it][e] = kg[grow(tsafe(8 * oct + e)) * dk + (c < dk ? c : 0)];
+    const int idx = (tid + kPrepThreads * it) % (C * (K / 8));
+    const int r = idx / (K / 8), c0 = (idx % (K / 8)) * 8;
+    E::ld8(kg, grow(tsafe(r)) * dk + (c0 < dk ? c0 : 0), k_r[it]);
   }
   const int I = wave;                                   // this wave's row tile in the A/P and W phases
   const int rq = 16 * (I < RT ? I : 0) + (lane % 16);
@@ -220,37 +223,59 @@ prep_kernel(PrepParams p) {
   }
   const int fast = __syncthreads_and(tid >= K || s_gc[tid] >= kFastLimit);
 
-  // ---- elementwise decay factors; item = (channel c, 8 consecutive rows)
+  // ---- elementwise decay factors; item = (row r, 8 consecutive channels).  Factors are
+  //      at least 2^-120 on the fast path, so the bare hardware exp2 is exact enough.
+  {
+    __bf16* kh_stage = reinterpret_cast<__bf16*>(s_mat);          // Kh rows, transposed below
+    __bf16* kh_stage_lo = kh_stage + C * KB;
 #pragma unroll
-  for (int it = 0; it < NKI; ++it) {
-    const int idx = tid + kPrepThreads * it;
-    if (idx < K * (C / 8)) {
-      const int c = idx % K, oct = idx / K;
-      const float gc = s_gc[c];
-      float kh[8];
+    for (int it = 0; it < NKI; ++it) {
+      const int idx = tid + kPrepThreads * it;
+      if (idx < C * (K / 8)) {
+        const int r = idx / (K / 8), c0 = (idx % (K / 8)) * 8;
+        const float sc = (c0 < dk && s_valid[r]) ? s_ks[r] : 0.f;
+        float g[8], gc[8], kt[8], ki[8], kh[8], gam[8];
+        ld8f(&s_G[r * KP + c0], g);
+        ld8f(&s_gc[c0], gc);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = oct * 8 + e;
-        const float kv = (c < dk && s_valid[r]) ? E::cvt(k_r[it][e]) * s_ks[r] : 0.f;
-        const float g = s_G[r * KP + c];
-        const float gam = exp2f(g);
-        const float kt = kv * gam;
-        const __bf16 kth = (__bf16)kt;
-        s_kt[0][r * KB + c] = kth;
-        s_kt[1][r * KB + c] = (__bf16)(kt - (float)kth);
-        const float ki = fast ? kv * exp2f(-g) : 0.f;
-        const __bf16 kih = (__bf16)ki;
-        s_ki[0][r * KB + c] = kih;
-        s_ki[1][r * KB + c] = (__bf16)(ki - (float)kih);
-        kh[e] = kv * exp2f(gc - g);
-        if (fast) s_G[r * KP + c] = gam;       // slow path keeps G for the exact pairwise decays
+        for (int e = 0; e < 8; ++e) {
+          const float kv = k_r[it][e] * sc;
+          gam[e] = __builtin_amdgcn_exp2f(g[e]);
+          kt[e] = kv * gam[e];
+          ki[e] = fast ? kv * __builtin_amdgcn_exp2f(-g[e]) : 0.f;
+          kh[e] = kv * __builtin_amdgcn_exp2f(gc[e] - g[e]);
+        }
+        bf16x8 hi, lo;
+        split8(kt, hi, lo);
+        *reinterpret_cast<bf16x8*>(&s_kt[0][r * KB + c0]) = hi;
+        *reinterpret_cast<bf16x8*>(&s_kt[1][r * KB + c0]) = lo;
+        split8(ki, hi, lo);
+        *reinterpret_cast<bf16x8*>(&s_ki[0][r * KB + c0]) = hi;
+        *reinterpret_cast<bf16x8*>(&s_ki[1][r * KB + c0]) = lo;
+        split8(kh, hi, lo);
+        *reinterpret_cast<bf16x8*>(&kh_stage[r * KB + c0]) = hi;
+        if (SPLIT) *reinterpret_cast<bf16x8*>(&kh_stage_lo[r * KB + c0]) = lo;
+        if (fast) {                         // slow path keeps G for the exact pairwise decays
+          float4* gp = reinterpret_cast<float4*>(&s_G[r * KP + c0]);
+          gp[0] = make_float4(gam[0], gam[1], gam[2], gam[3]);
+          gp[1] = make_float4(gam[4], gam[5], gam[6], gam[7]);
+        }
       }
-      // Kh^T fragment: row c, contraction over rows 8*oct .. +7
+    }
+    __syncthreads();
+    // Kh^T fragments: row c, contraction over rows 8*oct .. +7
+    for (int idx = tid; idx < K * (C / 8); idx += kPrepThreads) {
+      const int c = idx % K, oct = idx / K;
       const int rt = c / 16, ks = oct / 4, ln = (c % 16) + 16 * (oct % 4);
-      bf16x8 hi, lo;
-      split8(kh, hi, lo);
-      store_frag(wsb + L::off_kh + frag_off(rt, ks, ln, C), hi);
-      if (SPLIT) store_frag(wsb + L::off_kh + L::kCK + frag_off(rt, ks, ln, C), lo);
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = kh_stage[(8 * oct + e) * KB + c];
+      store_frag(wsb + L::off_kh + frag_off(rt, ks, ln, C), v);
+      if (SPLIT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = kh_stage_lo[(8 * oct + e) * KB + c];
+        store_frag(wsb + L::off_kh + L::kCK + frag_off(rt, ks, ln, C), v);
+      }
     }
   }
   if (tid < K) reinterpret_cast<float*>(wsb + L::off_gam)[tid] = exp2f(s_gc[tid]);
@@ -340,9 +365,12 @@ prep_kernel(PrepParams p) {
     float x[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
+      float arow[16];
+      ld8f(&s_A[(16 * Ib + rr) * CP + 16 * Ib], arow);
+      ld8f(&s_A[(16 * Ib + rr) * CP + 16 * Ib + 8], arow + 8);
       float v = (rr == cc) ? 1.f : 0.f;
 #pragma unroll
-      for (int jj = 0; jj < rr; ++jj) v -= s_A[(16 * Ib + rr) * CP + 16 * Ib + jj] * x[jj];
+      for (int jj = 0; jj < rr; ++jj) v -= arow[jj] * x[jj];
       x[rr] = v;
     }
 #pragma unroll
