@@ -61,13 +61,12 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
     if (final_state == nullptr || !aligned(final_state, 4)) return KDA_ERR_INVALID_ARG;
     if (init_state != nullptr && !aligned(init_state, 4)) return KDA_ERR_INVALID_ARG;
     if (T > 0) {
-      // q, k, log_alpha are read with 16-byte vector loads; the rest element by element
-      const void* vec[] = {q, k, log_alpha};
+      // q, k, v, log_alpha are read with 16-byte vector loads; the rest element by element
+      const void* vec[] = {q, k, v, log_alpha};
       for (const void* p : vec)
         if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
-      if (v == nullptr || o == nullptr || beta == nullptr) return KDA_ERR_INVALID_ARG;
-      if (!aligned(v, elem_bytes(dtype)) || !aligned(o, elem_bytes(dtype)) || !aligned(beta, 4))
-        return KDA_ERR_INVALID_ARG;
+      if (o == nullptr || beta == nullptr) return KDA_ERR_INVALID_ARG;
+      if (!aligned(o, elem_bytes(dtype)) || !aligned(beta, 4)) return KDA_ERR_INVALID_ARG;
     }
   }
   const size_t need = kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);

@@ -10,15 +10,18 @@
 // Qt = Q*Gam, Kh = K*Gam_last/Gam:
 //   A  = strict_lower(Diag(beta) Kt Ki^T)      P = lower(Qt Ki^T)
 //   T' = (I + A)^-1 Diag(beta)                 (unit lower-triangular solve, fp32)
-//   Wn = -T' Kt,   Qh = Qt - (P T') Kt
-//   U  = T' V + Wn S0                          (per-token corrections)
-//   O  = Qh S0 + P (T' V)
+//   Wn = -T' Kt,  Qh = Qt - (P T') Kt,  Ut = T' V,  O0 = P Ut
+//   U  = Ut + Wn S0                            (per-token corrections)
+//   O  = O0 + Qh S0
 //   S1 = Diag(Gam_last) S0 + Kh^T U
 // Only the last three lines depend on the state, so the work splits into:
 //   prep_kernel: one workgroup per (b, h, chunk), fully parallel; writes Wn, Qh,
-//     Kh^T, T', P and Gam_last to a workspace in MFMA operand order;
-//   scan_kernel: one workgroup per (b, h, dv-tile), a loop over the chunks in
-//     order with the fp32 state tile held in registers across chunks.
+//     Kh^T (bf16, MFMA operand order), Ut and O0 (fp32, MFMA accumulator order)
+//     and Gam_last to a workspace;
+//   scan_kernel: one workgroup per (b, h, 16-column dv tile); a loop over the
+//     chunks in order with the fp32 state tile in registers, each chunk's
+//     operands streamed into an LDS ring by direct global->LDS copies issued one
+//     chunk ahead of their use.
 // The factorisation Kt Ki^T (decay relative to the chunk start) is used when
 // every channel's decay over the chunk stays above 2^-120 (then no factor
 // over- or under-flows); otherwise that chunk computes A and P entry by entry
@@ -26,8 +29,8 @@
 // from a product, so nothing from a later position can reach an earlier one.
 //
 // Precision: bf16 MFMA operands that are not exactly bf16 are split into a
-// bf16 high part and a bf16 residual where that matters (A, P, T', S, U and
-// T'V); with fp32 inputs every operand is split.
+// bf16 high part and a bf16 residual where that matters (A, P, T', S, U, Ut);
+// with fp32 inputs every operand is split.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -35,58 +38,58 @@ namespace kda {
 
 constexpr int kPrepThreads = 256;
 constexpr int kScanThreads = 256;
-constexpr int kVT = 16;                 // dv columns per scan workgroup
-constexpr float kFastLimit = -120.0f;   // log2 decay over one chunk for the factorised path
+constexpr int kVT = 16;                  // dv columns per scan workgroup
+constexpr float kFastLimit = -120.0f;    // log2 decay over one chunk for the factorised path
+constexpr size_t kSinkBytes = 16384;     // workspace tail that absorbs the stores of rows past T
 
 // ---------------------------------------------------------------- workspace layout
-// Per (b, h, chunk), in 2-byte units.  Every matrix is stored in A-operand order
-// of v_mfma_f32_16x16x32_bf16: fragment (row tile rt, k step ks) is 64 lanes x
-// 8 bf16, lane l holding M[16 rt + l%16][32 ks + 8 (l/16) .. +7].
-template <int K, int C, bool SPLIT>
+// Per (b, h, chunk), in 2-byte units.  Wn, Qh and Kh^T are in A-operand order of
+// v_mfma_f32_16x16x32_bf16: fragment (row tile rt, k step ks) is 64 lanes x 8 bf16
+// (1 KB), lane l holding M[16 rt + l%16][32 ks + 8 (l/16) .. +7]; with fp32 inputs
+// the bf16 residual parts follow the high parts.  Ut and O0 are in accumulator
+// order: block (row tile rt, column tile ct) is 64 lanes x 4 fp32 (1 KB), lane l
+// holding M[16 rt + 4 (l/16) .. +3][16 ct + l%16].
+template <int K, int V, int C, bool SPLIT>
 struct WsLayout {
   static constexpr size_t kCK = (size_t)C * K;
-  static constexpr size_t kCC = (size_t)C * C;
   static constexpr size_t kSplitCK = SPLIT ? 2 * kCK : kCK;
-  static constexpr size_t off_wn = 0;                    // -T' Kt           [C x K] (hi, lo)
-  static constexpr size_t off_qh = off_wn + kSplitCK;    // Qt - P T' Kt     [C x K]
-  static constexpr size_t off_kh = off_qh + kSplitCK;    // Kh^T             [K x C]
-  static constexpr size_t off_tp = off_kh + kSplitCK;    // T' hi, lo        [C x C]
-  static constexpr size_t off_p = off_tp + 2 * kCC;      // P hi, lo         [C x C]
-  static constexpr size_t off_gam = off_p + 2 * kCC;     // Gam_last, K fp32
+  static constexpr size_t kCV = (size_t)C * V * 2;       // fp32 C x V in 2-byte units
+  static constexpr size_t off_wn = 0;                    // -T' Kt          [C x K]
+  static constexpr size_t off_qh = off_wn + kSplitCK;    // Qt - P T' Kt    [C x K]
+  static constexpr size_t off_kh = off_qh + kSplitCK;    // Kh^T            [K x C]
+  static constexpr size_t off_ut = off_kh + kSplitCK;    // T' V            [C x V] fp32
+  static constexpr size_t off_o0 = off_ut + kCV;         // P T' V          [C x V] fp32
+  static constexpr size_t off_gam = off_o0 + kCV;        // Gam_last        [K] fp32
   static constexpr size_t kElems = off_gam + 2 * (size_t)K;
 };
 
 __device__ __forceinline__ size_t frag_off(int rt, int ks, int lane, int kk) {
   return ((size_t)(rt * (kk / 32) + ks) * 64 + lane) * 8;
 }
+template <int V>
+__device__ __forceinline__ size_t acc_off(int rt, int ct, int lane) {
+  return ((size_t)(rt * (V / 16) + ct) * 64 + lane) * 8;
+}
 
 struct PrepParams {
-  const void *q, *k;
+  const void *q, *k, *v;
   const float *log_alpha, *beta;
   const uint8_t* mask;
   uint16_t* ws;
-  int B, T, H, dk, chunk, NC, l2norm;
+  int B, T, H, dk, dv, chunk, NC, l2norm;
 };
 
 struct ScanParams {
-  const void* v;
-  const uint8_t* mask;
   const float* init_state;
   float* final_state;
   void* o;
   const uint16_t* ws;
+  void* sink;
   int B, T, H, dk, dv, chunk, NC, NT, nbh;
 };
 
-__device__ __forceinline__ bool row_valid(const uint8_t* mask, int b, int T, int chunk, int r, int t) {
-  return r < chunk && t < T && (mask == nullptr || mask[(size_t)b * T + t] != 0);
-}
-
 __device__ __forceinline__ void store_frag(uint16_t* dst, const bf16x8& v) {
   *reinterpret_cast<bf16x8*>(dst) = v;
-}
-__device__ __forceinline__ bf16x8 load_frag(const uint16_t* src) {
-  return *reinterpret_cast<const bf16x8*>(src);
 }
 // 8 consecutive floats from 16-byte aligned LDS
 __device__ __forceinline__ void ld8f(const float* src, float* out) {
@@ -95,18 +98,26 @@ __device__ __forceinline__ void ld8f(const float* src, float* out) {
   out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
+// Element (n, j) of an n-major LDS matrix with C bf16 per row and no padding: the
+// 16-byte blocks of row n are permuted by an XOR with bits of n, so 16 lanes that
+// read one block column of 16 consecutive rows, or 64 lanes that write 16-byte
+// blocks of rows 4 apart, spread over the banks.
+template <int C>
+__device__ __forceinline__ int swz(int n, int j) {
+  return n * C + ((((j >> 3) ^ ((n ^ (n >> 3)) & (C / 8 - 1)))) << 3) + (j & 7);
+}
 
 // ================================================================ prep kernel
 // One workgroup per (chunk, head, batch row).  Every global load of the chunk is
 // issued first, unconditionally, from in-bounds rows; row validity (mask, ragged
 // tail) is applied afterwards by select, so no load waits on another.
-template <int DT, int K, int C>
+template <int DT, int K, int V, int C>
 __global__ void __launch_bounds__(kPrepThreads)
 prep_kernel(PrepParams p) {
   using E = Elem<DT>;
   using Raw = typename E::T;
   constexpr bool SPLIT = (DT == 1);
-  using L = WsLayout<K, C, SPLIT>;
+  using L = WsLayout<K, V, C, SPLIT>;
   constexpr int RT = C / 16;          // row tiles of the chunk
   constexpr int CS = C / 32;          // k steps over chunk rows
   constexpr int KS = K / 32;          // k steps over key channels
@@ -115,15 +126,23 @@ prep_kernel(PrepParams p) {
   constexpr int CP = C + 4;           // fp32 row stride of the C x C matrices (16 rows -> 16 bank groups)
   constexpr int NLA = C * (K / 4) / kPrepThreads;                        // float4 of log_alpha per thread
   constexpr int NKI = (C * (K / 8) + kPrepThreads - 1) / kPrepThreads;   // (row, 8 channels) items per thread
+  constexpr int NVB = (C / 8) * (V / 4);                                 // (8 rows, 4 columns) blocks of V
+  constexpr int NVI = (NVB + kPrepThreads - 1) / kPrepThreads;
   static_assert(NLA >= 1 && C * (K / 4) % kPrepThreads == 0, "log_alpha tiling");
 
-  __shared__ __attribute__((aligned(16))) float s_G[C * KP];   // G (log2), then Gam in the fast path
-  __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][C * KB];   // Kt hi, lo
-  __shared__ __attribute__((aligned(16))) __bf16 s_ki[2][C * KB];   // Ki hi, lo
-  // A (later M = P T'), T and P, carved from one buffer that first stages Kh rows
+  // LDS regions; a later phase reuses a region once every read of its first use is behind a barrier
+  constexpr int kGBytes = C * KP * 4, kUtTBytes = 2 * V * C * 2;                    // G, Gam | Ut^T hi, lo
+  constexpr int kKiBytes = 2 * C * KB * 2, kVTBytes = (SPLIT ? 2 : 1) * V * C * 2;   // Ki hi, lo | V^T
   constexpr int kMatBytes = 3 * C * CP * 4, kKhStageBytes = C * KB * 2 * (SPLIT ? 2 : 1);
+  __shared__ __attribute__((aligned(16))) unsigned char s_rg[kGBytes > kUtTBytes ? kGBytes : kUtTBytes];
+  __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][C * KB];                  // Kt hi, lo
+  __shared__ __attribute__((aligned(16))) unsigned char s_rki[kKiBytes > kVTBytes ? kKiBytes : kVTBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_mat[kMatBytes > kKhStageBytes ? kMatBytes : kKhStageBytes];
-  float* s_A = reinterpret_cast<float*>(s_mat);
+  float* s_G = reinterpret_cast<float*>(s_rg);            // G (log2), then Gam on the fast path
+  __bf16* s_utT = reinterpret_cast<__bf16*>(s_rg);        // [hi, lo][V][C], swizzled
+  __bf16* s_ki = reinterpret_cast<__bf16*>(s_rki);        // [hi, lo][C * KB]
+  __bf16* s_vT = reinterpret_cast<__bf16*>(s_rki);        // [hi(, lo)][V][C], swizzled
+  float* s_A = reinterpret_cast<float*>(s_mat);           // A, later M = P T'
   float* s_T = s_A + C * CP;
   float* s_P = s_T + C * CP;
   // inversion temporaries and (later) per-wave staging tiles share one buffer
@@ -137,9 +156,10 @@ prep_kernel(PrepParams p) {
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = n * p.chunk;
-  const int dk = p.dk;
+  const int dk = p.dk, dv = p.dv;
   const Raw* qg = (const Raw*)p.q;
   const Raw* kg = (const Raw*)p.k;
+  const Raw* vg = (const Raw*)p.v;
   uint16_t* wsb = p.ws + ((size_t)(b * p.H + h) * p.NC + n) * L::kElems;
   auto grow = [&](int t) -> size_t { return ((size_t)b * p.T + t) * p.H + h; };
   auto tsafe = [&](int r) -> int { const int t = t0 + r; return t < p.T ? t : p.T - 1; };
@@ -161,7 +181,15 @@ prep_kernel(PrepParams p) {
     const int r = idx / (K / 8), c0 = (idx % (K / 8)) * 8;
     E::ld8(kg, grow(tsafe(r)) * dk + (c0 < dk ? c0 : 0), k_r[it]);
   }
-  const int I = wave;                                   // this wave's row tile in the A/P and W phases
+  float v_r[NVI][8][4];                                 // V rows 8 rb .. +7, columns 4 cb .. +3
+#pragma unroll
+  for (int it = 0; it < NVI; ++it) {
+    const int idx = (tid + kPrepThreads * it) % NVB;
+    const int rb = idx / (V / 4), cb = idx % (V / 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) E::ld4(vg, grow(tsafe(8 * rb + e)) * dv + 4 * cb, v_r[it][e]);
+  }
+  const int I = wave;                                   // this wave's row tile in the MFMA phases
   const int rq = 16 * (I < RT ? I : 0) + (lane % 16);
   float qtf[KS][8];                                     // raw q now, Qt = q * scale * Gam later
 #pragma unroll
@@ -250,8 +278,8 @@ prep_kernel(PrepParams p) {
         *reinterpret_cast<bf16x8*>(&s_kt[0][r * KB + c0]) = hi;
         *reinterpret_cast<bf16x8*>(&s_kt[1][r * KB + c0]) = lo;
         split8(ki, hi, lo);
-        *reinterpret_cast<bf16x8*>(&s_ki[0][r * KB + c0]) = hi;
-        *reinterpret_cast<bf16x8*>(&s_ki[1][r * KB + c0]) = lo;
+        *reinterpret_cast<bf16x8*>(&s_ki[r * KB + c0]) = hi;
+        *reinterpret_cast<bf16x8*>(&s_ki[C * KB + r * KB + c0]) = lo;
         split8(kh, hi, lo);
         *reinterpret_cast<bf16x8*>(&kh_stage[r * KB + c0]) = hi;
         if (SPLIT) *reinterpret_cast<bf16x8*>(&kh_stage_lo[r * KB + c0]) = lo;
@@ -315,8 +343,8 @@ prep_kernel(PrepParams p) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const int c = 32 * ks + 8 * (lane / 16);
-            const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[0][j * KB + c]);
-            const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[1][j * KB + c]);
+            const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[j * KB + c]);
+            const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * KB + j * KB + c]);
             a[0] = mfma16(kth[ks], kih, a[0]);
             a[1] = mfma16(kth[ks], kil, a[1]);
             a[2] = mfma16(ktl[ks], kih, a[2]);
@@ -358,6 +386,29 @@ prep_kernel(PrepParams p) {
     }
   }
   __syncthreads();
+
+  // ---- V^T (hi, and lo for fp32 inputs) into the region Ki no longer needs; masked rows as 0
+#pragma unroll
+  for (int it = 0; it < NVI; ++it) {
+    const int idx = tid + kPrepThreads * it;
+    if (idx < NVB) {
+      const int rb = idx / (V / 4), cb = idx % (V / 4);
+      bool ok[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ok[e] = s_valid[8 * rb + e] != 0;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = ok[e] ? v_r[it][e][cc] : 0.f;
+        bf16x8 hi, lo;
+        split8(x, hi, lo);
+        const int at = swz<C>(4 * cb + cc, 8 * rb);
+        *reinterpret_cast<bf16x8*>(&s_vT[at]) = hi;
+        if (SPLIT) *reinterpret_cast<bf16x8*>(&s_vT[V * C + at]) = lo;
+      }
+    }
+  }
 
   // ---- T = (I + A)^-1, blocked: diagonal 16x16 blocks by forward substitution
   if (tid < RT * 16) {
@@ -403,28 +454,9 @@ prep_kernel(PrepParams p) {
     __syncthreads();
   }
 
-  // ---- T' = T Diag(beta) and P to the workspace (hi, lo), A-operand order
-  for (int idx = tid; idx < RT * CS * 64; idx += kPrepThreads) {
-    const int ln = idx % 64, ks = (idx / 64) % CS, rt = idx / (64 * CS);
-    const int r = 16 * rt + (ln % 16), j0 = 32 * ks + 8 * (ln / 16);
-    float tv[8], pv[8];
-    ld8f(&s_T[r * CP + j0], tv);
-    ld8f(&s_P[r * CP + j0], pv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tv[e] *= s_beta[j0 + e];
-    bf16x8 hi, lo;
-    split8(tv, hi, lo);
-    store_frag(wsb + L::off_tp + frag_off(rt, ks, ln, C), hi);
-    store_frag(wsb + L::off_tp + L::kCC + frag_off(rt, ks, ln, C), lo);
-    split8(pv, hi, lo);
-    store_frag(wsb + L::off_p + frag_off(rt, ks, ln, C), hi);
-    store_frag(wsb + L::off_p + L::kCC + frag_off(rt, ks, ln, C), lo);
-  }
-
-  // ---- M = P T' (lower triangular), into s_A; T' and -M A-fragments kept for the W phase
-  bf16x8 tnh[CS], tnl[CS], mnh[CS], mnl[CS];
+  // ---- M = P T' (lower triangular), into s_A; -T', -M and P A-fragments kept in registers
+  bf16x8 tnh[CS], tnl[CS], mnh[CS], mnl[CS], ph[CS], pl[CS];
   if (I < RT) {
-    bf16x8 ph[CS], pl[CS];
 #pragma unroll
     for (int ks = 0; ks < CS; ++ks) {
       float pv[8];
@@ -521,45 +553,119 @@ prep_kernel(PrepParams p) {
       }
     }
   }
+
+  // ---- Ut = T' V for this wave's rows, every dv tile: to the workspace, and (hi, lo)
+  //      transposed into the region G no longer needs
+  if (I < RT) {
+#pragma unroll
+    for (int N = 0; N < V / 16; ++N) {
+      const int vn = 16 * N + (lane % 16);
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < CS; ++ks) {
+        if (32 * ks > 16 * I + 15) continue;
+        const int j0 = 32 * ks + 8 * (lane / 16);
+        const bf16x8 vh = *reinterpret_cast<const bf16x8*>(&s_vT[swz<C>(vn, j0)]);
+        a0 = mfma16(tnh[ks], vh, a0);
+        a1 = mfma16(tnl[ks], vh, a1);
+        if (SPLIT) a1 = mfma16(tnh[ks], *reinterpret_cast<const bf16x8*>(&s_vT[V * C + swz<C>(vn, j0)]), a1);
+      }
+      f32x4 ut;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ut[i] = -(a0[i] + a1[i]);
+      *reinterpret_cast<f32x4*>(wsb + L::off_ut + acc_off<V>(I, N, lane)) = ut;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jr = 16 * I + 4 * (lane / 16) + i;
+        const __bf16 hi = (__bf16)ut[i];
+        s_utT[swz<C>(vn, jr)] = hi;
+        s_utT[V * C + swz<C>(vn, jr)] = (__bf16)(ut[i] - (float)hi);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- O0 = P Ut for this wave's rows, every dv tile
+  if (I < RT) {
+#pragma unroll
+    for (int N = 0; N < V / 16; ++N) {
+      const int vn = 16 * N + (lane % 16);
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < CS; ++ks) {
+        if (32 * ks > 16 * I + 15) continue;          // P is lower triangular
+        const int j0 = 32 * ks + 8 * (lane / 16);
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_utT[swz<C>(vn, j0)]);
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_utT[V * C + swz<C>(vn, j0)]);
+        a0 = mfma16(ph[ks], uh, a0);
+        a1 = mfma16(ph[ks], ul, a1);
+        a1 = mfma16(pl[ks], uh, a1);
+      }
+      f32x4 o0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o0[i] = a0[i] + a1[i];
+      *reinterpret_cast<f32x4*>(wsb + L::off_o0 + acc_off<V>(I, N, lane)) = o0;
+    }
+  }
 }
 
 // ================================================================ scan kernel
-// Operands of one chunk that a thread needs, loaded from the workspace one chunk
-// ahead so that the serial chain of chunks never waits on HBM.
-template <int K, int C, bool SPLIT>
-struct ScanOps {
-  static constexpr int CS = C / 32, KS = K / 32;
-  static constexpr int SPW = (K / 16 + 3) / 4;
-  static constexpr int VPT = C * 16 / 256;           // V-tile elements per thread
-  bf16x8 tph[CS], tpl[CS], ph[CS], pl[CS];
-  bf16x8 wn[KS], qh[KS];
-  bf16x8 wnl[SPLIT ? KS : 1], qhl[SPLIT ? KS : 1];
-  bf16x8 kh[SPW][CS];
-  bf16x8 khl[SPLIT ? SPW : 1][CS];
-  float gam[SPW][4];
-  uint32_t vraw[VPT];                                // V elements as stored (bf16 bits or fp32 bits)
-  uint8_t mraw[VPT];                                 // mask bytes of their rows
+// The operands of one chunk for one dv tile (Wn, Qh, Kh^T, the tile's Ut and O0
+// blocks, Gam_last) are whole 1 KB blocks of the workspace.  The four waves copy
+// them straight into an LDS ring slot with global_load_lds_dwordx4 (lane l writes
+// bytes 16 l .. 16 l + 15 of the block), every wave the same number of copies.
+template <int K, int V, int C, bool SPLIT>
+struct ScanRing {
+  static constexpr int RT = C / 16, KS = K / 32, CS = C / 32, SRT = K / 16;
+  static constexpr int kParts = SPLIT ? 2 : 1;
+  static constexpr int b_wn = 0;
+  static constexpr int b_qh = b_wn + RT * KS * kParts;
+  static constexpr int b_kh = b_qh + RT * KS * kParts;
+  static constexpr int b_ut = b_kh + SRT * CS * kParts;
+  static constexpr int b_o0 = b_ut + RT;
+  static constexpr int b_gam = b_o0 + RT;
+  static constexpr int kBlocks = b_gam + 1;                   // Gam_last (<= 512 B) takes one block
+  static constexpr int kPerWave = (kBlocks + 3) / 4;          // copies per wave per chunk
+  static constexpr int kSlotBytes = 4 * kPerWave * 1024;
+  static constexpr int kDepth = (2 * kSlotBytes <= 128 * 1024) ? 2 : 1;
+  static_assert(4 * K <= 1024, "Gam_last fits one block");
 };
 
-template <int DT, int K, int C>
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_barrier with compiler-only fences around it: no memory access moves across,
+// and (unlike __syncthreads) no wait for outstanding global->LDS copies is added
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// s_waitcnt with lgkmcnt(0) and vmcnt(n); memory accesses stay on their side of it
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 0xf) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+template <int DT, int K, int V, int C>
 __global__ void __launch_bounds__(kScanThreads)
 scan_kernel(ScanParams p) {
   using E = Elem<DT>;
   constexpr bool SPLIT = (DT == 1);
-  using L = WsLayout<K, C, SPLIT>;
-  using Ops = ScanOps<K, C, SPLIT>;
-  constexpr int RT = C / 16;
-  constexpr int CS = C / 32;
-  constexpr int KS = K / 32;
-  constexpr int SRT = K / 16;                       // state row tiles
-  constexpr int SPW = Ops::SPW;                     // state row tiles per wave
+  using L = WsLayout<K, V, C, SPLIT>;
+  using R = ScanRing<K, V, C, SPLIT>;
+  constexpr int RT = C / 16, CS = C / 32, KS = K / 32, SRT = K / 16;
+  constexpr int SPW = (SRT + 3) / 4;                // state row tiles per wave
   constexpr int KB = K + 8, CB = C + 8;
+  constexpr int kStores = 4;                        // global stores per lane and chunk, always
   static_assert(RT <= 4, "one U/O row tile per wave");
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state, B-operand rows = dv column
-  __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U
-  __shared__ __attribute__((aligned(16))) __bf16 s_Ut[2][kVT * CB];   // T'V
-  __shared__ __attribute__((aligned(16))) __bf16 s_V[2][kVT * CB];    // V tile, transposed
+  __shared__ __attribute__((aligned(1024))) unsigned char ring0[R::kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring1[R::kDepth == 2 ? R::kSlotBytes : 1024];
+  __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state hi, lo; B-operand rows = dv column
+  __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U hi, lo
 
   // XCD-aware mapping: all dv tiles of one head share blockIdx.x % 8 (one L2)
   const int L_id = blockIdx.x;
@@ -570,63 +676,43 @@ scan_kernel(ScanParams p) {
   const int v0 = tile * kVT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int I = wave;                                // this wave's U/O row tile
-  // predicates the tiling makes always true are compile-time constants, so the
-  // prefetch below is straight-line code and its waits stay exact
+  // predicates that the tiling makes always true are compile-time constants
   const bool has_rows = (RT >= 4) || (I < RT);
   auto srow = [&](int M) { return (SRT % 4 == 0) || (M < SRT); };
   const int dk = p.dk, dv = p.dv;
-  const typename E::T* vg = (const typename E::T*)p.v;
   typename E::T* og = (typename E::T*)p.o;
+  typename E::T* sink = (typename E::T*)p.sink + (L_id & 63) * 64;
   const uint16_t* wsh = p.ws + (size_t)bh * p.NC * L::kElems;
-  // any readable bytes stand in for the mask when there is none (the value is ignored)
-  const uint8_t* mp = p.mask != nullptr ? p.mask : reinterpret_cast<const uint8_t*>(p.v);
+  const int last = p.NC - 1;
 
-  auto load_ops = [&](int n, Ops& op) {
-    const uint16_t* wsb = wsh + (size_t)n * L::kElems;
-    if (has_rows) {
+  // workspace offset (2-byte units from the chunk base) of ring block bi, for this tile
+  auto block_src = [&](int bi) -> size_t {
+    if (bi < R::b_qh) return L::off_wn + (size_t)(bi - R::b_wn) * 512;
+    if (bi < R::b_kh) return L::off_qh + (size_t)(bi - R::b_qh) * 512;
+    if (bi < R::b_ut) return L::off_kh + (size_t)(bi - R::b_kh) * 512;
+    if (bi < R::b_o0) return L::off_ut + acc_off<V>(bi - R::b_ut, tile, 0);
+    if (bi < R::b_gam) return L::off_o0 + acc_off<V>(bi - R::b_o0, tile, 0);
+    return L::off_gam;
+  };
+  // chunk n into a ring slot: block wave + 4 j goes to slot block wave + 4 j; copies past
+  // the last block repeat it into the slot's spare blocks, so every wave issues kPerWave
+  auto copy_chunk = [&](int n, unsigned char* dst) {
+    const uint16_t* cb = wsh + (size_t)n * L::kElems;
 #pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        op.tph[ks] = load_frag(wsb + L::off_tp + frag_off(I, ks, lane, C));
-        op.tpl[ks] = load_frag(wsb + L::off_tp + L::kCC + frag_off(I, ks, lane, C));
-        op.ph[ks] = load_frag(wsb + L::off_p + frag_off(I, ks, lane, C));
-        op.pl[ks] = load_frag(wsb + L::off_p + L::kCC + frag_off(I, ks, lane, C));
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        op.wn[ks] = load_frag(wsb + L::off_wn + frag_off(I, ks, lane, K));
-        op.qh[ks] = load_frag(wsb + L::off_qh + frag_off(I, ks, lane, K));
-        if (SPLIT) {
-          op.wnl[ks] = load_frag(wsb + L::off_wn + L::kCK + frag_off(I, ks, lane, K));
-          op.qhl[ks] = load_frag(wsb + L::off_qh + L::kCK + frag_off(I, ks, lane, K));
-        }
-      }
+    for (int j = 0; j < R::kPerWave; ++j) {
+      const int pos = wave + 4 * j;
+      const int bi = pos < R::kBlocks ? pos : R::kBlocks - 1;
+      // the Gam_last block holds K floats: lanes past them re-read its start
+      const int ln = (bi == R::b_gam && lane >= K / 4) ? 0 : lane;
+      __builtin_amdgcn_global_load_lds((const void*)(cb + block_src(bi) + (size_t)ln * 8),
+                                       (lds_void_t*)(dst + pos * 1024), 16, 0, 0);
     }
-    const float* gam = reinterpret_cast<const float*>(wsb + L::off_gam);
-#pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-      const int M = wave + 4 * m;
-      if (srow(M)) {
-#pragma unroll
-        for (int ks = 0; ks < CS; ++ks) {
-          op.kh[m][ks] = load_frag(wsb + L::off_kh + frag_off(M, ks, lane, C));
-          if (SPLIT) op.khl[m][ks] = load_frag(wsb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
-        }
-        const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * M + 4 * (lane / 16));
-        op.gam[m][0] = g4.x; op.gam[m][1] = g4.y; op.gam[m][2] = g4.z; op.gam[m][3] = g4.w;
-      }
-    }
-    // unconditional loads from in-bounds rows; validity is applied when the chunk is used
-    const int t0 = n * p.chunk;
-#pragma unroll
-    for (int i = 0; i < Ops::VPT; ++i) {
-      const int idx = tid + kScanThreads * i;
-      const int r = idx / kVT, cidx = idx % kVT, t = t0 + r;
-      const int ts = t < p.T ? t : p.T - 1;
-      const size_t off = (((size_t)b * p.T + ts) * p.H + h) * dv + v0 + cidx;
-      if (DT == 0) op.vraw[i] = reinterpret_cast<const uint16_t*>(vg)[off];
-      else op.vraw[i] = __float_as_uint(reinterpret_cast<const float*>(vg)[off]);
-      op.mraw[i] = mp[(size_t)b * p.T + ts];
-    }
+  };
+  auto frag = [&](const unsigned char* sl, int bi) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(sl + bi * 1024 + lane * 16);
+  };
+  auto acc_blk = [&](const unsigned char* sl, int bi) -> f32x4 {
+    return *reinterpret_cast<const f32x4*>(sl + bi * 1024 + lane * 16);
   };
 
   // state tiles in registers: wave w owns state row tiles w, w+4, ...
@@ -657,66 +743,37 @@ scan_kernel(ScanParams p) {
     }
   };
 
-  auto process = [&](const Ops& op, Ops& next, int n, int n_next) {
+  // one chunk, operands in ring slot `sl`; ends with exactly kStores global stores per lane
+  auto process = [&](const unsigned char* sl, int n) {
     const int t0 = n * p.chunk;
-    // ---- V tile -> LDS (transposed, hi/lo)
-#pragma unroll
-    for (int i = 0; i < Ops::VPT; ++i) {
-      const int idx = tid + kScanThreads * i;
-      const int r = idx / kVT, cidx = idx % kVT, t = t0 + r;
-      const bool ok = r < p.chunk && t < p.T && (p.mask == nullptr || op.mraw[i] != 0);
-      const float x = ok ? (DT == 0 ? __uint_as_float(op.vraw[i] << 16) : __uint_as_float(op.vraw[i])) : 0.f;
-      const __bf16 hi = (__bf16)x;
-      s_V[0][cidx * CB + r] = hi;
-      s_V[1][cidx * CB + r] = (__bf16)(x - (float)hi);
-    }
-    load_ops(n_next, next);                                            // prefetch the next chunk
-    __syncthreads();                                                   // (a) V and S visible
-
-    bf16x8 sh[KS], sl[KS];
+    bf16x8 sh[KS], slo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int k0 = 32 * ks + 8 * (lane / 16);
       sh[ks] = *reinterpret_cast<const bf16x8*>(&s_S[0][(lane % 16) * KB + k0]);
-      sl[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(lane % 16) * KB + k0]);
+      slo[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(lane % 16) * KB + k0]);
     }
-    // ---- Ut = T' V and U = Ut + Wn S for this wave's 16 rows (independent accumulators
-    //      keep the MFMA dependency chains short)
+    // ---- U = Ut + Wn S for this wave's 16 rows (independent accumulators keep the chains short)
     if (has_rows) {
-      f32x4 ut0 = zero4(), ut1 = zero4();
-#pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        if (32 * ks > 16 * I + 15) continue;
-        const int j0 = 32 * ks + 8 * (lane / 16);
-        const bf16x8 vh = *reinterpret_cast<const bf16x8*>(&s_V[0][(lane % 16) * CB + j0]);
-        ut0 = mfma16(op.tph[ks], vh, ut0);
-        ut1 = mfma16(op.tpl[ks], vh, ut1);
-        if (SPLIT) {
-          const bf16x8 vl = *reinterpret_cast<const bf16x8*>(&s_V[1][(lane % 16) * CB + j0]);
-          ut1 = mfma16(op.tph[ks], vl, ut1);
-        }
-      }
-      f32x4 u[4] = {zero4(), zero4(), zero4(), zero4()};
+      f32x4 u[4] = {acc_blk(sl, R::b_ut + I), zero4(), zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        u[(ks & 1) * 2] = mfma16(op.wn[ks], sh[ks], u[(ks & 1) * 2]);
-        u[(ks & 1) * 2 + 1] = mfma16(op.wn[ks], sl[ks], u[(ks & 1) * 2 + 1]);
-        if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(op.wnl[ks], sh[ks], u[(ks & 1) * 2 + 1]);
+        const bf16x8 wn = frag(sl, R::b_wn + I * KS + ks);
+        u[(ks & 1) * 2] = mfma16(wn, sh[ks], u[(ks & 1) * 2]);
+        u[(ks & 1) * 2 + 1] = mfma16(wn, slo[ks], u[(ks & 1) * 2 + 1]);
+        if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(frag(sl, R::b_wn + RT * KS + I * KS + ks), sh[ks], u[(ks & 1) * 2 + 1]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * I + 4 * (lane / 16) + i;
-        const float utv = ut0[i] + ut1[i];
-        const float uv = utv + ((u[0][i] + u[2][i]) + (u[1][i] + u[3][i]));
-        __bf16 hi = (__bf16)utv;
-        s_Ut[0][(lane % 16) * CB + rr] = hi;
-        s_Ut[1][(lane % 16) * CB + rr] = (__bf16)(utv - (float)hi);
-        hi = (__bf16)uv;
+        const float uv = (u[0][i] + u[2][i]) + (u[1][i] + u[3][i]);
+        const __bf16 hi = (__bf16)uv;
         s_U[0][(lane % 16) * CB + rr] = hi;
         s_U[1][(lane % 16) * CB + rr] = (__bf16)(uv - (float)hi);
       }
     }
-    __syncthreads();                                                   // (b) Ut, U visible; S reads done
+    wait_vm_lgkm<63>();
+    wg_barrier();                                                      // U visible; S reads done
 
     // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
     {
@@ -727,6 +784,7 @@ scan_kernel(ScanParams p) {
         uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
         ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
       }
+      const float* gam = reinterpret_cast<const float*>(sl + R::b_gam * 1024);
 #pragma unroll
       for (int m = 0; m < SPW; ++m) {
         const int M = wave + 4 * m;
@@ -734,54 +792,78 @@ scan_kernel(ScanParams p) {
         f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
         for (int ks = 0; ks < CS; ++ks) {
-          a0 = mfma16(op.kh[m][ks], uh[ks], a0);
-          a1 = mfma16(op.kh[m][ks], ul[ks], a1);
-          if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
+          const bf16x8 kh = frag(sl, R::b_kh + M * CS + ks);
+          a0 = mfma16(kh, uh[ks], a0);
+          a1 = mfma16(kh, ul[ks], a1);
+          if (SPLIT) a1 = mfma16(frag(sl, R::b_kh + SRT * CS + M * CS + ks), uh[ks], a1);
         }
+        const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * M + 4 * (lane / 16));
+        const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[m][i] = op.gam[m][i] * S[m][i] + (a0[i] + a1[i]);
-      }
-    }
-
-    // ---- O = Qh S + P Ut (reads the previous state from registers)
-    if (has_rows) {
-      f32x4 o4[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        o4[ks & 1] = mfma16(op.qh[ks], sh[ks], o4[ks & 1]);
-        o4[ks & 1] = mfma16(op.qh[ks], sl[ks], o4[ks & 1]);
-        if (SPLIT) o4[ks & 1] = mfma16(op.qhl[ks], sh[ks], o4[ks & 1]);
-      }
-#pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        if (32 * ks > 16 * I + 15) continue;
-        const int j0 = 32 * ks + 8 * (lane / 16);
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_Ut[0][(lane % 16) * CB + j0]);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_Ut[1][(lane % 16) * CB + j0]);
-        o4[2] = mfma16(op.ph[ks], uh, o4[2]);
-        o4[3] = mfma16(op.ph[ks], ul, o4[3]);
-        o4[3] = mfma16(op.pl[ks], uh, o4[3]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * I + 4 * (lane / 16) + i, t = t0 + rr;
-        const float ov = (o4[0][i] + o4[1][i]) + (o4[2][i] + o4[3][i]);
-        if (rr < p.chunk && t < p.T) E::st(og, (((size_t)b * p.T + t) * p.H + h) * dv + v0 + (lane % 16), ov);
+        for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
       }
     }
     publish_state();
+
+    // ---- O = O0 + Qh S (the state entering the chunk, from the bf16 fragments)
+    if (has_rows) {
+      f32x4 o4[2] = {acc_blk(sl, R::b_o0 + I), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qh = frag(sl, R::b_qh + I * KS + ks);
+        o4[ks & 1] = mfma16(qh, sh[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(qh, slo[ks], o4[ks & 1]);
+        if (SPLIT) o4[ks & 1] = mfma16(frag(sl, R::b_qh + RT * KS + I * KS + ks), sh[ks], o4[ks & 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < kStores; ++i) {
+        const int rr = 16 * I + 4 * (lane / 16) + i, t = t0 + rr;
+        const bool ok = rr < p.chunk && t < p.T;
+        typename E::T* dst = ok ? og + (((size_t)b * p.T + t) * p.H + h) * dv + v0 + (lane % 16)
+                                : sink + 16 * i + (lane % 16);
+        E::st(dst, 0, o4[0][i] + o4[1][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kStores; ++i) {                             // keep the store count uniform
+        volatile typename E::T* dst = sink + 16 * i + (lane % 16);
+        *dst = (typename E::T)0;
+      }
+    }
   };
 
   publish_state();
-  // chunk n is processed from registers loaded one chunk earlier; the load for the
-  // chunk after the last one re-reads the last chunk (in bounds, unused)
-  const int last = p.NC - 1;
-  Ops opA, opB;
-  if (p.NC > 0) load_ops(0, opA);
-  for (int n = 0; n < p.NC; n += 2) {
-    process(opA, opB, n, n + 1 <= last ? n + 1 : last);
-    if (n + 1 < p.NC) process(opB, opA, n + 1, n + 2 <= last ? n + 2 : last);
+  if (p.NC > 0) copy_chunk(0, ring0);
+  wait_vm_lgkm<0>();                                                   // chunk 0, S0 landed
+  if constexpr (R::kDepth == 2) {
+    // Per wave, the copies into one slot are followed by exactly kStores stores before the
+    // wait for that slot, and vector memory operations complete in order, so vmcnt(kStores)
+    // means this wave's copies have landed; the barrier then publishes everyone's.
+    for (int n = 0; n < p.NC; n += 2) {
+      if (n > 0) wait_vm_lgkm<kStores>();
+      wg_barrier();
+      copy_chunk(n + 1 <= last ? n + 1 : last, ring1);
+      process(ring0, n);
+      if (n + 1 < p.NC) {
+        wait_vm_lgkm<kStores>();
+        wg_barrier();
+        copy_chunk(n + 2 <= last ? n + 2 : last, ring0);
+        process(ring1, n + 1);
+      }
+    }
+  } else {
+    for (int n = 0; n < p.NC; ++n) {
+      if (n > 0) {
+        wait_vm_lgkm<63>();
+        wg_barrier();                                                  // every wave is done with the slot
+        copy_chunk(n, ring0);
+        wait_vm_lgkm<0>();
+      }
+      wg_barrier();
+      process(ring0, n);
+    }
   }
+  wait_vm_lgkm<0>();
 
   // ---- final state
 #pragma unroll
@@ -805,50 +887,58 @@ bool prefill_supported(int dk, int dv, int chunk) {
   return chunk == 16 || chunk == 32 || chunk == 64;
 }
 
-template <int K, int C>
-static size_t ws_elems(int dtype) {
-  return dtype == 1 ? WsLayout<K, C, true>::kElems : WsLayout<K, C, false>::kElems;
-}
+// (padded dk, dv, tile chunk) instantiated
+#define KDA_FOR_SHAPES(X)                                                  \
+  X(32, 16, 32) X(32, 32, 32) X(32, 64, 32) X(32, 128, 32)                 \
+  X(64, 16, 32) X(64, 32, 32) X(64, 64, 32) X(64, 128, 32)                 \
+  X(128, 16, 32) X(128, 32, 32) X(128, 64, 32) X(128, 128, 32)             \
+  X(32, 16, 64) X(32, 32, 64) X(32, 64, 64) X(32, 128, 64)                 \
+  X(64, 16, 64) X(64, 32, 64) X(64, 64, 64) X(64, 128, 64)                 \
+  X(128, 16, 64) X(128, 32, 64) X(128, 64, 64) X(128, 128, 64)
 
-static size_t chunk_ws_elems(int K, int C, int dtype) {
-#define KDA_WS(KK, CC) if (K == KK && C == CC) return ws_elems<KK, CC>(dtype);
-  KDA_WS(32, 32) KDA_WS(32, 64) KDA_WS(64, 32) KDA_WS(64, 64) KDA_WS(128, 32) KDA_WS(128, 64)
+static size_t chunk_ws_elems(int K, int V, int C, int dtype) {
+#define KDA_WS(KK, VV, CC)                                                             \
+  if (K == KK && V == VV && C == CC)                                                   \
+    return dtype == 1 ? WsLayout<KK, VV, CC, true>::kElems : WsLayout<KK, VV, CC, false>::kElems;
+  KDA_FOR_SHAPES(KDA_WS)
 #undef KDA_WS
   return 0;
 }
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
-  (void)dv;
   if (T == 0 || B == 0 || H == 0) return 0;
   const int NC = (T + chunk - 1) / chunk;
-  return (size_t)B * H * NC * chunk_ws_elems(pad_k(dk), tile_chunk(chunk), dtype) * 2;
+  return (size_t)B * H * NC * chunk_ws_elems(pad_k(dk), dv, tile_chunk(chunk), dtype) * 2 + kSinkBytes;
 }
 
-template <int DT, int K, int C>
+template <int DT, int K, int V, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   const int NC = (a.T + a.chunk - 1) / a.chunk;
   const int NT = a.dv / kVT;
   const int nbh = a.B * a.H;
+  const size_t chunks_bytes = (size_t)nbh * NC * WsLayout<K, V, C, DT == 1>::kElems * 2;
   if (NC > 0) {
-    PrepParams pp{a.q, a.k, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace,
-                  a.B, a.T, a.H, a.dk, a.chunk, NC, a.l2norm};
-    hipLaunchKernelGGL((prep_kernel<DT, K, C>), dim3(NC, a.H, a.B), dim3(kPrepThreads), 0, st, pp);
+    PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace,
+                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm};
+    hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC, a.H, a.B), dim3(kPrepThreads), 0, st, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  ScanParams sp{a.v, a.mask, a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
+  ScanParams sp{a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
+                NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr,
                 a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
   const int groups = (nbh + 7) / 8;
-  hipLaunchKernelGGL((scan_kernel<DT, K, C>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);
+  hipLaunchKernelGGL((scan_kernel<DT, K, V, C>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);
   return hipGetLastError();
 }
 
 template <int DT>
 static hipError_t launch_prefill_dt(const PrefillArgs& a) {
-  const int K = pad_k(a.dk), C = tile_chunk(a.chunk);
-#define KDA_PF(KK, CC) if (K == KK && C == CC) return launch_prefill_t<DT, KK, CC>(a);
-  KDA_PF(32, 32) KDA_PF(32, 64) KDA_PF(64, 32) KDA_PF(64, 64) KDA_PF(128, 32) KDA_PF(128, 64)
+  const int K = pad_k(a.dk), V = a.dv, C = tile_chunk(a.chunk);
+#define KDA_PF(KK, VV, CC) \
+  if (K == KK && V == VV && C == CC) return launch_prefill_t<DT, KK, VV, CC>(a);
+  KDA_FOR_SHAPES(KDA_PF)
 #undef KDA_PF
   return hipErrorInvalidValue;
 }

@@ -88,6 +88,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, sT=None) == INVALID
     assert _prefill(lib, s0=ctypes.c_void_p(0x10002)) == INVALID
     assert _prefill(lib, la=MISALIGNED) == INVALID
+    assert _prefill(lib, v=MISALIGNED) == INVALID
+    assert _prefill(lib, o=ctypes.c_void_p(0x10001)) == INVALID
     assert _prefill(lib, wsb=16) == WORKSPACE
     assert _prefill(lib, ws=None) == WORKSPACE
     assert _prefill(lib, B=0, ws=None, wsb=0) == OK
@@ -99,9 +101,10 @@ def test_workspace_size_query(lib):
     assert f(1, 64, 32, 128, 128, 48, 0) == 0            # unsupported chunk
     assert f(1, 64, 32, 100, 128, 64, 0) == 0            # unsupported head size
     one = f(1, 64, 1, 128, 128, 64, 0)
-    assert one > 0 and one % 16 == 0
-    assert f(1, 65, 1, 128, 128, 64, 0) == 2 * one       # ragged tail takes a whole chunk
-    assert f(4, 4096, 32, 128, 128, 64, 0) == 4 * 32 * 64 * one
+    per_chunk = f(1, 128, 1, 128, 128, 64, 0) - one       # a fixed tail plus a size per chunk
+    assert one > 0 and one % 16 == 0 and per_chunk > 0 and per_chunk % 16 == 0
+    assert f(1, 65, 1, 128, 128, 64, 0) == one + per_chunk   # ragged tail takes a whole chunk
+    assert f(4, 4096, 32, 128, 128, 64, 0) == one + (4 * 32 * 64 - 1) * per_chunk
     assert f(1, 64, 1, 128, 128, 64, 1) > one            # fp32 inputs keep residual parts
 
 
