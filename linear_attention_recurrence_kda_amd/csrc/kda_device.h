@@ -85,6 +85,33 @@ template <> struct Elem<1> {
   }
 };
 
+// 8 consecutive elements kept as loaded (packed bf16 or fp32) until converted,
+// so a load issued early holds as few registers as possible
+template <int DT> struct Raw8;
+template <> struct Raw8<0> {
+  uint4 u;
+  __device__ __forceinline__ void load(const uint16_t* p, size_t i) { u = *reinterpret_cast<const uint4*>(p + i); }
+  __device__ __forceinline__ void to_float(float* out) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[2 * j] = __uint_as_float(w[j] << 16);
+      out[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<1> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p, size_t i) {
+    a = *reinterpret_cast<const float4*>(p + i);
+    b = *reinterpret_cast<const float4*>(p + i + 4);
+  }
+  __device__ __forceinline__ void to_float(float* out) const {
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+};
+
 // ---------------------------------------------------------------- MFMA
 // v_mfma_f32_16x16x32_bf16, D = A(16x32) * B(32x16) + C, one wavefront of 64 lanes.
 // Lane l holds  A[row = l%16][k = 8*(l/16) .. +7],  B[k = 8*(l/16) .. +7][col = l%16],

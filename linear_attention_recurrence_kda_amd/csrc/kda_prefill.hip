@@ -108,50 +108,74 @@ __device__ __forceinline__ int swz(int n, int j) {
 }
 
 // ================================================================ prep kernel
-// One workgroup per (chunk, head, batch row).  Every global load of the chunk is
-// issued first, unconditionally, from in-bounds rows; row validity (mask, ragged
-// tail) is applied afterwards by select, so no load waits on another.
+// LDS of one prep workgroup: three regions, each reused by a later phase once the
+// barrier after its last read has passed (bf16 rows padded to K + 8, fp32 C x C rows
+// to C + 4, so 16 consecutive rows fall into different banks).
 template <int DT, int K, int V, int C>
-__global__ void __launch_bounds__(kPrepThreads)
+struct PrepLds {
+  static constexpr bool SPLIT = DT == 1;
+  static constexpr int KP = K + 4, KB = K + 8, CP = C + 4, RT = C / 16;
+  static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+  static constexpr int kParts = SPLIT ? 2 : 1;
+  // R1: Ki hi, lo (fast path) or G (slow path); then T and V^T
+  static constexpr int kTBytes = C * CP * 4;
+  static constexpr int r1 = cmax(cmax(2 * C * KB * 2, C * KP * 4), kTBytes + kParts * V * C * 2);
+  // R2: Kt; then Ut^T hi (and lo when it fits)
+  static constexpr int kUtPart = V * C * 2;
+  static constexpr int kKtBytes = kParts * C * KB * 2;
+  static constexpr bool kUtLoInR2 = kKtBytes >= 2 * kUtPart;
+  static constexpr int r2 = cmax(kKtBytes, kUtLoInR2 ? 2 * kUtPart : kUtPart);
+  // R3: Kh rows until transposed; then A (later M = P T'); then Ut^T lo
+  static constexpr int r3 = cmax(cmax(kParts * C * KB * 2, C * CP * 4), kUtLoInR2 ? 0 : kUtPart);
+  // per-wave 16 x 17 staging tiles, or the inversion's temporaries
+  static constexpr int kScratch = cmax(4 * 16 * 17, (RT > 1 ? RT - 1 : 1) * 16 * 17);
+};
+
+// x shifted down by n lanes inside each row of 16 lanes (lanes below n read 0)
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
+}
+
+// One workgroup per (chunk, head, batch row); wave I owns rows 16 I .. 16 I + 15 of
+// the chunk.  Lane l of wave I holds row 16 I + l%16 and channels 32 ks + 8 (l/16) .. +7
+// for every k step ks: the A-operand layout of the MFMA, so Kt and Qt never leave
+// registers on their way into A and P.  All global loads are issued up front,
+// unconditionally, from in-bounds rows; validity (mask, ragged tail) is applied by
+// select afterwards.
+template <int DT, int K, int V, int C>
+__global__ void __launch_bounds__(kPrepThreads, DT == 0 ? 2 : 1)
 prep_kernel(PrepParams p) {
   using E = Elem<DT>;
   using Raw = typename E::T;
+  using Lds = PrepLds<DT, K, V, C>;
   constexpr bool SPLIT = (DT == 1);
   using L = WsLayout<K, V, C, SPLIT>;
   constexpr int RT = C / 16;          // row tiles of the chunk
   constexpr int CS = C / 32;          // k steps over chunk rows
   constexpr int KS = K / 32;          // k steps over key channels
-  constexpr int KP = K + 4;           // fp32 row stride
-  constexpr int KB = K + 8;           // bf16 row stride (16-byte aligned rows)
-  constexpr int CP = C + 4;           // fp32 row stride of the C x C matrices (16 rows -> 16 bank groups)
-  constexpr int NLA = C * (K / 4) / kPrepThreads;                        // float4 of log_alpha per thread
-  constexpr int NKI = (C * (K / 8) + kPrepThreads - 1) / kPrepThreads;   // (row, 8 channels) items per thread
+  constexpr int KP = Lds::KP, KB = Lds::KB, CP = Lds::CP;
   constexpr int NVB = (C / 8) * (V / 4);                                 // (8 rows, 4 columns) blocks of V
   constexpr int NVI = (NVB + kPrepThreads - 1) / kPrepThreads;
-  static_assert(NLA >= 1 && C * (K / 4) % kPrepThreads == 0, "log_alpha tiling");
+  static_assert(RT <= 4, "one row tile per wave");
 
-  // LDS regions; a later phase reuses a region once every read of its first use is behind a barrier
-  constexpr int kGBytes = C * KP * 4, kUtTBytes = 2 * V * C * 2;                    // G, Gam | Ut^T hi, lo
-  constexpr int kKiBytes = 2 * C * KB * 2, kVTBytes = (SPLIT ? 2 : 1) * V * C * 2;   // Ki hi, lo | V^T
-  constexpr int kMatBytes = 3 * C * CP * 4, kKhStageBytes = C * KB * 2 * (SPLIT ? 2 : 1);
-  __shared__ __attribute__((aligned(16))) unsigned char s_rg[kGBytes > kUtTBytes ? kGBytes : kUtTBytes];
-  __shared__ __attribute__((aligned(16))) __bf16 s_kt[2][C * KB];                  // Kt hi, lo
-  __shared__ __attribute__((aligned(16))) unsigned char s_rki[kKiBytes > kVTBytes ? kKiBytes : kVTBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char s_mat[kMatBytes > kKhStageBytes ? kMatBytes : kKhStageBytes];
-  float* s_G = reinterpret_cast<float*>(s_rg);            // G (log2), then Gam on the fast path
-  __bf16* s_utT = reinterpret_cast<__bf16*>(s_rg);        // [hi, lo][V][C], swizzled
-  __bf16* s_ki = reinterpret_cast<__bf16*>(s_rki);        // [hi, lo][C * KB]
-  __bf16* s_vT = reinterpret_cast<__bf16*>(s_rki);        // [hi(, lo)][V][C], swizzled
-  float* s_A = reinterpret_cast<float*>(s_mat);           // A, later M = P T'
-  float* s_T = s_A + C * CP;
-  float* s_P = s_T + C * CP;
-  // inversion temporaries and (later) per-wave staging tiles share one buffer
-  constexpr int kXSize = (RT > 1 ? RT - 1 : 1) * 16 * 17, kStageSize = 4 * 16 * 17;
-  __shared__ float s_scratch[kXSize > kStageSize ? kXSize : kStageSize];
-  float* s_X = s_scratch;
+  __shared__ __attribute__((aligned(16))) unsigned char s_r1[Lds::r1];
+  __shared__ __attribute__((aligned(16))) unsigned char s_r2[Lds::r2];
+  __shared__ __attribute__((aligned(16))) unsigned char s_r3[Lds::r3];
+  __shared__ __attribute__((aligned(16))) float s_scratch[Lds::kScratch];
+  __shared__ __attribute__((aligned(16))) float s_tot[RT * K];       // per-tile sums of log2 decay
   __shared__ float s_beta[C], s_qs[C], s_ks[C];
-  __shared__ __attribute__((aligned(16))) float s_gc[K];
   __shared__ int s_valid[C];
+  __bf16* s_ki = reinterpret_cast<__bf16*>(s_r1);                    // [hi, lo][C][KB]
+  float* s_G = reinterpret_cast<float*>(s_r1);                       // [C][KP] (slow path)
+  float* s_T = reinterpret_cast<float*>(s_r1);                       // [C][CP]
+  __bf16* s_vT = reinterpret_cast<__bf16*>(s_r1 + Lds::kTBytes);     // [hi(, lo)][V][C] swizzled
+  __bf16* s_kt = reinterpret_cast<__bf16*>(s_r2);                    // [hi(, lo)][C][KB]
+  __bf16* s_uth = reinterpret_cast<__bf16*>(s_r2);                   // [V][C] swizzled
+  __bf16* s_utl = Lds::kUtLoInR2 ? s_uth + V * C : reinterpret_cast<__bf16*>(s_r3);
+  __bf16* s_khs = reinterpret_cast<__bf16*>(s_r3);                   // [hi(, lo)][C][KB]
+  float* s_A = reinterpret_cast<float*>(s_r3);                       // [C][CP]
+  float* s_X = s_scratch;
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -166,22 +190,164 @@ prep_kernel(PrepParams p) {
   // any readable bytes stand in for the mask when there is none (the value is ignored)
   const uint8_t* mp = p.mask != nullptr ? p.mask : reinterpret_cast<const uint8_t*>(p.beta);
 
-  // ---- phase 1: issue every load of the chunk
-  float4 la_r[NLA];
+  const int I = wave;
+  const bool rows = I < RT;                                          // wave-uniform
+  const int rq = 16 * (rows ? I : 0) + (lane % 16);                  // this lane's row
+  const int cg = 8 * (lane / 16);                                    // channel offset inside a k step
+
+  // ---- phase 1: issue the loads of this lane's row (q, k, log_alpha, beta, mask)
+  Raw8<1> la_r[KS];
+  Raw8<DT> k_r[KS], q_r[KS];
 #pragma unroll
-  for (int i = 0; i < NLA; ++i) {
-    const int idx = tid + kPrepThreads * i;
-    const int r = idx / (K / 4), c = (idx % (K / 4)) * 4;
-    la_r[i] = *reinterpret_cast<const float4*>(p.log_alpha + grow(tsafe(r)) * dk + (c < dk ? c : 0));
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = 32 * ks + cg, cs = c < dk ? c : 0;
+    const size_t row = grow(tsafe(rq)) * dk + cs;
+    la_r[ks].load(p.log_alpha, row);
+    k_r[ks].load(kg, row);
+    q_r[ks].load(qg, row);
   }
-  float k_r[NKI][8];
+  const float beta_r = p.beta[grow(tsafe(rq))];
+  const uint8_t m_r = mp[(size_t)b * p.T + tsafe(rq)];
+  const bool rok = rows && rq < p.chunk && t0 + rq < p.T && (p.mask == nullptr || m_r != 0);
+
+  // ---- row scales of the optional L2 normalisation (channels past dk read as 0)
+  float qs = 1.f, ksc = 1.f;
+  if (p.l2norm) {
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-  for (int it = 0; it < NKI; ++it) {
-    const int idx = (tid + kPrepThreads * it) % (C * (K / 8));
-    const int r = idx / (K / 8), c0 = (idx % (K / 8)) * 8;
-    E::ld8(kg, grow(tsafe(r)) * dk + (c0 < dk ? c0 : 0), k_r[it]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool cok = 32 * ks + cg < dk;
+      float qf[8], kf[8];
+      q_r[ks].to_float(qf);
+      k_r[ks].to_float(kf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = cok ? qf[e] : 0.f, kk = cok ? kf[e] : 0.f;
+        sq += a * a; sk += kk * kk;
+      }
+    }
+    sq += __shfl_xor(sq, 16, 64); sk += __shfl_xor(sk, 16, 64);
+    sq += __shfl_xor(sq, 32, 64); sk += __shfl_xor(sk, 32, 64);
+    qs = rsqrtf(sq + 1e-6f);
+    ksc = rsqrtf(sk + 1e-6f);
   }
-  float v_r[NVI][8][4];                                 // V rows 8 rb .. +7, columns 4 cb .. +3
+  if (rows && lane < 16) {
+    s_valid[rq] = rok;
+    s_beta[rq] = rok ? beta_r : 0.f;
+    s_qs[rq] = qs;
+    s_ks[rq] = ksc;
+  }
+
+  // ---- inclusive cumulative sum of log2 decay over the tile's 16 rows (DPP row scan);
+  //      invalid rows and channels past dk contribute 0
+  float g_r[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bool cok = rok && 32 * ks + cg < dk;
+    float laf[8];
+    la_r[ks].to_float(laf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = cok ? laf[e] * kLog2e : 0.f;
+      x += row_shr<1>(x);
+      x += row_shr<2>(x);
+      x += row_shr<4>(x);
+      x += row_shr<8>(x);
+      g_r[ks][e] = x;
+    }
+  }
+  if (rows && (lane % 16) == 15) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      float4* dst = reinterpret_cast<float4*>(&s_tot[I * K + 32 * ks + cg]);
+      dst[0] = make_float4(g_r[ks][0], g_r[ks][1], g_r[ks][2], g_r[ks][3]);
+      dst[1] = make_float4(g_r[ks][4], g_r[ks][5], g_r[ks][6], g_r[ks][7]);
+    }
+  }
+  __syncthreads();
+
+  // ---- chunk totals Gc of this lane's channels: factorised path when every Gc >= -120
+  //      (each wave covers every channel, so all waves reach the same answer)
+  auto tile_sums = [&](int ks, float* pre, float* tot) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { pre[e] = 0.f; tot[e] = 0.f; }
+#pragma unroll
+    for (int J = 0; J < RT; ++J) {
+      float t[8];
+      ld8f(&s_tot[J * K + 32 * ks + cg], t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tot[e] += t[e];
+        pre[e] += (J < I) ? t[e] : 0.f;
+      }
+    }
+  };
+  bool lane_fast = true;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float pre[8], tot[8];
+    tile_sums(ks, pre, tot);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lane_fast = lane_fast && tot[e] >= kFastLimit;
+  }
+  const bool fast = __all(lane_fast);
+
+  // ---- decay factors for this lane's row.  On the fast path every factor lies in
+  //      [2^-120, 2^120], so the bare hardware exp2 is exact enough.
+  bf16x8 kth[KS], ktl[KS];
+  float qtf[KS][8];                                                  // Qt, fp32 (A and P take its hi, lo split)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c0 = 32 * ks + cg;
+    const bool cok = rok && c0 < dk;
+    float pre[8], gc[8];
+    tile_sums(ks, pre, gc);
+    float kt[8], ki[8], kh[8], kf[8], qf[8];
+    k_r[ks].to_float(kf);
+    q_r[ks].to_float(qf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = g_r[ks][e] + pre[e];
+      g_r[ks][e] = g;
+      const float kv = cok ? kf[e] * ksc : 0.f;
+      const float qv = cok ? qf[e] * qs : 0.f;
+      const float gam = __builtin_amdgcn_exp2f(g);
+      kt[e] = kv * gam;
+      ki[e] = fast ? kv * __builtin_amdgcn_exp2f(-g) : 0.f;
+      kh[e] = kv * __builtin_amdgcn_exp2f(gc[e] - g);
+      qtf[ks][e] = qv * gam;
+    }
+    split8(kt, kth[ks], ktl[ks]);
+    if (rows) {
+      *reinterpret_cast<bf16x8*>(&s_kt[rq * KB + c0]) = kth[ks];
+      if (SPLIT) *reinterpret_cast<bf16x8*>(&s_kt[C * KB + rq * KB + c0]) = ktl[ks];
+      bf16x8 hi, lo;
+      split8(kh, hi, lo);
+      *reinterpret_cast<bf16x8*>(&s_khs[rq * KB + c0]) = hi;
+      if (SPLIT) *reinterpret_cast<bf16x8*>(&s_khs[C * KB + rq * KB + c0]) = lo;
+      if (fast) {
+        split8(ki, hi, lo);
+        *reinterpret_cast<bf16x8*>(&s_ki[rq * KB + c0]) = hi;
+        *reinterpret_cast<bf16x8*>(&s_ki[C * KB + rq * KB + c0]) = lo;
+      } else {                                                       // exact pairwise decays need G
+        float4* gp = reinterpret_cast<float4*>(&s_G[rq * KP + c0]);
+        gp[0] = make_float4(g_r[ks][0], g_r[ks][1], g_r[ks][2], g_r[ks][3]);
+        gp[1] = make_float4(g_r[ks][4], g_r[ks][5], g_r[ks][6], g_r[ks][7]);
+      }
+    }
+    if (I == 0 && (lane % 16) == 0) {
+      // Gam_last: lanes 0, 16, 32, 48 of wave 0 cover every channel group once
+      float gl[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gl[e] = exp2f(gc[e]);
+      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(wsb + L::off_gam) + c0);
+      dst[0] = make_float4(gl[0], gl[1], gl[2], gl[3]);
+      dst[1] = make_float4(gl[4], gl[5], gl[6], gl[7]);
+    }
+  }
+
+  // ---- V: issued now, used after A and P
+  float v_r[NVI][8][4];                                              // rows 8 rb .. +7, columns 4 cb .. +3
 #pragma unroll
   for (int it = 0; it < NVI; ++it) {
     const int idx = (tid + kPrepThreads * it) % NVB;
@@ -189,152 +355,31 @@ prep_kernel(PrepParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) E::ld4(vg, grow(tsafe(8 * rb + e)) * dv + 4 * cb, v_r[it][e]);
   }
-  const int I = wave;                                   // this wave's row tile in the MFMA phases
-  const int rq = 16 * (I < RT ? I : 0) + (lane % 16);
-  float qtf[KS][8];                                     // raw q now, Qt = q * scale * Gam later
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c = 32 * ks + 8 * (lane / 16);
-    E::ld8(qg, grow(tsafe(rq)) * dk + (c < dk ? c : 0), qtf[ks]);
-  }
-  float beta_r = 0.f;
-  uint8_t m_r = 1;
-  if (tid < C) {
-    beta_r = p.beta[grow(tsafe(tid))];
-    m_r = mp[(size_t)b * p.T + tsafe(tid)];
-  }
-  if (tid < C) {
-    const int ok = tid < p.chunk && t0 + tid < p.T && (p.mask == nullptr || m_r != 0);
-    s_valid[tid] = ok;
-    s_beta[tid] = ok ? beta_r : 0.f;
-  }
   __syncthreads();
 
-  // ---- log_alpha (log2 units) into LDS, masked rows and padded channels as 0
+  // ---- Kh^T fragments: row c, contraction over rows 8*oct .. +7
+  for (int idx = tid; idx < K * (C / 8); idx += kPrepThreads) {
+    const int c = idx % K, oct = idx / K;
+    const int rt = c / 16, ks = oct / 4, ln = (c % 16) + 16 * (oct % 4);
+    bf16x8 v;
 #pragma unroll
-  for (int i = 0; i < NLA; ++i) {
-    const int idx = tid + kPrepThreads * i;
-    const int r = idx / (K / 4), c = (idx % (K / 4)) * 4;
-    const bool ok = c < dk && s_valid[r];
-    float* g = s_G + r * KP + c;
-    g[0] = ok ? la_r[i].x * kLog2e : 0.f; g[1] = ok ? la_r[i].y * kLog2e : 0.f;
-    g[2] = ok ? la_r[i].z * kLog2e : 0.f; g[3] = ok ? la_r[i].w * kLog2e : 0.f;
-  }
-  // ---- row scales for the optional L2 normalisation of q and k
-  if (p.l2norm) {
-    for (int r = wave; r < C; r += 4) {
-      float sq = 0.f, sk = 0.f;
-      const size_t row = grow(tsafe(r)) * dk;
-      for (int c = lane; c < dk; c += 64) {
-        const float a = E::ld(qg, row + c), kk = E::ld(kg, row + c);
-        sq += a * a; sk += kk * kk;
-      }
+    for (int e = 0; e < 8; ++e) v[e] = s_khs[(8 * oct + e) * KB + c];
+    store_frag(wsb + L::off_kh + frag_off(rt, ks, ln, C), v);
+    if (SPLIT) {
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) { sq += __shfl_xor(sq, off, 64); sk += __shfl_xor(sk, off, 64); }
-      if (lane == 0) { s_qs[r] = rsqrtf(sq + 1e-6f); s_ks[r] = rsqrtf(sk + 1e-6f); }
-    }
-  } else if (tid < C) {
-    s_qs[tid] = 1.0f;
-    s_ks[tid] = 1.0f;
-  }
-  __syncthreads();
-
-  // ---- inclusive cumulative sum over the chunk, per channel
-  if (tid < K) {
-    float g[C];
-#pragma unroll
-    for (int r = 0; r < C; ++r) g[r] = s_G[r * KP + tid];
-    float acc = 0.f;
-#pragma unroll
-    for (int r = 0; r < C; ++r) { acc += g[r]; s_G[r * KP + tid] = acc; }
-    s_gc[tid] = acc;
-  }
-  const int fast = __syncthreads_and(tid >= K || s_gc[tid] >= kFastLimit);
-
-  // ---- elementwise decay factors; item = (row r, 8 consecutive channels).  Factors are
-  //      at least 2^-120 on the fast path, so the bare hardware exp2 is exact enough.
-  {
-    __bf16* kh_stage = reinterpret_cast<__bf16*>(s_mat);          // Kh rows, transposed below
-    __bf16* kh_stage_lo = kh_stage + C * KB;
-#pragma unroll
-    for (int it = 0; it < NKI; ++it) {
-      const int idx = tid + kPrepThreads * it;
-      if (idx < C * (K / 8)) {
-        const int r = idx / (K / 8), c0 = (idx % (K / 8)) * 8;
-        const float sc = (c0 < dk && s_valid[r]) ? s_ks[r] : 0.f;
-        float g[8], gc[8], kt[8], ki[8], kh[8], gam[8];
-        ld8f(&s_G[r * KP + c0], g);
-        ld8f(&s_gc[c0], gc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kv = k_r[it][e] * sc;
-          gam[e] = __builtin_amdgcn_exp2f(g[e]);
-          kt[e] = kv * gam[e];
-          ki[e] = fast ? kv * __builtin_amdgcn_exp2f(-g[e]) : 0.f;
-          kh[e] = kv * __builtin_amdgcn_exp2f(gc[e] - g[e]);
-        }
-        bf16x8 hi, lo;
-        split8(kt, hi, lo);
-        *reinterpret_cast<bf16x8*>(&s_kt[0][r * KB + c0]) = hi;
-        *reinterpret_cast<bf16x8*>(&s_kt[1][r * KB + c0]) = lo;
-        split8(ki, hi, lo);
-        *reinterpret_cast<bf16x8*>(&s_ki[r * KB + c0]) = hi;
-        *reinterpret_cast<bf16x8*>(&s_ki[C * KB + r * KB + c0]) = lo;
-        split8(kh, hi, lo);
-        *reinterpret_cast<bf16x8*>(&kh_stage[r * KB + c0]) = hi;
-        if (SPLIT) *reinterpret_cast<bf16x8*>(&kh_stage_lo[r * KB + c0]) = lo;
-        if (fast) {                         // slow path keeps G for the exact pairwise decays
-          float4* gp = reinterpret_cast<float4*>(&s_G[r * KP + c0]);
-          gp[0] = make_float4(gam[0], gam[1], gam[2], gam[3]);
-          gp[1] = make_float4(gam[4], gam[5], gam[6], gam[7]);
-        }
-      }
-    }
-    __syncthreads();
-    // Kh^T fragments: row c, contraction over rows 8*oct .. +7
-    for (int idx = tid; idx < K * (C / 8); idx += kPrepThreads) {
-      const int c = idx % K, oct = idx / K;
-      const int rt = c / 16, ks = oct / 4, ln = (c % 16) + 16 * (oct % 4);
-      bf16x8 v;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = kh_stage[(8 * oct + e) * KB + c];
-      store_frag(wsb + L::off_kh + frag_off(rt, ks, ln, C), v);
-      if (SPLIT) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = kh_stage_lo[(8 * oct + e) * KB + c];
-        store_frag(wsb + L::off_kh + L::kCK + frag_off(rt, ks, ln, C), v);
-      }
+      for (int e = 0; e < 8; ++e) v[e] = s_khs[C * KB + (8 * oct + e) * KB + c];
+      store_frag(wsb + L::off_kh + L::kCK + frag_off(rt, ks, ln, C), v);
     }
   }
-  if (tid < K) reinterpret_cast<float*>(wsb + L::off_gam)[tid] = exp2f(s_gc[tid]);
-  __syncthreads();
+  __syncthreads();                                                   // Kh rows read: R3 takes A
 
-  // ---- Qt = q * scale * Gam for this wave's rows (kept in registers for the W phase)
-  if (I < RT) {
-    const bool rok = s_valid[rq] != 0;
-    const float sc = s_qs[rq];
+  // ---- A into LDS (shared by the inversion), P as this wave's A-fragments (hi, lo)
+  bf16x8 ph[CS], pl[CS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int c = 32 * ks + 8 * (lane / 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float g = s_G[rq * KP + c + e];
-        qtf[ks][e] = (rok && c < dk) ? qtf[ks][e] * sc * (fast ? g : exp2f(g)) : 0.f;
-      }
-    }
-  }
-
-  // ---- A and P
+  for (int ks = 0; ks < CS; ++ks) { ph[ks] = zero8(); pl[ks] = zero8(); }
   if (fast) {
-    if (I < RT) {
-      bf16x8 kth[KS], ktl[KS], qth[KS], qtl[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int c = 32 * ks + 8 * (lane / 16);
-        kth[ks] = *reinterpret_cast<const bf16x8*>(&s_kt[0][rq * KB + c]);
-        ktl[ks] = *reinterpret_cast<const bf16x8*>(&s_kt[1][rq * KB + c]);
-        split8(qtf[ks], qth[ks], qtl[ks]);
-      }
+    if (rows) {
+      float* stage = s_scratch + wave * 16 * 17;
       for (int J = 0; J < RT; ++J) {
         f32x4 accA = zero4(), accP = zero4();
         if (J <= I) {
@@ -342,15 +387,17 @@ prep_kernel(PrepParams p) {
           f32x4 a[3] = {zero4(), zero4(), zero4()}, pq[3] = {zero4(), zero4(), zero4()};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const int c = 32 * ks + 8 * (lane / 16);
+            const int c = 32 * ks + cg;
+            bf16x8 qth, qtl;
+            split8(qtf[ks], qth, qtl);
             const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[j * KB + c]);
             const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * KB + j * KB + c]);
             a[0] = mfma16(kth[ks], kih, a[0]);
             a[1] = mfma16(kth[ks], kil, a[1]);
             a[2] = mfma16(ktl[ks], kih, a[2]);
-            pq[0] = mfma16(qth[ks], kih, pq[0]);
-            pq[1] = mfma16(qth[ks], kil, pq[1]);
-            pq[2] = mfma16(qtl[ks], kih, pq[2]);
+            pq[0] = mfma16(qth, kih, pq[0]);
+            pq[1] = mfma16(qth, kil, pq[1]);
+            pq[2] = mfma16(qtl, kih, pq[2]);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -363,31 +410,52 @@ prep_kernel(PrepParams p) {
         for (int i = 0; i < 4; ++i) {
           const int rr = 16 * I + 4 * (lane / 16) + i;
           s_A[rr * CP + jj] = (jj < rr) ? s_beta[rr] * accA[i] : 0.f;
-          s_P[rr * CP + jj] = (jj <= rr) ? accP[i] : 0.f;
+          stage[(4 * (lane / 16) + i) * 17 + (lane % 16)] = (jj <= rr) ? accP[i] : 0.f;
         }
+        // D layout -> A-operand layout through the wave's staging tile
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0xc07f);                        // lgkmcnt(0)
+        const int half = (lane / 16) - 2 * (J % 2);
+        if (J <= I && (half == 0 || half == 1)) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv[e] = stage[(lane % 16) * 17 + 8 * half + e];
+#pragma unroll
+          for (int ks = 0; ks < CS; ++ks)
+            if (ks == J / 2) split8(pv, ph[ks], pl[ks]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_s_waitcnt(0xc07f);
       }
     }
-  } else {
-    // exact pairwise decays (chunks whose total decay in some channel is below 2^-120)
-    for (int idx = tid; idx < C * C; idx += kPrepThreads) {
-      const int rr = idx / C, jj = idx % C;
-      float sa = 0.f, sp = 0.f;
-      if (jj <= rr && s_valid[rr] && s_valid[jj]) {
-        const size_t tr = grow(t0 + rr) * dk, tj = grow(t0 + jj) * dk;
-        for (int c = 0; c < dk; ++c) {
-          const float d = exp2f(s_G[rr * KP + c] - s_G[jj * KP + c]);
-          const float kj = E::ld(kg, tj + c) * s_ks[jj];
-          sa += E::ld(kg, tr + c) * s_ks[rr] * kj * d;
-          sp += E::ld(qg, tr + c) * s_qs[rr] * kj * d;
+  } else if (rows) {
+    // exact pairwise decays, computed by each lane for its row and A-fragment columns
+    const size_t tr = grow(tsafe(rq)) * dk;
+#pragma unroll
+    for (int ks = 0; ks < CS; ++ks) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jj = 32 * ks + cg + e;
+        float sa = 0.f, sp = 0.f;
+        if (jj <= rq && rok && s_valid[jj]) {
+          const size_t tj = grow(t0 + jj) * dk;
+          for (int c = 0; c < dk; ++c) {
+            const float d = exp2f(s_G[rq * KP + c] - s_G[jj * KP + c]);
+            const float kj = E::ld(kg, tj + c) * s_ks[jj];
+            sa += E::ld(kg, tr + c) * ksc * kj * d;
+            sp += E::ld(qg, tr + c) * qs * kj * d;
+          }
         }
+        s_A[rq * CP + jj] = (jj < rq) ? beta_r * sa : 0.f;
+        pv[e] = sp;
       }
-      s_A[rr * CP + jj] = (jj < rr) ? s_beta[rr] * sa : 0.f;
-      s_P[rr * CP + jj] = (jj <= rr) ? sp : 0.f;
+      split8(pv, ph[ks], pl[ks]);
     }
   }
-  __syncthreads();
+  __syncthreads();                                                   // A complete; Ki or G read
 
-  // ---- V^T (hi, and lo for fp32 inputs) into the region Ki no longer needs; masked rows as 0
+  // ---- V^T (hi, and lo for fp32 inputs) behind T in R1; masked rows as 0
 #pragma unroll
   for (int it = 0; it < NVI; ++it) {
     const int idx = tid + kPrepThreads * it;
@@ -454,15 +522,10 @@ prep_kernel(PrepParams p) {
     __syncthreads();
   }
 
-  // ---- M = P T' (lower triangular), into s_A; -T', -M and P A-fragments kept in registers
-  bf16x8 tnh[CS], tnl[CS], mnh[CS], mnl[CS], ph[CS], pl[CS];
-  if (I < RT) {
-#pragma unroll
-    for (int ks = 0; ks < CS; ++ks) {
-      float pv[8];
-      ld8f(&s_P[rq * CP + 32 * ks + 8 * (lane / 16)], pv);
-      split8(pv, ph[ks], pl[ks]);
-    }
+  // ---- M = P T' (lower triangular), into this wave's rows of A's region; -T' and -M
+  //      A-fragments kept in registers
+  bf16x8 tnh[CS], tnl[CS], mnh[CS], mnl[CS];
+  if (rows) {
     for (int N = 0; N < RT; ++N) {
       f32x4 acc = zero4();
       if (N <= I) {
@@ -470,7 +533,7 @@ prep_kernel(PrepParams p) {
 #pragma unroll
         for (int ks = 0; ks < CS; ++ks) {
           float tv[8];
-          const int m0 = 32 * ks + 8 * (lane / 16);
+          const int m0 = 32 * ks + cg;
 #pragma unroll
           for (int e = 0; e < 8; ++e) tv[e] = s_T[(m0 + e) * CP + jn] * s_beta[jn];
           bf16x8 th, tl;
@@ -487,7 +550,7 @@ prep_kernel(PrepParams p) {
     __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's M rows landed
 #pragma unroll
     for (int ks = 0; ks < CS; ++ks) {
-      const int j0 = 32 * ks + 8 * (lane / 16);
+      const int j0 = 32 * ks + cg;
       float tv[8], mv[8];
       ld8f(&s_T[rq * CP + j0], tv);
       ld8f(&s_A[rq * CP + j0], mv);
@@ -499,7 +562,7 @@ prep_kernel(PrepParams p) {
   }
 
   // ---- Wn = -T' Kt and Qh = Qt - M Kt for this wave's 16 rows, all channel tiles
-  if (I < RT) {
+  if (rows) {
     float* stage = s_scratch + wave * 16 * 17;
 #pragma unroll
     for (int N = 0; N < K / 16; ++N) {
@@ -508,18 +571,18 @@ prep_kernel(PrepParams p) {
 #pragma unroll
       for (int ks = 0; ks < CS; ++ks) {
         if (32 * ks > 16 * I + 15) continue;          // T' and M are lower triangular
-        const int j0 = 32 * ks + 8 * (lane / 16);
-        bf16x8 kth, ktl;
+        const int j0 = 32 * ks + cg;
+        bf16x8 kth_b, ktl_b;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          kth[e] = s_kt[0][(j0 + e) * KB + cn];
-          if (SPLIT) ktl[e] = s_kt[1][(j0 + e) * KB + cn];
+          kth_b[e] = s_kt[(j0 + e) * KB + cn];
+          if (SPLIT) ktl_b[e] = s_kt[C * KB + (j0 + e) * KB + cn];
         }
-        accW = mfma16(tnh[ks], kth, accW);
-        accQ = mfma16(mnh[ks], kth, accQ);
+        accW = mfma16(tnh[ks], kth_b, accW);
+        accQ = mfma16(mnh[ks], kth_b, accQ);
         if (SPLIT) {
-          accW = mfma16(tnh[ks], ktl, accW); accW = mfma16(tnl[ks], kth, accW);
-          accQ = mfma16(mnh[ks], ktl, accQ); accQ = mfma16(mnl[ks], kth, accQ);
+          accW = mfma16(tnh[ks], ktl_b, accW); accW = mfma16(tnl[ks], kth_b, accW);
+          accQ = mfma16(mnh[ks], ktl_b, accQ); accQ = mfma16(mnl[ks], kth_b, accQ);
         }
       }
       // D layout -> A-operand order: lane L holds row L%16, channels 16N + 8*half .. +7
@@ -553,10 +616,11 @@ prep_kernel(PrepParams p) {
       }
     }
   }
+  __syncthreads();                                                   // Kt and M read: R2, R3 take Ut^T
 
   // ---- Ut = T' V for this wave's rows, every dv tile: to the workspace, and (hi, lo)
-  //      transposed into the region G no longer needs
-  if (I < RT) {
+  //      transposed into LDS
+  if (rows) {
 #pragma unroll
     for (int N = 0; N < V / 16; ++N) {
       const int vn = 16 * N + (lane % 16);
@@ -564,7 +628,7 @@ prep_kernel(PrepParams p) {
 #pragma unroll
       for (int ks = 0; ks < CS; ++ks) {
         if (32 * ks > 16 * I + 15) continue;
-        const int j0 = 32 * ks + 8 * (lane / 16);
+        const int j0 = 32 * ks + cg;
         const bf16x8 vh = *reinterpret_cast<const bf16x8*>(&s_vT[swz<C>(vn, j0)]);
         a0 = mfma16(tnh[ks], vh, a0);
         a1 = mfma16(tnl[ks], vh, a1);
@@ -578,15 +642,15 @@ prep_kernel(PrepParams p) {
       for (int i = 0; i < 4; ++i) {
         const int jr = 16 * I + 4 * (lane / 16) + i;
         const __bf16 hi = (__bf16)ut[i];
-        s_utT[swz<C>(vn, jr)] = hi;
-        s_utT[V * C + swz<C>(vn, jr)] = (__bf16)(ut[i] - (float)hi);
+        s_uth[swz<C>(vn, jr)] = hi;
+        s_utl[swz<C>(vn, jr)] = (__bf16)(ut[i] - (float)hi);
       }
     }
   }
   __syncthreads();
 
   // ---- O0 = P Ut for this wave's rows, every dv tile
-  if (I < RT) {
+  if (rows) {
 #pragma unroll
     for (int N = 0; N < V / 16; ++N) {
       const int vn = 16 * N + (lane % 16);
@@ -594,9 +658,9 @@ prep_kernel(PrepParams p) {
 #pragma unroll
       for (int ks = 0; ks < CS; ++ks) {
         if (32 * ks > 16 * I + 15) continue;          // P is lower triangular
-        const int j0 = 32 * ks + 8 * (lane / 16);
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_utT[swz<C>(vn, j0)]);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_utT[V * C + swz<C>(vn, j0)]);
+        const int j0 = 32 * ks + cg;
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_uth[swz<C>(vn, j0)]);
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_utl[swz<C>(vn, j0)]);
         a0 = mfma16(ph[ks], uh, a0);
         a1 = mfma16(ph[ks], ul, a1);
         a1 = mfma16(pl[ks], uh, a1);
