@@ -730,6 +730,7 @@ scan_kernel(ScanParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring1[R::kDepth == 2 ? R::kSlotBytes : 1024];
   __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state hi, lo; B-operand rows = dv column
   __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U hi, lo
+  __shared__ __attribute__((aligned(16))) unsigned char s_pf[4 * 64 * 4];  // L2 warm-up landing area, never read
 
   // XCD-aware mapping: all dv tiles of one head share blockIdx.x % 8 (one L2)
   const int L_id = blockIdx.x;
@@ -771,6 +772,35 @@ scan_kernel(ScanParams p) {
       __builtin_amdgcn_global_load_lds((const void*)(cb + block_src(bi) + (size_t)ln * 8),
                                        (lds_void_t*)(dst + pos * 1024), 16, 0, 0);
     }
+  };
+  // L2 warm-up two chunks ahead: one 4-byte copy per 128-byte line that this workgroup's
+  // copies will read, so the later 1 KB copies hit in L2.  Thread g takes line g of the
+  // list [its 1/NT share of the lines every tile reads (Wn, Qh, Kh^T); its tile's Ut and O0
+  // lines; the Gam_last lines]; threads past the end repeat the first line.
+  constexpr int kNT = V / kVT;
+  constexpr int kShLines = (int)(L::off_ut * 2 / 128);
+  constexpr int kOwnLines = 2 * (C / 16) * 8 + (4 * K + 127) / 128;
+  size_t pf_off = 0;                                                   // bytes from the chunk base
+  {
+    const int sh_mine = (kShLines - tile + kNT - 1) / kNT;
+    const int g = tid;
+    if (g < sh_mine) {
+      pf_off = (size_t)(tile + kNT * g) * 128;
+    } else if (g - sh_mine < kOwnLines) {
+      const int j = g - sh_mine;
+      if (j < 2 * (C / 16) * 8) {
+        const int blk = j / 8, line = j % 8;
+        const size_t base = blk < C / 16 ? L::off_ut + acc_off<V>(blk, tile, 0)
+                                         : L::off_o0 + acc_off<V>(blk - C / 16, tile, 0);
+        pf_off = base * 2 + (size_t)line * 128;
+      } else {
+        pf_off = L::off_gam * 2 + (size_t)(j - 2 * (C / 16) * 8) * 128;
+      }
+    }
+  }
+  auto warm_chunk = [&](int n) {
+    const unsigned char* cb = reinterpret_cast<const unsigned char*>(wsh + (size_t)n * L::kElems);
+    __builtin_amdgcn_global_load_lds((const void*)(cb + pf_off), (lds_void_t*)(s_pf + wave * 256), 4, 0, 0);
   };
   auto frag = [&](const unsigned char* sl, int bi) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(sl + bi * 1024 + lane * 16);
@@ -900,18 +930,22 @@ scan_kernel(ScanParams p) {
   if (p.NC > 0) copy_chunk(0, ring0);
   wait_vm_lgkm<0>();                                                   // chunk 0, S0 landed
   if constexpr (R::kDepth == 2) {
-    // Per wave, the copies into one slot are followed by exactly kStores stores before the
-    // wait for that slot, and vector memory operations complete in order, so vmcnt(kStores)
-    // means this wave's copies have landed; the barrier then publishes everyone's.
+    // Per wave, the copies into one slot are followed by exactly one warm-up copy and
+    // kStores stores before the wait for that slot, and vector memory operations complete
+    // in order, so vmcnt(kStores + 1) means this wave's copies have landed; the barrier
+    // then publishes everyone's.
+    if (p.NC > 1) warm_chunk(1);
     for (int n = 0; n < p.NC; n += 2) {
-      if (n > 0) wait_vm_lgkm<kStores>();
+      if (n > 0) wait_vm_lgkm<kStores + 1>();
       wg_barrier();
       copy_chunk(n + 1 <= last ? n + 1 : last, ring1);
+      warm_chunk(n + 2 <= last ? n + 2 : last);
       process(ring0, n);
       if (n + 1 < p.NC) {
-        wait_vm_lgkm<kStores>();
+        wait_vm_lgkm<kStores + 1>();
         wg_barrier();
         copy_chunk(n + 2 <= last ? n + 2 : last, ring0);
+        warm_chunk(n + 3 <= last ? n + 3 : last);
         process(ring1, n + 1);
       }
     }
