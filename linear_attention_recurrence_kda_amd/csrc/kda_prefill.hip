@@ -98,6 +98,14 @@ __device__ __forceinline__ void ld8f(const float* src, float* out) {
   out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
+// Cross-lane exchange through LDS inside one wave: the wave's LDS operations execute
+// in order in hardware, so no wait is needed, but the compiler must neither move LDS
+// accesses across this point nor split an all-lane store into divergent branches.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 // Element (n, j) of an n-major LDS matrix with C bf16 per row and no padding: the
 // 16-byte blocks of row n are permuted by an XOR with bits of n, so 16 lanes that
 // read one block column of 16 consecutive rows, or 64 lanes that write 16-byte
@@ -120,15 +128,15 @@ struct PrepLds {
   // R1: Ki hi, lo (fast path) or G (slow path); then T and V^T
   static constexpr int kTBytes = C * CP * 4;
   static constexpr int r1 = cmax(cmax(2 * C * KB * 2, C * KP * 4), kTBytes + kParts * V * C * 2);
-  // R2: Kt; then Ut^T hi (and lo when it fits)
+  // R2: Kt^T; then Ut^T hi (and lo when it fits)
   static constexpr int kUtPart = V * C * 2;
-  static constexpr int kKtBytes = kParts * C * KB * 2;
+  static constexpr int kKtBytes = kParts * K * C * 2;
   static constexpr bool kUtLoInR2 = kKtBytes >= 2 * kUtPart;
   static constexpr int r2 = cmax(kKtBytes, kUtLoInR2 ? 2 * kUtPart : kUtPart);
-  // R3: Kh rows until transposed; then A (later M = P T'); then Ut^T lo
-  static constexpr int r3 = cmax(cmax(kParts * C * KB * 2, C * CP * 4), kUtLoInR2 ? 0 : kUtPart);
-  // per-wave 16 x 17 staging tiles, or the inversion's temporaries
-  static constexpr int kScratch = cmax(4 * 16 * 17, (RT > 1 ? RT - 1 : 1) * 16 * 17);
+  // R3: Kh^T until stored; then A (later M = P T'); then Ut^T lo
+  static constexpr int r3 = cmax(cmax(kParts * K * C * 2, C * CP * 4), kUtLoInR2 ? 0 : kUtPart);
+  // two 16 x 17 fp32 staging tiles per wave
+  static constexpr int kScratch = 2 * 4 * 16 * 17;
 };
 
 // x shifted down by n lanes inside each row of 16 lanes (lanes below n read 0)
@@ -170,12 +178,11 @@ prep_kernel(PrepParams p) {
   float* s_G = reinterpret_cast<float*>(s_r1);                       // [C][KP] (slow path)
   float* s_T = reinterpret_cast<float*>(s_r1);                       // [C][CP]
   __bf16* s_vT = reinterpret_cast<__bf16*>(s_r1 + Lds::kTBytes);     // [hi(, lo)][V][C] swizzled
-  __bf16* s_kt = reinterpret_cast<__bf16*>(s_r2);                    // [hi(, lo)][C][KB]
+  __bf16* s_kt = reinterpret_cast<__bf16*>(s_r2);                    // Kt^T [hi(, lo)][K][C] swizzled
   __bf16* s_uth = reinterpret_cast<__bf16*>(s_r2);                   // [V][C] swizzled
   __bf16* s_utl = Lds::kUtLoInR2 ? s_uth + V * C : reinterpret_cast<__bf16*>(s_r3);
-  __bf16* s_khs = reinterpret_cast<__bf16*>(s_r3);                   // [hi(, lo)][C][KB]
+  __bf16* s_khs = reinterpret_cast<__bf16*>(s_r3);                   // Kh^T [hi(, lo)][K][C] swizzled
   float* s_A = reinterpret_cast<float*>(s_r3);                       // [C][CP]
-  float* s_X = s_scratch;
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -284,11 +291,11 @@ prep_kernel(PrepParams p) {
   };
   bool lane_fast = true;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    float pre[8], tot[8];
-    tile_sums(ks, pre, tot);
+  for (int c = lane; c < K; c += 64) {
+    float tot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) lane_fast = lane_fast && tot[e] >= kFastLimit;
+    for (int J = 0; J < RT; ++J) tot += s_tot[J * K + c];
+    lane_fast = lane_fast && tot >= kFastLimit;
   }
   const bool fast = __all(lane_fast);
 
@@ -319,12 +326,18 @@ prep_kernel(PrepParams p) {
     }
     split8(kt, kth[ks], ktl[ks]);
     if (rows) {
-      *reinterpret_cast<bf16x8*>(&s_kt[rq * KB + c0]) = kth[ks];
-      if (SPLIT) *reinterpret_cast<bf16x8*>(&s_kt[C * KB + rq * KB + c0]) = ktl[ks];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_kt[swz<C>(c0 + e, rq)] = kth[ks][e];
+        if (SPLIT) s_kt[K * C + swz<C>(c0 + e, rq)] = ktl[ks][e];
+      }
       bf16x8 hi, lo;
       split8(kh, hi, lo);
-      *reinterpret_cast<bf16x8*>(&s_khs[rq * KB + c0]) = hi;
-      if (SPLIT) *reinterpret_cast<bf16x8*>(&s_khs[C * KB + rq * KB + c0]) = lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_khs[swz<C>(c0 + e, rq)] = hi[e];
+        if (SPLIT) s_khs[K * C + swz<C>(c0 + e, rq)] = lo[e];
+      }
       if (fast) {
         split8(ki, hi, lo);
         *reinterpret_cast<bf16x8*>(&s_ki[rq * KB + c0]) = hi;
@@ -361,15 +374,10 @@ prep_kernel(PrepParams p) {
   for (int idx = tid; idx < K * (C / 8); idx += kPrepThreads) {
     const int c = idx % K, oct = idx / K;
     const int rt = c / 16, ks = oct / 4, ln = (c % 16) + 16 * (oct % 4);
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = s_khs[(8 * oct + e) * KB + c];
-    store_frag(wsb + L::off_kh + frag_off(rt, ks, ln, C), v);
-    if (SPLIT) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = s_khs[C * KB + (8 * oct + e) * KB + c];
-      store_frag(wsb + L::off_kh + L::kCK + frag_off(rt, ks, ln, C), v);
-    }
+    store_frag(wsb + L::off_kh + frag_off(rt, ks, ln, C), *reinterpret_cast<const bf16x8*>(&s_khs[swz<C>(c, 8 * oct)]));
+    if (SPLIT)
+      store_frag(wsb + L::off_kh + L::kCK + frag_off(rt, ks, ln, C),
+                 *reinterpret_cast<const bf16x8*>(&s_khs[K * C + swz<C>(c, 8 * oct)]));
   }
   __syncthreads();                                                   // Kh rows read: R3 takes A
 
@@ -380,6 +388,9 @@ prep_kernel(PrepParams p) {
   if (fast) {
     if (rows) {
       float* stage = s_scratch + wave * 16 * 17;
+      bf16x8 qth[KS], qtl[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) split8(qtf[ks], qth[ks], qtl[ks]);
       for (int J = 0; J < RT; ++J) {
         f32x4 accA = zero4(), accP = zero4();
         if (J <= I) {
@@ -388,16 +399,14 @@ prep_kernel(PrepParams p) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const int c = 32 * ks + cg;
-            bf16x8 qth, qtl;
-            split8(qtf[ks], qth, qtl);
             const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[j * KB + c]);
             const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * KB + j * KB + c]);
             a[0] = mfma16(kth[ks], kih, a[0]);
             a[1] = mfma16(kth[ks], kil, a[1]);
             a[2] = mfma16(ktl[ks], kih, a[2]);
-            pq[0] = mfma16(qth, kih, pq[0]);
-            pq[1] = mfma16(qth, kil, pq[1]);
-            pq[2] = mfma16(qtl, kih, pq[2]);
+            pq[0] = mfma16(qth[ks], kih, pq[0]);
+            pq[1] = mfma16(qth[ks], kil, pq[1]);
+            pq[2] = mfma16(qtl[ks], kih, pq[2]);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -413,8 +422,7 @@ prep_kernel(PrepParams p) {
           stage[(4 * (lane / 16) + i) * 17 + (lane % 16)] = (jj <= rr) ? accP[i] : 0.f;
         }
         // D layout -> A-operand layout through the wave's staging tile
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0xc07f);                        // lgkmcnt(0)
+        wave_lds_sync();
         const int half = (lane / 16) - 2 * (J % 2);
         if (J <= I && (half == 0 || half == 1)) {
           float pv[8];
@@ -424,8 +432,7 @@ prep_kernel(PrepParams p) {
           for (int ks = 0; ks < CS; ++ks)
             if (ks == J / 2) split8(pv, ph[ks], pl[ks]);
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0xc07f);
+        wave_lds_sync();
       }
     }
   } else if (rows) {
@@ -478,7 +485,8 @@ prep_kernel(PrepParams p) {
     }
   }
 
-  // ---- T = (I + A)^-1, blocked: diagonal 16x16 blocks by forward substitution
+  // ---- T = (I + A)^-1, blocked: diagonal 16x16 blocks by forward substitution (two
+  //      partial sums per row keep the dependency chain short)
   if (tid < RT * 16) {
     const int Ib = tid / 16, cc = tid % 16;
     float x[16];
@@ -487,10 +495,13 @@ prep_kernel(PrepParams p) {
       float arow[16];
       ld8f(&s_A[(16 * Ib + rr) * CP + 16 * Ib], arow);
       ld8f(&s_A[(16 * Ib + rr) * CP + 16 * Ib + 8], arow + 8);
-      float v = (rr == cc) ? 1.f : 0.f;
+      float v0 = (rr == cc) ? 1.f : 0.f, v1 = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < rr; ++jj) v -= arow[jj] * x[jj];
-      x[rr] = v;
+      for (int jj = 0; jj < rr; ++jj) {
+        if (jj & 1) v1 -= arow[jj] * x[jj];
+        else v0 -= arow[jj] * x[jj];
+      }
+      x[rr] = v0 + v1;
     }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) s_T[(16 * Ib + rr) * CP + 16 * Ib + cc] = x[rr];
@@ -500,24 +511,54 @@ prep_kernel(PrepParams p) {
     if (jj / 16 != rr / 16) s_T[rr * CP + jj] = 0.f;
   }
   __syncthreads();
-  // off-diagonal blocks by distance d: T_IJ = -T_II * sum_{L=J}^{I-1} A_IL T_LJ
+  // off-diagonal blocks by distance d, one block per wave on the MFMA:
+  //   X = sum_{L=J}^{I-1} A_IL T_LJ,   T_IJ = -T_II X      (I = J + d, wave J)
   for (int d = 1; d < RT; ++d) {
-    const int nblk = RT - d;
-    for (int e = tid; e < nblk * 256; e += kPrepThreads) {
-      const int J = e / 256, Ib = J + d, rr = (e % 256) / 16, cc = e % 16;
-      float x = 0.f;
-      for (int Lb = J; Lb < Ib; ++Lb)
+    const int J = wave, Ib = J + d;
+    if (Ib < RT) {
+      const int r = lane % 16, g = lane / 16;
+      f32x4 xa = zero4(), xb = zero4();
 #pragma unroll
-        for (int m = 0; m < 16; ++m) x += s_A[(16 * Ib + rr) * CP + 16 * Lb + m] * s_T[(16 * Lb + m) * CP + 16 * J + cc];
-      s_X[J * 272 + rr * 17 + cc] = x;
-    }
-    __syncthreads();
-    for (int e = tid; e < nblk * 256; e += kPrepThreads) {
-      const int J = e / 256, Ib = J + d, rr = (e % 256) / 16, cc = e % 16;
-      float x = 0.f;
+      for (int st = 0; st < (RT / 2); ++st) {
+        if (st >= (d + 1) / 2) break;
+        const int k0 = 16 * J + 32 * st + 8 * g;                     // contraction rows of T
+        const bool kin = k0 < 16 * Ib;                               // L < I only
+        float av[8], tv[8];
+        ld8f(&s_A[(16 * Ib + r) * CP + (kin ? k0 : 0)], av);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) x += s_T[(16 * Ib + rr) * CP + 16 * Ib + m] * s_X[J * 272 + m * 17 + cc];
-      s_T[(16 * Ib + rr) * CP + 16 * J + cc] = -x;
+        for (int e = 0; e < 8; ++e) {
+          av[e] = kin ? av[e] : 0.f;
+          tv[e] = kin ? s_T[(k0 + e) * CP + 16 * J + r] : 0.f;
+        }
+        bf16x8 ah, al, th, tl;
+        split8(av, ah, al);
+        split8(tv, th, tl);
+        xa = mfma16(ah, th, xa);
+        xb = mfma16(ah, tl, xb);
+        xb = mfma16(al, th, xb);
+      }
+      // X (D layout) through the wave's staging tile into B-operand order
+      float* stage = s_scratch + wave * 16 * 17;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) stage[(4 * g + i) * 17 + r] = xa[i] + xb[i];
+      wave_lds_sync();
+      float xv[8], tiv[8];
+      const bool klo = g < 2;                                        // contraction over 16 rows only
+      ld8f(&s_T[(16 * Ib + r) * CP + 16 * Ib + (klo ? 8 * g : 0)], tiv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xv[e] = klo ? stage[(8 * g + e) * 17 + r] : 0.f;
+        tiv[e] = klo ? tiv[e] : 0.f;
+      }
+      bf16x8 xh, xl, tih, til;
+      split8(xv, xh, xl);
+      split8(tiv, tih, til);
+      f32x4 ya = zero4(), yb = zero4();
+      ya = mfma16(tih, xh, ya);
+      yb = mfma16(tih, xl, yb);
+      yb = mfma16(til, xh, yb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_T[(16 * Ib + 4 * g + i) * CP + 16 * J + r] = -(ya[i] + yb[i]);
     }
     __syncthreads();
   }
@@ -542,12 +583,11 @@ prep_kernel(PrepParams p) {
           if (SPLIT) { acc = mfma16(ph[ks], tl, acc); acc = mfma16(pl[ks], th, acc); }
         }
       }
-      // each wave reads back only its own rows of M, so a wave-local order suffices
+      // each wave reads back only its own rows of M, so a wave-level exchange suffices
 #pragma unroll
       for (int i = 0; i < 4; ++i) s_A[(16 * I + 4 * (lane / 16) + i) * CP + 16 * N + (lane % 16)] = acc[i];
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0): this wave's M rows landed
+    wave_lds_sync();
 #pragma unroll
     for (int ks = 0; ks < CS; ++ks) {
       const int j0 = 32 * ks + cg;
@@ -563,7 +603,8 @@ prep_kernel(PrepParams p) {
 
   // ---- Wn = -T' Kt and Qh = Qt - M Kt for this wave's 16 rows, all channel tiles
   if (rows) {
-    float* stage = s_scratch + wave * 16 * 17;
+    float* stage_w = s_scratch + wave * 16 * 17;
+    float* stage_q = s_scratch + (4 + wave) * 16 * 17;
 #pragma unroll
     for (int N = 0; N < K / 16; ++N) {
       f32x4 accW = zero4(), accQ = zero4();
@@ -572,12 +613,8 @@ prep_kernel(PrepParams p) {
       for (int ks = 0; ks < CS; ++ks) {
         if (32 * ks > 16 * I + 15) continue;          // T' and M are lower triangular
         const int j0 = 32 * ks + cg;
-        bf16x8 kth_b, ktl_b;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kth_b[e] = s_kt[(j0 + e) * KB + cn];
-          if (SPLIT) ktl_b[e] = s_kt[C * KB + (j0 + e) * KB + cn];
-        }
+        const bf16x8 kth_b = *reinterpret_cast<const bf16x8*>(&s_kt[swz<C>(cn, j0)]);
+        const bf16x8 ktl_b = SPLIT ? *reinterpret_cast<const bf16x8*>(&s_kt[K * C + swz<C>(cn, j0)]) : kth_b;
         accW = mfma16(tnh[ks], kth_b, accW);
         accQ = mfma16(mnh[ks], kth_b, accQ);
         if (SPLIT) {
@@ -592,10 +629,10 @@ prep_kernel(PrepParams p) {
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
         const f32x4& acc = pass == 0 ? accW : accQ;
+        float* stage = pass == 0 ? stage_w : stage_q;
 #pragma unroll
         for (int i = 0; i < 4; ++i) stage[(4 * (lane / 16) + i) * 17 + (lane % 16)] = acc[i];
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): staging writes landed
+        wave_lds_sync();
         if (mine) {
           const int rr = lane % 16;
           float vals[8];
@@ -611,8 +648,7 @@ prep_kernel(PrepParams p) {
           store_frag(wsb + off, hi);
           if (SPLIT) store_frag(wsb + off + L::kCK, lo);
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_s_waitcnt(0xc07f);
+        wave_lds_sync();
       }
     }
   }
