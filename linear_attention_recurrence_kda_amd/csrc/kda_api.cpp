@@ -44,7 +44,7 @@ int kda_last_hip_error(void) { return g_last_hip_error; }
 
 size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return 0;
-  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk)) return 0;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535) return 0;
   return kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
 }
 
@@ -54,7 +54,7 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if ((flags & ~(unsigned)KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_INVALID_ARG;
-  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk))
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535)
     return KDA_ERR_UNSUPPORTED;
   const bool work = (size_t)B * H > 0;
   if (work) {

@@ -275,18 +275,25 @@ prep_kernel(PrepParams p) {
 
   // ---- chunk totals Gc of this lane's channels: factorised path when every Gc >= -120
   //      (each wave covers every channel, so all waves reach the same answer)
+  // sums of the earlier tiles (pre) and of all tiles (tot); the loop bounds are
+  // wave-uniform, so no per-element selects are needed
   auto tile_sums = [&](int ks, float* pre, float* tot) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { pre[e] = 0.f; tot[e] = 0.f; }
-#pragma unroll
-    for (int J = 0; J < RT; ++J) {
+    for (int e = 0; e < 8; ++e) pre[e] = 0.f;
+    const int ilim = rows ? I : 0;
+    for (int J = 0; J < ilim; ++J) {
       float t[8];
       ld8f(&s_tot[J * K + 32 * ks + cg], t);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        tot[e] += t[e];
-        pre[e] += (J < I) ? t[e] : 0.f;
-      }
+      for (int e = 0; e < 8; ++e) pre[e] += t[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tot[e] = pre[e];
+    for (int J = ilim; J < RT; ++J) {
+      float t[8];
+      ld8f(&s_tot[J * K + 32 * ks + cg], t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tot[e] += t[e];
     }
   };
   bool lane_fast = true;
@@ -775,7 +782,8 @@ scan_kernel(ScanParams p) {
   if (bh >= p.nbh) return;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = tile * kVT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // uniform: addresses stay scalar
   const int I = wave;                                // this wave's U/O row tile
   // predicates that the tiling makes always true are compile-time constants
   const bool has_rows = (RT >= 4) || (I < RT);
@@ -805,7 +813,8 @@ scan_kernel(ScanParams p) {
       const int bi = pos < R::kBlocks ? pos : R::kBlocks - 1;
       // the Gam_last block holds K floats: lanes past them re-read its start
       const int ln = (bi == R::b_gam && lane >= K / 4) ? 0 : lane;
-      __builtin_amdgcn_global_load_lds((const void*)(cb + block_src(bi) + (size_t)ln * 8),
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(cb + block_src(bi));  // uniform
+      __builtin_amdgcn_global_load_lds((const void*)(src + (uint32_t)(ln * 16)),
                                        (lds_void_t*)(dst + pos * 1024), 16, 0, 0);
     }
   };
@@ -857,6 +866,14 @@ scan_kernel(ScanParams p) {
                     ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
     }
   }
+  // byte offsets of this lane's output elements from token t0 of the chunk (tokens are
+  // H * dv elements apart; the host keeps these below 2^32)
+  const size_t o_row_bytes = (size_t)p.H * dv * sizeof(typename E::T);
+  uint32_t o_lane[kStores];
+#pragma unroll
+  for (int i = 0; i < kStores; ++i)
+    o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * o_row_bytes +
+                           ((size_t)h * dv + v0 + lane % 16) * sizeof(typename E::T));
   auto publish_state = [&]() {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -876,6 +893,9 @@ scan_kernel(ScanParams p) {
   // one chunk, operands in ring slot `sl`; ends with exactly kStores global stores per lane
   auto process = [&](const unsigned char* sl, int n) {
     const int t0 = n * p.chunk;
+    // every row of a full chunk is in range: its stores need no check
+    const bool full = (p.chunk == C) && (t0 + C <= p.T);
+    unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + ((size_t)b * p.T + t0) * o_row_bytes;
     bf16x8 sh[KS], slo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -947,10 +967,9 @@ scan_kernel(ScanParams p) {
       }
 #pragma unroll
       for (int i = 0; i < kStores; ++i) {
-        const int rr = 16 * I + 4 * (lane / 16) + i, t = t0 + rr;
-        const bool ok = rr < p.chunk && t < p.T;
-        typename E::T* dst = ok ? og + (((size_t)b * p.T + t) * p.H + h) * dv + v0 + (lane % 16)
-                                : sink + 16 * i + (lane % 16);
+        const int rr = 16 * I + 4 * (lane / 16) + i;
+        typename E::T* dst = reinterpret_cast<typename E::T*>(ochunk + o_lane[i]);
+        if (!full && !(rr < p.chunk && t0 + rr < p.T)) dst = sink + 16 * i + (lane % 16);
         E::st(dst, 0, o4[0][i] + o4[1][i]);
       }
     } else {
@@ -1048,6 +1067,7 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, i
 template <int DT, int K, int V, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
+  if ((size_t)(C + 1) * a.H * a.dv * 4 > 0xffffffffull) return hipErrorInvalidValue;   // 32-bit output offsets
   const int NC = (a.T + a.chunk - 1) / a.chunk;
   const int NT = a.dv / kVT;
   const int nbh = a.B * a.H;

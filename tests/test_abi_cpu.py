@@ -81,6 +81,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, chunk=48) == UNSUPPORTED
     assert _prefill(lib, chunk=0) == UNSUPPORTED
     assert _prefill(lib, dk=100) == UNSUPPORTED
+    assert _prefill(lib, H=65536) == UNSUPPORTED
+    assert _prefill(lib, B=65536) == UNSUPPORTED
     assert _prefill(lib, T=-3) == INVALID
     assert _prefill(lib, dtype=2) == INVALID
     assert _prefill(lib, flags=2) == INVALID            # SILU belongs to the short conv
