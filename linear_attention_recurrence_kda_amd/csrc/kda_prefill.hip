@@ -717,44 +717,35 @@ prep_kernel(PrepParams p) {
 }
 
 // ================================================================ scan kernel
-// The operands of one chunk for one dv tile (Wn, Qh, Kh^T, the tile's Ut and O0
-// blocks, Gam_last) are whole 1 KB blocks of the workspace.  The four waves copy
-// them straight into an LDS ring slot with global_load_lds_dwordx4 (lane l writes
-// bytes 16 l .. 16 l + 15 of the block), every wave the same number of copies.
-template <int K, int V, int C, bool SPLIT>
-struct ScanRing {
-  static constexpr int RT = C / 16, KS = K / 32, CS = C / 32, SRT = K / 16;
-  static constexpr int kParts = SPLIT ? 2 : 1;
-  static constexpr int b_wn = 0;
-  static constexpr int b_qh = b_wn + RT * KS * kParts;
-  static constexpr int b_kh = b_qh + RT * KS * kParts;
-  static constexpr int b_ut = b_kh + SRT * CS * kParts;
-  static constexpr int b_o0 = b_ut + RT;
-  static constexpr int b_gam = b_o0 + RT;
-  static constexpr int kBlocks = b_gam + 1;                   // Gam_last (<= 512 B) takes one block
-  static constexpr int kPerWave = (kBlocks + 3) / 4;          // copies per wave per chunk
-  static constexpr int kSlotBytes = 4 * kPerWave * 1024;
-  static constexpr int kDepth = (2 * kSlotBytes <= 128 * 1024) ? 2 : 1;
-  static_assert(4 * K <= 1024, "Gam_last fits one block");
+// One workgroup per (b, h, 16-column dv tile).  Each wave loads the operands it needs for
+// a chunk (its row tile of Wn and Qh, its state row tiles of Kh^T, the tile's Ut and O0
+// blocks, Gam_last) straight into registers one chunk ahead of their use, with an L2
+// warm-up two chunks ahead; LDS only carries the state and U between the waves.
+template <int K, int C, bool SPLIT>
+struct ScanOps {
+  static constexpr int KS = K / 32, CS = C / 32, SPW = (K / 16 + 3) / 4;
+  bf16x8 wn[KS], qh[KS];
+  bf16x8 wnl[SPLIT ? KS : 1], qhl[SPLIT ? KS : 1];
+  bf16x8 kh[SPW][CS];
+  bf16x8 khl[SPLIT ? SPW : 1][CS];
+  f32x4 ut, o0;
+  float4 gam[SPW];
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// s_barrier with compiler-only fences around it: no memory access moves across,
-// and (unlike __syncthreads) no wait for outstanding global->LDS copies is added
+// s_barrier with compiler-only fences around it: no memory access moves across
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-// s_waitcnt with lgkmcnt(0) and vmcnt(n); memory accesses stay on their side of it
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
+// wait for this wave's LDS operations (not for its global loads)
+__device__ __forceinline__ void wait_lgkm() {
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 0xf) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
 }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int DT, int K, int V, int C>
 __global__ void __launch_bounds__(kScanThreads)
@@ -762,18 +753,15 @@ scan_kernel(ScanParams p) {
   using E = Elem<DT>;
   constexpr bool SPLIT = (DT == 1);
   using L = WsLayout<K, V, C, SPLIT>;
-  using R = ScanRing<K, V, C, SPLIT>;
+  using Ops = ScanOps<K, C, SPLIT>;
   constexpr int RT = C / 16, CS = C / 32, KS = K / 32, SRT = K / 16;
-  constexpr int SPW = (SRT + 3) / 4;                // state row tiles per wave
+  constexpr int SPW = Ops::SPW;                     // state row tiles per wave
   constexpr int KB = K + 8, CB = C + 8;
   constexpr int kStores = 4;                        // global stores per lane and chunk, always
   static_assert(RT <= 4, "one U/O row tile per wave");
 
-  __shared__ __attribute__((aligned(1024))) unsigned char ring0[R::kSlotBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char ring1[R::kDepth == 2 ? R::kSlotBytes : 1024];
   __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state hi, lo; B-operand rows = dv column
   __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U hi, lo
-  __shared__ __attribute__((aligned(16))) unsigned char s_pf[4 * 64 * 4];  // L2 warm-up landing area, never read
 
   // XCD-aware mapping: all dv tiles of one head share blockIdx.x % 8 (one L2)
   const int L_id = blockIdx.x;
@@ -785,43 +773,55 @@ scan_kernel(ScanParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // uniform: addresses stay scalar
   const int I = wave;                                // this wave's U/O row tile
-  // predicates that the tiling makes always true are compile-time constants
+  // predicates that the tiling makes always true are compile-time constants, so the
+  // loads below are straight-line code and the compiler's waits stay exact
   const bool has_rows = (RT >= 4) || (I < RT);
-  auto srow = [&](int M) { return (SRT % 4 == 0) || (M < SRT); };
+  auto srow = [&](int M) __attribute__((always_inline)) { return (SRT % 4 == 0) || (M < SRT); };
   const int dk = p.dk, dv = p.dv;
   typename E::T* og = (typename E::T*)p.o;
   typename E::T* sink = (typename E::T*)p.sink + (L_id & 63) * 64;
   const uint16_t* wsh = p.ws + (size_t)bh * p.NC * L::kElems;
   const int last = p.NC - 1;
 
-  // workspace offset (2-byte units from the chunk base) of ring block bi, for this tile
-  auto block_src = [&](int bi) -> size_t {
-    if (bi < R::b_qh) return L::off_wn + (size_t)(bi - R::b_wn) * 512;
-    if (bi < R::b_kh) return L::off_qh + (size_t)(bi - R::b_qh) * 512;
-    if (bi < R::b_ut) return L::off_kh + (size_t)(bi - R::b_kh) * 512;
-    if (bi < R::b_o0) return L::off_ut + acc_off<V>(bi - R::b_ut, tile, 0);
-    if (bi < R::b_gam) return L::off_o0 + acc_off<V>(bi - R::b_o0, tile, 0);
-    return L::off_gam;
+  auto ld16 = [&](const uint16_t* src) __attribute__((always_inline)) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(src);
   };
-  // chunk n into a ring slot: block wave + 4 j goes to slot block wave + 4 j; copies past
-  // the last block repeat it into the slot's spare blocks, so every wave issues kPerWave
-  auto copy_chunk = [&](int n, unsigned char* dst) {
+  // chunk n's operands for this wave, into registers
+  auto load_ops = [&](int n, Ops& op) __attribute__((always_inline)) {
     const uint16_t* cb = wsh + (size_t)n * L::kElems;
+    if (has_rows) {
 #pragma unroll
-    for (int j = 0; j < R::kPerWave; ++j) {
-      const int pos = wave + 4 * j;
-      const int bi = pos < R::kBlocks ? pos : R::kBlocks - 1;
-      // the Gam_last block holds K floats: lanes past them re-read its start
-      const int ln = (bi == R::b_gam && lane >= K / 4) ? 0 : lane;
-      const unsigned char* src = reinterpret_cast<const unsigned char*>(cb + block_src(bi));  // uniform
-      __builtin_amdgcn_global_load_lds((const void*)(src + (uint32_t)(ln * 16)),
-                                       (lds_void_t*)(dst + pos * 1024), 16, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        op.wn[ks] = ld16(cb + L::off_wn + frag_off(I, ks, lane, K));
+        op.qh[ks] = ld16(cb + L::off_qh + frag_off(I, ks, lane, K));
+        if (SPLIT) {
+          op.wnl[ks] = ld16(cb + L::off_wn + L::kCK + frag_off(I, ks, lane, K));
+          op.qhl[ks] = ld16(cb + L::off_qh + L::kCK + frag_off(I, ks, lane, K));
+        }
+      }
+      op.ut = *reinterpret_cast<const f32x4*>(cb + L::off_ut + acc_off<V>(I, tile, lane));
+      op.o0 = *reinterpret_cast<const f32x4*>(cb + L::off_o0 + acc_off<V>(I, tile, lane));
+    }
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int M = wave + 4 * m;
+      if (srow(M)) {
+#pragma unroll
+        for (int ks = 0; ks < CS; ++ks) {
+          op.kh[m][ks] = ld16(cb + L::off_kh + frag_off(M, ks, lane, C));
+          if (SPLIT) op.khl[m][ks] = ld16(cb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
+        }
+        op.gam[m] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cb + L::off_gam) + 16 * M + 4 * (lane / 16));
+      }
     }
   };
-  // L2 warm-up two chunks ahead: one 4-byte copy per 128-byte line that this workgroup's
-  // copies will read, so the later 1 KB copies hit in L2.  Thread g takes line g of the
-  // list [its 1/NT share of the lines every tile reads (Wn, Qh, Kh^T); its tile's Ut and O0
-  // lines; the Gam_last lines]; threads past the end repeat the first line.
+
+  // L2 warm-up two chunks ahead: one 4-byte load per 128-byte line that this workgroup's
+  // loads will read, so they hit in L2.  The loaded word is consumed by an empty asm
+  // statement one chunk later, when it has long arrived, which keeps the load alive
+  // without a wait anywhere else.  Thread g takes line g of the list [its
+  // 1/NT share of the lines every tile reads (Wn, Qh, Kh^T); its tile's Ut and O0 lines; the
+  // Gam_last lines]; threads past the end repeat the first line.
   constexpr int kNT = V / kVT;
   constexpr int kShLines = (int)(L::off_ut * 2 / 128);
   constexpr int kOwnLines = 2 * (C / 16) * 8 + (4 * K + 127) / 128;
@@ -843,15 +843,11 @@ scan_kernel(ScanParams p) {
       }
     }
   }
-  auto warm_chunk = [&](int n) {
+  uint32_t warm_word = 0;
+  auto warm_chunk = [&](int n) __attribute__((always_inline)) {
     const unsigned char* cb = reinterpret_cast<const unsigned char*>(wsh + (size_t)n * L::kElems);
-    __builtin_amdgcn_global_load_lds((const void*)(cb + pf_off), (lds_void_t*)(s_pf + wave * 256), 4, 0, 0);
-  };
-  auto frag = [&](const unsigned char* sl, int bi) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(sl + bi * 1024 + lane * 16);
-  };
-  auto acc_blk = [&](const unsigned char* sl, int bi) -> f32x4 {
-    return *reinterpret_cast<const f32x4*>(sl + bi * 1024 + lane * 16);
+    asm volatile("" :: "v"(warm_word));
+    warm_word = *reinterpret_cast<const uint32_t*>(cb + pf_off);
   };
 
   // state tiles in registers: wave w owns state row tiles w, w+4, ...
@@ -874,7 +870,7 @@ scan_kernel(ScanParams p) {
   for (int i = 0; i < kStores; ++i)
     o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * o_row_bytes +
                            ((size_t)h * dv + v0 + lane % 16) * sizeof(typename E::T));
-  auto publish_state = [&]() {
+  auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
       const int M = wave + 4 * m;
@@ -890,8 +886,8 @@ scan_kernel(ScanParams p) {
     }
   };
 
-  // one chunk, operands in ring slot `sl`; ends with exactly kStores global stores per lane
-  auto process = [&](const unsigned char* sl, int n) {
+  // one chunk with its operands in registers; ends with exactly kStores global stores per lane
+  auto process = [&](const Ops& op, int n) __attribute__((always_inline)) {
     const int t0 = n * p.chunk;
     // every row of a full chunk is in range: its stores need no check
     const bool full = (p.chunk == C) && (t0 + C <= p.T);
@@ -905,13 +901,12 @@ scan_kernel(ScanParams p) {
     }
     // ---- U = Ut + Wn S for this wave's 16 rows (independent accumulators keep the chains short)
     if (has_rows) {
-      f32x4 u[4] = {acc_blk(sl, R::b_ut + I), zero4(), zero4(), zero4()};
+      f32x4 u[4] = {op.ut, zero4(), zero4(), zero4()};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 wn = frag(sl, R::b_wn + I * KS + ks);
-        u[(ks & 1) * 2] = mfma16(wn, sh[ks], u[(ks & 1) * 2]);
-        u[(ks & 1) * 2 + 1] = mfma16(wn, slo[ks], u[(ks & 1) * 2 + 1]);
-        if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(frag(sl, R::b_wn + RT * KS + I * KS + ks), sh[ks], u[(ks & 1) * 2 + 1]);
+        u[(ks & 1) * 2] = mfma16(op.wn[ks], sh[ks], u[(ks & 1) * 2]);
+        u[(ks & 1) * 2 + 1] = mfma16(op.wn[ks], slo[ks], u[(ks & 1) * 2 + 1]);
+        if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(op.wnl[ks], sh[ks], u[(ks & 1) * 2 + 1]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -922,7 +917,7 @@ scan_kernel(ScanParams p) {
         s_U[1][(lane % 16) * CB + rr] = (__bf16)(uv - (float)hi);
       }
     }
-    wait_vm_lgkm<63>();
+    wait_lgkm();
     wg_barrier();                                                      // U visible; S reads done
 
     // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
@@ -934,7 +929,6 @@ scan_kernel(ScanParams p) {
         uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
         ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
       }
-      const float* gam = reinterpret_cast<const float*>(sl + R::b_gam * 1024);
 #pragma unroll
       for (int m = 0; m < SPW; ++m) {
         const int M = wave + 4 * m;
@@ -942,28 +936,25 @@ scan_kernel(ScanParams p) {
         f32x4 a0 = zero4(), a1 = zero4();
 #pragma unroll
         for (int ks = 0; ks < CS; ++ks) {
-          const bf16x8 kh = frag(sl, R::b_kh + M * CS + ks);
-          a0 = mfma16(kh, uh[ks], a0);
-          a1 = mfma16(kh, ul[ks], a1);
-          if (SPLIT) a1 = mfma16(frag(sl, R::b_kh + SRT * CS + M * CS + ks), uh[ks], a1);
+          a0 = mfma16(op.kh[m][ks], uh[ks], a0);
+          a1 = mfma16(op.kh[m][ks], ul[ks], a1);
+          if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
         }
-        const float4 g4 = *reinterpret_cast<const float4*>(gam + 16 * M + 4 * (lane / 16));
-        const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+        const float gg[4] = {op.gam[m].x, op.gam[m].y, op.gam[m].z, op.gam[m].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
       }
     }
     publish_state();
 
-    // ---- O = O0 + Qh S (the state entering the chunk, from the bf16 fragments)
+    // ---- O = O0 + Qh S (the state entering the chunk, still in fragments)
     if (has_rows) {
-      f32x4 o4[2] = {acc_blk(sl, R::b_o0 + I), zero4()};
+      f32x4 o4[2] = {op.o0, zero4()};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qh = frag(sl, R::b_qh + I * KS + ks);
-        o4[ks & 1] = mfma16(qh, sh[ks], o4[ks & 1]);
-        o4[ks & 1] = mfma16(qh, slo[ks], o4[ks & 1]);
-        if (SPLIT) o4[ks & 1] = mfma16(frag(sl, R::b_qh + RT * KS + I * KS + ks), sh[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(op.qh[ks], sh[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(op.qh[ks], slo[ks], o4[ks & 1]);
+        if (SPLIT) o4[ks & 1] = mfma16(op.qhl[ks], sh[ks], o4[ks & 1]);
       }
 #pragma unroll
       for (int i = 0; i < kStores; ++i) {
@@ -982,41 +973,34 @@ scan_kernel(ScanParams p) {
   };
 
   publish_state();
-  if (p.NC > 0) copy_chunk(0, ring0);
-  wait_vm_lgkm<0>();                                                   // chunk 0, S0 landed
-  if constexpr (R::kDepth == 2) {
-    // Per wave, the copies into one slot are followed by exactly one warm-up copy and
-    // kStores stores before the wait for that slot, and vector memory operations complete
-    // in order, so vmcnt(kStores + 1) means this wave's copies have landed; the barrier
-    // then publishes everyone's.
-    if (p.NC > 1) warm_chunk(1);
-    for (int n = 0; n < p.NC; n += 2) {
-      if (n > 0) wait_vm_lgkm<kStores + 1>();
-      wg_barrier();
-      copy_chunk(n + 1 <= last ? n + 1 : last, ring1);
-      warm_chunk(n + 2 <= last ? n + 2 : last);
-      process(ring0, n);
-      if (n + 1 < p.NC) {
-        wait_vm_lgkm<kStores + 1>();
-        wg_barrier();
-        copy_chunk(n + 2 <= last ? n + 2 : last, ring0);
-        warm_chunk(n + 3 <= last ? n + 3 : last);
-        process(ring1, n + 1);
-      }
-    }
-  } else {
-    for (int n = 0; n < p.NC; ++n) {
-      if (n > 0) {
-        wait_vm_lgkm<63>();
-        wg_barrier();                                                  // every wave is done with the slot
-        copy_chunk(n, ring0);
-        wait_vm_lgkm<0>();
-      }
-      wg_barrier();
-      process(ring0, n);
-    }
+  // Operands of chunk n are loaded at the top of chunk n - 1 (the first ones here), the
+  // L2 warm-up for chunk n + 1 beside them; loads into the registers of one buffer are
+  // issued only after the previous chunk that used that buffer is done with it.
+  // The loop body holds two chunks with no condition between them, so each buffer keeps
+  // its own registers and the compiler's waits stay exact.
+  Ops opA, opB;
+  if (p.NC > 0) load_ops(0, opA);
+  if (p.NC > 1) warm_chunk(1);
+  int n = 0;
+  for (; n + 1 < p.NC; n += 2) {
+    wait_lgkm();
+    wg_barrier();                                                      // state visible
+    load_ops(n + 1, opB);
+    warm_chunk(n + 2 <= last ? n + 2 : last);
+    process(opA, n);
+    wait_lgkm();
+    wg_barrier();
+    load_ops(n + 2 <= last ? n + 2 : last, opA);
+    warm_chunk(n + 3 <= last ? n + 3 : last);
+    process(opB, n + 1);
   }
-  wait_vm_lgkm<0>();
+  if (n < p.NC) {                                                      // odd chunk count: the last one
+    wait_lgkm();
+    wg_barrier();
+    process(opA, n);
+  }
+  asm volatile("" :: "v"(warm_word));
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- final state
 #pragma unroll
