@@ -43,6 +43,16 @@ decode_step_kernel(const typename Elem<DT>::T* __restrict__ q, const typename El
   __shared__ float s_red[2][Sh::kRowGroups][V];
   __shared__ float s_scal[4];
 
+  // the state loads carry all of the traffic: issue them before anything waits
+  const int cq = tid % Sh::kColQuads;
+  const int rg = tid / Sh::kColQuads;
+  const int r0 = rg * Sh::kRows;
+  float* sp = state + (size_t)bh * K * V;
+  f32x4 s[Sh::kRows];
+#pragma unroll
+  for (int r = 0; r < Sh::kRows; ++r)
+    s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (size_t)(r0 + r) * V + 4 * cq));
+
   for (int i = tid; i < K; i += Sh::kThreads) {
     s_q[i] = E::ld(q, (size_t)bh * K + i);
     s_k[i] = E::ld(k, (size_t)bh * K + i);
@@ -72,16 +82,6 @@ decode_step_kernel(const typename Elem<DT>::T* __restrict__ q, const typename El
   }
   __syncthreads();
   const float rq = s_scal[0], rk = s_scal[1], qk = s_scal[2];
-
-  const int cq = tid % Sh::kColQuads;
-  const int rg = tid / Sh::kColQuads;
-  const int r0 = rg * Sh::kRows;
-  float* sp = state + (size_t)bh * K * V;
-
-  float4 s[Sh::kRows];
-#pragma unroll
-  for (int r = 0; r < Sh::kRows; ++r)
-    s[r] = *reinterpret_cast<const float4*>(sp + (size_t)(r0 + r) * V + 4 * cq);
 
   float pa[4] = {0.f, 0.f, 0.f, 0.f}, pc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -114,9 +114,9 @@ decode_step_kernel(const typename Elem<DT>::T* __restrict__ q, const typename El
 #pragma unroll
   for (int r = 0; r < Sh::kRows; ++r) {
     const float kr = s_k[r0 + r] * rk;
-    float4 n;
+    f32x4 n;
     n.x = s[r].x + kr * u0; n.y = s[r].y + kr * u1; n.z = s[r].z + kr * u2; n.w = s[r].w + kr * u3;
-    *reinterpret_cast<float4*>(sp + (size_t)(r0 + r) * V + 4 * cq) = n;
+    __builtin_nontemporal_store(n, reinterpret_cast<f32x4*>(sp + (size_t)(r0 + r) * V + 4 * cq));
   }
 }
 
