@@ -106,6 +106,19 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+// Two 16x16 products computed transposed, so lane l holds columns 4 (l/16) .. +3 of row
+// l%16 of column tiles 2s (t0) and 2s + 1 (t1), become the A-operand fragment of k step s
+// (lane l: columns 32 s + 8 (l/16) .. +7 of row l%16) with two cross-lane swaps per
+// register: the 32-lane swap pairs the tiles' halves, the 16-lane swap interleaves them.
+__device__ __forceinline__ void pair_to_afrag(const f32x4& t0, const f32x4& t1, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0[i]), __float_as_uint(t1[i]), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+    out[i] = __uint_as_float(b[0]);
+    out[4 + i] = __uint_as_float(b[1]);
+  }
+}
 // Element (n, j) of an n-major LDS matrix with C bf16 per row and no padding: the
 // 16-byte blocks of row n are permuted by an XOR with bits of n, so 16 lanes that
 // read one block column of 16 consecutive rows, or 64 lanes that write 16-byte
@@ -133,10 +146,10 @@ struct PrepLds {
   static constexpr int kKtBytes = kParts * K * C * 2;
   static constexpr bool kUtLoInR2 = kKtBytes >= 2 * kUtPart;
   static constexpr int r2 = cmax(kKtBytes, kUtLoInR2 ? 2 * kUtPart : kUtPart);
-  // R3: Kh^T until stored; then A (later M = P T'); then Ut^T lo
+  // R3: Kh^T until stored; then A; then Ut^T lo
   static constexpr int r3 = cmax(cmax(kParts * K * C * 2, C * CP * 4), kUtLoInR2 ? 0 : kUtPart);
-  // two 16 x 17 fp32 staging tiles per wave
-  static constexpr int kScratch = 2 * 4 * 16 * 17;
+  // one 16 x 17 fp32 staging tile per wave (the inversion's block exchange)
+  static constexpr int kScratch = 4 * 16 * 17;
 };
 
 // x shifted down by n lanes inside each row of 16 lanes (lanes below n read 0)
@@ -394,52 +407,53 @@ prep_kernel(PrepParams p) {
   for (int ks = 0; ks < CS; ++ks) { ph[ks] = zero8(); pl[ks] = zero8(); }
   if (fast) {
     if (rows) {
-      float* stage = s_scratch + wave * 16 * 17;
+      // transposed products: A-operand rows are Ki rows of column tile J (LDS), B-operand
+      // columns are this wave's Kt and Qt rows (registers); lane (g, r) gets columns
+      // 16 J + 4 g .. +3 of row rq of A and P
       bf16x8 qth[KS], qtl[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) split8(qtf[ks], qth[ks], qtl[ks]);
-      for (int J = 0; J < RT; ++J) {
-        f32x4 accA = zero4(), accP = zero4();
-        if (J <= I) {
-          const int j = 16 * J + (lane % 16);
-          f32x4 a[3] = {zero4(), zero4(), zero4()}, pq[3] = {zero4(), zero4(), zero4()};
+      const float beta_row = s_beta[rq];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int c = 32 * ks + cg;
-            const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[j * KB + c]);
-            const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * KB + j * KB + c]);
-            a[0] = mfma16(kth[ks], kih, a[0]);
-            a[1] = mfma16(kth[ks], kil, a[1]);
-            a[2] = mfma16(ktl[ks], kih, a[2]);
-            pq[0] = mfma16(qth[ks], kih, pq[0]);
-            pq[1] = mfma16(qth[ks], kil, pq[1]);
-            pq[2] = mfma16(qtl[ks], kih, pq[2]);
+      for (int s2 = 0; s2 < CS; ++s2) {
+        f32x4 pt[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int J = 2 * s2 + t;
+          f32x4 accA = zero4(), accP = zero4();
+          if (J <= I) {
+            const int j = 16 * J + (lane % 16);
+            f32x4 a[3] = {zero4(), zero4(), zero4()}, pq[3] = {zero4(), zero4(), zero4()};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              const int c = 32 * ks + cg;
+              const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[j * KB + c]);
+              const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * KB + j * KB + c]);
+              a[0] = mfma16(kih, kth[ks], a[0]);
+              a[1] = mfma16(kil, kth[ks], a[1]);
+              a[2] = mfma16(kih, ktl[ks], a[2]);
+              pq[0] = mfma16(kih, qth[ks], pq[0]);
+              pq[1] = mfma16(kil, qth[ks], pq[1]);
+              pq[2] = mfma16(kih, qtl[ks], pq[2]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              accA[i] = a[0][i] + (a[1][i] + a[2][i]);
+              accP[i] = pq[0][i] + (pq[1][i] + pq[2][i]);
+            }
           }
+          float av[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            accA[i] = a[0][i] + (a[1][i] + a[2][i]);
-            accP[i] = pq[0][i] + (pq[1][i] + pq[2][i]);
+            const int jj = 16 * J + 4 * (lane / 16) + i;
+            av[i] = (jj < rq) ? beta_row * accA[i] : 0.f;
+            pt[t][i] = (jj <= rq) ? accP[i] : 0.f;
           }
+          *reinterpret_cast<float4*>(&s_A[rq * CP + 16 * J + 4 * (lane / 16)]) = make_float4(av[0], av[1], av[2], av[3]);
         }
-        const int jj = 16 * J + (lane % 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 16 * I + 4 * (lane / 16) + i;
-          s_A[rr * CP + jj] = (jj < rr) ? s_beta[rr] * accA[i] : 0.f;
-          stage[(4 * (lane / 16) + i) * 17 + (lane % 16)] = (jj <= rr) ? accP[i] : 0.f;
-        }
-        // D layout -> A-operand layout through the wave's staging tile
-        wave_lds_sync();
-        const int half = (lane / 16) - 2 * (J % 2);
-        if (J <= I && (half == 0 || half == 1)) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e] = stage[(lane % 16) * 17 + 8 * half + e];
-#pragma unroll
-          for (int ks = 0; ks < CS; ++ks)
-            if (ks == J / 2) split8(pv, ph[ks], pl[ks]);
-        }
-        wave_lds_sync();
+        float pv[8];
+        pair_to_afrag(pt[0], pt[1], pv);
+        split8(pv, ph[s2], pl[s2]);
       }
     }
   } else if (rows) {
@@ -570,96 +584,94 @@ prep_kernel(PrepParams p) {
     __syncthreads();
   }
 
-  // ---- M = P T' (lower triangular), into this wave's rows of A's region; -T' and -M
-  //      A-fragments kept in registers
+  // ---- -T' rows of this wave, and M = P T' computed transposed (A operand: columns of
+  //      T', B operand: this wave's P rows), both as A-operand fragments in registers
   bf16x8 tnh[CS], tnl[CS], mnh[CS], mnl[CS];
   if (rows) {
-    for (int N = 0; N < RT; ++N) {
-      f32x4 acc = zero4();
-      if (N <= I) {
-        const int jn = 16 * N + (lane % 16);
-#pragma unroll
-        for (int ks = 0; ks < CS; ++ks) {
-          float tv[8];
-          const int m0 = 32 * ks + cg;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) tv[e] = s_T[(m0 + e) * CP + jn] * s_beta[jn];
-          bf16x8 th, tl;
-          split8(tv, th, tl);
-          acc = mfma16(ph[ks], th, acc);
-          if (SPLIT) { acc = mfma16(ph[ks], tl, acc); acc = mfma16(pl[ks], th, acc); }
-        }
-      }
-      // each wave reads back only its own rows of M, so a wave-level exchange suffices
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_A[(16 * I + 4 * (lane / 16) + i) * CP + 16 * N + (lane % 16)] = acc[i];
-    }
-    wave_lds_sync();
 #pragma unroll
     for (int ks = 0; ks < CS; ++ks) {
       const int j0 = 32 * ks + cg;
-      float tv[8], mv[8];
+      float tv[8];
       ld8f(&s_T[rq * CP + j0], tv);
-      ld8f(&s_A[rq * CP + j0], mv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { tv[e] = -tv[e] * s_beta[j0 + e]; mv[e] = -mv[e]; }
+      for (int e = 0; e < 8; ++e) tv[e] = -tv[e] * s_beta[j0 + e];
       split8(tv, tnh[ks], tnl[ks]);
-      split8(mv, mnh[ks], mnl[ks]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < CS; ++s2) {
+      f32x4 mt[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int N = 2 * s2 + t;
+        f32x4 acc = zero4();
+        if (N <= I) {
+          const int jn = 16 * N + (lane % 16);
+#pragma unroll
+          for (int ms = 0; ms < CS; ++ms) {
+            if (32 * ms > 16 * I + 15) continue;                   // P is lower triangular
+            const int m0 = 32 * ms + cg;
+            float tv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) tv[e] = s_T[(m0 + e) * CP + jn] * s_beta[jn];
+            bf16x8 th, tl;
+            split8(tv, th, tl);
+            acc = mfma16(th, ph[ms], acc);
+            if (SPLIT) { acc = mfma16(tl, ph[ms], acc); acc = mfma16(th, pl[ms], acc); }
+          }
+        }
+        mt[t] = acc;
+      }
+      float mv[8];
+      pair_to_afrag(mt[0], mt[1], mv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mv[e] = -mv[e];
+      split8(mv, mnh[s2], mnl[s2]);
     }
   }
 
-  // ---- Wn = -T' Kt and Qh = Qt - M Kt for this wave's 16 rows, all channel tiles
+  // ---- Wn = -T' Kt and Qh = Qt - M Kt for this wave's 16 rows, computed transposed
+  //      (A operand: Kt^T rows from LDS, B operand: -T' and -M rows in registers) and
+  //      turned into A-operand fragments by lane swaps
   if (rows) {
-    float* stage_w = s_scratch + wave * 16 * 17;
-    float* stage_q = s_scratch + (4 + wave) * 16 * 17;
 #pragma unroll
-    for (int N = 0; N < K / 16; ++N) {
-      f32x4 accW = zero4(), accQ = zero4();
-      const int cn = 16 * N + (lane % 16);
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x4 dw[2], dq[2];
 #pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        if (32 * ks > 16 * I + 15) continue;          // T' and M are lower triangular
-        const int j0 = 32 * ks + cg;
-        const bf16x8 kth_b = *reinterpret_cast<const bf16x8*>(&s_kt[swz<C>(cn, j0)]);
-        const bf16x8 ktl_b = SPLIT ? *reinterpret_cast<const bf16x8*>(&s_kt[K * C + swz<C>(cn, j0)]) : kth_b;
-        accW = mfma16(tnh[ks], kth_b, accW);
-        accQ = mfma16(mnh[ks], kth_b, accQ);
-        if (SPLIT) {
-          accW = mfma16(tnh[ks], ktl_b, accW); accW = mfma16(tnl[ks], kth_b, accW);
-          accQ = mfma16(mnh[ks], ktl_b, accQ); accQ = mfma16(mnl[ks], kth_b, accQ);
-        }
-      }
-      // D layout -> A-operand order: lane L holds row L%16, channels 16N + 8*half .. +7
-      // where L/16 = 2*(N%2) + half; that lane also holds those Qt values.
-      const int half = (lane / 16) - 2 * (N % 2);
-      const bool mine = half == 0 || half == 1;
+      for (int t = 0; t < 2; ++t) {
+        const int cn = 32 * ks + 16 * t + (lane % 16);
+        f32x4 aw = zero4(), aq = zero4();
 #pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-        const f32x4& acc = pass == 0 ? accW : accQ;
-        float* stage = pass == 0 ? stage_w : stage_q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) stage[(4 * (lane / 16) + i) * 17 + (lane % 16)] = acc[i];
-        wave_lds_sync();
-        if (mine) {
-          const int rr = lane % 16;
-          float vals[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vals[e] = stage[rr * 17 + 8 * half + e];
-          if (pass == 1) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] += qtf[N / 2][e];
+        for (int js = 0; js < CS; ++js) {
+          if (32 * js > 16 * I + 15) continue;                     // T' and M are lower triangular
+          const int j0 = 32 * js + cg;
+          const bf16x8 kt = *reinterpret_cast<const bf16x8*>(&s_kt[swz<C>(cn, j0)]);
+          aw = mfma16(kt, tnh[js], aw);
+          aq = mfma16(kt, mnh[js], aq);
+          if (SPLIT) {
+            const bf16x8 ktl_b = *reinterpret_cast<const bf16x8*>(&s_kt[K * C + swz<C>(cn, j0)]);
+            aw = mfma16(ktl_b, tnh[js], aw); aw = mfma16(kt, tnl[js], aw);
+            aq = mfma16(ktl_b, mnh[js], aq); aq = mfma16(kt, mnl[js], aq);
           }
-          bf16x8 hi, lo;
-          split8(vals, hi, lo);
-          const size_t off = (pass == 0 ? L::off_wn : L::off_qh) + frag_off(I, N / 2, lane, K);
-          store_frag(wsb + off, hi);
-          if (SPLIT) store_frag(wsb + off + L::kCK, lo);
         }
-        wave_lds_sync();
+        dw[t] = aw;
+        dq[t] = aq;
       }
+      float wv[8], qv[8];
+      pair_to_afrag(dw[0], dw[1], wv);
+      pair_to_afrag(dq[0], dq[1], qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] += qtf[ks][e];
+      bf16x8 hi, lo;
+      const size_t off = frag_off(I, ks, lane, K);
+      split8(wv, hi, lo);
+      store_frag(wsb + L::off_wn + off, hi);
+      if (SPLIT) store_frag(wsb + L::off_wn + L::kCK + off, lo);
+      split8(qv, hi, lo);
+      store_frag(wsb + L::off_qh + off, hi);
+      if (SPLIT) store_frag(wsb + L::off_qh + L::kCK + off, lo);
     }
   }
-  __syncthreads();                                                   // Kt and M read: R2, R3 take Ut^T
+  __syncthreads();                                                   // Kt and A read: R2, R3 take Ut^T
 
   // ---- Ut = T' V for this wave's rows, every dv tile: to the workspace, and (hi, lo)
   //      transposed into LDS
