@@ -1028,12 +1028,17 @@ scan_kernel(ScanParams p) {
 }
 
 // ================================================================ host side
+// The chunk size only changes rounding (the result is the token recurrence for any
+// chunk), so chunks above 64 tokens run as 64-token chunks: a 128- or 256-token WY
+// block would not fit the LDS of a workgroup, and its decay factors would leave the fp32
+// range for ordinary gates.
+static int run_chunk(int chunk) { return chunk > 64 ? 64 : chunk; }
 static int tile_chunk(int chunk) { return chunk <= 32 ? 32 : 64; }
 static int pad_k(int dk) { return dk < 32 ? 32 : dk; }
 
 bool prefill_supported(int dk, int dv, int chunk) {
   (void)dk; (void)dv;
-  return chunk == 16 || chunk == 32 || chunk == 64;
+  return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128 || chunk == 256;
 }
 
 // (padded dk, dv, tile chunk) instantiated
@@ -1056,6 +1061,7 @@ static size_t chunk_ws_elems(int K, int V, int C, int dtype) {
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (T == 0 || B == 0 || H == 0) return 0;
+  chunk = run_chunk(chunk);
   const int NC = (T + chunk - 1) / chunk;
   return (size_t)B * H * NC * chunk_ws_elems(pad_k(dk), dv, tile_chunk(chunk), dtype) * 2 + kSinkBytes;
 }
@@ -1093,7 +1099,9 @@ static hipError_t launch_prefill_dt(const PrefillArgs& a) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a) {
+hipError_t launch_prefill(const PrefillArgs& args) {
+  PrefillArgs a = args;
+  a.chunk = run_chunk(a.chunk);
   return a.dtype == 0 ? launch_prefill_dt<0>(a) : launch_prefill_dt<1>(a);
 }
 

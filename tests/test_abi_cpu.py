@@ -79,6 +79,7 @@ def _prefill(lib, **kw):
 
 def test_prefill_validation(lib):
     assert _prefill(lib, chunk=48) == UNSUPPORTED
+    assert _prefill(lib, chunk=512) == UNSUPPORTED
     assert _prefill(lib, chunk=0) == UNSUPPORTED
     assert _prefill(lib, dk=100) == UNSUPPORTED
     assert _prefill(lib, H=65536) == UNSUPPORTED
@@ -108,6 +109,9 @@ def test_workspace_size_query(lib):
     assert f(1, 65, 1, 128, 128, 64, 0) == one + per_chunk   # ragged tail takes a whole chunk
     assert f(4, 4096, 32, 128, 128, 64, 0) == one + (4 * 32 * 64 - 1) * per_chunk
     assert f(1, 64, 1, 128, 128, 64, 1) > one            # fp32 inputs keep residual parts
+    for big in (128, 256):                               # run as 64-token chunks: same workspace
+        assert f(4, 4096, 32, 128, 128, big, 0) == f(4, 4096, 32, 128, 128, 64, 0)
+    assert f(1, 64, 1, 128, 128, 512, 0) == 0
 
 
 def _conv(lib, **kw):

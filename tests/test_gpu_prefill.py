@@ -186,6 +186,26 @@ def test_needle_across_chunks(oracle):
     check("needle", host(o)[0, -1, 0], want, "bf16")
 
 
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_prefill_large_chunk_values(oracle, chunk):
+    """chunk 128 and 256 (the pages' value) are accepted and give the recurrence; they
+    run as 64-token chunks, so they match chunk 64 bitwise."""
+    import torch
+    dev = device()
+    B, T, H, dk, dv = 2, 600, 2, 128, 128
+    say(f"[case] prefill chunk {chunk} B={B} T={T}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=21)
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=21)
+    mask = D.padded_layout([T - 37, T], T, ["left", "right"])
+    o, s = _run(inp, "bf16", dev, chunk, mask, s0)
+    o64, s64 = _run(inp, "bf16", dev, 64, mask, s0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o64) and torch.equal(s, s64)
+    ro, rs = oracle.c_prefill(**inp, mask=mask, init_state=s0)
+    check(f"chunk{chunk} o", host(o), ro, "bf16")
+    check(f"chunk{chunk} state", host(s), rs, "bf16")
+
+
 def test_chunked_prefill_full_size_sampled(oracle):
     """B=4, H=32, T=4096, dk=dv=128, bf16, chunk 64, zero state: the full workload in the
     benchmark's launch configuration, with sampled heads checked against the oracle."""
@@ -202,3 +222,22 @@ def test_chunked_prefill_full_size_sampled(oracle):
         ro, rs = oracle.c_prefill(**one)
         check(f"full o b{b}h{h}", host(o[b:b + 1, :, h:h + 1]), ro, "bf16")
         check(f"full state b{b}h{h}", host(s[b:b + 1, h:h + 1]), rs, "bf16")
+
+
+def test_long_prefill_sampled_heads(oracle):
+    """B=1, H=32, T=524288, dk=dv=128, bf16, zero state: the long-prefill workload in one
+    call; three heads checked against the oracle over every position and the final state."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv = 1, 524288, 32, 128, 128
+    say("[case] prefill long 1x524288x32, sampled heads")
+    x = D.torch_kda_inputs(B, T, H, dk, dv, dev, "bf16", seed=3)
+    o, s = kda.chunk_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], chunk_size=64)
+    torch.cuda.synchronize()
+    heads = [0, 15, 31]
+    one = {n: host(t[:, :, heads]) for n, t in x.items()}
+    ro, rs = oracle.c_prefill(**one)
+    for i, h in enumerate(heads):
+        check(f"long o h{h}", host(o[:, :, h]), ro[:, :, i], "bf16")
+        check(f"long state h{h}", host(s[:, h]), rs[:, i], "bf16")
