@@ -10,18 +10,20 @@
 // Qt = Q*Gam, Kh = K*Gam_last/Gam:
 //   A  = strict_lower(Diag(beta) Kt Ki^T)      P = lower(Qt Ki^T)
 //   T' = (I + A)^-1 Diag(beta)                 (unit lower-triangular solve, fp32)
-//   Wn = -T' Kt,  Qh = Qt - (P T') Kt,  Ut = T' V,  O0 = P Ut
-//   U  = Ut + Wn S0                            (per-token corrections)
-//   O  = O0 + Qh S0
+//   Wn = -T' Kt
+//   U  = T' V + Wn S0                          (per-token corrections)
+//   O  = Qt S0 + P U
 //   S1 = Diag(Gam_last) S0 + Kh^T U
-// Only the last three lines depend on the state, so the work splits into:
-//   prep_kernel: one workgroup per (b, h, chunk), fully parallel; writes Wn, Qh,
-//     Kh^T (bf16, MFMA operand order), Ut and O0 (fp32, MFMA accumulator order)
-//     and Gam_last to a workspace;
+// (O = Qt S0 + P U is the token read-out q_t^T S_t summed up: P U adds the chunk's own
+// updates to what the decayed entry state gives.)  Nothing before the last three lines
+// depends on the state or on V, so the work splits into:
+//   prep_kernel: one workgroup per (b, h, chunk), fully parallel; writes Wn, Qt and
+//     Kh^T, the lower-triangular fragments of P and -T' (bf16, MFMA operand order),
+//     Gam_last and the validity bits of the chunk's rows to a workspace;
 //   scan_kernel: one workgroup per (b, h, 16-column dv tile); a loop over the
-//     chunks in order with the fp32 state tile in registers, each chunk's
-//     operands streamed into an LDS ring by direct global->LDS copies issued one
-//     chunk ahead of their use.
+//     chunks in order with the fp32 state tile in registers.  Each chunk's operands
+//     are loaded into registers one chunk ahead of their use, and T' V for the next
+//     chunk is formed from V read straight from the input.
 // The factorisation Kt Ki^T (decay relative to the chunk start) is used when
 // every channel's decay over the chunk stays above 2^-120 (then no factor
 // over- or under-flows); otherwise that chunk computes A and P entry by entry
@@ -29,7 +31,7 @@
 // from a product, so nothing from a later position can reach an earlier one.
 //
 // Precision: bf16 MFMA operands that are not exactly bf16 are split into a
-// bf16 high part and a bf16 residual where that matters (A, P, T', S, U, Ut);
+// bf16 high part and a bf16 residual where that matters (A, P, T', S, U);
 // with fp32 inputs every operand is split.
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -43,32 +45,40 @@ constexpr float kFastLimit = -120.0f;    // log2 decay over one chunk for the fa
 constexpr size_t kSinkBytes = 16384;     // workspace tail that absorbs the stores of rows past T
 
 // ---------------------------------------------------------------- workspace layout
-// Per (b, h, chunk), in 2-byte units.  Wn, Qh and Kh^T are in A-operand order of
+// Per (b, h, chunk), in 2-byte units.  Wn, Qt and Kh^T are in A-operand order of
 // v_mfma_f32_16x16x32_bf16: fragment (row tile rt, k step ks) is 64 lanes x 8 bf16
 // (1 KB), lane l holding M[16 rt + l%16][32 ks + 8 (l/16) .. +7]; with fp32 inputs
-// the bf16 residual parts follow the high parts.  Ut and O0 are in accumulator
-// order: block (row tile rt, column tile ct) is 64 lanes x 4 fp32 (1 KB), lane l
-// holding M[16 rt + 4 (l/16) .. +3][16 ct + l%16].
+// the bf16 residual parts follow the high parts.  P and -T' (C x C, lower
+// triangular) keep only the fragments of k steps that reach the diagonal, packed
+// row tile by row tile, as a high part followed by a residual part.
+// Number of k steps (32 columns) that row tile I of a lower-triangular C x C matrix
+// needs, and the packed fragments before row tile I.
+// (row tile I ends at column 16 I + 15, i.e. in k step I/2; the sum of i/2 + 1 over i < I
+// is I + (I/2) ((I-1)/2).)
+__host__ __device__ constexpr int tri_steps(int I) { return I / 2 + 1; }
+__host__ __device__ constexpr int tri_before(int I) { return I + (I / 2) * ((I - 1) / 2); }
+
 template <int K, int V, int C, bool SPLIT>
 struct WsLayout {
   static constexpr size_t kCK = (size_t)C * K;
   static constexpr size_t kSplitCK = SPLIT ? 2 * kCK : kCK;
-  static constexpr size_t kCV = (size_t)C * V * 2;       // fp32 C x V in 2-byte units
+  static constexpr size_t kPF = (size_t)tri_before(C / 16) * 512;  // packed C x C, one part
   static constexpr size_t off_wn = 0;                    // -T' Kt          [C x K]
-  static constexpr size_t off_qh = off_wn + kSplitCK;    // Qt - P T' Kt    [C x K]
-  static constexpr size_t off_kh = off_qh + kSplitCK;    // Kh^T            [K x C]
-  static constexpr size_t off_ut = off_kh + kSplitCK;    // T' V            [C x V] fp32
-  static constexpr size_t off_o0 = off_ut + kCV;         // P T' V          [C x V] fp32
-  static constexpr size_t off_gam = off_o0 + kCV;        // Gam_last        [K] fp32
-  static constexpr size_t kElems = off_gam + 2 * (size_t)K;
+  static constexpr size_t off_qt = off_wn + kSplitCK;    // Qt              [C x K]
+  static constexpr size_t off_kh = off_qt + kSplitCK;    // Kh^T            [K x C]
+  static constexpr size_t off_p = off_kh + kSplitCK;     // P   hi, lo      packed
+  static constexpr size_t off_tn = off_p + 2 * kPF;      // -T' hi, lo      packed
+  static constexpr size_t off_gam = off_tn + 2 * kPF;    // Gam_last        [K] fp32
+  static constexpr size_t off_valid = off_gam + 2 * (size_t)K;   // 4 x 16 row-valid bits
+  static constexpr size_t kElems = off_valid + 8;
 };
 
 __device__ __forceinline__ size_t frag_off(int rt, int ks, int lane, int kk) {
   return ((size_t)(rt * (kk / 32) + ks) * 64 + lane) * 8;
 }
-template <int V>
-__device__ __forceinline__ size_t acc_off(int rt, int ct, int lane) {
-  return ((size_t)(rt * (V / 16) + ct) * 64 + lane) * 8;
+// fragment (row tile I, k step ks) of a packed lower-triangular C x C matrix
+__device__ __forceinline__ size_t tri_off(int I, int ks, int lane) {
+  return ((size_t)(tri_before(I) + ks) * 64 + lane) * 8;
 }
 
 struct PrepParams {
@@ -80,6 +90,7 @@ struct PrepParams {
 };
 
 struct ScanParams {
+  const void* v;
   const float* init_state;
   float* final_state;
   void* o;
@@ -138,16 +149,12 @@ struct PrepLds {
   static constexpr int KP = K + 4, KB = K + 8, CP = C + 4, RT = C / 16;
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
   static constexpr int kParts = SPLIT ? 2 : 1;
-  // R1: Ki hi, lo (fast path) or G (slow path); then T and V^T
-  static constexpr int kTBytes = C * CP * 4;
-  static constexpr int r1 = cmax(cmax(2 * C * KB * 2, C * KP * 4), kTBytes + kParts * V * C * 2);
-  // R2: Kt^T; then Ut^T hi (and lo when it fits)
-  static constexpr int kUtPart = V * C * 2;
-  static constexpr int kKtBytes = kParts * K * C * 2;
-  static constexpr bool kUtLoInR2 = kKtBytes >= 2 * kUtPart;
-  static constexpr int r2 = cmax(kKtBytes, kUtLoInR2 ? 2 * kUtPart : kUtPart);
-  // R3: Kh^T until stored; then A; then Ut^T lo
-  static constexpr int r3 = cmax(cmax(kParts * K * C * 2, C * CP * 4), kUtLoInR2 ? 0 : kUtPart);
+  // R1: Ki hi, lo (fast path) or G (slow path); then T
+  static constexpr int r1 = cmax(cmax(2 * C * KB * 2, C * KP * 4), C * CP * 4);
+  // R2: Kt^T
+  static constexpr int r2 = kParts * K * C * 2;
+  // R3: Kh^T until stored; then A
+  static constexpr int r3 = cmax(kParts * K * C * 2, C * CP * 4);
   // one 16 x 17 fp32 staging tile per wave (the inversion's block exchange)
   static constexpr int kScratch = 4 * 16 * 17;
 };
@@ -176,8 +183,6 @@ prep_kernel(PrepParams p) {
   constexpr int CS = C / 32;          // k steps over chunk rows
   constexpr int KS = K / 32;          // k steps over key channels
   constexpr int KP = Lds::KP, KB = Lds::KB, CP = Lds::CP;
-  constexpr int NVB = (C / 8) * (V / 4);                                 // (8 rows, 4 columns) blocks of V
-  constexpr int NVI = (NVB + kPrepThreads - 1) / kPrepThreads;
   static_assert(RT <= 4, "one row tile per wave");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_r1[Lds::r1];
@@ -190,10 +195,7 @@ prep_kernel(PrepParams p) {
   __bf16* s_ki = reinterpret_cast<__bf16*>(s_r1);                    // [hi, lo][C][KB]
   float* s_G = reinterpret_cast<float*>(s_r1);                       // [C][KP] (slow path)
   float* s_T = reinterpret_cast<float*>(s_r1);                       // [C][CP]
-  __bf16* s_vT = reinterpret_cast<__bf16*>(s_r1 + Lds::kTBytes);     // [hi(, lo)][V][C] swizzled
   __bf16* s_kt = reinterpret_cast<__bf16*>(s_r2);                    // Kt^T [hi(, lo)][K][C] swizzled
-  __bf16* s_uth = reinterpret_cast<__bf16*>(s_r2);                   // [V][C] swizzled
-  __bf16* s_utl = Lds::kUtLoInR2 ? s_uth + V * C : reinterpret_cast<__bf16*>(s_r3);
   __bf16* s_khs = reinterpret_cast<__bf16*>(s_r3);                   // Kh^T [hi(, lo)][K][C] swizzled
   float* s_A = reinterpret_cast<float*>(s_r3);                       // [C][CP]
 
@@ -203,7 +205,6 @@ prep_kernel(PrepParams p) {
   const int dk = p.dk, dv = p.dv;
   const Raw* qg = (const Raw*)p.q;
   const Raw* kg = (const Raw*)p.k;
-  const Raw* vg = (const Raw*)p.v;
   uint16_t* wsb = p.ws + ((size_t)(b * p.H + h) * p.NC + n) * L::kElems;
   auto grow = [&](int t) -> size_t { return ((size_t)b * p.T + t) * p.H + h; };
   auto tsafe = [&](int r) -> int { const int t = t0 + r; return t < p.T ? t : p.T - 1; };
@@ -321,15 +322,14 @@ prep_kernel(PrepParams p) {
 
   // ---- decay factors for this lane's row.  On the fast path every factor lies in
   //      [2^-120, 2^120], so the bare hardware exp2 is exact enough.
-  bf16x8 kth[KS], ktl[KS];
-  float qtf[KS][8];                                                  // Qt, fp32 (A and P take its hi, lo split)
+  bf16x8 kth[KS], ktl[KS], qth[KS], qtl[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int c0 = 32 * ks + cg;
     const bool cok = rok && c0 < dk;
     float pre[8], gc[8];
     tile_sums(ks, pre, gc);
-    float kt[8], ki[8], kh[8], kf[8], qf[8];
+    float kt[8], ki[8], kh[8], qt[8], kf[8], qf[8];
     k_r[ks].to_float(kf);
     q_r[ks].to_float(qf);
 #pragma unroll
@@ -342,10 +342,15 @@ prep_kernel(PrepParams p) {
       kt[e] = kv * gam;
       ki[e] = fast ? kv * __builtin_amdgcn_exp2f(-g) : 0.f;
       kh[e] = kv * __builtin_amdgcn_exp2f(gc[e] - g);
-      qtf[ks][e] = qv * gam;
+      qt[e] = qv * gam;
     }
     split8(kt, kth[ks], ktl[ks]);
+    split8(qt, qth[ks], qtl[ks]);
     if (rows) {
+      // Qt rows to the workspace (invalid rows are 0)
+      const size_t off = frag_off(I, ks, lane, K);
+      store_frag(wsb + L::off_qt + off, qth[ks]);
+      if (SPLIT) store_frag(wsb + L::off_qt + L::kCK + off, qtl[ks]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         s_kt[swz<C>(c0 + e, rq)] = kth[ks][e];
@@ -379,14 +384,10 @@ prep_kernel(PrepParams p) {
     }
   }
 
-  // ---- V: issued now, used after A and P
-  float v_r[NVI][8][4];                                              // rows 8 rb .. +7, columns 4 cb .. +3
-#pragma unroll
-  for (int it = 0; it < NVI; ++it) {
-    const int idx = (tid + kPrepThreads * it) % NVB;
-    const int rb = idx / (V / 4), cb = idx % (V / 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) E::ld4(vg, grow(tsafe(8 * rb + e)) * dv + 4 * cb, v_r[it][e]);
+  // ---- validity of the chunk's rows, 16 bits per row tile (bit r: row 16 I + r)
+  {
+    const unsigned long long bal = __ballot(rok);
+    if (lane == 0) wsb[L::off_valid + I] = rows ? (uint16_t)(bal & 0xffffu) : (uint16_t)0;
   }
   __syncthreads();
 
@@ -410,9 +411,6 @@ prep_kernel(PrepParams p) {
       // transposed products: A-operand rows are Ki rows of column tile J (LDS), B-operand
       // columns are this wave's Kt and Qt rows (registers); lane (g, r) gets columns
       // 16 J + 4 g .. +3 of row rq of A and P
-      bf16x8 qth[KS], qtl[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) split8(qtf[ks], qth[ks], qtl[ks]);
       const float beta_row = s_beta[rq];
 #pragma unroll
       for (int s2 = 0; s2 < CS; ++s2) {
@@ -481,30 +479,17 @@ prep_kernel(PrepParams p) {
       split8(pv, ph[ks], pl[ks]);
     }
   }
-  __syncthreads();                                                   // A complete; Ki or G read
-
-  // ---- V^T (hi, and lo for fp32 inputs) behind T in R1; masked rows as 0
+  // P rows of this wave to the workspace: the k steps that reach the diagonal
+  if (rows) {
 #pragma unroll
-  for (int it = 0; it < NVI; ++it) {
-    const int idx = tid + kPrepThreads * it;
-    if (idx < NVB) {
-      const int rb = idx / (V / 4), cb = idx % (V / 4);
-      bool ok[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ok[e] = s_valid[8 * rb + e] != 0;
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = ok[e] ? v_r[it][e][cc] : 0.f;
-        bf16x8 hi, lo;
-        split8(x, hi, lo);
-        const int at = swz<C>(4 * cb + cc, 8 * rb);
-        *reinterpret_cast<bf16x8*>(&s_vT[at]) = hi;
-        if (SPLIT) *reinterpret_cast<bf16x8*>(&s_vT[V * C + at]) = lo;
-      }
+    for (int s2 = 0; s2 < CS; ++s2) {
+      if (s2 >= tri_steps(I)) continue;
+      const size_t off = tri_off(I, s2, lane);
+      store_frag(wsb + L::off_p + off, ph[s2]);
+      store_frag(wsb + L::off_p + L::kPF + off, pl[s2]);
     }
   }
+  __syncthreads();                                                   // A complete; Ki or G read
 
   // ---- T = (I + A)^-1, blocked: diagonal 16x16 blocks by forward substitution (two
   //      partial sums per row keep the dependency chain short)
@@ -584,9 +569,8 @@ prep_kernel(PrepParams p) {
     __syncthreads();
   }
 
-  // ---- -T' rows of this wave, and M = P T' computed transposed (A operand: columns of
-  //      T', B operand: this wave's P rows), both as A-operand fragments in registers
-  bf16x8 tnh[CS], tnl[CS], mnh[CS], mnl[CS];
+  // ---- -T' rows of this wave as A-operand fragments: to registers and the workspace
+  bf16x8 tnh[CS], tnl[CS];
   if (rows) {
 #pragma unroll
     for (int ks = 0; ks < CS; ++ks) {
@@ -596,153 +580,95 @@ prep_kernel(PrepParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) tv[e] = -tv[e] * s_beta[j0 + e];
       split8(tv, tnh[ks], tnl[ks]);
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < CS; ++s2) {
-      f32x4 mt[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int N = 2 * s2 + t;
-        f32x4 acc = zero4();
-        if (N <= I) {
-          const int jn = 16 * N + (lane % 16);
-#pragma unroll
-          for (int ms = 0; ms < CS; ++ms) {
-            if (32 * ms > 16 * I + 15) continue;                   // P is lower triangular
-            const int m0 = 32 * ms + cg;
-            float tv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) tv[e] = s_T[(m0 + e) * CP + jn] * s_beta[jn];
-            bf16x8 th, tl;
-            split8(tv, th, tl);
-            acc = mfma16(th, ph[ms], acc);
-            if (SPLIT) { acc = mfma16(tl, ph[ms], acc); acc = mfma16(th, pl[ms], acc); }
-          }
-        }
-        mt[t] = acc;
+      if (ks < tri_steps(I)) {
+        const size_t off = tri_off(I, ks, lane);
+        store_frag(wsb + L::off_tn + off, tnh[ks]);
+        store_frag(wsb + L::off_tn + L::kPF + off, tnl[ks]);
       }
-      float mv[8];
-      pair_to_afrag(mt[0], mt[1], mv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mv[e] = -mv[e];
-      split8(mv, mnh[s2], mnl[s2]);
     }
   }
 
-  // ---- Wn = -T' Kt and Qh = Qt - M Kt for this wave's 16 rows, computed transposed
-  //      (A operand: Kt^T rows from LDS, B operand: -T' and -M rows in registers) and
-  //      turned into A-operand fragments by lane swaps
+  // ---- Wn = -T' Kt for this wave's 16 rows, computed transposed (A operand: Kt^T rows
+  //      from LDS, B operand: -T' rows in registers) and turned into A-operand
+  //      fragments by lane swaps
   if (rows) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      f32x4 dw[2], dq[2];
+      f32x4 dw[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int cn = 32 * ks + 16 * t + (lane % 16);
-        f32x4 aw = zero4(), aq = zero4();
+        f32x4 aw = zero4();
 #pragma unroll
         for (int js = 0; js < CS; ++js) {
-          if (32 * js > 16 * I + 15) continue;                     // T' and M are lower triangular
+          if (js >= tri_steps(I)) continue;                          // T' is lower triangular
           const int j0 = 32 * js + cg;
           const bf16x8 kt = *reinterpret_cast<const bf16x8*>(&s_kt[swz<C>(cn, j0)]);
           aw = mfma16(kt, tnh[js], aw);
-          aq = mfma16(kt, mnh[js], aq);
           if (SPLIT) {
             const bf16x8 ktl_b = *reinterpret_cast<const bf16x8*>(&s_kt[K * C + swz<C>(cn, j0)]);
-            aw = mfma16(ktl_b, tnh[js], aw); aw = mfma16(kt, tnl[js], aw);
-            aq = mfma16(ktl_b, mnh[js], aq); aq = mfma16(kt, mnl[js], aq);
+            aw = mfma16(ktl_b, tnh[js], aw);
+            aw = mfma16(kt, tnl[js], aw);
           }
         }
         dw[t] = aw;
-        dq[t] = aq;
       }
-      float wv[8], qv[8];
+      float wv[8];
       pair_to_afrag(dw[0], dw[1], wv);
-      pair_to_afrag(dq[0], dq[1], qv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] += qtf[ks][e];
       bf16x8 hi, lo;
-      const size_t off = frag_off(I, ks, lane, K);
       split8(wv, hi, lo);
+      const size_t off = frag_off(I, ks, lane, K);
       store_frag(wsb + L::off_wn + off, hi);
       if (SPLIT) store_frag(wsb + L::off_wn + L::kCK + off, lo);
-      split8(qv, hi, lo);
-      store_frag(wsb + L::off_qh + off, hi);
-      if (SPLIT) store_frag(wsb + L::off_qh + L::kCK + off, lo);
-    }
-  }
-  __syncthreads();                                                   // Kt and A read: R2, R3 take Ut^T
-
-  // ---- Ut = T' V for this wave's rows, every dv tile: to the workspace, and (hi, lo)
-  //      transposed into LDS
-  if (rows) {
-#pragma unroll
-    for (int N = 0; N < V / 16; ++N) {
-      const int vn = 16 * N + (lane % 16);
-      f32x4 a0 = zero4(), a1 = zero4();
-#pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        if (32 * ks > 16 * I + 15) continue;
-        const int j0 = 32 * ks + cg;
-        const bf16x8 vh = *reinterpret_cast<const bf16x8*>(&s_vT[swz<C>(vn, j0)]);
-        a0 = mfma16(tnh[ks], vh, a0);
-        a1 = mfma16(tnl[ks], vh, a1);
-        if (SPLIT) a1 = mfma16(tnh[ks], *reinterpret_cast<const bf16x8*>(&s_vT[V * C + swz<C>(vn, j0)]), a1);
-      }
-      f32x4 ut;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ut[i] = -(a0[i] + a1[i]);
-      *reinterpret_cast<f32x4*>(wsb + L::off_ut + acc_off<V>(I, N, lane)) = ut;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jr = 16 * I + 4 * (lane / 16) + i;
-        const __bf16 hi = (__bf16)ut[i];
-        s_uth[swz<C>(vn, jr)] = hi;
-        s_utl[swz<C>(vn, jr)] = (__bf16)(ut[i] - (float)hi);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- O0 = P Ut for this wave's rows, every dv tile
-  if (rows) {
-#pragma unroll
-    for (int N = 0; N < V / 16; ++N) {
-      const int vn = 16 * N + (lane % 16);
-      f32x4 a0 = zero4(), a1 = zero4();
-#pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        if (32 * ks > 16 * I + 15) continue;          // P is lower triangular
-        const int j0 = 32 * ks + cg;
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_uth[swz<C>(vn, j0)]);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_utl[swz<C>(vn, j0)]);
-        a0 = mfma16(ph[ks], uh, a0);
-        a1 = mfma16(ph[ks], ul, a1);
-        a1 = mfma16(pl[ks], uh, a1);
-      }
-      f32x4 o0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o0[i] = a0[i] + a1[i];
-      *reinterpret_cast<f32x4*>(wsb + L::off_o0 + acc_off<V>(I, N, lane)) = o0;
     }
   }
 }
 
 // ================================================================ scan kernel
-// One workgroup per (b, h, 16-column dv tile).  Each wave loads the operands it needs for
-// a chunk (its row tile of Wn and Qh, its state row tiles of Kh^T, the tile's Ut and O0
-// blocks, Gam_last) straight into registers one chunk ahead of their use, with an L2
-// warm-up two chunks ahead; LDS only carries the state and U between the waves.
+// One workgroup per (b, h, 16-column dv tile).  Each wave loads what it needs for a
+// chunk (its row tile of Wn, Qt, P and -T', its state row tiles of Kh^T, V of the
+// chunk in the tile's columns, Gam_last) straight into registers one chunk ahead of
+// their use, with an L2 warm-up two chunks ahead; LDS only carries the state and U
+// between the waves.
 template <int K, int C, bool SPLIT>
 struct ScanOps {
   static constexpr int KS = K / 32, CS = C / 32, SPW = (K / 16 + 3) / 4;
-  bf16x8 wn[KS], qh[KS];
-  bf16x8 wnl[SPLIT ? KS : 1], qhl[SPLIT ? KS : 1];
+  bf16x8 wn[KS], qt[KS];
+  bf16x8 wnl[SPLIT ? KS : 1], qtl[SPLIT ? KS : 1];
   bf16x8 kh[SPW][CS];
   bf16x8 khl[SPLIT ? SPW : 1][CS];
-  f32x4 ut, o0;
+  bf16x8 ph[CS], pl[CS];                             // P, this wave's rows
+  bf16x8 th[CS], tl[CS];                             // -T', this wave's rows
   float4 gam[SPW];
 };
+
+// Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, raw addressing.
+constexpr int kBufWord3 = 0x00020000;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// V of one chunk in a 16-column tile, split evenly over the four waves (so every wave
+// issues the same loads): lane l of wave w holds row (C/4) w + l / (256/C), columns
+// (C/16) (l % (256/C)) .. + C/16 - 1.
+template <int C>
+struct VTile {
+  static constexpr int kPerLane = C / 16;            // elements per lane
+  static constexpr int kLanesPerRow = 256 / C;
+  __device__ __forceinline__ static int row(int w, int l) { return (C / 4) * w + l / kLanesPerRow; }
+  __device__ __forceinline__ static int col(int l) { return kPerLane * (l % kLanesPerRow); }
+};
+// kPerLane elements of type Tv at byte offset off (4, 8 or 16 bytes), zero-extended
+template <int BYTES>
+__device__ __forceinline__ u32x4 buffer_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  u32x4 x = {0u, 0u, 0u, 0u};
+  if (BYTES == 16) {
+    x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  } else if (BYTES == 8) {
+    const auto y = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    x[0] = y[0]; x[1] = y[1];
+  } else {
+    x[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  }
+  return x;
+}
 
 // s_barrier with compiler-only fences around it: no memory access moves across
 __device__ __forceinline__ void wg_barrier() {
@@ -757,23 +683,25 @@ __device__ __forceinline__ void wait_lgkm() {
   asm volatile("" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 template <int DT, int K, int V, int C>
 __global__ void __launch_bounds__(kScanThreads)
 scan_kernel(ScanParams p) {
   using E = Elem<DT>;
+  using Tv = typename E::T;
   constexpr bool SPLIT = (DT == 1);
   using L = WsLayout<K, V, C, SPLIT>;
   using Ops = ScanOps<K, C, SPLIT>;
+  using VT = VTile<C>;
   constexpr int RT = C / 16, CS = C / 32, KS = K / 32, SRT = K / 16;
   constexpr int SPW = Ops::SPW;                     // state row tiles per wave
   constexpr int KB = K + 8, CB = C + 8;
   constexpr int kStores = 4;                        // global stores per lane and chunk, always
+  constexpr int kParts = SPLIT ? 2 : 1;
   static_assert(RT <= 4, "one U/O row tile per wave");
 
   __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state hi, lo; B-operand rows = dv column
   __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U hi, lo
+  __shared__ __attribute__((aligned(16))) __bf16 s_vT[kParts][kVT * C]; // V^T (hi, lo) of the next chunk, swizzled
 
   // XCD-aware mapping: all dv tiles of one head share blockIdx.x % 8 (one L2)
   const int L_id = blockIdx.x;
@@ -785,81 +713,154 @@ scan_kernel(ScanParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // uniform: addresses stay scalar
   const int I = wave;                                // this wave's U/O row tile
+  const int nsteps = tri_steps(I);                   // k steps of row tile I that reach the diagonal
   // predicates that the tiling makes always true are compile-time constants, so the
   // loads below are straight-line code and the compiler's waits stay exact
   const bool has_rows = (RT >= 4) || (I < RT);
   auto srow = [&](int M) __attribute__((always_inline)) { return (SRT % 4 == 0) || (M < SRT); };
+  auto tri = [&](int ks) __attribute__((always_inline)) { return ks == 0 || ks < nsteps; };
   const int dk = p.dk, dv = p.dv;
-  typename E::T* og = (typename E::T*)p.o;
-  typename E::T* sink = (typename E::T*)p.sink + (L_id & 63) * 64;
+  const Tv* vg = (const Tv*)p.v;
+  Tv* og = (Tv*)p.o;
+  Tv* sink = (Tv*)p.sink + (L_id & 63) * 64;
   const uint16_t* wsh = p.ws + (size_t)bh * p.NC * L::kElems;
   const int last = p.NC - 1;
+  // tokens are H * dv elements apart in q, k, v and o; byte offsets inside a chunk stay
+  // below 2^32 (checked on the host)
+  const size_t row_bytes = (size_t)p.H * dv * sizeof(Tv);
+  const uint32_t col_bytes = (uint32_t)(((size_t)h * dv + v0 + lane % 16) * sizeof(Tv));
+  auto token_base = [&](int t0) __attribute__((always_inline)) {
+    return ((size_t)b * p.T + t0) * row_bytes;
+  };
+  const int v_row = VT::row(wave, lane), v_col = VT::col(lane);
+  const uint32_t v_off = (uint32_t)v_row * (uint32_t)row_bytes +
+                         (uint32_t)(((size_t)h * dv + v0 + v_col) * sizeof(Tv));
 
   auto ld16 = [&](const uint16_t* src) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(src);
   };
-  // chunk n's operands for this wave, into registers
-  auto load_ops = [&](int n, Ops& op) __attribute__((always_inline)) {
+  // chunk n's V in the tile's columns (this lane's part), through a buffer resource whose
+  // range ends at token T: rows past T read as 0
+  auto load_v = [&](int n) __attribute__((always_inline)) -> u32x4 {
+    const int t0 = n * p.chunk;
+    const unsigned long long span = (unsigned long long)(p.T - t0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<Tv*>(vg) + token_base(t0) / sizeof(Tv), (short)0,
+        (int)(uint32_t)(span < 0xffffffffull ? span : 0xffffffffull), kBufWord3);
+    return buffer_load_words<VT::kPerLane * (int)sizeof(Tv)>(vr, v_off);
+  };
+  // the chunk's row-valid bits (a vector load: a scalar one would share its counter with
+  // the LDS reads, and every wait for those would also wait for it)
+  auto load_valid = [&](int n) __attribute__((always_inline)) -> unsigned long long {
+    return *reinterpret_cast<const unsigned long long*>(wsh + (size_t)n * L::kElems + L::off_valid);
+  };
+  // Chunk n's operands for this wave, into registers.  Every wave issues the same loads
+  // (fragments of P and -T' past a wave's diagonal are loaded from inside the packed
+  // block and never used), so the compiler's wait counts are the same on every path.
+  // The loads are numbered in the order the next chunk step uses them and issued in
+  // small groups spread over the current step (see process), so that no wave ever
+  // waits for room in the CU's load queue: each step moves about 75 KB per CU from L2.
+  constexpr int kLoads = 1 + 2 * KS + 4 * CS + SPW * CS + SPW + (SPLIT ? 2 * KS + SPW * CS : 0);
+  auto issue_load = [&](int idx, int n, Ops& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
     const uint16_t* cb = wsh + (size_t)n * L::kElems;
-    if (has_rows) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        op.wn[ks] = ld16(cb + L::off_wn + frag_off(I, ks, lane, K));
-        op.qh[ks] = ld16(cb + L::off_qh + frag_off(I, ks, lane, K));
-        if (SPLIT) {
-          op.wnl[ks] = ld16(cb + L::off_wn + L::kCK + frag_off(I, ks, lane, K));
-          op.qhl[ks] = ld16(cb + L::off_qh + L::kCK + frag_off(I, ks, lane, K));
-        }
+    int k = idx;
+    if (k == 0) { v = load_v(n); valid = load_valid(n); return; }
+    k -= 1;
+    if (k < 2 * CS) {                                // -T' (hi, lo) of this wave's rows
+      const int ks = k / 2;
+      if (has_rows) {
+        if (k & 1) op.tl[ks] = ld16(cb + L::off_tn + L::kPF + tri_off(I, ks, lane));
+        else op.th[ks] = ld16(cb + L::off_tn + tri_off(I, ks, lane));
       }
-      op.ut = *reinterpret_cast<const f32x4*>(cb + L::off_ut + acc_off<V>(I, tile, lane));
-      op.o0 = *reinterpret_cast<const f32x4*>(cb + L::off_o0 + acc_off<V>(I, tile, lane));
+      return;
     }
+    k -= 2 * CS;
+    if (k < KS) { if (has_rows) op.wn[k] = ld16(cb + L::off_wn + frag_off(I, k, lane, K)); return; }
+    k -= KS;
+    if (k < KS) { if (has_rows) op.qt[k] = ld16(cb + L::off_qt + frag_off(I, k, lane, K)); return; }
+    k -= KS;
+    if (k < SPW * CS) {                              // Kh^T of this wave's state rows
+      const int m = k / CS, ks = k % CS, M = wave + 4 * m;
+      if (srow(M)) op.kh[m][ks] = ld16(cb + L::off_kh + frag_off(M, ks, lane, C));
+      return;
+    }
+    k -= SPW * CS;
+    if (k < SPW) {
+      const int M = wave + 4 * k;
+      if (srow(M)) op.gam[k] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cb + L::off_gam) + 16 * M + 4 * (lane / 16));
+      return;
+    }
+    k -= SPW;
+    if (k < 2 * CS) {                                // P (hi, lo) of this wave's rows
+      const int ks = k / 2;
+      if (has_rows) {
+        if (k & 1) op.pl[ks] = ld16(cb + L::off_p + L::kPF + tri_off(I, ks, lane));
+        else op.ph[ks] = ld16(cb + L::off_p + tri_off(I, ks, lane));
+      }
+      return;
+    }
+    k -= 2 * CS;
+    if (SPLIT) {                                     // residual parts (fp32 inputs)
+      if (k < KS) { if (has_rows) op.wnl[k] = ld16(cb + L::off_wn + L::kCK + frag_off(I, k, lane, K)); return; }
+      k -= KS;
+      if (k < KS) { if (has_rows) op.qtl[k] = ld16(cb + L::off_qt + L::kCK + frag_off(I, k, lane, K)); return; }
+      k -= KS;
+      const int m = k / CS, ks = k % CS, M = wave + 4 * m;
+      if (srow(M)) op.khl[m][ks] = ld16(cb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
+    }
+  };
+  constexpr int kGroups = 8;
+  // group g of the loads of chunk n, pinned in place: the scheduler moves nothing across
+  auto load_group = [&](int g, int n, Ops& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-      const int M = wave + 4 * m;
-      if (srow(M)) {
+    for (int idx = 0; idx < kLoads; ++idx)
+      if (idx * kGroups / kLoads == g) issue_load(idx, n, op, v, valid);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // V^T of a chunk into LDS, rows that are not valid as 0 (their values may be anything)
+  auto write_vt = [&](const u32x4& x, unsigned long long valid) __attribute__((always_inline)) {
+    const bool ok = (valid >> v_row) & 1ull;
 #pragma unroll
-        for (int ks = 0; ks < CS; ++ks) {
-          op.kh[m][ks] = ld16(cb + L::off_kh + frag_off(M, ks, lane, C));
-          if (SPLIT) op.khl[m][ks] = ld16(cb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
-        }
-        op.gam[m] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cb + L::off_gam) + 16 * M + 4 * (lane / 16));
+    for (int e = 0; e < VT::kPerLane; ++e) {
+      if (!SPLIT) {
+        const uint32_t w = ok ? x[e / 2] : 0u;
+        const uint16_t hv = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu));
+        s_vT[0][swz<C>(v_col + e, v_row)] = __builtin_bit_cast(__bf16, hv);
+      } else {
+        const float f = ok ? __uint_as_float(x[e]) : 0.f;
+        const __bf16 hi = (__bf16)f;
+        s_vT[0][swz<C>(v_col + e, v_row)] = hi;
+        s_vT[kParts - 1][swz<C>(v_col + e, v_row)] = (__bf16)(f - (float)hi);
       }
     }
   };
 
   // L2 warm-up two chunks ahead: one 4-byte load per 128-byte line that this workgroup's
-  // loads will read, so they hit in L2.  The loaded word is consumed by an empty asm
-  // statement one chunk later, when it has long arrived, which keeps the load alive
-  // without a wait anywhere else.  Thread g takes line g of the list [its
-  // 1/NT share of the lines every tile reads (Wn, Qh, Kh^T); its tile's Ut and O0 lines; the
-  // Gam_last lines]; threads past the end repeat the first line.
+  // loads will read, so they hit in L2.  It is the last load of its chunk step (waits
+  // complete in issue order, so nothing waits behind its miss), and the loaded word is
+  // consumed by an empty asm statement at the end of the next chunk step (before that
+  // step's stores), when it has long arrived: that keeps the load alive without a wait
+  // on anything recent.  Thread g takes line g of the list [its 1/NT share of
+  // the chunk's workspace lines (every tile reads all of them); the lines of the chunk's
+  // V rows that hold the tile's columns]; threads past the end repeat the first line.
   constexpr int kNT = V / kVT;
-  constexpr int kShLines = (int)(L::off_ut * 2 / 128);
-  constexpr int kOwnLines = 2 * (C / 16) * 8 + (4 * K + 127) / 128;
+  constexpr int kShLines = (int)((L::kElems * 2 + 127) / 128);
   size_t pf_off = 0;                                                   // bytes from the chunk base
+  int pf_row = -1;                                                     // V row, or -1
   {
     const int sh_mine = (kShLines - tile + kNT - 1) / kNT;
     const int g = tid;
-    if (g < sh_mine) {
-      pf_off = (size_t)(tile + kNT * g) * 128;
-    } else if (g - sh_mine < kOwnLines) {
-      const int j = g - sh_mine;
-      if (j < 2 * (C / 16) * 8) {
-        const int blk = j / 8, line = j % 8;
-        const size_t base = blk < C / 16 ? L::off_ut + acc_off<V>(blk, tile, 0)
-                                         : L::off_o0 + acc_off<V>(blk - C / 16, tile, 0);
-        pf_off = base * 2 + (size_t)line * 128;
-      } else {
-        pf_off = L::off_gam * 2 + (size_t)(j - 2 * (C / 16) * 8) * 128;
-      }
-    }
+    if (g < sh_mine) pf_off = (size_t)(tile + kNT * g) * 128;
+    else if (g - sh_mine < C) pf_row = g - sh_mine;
   }
-  uint32_t warm_word = 0;
-  auto warm_chunk = [&](int n) __attribute__((always_inline)) {
-    const unsigned char* cb = reinterpret_cast<const unsigned char*>(wsh + (size_t)n * L::kElems);
-    asm volatile("" :: "v"(warm_word));
-    warm_word = *reinterpret_cast<const uint32_t*>(cb + pf_off);
+  const uint32_t tile_bytes = (uint32_t)(((size_t)h * dv + v0) * sizeof(Tv));
+  auto warm_chunk = [&](int n) __attribute__((always_inline)) -> uint32_t {
+    const unsigned char* ws_line = reinterpret_cast<const unsigned char*>(wsh + (size_t)n * L::kElems) + pf_off;
+    const int t0 = n * p.chunk, tmax = p.T - 1 - t0;
+    const unsigned char* v_line = reinterpret_cast<const unsigned char*>(vg) + token_base(t0) +
+                                  (uint32_t)(pf_row < tmax ? pf_row : tmax) * (uint32_t)row_bytes + tile_bytes;
+    return *reinterpret_cast<const uint32_t*>(pf_row >= 0 ? v_line : ws_line);
   };
 
   // state tiles in registers: wave w owns state row tiles w, w+4, ...
@@ -874,14 +875,11 @@ scan_kernel(ScanParams p) {
                     ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
     }
   }
-  // byte offsets of this lane's output elements from token t0 of the chunk (tokens are
-  // H * dv elements apart; the host keeps these below 2^32)
-  const size_t o_row_bytes = (size_t)p.H * dv * sizeof(typename E::T);
+  // byte offsets of this lane's output elements from token t0 of the chunk
   uint32_t o_lane[kStores];
 #pragma unroll
   for (int i = 0; i < kStores; ++i)
-    o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * o_row_bytes +
-                           ((size_t)h * dv + v0 + lane % 16) * sizeof(typename E::T));
+    o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * row_bytes) + col_bytes;
   auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -898,12 +896,24 @@ scan_kernel(ScanParams p) {
     }
   };
 
-  // one chunk with its operands in registers; ends with exactly kStores global stores per lane
-  auto process = [&](const Ops& op, int n) __attribute__((always_inline)) {
+  // One chunk with its operands in registers and its V^T in LDS; writes the next chunk's
+  // V^T (when there is one) once every wave has read this one; ends with exactly kStores
+  // global stores per lane.
+  auto process = [&](const Ops& op, int n, bool write_next, const u32x4& vnext,
+                     const unsigned long long& valid_next, uint32_t warm_old, auto&& group)
+                     __attribute__((always_inline)) {
     const int t0 = n * p.chunk;
     // every row of a full chunk is in range: its stores need no check
     const bool full = (p.chunk == C) && (t0 + C <= p.T);
-    unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + ((size_t)b * p.T + t0) * o_row_bytes;
+    unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
+    // V^T first: T' V needs nothing else and can start while the state arrives
+    bf16x8 vth[CS], vtl[SPLIT ? CS : 1];
+#pragma unroll
+    for (int ks = 0; ks < CS; ++ks) {
+      const int j0 = 32 * ks + 8 * (lane / 16);
+      vth[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[0][swz<C>(lane % 16, j0)]);
+      if (SPLIT) vtl[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[kParts - 1][swz<C>(lane % 16, j0)]);
+    }
     bf16x8 sh[KS], slo[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -911,107 +921,150 @@ scan_kernel(ScanParams p) {
       sh[ks] = *reinterpret_cast<const bf16x8*>(&s_S[0][(lane % 16) * KB + k0]);
       slo[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(lane % 16) * KB + k0]);
     }
-    // ---- U = Ut + Wn S for this wave's 16 rows (independent accumulators keep the chains short)
+    group(0);
+    f32x4 o4[2] = {zero4(), zero4()};
     if (has_rows) {
-      f32x4 u[4] = {op.ut, zero4(), zero4(), zero4()};
+      // ---- U = T' V + Wn S for this wave's 16 rows (independent accumulators keep the
+      //      chains short; -T' is stored, so T' V enters with a minus sign)
+      f32x4 u[4] = {zero4(), zero4(), zero4(), zero4()};
+      f32x4 tv[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < CS; ++ks) {
+        if (!tri(ks)) continue;                      // T' is lower triangular
+        tv[0] = mfma16(op.th[ks], vth[ks], tv[0]);
+        tv[1] = mfma16(op.tl[ks], vth[ks], tv[1]);
+        if (SPLIT) tv[1] = mfma16(op.th[ks], vtl[ks], tv[1]);
+      }
+      group(1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u[(ks & 1) * 2] = mfma16(op.wn[ks], sh[ks], u[(ks & 1) * 2]);
         u[(ks & 1) * 2 + 1] = mfma16(op.wn[ks], slo[ks], u[(ks & 1) * 2 + 1]);
         if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(op.wnl[ks], sh[ks], u[(ks & 1) * 2 + 1]);
       }
+      group(2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * I + 4 * (lane / 16) + i;
-        const float uv = (u[0][i] + u[2][i]) + (u[1][i] + u[3][i]);
+        const float uv = ((u[0][i] + u[2][i]) + (u[1][i] + u[3][i])) - (tv[0][i] + tv[1][i]);
         const __bf16 hi = (__bf16)uv;
         s_U[0][(lane % 16) * CB + rr] = hi;
         s_U[1][(lane % 16) * CB + rr] = (__bf16)(uv - (float)hi);
       }
-    }
-    wait_lgkm();
-    wg_barrier();                                                      // U visible; S reads done
-
-    // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
-    {
-      bf16x8 uh[CS], ul[CS];
-#pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        const int j0 = 32 * ks + 8 * (lane / 16);
-        uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
-        ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
-      }
-#pragma unroll
-      for (int m = 0; m < SPW; ++m) {
-        const int M = wave + 4 * m;
-        if (!srow(M)) continue;
-        f32x4 a0 = zero4(), a1 = zero4();
-#pragma unroll
-        for (int ks = 0; ks < CS; ++ks) {
-          a0 = mfma16(op.kh[m][ks], uh[ks], a0);
-          a1 = mfma16(op.kh[m][ks], ul[ks], a1);
-          if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
-        }
-        const float gg[4] = {op.gam[m].x, op.gam[m].y, op.gam[m].z, op.gam[m].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
-      }
-    }
-    publish_state();
-
-    // ---- O = O0 + Qh S (the state entering the chunk, still in fragments)
-    if (has_rows) {
-      f32x4 o4[2] = {op.o0, zero4()};
+      group(3);
+      // ---- O, first part: Qt S (the state entering the chunk), while U lands in LDS
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        o4[ks & 1] = mfma16(op.qh[ks], sh[ks], o4[ks & 1]);
-        o4[ks & 1] = mfma16(op.qh[ks], slo[ks], o4[ks & 1]);
-        if (SPLIT) o4[ks & 1] = mfma16(op.qhl[ks], sh[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(op.qt[ks], sh[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(op.qt[ks], slo[ks], o4[ks & 1]);
+        if (SPLIT) o4[ks & 1] = mfma16(op.qtl[ks], sh[ks], o4[ks & 1]);
+      }
+    } else {
+      group(1); group(2); group(3);
+    }
+    group(4);
+    wait_lgkm();
+    wg_barrier();                                    // U visible; S and V^T reads done
+
+    bf16x8 uh[CS], ul[CS];
+#pragma unroll
+    for (int ks = 0; ks < CS; ++ks) {
+      const int j0 = 32 * ks + 8 * (lane / 16);
+      uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
+      ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
+    }
+    group(5);
+    // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int M = wave + 4 * m;
+      if (!srow(M)) continue;
+      f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+      for (int ks = 0; ks < CS; ++ks) {
+        a0 = mfma16(op.kh[m][ks], uh[ks], a0);
+        a1 = mfma16(op.kh[m][ks], ul[ks], a1);
+        if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
+      }
+      const float gg[4] = {op.gam[m].x, op.gam[m].y, op.gam[m].z, op.gam[m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
+    }
+    group(6);
+    publish_state();
+    if (write_next) write_vt(vnext, valid_next);
+    group(7);
+    group(8);                                        // the L2 warm-up: always the last load
+    asm volatile("" :: "v"(warm_old));              // the warm-up load of two steps back
+    if (has_rows) {
+      // ---- O, second part: P U (P is lower triangular)
+#pragma unroll
+      for (int ks = 0; ks < CS; ++ks) {
+        if (!tri(ks)) continue;
+        o4[ks & 1] = mfma16(op.ph[ks], uh[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(op.ph[ks], ul[ks], o4[ks & 1]);
+        o4[ks & 1] = mfma16(op.pl[ks], uh[ks], o4[ks & 1]);
       }
 #pragma unroll
       for (int i = 0; i < kStores; ++i) {
         const int rr = 16 * I + 4 * (lane / 16) + i;
-        typename E::T* dst = reinterpret_cast<typename E::T*>(ochunk + o_lane[i]);
+        Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i]);
         if (!full && !(rr < p.chunk && t0 + rr < p.T)) dst = sink + 16 * i + (lane % 16);
         E::st(dst, 0, o4[0][i] + o4[1][i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < kStores; ++i) {                             // keep the store count uniform
-        volatile typename E::T* dst = sink + 16 * i + (lane % 16);
-        *dst = (typename E::T)0;
+        volatile Tv* dst = sink + 16 * i + (lane % 16);
+        *dst = (Tv)0;
       }
     }
   };
 
   publish_state();
-  // Operands of chunk n are loaded at the top of chunk n - 1 (the first ones here), the
-  // L2 warm-up for chunk n + 1 beside them; loads into the registers of one buffer are
-  // issued only after the previous chunk that used that buffer is done with it.
-  // The loop body holds two chunks with no condition between them, so each buffer keeps
-  // its own registers and the compiler's waits stay exact.
+  // Operands of chunk n are loaded during chunk n - 1 (the first ones here), the L2
+  // warm-up for chunk n + 1 after them; chunk n's V^T is written to LDS during chunk
+  // n - 1.  Loads into the registers of one buffer are issued only after the previous
+  // chunk that used that buffer is done with it.  The loop body holds two chunks with no
+  // condition between them, so each buffer keeps its own registers and the compiler's
+  // waits stay exact.
   Ops opA, opB;
-  if (p.NC > 0) load_ops(0, opA);
-  if (p.NC > 1) warm_chunk(1);
+  uint32_t warmA = 0, warmB = 0;
+  if (p.NC > 0) {
+    u32x4 v;
+    unsigned long long valid;
+#pragma unroll
+    for (int idx = 0; idx < kLoads; ++idx) issue_load(idx, 0, opA, v, valid);
+    write_vt(v, valid);
+  }
+  if (p.NC > 1) warmB = warm_chunk(1);
   int n = 0;
   for (; n + 1 < p.NC; n += 2) {
     wait_lgkm();
-    wg_barrier();                                                      // state visible
-    load_ops(n + 1, opB);
-    warm_chunk(n + 2 <= last ? n + 2 : last);
-    process(opA, n);
+    wg_barrier();                                    // state and V^T visible
+    u32x4 vB;
+    unsigned long long validB;
+    process(opA, n, true, vB, validB, warmB, [&](int g) __attribute__((always_inline)) {
+      if (g < kGroups) load_group(g, n + 1, opB, vB, validB);
+      else warmA = warm_chunk(n + 2 <= last ? n + 2 : last);
+    });
     wait_lgkm();
     wg_barrier();
-    load_ops(n + 2 <= last ? n + 2 : last, opA);
-    warm_chunk(n + 3 <= last ? n + 3 : last);
-    process(opB, n + 1);
+    const int nn = n + 2 <= last ? n + 2 : last;
+    u32x4 vA;
+    unsigned long long validA;
+    process(opB, n + 1, true, vA, validA, warmA, [&](int g) __attribute__((always_inline)) {
+      if (g < kGroups) load_group(g, nn, opA, vA, validA);
+      else warmB = warm_chunk(n + 3 <= last ? n + 3 : last);
+    });
   }
-  if (n < p.NC) {                                                      // odd chunk count: the last one
+  if (n < p.NC) {                                    // odd chunk count: the last one
     wait_lgkm();
     wg_barrier();
-    process(opA, n);
+    const u32x4 none = {0u, 0u, 0u, 0u};
+    process(opA, n, false, none, 0ull, warmB, [](int) {});
   }
-  asm volatile("" :: "v"(warm_word));
+  asm volatile("" :: "v"(warmA), "v"(warmB));
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---- final state
@@ -1081,7 +1134,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  ScanParams sp{a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
+  ScanParams sp{a.v, a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
                 NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr,
                 a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
   const int groups = (nbh + 7) / 8;
