@@ -39,7 +39,7 @@
 namespace kda {
 
 constexpr int kPrepThreads = 256;
-constexpr int kScanThreads = 256;
+constexpr int kScanThreads = 512;
 constexpr int kVT = 16;                  // dv columns per scan workgroup
 constexpr float kFastLimit = -120.0f;    // log2 decay over one chunk for the factorised path
 constexpr size_t kSinkBytes = 16384;     // workspace tail that absorbs the stores of rows past T
@@ -625,29 +625,41 @@ prep_kernel(PrepParams p) {
 }
 
 // ================================================================ scan kernel
-// One workgroup per (b, h, 16-column dv tile).  Each wave loads what it needs for a
-// chunk (its row tile of Wn, Qt, P and -T', its state row tiles of Kh^T, V of the
-// chunk in the tile's columns, Gam_last) straight into registers one chunk ahead of
-// their use, with an L2 warm-up two chunks ahead; LDS only carries the state and U
-// between the waves.
+// One workgroup per (b, h, 16-column dv tile), eight waves in two roles.
+//   Waves 0-3 carry the state: wave w owns state row tiles w, w+4, ... and row tile w of
+//   U.  Per chunk: T' V and U = T' V + Wn S, U exchanged through LDS, then
+//   S <- Diag(Gam_last) S + Kh^T U, published to LDS for the next chunk.
+//   Waves 4-7 form the output: wave 4 + I computes O = Qt S + P U for row tile I from
+//   the same S and U in LDS and stores it.  Nothing of O feeds the next chunk, so it
+//   runs beside the state chain instead of lengthening it.
+// Every wave loads what it needs for the next chunk into registers during the current
+// one, in small groups spread over the step (the CU moves about 75 KB of operands per
+// step from L2, and a wave that issues a burst of loads waits for room in the load
+// queue), with an L2 warm-up two chunks ahead.  Each step has two barriers, which all
+// eight waves join: one when U is in LDS, one when the next state and V^T are.
 template <int K, int C, bool SPLIT>
-struct ScanOps {
+struct ChainOps {
   static constexpr int KS = K / 32, CS = C / 32, SPW = (K / 16 + 3) / 4;
-  bf16x8 wn[KS], qt[KS];
-  bf16x8 wnl[SPLIT ? KS : 1], qtl[SPLIT ? KS : 1];
+  bf16x8 wn[KS];
+  bf16x8 wnl[SPLIT ? KS : 1];
   bf16x8 kh[SPW][CS];
   bf16x8 khl[SPLIT ? SPW : 1][CS];
-  bf16x8 ph[CS], pl[CS];                             // P, this wave's rows
   bf16x8 th[CS], tl[CS];                             // -T', this wave's rows
   float4 gam[SPW];
+};
+template <int K, int C, bool SPLIT>
+struct OutOps {
+  static constexpr int KS = K / 32, CS = C / 32;
+  bf16x8 qt[KS];
+  bf16x8 qtl[SPLIT ? KS : 1];
+  bf16x8 ph[CS], pl[CS];                             // P, this wave's rows
 };
 
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, raw addressing.
 constexpr int kBufWord3 = 0x00020000;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// V of one chunk in a 16-column tile, split evenly over the four waves (so every wave
-// issues the same loads): lane l of wave w holds row (C/4) w + l / (256/C), columns
-// (C/16) (l % (256/C)) .. + C/16 - 1.
+// V of one chunk in a 16-column tile, split evenly over the four state waves: lane l of
+// wave w holds row (C/4) w + l / (256/C), columns (C/16) (l % (256/C)) .. + C/16 - 1.
 template <int C>
 struct VTile {
   static constexpr int kPerLane = C / 16;            // elements per lane
@@ -655,7 +667,7 @@ struct VTile {
   __device__ __forceinline__ static int row(int w, int l) { return (C / 4) * w + l / kLanesPerRow; }
   __device__ __forceinline__ static int col(int l) { return kPerLane * (l % kLanesPerRow); }
 };
-// kPerLane elements of type Tv at byte offset off (4, 8 or 16 bytes), zero-extended
+// 4, 8 or 16 bytes at byte offset off of a buffer resource, zero-extended
 template <int BYTES>
 __device__ __forceinline__ u32x4 buffer_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   u32x4 x = {0u, 0u, 0u, 0u};
@@ -682,6 +694,13 @@ __device__ __forceinline__ void wait_lgkm() {
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
 }
+// loads issued in place: the scheduler moves nothing across either side
+template <typename F>
+__device__ __forceinline__ void pinned(F&& f) {
+  __builtin_amdgcn_sched_barrier(0);
+  f();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 template <int DT, int K, int V, int C>
 __global__ void __launch_bounds__(kScanThreads)
@@ -690,10 +709,11 @@ scan_kernel(ScanParams p) {
   using Tv = typename E::T;
   constexpr bool SPLIT = (DT == 1);
   using L = WsLayout<K, V, C, SPLIT>;
-  using Ops = ScanOps<K, C, SPLIT>;
+  using Ch = ChainOps<K, C, SPLIT>;
+  using Ou = OutOps<K, C, SPLIT>;
   using VT = VTile<C>;
   constexpr int RT = C / 16, CS = C / 32, KS = K / 32, SRT = K / 16;
-  constexpr int SPW = Ops::SPW;                     // state row tiles per wave
+  constexpr int SPW = Ch::SPW;                      // state row tiles per state wave
   constexpr int KB = K + 8, CB = C + 8;
   constexpr int kStores = 4;                        // global stores per lane and chunk, always
   constexpr int kParts = SPLIT ? 2 : 1;
@@ -712,7 +732,7 @@ scan_kernel(ScanParams p) {
   const int v0 = tile * kVT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // uniform: addresses stay scalar
-  const int I = wave;                                // this wave's U/O row tile
+  const int I = wave & 3;                            // row tile (and first state row tile)
   const int nsteps = tri_steps(I);                   // k steps of row tile I that reach the diagonal
   // predicates that the tiling makes always true are compile-time constants, so the
   // loads below are straight-line code and the compiler's waits stay exact
@@ -720,9 +740,6 @@ scan_kernel(ScanParams p) {
   auto srow = [&](int M) __attribute__((always_inline)) { return (SRT % 4 == 0) || (M < SRT); };
   auto tri = [&](int ks) __attribute__((always_inline)) { return ks == 0 || ks < nsteps; };
   const int dk = p.dk, dv = p.dv;
-  const Tv* vg = (const Tv*)p.v;
-  Tv* og = (Tv*)p.o;
-  Tv* sink = (Tv*)p.sink + (L_id & 63) * 64;
   const uint16_t* wsh = p.ws + (size_t)bh * p.NC * L::kElems;
   const int last = p.NC - 1;
   // tokens are H * dv elements apart in q, k, v and o; byte offsets inside a chunk stay
@@ -732,13 +749,126 @@ scan_kernel(ScanParams p) {
   auto token_base = [&](int t0) __attribute__((always_inline)) {
     return ((size_t)b * p.T + t0) * row_bytes;
   };
-  const int v_row = VT::row(wave, lane), v_col = VT::col(lane);
-  const uint32_t v_off = (uint32_t)v_row * (uint32_t)row_bytes +
-                         (uint32_t)(((size_t)h * dv + v0 + v_col) * sizeof(Tv));
-
   auto ld16 = [&](const uint16_t* src) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(src);
   };
+  // the state entering the chunk and U, as B-operand fragments (hi, lo) from LDS
+  auto read_state = [&](bf16x8* sh, bf16x8* slo) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k0 = 32 * ks + 8 * (lane / 16);
+      sh[ks] = *reinterpret_cast<const bf16x8*>(&s_S[0][(lane % 16) * KB + k0]);
+      slo[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(lane % 16) * KB + k0]);
+    }
+  };
+  auto read_u = [&](bf16x8* uh, bf16x8* ul) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < CS; ++ks) {
+      const int j0 = 32 * ks + 8 * (lane / 16);
+      uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
+      ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
+    }
+  };
+
+  if (wave >= 4) {
+    // ================= output waves: O = Qt S + P U for row tile I
+    // Loads in the order the next step uses them, except that the P fragments past this
+    // wave's diagonal are not loaded at all, and the ones that may be skipped come first
+    // (so the waits for the others do not depend on the branch).
+    auto load_out = [&](int part, int n, Ou& o) __attribute__((always_inline)) {
+      const uint16_t* cb = wsh + (size_t)n * L::kElems;
+      if (!has_rows) return;
+      if (part == 0) {
+#pragma unroll
+        for (int ks = 1; ks < CS; ++ks) {
+          if (!tri(ks)) continue;
+          o.ph[ks] = ld16(cb + L::off_p + tri_off(I, ks, lane));
+          o.pl[ks] = ld16(cb + L::off_p + L::kPF + tri_off(I, ks, lane));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) o.qt[ks] = ld16(cb + L::off_qt + frag_off(I, ks, lane, K));
+      } else {
+        o.ph[0] = ld16(cb + L::off_p + tri_off(I, 0, lane));
+        o.pl[0] = ld16(cb + L::off_p + L::kPF + tri_off(I, 0, lane));
+        if (SPLIT) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) o.qtl[ks] = ld16(cb + L::off_qt + L::kCK + frag_off(I, ks, lane, K));
+        }
+      }
+    };
+    Tv* og = (Tv*)p.o;
+    Tv* sink = (Tv*)p.sink + (L_id & 63) * 64;
+    uint32_t o_lane[kStores];
+#pragma unroll
+    for (int i = 0; i < kStores; ++i)
+      o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * row_bytes) + col_bytes;
+    auto out_step = [&](const Ou& o, int n, auto&& loads) __attribute__((always_inline)) {
+      const int t0 = n * p.chunk;
+      const bool full = (p.chunk == C) && (t0 + C <= p.T);         // every row in range
+      unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
+      bf16x8 sh[KS], slo[KS];
+      read_state(sh, slo);
+      pinned([&] { loads(0); });
+      f32x4 o4[2] = {zero4(), zero4()};
+      if (has_rows) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          o4[ks & 1] = mfma16(o.qt[ks], sh[ks], o4[ks & 1]);
+          o4[ks & 1] = mfma16(o.qt[ks], slo[ks], o4[ks & 1]);
+          if (SPLIT) o4[ks & 1] = mfma16(o.qtl[ks], sh[ks], o4[ks & 1]);
+        }
+      }
+      pinned([&] { loads(1); });
+      wait_lgkm();
+      wg_barrier();                                  // U in LDS
+      bf16x8 uh[CS], ul[CS];
+      read_u(uh, ul);
+      if (has_rows) {
+#pragma unroll
+        for (int ks = 0; ks < CS; ++ks) {
+          if (!tri(ks)) continue;                    // P is lower triangular
+          o4[ks & 1] = mfma16(o.ph[ks], uh[ks], o4[ks & 1]);
+          o4[ks & 1] = mfma16(o.ph[ks], ul[ks], o4[ks & 1]);
+          o4[ks & 1] = mfma16(o.pl[ks], uh[ks], o4[ks & 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < kStores; ++i) {
+          const int rr = 16 * I + 4 * (lane / 16) + i;
+          Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i]);
+          if (!full && !(rr < p.chunk && t0 + rr < p.T)) dst = sink + 16 * i + (lane % 16);
+          E::st(dst, 0, o4[0][i] + o4[1][i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kStores; ++i) {                           // keep the store count uniform
+          volatile Tv* dst = sink + 16 * i + (lane % 16);
+          *dst = (Tv)0;
+        }
+      }
+      wait_lgkm();
+      wg_barrier();                                  // next state and V^T in LDS
+    };
+
+    Ou oA, oB;
+    if (p.NC > 0) { load_out(0, 0, oA); load_out(1, 0, oA); }
+    wg_barrier();                                    // initial state and V^T in LDS
+    int n = 0;
+    for (; n + 1 < p.NC; n += 2) {
+      out_step(oA, n, [&](int part) __attribute__((always_inline)) { load_out(part, n + 1, oB); });
+      const int nn = n + 2 <= last ? n + 2 : last;
+      out_step(oB, n + 1, [&](int part) __attribute__((always_inline)) { load_out(part, nn, oA); });
+    }
+    if (n < p.NC) out_step(oA, n, [](int) {});
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  // ================= state waves
+  __builtin_amdgcn_s_setprio(2);                     // issue ahead of the output waves
+  const Tv* vg = (const Tv*)p.v;
+  const int v_row = VT::row(wave, lane), v_col = VT::col(lane);
+  const uint32_t v_off = (uint32_t)v_row * (uint32_t)row_bytes +
+                         (uint32_t)(((size_t)h * dv + v0 + v_col) * sizeof(Tv));
   // chunk n's V in the tile's columns (this lane's part), through a buffer resource whose
   // range ends at token T: rows past T read as 0
   auto load_v = [&](int n) __attribute__((always_inline)) -> u32x4 {
@@ -753,70 +883,6 @@ scan_kernel(ScanParams p) {
   // the LDS reads, and every wait for those would also wait for it)
   auto load_valid = [&](int n) __attribute__((always_inline)) -> unsigned long long {
     return *reinterpret_cast<const unsigned long long*>(wsh + (size_t)n * L::kElems + L::off_valid);
-  };
-  // Chunk n's operands for this wave, into registers.  Every wave issues the same loads
-  // (fragments of P and -T' past a wave's diagonal are loaded from inside the packed
-  // block and never used), so the compiler's wait counts are the same on every path.
-  // The loads are numbered in the order the next chunk step uses them and issued in
-  // small groups spread over the current step (see process), so that no wave ever
-  // waits for room in the CU's load queue: each step moves about 75 KB per CU from L2.
-  constexpr int kLoads = 1 + 2 * KS + 4 * CS + SPW * CS + SPW + (SPLIT ? 2 * KS + SPW * CS : 0);
-  auto issue_load = [&](int idx, int n, Ops& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
-    const uint16_t* cb = wsh + (size_t)n * L::kElems;
-    int k = idx;
-    if (k == 0) { v = load_v(n); valid = load_valid(n); return; }
-    k -= 1;
-    if (k < 2 * CS) {                                // -T' (hi, lo) of this wave's rows
-      const int ks = k / 2;
-      if (has_rows) {
-        if (k & 1) op.tl[ks] = ld16(cb + L::off_tn + L::kPF + tri_off(I, ks, lane));
-        else op.th[ks] = ld16(cb + L::off_tn + tri_off(I, ks, lane));
-      }
-      return;
-    }
-    k -= 2 * CS;
-    if (k < KS) { if (has_rows) op.wn[k] = ld16(cb + L::off_wn + frag_off(I, k, lane, K)); return; }
-    k -= KS;
-    if (k < KS) { if (has_rows) op.qt[k] = ld16(cb + L::off_qt + frag_off(I, k, lane, K)); return; }
-    k -= KS;
-    if (k < SPW * CS) {                              // Kh^T of this wave's state rows
-      const int m = k / CS, ks = k % CS, M = wave + 4 * m;
-      if (srow(M)) op.kh[m][ks] = ld16(cb + L::off_kh + frag_off(M, ks, lane, C));
-      return;
-    }
-    k -= SPW * CS;
-    if (k < SPW) {
-      const int M = wave + 4 * k;
-      if (srow(M)) op.gam[k] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cb + L::off_gam) + 16 * M + 4 * (lane / 16));
-      return;
-    }
-    k -= SPW;
-    if (k < 2 * CS) {                                // P (hi, lo) of this wave's rows
-      const int ks = k / 2;
-      if (has_rows) {
-        if (k & 1) op.pl[ks] = ld16(cb + L::off_p + L::kPF + tri_off(I, ks, lane));
-        else op.ph[ks] = ld16(cb + L::off_p + tri_off(I, ks, lane));
-      }
-      return;
-    }
-    k -= 2 * CS;
-    if (SPLIT) {                                     // residual parts (fp32 inputs)
-      if (k < KS) { if (has_rows) op.wnl[k] = ld16(cb + L::off_wn + L::kCK + frag_off(I, k, lane, K)); return; }
-      k -= KS;
-      if (k < KS) { if (has_rows) op.qtl[k] = ld16(cb + L::off_qt + L::kCK + frag_off(I, k, lane, K)); return; }
-      k -= KS;
-      const int m = k / CS, ks = k % CS, M = wave + 4 * m;
-      if (srow(M)) op.khl[m][ks] = ld16(cb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
-    }
-  };
-  constexpr int kGroups = 8;
-  // group g of the loads of chunk n, pinned in place: the scheduler moves nothing across
-  auto load_group = [&](int g, int n, Ops& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int idx = 0; idx < kLoads; ++idx)
-      if (idx * kGroups / kLoads == g) issue_load(idx, n, op, v, valid);
-    __builtin_amdgcn_sched_barrier(0);
   };
   // V^T of a chunk into LDS, rows that are not valid as 0 (their values may be anything)
   auto write_vt = [&](const u32x4& x, unsigned long long valid) __attribute__((always_inline)) {
@@ -835,15 +901,74 @@ scan_kernel(ScanParams p) {
       }
     }
   };
+  // Chunk n's operands for this wave, into registers, numbered in the order the next
+  // step uses them; the -T' fragments past this wave's diagonal are not loaded, and the
+  // ones that may be skipped come right after V (so the waits for everything later do
+  // not depend on the branch).
+  constexpr int kLoads = 1 + 2 * CS + KS + SPW * CS + SPW + (SPLIT ? KS + SPW * CS : 0);
+  auto issue_load = [&](int idx, int n, Ch& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
+    const uint16_t* cb = wsh + (size_t)n * L::kElems;
+    int k = idx;
+    if (k == 0) {
+      v = load_v(n);
+      valid = load_valid(n);
+      if (has_rows) {
+#pragma unroll
+        for (int ks = 1; ks < CS; ++ks) {
+          if (!tri(ks)) continue;
+          op.th[ks] = ld16(cb + L::off_tn + tri_off(I, ks, lane));
+          op.tl[ks] = ld16(cb + L::off_tn + L::kPF + tri_off(I, ks, lane));
+        }
+      }
+      return;
+    }
+    k -= 1;
+    if (k < 2 * CS) {                                // k steps >= 1 were loaded with V
+      if (has_rows && k < 2) {
+        if (k & 1) op.tl[0] = ld16(cb + L::off_tn + L::kPF + tri_off(I, 0, lane));
+        else op.th[0] = ld16(cb + L::off_tn + tri_off(I, 0, lane));
+      }
+      return;
+    }
+    k -= 2 * CS;
+    if (k < KS) { if (has_rows) op.wn[k] = ld16(cb + L::off_wn + frag_off(I, k, lane, K)); return; }
+    k -= KS;
+    if (k < SPW * CS) {                              // Kh^T of this wave's state rows
+      const int m = k / CS, ks = k % CS, M = wave + 4 * m;
+      if (srow(M)) op.kh[m][ks] = ld16(cb + L::off_kh + frag_off(M, ks, lane, C));
+      return;
+    }
+    k -= SPW * CS;
+    if (k < SPW) {
+      const int M = wave + 4 * k;
+      if (srow(M)) op.gam[k] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cb + L::off_gam) + 16 * M + 4 * (lane / 16));
+      return;
+    }
+    k -= SPW;
+    if (SPLIT) {                                     // residual parts (fp32 inputs)
+      if (k < KS) { if (has_rows) op.wnl[k] = ld16(cb + L::off_wn + L::kCK + frag_off(I, k, lane, K)); return; }
+      k -= KS;
+      const int m = k / CS, ks = k % CS, M = wave + 4 * m;
+      if (srow(M)) op.khl[m][ks] = ld16(cb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
+    }
+  };
+  constexpr int kGroups = 6;
+  auto load_group = [&](int g, int n, Ch& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
+    pinned([&] {
+#pragma unroll
+      for (int idx = 0; idx < kLoads; ++idx)
+        if (idx * kGroups / kLoads == g) issue_load(idx, n, op, v, valid);
+    });
+  };
 
-  // L2 warm-up two chunks ahead: one 4-byte load per 128-byte line that this workgroup's
+  // L2 warm-up two chunks ahead: one 4-byte load per 128-byte line that the workgroup's
   // loads will read, so they hit in L2.  It is the last load of its chunk step (waits
   // complete in issue order, so nothing waits behind its miss), and the loaded word is
-  // consumed by an empty asm statement at the end of the next chunk step (before that
-  // step's stores), when it has long arrived: that keeps the load alive without a wait
-  // on anything recent.  Thread g takes line g of the list [its 1/NT share of
-  // the chunk's workspace lines (every tile reads all of them); the lines of the chunk's
-  // V rows that hold the tile's columns]; threads past the end repeat the first line.
+  // consumed by an empty asm statement at the end of the next chunk step, when it has
+  // long arrived: that keeps the load alive without a wait on anything recent.  Thread g
+  // of the state waves takes line g of the list [its 1/NT share of the chunk's workspace
+  // lines (every tile reads all of them); the lines of the chunk's V rows that hold the
+  // tile's columns]; threads past the end repeat the first line.
   constexpr int kNT = V / kVT;
   constexpr int kShLines = (int)((L::kElems * 2 + 127) / 128);
   size_t pf_off = 0;                                                   // bytes from the chunk base
@@ -875,11 +1000,6 @@ scan_kernel(ScanParams p) {
                     ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
     }
   }
-  // byte offsets of this lane's output elements from token t0 of the chunk
-  uint32_t o_lane[kStores];
-#pragma unroll
-  for (int i = 0; i < kStores; ++i)
-    o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * row_bytes) + col_bytes;
   auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -896,16 +1016,11 @@ scan_kernel(ScanParams p) {
     }
   };
 
-  // One chunk with its operands in registers and its V^T in LDS; writes the next chunk's
-  // V^T (when there is one) once every wave has read this one; ends with exactly kStores
-  // global stores per lane.
-  auto process = [&](const Ops& op, int n, bool write_next, const u32x4& vnext,
-                     const unsigned long long& valid_next, uint32_t warm_old, auto&& group)
-                     __attribute__((always_inline)) {
-    const int t0 = n * p.chunk;
-    // every row of a full chunk is in range: its stores need no check
-    const bool full = (p.chunk == C) && (t0 + C <= p.T);
-    unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
+  // One chunk step: operands in registers, V^T and S in LDS.  Writes the next chunk's
+  // V^T (when there is one) after every wave has read this one.
+  auto chain_step = [&](const Ch& op, int n, bool write_next, const u32x4& vnext,
+                        const unsigned long long& valid_next, uint32_t warm_old, auto&& group)
+                        __attribute__((always_inline)) {
     // V^T first: T' V needs nothing else and can start while the state arrives
     bf16x8 vth[CS], vtl[SPLIT ? CS : 1];
 #pragma unroll
@@ -915,14 +1030,8 @@ scan_kernel(ScanParams p) {
       if (SPLIT) vtl[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[kParts - 1][swz<C>(lane % 16, j0)]);
     }
     bf16x8 sh[KS], slo[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int k0 = 32 * ks + 8 * (lane / 16);
-      sh[ks] = *reinterpret_cast<const bf16x8*>(&s_S[0][(lane % 16) * KB + k0]);
-      slo[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(lane % 16) * KB + k0]);
-    }
+    read_state(sh, slo);
     group(0);
-    f32x4 o4[2] = {zero4(), zero4()};
     if (has_rows) {
       // ---- U = T' V + Wn S for this wave's 16 rows (independent accumulators keep the
       //      chains short; -T' is stored, so T' V enters with a minus sign)
@@ -951,29 +1060,14 @@ scan_kernel(ScanParams p) {
         s_U[0][(lane % 16) * CB + rr] = hi;
         s_U[1][(lane % 16) * CB + rr] = (__bf16)(uv - (float)hi);
       }
-      group(3);
-      // ---- O, first part: Qt S (the state entering the chunk), while U lands in LDS
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        o4[ks & 1] = mfma16(op.qt[ks], sh[ks], o4[ks & 1]);
-        o4[ks & 1] = mfma16(op.qt[ks], slo[ks], o4[ks & 1]);
-        if (SPLIT) o4[ks & 1] = mfma16(op.qtl[ks], sh[ks], o4[ks & 1]);
-      }
     } else {
-      group(1); group(2); group(3);
+      group(1); group(2);
     }
-    group(4);
     wait_lgkm();
-    wg_barrier();                                    // U visible; S and V^T reads done
-
+    wg_barrier();                                    // U in LDS; S and V^T reads done
     bf16x8 uh[CS], ul[CS];
-#pragma unroll
-    for (int ks = 0; ks < CS; ++ks) {
-      const int j0 = 32 * ks + 8 * (lane / 16);
-      uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
-      ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
-    }
-    group(5);
+    read_u(uh, ul);
+    group(3);
     // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -990,45 +1084,18 @@ scan_kernel(ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
     }
-    group(6);
+    group(4);
     publish_state();
     if (write_next) write_vt(vnext, valid_next);
-    group(7);
-    group(8);                                        // the L2 warm-up: always the last load
-    asm volatile("" :: "v"(warm_old));              // the warm-up load of two steps back
-    if (has_rows) {
-      // ---- O, second part: P U (P is lower triangular)
-#pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        if (!tri(ks)) continue;
-        o4[ks & 1] = mfma16(op.ph[ks], uh[ks], o4[ks & 1]);
-        o4[ks & 1] = mfma16(op.ph[ks], ul[ks], o4[ks & 1]);
-        o4[ks & 1] = mfma16(op.pl[ks], uh[ks], o4[ks & 1]);
-      }
-#pragma unroll
-      for (int i = 0; i < kStores; ++i) {
-        const int rr = 16 * I + 4 * (lane / 16) + i;
-        Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i]);
-        if (!full && !(rr < p.chunk && t0 + rr < p.T)) dst = sink + 16 * i + (lane % 16);
-        E::st(dst, 0, o4[0][i] + o4[1][i]);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kStores; ++i) {                             // keep the store count uniform
-        volatile Tv* dst = sink + 16 * i + (lane % 16);
-        *dst = (Tv)0;
-      }
-    }
+    group(5);
+    group(6);                                        // the L2 warm-up: always the last load
+    asm volatile("" :: "v"(warm_old));               // the warm-up load of two steps back
+    wait_lgkm();
+    wg_barrier();                                    // next state and V^T in LDS
   };
 
   publish_state();
-  // Operands of chunk n are loaded during chunk n - 1 (the first ones here), the L2
-  // warm-up for chunk n + 1 after them; chunk n's V^T is written to LDS during chunk
-  // n - 1.  Loads into the registers of one buffer are issued only after the previous
-  // chunk that used that buffer is done with it.  The loop body holds two chunks with no
-  // condition between them, so each buffer keeps its own registers and the compiler's
-  // waits stay exact.
-  Ops opA, opB;
+  Ch opA, opB;
   uint32_t warmA = 0, warmB = 0;
   if (p.NC > 0) {
     u32x4 v;
@@ -1038,31 +1105,28 @@ scan_kernel(ScanParams p) {
     write_vt(v, valid);
   }
   if (p.NC > 1) warmB = warm_chunk(1);
+  wait_lgkm();
+  wg_barrier();                                      // initial state and V^T in LDS
   int n = 0;
   for (; n + 1 < p.NC; n += 2) {
-    wait_lgkm();
-    wg_barrier();                                    // state and V^T visible
     u32x4 vB;
     unsigned long long validB;
-    process(opA, n, true, vB, validB, warmB, [&](int g) __attribute__((always_inline)) {
+    chain_step(opA, n, true, vB, validB, warmB, [&](int g) __attribute__((always_inline)) {
       if (g < kGroups) load_group(g, n + 1, opB, vB, validB);
       else warmA = warm_chunk(n + 2 <= last ? n + 2 : last);
     });
-    wait_lgkm();
-    wg_barrier();
     const int nn = n + 2 <= last ? n + 2 : last;
     u32x4 vA;
     unsigned long long validA;
-    process(opB, n + 1, true, vA, validA, warmA, [&](int g) __attribute__((always_inline)) {
+    chain_step(opB, n + 1, true, vA, validA, warmA, [&](int g) __attribute__((always_inline)) {
       if (g < kGroups) load_group(g, nn, opA, vA, validA);
       else warmB = warm_chunk(n + 3 <= last ? n + 3 : last);
     });
   }
   if (n < p.NC) {                                    // odd chunk count: the last one
-    wait_lgkm();
-    wg_barrier();
     const u32x4 none = {0u, 0u, 0u, 0u};
-    process(opA, n, false, none, 0ull, warmB, [](int) {});
+    const unsigned long long no_valid = 0;
+    chain_step(opA, n, false, none, no_valid, warmB, [](int) {});
   }
   asm volatile("" :: "v"(warmA), "v"(warmB));
   __builtin_amdgcn_s_waitcnt(0);
