@@ -189,7 +189,9 @@ prep_kernel(PrepParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_r2[Lds::r2];
   __shared__ __attribute__((aligned(16))) unsigned char s_r3[Lds::r3];
   __shared__ __attribute__((aligned(16))) float s_scratch[Lds::kScratch];
-  __shared__ __attribute__((aligned(16))) float s_tot[RT * K];       // per-tile sums of log2 decay
+  __shared__ __attribute__((aligned(16))) float s_tot[RT * K];       // per-tile sums of log2 decay, then
+                                                                     // the sums of the earlier tiles
+  __shared__ __attribute__((aligned(16))) float s_gc[K], s_gce[K];   // chunk total Gc and exp2(Gc) per channel
   __shared__ float s_beta[C], s_qs[C], s_ks[C];
   __shared__ int s_valid[C];
   __bf16* s_ki = reinterpret_cast<__bf16*>(s_r1);                    // [hi, lo][C][KB]
@@ -200,7 +202,8 @@ prep_kernel(PrepParams p) {
   float* s_A = reinterpret_cast<float*>(s_r3);                       // [C][CP]
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);          // uniform: loops over row tiles stay scalar
   const int t0 = n * p.chunk;
   const int dk = p.dk, dv = p.dv;
   const Raw* qg = (const Raw*)p.q;
@@ -287,100 +290,86 @@ prep_kernel(PrepParams p) {
   }
   __syncthreads();
 
-  // ---- chunk totals Gc of this lane's channels: factorised path when every Gc >= -120
-  //      (each wave covers every channel, so all waves reach the same answer)
-  // sums of the earlier tiles (pre) and of all tiles (tot); the loop bounds are
-  // wave-uniform, so no per-element selects are needed
-  auto tile_sums = [&](int ks, float* pre, float* tot) {
+  // ---- per channel (one thread each): the sums of the earlier tiles (in place of the tile
+  //      totals), the chunk total Gc, Gam_last = exp2(Gc) (also to the workspace), and the
+  //      test for the factorised path: every Gc >= -120
+  bool ch_fast = true;
+  if (tid < K) {
+    float run = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pre[e] = 0.f;
-    const int ilim = rows ? I : 0;
-    for (int J = 0; J < ilim; ++J) {
-      float t[8];
-      ld8f(&s_tot[J * K + 32 * ks + cg], t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pre[e] += t[e];
+    for (int J = 0; J < RT; ++J) {
+      const float t = s_tot[J * K + tid];
+      s_tot[J * K + tid] = run;
+      run += t;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tot[e] = pre[e];
-    for (int J = ilim; J < RT; ++J) {
-      float t[8];
-      ld8f(&s_tot[J * K + 32 * ks + cg], t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tot[e] += t[e];
-    }
-  };
-  bool lane_fast = true;
-#pragma unroll
-  for (int c = lane; c < K; c += 64) {
-    float tot = 0.f;
-#pragma unroll
-    for (int J = 0; J < RT; ++J) tot += s_tot[J * K + c];
-    lane_fast = lane_fast && tot >= kFastLimit;
+    const float ge = exp2f(run);
+    s_gc[tid] = run;
+    s_gce[tid] = ge;
+    reinterpret_cast<float*>(wsb + L::off_gam)[tid] = ge;
+    ch_fast = run >= kFastLimit;
   }
-  const bool fast = __all(lane_fast);
+  const bool fast = __syncthreads_and(ch_fast);
 
   // ---- decay factors for this lane's row.  On the fast path every factor lies in
-  //      [2^-120, 2^120], so the bare hardware exp2 is exact enough.
+  //      [2^-120, 2^120], so the bare hardware exp2 is exact enough, and
+  //      Gam_last / Gam = (1 / Gam) Gam_last.
+  // One exp2 besides Gam per element on either path: exp2(-G) on the fast path (Ki, then
+  // Kh = Ki Gam_last), exp2(Gc - G) on the other (Kh; Ki is not used there).
   bf16x8 kth[KS], ktl[KS], qth[KS], qtl[KS];
+  {
+    const float* gcs = fast ? s_gce : s_gc;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int c0 = 32 * ks + cg;
-    const bool cok = rok && c0 < dk;
-    float pre[8], gc[8];
-    tile_sums(ks, pre, gc);
-    float kt[8], ki[8], kh[8], qt[8], kf[8], qf[8];
-    k_r[ks].to_float(kf);
-    q_r[ks].to_float(qf);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float g = g_r[ks][e] + pre[e];
-      g_r[ks][e] = g;
-      const float kv = cok ? kf[e] * ksc : 0.f;
-      const float qv = cok ? qf[e] * qs : 0.f;
-      const float gam = __builtin_amdgcn_exp2f(g);
-      kt[e] = kv * gam;
-      ki[e] = fast ? kv * __builtin_amdgcn_exp2f(-g) : 0.f;
-      kh[e] = kv * __builtin_amdgcn_exp2f(gc[e] - g);
-      qt[e] = qv * gam;
-    }
-    split8(kt, kth[ks], ktl[ks]);
-    split8(qt, qth[ks], qtl[ks]);
-    if (rows) {
-      // Qt rows to the workspace (invalid rows are 0)
-      const size_t off = frag_off(I, ks, lane, K);
-      store_frag(wsb + L::off_qt + off, qth[ks]);
-      if (SPLIT) store_frag(wsb + L::off_qt + L::kCK + off, qtl[ks]);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int c0 = 32 * ks + cg;
+      const bool cok = rok && c0 < dk;
+      float pre[8], gcx[8];
+      ld8f(&s_tot[(rows ? I : 0) * K + c0], pre);
+      ld8f(&gcs[c0], gcx);
+      float kt[8], ki[8], kh[8], qt[8], kf[8], qf[8];
+      k_r[ks].to_float(kf);
+      q_r[ks].to_float(qf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        s_kt[swz<C>(c0 + e, rq)] = kth[ks][e];
-        if (SPLIT) s_kt[K * C + swz<C>(c0 + e, rq)] = ktl[ks][e];
+        const float g = g_r[ks][e] + pre[e];
+        g_r[ks][e] = g;
+        const float kv = cok ? kf[e] * ksc : 0.f;
+        const float qv = cok ? qf[e] * qs : 0.f;
+        const float gam = __builtin_amdgcn_exp2f(g);
+        kt[e] = kv * gam;
+        qt[e] = qv * gam;
+        const float e2 = kv * __builtin_amdgcn_exp2f(fast ? -g : gcx[e] - g);
+        ki[e] = fast ? e2 : 0.f;
+        kh[e] = fast ? e2 * gcx[e] : e2;
       }
-      bf16x8 hi, lo;
-      split8(kh, hi, lo);
+      split8(kt, kth[ks], ktl[ks]);
+      split8(qt, qth[ks], qtl[ks]);
+      if (rows) {
+        // Qt rows to the workspace (invalid rows are 0)
+        const size_t off = frag_off(I, ks, lane, K);
+        store_frag(wsb + L::off_qt + off, qth[ks]);
+        if (SPLIT) store_frag(wsb + L::off_qt + L::kCK + off, qtl[ks]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s_khs[swz<C>(c0 + e, rq)] = hi[e];
-        if (SPLIT) s_khs[K * C + swz<C>(c0 + e, rq)] = lo[e];
-      }
-      if (fast) {
-        split8(ki, hi, lo);
-        *reinterpret_cast<bf16x8*>(&s_ki[rq * KB + c0]) = hi;
-        *reinterpret_cast<bf16x8*>(&s_ki[C * KB + rq * KB + c0]) = lo;
-      } else {                                                       // exact pairwise decays need G
-        float4* gp = reinterpret_cast<float4*>(&s_G[rq * KP + c0]);
-        gp[0] = make_float4(g_r[ks][0], g_r[ks][1], g_r[ks][2], g_r[ks][3]);
-        gp[1] = make_float4(g_r[ks][4], g_r[ks][5], g_r[ks][6], g_r[ks][7]);
-      }
-    }
-    if (I == 0 && (lane % 16) == 0) {
-      // Gam_last: lanes 0, 16, 32, 48 of wave 0 cover every channel group once
-      float gl[8];
+        for (int e = 0; e < 8; ++e) {
+          s_kt[swz<C>(c0 + e, rq)] = kth[ks][e];
+          if (SPLIT) s_kt[K * C + swz<C>(c0 + e, rq)] = ktl[ks][e];
+        }
+        bf16x8 hi, lo;
+        split8(kh, hi, lo);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gl[e] = exp2f(gc[e]);
-      float4* dst = reinterpret_cast<float4*>(reinterpret_cast<float*>(wsb + L::off_gam) + c0);
-      dst[0] = make_float4(gl[0], gl[1], gl[2], gl[3]);
-      dst[1] = make_float4(gl[4], gl[5], gl[6], gl[7]);
+        for (int e = 0; e < 8; ++e) {
+          s_khs[swz<C>(c0 + e, rq)] = hi[e];
+          if (SPLIT) s_khs[K * C + swz<C>(c0 + e, rq)] = lo[e];
+        }
+        if (fast) {
+          split8(ki, hi, lo);
+          *reinterpret_cast<bf16x8*>(&s_ki[rq * KB + c0]) = hi;
+          *reinterpret_cast<bf16x8*>(&s_ki[C * KB + rq * KB + c0]) = lo;
+        } else {                                                     // exact pairwise decays need G
+          float4* gp = reinterpret_cast<float4*>(&s_G[rq * KP + c0]);
+          gp[0] = make_float4(g_r[ks][0], g_r[ks][1], g_r[ks][2], g_r[ks][3]);
+          gp[1] = make_float4(g_r[ks][4], g_r[ks][5], g_r[ks][6], g_r[ks][7]);
+        }
+      }
     }
   }
 
