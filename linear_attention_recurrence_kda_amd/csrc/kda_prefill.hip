@@ -797,7 +797,6 @@ scan_kernel(ScanParams p) {
       unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
       bf16x8 sh[KS], slo[KS];
       read_state(sh, slo);
-      pinned([&] { loads(0); });
       f32x4 o4[2] = {zero4(), zero4()};
       if (has_rows) {
 #pragma unroll
@@ -807,7 +806,9 @@ scan_kernel(ScanParams p) {
           if (SPLIT) o4[ks & 1] = mfma16(o.qtl[ks], sh[ks], o4[ks & 1]);
         }
       }
-      pinned([&] { loads(1); });
+      // the loads for the next step go after this wave's products, when the state waves'
+      // loads have had time to drain from the CU's queue
+      pinned([&] { loads(0); });
       wait_lgkm();
       wg_barrier();                                  // U in LDS
       bf16x8 uh[CS], ul[CS];
@@ -820,6 +821,7 @@ scan_kernel(ScanParams p) {
           o4[ks & 1] = mfma16(o.ph[ks], ul[ks], o4[ks & 1]);
           o4[ks & 1] = mfma16(o.pl[ks], uh[ks], o4[ks & 1]);
         }
+        pinned([&] { loads(1); });
 #pragma unroll
         for (int i = 0; i < kStores; ++i) {
           const int rr = 16 * I + 4 * (lane / 16) + i;
@@ -941,7 +943,7 @@ scan_kernel(ScanParams p) {
       if (srow(M)) op.khl[m][ks] = ld16(cb + L::off_kh + L::kCK + frag_off(M, ks, lane, C));
     }
   };
-  constexpr int kGroups = 6;
+  constexpr int kGroups = 7;
   auto load_group = [&](int g, int n, Ch& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
     pinned([&] {
 #pragma unroll
@@ -1049,14 +1051,15 @@ scan_kernel(ScanParams p) {
         s_U[0][(lane % 16) * CB + rr] = hi;
         s_U[1][(lane % 16) * CB + rr] = (__bf16)(uv - (float)hi);
       }
+      group(3);
     } else {
-      group(1); group(2);
+      group(1); group(2); group(3);
     }
     wait_lgkm();
     wg_barrier();                                    // U in LDS; S and V^T reads done
     bf16x8 uh[CS], ul[CS];
     read_u(uh, ul);
-    group(3);
+    group(4);
     // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -1073,11 +1076,11 @@ scan_kernel(ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
     }
-    group(4);
+    group(5);
     publish_state();
     if (write_next) write_vt(vnext, valid_next);
-    group(5);
-    group(6);                                        // the L2 warm-up: always the last load
+    group(6);
+    group(7);                                        // the L2 warm-up: always the last load
     asm volatile("" :: "v"(warm_old));               // the warm-up load of two steps back
     wait_lgkm();
     wg_barrier();                                    // next state and V^T in LDS
