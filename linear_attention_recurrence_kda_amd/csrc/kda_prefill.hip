@@ -102,6 +102,15 @@ struct ScanParams {
 __device__ __forceinline__ void store_frag(uint16_t* dst, const bf16x8& v) {
   *reinterpret_cast<bf16x8*>(dst) = v;
 }
+// Materialise a packed value in registers here.  Without this the compiler sinks the
+// conversions into the later, conditional uses and keeps their fp32 inputs alive in
+// the meantime (about twice the registers).
+__device__ __forceinline__ void pin8(bf16x8& v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  asm volatile("" : "+v"(u));
+  v = __builtin_bit_cast(bf16x8, u);
+}
 // 8 consecutive floats from 16-byte aligned LDS
 __device__ __forceinline__ void ld8f(const float* src, float* out) {
   const float4 a = reinterpret_cast<const float4*>(src)[0];
@@ -140,24 +149,49 @@ __device__ __forceinline__ int swz(int n, int j) {
 }
 
 // ================================================================ prep kernel
-// LDS of one prep workgroup: three regions, each reused by a later phase once the
-// barrier after its last read has passed (bf16 rows padded to K + 8, fp32 C x C rows
-// to C + 4, so 16 consecutive rows fall into different banks).
+// LDS of one prep workgroup, sized so that three workgroups share a CU: two regions,
+// each reused by a later phase once the barrier after its last read has passed.
+// Rows are unpadded; bank conflicts are avoided by permuting the 16-byte blocks of
+// each row with an XOR of the row index (swz, swzk, swzf).
+//   R1: Ki hi, lo (fast path) or G (other path); then T (fp32 C x C) and Kt^T.
+//   R3: Kh^T until stored; then A.
+//   R4: the per-channel decay sums, the row scales and validity flags of the other
+//       path; then one 16 x 17 fp32 staging tile for each wave of the inversion's
+//       block steps (waves 0 .. C/16 - 2).
 template <int DT, int K, int V, int C>
 struct PrepLds {
   static constexpr bool SPLIT = DT == 1;
-  static constexpr int KP = K + 4, KB = K + 8, CP = C + 4, RT = C / 16;
+  static constexpr int RT = C / 16;
   static constexpr int cmax(int a, int b) { return a > b ? a : b; }
   static constexpr int kParts = SPLIT ? 2 : 1;
-  // R1: Ki hi, lo (fast path) or G (slow path); then T
-  static constexpr int r1 = cmax(cmax(2 * C * KB * 2, C * KP * 4), C * CP * 4);
-  // R2: Kt^T
-  static constexpr int r2 = kParts * K * C * 2;
-  // R3: Kh^T until stored; then A
-  static constexpr int r3 = cmax(kParts * K * C * 2, C * CP * 4);
-  // one 16 x 17 fp32 staging tile per wave (the inversion's block exchange)
-  static constexpr int kScratch = 4 * 16 * 17;
+  static constexpr int kT = C * C * 4;                   // bytes of T
+  static constexpr int r1 = cmax(cmax(2 * C * K * 2, C * K * 4), kT + kParts * K * C * 2);
+  static constexpr int r3 = cmax(kParts * K * C * 2, C * C * 4);
+  // R4 in floats: s_tot [RT][K], s_gc [K], s_gce [K], s_ks [C], s_valid [C]
+  static constexpr int off_gc = RT * K, off_gce = off_gc + K, off_ks = off_gce + K, off_valid = off_ks + C;
+  static constexpr int kStage = 16 * 17;
+  static constexpr int r4 = cmax(off_valid + C, cmax(RT - 1, 1) * kStage);
 };
+
+// Element (r, c) of an r-major bf16 matrix with K per row: 16-byte blocks permuted by
+// an XOR with the row, so 16 lanes reading one block column of 16 rows hit all banks.
+template <int K>
+__device__ __forceinline__ int swzk(int r, int c) {
+  return r * K + ((((c >> 3) ^ (r & (K / 8 - 1)))) << 3) + (c & 7);
+}
+// Element (r, c) of an r-major fp32 C x C matrix, 16-byte blocks permuted likewise.
+template <int C>
+__device__ __forceinline__ int swzf(int r, int c) {
+  return r * C + ((((c >> 2) ^ (r & (C / 4 - 1)))) << 2) + (c & 3);
+}
+// 8 consecutive floats of row r from column c (c a multiple of 8) of a swzf matrix
+template <int C>
+__device__ __forceinline__ void ld8t(const float* m, int r, int c, float* out) {
+  const float4 a = *reinterpret_cast<const float4*>(&m[swzf<C>(r, c)]);
+  const float4 b = *reinterpret_cast<const float4*>(&m[swzf<C>(r, c + 4)]);
+  out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+  out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+}
 
 // x shifted down by n lanes inside each row of 16 lanes (lanes below n read 0)
 template <int N>
@@ -172,7 +206,7 @@ __device__ __forceinline__ float row_shr(float x) {
 // unconditionally, from in-bounds rows; validity (mask, ragged tail) is applied by
 // select afterwards.
 template <int DT, int K, int V, int C>
-__global__ void __launch_bounds__(kPrepThreads, DT == 0 ? 2 : 1)
+__global__ void __launch_bounds__(kPrepThreads, DT == 0 ? 3 : 1)
 prep_kernel(PrepParams p) {
   using E = Elem<DT>;
   using Raw = typename E::T;
@@ -182,24 +216,25 @@ prep_kernel(PrepParams p) {
   constexpr int RT = C / 16;          // row tiles of the chunk
   constexpr int CS = C / 32;          // k steps over chunk rows
   constexpr int KS = K / 32;          // k steps over key channels
-  constexpr int KP = Lds::KP, KB = Lds::KB, CP = Lds::CP;
   static_assert(RT <= 4, "one row tile per wave");
 
   __shared__ __attribute__((aligned(16))) unsigned char s_r1[Lds::r1];
-  __shared__ __attribute__((aligned(16))) unsigned char s_r2[Lds::r2];
   __shared__ __attribute__((aligned(16))) unsigned char s_r3[Lds::r3];
-  __shared__ __attribute__((aligned(16))) float s_scratch[Lds::kScratch];
-  __shared__ __attribute__((aligned(16))) float s_tot[RT * K];       // per-tile sums of log2 decay, then
+  __shared__ __attribute__((aligned(16))) float s_r4[Lds::r4];
+  __shared__ float s_beta[C];
+  __bf16* s_ki = reinterpret_cast<__bf16*>(s_r1);                    // [hi, lo][C][K] swzk (fast path)
+  float* s_G = reinterpret_cast<float*>(s_r1);                       // [C][K] (other path)
+  float* s_T = reinterpret_cast<float*>(s_r1);                       // [C][C] swzf
+  __bf16* s_kt = reinterpret_cast<__bf16*>(s_r1 + Lds::kT);          // Kt^T [hi(, lo)][K][C] swz
+  __bf16* s_khs = reinterpret_cast<__bf16*>(s_r3);                   // Kh^T [hi(, lo)][K][C] swz
+  float* s_A = reinterpret_cast<float*>(s_r3);                       // [C][C] swzf
+  float* s_tot = s_r4;                                               // per-tile sums of log2 decay, then
                                                                      // the sums of the earlier tiles
-  __shared__ __attribute__((aligned(16))) float s_gc[K], s_gce[K];   // chunk total Gc and exp2(Gc) per channel
-  __shared__ float s_beta[C], s_qs[C], s_ks[C];
-  __shared__ int s_valid[C];
-  __bf16* s_ki = reinterpret_cast<__bf16*>(s_r1);                    // [hi, lo][C][KB]
-  float* s_G = reinterpret_cast<float*>(s_r1);                       // [C][KP] (slow path)
-  float* s_T = reinterpret_cast<float*>(s_r1);                       // [C][CP]
-  __bf16* s_kt = reinterpret_cast<__bf16*>(s_r2);                    // Kt^T [hi(, lo)][K][C] swizzled
-  __bf16* s_khs = reinterpret_cast<__bf16*>(s_r3);                   // Kh^T [hi(, lo)][K][C] swizzled
-  float* s_A = reinterpret_cast<float*>(s_r3);                       // [C][CP]
+  float* s_gc = s_r4 + Lds::off_gc;                                  // chunk total Gc per channel
+  float* s_gce = s_r4 + Lds::off_gce;                                // exp2(Gc)
+  float* s_ks = s_r4 + Lds::off_ks;                                  // key row scales (other path)
+  int* s_valid = reinterpret_cast<int*>(s_r4 + Lds::off_valid);      // row validity (other path)
+  float* s_scratch = s_r4;                                           // staging tiles, in the inversion
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -258,7 +293,6 @@ prep_kernel(PrepParams p) {
   if (rows && lane < 16) {
     s_valid[rq] = rok;
     s_beta[rq] = rok ? beta_r : 0.f;
-    s_qs[rq] = qs;
     s_ks[rq] = ksc;
   }
 
@@ -343,16 +377,12 @@ prep_kernel(PrepParams p) {
       }
       split8(kt, kth[ks], ktl[ks]);
       split8(qt, qth[ks], qtl[ks]);
+      pin8(kth[ks]); pin8(ktl[ks]); pin8(qth[ks]); pin8(qtl[ks]);
       if (rows) {
         // Qt rows to the workspace (invalid rows are 0)
         const size_t off = frag_off(I, ks, lane, K);
         store_frag(wsb + L::off_qt + off, qth[ks]);
         if (SPLIT) store_frag(wsb + L::off_qt + L::kCK + off, qtl[ks]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          s_kt[swz<C>(c0 + e, rq)] = kth[ks][e];
-          if (SPLIT) s_kt[K * C + swz<C>(c0 + e, rq)] = ktl[ks][e];
-        }
         bf16x8 hi, lo;
         split8(kh, hi, lo);
 #pragma unroll
@@ -362,10 +392,10 @@ prep_kernel(PrepParams p) {
         }
         if (fast) {
           split8(ki, hi, lo);
-          *reinterpret_cast<bf16x8*>(&s_ki[rq * KB + c0]) = hi;
-          *reinterpret_cast<bf16x8*>(&s_ki[C * KB + rq * KB + c0]) = lo;
+          *reinterpret_cast<bf16x8*>(&s_ki[swzk<K>(rq, c0)]) = hi;
+          *reinterpret_cast<bf16x8*>(&s_ki[C * K + swzk<K>(rq, c0)]) = lo;
         } else {                                                     // exact pairwise decays need G
-          float4* gp = reinterpret_cast<float4*>(&s_G[rq * KP + c0]);
+          float4* gp = reinterpret_cast<float4*>(&s_G[rq * K + c0]);
           gp[0] = make_float4(g_r[ks][0], g_r[ks][1], g_r[ks][2], g_r[ks][3]);
           gp[1] = make_float4(g_r[ks][4], g_r[ks][5], g_r[ks][6], g_r[ks][7]);
         }
@@ -414,8 +444,8 @@ prep_kernel(PrepParams p) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
               const int c = 32 * ks + cg;
-              const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[j * KB + c]);
-              const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * KB + j * KB + c]);
+              const bf16x8 kih = *reinterpret_cast<const bf16x8*>(&s_ki[swzk<K>(j, c)]);
+              const bf16x8 kil = *reinterpret_cast<const bf16x8*>(&s_ki[C * K + swzk<K>(j, c)]);
               a[0] = mfma16(kih, kth[ks], a[0]);
               a[1] = mfma16(kil, kth[ks], a[1]);
               a[2] = mfma16(kih, ktl[ks], a[2]);
@@ -436,7 +466,7 @@ prep_kernel(PrepParams p) {
             av[i] = (jj < rq) ? beta_row * accA[i] : 0.f;
             pt[t][i] = (jj <= rq) ? accP[i] : 0.f;
           }
-          *reinterpret_cast<float4*>(&s_A[rq * CP + 16 * J + 4 * (lane / 16)]) = make_float4(av[0], av[1], av[2], av[3]);
+          *reinterpret_cast<float4*>(&s_A[swzf<C>(rq, 16 * J + 4 * (lane / 16))]) = make_float4(av[0], av[1], av[2], av[3]);
         }
         float pv[8];
         pair_to_afrag(pt[0], pt[1], pv);
@@ -456,13 +486,13 @@ prep_kernel(PrepParams p) {
         if (jj <= rq && rok && s_valid[jj]) {
           const size_t tj = grow(t0 + jj) * dk;
           for (int c = 0; c < dk; ++c) {
-            const float d = exp2f(s_G[rq * KP + c] - s_G[jj * KP + c]);
+            const float d = exp2f(s_G[rq * K + c] - s_G[jj * K + c]);
             const float kj = E::ld(kg, tj + c) * s_ks[jj];
             sa += E::ld(kg, tr + c) * ksc * kj * d;
             sp += E::ld(qg, tr + c) * qs * kj * d;
           }
         }
-        s_A[rq * CP + jj] = (jj < rq) ? beta_r * sa : 0.f;
+        s_A[swzf<C>(rq, jj)] = (jj < rq) ? beta_r * sa : 0.f;
         pv[e] = sp;
       }
       split8(pv, ph[ks], pl[ks]);
@@ -480,6 +510,18 @@ prep_kernel(PrepParams p) {
   }
   __syncthreads();                                                   // A complete; Ki or G read
 
+  // ---- Kt^T into R1 after T: row c holds channel c of every row of the chunk
+  if (rows) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s_kt[swz<C>(32 * ks + cg + e, rq)] = kth[ks][e];
+        if (SPLIT) s_kt[K * C + swz<C>(32 * ks + cg + e, rq)] = ktl[ks][e];
+      }
+    }
+  }
+
   // ---- T = (I + A)^-1, blocked: diagonal 16x16 blocks by forward substitution (two
   //      partial sums per row keep the dependency chain short)
   if (tid < RT * 16) {
@@ -488,8 +530,8 @@ prep_kernel(PrepParams p) {
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       float arow[16];
-      ld8f(&s_A[(16 * Ib + rr) * CP + 16 * Ib], arow);
-      ld8f(&s_A[(16 * Ib + rr) * CP + 16 * Ib + 8], arow + 8);
+      ld8t<C>(s_A, 16 * Ib + rr, 16 * Ib, arow);
+      ld8t<C>(s_A, 16 * Ib + rr, 16 * Ib + 8, arow + 8);
       float v0 = (rr == cc) ? 1.f : 0.f, v1 = 0.f;
 #pragma unroll
       for (int jj = 0; jj < rr; ++jj) {
@@ -499,11 +541,11 @@ prep_kernel(PrepParams p) {
       x[rr] = v0 + v1;
     }
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) s_T[(16 * Ib + rr) * CP + 16 * Ib + cc] = x[rr];
+    for (int rr = 0; rr < 16; ++rr) s_T[swzf<C>(16 * Ib + rr, 16 * Ib + cc)] = x[rr];
   }
   for (int idx = tid; idx < C * C; idx += kPrepThreads) {
     const int rr = idx / C, jj = idx % C;
-    if (jj / 16 != rr / 16) s_T[rr * CP + jj] = 0.f;
+    if (jj / 16 != rr / 16) s_T[swzf<C>(rr, jj)] = 0.f;
   }
   __syncthreads();
   // off-diagonal blocks by distance d, one block per wave on the MFMA:
@@ -519,11 +561,11 @@ prep_kernel(PrepParams p) {
         const int k0 = 16 * J + 32 * st + 8 * g;                     // contraction rows of T
         const bool kin = k0 < 16 * Ib;                               // L < I only
         float av[8], tv[8];
-        ld8f(&s_A[(16 * Ib + r) * CP + (kin ? k0 : 0)], av);
+        ld8t<C>(s_A, 16 * Ib + r, kin ? k0 : 0, av);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           av[e] = kin ? av[e] : 0.f;
-          tv[e] = kin ? s_T[(k0 + e) * CP + 16 * J + r] : 0.f;
+          tv[e] = kin ? s_T[swzf<C>(k0 + e, 16 * J + r)] : 0.f;
         }
         bf16x8 ah, al, th, tl;
         split8(av, ah, al);
@@ -539,7 +581,7 @@ prep_kernel(PrepParams p) {
       wave_lds_sync();
       float xv[8], tiv[8];
       const bool klo = g < 2;                                        // contraction over 16 rows only
-      ld8f(&s_T[(16 * Ib + r) * CP + 16 * Ib + (klo ? 8 * g : 0)], tiv);
+      ld8t<C>(s_T, 16 * Ib + r, 16 * Ib + (klo ? 8 * g : 0), tiv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         xv[e] = klo ? stage[(8 * g + e) * 17 + r] : 0.f;
@@ -553,7 +595,7 @@ prep_kernel(PrepParams p) {
       yb = mfma16(tih, xl, yb);
       yb = mfma16(til, xh, yb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_T[(16 * Ib + 4 * g + i) * CP + 16 * J + r] = -(ya[i] + yb[i]);
+      for (int i = 0; i < 4; ++i) s_T[swzf<C>(16 * Ib + 4 * g + i, 16 * J + r)] = -(ya[i] + yb[i]);
     }
     __syncthreads();
   }
@@ -565,7 +607,7 @@ prep_kernel(PrepParams p) {
     for (int ks = 0; ks < CS; ++ks) {
       const int j0 = 32 * ks + cg;
       float tv[8];
-      ld8f(&s_T[rq * CP + j0], tv);
+      ld8t<C>(s_T, rq, j0, tv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) tv[e] = -tv[e] * s_beta[j0 + e];
       split8(tv, tnh[ks], tnl[ks]);
