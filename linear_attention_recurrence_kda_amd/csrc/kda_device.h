@@ -91,6 +91,10 @@ template <int DT> struct Raw8;
 template <> struct Raw8<0> {
   uint4 u;
   __device__ __forceinline__ void load(const uint16_t* p, size_t i) { u = *reinterpret_cast<const uint4*>(p + i); }
+  // all eight values replaced by +0 unless ok (a select on the raw words: NaN cannot pass)
+  __device__ __forceinline__ void keep(bool ok) {
+    u.x = ok ? u.x : 0u; u.y = ok ? u.y : 0u; u.z = ok ? u.z : 0u; u.w = ok ? u.w : 0u;
+  }
   __device__ __forceinline__ void to_float(float* out) const {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -105,6 +109,10 @@ template <> struct Raw8<1> {
   __device__ __forceinline__ void load(const float* p, size_t i) {
     a = *reinterpret_cast<const float4*>(p + i);
     b = *reinterpret_cast<const float4*>(p + i + 4);
+  }
+  __device__ __forceinline__ void keep(bool ok) {
+    a.x = ok ? a.x : 0.f; a.y = ok ? a.y : 0.f; a.z = ok ? a.z : 0.f; a.w = ok ? a.w : 0.f;
+    b.x = ok ? b.x : 0.f; b.y = ok ? b.y : 0.f; b.z = ok ? b.z : 0.f; b.w = ok ? b.w : 0.f;
   }
   __device__ __forceinline__ void to_float(float* out) const {
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
@@ -128,12 +136,19 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
 }
 // Split fp32 values into a bf16 high part and a bf16 residual: v ~= hi + lo with
 // about 16 significant bits, so products on the bf16 MFMA keep near-fp32 accuracy.
+// Pairs are converted by one instruction each, and the high parts are widened back by
+// a shift and a mask of the packed word (round to nearest even either way).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __bf16 h = (__bf16)v[i];
-    hi[i] = h;
-    lo[i] = (__bf16)(v[i] - (float)h);
+  for (int i = 0; i < 8; i += 2) {
+    const bf16x2 h = __builtin_convertvector((f32x2){v[i], v[i + 1]}, bf16x2);
+    const uint32_t u = __builtin_bit_cast(uint32_t, h);
+    const bf16x2 l = __builtin_convertvector(
+        (f32x2){v[i] - __uint_as_float(u << 16), v[i + 1] - __uint_as_float(u & 0xffff0000u)}, bf16x2);
+    hi[i] = h[0]; hi[i + 1] = h[1];
+    lo[i] = l[0]; lo[i + 1] = l[1];
   }
 }
 __device__ __forceinline__ bf16x8 zero8() {

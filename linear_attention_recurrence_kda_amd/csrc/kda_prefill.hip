@@ -155,8 +155,8 @@ __device__ __forceinline__ int swz(int n, int j) {
 // each row with an XOR of the row index (swz, swzk, swzf).
 //   R1: Ki hi, lo (fast path) or G (other path); then T (fp32 C x C) and Kt^T.
 //   R3: Kh^T until stored; then A.
-//   R4: the per-channel decay sums, the row scales and validity flags of the other
-//       path; then one 16 x 17 fp32 staging tile for each wave of the inversion's
+//   R4: the per-channel decay sums, eight zeros and eight ones, the key row scales of
+//       the other path (0 for rows that are not valid); then one 16 x 17 fp32 staging tile for each wave of the inversion's
 //       block steps (waves 0 .. C/16 - 2).
 template <int DT, int K, int V, int C>
 struct PrepLds {
@@ -167,10 +167,11 @@ struct PrepLds {
   static constexpr int kT = C * C * 4;                   // bytes of T
   static constexpr int r1 = cmax(cmax(2 * C * K * 2, C * K * 4), kT + kParts * K * C * 2);
   static constexpr int r3 = cmax(kParts * K * C * 2, C * C * 4);
-  // R4 in floats: s_tot [RT][K], s_gc [K], s_gce [K], s_ks [C], s_valid [C]
-  static constexpr int off_gc = RT * K, off_gce = off_gc + K, off_ks = off_gce + K, off_valid = off_ks + C;
+  // R4 in floats: s_tot [RT][K], s_gc [K], s_gce [K], 8 zeros, 8 ones, s_ks [C]
+  static constexpr int off_gc = RT * K, off_gce = off_gc + K, off_zero = off_gce + K, off_one = off_zero + 8;
+  static constexpr int off_ks = off_one + 8;
   static constexpr int kStage = 16 * 17;
-  static constexpr int r4 = cmax(off_valid + C, cmax(RT - 1, 1) * kStage);
+  static constexpr int r4 = cmax(off_ks + C, cmax(RT - 1, 1) * kStage);
 };
 
 // Element (r, c) of an r-major bf16 matrix with K per row: 16-byte blocks permuted by
@@ -232,8 +233,9 @@ prep_kernel(PrepParams p) {
                                                                      // the sums of the earlier tiles
   float* s_gc = s_r4 + Lds::off_gc;                                  // chunk total Gc per channel
   float* s_gce = s_r4 + Lds::off_gce;                                // exp2(Gc)
-  float* s_ks = s_r4 + Lds::off_ks;                                  // key row scales (other path)
-  int* s_valid = reinterpret_cast<int*>(s_r4 + Lds::off_valid);      // row validity (other path)
+  float* s_zero = s_r4 + Lds::off_zero;                              // 8 x 0
+  float* s_one = s_r4 + Lds::off_one;                                // 8 x 1
+  float* s_ks = s_r4 + Lds::off_ks;                                  // key row scales, 0: row not valid
   float* s_scratch = s_r4;                                           // staging tiles, in the inversion
 
   const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -268,32 +270,35 @@ prep_kernel(PrepParams p) {
   const float beta_r = p.beta[grow(tsafe(rq))];
   const uint8_t m_r = mp[(size_t)b * p.T + tsafe(rq)];
   const bool rok = rows && rq < p.chunk && t0 + rq < p.T && (p.mask == nullptr || m_r != 0);
+  // q and k of rows that are not valid and of channels past dk become 0 here
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bool cok = rok && 32 * ks + cg < dk;
+    k_r[ks].keep(cok);
+    q_r[ks].keep(cok);
+  }
 
-  // ---- row scales of the optional L2 normalisation (channels past dk read as 0)
+  // ---- row scales of the optional L2 normalisation
   float qs = 1.f, ksc = 1.f;
   if (p.l2norm) {
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bool cok = 32 * ks + cg < dk;
       float qf[8], kf[8];
       q_r[ks].to_float(qf);
       k_r[ks].to_float(kf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = cok ? qf[e] : 0.f, kk = cok ? kf[e] : 0.f;
-        sq += a * a; sk += kk * kk;
-      }
+      for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
     }
     sq += __shfl_xor(sq, 16, 64); sk += __shfl_xor(sk, 16, 64);
     sq += __shfl_xor(sq, 32, 64); sk += __shfl_xor(sk, 32, 64);
     qs = rsqrtf(sq + 1e-6f);
     ksc = rsqrtf(sk + 1e-6f);
   }
+  if (tid < 8) { s_zero[tid] = 0.f; s_one[tid] = 1.f; }
   if (rows && lane < 16) {
-    s_valid[rq] = rok;
     s_beta[rq] = rok ? beta_r : 0.f;
-    s_ks[rq] = ksc;
+    s_ks[rq] = rok ? ksc : 0.f;
   }
 
   // ---- inclusive cumulative sum of log2 decay over the tile's 16 rows (DPP row scan);
@@ -347,33 +352,34 @@ prep_kernel(PrepParams p) {
   // ---- decay factors for this lane's row.  On the fast path every factor lies in
   //      [2^-120, 2^120], so the bare hardware exp2 is exact enough, and
   //      Gam_last / Gam = (1 / Gam) Gam_last.
-  // One exp2 besides Gam per element on either path: exp2(-G) on the fast path (Ki, then
-  // Kh = Ki Gam_last), exp2(Gc - G) on the other (Kh; Ki is not used there).
+  // One exp2 besides Gam per element on either path: e = k exp2(X - G) with X = 0 on
+  // the fast path (e is Ki, and Kh = e Gam_last), X = Gc on the other (Kh = e; Ki is not
+  // used there).  X and the factor after it are read from Gc / Gam_last or from blocks
+  // of eight zeros / ones, chosen per k step, so the elementwise work has no selects.
   bf16x8 kth[KS], ktl[KS], qth[KS], qtl[KS];
   {
-    const float* gcs = fast ? s_gce : s_gc;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = 32 * ks + cg;
-      const bool cok = rok && c0 < dk;
-      float pre[8], gcx[8];
+      float pre[8], xv[8], mv[8];
       ld8f(&s_tot[(rows ? I : 0) * K + c0], pre);
-      ld8f(&gcs[c0], gcx);
-      float kt[8], ki[8], kh[8], qt[8], kf[8], qf[8];
-      k_r[ks].to_float(kf);
-      q_r[ks].to_float(qf);
+      ld8f(fast ? s_zero : &s_gc[c0], xv);
+      ld8f(fast ? &s_gce[c0] : s_one, mv);
+      float kt[8], ki[8], kh[8], qt[8], kv[8], qv[8], g[8];
+      k_r[ks].to_float(kv);
+      q_r[ks].to_float(qv);
+      if (p.l2norm) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kv[e] *= ksc; qv[e] *= qs; }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float g = g_r[ks][e] + pre[e];
-        g_r[ks][e] = g;
-        const float kv = cok ? kf[e] * ksc : 0.f;
-        const float qv = cok ? qf[e] * qs : 0.f;
-        const float gam = __builtin_amdgcn_exp2f(g);
-        kt[e] = kv * gam;
-        qt[e] = qv * gam;
-        const float e2 = kv * __builtin_amdgcn_exp2f(fast ? -g : gcx[e] - g);
-        ki[e] = fast ? e2 : 0.f;
-        kh[e] = fast ? e2 * gcx[e] : e2;
+        g[e] = g_r[ks][e] + pre[e];
+        const float gam = __builtin_amdgcn_exp2f(g[e]);
+        kt[e] = kv[e] * gam;
+        qt[e] = qv[e] * gam;
+        ki[e] = kv[e] * __builtin_amdgcn_exp2f(xv[e] - g[e]);
+        kh[e] = ki[e] * mv[e];
       }
       split8(kt, kth[ks], ktl[ks]);
       split8(qt, qth[ks], qtl[ks]);
@@ -396,8 +402,8 @@ prep_kernel(PrepParams p) {
           *reinterpret_cast<bf16x8*>(&s_ki[C * K + swzk<K>(rq, c0)]) = lo;
         } else {                                                     // exact pairwise decays need G
           float4* gp = reinterpret_cast<float4*>(&s_G[rq * K + c0]);
-          gp[0] = make_float4(g_r[ks][0], g_r[ks][1], g_r[ks][2], g_r[ks][3]);
-          gp[1] = make_float4(g_r[ks][4], g_r[ks][5], g_r[ks][6], g_r[ks][7]);
+          gp[0] = make_float4(g[0], g[1], g[2], g[3]);
+          gp[1] = make_float4(g[4], g[5], g[6], g[7]);
         }
       }
     }
@@ -483,7 +489,7 @@ prep_kernel(PrepParams p) {
       for (int e = 0; e < 8; ++e) {
         const int jj = 32 * ks + cg + e;
         float sa = 0.f, sp = 0.f;
-        if (jj <= rq && rok && s_valid[jj]) {
+        if (jj <= rq && rok && s_ks[jj] > 0.f) {
           const size_t tj = grow(t0 + jj) * dk;
           for (int c = 0; c < dk; ++c) {
             const float d = exp2f(s_G[rq * K + c] - s_G[jj * K + c]);
