@@ -99,7 +99,8 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  *   final_state [B,H,dk,dv]  fp32, written; may be the same pointer as init_state
  *
  * Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64, 128, 256} (128
- * and 256 run as 64-token chunks); B, H <= 65535;
+ * and 256 run as 64-token chunks); B, H <= 65535; H times the number of
+ * chunks < 2^31 (KDA_ERR_UNSUPPORTED otherwise);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
  * log_alpha.  The ragged tail of the last chunk is handled as masked
  * positions.  `flags` may hold KDA_FLAG_L2NORM_QK.

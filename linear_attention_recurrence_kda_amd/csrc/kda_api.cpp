@@ -54,7 +54,8 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if ((flags & ~(unsigned)KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_INVALID_ARG;
-  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535)
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
+      !kda::prefill_grid_ok(T, H, chunk))
     return KDA_ERR_UNSUPPORTED;
   const bool work = (size_t)B * H > 0;
   if (work) {

@@ -45,5 +45,7 @@ hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
 bool prefill_supported(int dk, int dv, int chunk);
+// the chunk-local kernel's grid: H times the number of chunks below 2^31
+bool prefill_grid_ok(int T, int H, int chunk);
 
 }  // namespace kda

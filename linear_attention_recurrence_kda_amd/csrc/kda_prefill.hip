@@ -200,7 +200,7 @@ __device__ __forceinline__ float row_shr(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
 }
 
-// One workgroup per (chunk, head, batch row); wave I owns rows 16 I .. 16 I + 15 of
+// One workgroup per (chunk, head) and batch row; wave I owns rows 16 I .. 16 I + 15 of
 // the chunk.  Lane l of wave I holds row 16 I + l%16 and channels 32 ks + 8 (l/16) .. +7
 // for every k step ks: the A-operand layout of the MFMA, so Kt and Qt never leave
 // registers on their way into A and P.  All global loads are issued up front,
@@ -238,7 +238,9 @@ prep_kernel(PrepParams p) {
   float* s_ks = s_r4 + Lds::off_ks;                                  // key row scales, 0: row not valid
   float* s_scratch = s_r4;                                           // staging tiles, in the inversion
 
-  const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // heads vary fastest across workgroups, so the ones running together read whole token
+  // rows of q, k and log_alpha (all heads side by side) instead of one head's slice of each
+  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);          // uniform: loops over row tiles stay scalar
   const int t0 = n * p.chunk;
@@ -682,7 +684,6 @@ struct ChainOps {
   bf16x8 kh[SPW][CS];
   bf16x8 khl[SPLIT ? SPW : 1][CS];
   bf16x8 th[CS], tl[CS];                             // -T', this wave's rows
-  float4 gam[SPW];
 };
 template <int K, int C, bool SPLIT>
 struct OutOps {
@@ -759,6 +760,10 @@ scan_kernel(ScanParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state hi, lo; B-operand rows = dv column
   __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U hi, lo
   __shared__ __attribute__((aligned(16))) __bf16 s_vT[kParts][kVT * C]; // V^T (hi, lo) of the next chunk, swizzled
+  // Gam_last (K floats) and the row-valid bits (the next 16 bytes) of chunk c in slot c % 3,
+  // written two chunk steps ahead by one output wave with a single load (a load per state
+  // wave would have sixteen lanes on each address)
+  __shared__ __attribute__((aligned(16))) float s_gv[3][K + 4];
 
   // XCD-aware mapping: all dv tiles of one head share blockIdx.x % 8 (one L2)
   const int L_id = blockIdx.x;
@@ -833,6 +838,18 @@ scan_kernel(ScanParams p) {
         }
       }
     };
+    // Gam_last and the valid bits of chunk c: lane l < K/4 takes Gam_last[4 l .. 4 l + 3],
+    // lane K/4 the 16 bytes of valid bits (the workspace tail of the chunk)
+    auto load_gv = [&](int c) __attribute__((always_inline)) -> float4 {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint16_t* cb = wsh + (size_t)(c <= last ? c : last) * L::kElems;
+      if (lane <= K / 4)
+        x = *reinterpret_cast<const float4*>(lane < K / 4 ? cb + L::off_gam + 8 * lane : cb + L::off_valid);
+      return x;
+    };
+    auto store_gv = [&](int c, const float4& x) __attribute__((always_inline)) {
+      if (lane <= K / 4) *reinterpret_cast<float4*>(&s_gv[c % 3][4 * lane]) = x;
+    };
     Tv* og = (Tv*)p.o;
     Tv* sink = (Tv*)p.sink + (L_id & 63) * 64;
     uint32_t o_lane[kStores];
@@ -843,6 +860,8 @@ scan_kernel(ScanParams p) {
       const int t0 = n * p.chunk;
       const bool full = (p.chunk == C) && (t0 + C <= p.T);         // every row in range
       unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
+      float4 gv;
+      if (wave == 4) gv = load_gv(n + 2);
       bf16x8 sh[KS], slo[KS];
       read_state(sh, slo);
       f32x4 o4[2] = {zero4(), zero4()};
@@ -884,12 +903,19 @@ scan_kernel(ScanParams p) {
           *dst = (Tv)0;
         }
       }
+      if (wave == 4) store_gv(n + 2, gv);
       wait_lgkm();
       wg_barrier();                                  // next state and V^T in LDS
     };
 
     Ou oA, oB;
     if (p.NC > 0) { load_out(0, 0, oA); load_out(1, 0, oA); }
+    if (wave == 4 && p.NC > 0) {
+      const float4 g0 = load_gv(0), g1 = load_gv(1);
+      store_gv(0, g0);
+      store_gv(1, g1);
+    }
+    wait_lgkm();
     wg_barrier();                                    // initial state and V^T in LDS
     int n = 0;
     for (; n + 1 < p.NC; n += 2) {
@@ -944,13 +970,12 @@ scan_kernel(ScanParams p) {
   // step uses them; the -T' fragments past this wave's diagonal are not loaded, and the
   // ones that may be skipped come right after V (so the waits for everything later do
   // not depend on the branch).
-  constexpr int kLoads = 1 + 2 * CS + KS + SPW * CS + SPW + (SPLIT ? KS + SPW * CS : 0);
-  auto issue_load = [&](int idx, int n, Ch& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
+  constexpr int kLoads = 1 + 2 * CS + KS + SPW * CS + (SPLIT ? KS + SPW * CS : 0);
+  auto issue_load = [&](int idx, int n, Ch& op, u32x4& v) __attribute__((always_inline)) {
     const uint16_t* cb = wsh + (size_t)n * L::kElems;
     int k = idx;
     if (k == 0) {
       v = load_v(n);
-      valid = load_valid(n);
       if (has_rows) {
 #pragma unroll
         for (int ks = 1; ks < CS; ++ks) {
@@ -978,12 +1003,6 @@ scan_kernel(ScanParams p) {
       return;
     }
     k -= SPW * CS;
-    if (k < SPW) {
-      const int M = wave + 4 * k;
-      if (srow(M)) op.gam[k] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cb + L::off_gam) + 16 * M + 4 * (lane / 16));
-      return;
-    }
-    k -= SPW;
     if (SPLIT) {                                     // residual parts (fp32 inputs)
       if (k < KS) { if (has_rows) op.wnl[k] = ld16(cb + L::off_wn + L::kCK + frag_off(I, k, lane, K)); return; }
       k -= KS;
@@ -992,11 +1011,11 @@ scan_kernel(ScanParams p) {
     }
   };
   constexpr int kGroups = 7;
-  auto load_group = [&](int g, int n, Ch& op, u32x4& v, unsigned long long& valid) __attribute__((always_inline)) {
+  auto load_group = [&](int g, int n, Ch& op, u32x4& v) __attribute__((always_inline)) {
     pinned([&] {
 #pragma unroll
       for (int idx = 0; idx < kLoads; ++idx)
-        if (idx * kGroups / kLoads == g) issue_load(idx, n, op, v, valid);
+        if (idx * kGroups / kLoads == g) issue_load(idx, n, op, v);
     });
   };
 
@@ -1058,8 +1077,16 @@ scan_kernel(ScanParams p) {
   // One chunk step: operands in registers, V^T and S in LDS.  Writes the next chunk's
   // V^T (when there is one) after every wave has read this one.
   auto chain_step = [&](const Ch& op, int n, bool write_next, const u32x4& vnext,
-                        const unsigned long long& valid_next, uint32_t warm_old, auto&& group)
+                        uint32_t warm_old, auto&& group)
                         __attribute__((always_inline)) {
+    // this chunk's Gam_last rows and the next chunk's valid bits, from their LDS slots
+    float4 gam[SPW];
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int M = wave + 4 * m;
+      if (srow(M)) gam[m] = *reinterpret_cast<const float4*>(&s_gv[n % 3][16 * M + 4 * (lane / 16)]);
+    }
+    const unsigned long long valid_next = *reinterpret_cast<const unsigned long long*>(&s_gv[(n + 1) % 3][K]);
     // V^T first: T' V needs nothing else and can start while the state arrives
     bf16x8 vth[CS], vtl[SPLIT ? CS : 1];
 #pragma unroll
@@ -1120,7 +1147,7 @@ scan_kernel(ScanParams p) {
         a1 = mfma16(op.kh[m][ks], ul[ks], a1);
         if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
       }
-      const float gg[4] = {op.gam[m].x, op.gam[m].y, op.gam[m].z, op.gam[m].w};
+      const float gg[4] = {gam[m].x, gam[m].y, gam[m].z, gam[m].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
     }
@@ -1139,10 +1166,9 @@ scan_kernel(ScanParams p) {
   uint32_t warmA = 0, warmB = 0;
   if (p.NC > 0) {
     u32x4 v;
-    unsigned long long valid;
 #pragma unroll
-    for (int idx = 0; idx < kLoads; ++idx) issue_load(idx, 0, opA, v, valid);
-    write_vt(v, valid);
+    for (int idx = 0; idx < kLoads; ++idx) issue_load(idx, 0, opA, v);
+    write_vt(v, load_valid(0));
   }
   if (p.NC > 1) warmB = warm_chunk(1);
   wait_lgkm();
@@ -1150,23 +1176,20 @@ scan_kernel(ScanParams p) {
   int n = 0;
   for (; n + 1 < p.NC; n += 2) {
     u32x4 vB;
-    unsigned long long validB;
-    chain_step(opA, n, true, vB, validB, warmB, [&](int g) __attribute__((always_inline)) {
-      if (g < kGroups) load_group(g, n + 1, opB, vB, validB);
+    chain_step(opA, n, true, vB, warmB, [&](int g) __attribute__((always_inline)) {
+      if (g < kGroups) load_group(g, n + 1, opB, vB);
       else warmA = warm_chunk(n + 2 <= last ? n + 2 : last);
     });
     const int nn = n + 2 <= last ? n + 2 : last;
     u32x4 vA;
-    unsigned long long validA;
-    chain_step(opB, n + 1, true, vA, validA, warmA, [&](int g) __attribute__((always_inline)) {
-      if (g < kGroups) load_group(g, nn, opA, vA, validA);
+    chain_step(opB, n + 1, true, vA, warmA, [&](int g) __attribute__((always_inline)) {
+      if (g < kGroups) load_group(g, nn, opA, vA);
       else warmB = warm_chunk(n + 3 <= last ? n + 3 : last);
     });
   }
   if (n < p.NC) {                                    // odd chunk count: the last one
     const u32x4 none = {0u, 0u, 0u, 0u};
-    const unsigned long long no_valid = 0;
-    chain_step(opA, n, false, none, no_valid, warmB, [](int) {});
+    chain_step(opA, n, false, none, warmB, [](int) {});
   }
   asm volatile("" :: "v"(warmA), "v"(warmB));
   __builtin_amdgcn_s_waitcnt(0);
@@ -1216,6 +1239,12 @@ static size_t chunk_ws_elems(int K, int V, int C, int dtype) {
   return 0;
 }
 
+bool prefill_grid_ok(int T, int H, int chunk) {
+  const int c = run_chunk(chunk);
+  const long long nc = T > 0 ? ((long long)T + c - 1) / c : 0;
+  return nc * H <= 0x7fffffffll;
+}
+
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (T == 0 || B == 0 || H == 0) return 0;
   chunk = run_chunk(chunk);
@@ -1234,7 +1263,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if (NC > 0) {
     PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace,
                   a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm};
-    hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC, a.H, a.B), dim3(kPrepThreads), 0, st, pp);
+    hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC * a.H, a.B), dim3(kPrepThreads), 0, st, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

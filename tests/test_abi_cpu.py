@@ -84,6 +84,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, dk=100) == UNSUPPORTED
     assert _prefill(lib, H=65536) == UNSUPPORTED
     assert _prefill(lib, B=65536) == UNSUPPORTED
+    # the chunk-local grid holds H x chunks workgroups: at most 2^31 - 1
+    assert _prefill(lib, T=1 << 30, H=256, chunk=64) == UNSUPPORTED
     assert _prefill(lib, T=-3) == INVALID
     assert _prefill(lib, dtype=2) == INVALID
     assert _prefill(lib, flags=2) == INVALID            # SILU belongs to the short conv
