@@ -732,15 +732,6 @@ __device__ __forceinline__ void wait_lgkm() {
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
 }
-// wait for all of this wave's vector memory operations.  At the end of a prologue this
-// keeps the loop's first iteration from sharing the prologue's load order: otherwise the
-// compiler merges the two at the loop head and the waits of every iteration turn
-// conservative (a wait for last step's loads would also wait for this step's).
-__device__ __forceinline__ void wait_vm_all() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0f70);
-  asm volatile("" ::: "memory");
-}
 // loads issued in place: the scheduler moves nothing across either side
 template <typename F>
 __device__ __forceinline__ void pinned(F&& f) {
@@ -823,19 +814,18 @@ scan_kernel(ScanParams p) {
 
   if (wave >= 4) {
     // ================= output waves: O = Qt S + P U for row tile I
-    // Loads in the order the next step uses them.  No load sits under a branch: at a join
-    // the compiler's wait counts turn conservative and a wait for last step's loads would
-    // also wait for this step's; the P fragments past this wave's diagonal are replaced
-    // by one that is loaded and not used.
+    // Loads in the order the next step uses them, except that the P fragments past this
+    // wave's diagonal are not loaded at all, and the ones that may be skipped come first
+    // (so the waits for the others do not depend on the branch).
     auto load_out = [&](int part, int n, Ou& o) __attribute__((always_inline)) {
       const uint16_t* cb = wsh + (size_t)n * L::kElems;
       if (!has_rows) return;
       if (part == 0) {
 #pragma unroll
         for (int ks = 1; ks < CS; ++ks) {
-          const int kk = tri(ks) ? ks : 0;          // past the diagonal: a fragment that is not used
-          o.ph[ks] = ld16(cb + L::off_p + tri_off(I, kk, lane));
-          o.pl[ks] = ld16(cb + L::off_p + L::kPF + tri_off(I, kk, lane));
+          if (!tri(ks)) continue;
+          o.ph[ks] = ld16(cb + L::off_p + tri_off(I, ks, lane));
+          o.pl[ks] = ld16(cb + L::off_p + L::kPF + tri_off(I, ks, lane));
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) o.qt[ks] = ld16(cb + L::off_qt + frag_off(I, ks, lane, K));
@@ -850,14 +840,15 @@ scan_kernel(ScanParams p) {
     };
     // Gam_last and the valid bits of chunk c: lane l < K/4 takes Gam_last[4 l .. 4 l + 3],
     // lane K/4 the 16 bytes of valid bits (the workspace tail of the chunk)
-    // (every lane and every output wave loads, so that no load sits under a branch; lanes
-    // past K/4 repeat the valid bits and only wave 4 stores)
     auto load_gv = [&](int c) __attribute__((always_inline)) -> float4 {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       const uint16_t* cb = wsh + (size_t)(c <= last ? c : last) * L::kElems;
-      return *reinterpret_cast<const float4*>(lane < K / 4 ? cb + L::off_gam + 8 * lane : cb + L::off_valid);
+      if (lane <= K / 4)
+        x = *reinterpret_cast<const float4*>(lane < K / 4 ? cb + L::off_gam + 8 * lane : cb + L::off_valid);
+      return x;
     };
     auto store_gv = [&](int c, const float4& x) __attribute__((always_inline)) {
-      if (wave == 4 && lane <= K / 4) *reinterpret_cast<float4*>(&s_gv[c % 3][4 * lane]) = x;
+      if (lane <= K / 4) *reinterpret_cast<float4*>(&s_gv[c % 3][4 * lane]) = x;
     };
     Tv* og = (Tv*)p.o;
     Tv* sink = (Tv*)p.sink + (L_id & 63) * 64;
@@ -869,7 +860,8 @@ scan_kernel(ScanParams p) {
       const int t0 = n * p.chunk;
       const bool full = (p.chunk == C) && (t0 + C <= p.T);         // every row in range
       unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
-      const float4 gv = load_gv(n + 2);
+      float4 gv;
+      if (wave == 4) gv = load_gv(n + 2);
       bf16x8 sh[KS], slo[KS];
       read_state(sh, slo);
       f32x4 o4[2] = {zero4(), zero4()};
@@ -911,19 +903,18 @@ scan_kernel(ScanParams p) {
           *dst = (Tv)0;
         }
       }
-      store_gv(n + 2, gv);
+      if (wave == 4) store_gv(n + 2, gv);
       wait_lgkm();
       wg_barrier();                                  // next state and V^T in LDS
     };
 
     Ou oA, oB;
     if (p.NC > 0) { load_out(0, 0, oA); load_out(1, 0, oA); }
-    if (p.NC > 0) {
+    if (wave == 4 && p.NC > 0) {
       const float4 g0 = load_gv(0), g1 = load_gv(1);
       store_gv(0, g0);
       store_gv(1, g1);
     }
-    wait_vm_all();
     wait_lgkm();
     wg_barrier();                                    // initial state and V^T in LDS
     int n = 0;
@@ -976,9 +967,9 @@ scan_kernel(ScanParams p) {
     }
   };
   // Chunk n's operands for this wave, into registers, numbered in the order the next
-  // step uses them.  No load sits under a branch (the compiler's wait counts would turn
-  // conservative at the join): the -T' fragments past this wave's diagonal are replaced by
-  // one that is loaded and not used.
+  // step uses them; the -T' fragments past this wave's diagonal are not loaded, and the
+  // ones that may be skipped come right after V (so the waits for everything later do
+  // not depend on the branch).
   constexpr int kLoads = 1 + 2 * CS + KS + SPW * CS + (SPLIT ? KS + SPW * CS : 0);
   auto issue_load = [&](int idx, int n, Ch& op, u32x4& v) __attribute__((always_inline)) {
     const uint16_t* cb = wsh + (size_t)n * L::kElems;
@@ -988,9 +979,9 @@ scan_kernel(ScanParams p) {
       if (has_rows) {
 #pragma unroll
         for (int ks = 1; ks < CS; ++ks) {
-          const int kk = tri(ks) ? ks : 0;          // past the diagonal: loaded, not used
-          op.th[ks] = ld16(cb + L::off_tn + tri_off(I, kk, lane));
-          op.tl[ks] = ld16(cb + L::off_tn + L::kPF + tri_off(I, kk, lane));
+          if (!tri(ks)) continue;
+          op.th[ks] = ld16(cb + L::off_tn + tri_off(I, ks, lane));
+          op.tl[ks] = ld16(cb + L::off_tn + L::kPF + tri_off(I, ks, lane));
         }
       }
       return;
@@ -1180,7 +1171,6 @@ scan_kernel(ScanParams p) {
     write_vt(v, load_valid(0));
   }
   if (p.NC > 1) warmB = warm_chunk(1);
-  wait_vm_all();
   wait_lgkm();
   wg_barrier();                                      // initial state and V^T in LDS
   int n = 0;
