@@ -720,6 +720,23 @@ __device__ __forceinline__ u32x4 buffer_load_words(__amdgpu_buffer_rsrc_t r, uin
   return x;
 }
 
+// Four consecutive values as bf16 high parts and residuals (round to nearest even, as
+// a single conversion would), each part stored to LDS with one 8-byte write.
+__device__ __forceinline__ void store_split4(const float* v, __bf16* hi, __bf16* lo) {
+  uint32_t h[2], l[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16x2 hh = __builtin_convertvector((f32x2){v[2 * j], v[2 * j + 1]}, bf16x2);
+    const uint32_t u = __builtin_bit_cast(uint32_t, hh);
+    const bf16x2 ll = __builtin_convertvector(
+        (f32x2){v[2 * j] - __uint_as_float(u << 16), v[2 * j + 1] - __uint_as_float(u & 0xffff0000u)}, bf16x2);
+    h[j] = u;
+    l[j] = __builtin_bit_cast(uint32_t, ll);
+  }
+  *reinterpret_cast<uint2*>(hi) = make_uint2(h[0], h[1]);
+  *reinterpret_cast<uint2*>(lo) = make_uint2(l[0], l[1]);
+}
+
 // s_barrier with compiler-only fences around it: no memory access moves across
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
@@ -1062,14 +1079,10 @@ scan_kernel(ScanParams p) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
       const int M = wave + 4 * m;
-      if (srow(M)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * M + 4 * (lane / 16) + i;
-          const __bf16 hi = (__bf16)S[m][i];
-          s_S[0][(lane % 16) * KB + row] = hi;
-          s_S[1][(lane % 16) * KB + row] = (__bf16)(S[m][i] - (float)hi);
-        }
+      if (srow(M)) {                                 // rows 16 M + 4 (lane / 16) .. + 3: consecutive
+        const float v4[4] = {S[m][0], S[m][1], S[m][2], S[m][3]};
+        const int at = (lane % 16) * KB + 16 * M + 4 * (lane / 16);
+        store_split4(v4, &s_S[0][at], &s_S[1][at]);
       }
     }
   };
@@ -1118,14 +1131,11 @@ scan_kernel(ScanParams p) {
         if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(op.wnl[ks], sh[ks], u[(ks & 1) * 2 + 1]);
       }
       group(2);
+      float uv[4];                                   // rows 16 I + 4 (lane / 16) .. + 3
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * I + 4 * (lane / 16) + i;
-        const float uv = ((u[0][i] + u[2][i]) + (u[1][i] + u[3][i])) - (tv[0][i] + tv[1][i]);
-        const __bf16 hi = (__bf16)uv;
-        s_U[0][(lane % 16) * CB + rr] = hi;
-        s_U[1][(lane % 16) * CB + rr] = (__bf16)(uv - (float)hi);
-      }
+      for (int i = 0; i < 4; ++i) uv[i] = ((u[0][i] + u[2][i]) + (u[1][i] + u[3][i])) - (tv[0][i] + tv[1][i]);
+      const int at = (lane % 16) * CB + 16 * I + 4 * (lane / 16);
+      store_split4(uv, &s_U[0][at], &s_U[1][at]);
       group(3);
     } else {
       group(1); group(2); group(3);
