@@ -65,6 +65,21 @@ def test_prefill_head_sizes(oracle, dk, dv):
     check(f"dk{dk}dv{dv} state", host(s), rs, "bf16")
 
 
+@pytest.mark.parametrize("T", [1, 64, 65, 128])
+def test_prefill_one_or_two_chunks(oracle, T):
+    """One or two 64-token chunks: the scan's prologue and its odd/even tails, where the
+    next chunk's operands (and the decay/valid slots two chunks ahead) are clamped."""
+    dev = device()
+    B, H, dk, dv = 2, 3, 128, 128
+    say(f"[case] prefill bf16 chunk=64 T={T}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=9)
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=9)
+    o, s = _run(inp, "bf16", dev, 64, None, s0)
+    ro, rs = oracle.c_prefill(**inp, init_state=s0)
+    check(f"T{T} o", host(o), ro, "bf16")
+    check(f"T{T} state", host(s), rs, "bf16")
+
+
 @pytest.mark.parametrize("decay", ["slow", "strong"])
 def test_prefill_decay_regimes(oracle, decay):
     """Slow gates (state lives for hundreds of tokens) and strong gates (some channels decay
