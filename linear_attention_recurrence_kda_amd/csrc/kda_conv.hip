@@ -9,7 +9,10 @@
 // and masked positions get y = 0.  The new cache is the last W-1 entries of x~.
 //
 // Two launches on the caller's stream: conv_y_kernel reads the old cache,
-// conv_cache_kernel then overwrites it (stream order separates the two).
+// conv_cache_kernel then overwrites it (stream order separates the two).  When the
+// whole sequence is one token segment (decode: T = 1), the thread that forms y for a
+// channel group has read that group's old cache before anything else and ends holding
+// the new one, so it writes the cache itself and the second launch is skipped.
 // Each thread owns 8 consecutive channels (one 16-byte bf16 vector) and a
 // segment of tokens; its window history is found by walking back over the mask.
 #include "kda_device.h"
@@ -52,8 +55,8 @@ template <int DT, int W>
 __global__ void __launch_bounds__(kConvThreads)
 conv_y_kernel(const typename Elem<DT>::T* __restrict__ x, const float* __restrict__ w,
               const float* __restrict__ bias, const uint8_t* __restrict__ mask,
-              const typename Elem<DT>::T* __restrict__ cache, typename Elem<DT>::T* __restrict__ y,
-              int T, int D, int silu) {
+              typename Elem<DT>::T* __restrict__ cache, typename Elem<DT>::T* __restrict__ y,
+              int T, int D, int silu, int write_cache) {
   using E = Elem<DT>;
   const int c0 = (blockIdx.x * kConvThreads + threadIdx.x) * 8;
   if (c0 >= D) return;
@@ -100,6 +103,10 @@ conv_y_kernel(const typename Elem<DT>::T* __restrict__ x, const float* __restric
     }
     E::st8(y, off, out);
   }
+  if (write_cache) {                     // one segment from t = 0: hist is the new cache
+#pragma unroll
+    for (int j = 0; j < W - 1; ++j) E::st8(cache, ((size_t)b * (W - 1) + j) * D + c0, hist[j]);
+  }
 }
 
 template <int DT, int W>
@@ -123,10 +130,11 @@ static hipError_t launch_conv_t(const ConvArgs& a) {
   const int cblocks = (a.D / 8 + kConvThreads - 1) / kConvThreads;
   const int segs = (a.T + kConvSeg - 1) / kConvSeg;
   hipStream_t st = (hipStream_t)a.stream;
+  const int fused = (segs == 1 && a.cache != nullptr) ? 1 : 0;
   hipLaunchKernelGGL((conv_y_kernel<DT, W>), dim3(cblocks, segs, a.B), dim3(kConvThreads), 0, st,
-                     (const T*)a.x, a.weight, a.bias, a.mask, (const T*)a.cache, (T*)a.y, a.T, a.D, a.silu);
+                     (const T*)a.x, a.weight, a.bias, a.mask, (T*)a.cache, (T*)a.y, a.T, a.D, a.silu, fused);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.cache == nullptr) return e;
+  if (e != hipSuccess || a.cache == nullptr || fused) return e;
   hipLaunchKernelGGL((conv_cache_kernel<DT, W>), dim3(cblocks, 1, a.B), dim3(kConvThreads), 0, st,
                      (const T*)a.x, a.mask, (T*)a.cache, a.T, a.D);
   return hipGetLastError();

@@ -20,7 +20,7 @@ def _mask(kind, B, T, seed):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("W", [2, 3, 4])
-@pytest.mark.parametrize("T", [1, 5, 77])
+@pytest.mark.parametrize("T", [1, 5, 32, 33, 77])
 @pytest.mark.parametrize("kind", ["none", "pad", "random"])
 def test_conv_matches_oracle(oracle, dtype, W, T, kind):
     from linear_attention_recurrence_kda_amd import kda
