@@ -164,6 +164,18 @@ def main():
     torch.cuda.synchronize()
     dstep_ms = sum(a_.elapsed_time(b_) for a_, b_ in dev_ev) / reps
 
+    # the same decode step fused into one launch (three convolutions at T = 1 with their
+    # caches, the L2 norm and the state update): kda_decode_step_fused
+    dxf = {n: dx[n].view(Bd, H * dk) for n in dx}
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a_, b_ in fev:
+        a_.record()
+        kda.decode_step_fused(dxf["q"], dxf["k"], dxf["v"], cw["q"], cw["k"], cw["v"], cache["q"],
+                              cache["k"], cache["v"], dla, dbeta, state, H, l2norm_qk=True, out=do)
+        b_.record()
+    torch.cuda.synchronize()
+    fused_ms = sum(a_.elapsed_time(b_) for a_, b_ in fev) / reps
+
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
     # (read 1 GiB, write 1 GiB), the reference point beside the nominal 8 TB/s
     cn = (1 << 30) // 4
@@ -210,7 +222,8 @@ def main():
                     "hbm_frac_of_copy": pre_gbs / copy_gbs,
                     "model_tflops": pre_tflops, "mfma_frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
                     "roofline_frac": max(pre_gbs / HBM_PEAK_GBS, pre_tflops / MFMA_BF16_PEAK_TFLOPS)},
-        "decode": {"step_ms_with_conv": dec_avg, "state_update_ms": dstep_ms,
+        "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms,
+                   "fused_tokens_per_s": Bd / (fused_ms * 1e-3), "state_update_ms": dstep_ms,
                    "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
                    "hbm_frac_of_copy": dec_gbs / copy_gbs,
                    "tokens_per_s": Bd / (dec_avg * 1e-3),

@@ -158,6 +158,42 @@ int kda_short_conv(const void* x, const float* weight, const float* bias, const 
                    void* conv_cache, void* y, int B, int T, int D, int W, int dtype,
                    unsigned flags, void* stream);
 
+/*
+ * Fused decode step for a serving loop: per sequence b (one new token) the three
+ * short convolutions at T = 1 of kda_short_conv (with their caches), the optional
+ * q/k L2 norm and the state update of kda_decode_step, in one launch; sequence b's
+ * state is slot[b] of a pool (remio.ai page on Kimi Linear, decode section: each KDA
+ * layer keeps a fixed-size recurrent state per sequence; closing paragraphs: serving
+ * stacks need continuous batching that keeps KDA's state handling correct).  The conv
+ * outputs are rounded to `dtype` before the update, as kda_short_conv stores them, so
+ * the result equals three kda_short_conv calls followed by kda_decode_step bit for bit.
+ *
+ *   xq, xk      [B,H*dk]     dtype, raw inputs of the q and k convolutions
+ *   xv          [B,H*dv]     dtype, raw input of the v convolution
+ *   wq, wk      [H*dk,W]     fp32;  wv [H*dv,W] fp32
+ *   bq, bk, bv  [H*dk], [H*dk], [H*dv]  fp32 or NULL (no bias)
+ *   cache_q, cache_k [B,W-1,H*dk], cache_v [B,W-1,H*dv]   dtype, read then shifted
+ *   log_alpha   [B,H,dk]     fp32
+ *   beta        [B,H]        fp32
+ *   mask        [B]          uint8 0/1 or NULL; 0 leaves caches and state untouched, o = 0
+ *   state       [S,H,dk,dv]  fp32 pool, slot slot[b] read and written in place
+ *   slot        [B]          int32 or NULL (sequence b uses slot b; then S >= B).  The
+ *                            slots of the valid sequences must be distinct; a slot
+ *                            outside [0, S) is treated like a masked sequence.
+ *   o           [B,H,dv]     dtype, written
+ * No output may overlap an input.  Supported: dk, dv in {16, 32, 64, 128};
+ * W in {2, 3, 4}.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SILU (SiLU
+ * after each convolution).  16-byte aligned: state.
+ */
+int kda_decode_step_fused(const void* xq, const void* xk, const void* xv,
+                          const float* wq, const float* wk, const float* wv,
+                          const float* bq, const float* bk, const float* bv,
+                          void* cache_q, void* cache_k, void* cache_v,
+                          const float* log_alpha, const float* beta, const uint8_t* mask,
+                          float* state, const int32_t* slot, void* o,
+                          int B, int H, int S, int dk, int dv, int W, int dtype,
+                          unsigned flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -100,6 +100,33 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
   return hip_status(kda::launch_decode(a));
 }
 
+int kda_decode_step_fused(const void* xq, const void* xk, const void* xv, const float* wq,
+                          const float* wk, const float* wv, const float* bq, const float* bk,
+                          const float* bv, void* cache_q, void* cache_k, void* cache_v,
+                          const float* log_alpha, const float* beta, const uint8_t* mask,
+                          float* state, const int32_t* slot, void* o, int B, int H, int S, int dk,
+                          int dv, int W, int dtype, unsigned flags, void* stream) {
+  if (B < 0 || H < 0 || S < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SILU)) != 0) return KDA_ERR_INVALID_ARG;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || W < 2 || W > 4) return KDA_ERR_UNSUPPORTED;
+  if ((size_t)B * H == 0) return KDA_OK;
+  if (slot == nullptr && S < B) return KDA_ERR_INVALID_ARG;          // sequence b uses slot b
+  const void* req[] = {xq, xk, xv, wq, wk, wv, cache_q, cache_k, cache_v, log_alpha, beta, state, o};
+  for (const void* p : req)
+    if (p == nullptr) return KDA_ERR_INVALID_ARG;
+  if (!aligned16(state) || !aligned(slot, 4)) return KDA_ERR_INVALID_ARG;
+  const void* f32[] = {wq, wk, wv, bq, bk, bv, log_alpha, beta};
+  for (const void* p : f32)
+    if (!aligned(p, 4)) return KDA_ERR_INVALID_ARG;
+  const void* el[] = {xq, xk, xv, cache_q, cache_k, cache_v, o};
+  for (const void* p : el)
+    if (!aligned(p, elem_bytes(dtype))) return KDA_ERR_INVALID_ARG;
+  kda::FusedDecodeArgs a{xq, xk, xv, wq, wk, wv, bq, bk, bv, cache_q, cache_k, cache_v,
+                         log_alpha, beta, mask, state, slot, o, B, H, S, dk, dv, W, dtype,
+                         (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, (flags & KDA_FLAG_SILU) ? 1 : 0, stream};
+  return hip_status(kda::launch_decode_fused(a));
+}
+
 int kda_short_conv(const void* x, const float* weight, const float* bias, const uint8_t* mask,
                    void* conv_cache, void* y, int B, int T, int D, int W, int dtype, unsigned flags,
                    void* stream) {

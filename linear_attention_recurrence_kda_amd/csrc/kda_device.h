@@ -29,6 +29,8 @@ template <> struct Elem<0> {
   __device__ __forceinline__ static float cvt(T x) { return bf16_bits_to_f32(x); }
   __device__ __forceinline__ static float ld(const T* p, size_t i) { return bf16_bits_to_f32(p[i]); }
   __device__ __forceinline__ static void st(T* p, size_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+  // v as it reads back after a store
+  __device__ __forceinline__ static float round(float v) { return bf16_bits_to_f32(f32_to_bf16_bits(v)); }
   // 8 consecutive values starting at p[i] (i multiple of 8, 16-byte aligned)
   __device__ __forceinline__ static void ld8(const T* p, size_t i, float* out) {
     uint4 u = *reinterpret_cast<const uint4*>(p + i);
@@ -66,6 +68,7 @@ template <> struct Elem<1> {
   __device__ __forceinline__ static float cvt(T x) { return x; }
   __device__ __forceinline__ static float ld(const T* p, size_t i) { return p[i]; }
   __device__ __forceinline__ static void st(T* p, size_t i, float v) { p[i] = v; }
+  __device__ __forceinline__ static float round(float v) { return v; }
   __device__ __forceinline__ static void ld8(const T* p, size_t i, float* out) {
     float4 a = *reinterpret_cast<const float4*>(p + i);
     float4 b = *reinterpret_cast<const float4*>(p + i + 4);

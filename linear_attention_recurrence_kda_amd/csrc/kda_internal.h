@@ -17,6 +17,22 @@ struct DecodeArgs {
   void* stream;
 };
 
+// the three short convs at T = 1, the optional q/k L2 norm and the state update of one
+// decode step, with the state taken from a pool of slots
+struct FusedDecodeArgs {
+  const void *xq, *xk, *xv;                // raw conv inputs [B, H*dk] / [B, H*dv]
+  const float *wq, *wk, *wv;               // conv weights [D, W]
+  const float *bq, *bk, *bv;               // conv biases [D] or null
+  void *cq, *ck, *cv;                      // conv caches [B, W-1, D], updated
+  const float *log_alpha, *beta;
+  const uint8_t* mask;
+  float* state;                            // [S, H, dk, dv]
+  const int32_t* slot;                     // [B] or null (slot b)
+  void* o;
+  int B, H, S, dk, dv, W, dtype, l2norm, silu;
+  void* stream;
+};
+
 struct ConvArgs {
   const void* x;
   const float *weight, *bias;
@@ -42,6 +58,7 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_short_conv(const ConvArgs& a);
+hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
 bool prefill_supported(int dk, int dv, int chunk);

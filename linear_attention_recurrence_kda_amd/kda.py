@@ -20,7 +20,7 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
           -3: "KDA_ERR_WORKSPACE", -4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
            "kda_chunk_prefill_workspace_size", "kda_chunk_prefill", "kda_decode_step",
-           "kda_short_conv")
+           "kda_short_conv", "kda_decode_step_fused")
 
 _lib = None
 
@@ -60,6 +60,9 @@ def load():
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, i, i, i, i, i, u, vp]
     lib.kda_short_conv.restype = i
     lib.kda_short_conv.argtypes = [vp, fp, fp, up, vp, vp, i, i, i, i, i, u, vp]
+    lib.kda_decode_step_fused.restype = i
+    lib.kda_decode_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, vp, vp, vp, fp, fp, up,
+                                          fp, vp, vp, i, i, i, i, i, i, i, u, vp]
     _lib = lib
     return lib
 
@@ -171,6 +174,59 @@ def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out
                              _ptr(state), _ptr(out), B, H, dk, dv, dt,
                              KDA_FLAG_L2NORM_QK if l2norm_qk else 0, _stream())
     _check("kda_decode_step", st)
+    return out
+
+
+def decode_step_fused(xq, xk, xv, wq, wk, wv, cache_q, cache_k, cache_v, log_alpha, beta,
+                      state, H, mask=None, slot=None, biases=None, l2norm_qk=False, silu=False,
+                      out=None):
+    """One fused decode step: the three short convs at T = 1 (caches updated in place), the
+    optional q/k L2 norm and the state update, in one launch.  xq, xk [B,H*dk], xv [B,H*dv]
+    raw inputs; wq, wk [H*dk,W], wv [H*dv,W] fp32; caches [B,W-1,H*d] (x's dtype);
+    log_alpha [B,H,dk], beta [B,H]; state [S,H,dk,dv] fp32 pool updated in place at slot[b]
+    (slot [B] int32, or None for slot b); mask [B] or None; biases (bq, bk, bv) or None.
+    Returns o [B,H,dv]."""
+    import torch
+    lib = load()
+    dt = _dtype_code(xq)
+    B = xq.shape[0]
+    dk, dv = xq.shape[1] // H, xv.shape[1] // H
+    W = wq.shape[1]
+    S = state.shape[0]
+    _req(xq, "xq", shape=(B, H * dk))
+    _req(xk, "xk", xq.dtype, (B, H * dk))
+    _req(xv, "xv", xq.dtype, (B, H * dv))
+    _req(wq, "wq", torch.float32, (H * dk, W))
+    _req(wk, "wk", torch.float32, (H * dk, W))
+    _req(wv, "wv", torch.float32, (H * dv, W))
+    _req(cache_q, "cache_q", xq.dtype, (B, W - 1, H * dk))
+    _req(cache_k, "cache_k", xq.dtype, (B, W - 1, H * dk))
+    _req(cache_v, "cache_v", xq.dtype, (B, W - 1, H * dv))
+    _req(log_alpha, "log_alpha", torch.float32, (B, H, dk))
+    _req(beta, "beta", torch.float32, (B, H))
+    _req(state, "state", torch.float32, (S, H, dk, dv))
+    bq = bk = bv = None
+    if biases is not None:
+        bq, bk, bv = biases
+        _req(bq, "bq", torch.float32, (H * dk,))
+        _req(bk, "bk", torch.float32, (H * dk,))
+        _req(bv, "bv", torch.float32, (H * dv,))
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        _req(mask, "mask", torch.uint8, (B,))
+    if slot is not None:
+        _req(slot, "slot", torch.int32, (B,))
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=xq.dtype, device=xq.device)
+    _req(out, "out", xq.dtype, (B, H, dv))
+    flags = (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_SILU if silu else 0)
+    st = lib.kda_decode_step_fused(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
+                                   _ptr(bq), _ptr(bk), _ptr(bv), _ptr(cache_q), _ptr(cache_k),
+                                   _ptr(cache_v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                                   _ptr(state), _ptr(slot), _ptr(out), B, H, S, dk, dv, W, dt,
+                                   flags, _stream())
+    _check("kda_decode_step_fused", st)
     return out
 
 

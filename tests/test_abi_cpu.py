@@ -68,6 +68,33 @@ def test_decode_validation(lib):
     assert _decode(lib, H=0, q=None) == OK
 
 
+def _fused(lib, **kw):
+    a = dict(xq=FAKE, xk=FAKE, xv=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, bq=None, bk=None, bv=None,
+             cq=FAKE, ck=FAKE, cv=FAKE, la=FAKE, beta=FAKE, mask=None, state=FAKE, slot=None, o=FAKE,
+             B=2, H=2, S=2, dk=128, dv=128, W=4, dtype=0, flags=0)
+    a.update(kw)
+    return lib.kda_decode_step_fused(a["xq"], a["xk"], a["xv"], a["wq"], a["wk"], a["wv"], a["bq"],
+                                     a["bk"], a["bv"], a["cq"], a["ck"], a["cv"], a["la"], a["beta"],
+                                     a["mask"], a["state"], a["slot"], a["o"], a["B"], a["H"], a["S"],
+                                     a["dk"], a["dv"], a["W"], a["dtype"], a["flags"], None)
+
+
+def test_fused_decode_validation(lib):
+    assert _fused(lib, dk=48) == UNSUPPORTED
+    assert _fused(lib, W=5) == UNSUPPORTED
+    assert _fused(lib, W=1) == UNSUPPORTED
+    assert _fused(lib, dtype=3) == INVALID
+    assert _fused(lib, flags=4) == INVALID
+    assert _fused(lib, S=-1) == INVALID
+    assert _fused(lib, S=1) == INVALID              # no slot array: sequence b needs slot b < S
+    assert _fused(lib, xv=None) == INVALID
+    assert _fused(lib, cv=None) == INVALID
+    assert _fused(lib, state=MISALIGNED) == INVALID
+    assert _fused(lib, slot=ctypes.c_void_p(0x10002)) == INVALID
+    assert _fused(lib, B=0) == OK                   # nothing to do, nothing launched
+    assert _fused(lib, H=0, xq=None) == OK
+
+
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, mask=None, s0=None, o=FAKE, sT=FAKE,
              B=1, T=64, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0, ws=FAKE, wsb=1 << 40)
