@@ -134,3 +134,61 @@ def test_fused_state_slots():
         assert torch.equal(pool[i], before[i]), f"slot {i} changed"
     for n in "qkv":
         assert torch.equal(cf[n], cu[n])
+
+
+def test_fused_step_in_graph_replays():
+    """The fused step captured once in a graph and replayed step after step (new inputs
+    copied into the captured buffers eagerly between replays, with a synchronisation each
+    time) gives every step the eager result bit for bit."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, H, dk, dv, W, steps = 4, 4, 128, 128, 4, 4
+    say("[case] fused decode graph replay")
+    x0, w, c, _, la0, beta0 = _inputs(B, H, dk, dv, W, "bf16", seed=120)
+    wd = {n: to_dev(w[n], dev=dev) for n in "qkv"}
+    s0 = to_dev(D.np_state(B, H, dk, dv, 0.2, seed=12), dev=dev)
+    # captured buffers
+    xg = {n: to_dev(x0[n], "bf16", dev) for n in "qkv"}
+    cg = {n: to_dev(c[n], "bf16", dev) for n in "qkv"}
+    lag, betag, stg = to_dev(la0, dev=dev), to_dev(beta0, dev=dev), s0.clone()
+    og = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+    ce = {n: cg[n].clone() for n in "qkv"}                 # eager copies
+    ste = s0.clone()
+
+    def step(x, cch, la, beta, st, out):
+        kda.decode_step_fused(x["q"], x["k"], x["v"], wd["q"], wd["k"], wd["v"], cch["q"], cch["k"],
+                              cch["v"], la, beta, st, H, l2norm_qk=True, out=out)
+
+    # warm up on a side stream on scratch copies, then capture one step
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(xg, {n: cg[n].clone() for n in "qkv"}, lag, betag, stg.clone(), torch.empty_like(og))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(xg, cg, lag, betag, stg, og)
+    torch.cuda.synchronize()
+    # capture does not run the step: reset the captured state and caches to the start
+    stg.copy_(s0)
+    for n in "qkv":
+        cg[n].copy_(ce[n])
+    torch.cuda.synchronize()
+    for s in range(steps):
+        x, _, _, _, la, beta = _inputs(B, H, dk, dv, W, "bf16", seed=130 + s)
+        for n in "qkv":
+            xg[n].copy_(to_dev(x[n], "bf16", dev))
+        lag.copy_(to_dev(la, dev=dev))
+        betag.copy_(to_dev(beta, dev=dev))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        oe = torch.empty_like(og)
+        step({n: to_dev(x[n], "bf16", dev) for n in "qkv"}, ce, to_dev(la, dev=dev), to_dev(beta, dev=dev), ste, oe)
+        torch.cuda.synchronize()
+        assert torch.equal(og, oe), f"o differs at replay {s}"
+        assert torch.equal(stg, ste), f"state differs at replay {s}"
+        for n in "qkv":
+            assert torch.equal(cg[n], ce[n]), f"cache {n} differs at replay {s}"
