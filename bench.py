@@ -175,6 +175,25 @@ def main():
         b_.record()
     torch.cuda.synchronize()
     fused_ms = sum(a_.elapsed_time(b_) for a_, b_ in fev) / reps
+    # and replayed from a graph: 8 fused steps captured once (a decode loop with no
+    # per-launch host work), timed over whole replays
+    def fused_step():
+        kda.decode_step_fused(dxf["q"], dxf["k"], dxf["v"], cw["q"], cw["k"], cw["v"], cache["q"],
+                              cache["k"], cache["v"], dla, dbeta, state, H, l2norm_qk=True, out=do)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(8):
+            fused_step()
+    graph.replay()
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a_, b_ in gev:
+        a_.record()
+        graph.replay()
+        b_.record()
+    torch.cuda.synchronize()
+    graph_step_ms = sum(a_.elapsed_time(b_) for a_, b_ in gev) / (5 * 8)
+    del graph
 
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
     # (read 1 GiB, write 1 GiB), the reference point beside the nominal 8 TB/s
@@ -222,7 +241,7 @@ def main():
                     "hbm_frac_of_copy": pre_gbs / copy_gbs,
                     "model_tflops": pre_tflops, "mfma_frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
                     "roofline_frac": max(pre_gbs / HBM_PEAK_GBS, pre_tflops / MFMA_BF16_PEAK_TFLOPS)},
-        "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms,
+        "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms, "fused_step_graph_ms": graph_step_ms,
                    "fused_tokens_per_s": Bd / (fused_ms * 1e-3), "state_update_ms": dstep_ms,
                    "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
                    "hbm_frac_of_copy": dec_gbs / copy_gbs,
