@@ -63,7 +63,12 @@ enum {
   /* normalise q and k per (b,t,h) to x / sqrt(sum x^2 + 1e-6) before use */
   KDA_FLAG_L2NORM_QK = 1u,
   /* short convolution: apply SiLU, y = z / (1 + exp(-z)) */
-  KDA_FLAG_SILU = 2u
+  KDA_FLAG_SILU = 2u,
+  /* Gated DeltaNet's gate: one log forget gate per (token, head), applied to every key
+   * channel; log_alpha is then [B,T,H] in a prefill and [B,H] in a decode step (Kimi
+   * Linear summary page, recurrent-layers paragraph: earlier variants gate whole heads,
+   * KDA each channel; remio.ai page, KDA section: KDA extends Gated DeltaNet) */
+  KDA_FLAG_SCALAR_GATE = 4u
 };
 
 /* KDA_ABI_VERSION of the built library. */
@@ -91,7 +96,8 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  *
  *   q, k        [B,T,H,dk]   dtype
  *   v           [B,T,H,dv]   dtype
- *   log_alpha   [B,T,H,dk]   fp32, finite, <= 0 (per-channel log forget gate)
+ *   log_alpha   [B,T,H,dk]   fp32, finite, <= 0 (per-channel log forget gate);
+ *                            [B,T,H] with KDA_FLAG_SCALAR_GATE
  *   beta        [B,T,H]      fp32 in [0,1]
  *   mask        [B,T]        uint8 0/1, NULL = every position valid
  *   init_state  [B,H,dk,dv]  fp32, NULL = zeros
@@ -103,7 +109,7 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * chunks < 2^31 (KDA_ERR_UNSUPPORTED otherwise);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
  * log_alpha.  The ragged tail of the last chunk is handled as masked
- * positions.  `flags` may hold KDA_FLAG_L2NORM_QK.
+ * positions.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
  * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
  * bytes of device memory (may be NULL when that size is 0).
  */
@@ -120,14 +126,14 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
  *
  *   q, k        [B,H,dk]     dtype
  *   v           [B,H,dv]     dtype
- *   log_alpha   [B,H,dk]     fp32
+ *   log_alpha   [B,H,dk]     fp32 ([B,H] with KDA_FLAG_SCALAR_GATE)
  *   beta        [B,H]        fp32
  *   mask        [B]          uint8 0/1, NULL = all valid (0 leaves S untouched, o = 0)
  *   state       [B,H,dk,dv]  fp32, read and written in place
  *   o           [B,H,dv]     dtype, written
  *
  * Supported: dk, dv in {16, 32, 64, 128}; B, H >= 0.  `flags` may hold
- * KDA_FLAG_L2NORM_QK.  16-byte aligned: state.
+ * KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.  16-byte aligned: state.
  */
 int kda_decode_step(const void* q, const void* k, const void* v,
                     const float* log_alpha, const float* beta, const uint8_t* mask,
@@ -173,7 +179,7 @@ int kda_short_conv(const void* x, const float* weight, const float* bias, const 
  *   wq, wk      [H*dk,W]     fp32;  wv [H*dv,W] fp32
  *   bq, bk, bv  [H*dk], [H*dk], [H*dv]  fp32 or NULL (no bias)
  *   cache_q, cache_k [B,W-1,H*dk], cache_v [B,W-1,H*dv]   dtype, read then shifted
- *   log_alpha   [B,H,dk]     fp32
+ *   log_alpha   [B,H,dk]     fp32 ([B,H] with KDA_FLAG_SCALAR_GATE)
  *   beta        [B,H]        fp32
  *   mask        [B]          uint8 0/1 or NULL; 0 leaves caches and state untouched, o = 0
  *   state       [S,H,dk,dv]  fp32 pool, slot slot[b] read and written in place
@@ -182,8 +188,8 @@ int kda_short_conv(const void* x, const float* weight, const float* bias, const 
  *                            outside [0, S) is treated like a masked sequence.
  *   o           [B,H,dv]     dtype, written
  * No output may overlap an input.  Supported: dk, dv in {16, 32, 64, 128};
- * W in {2, 3, 4}.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SILU (SiLU
- * after each convolution).  16-byte aligned: state.
+ * W in {2, 3, 4}.  `flags` may hold KDA_FLAG_L2NORM_QK, KDA_FLAG_SILU (SiLU after
+ * each convolution) and KDA_FLAG_SCALAR_GATE.  16-byte aligned: state.
  */
 int kda_decode_step_fused(const void* xq, const void* xk, const void* xv,
                           const float* wq, const float* wk, const float* wv,

@@ -53,7 +53,7 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
                       float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
-  if ((flags & ~(unsigned)KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
   if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
       !kda::prefill_grid_ok(T, H, chunk))
     return KDA_ERR_UNSUPPORTED;
@@ -76,7 +76,7 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
   if (!work) return KDA_OK;
   kda::PrefillArgs a{q, k, v, log_alpha, beta, mask, init_state, o, final_state,
                      B, T, H, dk, dv, chunk, dtype, (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0,
-                     workspace, workspace_bytes, stream};
+                     (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, workspace, workspace_bytes, stream};
   return hip_status(kda::launch_prefill(a));
 }
 
@@ -84,7 +84,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
                     const float* beta, const uint8_t* mask, float* state, void* o, int B, int H,
                     int dk, int dv, int dtype, unsigned flags, void* stream) {
   if (B < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
-  if ((flags & ~(unsigned)KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
   if (!head_dim_ok(dk) || !head_dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
   const void* req[] = {q, k, v, log_alpha, beta, state, o};
@@ -96,7 +96,7 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
   for (const void* p : el)
     if (!aligned(p, elem_bytes(dtype))) return KDA_ERR_INVALID_ARG;
   kda::DecodeArgs a{q, k, v, log_alpha, beta, mask, state, o, B, H, dk, dv, dtype,
-                    (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, stream};
+                    (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, stream};
   return hip_status(kda::launch_decode(a));
 }
 
@@ -107,7 +107,7 @@ int kda_decode_step_fused(const void* xq, const void* xk, const void* xv, const 
                           float* state, const int32_t* slot, void* o, int B, int H, int S, int dk,
                           int dv, int W, int dtype, unsigned flags, void* stream) {
   if (B < 0 || H < 0 || S < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
-  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SILU)) != 0) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SILU | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
   if (!head_dim_ok(dk) || !head_dim_ok(dv) || W < 2 || W > 4) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
   if (slot == nullptr && S < B) return KDA_ERR_INVALID_ARG;          // sequence b uses slot b
@@ -123,7 +123,8 @@ int kda_decode_step_fused(const void* xq, const void* xk, const void* xv, const 
     if (!aligned(p, elem_bytes(dtype))) return KDA_ERR_INVALID_ARG;
   kda::FusedDecodeArgs a{xq, xk, xv, wq, wk, wv, bq, bk, bv, cache_q, cache_k, cache_v,
                          log_alpha, beta, mask, state, slot, o, B, H, S, dk, dv, W, dtype,
-                         (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, (flags & KDA_FLAG_SILU) ? 1 : 0, stream};
+                         (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0, (flags & KDA_FLAG_SILU) ? 1 : 0,
+                         (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, stream};
   return hip_status(kda::launch_decode_fused(a));
 }
 

@@ -117,7 +117,8 @@ __global__ void __launch_bounds__((DecodeShape<K, V>::kThreads))
 decode_step_kernel(const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ k,
                    const typename Elem<DT>::T* __restrict__ v, const float* __restrict__ log_alpha,
                    const float* __restrict__ beta, const uint8_t* __restrict__ mask,
-                   float* __restrict__ state, typename Elem<DT>::T* __restrict__ o, int H, int l2norm) {
+                   float* __restrict__ state, typename Elem<DT>::T* __restrict__ o, int H, int l2norm,
+                   int scalar_gate) {
   using Sh = DecodeShape<K, V>;
   using E = Elem<DT>;
   const int bh = blockIdx.x;
@@ -138,7 +139,8 @@ decode_step_kernel(const typename Elem<DT>::T* __restrict__ q, const typename El
   static_assert(K <= Sh::kThreads && V <= Sh::kThreads, "one element per thread");
   const int ik = tid < K ? tid : K - 1, iv = tid < V ? tid : V - 1;
   const float qv = E::ld(q, (size_t)bh * K + ik), kv = E::ld(k, (size_t)bh * K + ik);
-  const float la = log_alpha[(size_t)bh * K + ik], vv = E::ld(v, (size_t)bh * V + iv);
+  // Gated DeltaNet's gate: one log_alpha per (b, h) for every channel
+  const float la = log_alpha[scalar_gate ? (size_t)bh : (size_t)bh * K + ik], vv = E::ld(v, (size_t)bh * V + iv);
   __builtin_amdgcn_sched_barrier(0);
   f32x4 s[Sh::kRows];
   load_state_rows<K, V>(sp, s, tid);
@@ -196,7 +198,7 @@ struct FusedDecodeParams {
   float* state;
   const int32_t* slot;
   void* o;
-  int H, S, W, l2norm, silu;
+  int H, S, W, l2norm, silu, scalar_gate;
 };
 
 template <int DT, int K, int V>
@@ -240,7 +242,7 @@ fused_decode_kernel(FusedDecodeParams p) {
     ch[t].load(xp, wp, bp, cp, b, D, c, p.W);
   }
   static_assert(K <= Sh::kThreads, "one log_alpha per thread");
-  const float la = p.log_alpha[(size_t)bh * K + (tid < K ? tid : K - 1)];
+  const float la = p.log_alpha[p.scalar_gate ? (size_t)bh : (size_t)bh * K + (tid < K ? tid : K - 1)];
   __builtin_amdgcn_sched_barrier(0);                // every small load ahead of the state's
   f32x4 s[Sh::kRows];
   load_state_rows<K, V>(sp, s, tid);
@@ -268,7 +270,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   if (nbh == 0) return hipSuccess;
   hipLaunchKernelGGL((decode_step_kernel<DT, K, V>), dim3(nbh), dim3(DecodeShape<K, V>::kThreads), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.log_alpha,
-                     a.beta, a.mask, a.state, (T*)a.o, a.H, a.l2norm);
+                     a.beta, a.mask, a.state, (T*)a.o, a.H, a.l2norm, a.scalar_gate);
   return hipGetLastError();
 }
 
@@ -277,7 +279,8 @@ static hipError_t launch_fused_t(const FusedDecodeArgs& a) {
   const int nbh = a.B * a.H;
   if (nbh == 0) return hipSuccess;
   FusedDecodeParams p{a.xq, a.xk, a.xv, a.wq, a.wk, a.wv, a.bq, a.bk, a.bv, a.cq, a.ck, a.cv,
-                      a.log_alpha, a.beta, a.mask, a.state, a.slot, a.o, a.H, a.S, a.W, a.l2norm, a.silu};
+                      a.log_alpha, a.beta, a.mask, a.state, a.slot, a.o, a.H, a.S, a.W, a.l2norm, a.silu,
+                      a.scalar_gate};
   hipLaunchKernelGGL((fused_decode_kernel<DT, K, V>), dim3(nbh), dim3(DecodeShape<K, V>::kThreads), 0,
                      (hipStream_t)a.stream, p);
   return hipGetLastError();

@@ -113,6 +113,8 @@ template <> struct Raw8<1> {
     a = *reinterpret_cast<const float4*>(p + i);
     b = *reinterpret_cast<const float4*>(p + i + 4);
   }
+  // one value in all eight places
+  __device__ __forceinline__ void fill(float x) { a = make_float4(x, x, x, x); b = a; }
   __device__ __forceinline__ void keep(bool ok) {
     a.x = ok ? a.x : 0.f; a.y = ok ? a.y : 0.f; a.z = ok ? a.z : 0.f; a.w = ok ? a.w : 0.f;
     b.x = ok ? b.x : 0.f; b.y = ok ? b.y : 0.f; b.z = ok ? b.z : 0.f; b.w = ok ? b.w : 0.f;

@@ -13,7 +13,7 @@ struct DecodeArgs {
   const uint8_t* mask;
   float* state;
   void* o;
-  int B, H, dk, dv, dtype, l2norm;
+  int B, H, dk, dv, dtype, l2norm, scalar_gate;
   void* stream;
 };
 
@@ -29,7 +29,7 @@ struct FusedDecodeArgs {
   float* state;                            // [S, H, dk, dv]
   const int32_t* slot;                     // [B] or null (slot b)
   void* o;
-  int B, H, S, dk, dv, W, dtype, l2norm, silu;
+  int B, H, S, dk, dv, W, dtype, l2norm, silu, scalar_gate;
   void* stream;
 };
 
@@ -50,7 +50,7 @@ struct PrefillArgs {
   const float* init_state;
   void* o;
   float* final_state;
-  int B, T, H, dk, dv, chunk, dtype, l2norm;
+  int B, T, H, dk, dv, chunk, dtype, l2norm, scalar_gate;
   void* workspace;
   size_t workspace_bytes;
   void* stream;

@@ -86,7 +86,7 @@ struct PrepParams {
   const float *log_alpha, *beta;
   const uint8_t* mask;
   uint16_t* ws;
-  int B, T, H, dk, dv, chunk, NC, l2norm;
+  int B, T, H, dk, dv, chunk, NC, l2norm, scalar_gate;
 };
 
 struct ScanParams {
@@ -265,7 +265,8 @@ prep_kernel(PrepParams p) {
   for (int ks = 0; ks < KS; ++ks) {
     const int c = 32 * ks + cg, cs = c < dk ? c : 0;
     const size_t row = grow(tsafe(rq)) * dk + cs;
-    la_r[ks].load(p.log_alpha, row);
+    if (p.scalar_gate) la_r[ks].fill(p.log_alpha[grow(tsafe(rq))]);   // one gate per (t, h)
+    else la_r[ks].load(p.log_alpha, row);
     k_r[ks].load(kg, row);
     q_r[ks].load(qg, row);
   }
@@ -1272,7 +1273,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const size_t chunks_bytes = (size_t)nbh * NC * WsLayout<K, V, C, DT == 1>::kElems * 2;
   if (NC > 0) {
     PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace,
-                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm};
+                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate};
     hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC * a.H, a.B), dim3(kPrepThreads), 0, st, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

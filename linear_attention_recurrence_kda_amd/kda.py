@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
-KDA_FLAG_L2NORM_QK, KDA_FLAG_SILU = 1, 2
+KDA_FLAG_L2NORM_QK, KDA_FLAG_SILU, KDA_FLAG_SCALAR_GATE = 1, 2, 4
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
           -3: "KDA_ERR_WORKSPACE", -4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
@@ -110,7 +110,7 @@ def prefill_workspace_size(B, T, H, dk, dv, chunk, dtype_code) -> int:
 
 
 def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
-                  l2norm_qk=False, out=None, final_state=None, workspace=None):
+                  l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False):
     """KDA prefill.  q,k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32), log_alpha [B,T,H,dk] fp32,
     beta [B,T,H] fp32, mask [B,T] uint8/bool or None, initial_state [B,H,dk,dv] fp32 or None.
     Returns (o [B,T,H,dv] in q's dtype, final_state [B,H,dk,dv] fp32)."""
@@ -122,7 +122,7 @@ def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk
     _req(q, "q")
     _req(k, "k", q.dtype, (B, T, H, dk))
     _req(v, "v", q.dtype, (B, T, H, dv))
-    _req(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _req(log_alpha, "log_alpha", torch.float32, (B, T, H) if scalar_gate else (B, T, H, dk))
     _req(beta, "beta", torch.float32, (B, T, H))
     if mask is not None:
         if mask.dtype == torch.bool:
@@ -143,13 +143,15 @@ def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk
     st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
                                _ptr(initial_state), _ptr(out), _ptr(final_state),
                                B, T, H, dk, dv, int(chunk_size), dt,
-                               KDA_FLAG_L2NORM_QK if l2norm_qk else 0,
+                               (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
+                               (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
                                _ptr(workspace), wbytes, _stream())
     _check("kda_chunk_prefill", st)
     return out, final_state
 
 
-def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out=None):
+def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out=None,
+                scalar_gate=False):
     """One decode step.  q,k [B,H,dk], v [B,H,dv], log_alpha [B,H,dk], beta [B,H],
     state [B,H,dk,dv] fp32 updated in place, mask [B] or None.  Returns o [B,H,dv]."""
     import torch
@@ -160,7 +162,7 @@ def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out
     _req(q, "q")
     _req(k, "k", q.dtype, (B, H, dk))
     _req(v, "v", q.dtype, (B, H, dv))
-    _req(log_alpha, "log_alpha", torch.float32, (B, H, dk))
+    _req(log_alpha, "log_alpha", torch.float32, (B, H) if scalar_gate else (B, H, dk))
     _req(beta, "beta", torch.float32, (B, H))
     _req(state, "state", torch.float32, (B, H, dk, dv))
     if mask is not None:
@@ -172,14 +174,15 @@ def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out
     _req(out, "out", q.dtype, (B, H, dv))
     st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
                              _ptr(state), _ptr(out), B, H, dk, dv, dt,
-                             KDA_FLAG_L2NORM_QK if l2norm_qk else 0, _stream())
+                             (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
+                             (KDA_FLAG_SCALAR_GATE if scalar_gate else 0), _stream())
     _check("kda_decode_step", st)
     return out
 
 
 def decode_step_fused(xq, xk, xv, wq, wk, wv, cache_q, cache_k, cache_v, log_alpha, beta,
                       state, H, mask=None, slot=None, biases=None, l2norm_qk=False, silu=False,
-                      out=None):
+                      out=None, scalar_gate=False):
     """One fused decode step: the three short convs at T = 1 (caches updated in place), the
     optional q/k L2 norm and the state update, in one launch.  xq, xk [B,H*dk], xv [B,H*dv]
     raw inputs; wq, wk [H*dk,W], wv [H*dv,W] fp32; caches [B,W-1,H*d] (x's dtype);
@@ -202,7 +205,7 @@ def decode_step_fused(xq, xk, xv, wq, wk, wv, cache_q, cache_k, cache_v, log_alp
     _req(cache_q, "cache_q", xq.dtype, (B, W - 1, H * dk))
     _req(cache_k, "cache_k", xq.dtype, (B, W - 1, H * dk))
     _req(cache_v, "cache_v", xq.dtype, (B, W - 1, H * dv))
-    _req(log_alpha, "log_alpha", torch.float32, (B, H, dk))
+    _req(log_alpha, "log_alpha", torch.float32, (B, H) if scalar_gate else (B, H, dk))
     _req(beta, "beta", torch.float32, (B, H))
     _req(state, "state", torch.float32, (S, H, dk, dv))
     bq = bk = bv = None
@@ -220,7 +223,8 @@ def decode_step_fused(xq, xk, xv, wq, wk, wv, cache_q, cache_k, cache_v, log_alp
     if out is None:
         out = torch.empty((B, H, dv), dtype=xq.dtype, device=xq.device)
     _req(out, "out", xq.dtype, (B, H, dv))
-    flags = (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_SILU if silu else 0)
+    flags = ((KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_SILU if silu else 0) |
+             (KDA_FLAG_SCALAR_GATE if scalar_gate else 0))
     st = lib.kda_decode_step_fused(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv),
                                    _ptr(bq), _ptr(bk), _ptr(bv), _ptr(cache_q), _ptr(cache_k),
                                    _ptr(cache_v), _ptr(log_alpha), _ptr(beta), _ptr(mask),

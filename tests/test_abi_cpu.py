@@ -84,7 +84,7 @@ def test_fused_decode_validation(lib):
     assert _fused(lib, W=5) == UNSUPPORTED
     assert _fused(lib, W=1) == UNSUPPORTED
     assert _fused(lib, dtype=3) == INVALID
-    assert _fused(lib, flags=4) == INVALID
+    assert _fused(lib, flags=8) == INVALID
     assert _fused(lib, S=-1) == INVALID
     assert _fused(lib, S=1) == INVALID              # no slot array: sequence b needs slot b < S
     assert _fused(lib, xv=None) == INVALID
