@@ -108,7 +108,7 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * and 256 run as 64-token chunks); B, H <= 65535; H times the number of
  * chunks < 2^31 (KDA_ERR_UNSUPPORTED otherwise);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
- * log_alpha.  The ragged tail of the last chunk is handled as masked
+ * and log_alpha unless KDA_FLAG_SCALAR_GATE is set.  The ragged tail of the last chunk is handled as masked
  * positions.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
  * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
  * bytes of device memory (may be NULL when that size is 0).
@@ -118,6 +118,53 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       const float* init_state, void* o, float* final_state,
                       int B, int T, int H, int dk, int dv, int chunk, int dtype,
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace kda_chunk_prefill_varlen needs for N packed
+ * sequences of T tokens in total (0 when none is needed; 0 as well for
+ * arguments that the call itself would reject).  It depends on N and T only,
+ * not on how the tokens are split between the sequences.
+ */
+size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int dv, int chunk,
+                                               int dtype);
+
+/*
+ * Chunked prefill of N sequences of different lengths packed end to end
+ * without padding (continuous batching and prefix reuse are what serving
+ * stacks must support without breaking KDA: remio.ai page, sections on the
+ * software-stack risk and on what to watch after the release).  Sequence i
+ * owns tokens [cu_seqlens[i], cu_seqlens[i+1]) of the packed arrays and runs
+ * the recurrence above from init_state[i] over those tokens only: no state or
+ * output crosses a boundary (dev.to prefix-invariance page: the output at a
+ * position depends on its own prefix and nothing else).  Each sequence's
+ * chunks start at its first token, so its results equal those of
+ * kda_chunk_prefill on that sequence alone with the same chunk, bit for bit.
+ *
+ *   q, k        [T,H,dk]     dtype (T = total tokens)
+ *   v           [T,H,dv]     dtype
+ *   log_alpha   [T,H,dk]     fp32, finite, <= 0; [T,H] with KDA_FLAG_SCALAR_GATE
+ *   beta        [T,H]        fp32 in [0,1]
+ *   cu_seqlens  [N+1]        int32 device array, cu_seqlens[0] = 0,
+ *                            non-decreasing, cu_seqlens[N] = T
+ *   init_state  [N,H,dk,dv]  fp32, NULL = zeros
+ *   o           [T,H,dv]     dtype, written
+ *   final_state [N,H,dk,dv]  fp32, written; may be the same pointer as init_state
+ *
+ * Every token is valid (there is no mask: a packed batch has no padding).  A
+ * sequence of length 0 copies its init_state to final_state.  cu_seqlens is
+ * read on the device, not on the host: entries outside [0, T] are clamped
+ * into it and a decreasing entry gives an empty sequence, so a malformed
+ * array gives wrong results but no out-of-bounds access.  Supported: as
+ * kda_chunk_prefill with B = N (N <= 65535), and H times (ceil(T/chunk) + N)
+ * < 2^31.  16-byte aligned: q, k, v, and log_alpha unless KDA_FLAG_SCALAR_GATE
+ * is set.
+ * `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
+ */
+int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const int32_t* cu_seqlens,
+                             const float* init_state, void* o, float* final_state,
+                             int N, int T, int H, int dk, int dv, int chunk, int dtype,
+                             unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One decode step: a single new token per sequence, state updated in place

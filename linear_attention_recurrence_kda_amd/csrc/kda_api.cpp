@@ -45,39 +45,69 @@ int kda_last_hip_error(void) { return g_last_hip_error; }
 size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return 0;
   if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535) return 0;
-  return kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
+  return kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype, false);
+}
+
+size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int dv, int chunk, int dtype) {
+  if (N < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return 0;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || N > 65535) return 0;
+  return kda::prefill_workspace_bytes(N, T, H, dk, dv, chunk, dtype, true);
+}
+
+// The checks and the launch shared by the batch layout (B rows of T tokens, optional mask)
+// and the packed layout (B sequences of T tokens in total, cu_seqlens given).
+static int prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const uint8_t* mask, const int32_t* cu_seqlens, bool varlen,
+                         const float* init_state, void* o, float* final_state, int B, int T, int H,
+                         int dk, int dv, int chunk, int dtype, unsigned flags, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
+      !kda::prefill_grid_ok(B, T, H, chunk, varlen))
+    return KDA_ERR_UNSUPPORTED;
+  const bool work = (size_t)B * H > 0;
+  if (work) {
+    if (final_state == nullptr || !aligned(final_state, 4)) return KDA_ERR_INVALID_ARG;
+    if (init_state != nullptr && !aligned(init_state, 4)) return KDA_ERR_INVALID_ARG;
+    if (varlen && (cu_seqlens == nullptr || !aligned(cu_seqlens, 4))) return KDA_ERR_INVALID_ARG;
+    if (T > 0) {
+      // q, k, v and the per-channel log_alpha are read with 16-byte vector loads; the rest,
+      // the per-head gate included, element by element
+      const void* vec[] = {q, k, v};
+      for (const void* p : vec)
+        if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+      if (o == nullptr || beta == nullptr || log_alpha == nullptr) return KDA_ERR_INVALID_ARG;
+      if (!aligned(log_alpha, (flags & KDA_FLAG_SCALAR_GATE) ? 4 : 16)) return KDA_ERR_INVALID_ARG;
+      if (!aligned(o, elem_bytes(dtype)) || !aligned(beta, 4)) return KDA_ERR_INVALID_ARG;
+    }
+  }
+  const size_t need = kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype, varlen);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return KDA_ERR_WORKSPACE;
+  if (!work) return KDA_OK;
+  kda::PrefillArgs a{q, k, v, log_alpha, beta, mask, init_state, o, final_state,
+                     B, T, H, dk, dv, chunk, dtype, (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0,
+                     (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, workspace, workspace_bytes, stream,
+                     varlen ? cu_seqlens : nullptr};
+  return hip_status(kda::launch_prefill(a));
 }
 
 int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
                       const float* beta, const uint8_t* mask, const float* init_state, void* o,
                       float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
-  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
-  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
-      !kda::prefill_grid_ok(T, H, chunk))
-    return KDA_ERR_UNSUPPORTED;
-  const bool work = (size_t)B * H > 0;
-  if (work) {
-    if (final_state == nullptr || !aligned(final_state, 4)) return KDA_ERR_INVALID_ARG;
-    if (init_state != nullptr && !aligned(init_state, 4)) return KDA_ERR_INVALID_ARG;
-    if (T > 0) {
-      // q, k, v, log_alpha are read with 16-byte vector loads; the rest element by element
-      const void* vec[] = {q, k, v, log_alpha};
-      for (const void* p : vec)
-        if (p == nullptr || !aligned16(p)) return KDA_ERR_INVALID_ARG;
-      if (o == nullptr || beta == nullptr) return KDA_ERR_INVALID_ARG;
-      if (!aligned(o, elem_bytes(dtype)) || !aligned(beta, 4)) return KDA_ERR_INVALID_ARG;
-    }
-  }
-  const size_t need = kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
-    return KDA_ERR_WORKSPACE;
-  if (!work) return KDA_OK;
-  kda::PrefillArgs a{q, k, v, log_alpha, beta, mask, init_state, o, final_state,
-                     B, T, H, dk, dv, chunk, dtype, (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0,
-                     (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, workspace, workspace_bytes, stream};
-  return hip_status(kda::launch_prefill(a));
+  return prefill_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, o, final_state, B, T, H,
+                       dk, dv, chunk, dtype, flags, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const int32_t* cu_seqlens, const float* init_state,
+                             void* o, float* final_state, int N, int T, int H, int dk, int dv, int chunk,
+                             int dtype, unsigned flags, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return prefill_entry(q, k, v, log_alpha, beta, nullptr, cu_seqlens, true, init_state, o, final_state, N, T,
+                       H, dk, dv, chunk, dtype, flags, workspace, workspace_bytes, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

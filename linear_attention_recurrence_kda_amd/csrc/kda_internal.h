@@ -54,15 +54,17 @@ struct PrefillArgs {
   void* workspace;
   size_t workspace_bytes;
   void* stream;
+  const int32_t* cu_seqlens;               // packed sequences (then B = their number), or null
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
-size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype);
+// varlen: B packed sequences of T tokens in total (cu_seqlens given)
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen);
 bool prefill_supported(int dk, int dv, int chunk);
 // the chunk-local kernel's grid: H times the number of chunks below 2^31
-bool prefill_grid_ok(int T, int H, int chunk);
+bool prefill_grid_ok(int B, int T, int H, int chunk, bool varlen);
 
 }  // namespace kda

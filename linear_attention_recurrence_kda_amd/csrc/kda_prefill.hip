@@ -81,11 +81,15 @@ __device__ __forceinline__ size_t tri_off(int I, int ks, int lane) {
   return ((size_t)(tri_before(I) + ks) * 64 + lane) * 8;
 }
 
+// Packed sequences of different lengths (varlen): chunk g of the packed layout spans tokens
+// [span[g].x, span[g].y), its first token and the end of its sequence; x < 0 past the last
+// chunk.  Sequence i owns chunks first[i] .. first[i + 1] - 1.
 struct PrepParams {
   const void *q, *k, *v;
   const float *log_alpha, *beta;
   const uint8_t* mask;
   uint16_t* ws;
+  const int2* span;                        // varlen chunk spans, or null (batch layout)
   int B, T, H, dk, dv, chunk, NC, l2norm, scalar_gate;
 };
 
@@ -96,6 +100,8 @@ struct ScanParams {
   void* o;
   const uint16_t* ws;
   void* sink;
+  const int2* seq;                         // varlen: each sequence's [first token, end), or null
+  const int32_t* first;                    // varlen: each sequence's first chunk (N + 1 entries)
   int B, T, H, dk, dv, chunk, NC, NT, nbh;
 };
 
@@ -243,13 +249,20 @@ prep_kernel(PrepParams p) {
   const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);          // uniform: loops over row tiles stay scalar
-  const int t0 = n * p.chunk;
+  // the chunk's first token and the end of its sequence
+  int t0 = n * p.chunk, tend = p.T;
+  if (p.span != nullptr) {
+    const int2 sp = p.span[n];
+    if (sp.x < 0) return;                                            // past the last packed chunk
+    t0 = sp.x;
+    tend = sp.y;
+  }
   const int dk = p.dk, dv = p.dv;
   const Raw* qg = (const Raw*)p.q;
   const Raw* kg = (const Raw*)p.k;
   uint16_t* wsb = p.ws + ((size_t)(b * p.H + h) * p.NC + n) * L::kElems;
   auto grow = [&](int t) -> size_t { return ((size_t)b * p.T + t) * p.H + h; };
-  auto tsafe = [&](int r) -> int { const int t = t0 + r; return t < p.T ? t : p.T - 1; };
+  auto tsafe = [&](int r) -> int { const int t = t0 + r; return t < tend ? t : tend - 1; };
   // any readable bytes stand in for the mask when there is none (the value is ignored)
   const uint8_t* mp = p.mask != nullptr ? p.mask : reinterpret_cast<const uint8_t*>(p.beta);
 
@@ -272,7 +285,7 @@ prep_kernel(PrepParams p) {
   }
   const float beta_r = p.beta[grow(tsafe(rq))];
   const uint8_t m_r = mp[(size_t)b * p.T + tsafe(rq)];
-  const bool rok = rows && rq < p.chunk && t0 + rq < p.T && (p.mask == nullptr || m_r != 0);
+  const bool rok = rows && rq < p.chunk && t0 + rq < tend && (p.mask == nullptr || m_r != 0);
   // q and k of rows that are not valid and of channels past dk become 0 here
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -800,14 +813,25 @@ scan_kernel(ScanParams p) {
   auto srow = [&](int M) __attribute__((always_inline)) { return (SRT % 4 == 0) || (M < SRT); };
   auto tri = [&](int ks) __attribute__((always_inline)) { return ks == 0 || ks < nsteps; };
   const int dk = p.dk, dv = p.dv;
-  const uint16_t* wsh = p.ws + (size_t)bh * p.NC * L::kElems;
-  const int last = p.NC - 1;
+  // the sequence this workgroup scans: its first token, its length, its first chunk in
+  // the workspace and its number of chunks (row b of the batch, or packed sequence b)
+  size_t seq_tok0 = (size_t)b * p.T, ws_chunk0 = (size_t)bh * p.NC;
+  int seq_T = p.T, NCs = p.NC;
+  if (p.seq != nullptr) {
+    const int2 sq = p.seq[b];
+    seq_tok0 = (size_t)sq.x;
+    seq_T = sq.y - sq.x;
+    ws_chunk0 = (size_t)h * p.NC + p.first[b];
+    NCs = p.first[b + 1] - p.first[b];
+  }
+  const uint16_t* wsh = p.ws + ws_chunk0 * L::kElems;
+  const int last = NCs - 1;
   // tokens are H * dv elements apart in q, k, v and o; byte offsets inside a chunk stay
   // below 2^32 (checked on the host)
   const size_t row_bytes = (size_t)p.H * dv * sizeof(Tv);
   const uint32_t col_bytes = (uint32_t)(((size_t)h * dv + v0 + lane % 16) * sizeof(Tv));
   auto token_base = [&](int t0) __attribute__((always_inline)) {
-    return ((size_t)b * p.T + t0) * row_bytes;
+    return (seq_tok0 + t0) * row_bytes;
   };
   auto ld16 = [&](const uint16_t* src) __attribute__((always_inline)) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(src);
@@ -876,7 +900,7 @@ scan_kernel(ScanParams p) {
       o_lane[i] = (uint32_t)((16 * I + 4 * (lane / 16) + i) * row_bytes) + col_bytes;
     auto out_step = [&](const Ou& o, int n, auto&& loads) __attribute__((always_inline)) {
       const int t0 = n * p.chunk;
-      const bool full = (p.chunk == C) && (t0 + C <= p.T);         // every row in range
+      const bool full = (p.chunk == C) && (t0 + C <= seq_T);       // every row in range
       unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
       float4 gv;
       if (wave == 4) gv = load_gv(n + 2);
@@ -911,7 +935,7 @@ scan_kernel(ScanParams p) {
         for (int i = 0; i < kStores; ++i) {
           const int rr = 16 * I + 4 * (lane / 16) + i;
           Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i]);
-          if (!full && !(rr < p.chunk && t0 + rr < p.T)) dst = sink + 16 * i + (lane % 16);
+          if (!full && !(rr < p.chunk && t0 + rr < seq_T)) dst = sink + 16 * i + (lane % 16);
           E::st(dst, 0, o4[0][i] + o4[1][i]);
         }
       } else {
@@ -927,8 +951,8 @@ scan_kernel(ScanParams p) {
     };
 
     Ou oA, oB;
-    if (p.NC > 0) { load_out(0, 0, oA); load_out(1, 0, oA); }
-    if (wave == 4 && p.NC > 0) {
+    if (NCs > 0) { load_out(0, 0, oA); load_out(1, 0, oA); }
+    if (wave == 4 && NCs > 0) {
       const float4 g0 = load_gv(0), g1 = load_gv(1);
       store_gv(0, g0);
       store_gv(1, g1);
@@ -936,12 +960,12 @@ scan_kernel(ScanParams p) {
     wait_lgkm();
     wg_barrier();                                    // initial state and V^T in LDS
     int n = 0;
-    for (; n + 1 < p.NC; n += 2) {
+    for (; n + 1 < NCs; n += 2) {
       out_step(oA, n, [&](int part) __attribute__((always_inline)) { load_out(part, n + 1, oB); });
       const int nn = n + 2 <= last ? n + 2 : last;
       out_step(oB, n + 1, [&](int part) __attribute__((always_inline)) { load_out(part, nn, oA); });
     }
-    if (n < p.NC) out_step(oA, n, [](int) {});
+    if (n < NCs) out_step(oA, n, [](int) {});
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
@@ -956,7 +980,7 @@ scan_kernel(ScanParams p) {
   // range ends at token T: rows past T read as 0
   auto load_v = [&](int n) __attribute__((always_inline)) -> u32x4 {
     const int t0 = n * p.chunk;
-    const unsigned long long span = (unsigned long long)(p.T - t0) * row_bytes;
+    const unsigned long long span = (unsigned long long)(seq_T - t0) * row_bytes;
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<Tv*>(vg) + token_base(t0) / sizeof(Tv), (short)0,
         (int)(uint32_t)(span < 0xffffffffull ? span : 0xffffffffull), kBufWord3);
@@ -1058,7 +1082,7 @@ scan_kernel(ScanParams p) {
   const uint32_t tile_bytes = (uint32_t)(((size_t)h * dv + v0) * sizeof(Tv));
   auto warm_chunk = [&](int n) __attribute__((always_inline)) -> uint32_t {
     const unsigned char* ws_line = reinterpret_cast<const unsigned char*>(wsh + (size_t)n * L::kElems) + pf_off;
-    const int t0 = n * p.chunk, tmax = p.T - 1 - t0;
+    const int t0 = n * p.chunk, tmax = seq_T - 1 - t0;
     const unsigned char* v_line = reinterpret_cast<const unsigned char*>(vg) + token_base(t0) +
                                   (uint32_t)(pf_row < tmax ? pf_row : tmax) * (uint32_t)row_bytes + tile_bytes;
     return *reinterpret_cast<const uint32_t*>(pf_row >= 0 ? v_line : ws_line);
@@ -1175,17 +1199,17 @@ scan_kernel(ScanParams p) {
   publish_state();
   Ch opA, opB;
   uint32_t warmA = 0, warmB = 0;
-  if (p.NC > 0) {
+  if (NCs > 0) {
     u32x4 v;
 #pragma unroll
     for (int idx = 0; idx < kLoads; ++idx) issue_load(idx, 0, opA, v);
     write_vt(v, load_valid(0));
   }
-  if (p.NC > 1) warmB = warm_chunk(1);
+  if (NCs > 1) warmB = warm_chunk(1);
   wait_lgkm();
   wg_barrier();                                      // initial state and V^T in LDS
   int n = 0;
-  for (; n + 1 < p.NC; n += 2) {
+  for (; n + 1 < NCs; n += 2) {
     u32x4 vB;
     chain_step(opA, n, true, vB, warmB, [&](int g) __attribute__((always_inline)) {
       if (g < kGroups) load_group(g, n + 1, opB, vB);
@@ -1198,7 +1222,7 @@ scan_kernel(ScanParams p) {
       else warmB = warm_chunk(n + 3 <= last ? n + 3 : last);
     });
   }
-  if (n < p.NC) {                                    // odd chunk count: the last one
+  if (n < NCs) {                                    // odd chunk count: the last one
     const u32x4 none = {0u, 0u, 0u, 0u};
     chain_step(opA, n, false, none, warmB, [](int) {});
   }
@@ -1216,6 +1240,50 @@ scan_kernel(ScanParams p) {
       if (row < dk) p.final_state[((size_t)bh * dk + row) * dv + v0 + (lane % 16)] = S[m][i];
     }
   }
+}
+
+// ================================================================ packed sequences
+// The chunk table of N packed sequences cu[i] .. cu[i + 1] - 1, built by one workgroup:
+// first[i] = the number of chunks of the sequences before i (i = 0 .. N), seq[i] = the
+// sequence's [first token, end) and span[g] = (first token, end of its sequence) of every
+// chunk g, (-1, -1) past the last.  Token bounds are clamped into [0, T] and chunk indexes
+// to the NCmax chunks the workspace holds, so a malformed cu cannot send any kernel
+// outside its buffers.
+constexpr int kSetupThreads = 1024;
+__global__ void __launch_bounds__(kSetupThreads)
+varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCmax,
+                    int2* __restrict__ span, int2* __restrict__ seq, int32_t* __restrict__ first) {
+  __shared__ int s_scan[kSetupThreads];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base <= N; base += kSetupThreads) {
+    const int i = base + tid;
+    int start = 0, end = 0, nc = 0;
+    if (i < N) {
+      start = min(max(cu[i], 0), T);
+      end = min(max(cu[i + 1], start), T);
+      nc = (end - start + C - 1) / C;
+      seq[i] = make_int2(start, end);
+    }
+    s_scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < kSetupThreads; off <<= 1) {     // inclusive scan of the counts
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const int carry = s_carry;
+    const int excl = min(carry + s_scan[tid] - nc, NCmax);
+    if (i <= N) first[i] = excl;
+    for (int j = 0; j < nc && excl + j < NCmax; ++j) span[excl + j] = make_int2(start + j * C, end);
+    __syncthreads();
+    if (tid == kSetupThreads - 1) s_carry = carry + s_scan[tid];
+    __syncthreads();
+  }
+  for (int g = min(s_carry, NCmax) + tid; g < NCmax; g += kSetupThreads) span[g] = make_int2(-1, -1);
 }
 
 // ================================================================ host side
@@ -1250,36 +1318,61 @@ static size_t chunk_ws_elems(int K, int V, int C, int dtype) {
   return 0;
 }
 
-bool prefill_grid_ok(int T, int H, int chunk) {
+// chunks the workspace holds: per batch row, or for N packed sequences the bound
+// T / chunk + N (each sequence adds at most one partial chunk)
+static long long prefill_chunks(int B, int T, int chunk, bool varlen) {
   const int c = run_chunk(chunk);
   const long long nc = T > 0 ? ((long long)T + c - 1) / c : 0;
-  return nc * H <= 0x7fffffffll;
+  return varlen ? nc + B : nc;
 }
 
-size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
-  if (T == 0 || B == 0 || H == 0) return 0;
-  chunk = run_chunk(chunk);
-  const int NC = (T + chunk - 1) / chunk;
-  return (size_t)B * H * NC * chunk_ws_elems(pad_k(dk), dv, tile_chunk(chunk), dtype) * 2 + kSinkBytes;
+bool prefill_grid_ok(int B, int T, int H, int chunk, bool varlen) {
+  return prefill_chunks(B, T, chunk, varlen) * H <= 0x7fffffffll;
+}
+
+static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen) {
+  if (B == 0 || H == 0 || (T == 0 && !varlen)) return 0;
+  const long long NC = prefill_chunks(B, T, chunk, varlen);
+  const size_t per_chunk = chunk_ws_elems(pad_k(dk), dv, tile_chunk(run_chunk(chunk)), dtype) * 2;
+  if (!varlen) return (size_t)B * H * NC * per_chunk + kSinkBytes;
+  // packed: H x NC chunks, the sink, then the chunk table (span, seq, first)
+  return (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + align16((size_t)B * 8) +
+         align16((size_t)(B + 1) * 4);
 }
 
 template <int DT, int K, int V, int C>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if ((size_t)(C + 1) * a.H * a.dv * 4 > 0xffffffffull) return hipErrorInvalidValue;   // 32-bit output offsets
-  const int NC = (a.T + a.chunk - 1) / a.chunk;
+  const bool varlen = a.cu_seqlens != nullptr;
+  const int NC = (int)prefill_chunks(a.B, a.T, a.chunk, varlen);
   const int NT = a.dv / kVT;
   const int nbh = a.B * a.H;
-  const size_t chunks_bytes = (size_t)nbh * NC * WsLayout<K, V, C, DT == 1>::kElems * 2;
+  const size_t chunks_bytes = (size_t)(varlen ? a.H : nbh) * NC * WsLayout<K, V, C, DT == 1>::kElems * 2;
+  int2 *span = nullptr, *seq = nullptr;
+  int32_t* first = nullptr;
+  if (varlen) {
+    unsigned char* tail = (unsigned char*)a.workspace + chunks_bytes + kSinkBytes;
+    span = reinterpret_cast<int2*>(tail);
+    seq = reinterpret_cast<int2*>(tail + align16((size_t)NC * 8));
+    first = reinterpret_cast<int32_t*>(tail + align16((size_t)NC * 8) + align16((size_t)a.B * 8));
+    hipLaunchKernelGGL(varlen_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.cu_seqlens, a.B, a.T,
+                       a.chunk, NC, span, seq, first);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (NC > 0) {
-    PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace,
+    PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace, span,
                   a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate};
-    hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC * a.H, a.B), dim3(kPrepThreads), 0, st, pp);
+    hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC * a.H, varlen ? 1 : a.B), dim3(kPrepThreads), 0,
+                       st, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ScanParams sp{a.v, a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
-                NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr,
+                NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr, seq, first,
                 a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
   const int groups = (nbh + 7) / 8;
   hipLaunchKernelGGL((scan_kernel<DT, K, V, C>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);

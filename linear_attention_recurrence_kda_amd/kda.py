@@ -20,7 +20,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
           -3: "KDA_ERR_WORKSPACE", -4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
            "kda_chunk_prefill_workspace_size", "kda_chunk_prefill", "kda_decode_step",
-           "kda_short_conv", "kda_decode_step_fused")
+           "kda_short_conv", "kda_decode_step_fused", "kda_chunk_prefill_varlen_workspace_size",
+           "kda_chunk_prefill_varlen")
 
 _lib = None
 
@@ -63,6 +64,11 @@ def load():
     lib.kda_decode_step_fused.restype = i
     lib.kda_decode_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, fp, vp, vp, vp, fp, fp, up,
                                           fp, vp, vp, i, i, i, i, i, i, i, u, vp]
+    lib.kda_chunk_prefill_varlen_workspace_size.restype = sz
+    lib.kda_chunk_prefill_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_chunk_prefill_varlen.restype = i
+    lib.kda_chunk_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp,
+                                             i, i, i, i, i, i, i, u, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -147,6 +153,52 @@ def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk
                                (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
                                _ptr(workspace), wbytes, _stream())
     _check("kda_chunk_prefill", st)
+    return out, final_state
+
+
+def prefill_varlen_workspace_size(N, T, H, dk, dv, chunk, dtype_code) -> int:
+    return int(load().kda_chunk_prefill_varlen_workspace_size(N, T, H, dk, dv, chunk, dtype_code))
+
+
+def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=None, chunk_size=64,
+                         l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False):
+    """KDA prefill of N sequences packed end to end.  q,k [T,H,dk], v [T,H,dv] (bf16 or fp32),
+    log_alpha [T,H,dk] fp32 ([T,H] with scalar_gate), beta [T,H] fp32, cu_seqlens [N+1] int32
+    on the GPU (sequence i = tokens cu_seqlens[i] .. cu_seqlens[i+1]-1), initial_state
+    [N,H,dk,dv] fp32 or None.  Returns (o [T,H,dv] in q's dtype, final_state [N,H,dk,dv] fp32)."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (T, H, dk))
+    _req(v, "v", q.dtype, (T, H, dv))
+    _req(log_alpha, "log_alpha", torch.float32, (T, H) if scalar_gate else (T, H, dk))
+    _req(beta, "beta", torch.float32, (T, H))
+    _req(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    _req(out, "out", q.dtype, (T, H, dv))
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    _req(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    need = prefill_varlen_workspace_size(N, T, H, dk, dv, chunk_size, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                      _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                      N, T, H, dk, dv, int(chunk_size), dt,
+                                      (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
+                                      (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
+                                      _ptr(workspace), wbytes, _stream())
+    _check("kda_chunk_prefill_varlen", st)
     return out, final_state
 
 

@@ -120,6 +120,10 @@ def test_prefill_validation(lib):
     assert _prefill(lib, sT=None) == INVALID
     assert _prefill(lib, s0=ctypes.c_void_p(0x10002)) == INVALID
     assert _prefill(lib, la=MISALIGNED) == INVALID
+    # the per-head gate is read element by element: 4-byte alignment passes (the call then
+    # stops at the short workspace, before any launch)
+    assert _prefill(lib, la=MISALIGNED, flags=4, wsb=16) == WORKSPACE
+    assert _prefill(lib, la=ctypes.c_void_p(0x10002), flags=4) == INVALID
     assert _prefill(lib, v=MISALIGNED) == INVALID
     assert _prefill(lib, o=ctypes.c_void_p(0x10001)) == INVALID
     assert _prefill(lib, wsb=16) == WORKSPACE
@@ -141,6 +145,55 @@ def test_workspace_size_query(lib):
     for big in (128, 256):                               # run as 64-token chunks: same workspace
         assert f(4, 4096, 32, 128, 128, big, 0) == f(4, 4096, 32, 128, 128, 64, 0)
     assert f(1, 64, 1, 128, 128, 512, 0) == 0
+
+
+def _varlen(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, cu=FAKE, s0=None, o=FAKE, sT=FAKE,
+             N=3, T=200, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_chunk_prefill_varlen(a["q"], a["k"], a["v"], a["la"], a["beta"], a["cu"], a["s0"],
+                                        a["o"], a["sT"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                        a["chunk"], a["dtype"], a["flags"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_varlen_validation(lib):
+    assert _varlen(lib, chunk=48) == UNSUPPORTED
+    assert _varlen(lib, dv=8) == UNSUPPORTED
+    assert _varlen(lib, N=65536) == UNSUPPORTED
+    # H x (ceil(T / chunk) + N) chunk workgroups must stay below 2^31
+    assert _varlen(lib, T=(1 << 29) - 64 * 1000, N=1000, H=256, chunk=64) == UNSUPPORTED
+    assert _varlen(lib, N=-1) == INVALID
+    assert _varlen(lib, T=-1) == INVALID
+    assert _varlen(lib, flags=2) == INVALID
+    assert _varlen(lib, cu=None) == INVALID               # the offsets are required
+    assert _varlen(lib, cu=ctypes.c_void_p(0x10002)) == INVALID
+    assert _varlen(lib, q=MISALIGNED) == INVALID
+    assert _varlen(lib, sT=None) == INVALID
+    assert _varlen(lib, beta=None) == INVALID
+    assert _varlen(lib, wsb=64) == WORKSPACE
+    assert _varlen(lib, ws=None) == WORKSPACE
+    assert _varlen(lib, N=0, cu=None, ws=None, wsb=0) == OK   # no sequence: nothing to do
+
+
+def test_varlen_workspace_size_query(lib):
+    f = lib.kda_chunk_prefill_varlen_workspace_size
+    g = lib.kda_chunk_prefill_workspace_size
+    assert f(0, 100, 32, 128, 128, 64, 0) == 0
+    assert f(2, 100, 32, 128, 128, 48, 0) == 0             # unsupported chunk
+    assert f(-1, 100, 32, 128, 128, 64, 0) == 0
+    assert f(65536, 100, 1, 128, 128, 64, 0) == 0
+    # room for ceil(T / chunk) + N chunks per head, plus the chunk table; T = 0 still needs
+    # the table (empty sequences copy their state through the scan)
+    per_chunk = g(1, 128, 1, 128, 128, 64, 0) - g(1, 64, 1, 128, 128, 64, 0)
+    assert f(3, 0, 1, 128, 128, 64, 0) > 3 * per_chunk
+    for N, T in ((1, 64), (4, 1000), (17, 4096)):
+        nc = -(-T // 64) + N
+        base = f(N, T, 2, 128, 128, 64, 0)
+        assert base % 16 == 0
+        assert base >= 2 * nc * per_chunk
+        # one more chunk per head, and 8 more bytes of chunk table (kept 16-byte aligned)
+        assert 0 <= f(N, T + 64, 2, 128, 128, 64, 0) - (base + 2 * per_chunk) <= 16
+        assert f(N, T, 3, 128, 128, 64, 0) == base + nc * per_chunk
 
 
 def _conv(lib, **kw):

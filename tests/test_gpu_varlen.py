@@ -1,0 +1,179 @@
+"""GPU parity of kda_chunk_prefill_varlen: N sequences of different lengths packed end to end.
+
+Each packed sequence must give, bit for bit, what kda_chunk_prefill gives for that sequence
+alone (its chunks start at its own first token, so the arithmetic is the same) and what the
+right-padded, masked batch gives; and it must match the fp64 oracle run on each sequence.
+Prefix reuse: the state a packed call leaves after a prefix, fed back as the initial state of
+a later packed call holding the continuation beside fresh prompts, continues the sequence."""
+import numpy as np
+import pytest
+
+from linear_attention_recurrence_kda_amd import datagen as D
+from tests.gpu_util import check, device, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed_inputs(lengths, H, dk, dv, dtype, seed, scalar=False):
+    T = int(sum(lengths))
+    inp = {n: x[0] for n, x in D.np_kda_inputs(1, max(T, 1), H, dk, dv, dtype, seed=seed).items()}
+    inp = {n: np.ascontiguousarray(x[:T]) for n, x in inp.items()}
+    if scalar:
+        inp["log_alpha"] = np.ascontiguousarray(inp["log_alpha"][..., 0])
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return inp, cu
+
+
+def _dev(inp, dtype, dev):
+    return {n: to_dev(x, dtype if n in "qkv" else None, dev) for n, x in inp.items()}
+
+
+def _varlen(kda, d, cu, dev, chunk, s0=None, l2=False, scalar=False):
+    return kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                    initial_state=s0, chunk_size=chunk, l2norm_qk=l2, scalar_gate=scalar)
+
+
+@pytest.mark.parametrize("dtype,chunk,l2,scalar", [("bf16", 64, False, False), ("bf16", 32, True, False),
+                                                   ("fp32", 16, False, False), ("bf16", 128, False, True),
+                                                   ("fp32", 64, True, True)])
+def test_varlen_equals_each_sequence_alone_and_padded_batch(dtype, chunk, l2, scalar):
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    lengths = [0, 1, 63, 64, 65, 200, 130, 0, 17]
+    N, H, dk, dv = len(lengths), 3, 128, 64
+    say(f"[case] varlen vs alone and padded {dtype} chunk={chunk} l2={l2} scalar={scalar}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, dtype, seed=31, scalar=scalar)
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=31), dev=dev)
+    d = _dev(inp, dtype, dev)
+    o, sN = _varlen(kda, d, cu, dev, chunk, s0=s0, l2=l2, scalar=scalar)
+    # right-padded batch: sequence i in row i, positions past its length masked
+    Tmax = max(lengths)
+    pad = {n: torch.zeros((N, Tmax) + x.shape[1:], dtype=x.dtype, device=dev) for n, x in d.items()}
+    for i in range(N):
+        for n in pad:
+            pad[n][i, :lengths[i]] = d[n][int(cu[i]):int(cu[i + 1])]
+    mask = to_dev(D.padded_layout(lengths, Tmax, ["right"] * N), dev=dev)
+    op, sp = kda.chunk_prefill(pad["q"], pad["k"], pad["v"], pad["log_alpha"], pad["beta"], mask=mask,
+                               initial_state=s0, chunk_size=chunk, l2norm_qk=l2, scalar_gate=scalar)
+    torch.cuda.synchronize()
+    assert torch.equal(sN, sp), "final states differ from the padded batch"
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        oi, si = kda.chunk_prefill(*(d[n][a:b].unsqueeze(0).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                   initial_state=s0[i:i + 1].contiguous(), chunk_size=chunk, l2norm_qk=l2,
+                                   scalar_gate=scalar)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], oi[0]), f"o of sequence {i} (length {b - a}) differs from the lone run"
+        assert torch.equal(sN[i], si[0]), f"state of sequence {i} differs from the lone run"
+        assert torch.equal(o[a:b], op[i, :b - a]), f"o of sequence {i} differs from the padded batch"
+        if b == a:
+            assert torch.equal(sN[i], s0[i]), "an empty sequence must keep its initial state"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_varlen_matches_oracle(oracle, dtype):
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    lengths = [100, 0, 257, 64, 3]
+    N, H, dk, dv = len(lengths), 2, 64, 128
+    say(f"[case] varlen vs oracle {dtype}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, dtype, seed=32)
+    s0 = D.np_state(N, H, dk, dv, 0.1, seed=32)
+    o, sN = _varlen(kda, _dev(inp, dtype, dev), cu, dev, 64, s0=to_dev(s0, dev=dev), l2=True)
+    go, gs = host(o), host(sN)
+    ro = np.zeros_like(go)
+    rs = np.zeros_like(gs)
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        seq = {n: x[None, a:b] for n, x in inp.items()}
+        oi, si = oracle.c_prefill(**seq, init_state=s0[i:i + 1], l2norm_qk=True)
+        ro[a:b], rs[i] = oi[0], si[0]
+    check("varlen o", go, ro, dtype)
+    check("varlen state", gs, rs, dtype)
+
+
+def test_varlen_prefix_reuse_in_a_mixed_batch(oracle):
+    """Continuous batching with cached prefixes: call 1 packs the prefixes, call 2 packs the
+    continuations (initial state = the cached one) beside a fresh prompt (zero state).  A
+    prefix that ends on a chunk boundary continues bit for bit as the whole sequence run at
+    once; every continuation matches the oracle run on prefix + continuation."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    H, dk, dv = 4, 128, 128
+    prefix, cont, _ = D.continuation_lengths(3, seed=33, prefix_max=700, cont_max=300)
+    prefix[0] = 256                                            # chunk-aligned prefix
+    say(f"[case] varlen prefix reuse prefixes={prefix} continuations={cont}")
+    full = [p + c for p, c in zip(prefix, cont)]
+    whole, _ = _packed_inputs(full, H, dk, dv, "bf16", seed=33)
+    fresh_len = 190
+    fresh, _ = _packed_inputs([fresh_len], H, dk, dv, "bf16", seed=34)
+    starts = np.concatenate([[0], np.cumsum(full)])
+    pre = {n: np.concatenate([x[s:s + p] for s, p in zip(starts, prefix)]) for n, x in whole.items()}
+    con = {n: np.concatenate([x[s + p:s + p + c] for s, p, c in zip(starts, prefix, cont)] + [fresh[n]])
+           for n, x in whole.items()}
+    cu_pre = np.concatenate([[0], np.cumsum(prefix)]).astype(np.int32)
+    cu_con = np.concatenate([[0], np.cumsum(cont + [fresh_len])]).astype(np.int32)
+    _, cached = _varlen(kda, _dev(pre, "bf16", dev), cu_pre, dev, 64)
+    s_in = torch.cat([cached, torch.zeros_like(cached[:1])]).contiguous()
+    o2, s2 = _varlen(kda, _dev(con, "bf16", dev), cu_con, dev, 64, s0=s_in)
+    o_all, s_all = _varlen(kda, _dev(whole, "bf16", dev), np.concatenate([[0], np.cumsum(full)]).astype(np.int32),
+                           dev, 64)
+    torch.cuda.synchronize()
+    # the chunk-aligned prefix: the continuation equals the tail of the single run bit for bit
+    a0 = int(cu_con[0])
+    assert torch.equal(o2[a0:a0 + cont[0]], o_all[prefix[0]:full[0]])
+    assert torch.equal(s2[0], s_all[0])
+    go2, gs2 = host(o2), host(s2)
+    for i in range(3):
+        s, p, c = int(starts[i]), prefix[i], cont[i]
+        seq = {n: x[None, s:s + p + c] for n, x in whole.items()}
+        ro, rs = oracle.c_prefill(**seq)
+        check(f"continuation {i} o", go2[cu_con[i]:cu_con[i + 1]], ro[0, p:], "bf16")
+        check(f"continuation {i} state", gs2[i], rs[0], "bf16")
+    ro, rs = oracle.c_prefill(**{n: x[None] for n, x in fresh.items()})
+    check("fresh prompt o", go2[cu_con[3]:], ro[0], "bf16")
+    check("fresh prompt state", gs2[3], rs[0], "bf16")
+
+
+def test_varlen_state_in_place():
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    lengths = [70, 0, 129]
+    N, H, dk, dv = 3, 2, 128, 128
+    say("[case] varlen final_state aliasing initial_state")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, "bf16", seed=35)
+    d = _dev(inp, "bf16", dev)
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=35), dev=dev)
+    o_ref, s_ref = _varlen(kda, d, cu, dev, 64, s0=s0.clone())
+    st = s0.clone()
+    o, s = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                    initial_state=st, final_state=st)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == st.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(st, s_ref)
+
+
+def test_varlen_serving_mix_equals_lone_runs():
+    """A serving-sized pack: 16 prompts of 1 .. 4096 tokens (uniform), 32 heads of 128 x 128,
+    bf16; every sequence equals its lone run bit for bit."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    r = np.random.default_rng(36)
+    lengths = [int(x) for x in r.integers(1, 4097, 16)]
+    H, dk, dv = 32, 128, 128
+    T = sum(lengths)
+    say(f"[case] varlen serving mix T={T} lengths={lengths}")
+    d = D.torch_kda_inputs(1, T, H, dk, dv, dev, "bf16", seed=36)
+    d = {n: x[0].contiguous() for n, x in d.items()}
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    o, sN = _varlen(kda, d, cu, dev, 64)
+    for i in range(len(lengths)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        oi, si = kda.chunk_prefill(*(d[n][a:b].unsqueeze(0).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")))
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], oi[0]), f"o of sequence {i} (length {b - a})"
+        assert torch.equal(sN[i], si[0]), f"state of sequence {i}"
