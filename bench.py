@@ -7,7 +7,8 @@ One step = one pass of the whole path on synthetic, seeded inputs resident in HB
   * one batched decode step: 256 sequences x 32 heads, fp32 128x128 states ~ N(0, 0.02),
     raw bf16 activations -> width-4 short conv with cache (q, k, v) -> decode step with
     in-kernel L2 normalisation of q and k.
-`value` is prefill tokens/s; the decode state-update GB/s is reported beside it.
+`value` is prefill tokens/s; the decode state-update GB/s is reported beside it, and so is the
+same 128k tokens prefilled as 32 packed prompts of seeded lengths (kda_chunk_prefill_varlen).
 Prints one JSON line.
 """
 import argparse
@@ -195,6 +196,33 @@ def main():
     graph_step_ms = sum(a_.elapsed_time(b_) for a_, b_ in gev) / (5 * 8)
     del graph
 
+    # the same 128k tokens served as 32 prompts packed end to end (kda_chunk_prefill_varlen):
+    # seeded cut points, so lengths vary from a few tokens to several thousand
+    Nv = 32
+    gcut = torch.Generator()
+    gcut.manual_seed(2)
+    cuts = torch.sort(torch.randperm(T - 1, generator=gcut)[:Nv - 1] + 1).values
+    cu = torch.cat([torch.zeros(1, dtype=torch.int64), cuts, torch.full((1,), T)]).to(torch.int32)
+    lens = (cu[1:] - cu[:-1]).tolist()
+    cu_d = cu.to(dev)
+    xv = {n: t[0] for n, t in x.items()}
+    fsv = torch.empty(Nv, H, dk, dv, dtype=torch.float32, device=dev)
+    wsv = torch.empty(kda.prefill_varlen_workspace_size(Nv, T, H, dk, dv, C, kda.KDA_BF16), dtype=torch.uint8,
+                      device=dev)
+
+    def prefill_varlen():
+        kda.chunk_prefill_varlen(xv["q"], xv["k"], xv["v"], xv["log_alpha"], xv["beta"], cu_d, chunk_size=C,
+                                 out=o[0], final_state=fsv, workspace=wsv)
+    prefill_varlen()
+    vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a_, b_ in vev:
+        a_.record()
+        prefill_varlen()
+        b_.record()
+    torch.cuda.synchronize()
+    varlen_ms = sum(a_.elapsed_time(b_) for a_, b_ in vev) / reps
+    del wsv
+
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
     # (read 1 GiB, write 1 GiB), the reference point beside the nominal 8 TB/s
     cn = (1 << 30) // 4
@@ -241,6 +269,10 @@ def main():
                     "hbm_frac_of_copy": pre_gbs / copy_gbs,
                     "model_tflops": pre_tflops, "mfma_frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
                     "roofline_frac": max(pre_gbs / HBM_PEAK_GBS, pre_tflops / MFMA_BF16_PEAK_TFLOPS)},
+        "prefill_varlen": {"N": Nv, "T_total": T, "len_min": min(lens), "len_max": max(lens), "ms": varlen_ms,
+                           "tokens_per_s": T / (varlen_ms * 1e-3),
+                           "algorithmic_GBps": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9,
+                           "hbm_frac": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms, "fused_step_graph_ms": graph_step_ms,
                    "fused_tokens_per_s": Bd / (fused_ms * 1e-3), "state_update_ms": dstep_ms,
                    "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,

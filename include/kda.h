@@ -149,20 +149,35 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  *   init_state  [N,H,dk,dv]  fp32, NULL = zeros
  *   o           [T,H,dv]     dtype, written
  *   final_state [N,H,dk,dv]  fp32, written; may be the same pointer as init_state
+ *   chunk_states [M,H,dk,dv] fp32, written, or NULL: state checkpoints for prefix
+ *                            caching (remio.ai page, software-stack section: prefix
+ *                            caching and the state at chunk boundaries are named among
+ *                            what to test).  Sequence i of length L_i saves the state
+ *                            after each of its first j * state_interval tokens,
+ *                            j = 1 .. floor(L_i / state_interval), in that order, at
+ *                            entries sum_{i' < i} floor(L_i' / state_interval) + j - 1;
+ *                            M is that sum over all sequences.  Passing checkpoint j as
+ *                            init_state for the rest of the sequence continues it bit
+ *                            for bit.
+ *   num_states               entries chunk_states holds (>= M); checkpoints past it
+ *                            are not written
+ *   state_interval           tokens between checkpoints: a positive multiple of chunk
+ *   (num_states and state_interval are ignored when chunk_states is NULL)
  *
  * Every token is valid (there is no mask: a packed batch has no padding).  A
  * sequence of length 0 copies its init_state to final_state.  cu_seqlens is
  * read on the device, not on the host: entries outside [0, T] are clamped
  * into it and a decreasing entry gives an empty sequence, so a malformed
- * array gives wrong results but no out-of-bounds access.  Supported: as
+ * array gives wrong results but no out-of-bounds access (checkpoints included,
+ * as num_states bounds them).  Supported: as
  * kda_chunk_prefill with B = N (N <= 65535), and H times (ceil(T/chunk) + N)
  * < 2^31.  16-byte aligned: q, k, v, and log_alpha unless KDA_FLAG_SCALAR_GATE
- * is set.
- * `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
+ * is set; chunk_states 4-byte aligned.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
  */
 int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, const int32_t* cu_seqlens,
                              const float* init_state, void* o, float* final_state,
+                             float* chunk_states, int num_states, int state_interval,
                              int N, int T, int H, int dk, int dv, int chunk, int dtype,
                              unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -55,6 +55,9 @@ struct PrefillArgs {
   size_t workspace_bytes;
   void* stream;
   const int32_t* cu_seqlens;               // packed sequences (then B = their number), or null
+  float* chunk_states;                     // packed only: the state every state_interval tokens, or null
+  int num_states;                          // entries chunk_states holds
+  int state_interval;                      // a multiple of chunk
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

@@ -83,7 +83,8 @@ __device__ __forceinline__ size_t tri_off(int I, int ks, int lane) {
 
 // Packed sequences of different lengths (varlen): chunk g of the packed layout spans tokens
 // [span[g].x, span[g].y), its first token and the end of its sequence; x < 0 past the last
-// chunk.  Sequence i owns chunks first[i] .. first[i + 1] - 1.
+// chunk.  Sequence i owns chunks first[i] .. first[i + 1] - 1, tokens [seq[i].x, seq[i].y),
+// and its saved states start at entry seq[i].z of the state checkpoints.
 struct PrepParams {
   const void *q, *k, *v;
   const float *log_alpha, *beta;
@@ -100,8 +101,10 @@ struct ScanParams {
   void* o;
   const uint16_t* ws;
   void* sink;
-  const int2* seq;                         // varlen: each sequence's [first token, end), or null
+  const int4* seq;                         // varlen: each sequence's first token, end, first checkpoint
   const int32_t* first;                    // varlen: each sequence's first chunk (N + 1 entries)
+  float* ckpt;                             // varlen: states saved every ck_every chunks, or null
+  int ck_every, ck_cap;                    // ck_cap: entries ckpt holds
   int B, T, H, dk, dv, chunk, NC, NT, nbh;
 };
 
@@ -816,11 +819,12 @@ scan_kernel(ScanParams p) {
   // the sequence this workgroup scans: its first token, its length, its first chunk in
   // the workspace and its number of chunks (row b of the batch, or packed sequence b)
   size_t seq_tok0 = (size_t)b * p.T, ws_chunk0 = (size_t)bh * p.NC;
-  int seq_T = p.T, NCs = p.NC;
+  int seq_T = p.T, NCs = p.NC, ck0 = 0;
   if (p.seq != nullptr) {
-    const int2 sq = p.seq[b];
+    const int4 sq = p.seq[b];
     seq_tok0 = (size_t)sq.x;
     seq_T = sq.y - sq.x;
+    ck0 = sq.z;
     ws_chunk0 = (size_t)h * p.NC + p.first[b];
     NCs = p.first[b + 1] - p.first[b];
   }
@@ -1100,6 +1104,23 @@ scan_kernel(ScanParams p) {
                     ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
     }
   }
+  // this workgroup's 16 columns of the state to a dk x dv fp32 matrix in HBM
+  auto store_state = [&](float* dst) __attribute__((always_inline)) {
+    // the lane index passes through an empty asm so the addresses are formed here, not
+    // hoisted out of the chunk loop into registers held across it
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+      const int M = wave + 4 * m;
+      if (M >= SRT) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * M + 4 * (ln / 16) + i;
+        if (row < dk) dst[(size_t)row * dv + v0 + (ln % 16)] = S[m][i];
+      }
+    }
+  };
   auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -1196,6 +1217,15 @@ scan_kernel(ScanParams p) {
     wg_barrier();                                    // next state and V^T in LDS
   };
 
+  // the state after chunk n when it closes a checkpoint interval (every ck_every full
+  // chunks), for prefix caching
+  auto checkpoint = [&](int n) __attribute__((always_inline)) {
+    if (p.ckpt != nullptr && (n + 1) % p.ck_every == 0 && (n + 1) * p.chunk <= seq_T) {
+      const int idx = ck0 + (n + 1) / p.ck_every - 1;
+      if (idx < p.ck_cap) store_state(p.ckpt + ((size_t)idx * p.H + h) * dk * dv);
+    }
+  };
+
   publish_state();
   Ch opA, opB;
   uint32_t warmA = 0, warmB = 0;
@@ -1215,75 +1245,74 @@ scan_kernel(ScanParams p) {
       if (g < kGroups) load_group(g, n + 1, opB, vB);
       else warmA = warm_chunk(n + 2 <= last ? n + 2 : last);
     });
+    checkpoint(n);
     const int nn = n + 2 <= last ? n + 2 : last;
     u32x4 vA;
     chain_step(opB, n + 1, true, vA, warmA, [&](int g) __attribute__((always_inline)) {
       if (g < kGroups) load_group(g, nn, opA, vA);
       else warmB = warm_chunk(n + 3 <= last ? n + 3 : last);
     });
+    checkpoint(n + 1);
   }
   if (n < NCs) {                                    // odd chunk count: the last one
     const u32x4 none = {0u, 0u, 0u, 0u};
     chain_step(opA, n, false, none, warmB, [](int) {});
+    checkpoint(n);
   }
   asm volatile("" :: "v"(warmA), "v"(warmB));
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- final state
-#pragma unroll
-  for (int m = 0; m < SPW; ++m) {
-    const int M = wave + 4 * m;
-    if (M >= SRT) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * M + 4 * (lane / 16) + i;
-      if (row < dk) p.final_state[((size_t)bh * dk + row) * dv + v0 + (lane % 16)] = S[m][i];
-    }
-  }
+  store_state(p.final_state + (size_t)bh * dk * dv);
 }
 
 // ================================================================ packed sequences
 // The chunk table of N packed sequences cu[i] .. cu[i + 1] - 1, built by one workgroup:
-// first[i] = the number of chunks of the sequences before i (i = 0 .. N), seq[i] = the
-// sequence's [first token, end) and span[g] = (first token, end of its sequence) of every
-// chunk g, (-1, -1) past the last.  Token bounds are clamped into [0, T] and chunk indexes
-// to the NCmax chunks the workspace holds, so a malformed cu cannot send any kernel
-// outside its buffers.
+// first[i] = the number of chunks of the sequences before i (i = 0 .. N); seq[i] = the
+// sequence's first token, its end and the number of state checkpoints (one per `interval`
+// tokens, 0 when interval is 0) of the sequences before it; span[g] = (first token, end of
+// its sequence) of every chunk g, (-1, -1) past the last.  Token bounds are clamped into
+// [0, T] and chunk indexes to the NCmax chunks the workspace holds, so a malformed cu cannot
+// send any kernel outside its buffers.
 constexpr int kSetupThreads = 1024;
 __global__ void __launch_bounds__(kSetupThreads)
-varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCmax,
-                    int2* __restrict__ span, int2* __restrict__ seq, int32_t* __restrict__ first) {
-  __shared__ int s_scan[kSetupThreads];
-  __shared__ int s_carry;
+varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCmax, int interval,
+                    int2* __restrict__ span, int4* __restrict__ seq, int32_t* __restrict__ first) {
+  // chunk counts in the low 32 bits, checkpoint counts in the high ones: both totals stay
+  // below 2^31, so one 64-bit scan carries the two
+  __shared__ long long s_scan[kSetupThreads];
+  __shared__ long long s_carry;
   const int tid = threadIdx.x;
   if (tid == 0) s_carry = 0;
   __syncthreads();
   for (int base = 0; base <= N; base += kSetupThreads) {
     const int i = base + tid;
-    int start = 0, end = 0, nc = 0;
+    int start = 0, end = 0, nc = 0, ck = 0;
     if (i < N) {
       start = min(max(cu[i], 0), T);
       end = min(max(cu[i + 1], start), T);
       nc = (end - start + C - 1) / C;
-      seq[i] = make_int2(start, end);
+      ck = interval > 0 ? (end - start) / interval : 0;
     }
-    s_scan[tid] = nc;
+    const long long mine = ((long long)ck << 32) | (unsigned)nc;
+    s_scan[tid] = mine;
     __syncthreads();
     for (int off = 1; off < kSetupThreads; off <<= 1) {     // inclusive scan of the counts
-      const int v = tid >= off ? s_scan[tid - off] : 0;
+      const long long v = tid >= off ? s_scan[tid - off] : 0;
       __syncthreads();
       s_scan[tid] += v;
       __syncthreads();
     }
-    const int carry = s_carry;
-    const int excl = min(carry + s_scan[tid] - nc, NCmax);
+    const long long before = s_carry + s_scan[tid] - mine;
+    const int excl = min((int)(before & 0xffffffffll), NCmax);
+    if (i < N) seq[i] = make_int4(start, end, (int)(before >> 32), 0);
     if (i <= N) first[i] = excl;
     for (int j = 0; j < nc && excl + j < NCmax; ++j) span[excl + j] = make_int2(start + j * C, end);
     __syncthreads();
-    if (tid == kSetupThreads - 1) s_carry = carry + s_scan[tid];
+    if (tid == kSetupThreads - 1) s_carry += s_scan[tid];
     __syncthreads();
   }
-  for (int g = min(s_carry, NCmax) + tid; g < NCmax; g += kSetupThreads) span[g] = make_int2(-1, -1);
+  for (int g = min((int)(s_carry & 0xffffffffll), NCmax) + tid; g < NCmax; g += kSetupThreads)
+    span[g] = make_int2(-1, -1);
 }
 
 // ================================================================ host side
@@ -1338,7 +1367,7 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, i
   const size_t per_chunk = chunk_ws_elems(pad_k(dk), dv, tile_chunk(run_chunk(chunk)), dtype) * 2;
   if (!varlen) return (size_t)B * H * NC * per_chunk + kSinkBytes;
   // packed: H x NC chunks, the sink, then the chunk table (span, seq, first)
-  return (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + align16((size_t)B * 8) +
+  return (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + (size_t)B * 16 +
          align16((size_t)(B + 1) * 4);
 }
 
@@ -1351,15 +1380,17 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const int NT = a.dv / kVT;
   const int nbh = a.B * a.H;
   const size_t chunks_bytes = (size_t)(varlen ? a.H : nbh) * NC * WsLayout<K, V, C, DT == 1>::kElems * 2;
-  int2 *span = nullptr, *seq = nullptr;
+  int2* span = nullptr;
+  int4* seq = nullptr;
   int32_t* first = nullptr;
+  const bool ckpt = varlen && a.chunk_states != nullptr;
   if (varlen) {
     unsigned char* tail = (unsigned char*)a.workspace + chunks_bytes + kSinkBytes;
     span = reinterpret_cast<int2*>(tail);
-    seq = reinterpret_cast<int2*>(tail + align16((size_t)NC * 8));
-    first = reinterpret_cast<int32_t*>(tail + align16((size_t)NC * 8) + align16((size_t)a.B * 8));
+    seq = reinterpret_cast<int4*>(tail + align16((size_t)NC * 8));
+    first = reinterpret_cast<int32_t*>(tail + align16((size_t)NC * 8) + (size_t)a.B * 16);
     hipLaunchKernelGGL(varlen_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.cu_seqlens, a.B, a.T,
-                       a.chunk, NC, span, seq, first);
+                       a.chunk, NC, ckpt ? a.state_interval : 0, span, seq, first);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1373,6 +1404,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   }
   ScanParams sp{a.v, a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
                 NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr, seq, first,
+                ckpt ? a.chunk_states : nullptr, ckpt ? a.state_interval / a.chunk : 0, ckpt ? a.num_states : 0,
                 a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
   const int groups = (nbh + 7) / 8;
   hipLaunchKernelGGL((scan_kernel<DT, K, V, C>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);

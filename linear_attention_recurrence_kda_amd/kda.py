@@ -67,7 +67,7 @@ def load():
     lib.kda_chunk_prefill_varlen_workspace_size.restype = sz
     lib.kda_chunk_prefill_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.kda_chunk_prefill_varlen.restype = i
-    lib.kda_chunk_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp,
+    lib.kda_chunk_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp, fp, i, i,
                                              i, i, i, i, i, i, i, u, vp, sz, vp]
     _lib = lib
     return lib
@@ -160,12 +160,26 @@ def prefill_varlen_workspace_size(N, T, H, dk, dv, chunk, dtype_code) -> int:
     return int(load().kda_chunk_prefill_varlen_workspace_size(N, T, H, dk, dv, chunk, dtype_code))
 
 
+def num_checkpoints(cu_seqlens, state_interval) -> int:
+    """Entries of the state checkpoints of a packed prefill: sum over the sequences of
+    floor(length / state_interval).  cu_seqlens may be a list or a tensor (a GPU tensor is
+    copied to the host, which synchronises)."""
+    import torch
+    cu = torch.as_tensor(cu_seqlens).to("cpu", torch.int64)
+    return int(((cu[1:] - cu[:-1]).clamp_min(0) // int(state_interval)).sum())
+
+
 def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=None, chunk_size=64,
-                         l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False):
+                         l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False,
+                         state_interval=0, chunk_states=None):
     """KDA prefill of N sequences packed end to end.  q,k [T,H,dk], v [T,H,dv] (bf16 or fp32),
     log_alpha [T,H,dk] fp32 ([T,H] with scalar_gate), beta [T,H] fp32, cu_seqlens [N+1] int32
     on the GPU (sequence i = tokens cu_seqlens[i] .. cu_seqlens[i+1]-1), initial_state
-    [N,H,dk,dv] fp32 or None.  Returns (o [T,H,dv] in q's dtype, final_state [N,H,dk,dv] fp32)."""
+    [N,H,dk,dv] fp32 or None.  Returns (o [T,H,dv] in q's dtype, final_state [N,H,dk,dv] fp32).
+    With state_interval > 0 it also saves each sequence's state after every state_interval
+    tokens (a multiple of chunk_size) and returns (o, final_state, chunk_states [M,H,dk,dv]),
+    sequence by sequence in order; chunk_states is allocated when not given (M from
+    cu_seqlens, copied to the host)."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -188,17 +202,32 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     if final_state is None:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     _req(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    n_states = 0
+    if state_interval:
+        if chunk_states is None:
+            m = num_checkpoints(cu_seqlens, state_interval)
+            chunk_states = torch.empty((m, H, dk, dv), dtype=torch.float32, device=q.device)
+        _req(chunk_states, "chunk_states", torch.float32)
+        if chunk_states.dim() != 4 or tuple(chunk_states.shape[1:]) != (H, dk, dv):
+            raise ValueError(f"chunk_states must be [M,{H},{dk},{dv}], got {tuple(chunk_states.shape)}")
+        n_states = chunk_states.shape[0]
+    elif chunk_states is not None:
+        raise ValueError("chunk_states needs state_interval > 0")
     need = prefill_varlen_workspace_size(N, T, H, dk, dv, chunk_size, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_chunk_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                       _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                      _ptr(chunk_states) if state_interval else None, n_states,
+                                      int(state_interval),
                                       N, T, H, dk, dv, int(chunk_size), dt,
                                       (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
                                       (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
                                       _ptr(workspace), wbytes, _stream())
     _check("kda_chunk_prefill_varlen", st)
+    if state_interval:
+        return out, final_state, chunk_states
     return out, final_state
 
 

@@ -148,11 +148,13 @@ def test_workspace_size_query(lib):
 
 
 def _varlen(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, cu=FAKE, s0=None, o=FAKE, sT=FAKE,
-             N=3, T=200, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0, ws=FAKE, wsb=1 << 40)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, cu=FAKE, s0=None, o=FAKE, sT=FAKE, ck=None,
+             nck=0, every=0, N=3, T=200, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0, ws=FAKE,
+             wsb=1 << 40)
     a.update(kw)
     return lib.kda_chunk_prefill_varlen(a["q"], a["k"], a["v"], a["la"], a["beta"], a["cu"], a["s0"],
-                                        a["o"], a["sT"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                        a["o"], a["sT"], a["ck"], a["nck"], a["every"], a["N"], a["T"],
+                                        a["H"], a["dk"], a["dv"],
                                         a["chunk"], a["dtype"], a["flags"], a["ws"], a["wsb"], None)
 
 
@@ -170,6 +172,14 @@ def test_prefill_varlen_validation(lib):
     assert _varlen(lib, q=MISALIGNED) == INVALID
     assert _varlen(lib, sT=None) == INVALID
     assert _varlen(lib, beta=None) == INVALID
+    # state checkpoints: an interval that is a positive multiple of chunk, a 4-byte aligned
+    # array and a capacity >= 0 (each valid case stops at the short workspace, before a launch)
+    assert _varlen(lib, ck=FAKE, nck=4, every=0) == INVALID
+    assert _varlen(lib, ck=FAKE, nck=4, every=96) == INVALID
+    assert _varlen(lib, ck=FAKE, nck=-1, every=128) == INVALID
+    assert _varlen(lib, ck=ctypes.c_void_p(0x10002), nck=4, every=128) == INVALID
+    assert _varlen(lib, ck=FAKE, nck=4, every=128, wsb=64) == WORKSPACE
+    assert _varlen(lib, ck=None, nck=-5, every=-1, wsb=64) == WORKSPACE   # ignored without an array
     assert _varlen(lib, wsb=64) == WORKSPACE
     assert _varlen(lib, ws=None) == WORKSPACE
     assert _varlen(lib, N=0, cu=None, ws=None, wsb=0) == OK   # no sequence: nothing to do

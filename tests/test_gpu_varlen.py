@@ -177,3 +177,75 @@ def test_varlen_serving_mix_equals_lone_runs():
         torch.cuda.synchronize()
         assert torch.equal(o[a:b], oi[0]), f"o of sequence {i} (length {b - a})"
         assert torch.equal(sN[i], si[0]), f"state of sequence {i}"
+
+
+@pytest.mark.parametrize("dtype,chunk,interval", [("bf16", 64, 128), ("bf16", 32, 64), ("fp32", 128, 256)])
+def test_varlen_state_checkpoints(dtype, chunk, interval):
+    """Checkpoint j of sequence i is the state after its first j * interval tokens: bit for
+    bit the final state of a packed run over those prefixes (one sequence per prefix)."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    lengths = [300, 0, 2 * interval, 1000, interval - 1, interval]
+    N, H, dk, dv = len(lengths), 2, 128, 128
+    say(f"[case] varlen checkpoints {dtype} chunk={chunk} interval={interval}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, dtype, seed=37)
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=37), dev=dev)
+    d = _dev(inp, dtype, dev)
+    o, sN, ck = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                         initial_state=s0, chunk_size=chunk, state_interval=interval)
+    counts = [L // interval for L in lengths]
+    assert ck.shape[0] == sum(counts) == kda.num_checkpoints(cu, interval)
+    # every prefix as its own packed sequence, each from its sequence's initial state
+    pre_idx, pre_len, pre_seq = [], [], []
+    for i, L in enumerate(lengths):
+        for j in range(1, counts[i] + 1):
+            pre_idx.append(np.arange(cu[i], cu[i] + j * interval))
+            pre_len.append(j * interval)
+            pre_seq.append(i)
+    sel = torch.from_numpy(np.concatenate(pre_idx)).to(dev)
+    dp = {n: x.index_select(0, sel).contiguous() for n, x in d.items()}
+    cu_p = np.concatenate([[0], np.cumsum(pre_len)]).astype(np.int32)
+    _, s_pre = kda.chunk_prefill_varlen(dp["q"], dp["k"], dp["v"], dp["log_alpha"], dp["beta"],
+                                        to_dev(cu_p, dev=dev), initial_state=s0[pre_seq].contiguous(),
+                                        chunk_size=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(ck, s_pre)
+    # a sequence whose length is a multiple of the interval: its last checkpoint is its final state
+    last = int(np.cumsum(counts)[2]) - 1
+    assert torch.equal(ck[last], sN[2])
+    # the outputs do not change when checkpoints are saved
+    o2, s2 = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                      initial_state=s0, chunk_size=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(sN, s2)
+
+
+def test_varlen_checkpoints_match_oracle_and_respect_capacity(oracle):
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    lengths = [200, 450]
+    N, H, dk, dv, interval = 2, 2, 64, 64, 128
+    say("[case] varlen checkpoints vs oracle, short checkpoint array")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, "bf16", seed=38)
+    d = _dev(inp, "bf16", dev)
+    M = kda.num_checkpoints(cu, interval)                       # 1 + 3
+    _, _, ck = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                        l2norm_qk=True, state_interval=interval)
+    got = host(ck)
+    k = 0
+    for i, L in enumerate(lengths):
+        for j in range(1, L // interval + 1):
+            a = int(cu[i])
+            _, rs = oracle.c_prefill(**{n: x[None, a:a + j * interval] for n, x in inp.items()}, l2norm_qk=True)
+            check(f"checkpoint {i}.{j}", got[k], rs[0], "bf16")
+            k += 1
+    assert k == M
+    # an array that holds fewer entries than the checkpoints: those past it are not written
+    big = torch.full((M, H, dk, dv), float("nan"), device=dev)
+    kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                             l2norm_qk=True, state_interval=interval, chunk_states=big[:2])
+    torch.cuda.synchronize()
+    assert torch.equal(big[:2], ck[:2])
+    assert torch.isnan(big[2:]).all()
