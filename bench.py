@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--T", type=int, default=131072)
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--decode-batch", type=int, default=256)
+    ap.add_argument("--long-T", type=int, default=524288,
+                    help="tokens of the long single-sequence prefill timed beside the headline (0: skip)")
     ap.add_argument("--cpu-segment", type=int, default=8192,
                     help="tokens of the oracle's CPU-baseline segment (32 heads)")
     ap.add_argument("--cpu-repeats", type=int, default=16,
@@ -223,6 +225,33 @@ def main():
     varlen_ms = sum(a_.elapsed_time(b_) for a_, b_ in vev) / reps
     del wsv
 
+    # the long-context end of the pages' range: one 512k-token sequence, 32 heads, timed
+    # after the headline workload (its inputs replace the 128k ones in HBM)
+    long_line = None
+    if args.long_T > 0:
+        TL = args.long_T
+        del x, o, ws, xv
+        xl = D.torch_kda_inputs(1, TL, H, dk, dv, dev, "bf16", seed=3)
+        ol = torch.empty(1, TL, H, dv, dtype=torch.bfloat16, device=dev)
+        wsl = torch.empty(kda.prefill_workspace_size(1, TL, H, dk, dv, C, kda.KDA_BF16), dtype=torch.uint8,
+                          device=dev)
+
+        def prefill_long():
+            kda.chunk_prefill(xl["q"], xl["k"], xl["v"], xl["log_alpha"], xl["beta"], chunk_size=C,
+                              out=ol, final_state=fs, workspace=wsl)
+        prefill_long()
+        lev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for a_, b_ in lev:
+            a_.record()
+            prefill_long()
+            b_.record()
+        torch.cuda.synchronize()
+        long_ms = sum(a_.elapsed_time(b_) for a_, b_ in lev) / len(lev)
+        long_gbs = PREFILL_BYTES_PER_TH * TL * H / (long_ms * 1e-3) / 1e9
+        long_line = {"B": 1, "T": TL, "H": H, "ms": long_ms, "tokens_per_s": TL / (long_ms * 1e-3),
+                     "algorithmic_GBps": long_gbs, "hbm_frac": long_gbs / HBM_PEAK_GBS}
+        del xl, ol, wsl
+
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
     # (read 1 GiB, write 1 GiB), the reference point beside the nominal 8 TB/s
     cn = (1 << 30) // 4
@@ -273,6 +302,7 @@ def main():
                            "tokens_per_s": T / (varlen_ms * 1e-3),
                            "algorithmic_GBps": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9,
                            "hbm_frac": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "prefill_long": long_line,
         "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms, "fused_step_graph_ms": graph_step_ms,
                    "fused_tokens_per_s": Bd / (fused_ms * 1e-3), "state_update_ms": dstep_ms,
                    "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
