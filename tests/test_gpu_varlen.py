@@ -249,3 +249,39 @@ def test_varlen_checkpoints_match_oracle_and_respect_capacity(oracle):
     torch.cuda.synchronize()
     assert torch.equal(big[:2], ck[:2])
     assert torch.isnan(big[2:]).all()
+
+
+@pytest.mark.parametrize("dk,dv,dtype,chunk", [(16, 16, "fp32", 16), (32, 128, "bf16", 32), (64, 32, "bf16", 64),
+                                               (128, 16, "fp32", 128)])
+def test_varlen_head_sizes_with_checkpoints(dk, dv, dtype, chunk):
+    """Every supported head-size family through the packed path: each sequence equals its
+    lone run, and every checkpoint equals the lone run over that prefix, bit for bit."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    interval = 2 * chunk
+    lengths = [3 * interval + 5, 0, interval, 77]
+    N, H = len(lengths), 3
+    say(f"[case] varlen dk={dk} dv={dv} {dtype} chunk={chunk}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, dtype, seed=39)
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=39), dev=dev)
+    d = _dev(inp, dtype, dev)
+    o, sN, ck = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                         initial_state=s0, chunk_size=chunk, l2norm_qk=True,
+                                         state_interval=interval)
+    k = 0
+    for i, L in enumerate(lengths):
+        a = int(cu[i])
+        oi, si = kda.chunk_prefill(*(d[n][a:a + L].unsqueeze(0).contiguous()
+                                     for n in ("q", "k", "v", "log_alpha", "beta")),
+                                   initial_state=s0[i:i + 1].contiguous(), chunk_size=chunk, l2norm_qk=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:a + L], oi[0]) and torch.equal(sN[i], si[0]), f"sequence {i}"
+        for j in range(1, L // interval + 1):
+            _, sj = kda.chunk_prefill(*(d[n][a:a + j * interval].unsqueeze(0).contiguous()
+                                        for n in ("q", "k", "v", "log_alpha", "beta")),
+                                      initial_state=s0[i:i + 1].contiguous(), chunk_size=chunk, l2norm_qk=True)
+            torch.cuda.synchronize()
+            assert torch.equal(ck[k], sj[0]), f"checkpoint {j} of sequence {i}"
+            k += 1
+    assert k == ck.shape[0]
