@@ -766,6 +766,16 @@ __device__ __forceinline__ void wait_lgkm() {
   __builtin_amdgcn_s_waitcnt(0xc07f);
   asm volatile("" ::: "memory");
 }
+// wait for every global load of this wave (not for its LDS operations).  Used once
+// before each chunk loop: the compiler derives the waits at the top of the loop from
+// every path into it, and without this the first chunk's loads, issued in the compiler's
+// own order, would set them for every later chunk too: the first step of each unrolled
+// pair would then wait for nearly all loads in flight, the L2 warm-up included.
+__device__ __forceinline__ void drain_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  asm volatile("" ::: "memory");
+}
 // loads issued in place: the scheduler moves nothing across either side
 template <typename F>
 __device__ __forceinline__ void pinned(F&& f) {
@@ -963,6 +973,7 @@ scan_kernel(ScanParams p) {
     }
     wait_lgkm();
     wg_barrier();                                    // initial state and V^T in LDS
+    drain_loads();
     int n = 0;
     for (; n + 1 < NCs; n += 2) {
       out_step(oA, n, [&](int part) __attribute__((always_inline)) { load_out(part, n + 1, oB); });
@@ -1238,6 +1249,7 @@ scan_kernel(ScanParams p) {
   if (NCs > 1) warmB = warm_chunk(1);
   wait_lgkm();
   wg_barrier();                                      // initial state and V^T in LDS
+  drain_loads();
   int n = 0;
   for (; n + 1 < NCs; n += 2) {
     u32x4 vB;
