@@ -285,3 +285,67 @@ def test_varlen_head_sizes_with_checkpoints(dk, dv, dtype, chunk):
             assert torch.equal(ck[k], sj[0]), f"checkpoint {j} of sequence {i}"
             k += 1
     assert k == ck.shape[0]
+
+
+def test_prefill_calls_in_graph_replays():
+    """The batch and the packed prefill captured once in a graph (workspace and outputs
+    fixed) and replayed with new inputs copied in eagerly, with a synchronisation between
+    replays: every replay equals the eager call bit for bit, checkpoints included."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    H, dk, dv, chunk, interval = 2, 128, 128, 64, 128
+    lengths = [130, 0, 256, 61]
+    N, T = len(lengths), sum(lengths)
+    say("[case] prefill and packed prefill in a graph")
+    cu = to_dev(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), dev=dev)
+    M = kda.num_checkpoints(cu, interval)
+
+    def inputs(seed):
+        inp, _ = _packed_inputs(lengths, H, dk, dv, "bf16", seed=seed)
+        return _dev(inp, "bf16", dev)
+    d0 = inputs(50)
+    g = {n: x.clone() for n, x in d0.items()}                      # captured input buffers
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=50), dev=dev)
+    out = torch.empty(T, H, dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    ck = torch.empty(M, H, dk, dv, dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.prefill_varlen_workspace_size(N, T, H, dk, dv, chunk, kda.KDA_BF16), dtype=torch.uint8,
+                     device=dev)
+    gb = {n: x[None, :64].contiguous() for n, x in d0.items()}     # a batch call beside it
+    ob = torch.empty(1, 64, H, dv, dtype=torch.bfloat16, device=dev)
+    fb = torch.empty(1, H, dk, dv, dtype=torch.float32, device=dev)
+    wsb = torch.empty(kda.prefill_workspace_size(1, 64, H, dk, dv, chunk, kda.KDA_BF16), dtype=torch.uint8,
+                      device=dev)
+
+    def step():
+        kda.chunk_prefill_varlen(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], cu, initial_state=s0,
+                                 chunk_size=chunk, out=out, final_state=fs, workspace=ws,
+                                 state_interval=interval, chunk_states=ck)
+        kda.chunk_prefill(gb["q"], gb["k"], gb["v"], gb["log_alpha"], gb["beta"], chunk_size=chunk,
+                          out=ob, final_state=fb, workspace=wsb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        d = inputs(60 + r)
+        for n in g:
+            g[n].copy_(d[n])
+            gb[n].copy_(d[n][None, :64])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_e, s_e, c_e = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], cu,
+                                                 initial_state=s0, chunk_size=chunk, state_interval=interval)
+        ob_e, fb_e = kda.chunk_prefill(*(d[n][None, :64].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                       chunk_size=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_e) and torch.equal(fs, s_e) and torch.equal(ck, c_e), f"packed, replay {r}"
+        assert torch.equal(ob, ob_e) and torch.equal(fb, fb_e), f"batch, replay {r}"
