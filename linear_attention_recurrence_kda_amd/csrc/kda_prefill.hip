@@ -40,7 +40,7 @@ namespace kda {
 
 constexpr int kPrepThreads = 256;
 constexpr int kScanThreads = 512;
-constexpr int kVT = 16;                  // dv columns per scan workgroup
+constexpr int kVT = 16;                  // dv columns per MFMA tile (a scan workgroup takes 1 or 2)
 constexpr float kFastLimit = -120.0f;    // log2 decay over one chunk for the factorised path
 constexpr size_t kSinkBytes = 16384;     // workspace tail that absorbs the stores of rows past T
 
@@ -713,11 +713,11 @@ struct OutOps {
 // Word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle, raw addressing.
 constexpr int kBufWord3 = 0x00020000;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-// V of one chunk in a 16-column tile, split evenly over the four state waves: lane l of
-// wave w holds row (C/4) w + l / (256/C), columns (C/16) (l % (256/C)) .. + C/16 - 1.
-template <int C>
+// V of one chunk in a TW-column tile, split evenly over the four state waves: lane l of
+// wave w holds row (C/4) w + l / (256/C), columns (C TW/256) (l % (256/C)) .. + C TW/256 - 1.
+template <int C, int TW>
 struct VTile {
-  static constexpr int kPerLane = C / 16;            // elements per lane
+  static constexpr int kPerLane = C * TW / 256;      // elements per lane
   static constexpr int kLanesPerRow = 256 / C;
   __device__ __forceinline__ static int row(int w, int l) { return (C / 4) * w + l / kLanesPerRow; }
   __device__ __forceinline__ static int col(int l) { return kPerLane * (l % kLanesPerRow); }
@@ -784,7 +784,11 @@ __device__ __forceinline__ void pinned(F&& f) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int DT, int K, int V, int C>
+// TW = 16 or 32 dv columns per workgroup.  With 32 every operand fragment loaded from the
+// workspace feeds two 16-column MFMA tiles ("halves"), so a CU streams half the operand
+// bytes per output column; that pays when there are enough (b, h) pairs to fill the chip
+// with half as many workgroups.
+template <int DT, int K, int V, int C, int TW>
 __global__ void __launch_bounds__(kScanThreads)
 scan_kernel(ScanParams p) {
   using E = Elem<DT>;
@@ -793,7 +797,8 @@ scan_kernel(ScanParams p) {
   using L = WsLayout<K, V, C, SPLIT>;
   using Ch = ChainOps<K, C, SPLIT>;
   using Ou = OutOps<K, C, SPLIT>;
-  using VT = VTile<C>;
+  using VT = VTile<C, TW>;
+  constexpr int NH = TW / kVT;                      // 16-column halves per workgroup
   constexpr int RT = C / 16, CS = C / 32, KS = K / 32, SRT = K / 16;
   constexpr int SPW = Ch::SPW;                      // state row tiles per state wave
   constexpr int KB = K + 8, CB = C + 8;
@@ -801,9 +806,9 @@ scan_kernel(ScanParams p) {
   constexpr int kParts = SPLIT ? 2 : 1;
   static_assert(RT <= 4, "one U/O row tile per wave");
 
-  __shared__ __attribute__((aligned(16))) __bf16 s_S[2][kVT * KB];    // state hi, lo; B-operand rows = dv column
-  __shared__ __attribute__((aligned(16))) __bf16 s_U[2][kVT * CB];    // U hi, lo
-  __shared__ __attribute__((aligned(16))) __bf16 s_vT[kParts][kVT * C]; // V^T (hi, lo) of the next chunk, swizzled
+  __shared__ __attribute__((aligned(16))) __bf16 s_S[2][TW * KB];     // state hi, lo; B-operand rows = dv column
+  __shared__ __attribute__((aligned(16))) __bf16 s_U[2][TW * CB];     // U hi, lo
+  __shared__ __attribute__((aligned(16))) __bf16 s_vT[kParts][TW * C];  // V^T (hi, lo) of the next chunk, swizzled
   // Gam_last (K floats) and the row-valid bits (the next 16 bytes) of chunk c in slot c % 3,
   // written two chunk steps ahead by one output wave with a single load (a load per state
   // wave would have sixteen lanes on each address)
@@ -815,7 +820,7 @@ scan_kernel(ScanParams p) {
   const int bh = (slot / p.NT) * 8 + xcd, tile = slot % p.NT;
   if (bh >= p.nbh) return;
   const int b = bh / p.H, h = bh % p.H;
-  const int v0 = tile * kVT;
+  const int v0 = tile * TW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);        // uniform: addresses stay scalar
   const int I = wave & 3;                            // row tile (and first state row tile)
@@ -851,20 +856,20 @@ scan_kernel(ScanParams p) {
     return *reinterpret_cast<const bf16x8*>(src);
   };
   // the state entering the chunk and U, as B-operand fragments (hi, lo) from LDS
-  auto read_state = [&](bf16x8* sh, bf16x8* slo) __attribute__((always_inline)) {
+  auto read_state = [&](int hf, bf16x8* sh, bf16x8* slo) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int k0 = 32 * ks + 8 * (lane / 16);
-      sh[ks] = *reinterpret_cast<const bf16x8*>(&s_S[0][(lane % 16) * KB + k0]);
-      slo[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(lane % 16) * KB + k0]);
+      sh[ks] = *reinterpret_cast<const bf16x8*>(&s_S[0][(kVT * hf + lane % 16) * KB + k0]);
+      slo[ks] = *reinterpret_cast<const bf16x8*>(&s_S[1][(kVT * hf + lane % 16) * KB + k0]);
     }
   };
-  auto read_u = [&](bf16x8* uh, bf16x8* ul) __attribute__((always_inline)) {
+  auto read_u = [&](int hf, bf16x8* uh, bf16x8* ul) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < CS; ++ks) {
       const int j0 = 32 * ks + 8 * (lane / 16);
-      uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(lane % 16) * CB + j0]);
-      ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(lane % 16) * CB + j0]);
+      uh[ks] = *reinterpret_cast<const bf16x8*>(&s_U[0][(kVT * hf + lane % 16) * CB + j0]);
+      ul[ks] = *reinterpret_cast<const bf16x8*>(&s_U[1][(kVT * hf + lane % 16) * CB + j0]);
     }
   };
 
@@ -907,7 +912,8 @@ scan_kernel(ScanParams p) {
       if (lane <= K / 4) *reinterpret_cast<float4*>(&s_gv[c % 3][4 * lane]) = x;
     };
     Tv* og = (Tv*)p.o;
-    Tv* sink = (Tv*)p.sink + (L_id & 63) * 64;
+    constexpr int kSinkSlot = 64 * NH;               // elements of the sink per workgroup
+    Tv* sink = (Tv*)p.sink + (L_id & (4096 / kSinkSlot - 1)) * kSinkSlot;
     uint32_t o_lane[kStores];
 #pragma unroll
     for (int i = 0; i < kStores; ++i)
@@ -918,15 +924,20 @@ scan_kernel(ScanParams p) {
       unsigned char* ochunk = reinterpret_cast<unsigned char*>(og) + token_base(t0);
       float4 gv;
       if (wave == 4) gv = load_gv(n + 2);
-      bf16x8 sh[KS], slo[KS];
-      read_state(sh, slo);
-      f32x4 o4[2] = {zero4(), zero4()};
-      if (has_rows) {
+      f32x4 o4[NH][2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          o4[ks & 1] = mfma16(o.qt[ks], sh[ks], o4[ks & 1]);
-          o4[ks & 1] = mfma16(o.qt[ks], slo[ks], o4[ks & 1]);
-          if (SPLIT) o4[ks & 1] = mfma16(o.qtl[ks], sh[ks], o4[ks & 1]);
+      for (int hf = 0; hf < NH; ++hf) {
+        o4[hf][0] = zero4();
+        o4[hf][1] = zero4();
+        bf16x8 sh[KS], slo[KS];
+        read_state(hf, sh, slo);
+        if (has_rows) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            o4[hf][ks & 1] = mfma16(o.qt[ks], sh[ks], o4[hf][ks & 1]);
+            o4[hf][ks & 1] = mfma16(o.qt[ks], slo[ks], o4[hf][ks & 1]);
+            if (SPLIT) o4[hf][ks & 1] = mfma16(o.qtl[ks], sh[ks], o4[hf][ks & 1]);
+          }
         }
       }
       // the loads for the next step go after this wave's products, when the state waves'
@@ -934,27 +945,35 @@ scan_kernel(ScanParams p) {
       pinned([&] { loads(0); });
       wait_lgkm();
       wg_barrier();                                  // U in LDS
-      bf16x8 uh[CS], ul[CS];
-      read_u(uh, ul);
-      if (has_rows) {
 #pragma unroll
-        for (int ks = 0; ks < CS; ++ks) {
-          if (!tri(ks)) continue;                    // P is lower triangular
-          o4[ks & 1] = mfma16(o.ph[ks], uh[ks], o4[ks & 1]);
-          o4[ks & 1] = mfma16(o.ph[ks], ul[ks], o4[ks & 1]);
-          o4[ks & 1] = mfma16(o.pl[ks], uh[ks], o4[ks & 1]);
+      for (int hf = 0; hf < NH; ++hf) {
+        bf16x8 uh[CS], ul[CS];
+        read_u(hf, uh, ul);
+        if (has_rows) {
+#pragma unroll
+          for (int ks = 0; ks < CS; ++ks) {
+            if (!tri(ks)) continue;                  // P is lower triangular
+            o4[hf][ks & 1] = mfma16(o.ph[ks], uh[ks], o4[hf][ks & 1]);
+            o4[hf][ks & 1] = mfma16(o.ph[ks], ul[ks], o4[hf][ks & 1]);
+            o4[hf][ks & 1] = mfma16(o.pl[ks], uh[ks], o4[hf][ks & 1]);
+          }
         }
+      }
+      if (has_rows) {
         pinned([&] { loads(1); });
 #pragma unroll
-        for (int i = 0; i < kStores; ++i) {
-          const int rr = 16 * I + 4 * (lane / 16) + i;
-          Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i]);
-          if (!full && !(rr < p.chunk && t0 + rr < seq_T)) dst = sink + 16 * i + (lane % 16);
-          E::st(dst, 0, o4[0][i] + o4[1][i]);
+        for (int hf = 0; hf < NH; ++hf) {
+#pragma unroll
+          for (int i = 0; i < kStores; ++i) {
+            const int rr = 16 * I + 4 * (lane / 16) + i;
+            Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i] + kVT * hf * (uint32_t)sizeof(Tv));
+            if (!full && !(rr < p.chunk && t0 + rr < seq_T)) dst = sink + 64 * hf + 16 * i + (lane % 16);
+            E::st(dst, 0, o4[hf][0][i] + o4[hf][1][i]);
+          }
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < kStores; ++i) {                           // keep the store count uniform
+        for (int i = 0; i < kStores * NH; ++i) {                      // keep the store count uniform
           volatile Tv* dst = sink + 16 * i + (lane % 16);
           *dst = (Tv)0;
         }
@@ -1084,7 +1103,7 @@ scan_kernel(ScanParams p) {
   // of the state waves takes line g of the list [its 1/NT share of the chunk's workspace
   // lines (every tile reads all of them); the lines of the chunk's V rows that hold the
   // tile's columns]; threads past the end repeat the first line.
-  constexpr int kNT = V / kVT;
+  constexpr int kNT = V / TW;
   constexpr int kShLines = (int)((L::kElems * 2 + 127) / 128);
   size_t pf_off = 0;                                                   // bytes from the chunk base
   int pf_row = -1;                                                     // V row, or -1
@@ -1104,42 +1123,51 @@ scan_kernel(ScanParams p) {
   };
 
   // state tiles in registers: wave w owns state row tiles w, w+4, ...
-  f32x4 S[SPW];
+  f32x4 S[NH][SPW];
 #pragma unroll
-  for (int m = 0; m < SPW; ++m) {
-    const int M = wave + 4 * m;
+  for (int hf = 0; hf < NH; ++hf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * M + 4 * (lane / 16) + i, col = v0 + (lane % 16);
-      S[m][i] = (M < SRT && row < dk && p.init_state != nullptr)
-                    ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
+    for (int m = 0; m < SPW; ++m) {
+      const int M = wave + 4 * m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * M + 4 * (lane / 16) + i, col = v0 + kVT * hf + (lane % 16);
+        S[hf][m][i] = (M < SRT && row < dk && p.init_state != nullptr)
+                          ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
+      }
     }
   }
-  // this workgroup's 16 columns of the state to a dk x dv fp32 matrix in HBM
+  // this workgroup's columns of the state to a dk x dv fp32 matrix in HBM
   auto store_state = [&](float* dst) __attribute__((always_inline)) {
     // the lane index passes through an empty asm so the addresses are formed here, not
     // hoisted out of the chunk loop into registers held across it
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-      const int M = wave + 4 * m;
-      if (M >= SRT) continue;
+    for (int hf = 0; hf < NH; ++hf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * M + 4 * (ln / 16) + i;
-        if (row < dk) dst[(size_t)row * dv + v0 + (ln % 16)] = S[m][i];
+      for (int m = 0; m < SPW; ++m) {
+        const int M = wave + 4 * m;
+        if (M >= SRT) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * M + 4 * (ln / 16) + i;
+          if (row < dk) dst[(size_t)row * dv + v0 + kVT * hf + (ln % 16)] = S[hf][m][i];
+        }
       }
     }
   };
   auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-      const int M = wave + 4 * m;
-      if (srow(M)) {                                 // rows 16 M + 4 (lane / 16) .. + 3: consecutive
-        const float v4[4] = {S[m][0], S[m][1], S[m][2], S[m][3]};
-        const int at = (lane % 16) * KB + 16 * M + 4 * (lane / 16);
-        store_split4(v4, &s_S[0][at], &s_S[1][at]);
+    for (int hf = 0; hf < NH; ++hf) {
+#pragma unroll
+      for (int m = 0; m < SPW; ++m) {
+        const int M = wave + 4 * m;
+        if (srow(M)) {                               // rows 16 M + 4 (lane / 16) .. + 3: consecutive
+          const float v4[4] = {S[hf][m][0], S[hf][m][1], S[hf][m][2], S[hf][m][3]};
+          const int at = (kVT * hf + lane % 16) * KB + 16 * M + 4 * (lane / 16);
+          store_split4(v4, &s_S[0][at], &s_S[1][at]);
+        }
       }
     }
   };
@@ -1157,66 +1185,72 @@ scan_kernel(ScanParams p) {
       if (srow(M)) gam[m] = *reinterpret_cast<const float4*>(&s_gv[n % 3][16 * M + 4 * (lane / 16)]);
     }
     const unsigned long long valid_next = *reinterpret_cast<const unsigned long long*>(&s_gv[(n + 1) % 3][K]);
-    // V^T first: T' V needs nothing else and can start while the state arrives
-    bf16x8 vth[CS], vtl[SPLIT ? CS : 1];
 #pragma unroll
-    for (int ks = 0; ks < CS; ++ks) {
-      const int j0 = 32 * ks + 8 * (lane / 16);
-      vth[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[0][swz<C>(lane % 16, j0)]);
-      if (SPLIT) vtl[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[kParts - 1][swz<C>(lane % 16, j0)]);
-    }
-    bf16x8 sh[KS], slo[KS];
-    read_state(sh, slo);
-    group(0);
-    if (has_rows) {
-      // ---- U = T' V + Wn S for this wave's 16 rows (independent accumulators keep the
-      //      chains short; -T' is stored, so T' V enters with a minus sign)
-      f32x4 u[4] = {zero4(), zero4(), zero4(), zero4()};
-      f32x4 tv[2] = {zero4(), zero4()};
+    for (int hf = 0; hf < NH; ++hf) {
+      // V^T first: T' V needs nothing else and can start while the state arrives
+      bf16x8 vth[CS], vtl[SPLIT ? CS : 1];
 #pragma unroll
       for (int ks = 0; ks < CS; ++ks) {
-        if (!tri(ks)) continue;                      // T' is lower triangular
-        tv[0] = mfma16(op.th[ks], vth[ks], tv[0]);
-        tv[1] = mfma16(op.tl[ks], vth[ks], tv[1]);
-        if (SPLIT) tv[1] = mfma16(op.th[ks], vtl[ks], tv[1]);
+        const int j0 = 32 * ks + 8 * (lane / 16);
+        vth[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[0][swz<C>(kVT * hf + lane % 16, j0)]);
+        if (SPLIT) vtl[ks] = *reinterpret_cast<const bf16x8*>(&s_vT[kParts - 1][swz<C>(kVT * hf + lane % 16, j0)]);
       }
-      group(1);
+      bf16x8 sh[KS], slo[KS];
+      read_state(hf, sh, slo);
+      if (hf == 0) group(0);
+      if (has_rows) {
+        // ---- U = T' V + Wn S for this wave's 16 rows (independent accumulators keep the
+        //      chains short; -T' is stored, so T' V enters with a minus sign)
+        f32x4 u[4] = {zero4(), zero4(), zero4(), zero4()};
+        f32x4 tv[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u[(ks & 1) * 2] = mfma16(op.wn[ks], sh[ks], u[(ks & 1) * 2]);
-        u[(ks & 1) * 2 + 1] = mfma16(op.wn[ks], slo[ks], u[(ks & 1) * 2 + 1]);
-        if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(op.wnl[ks], sh[ks], u[(ks & 1) * 2 + 1]);
+        for (int ks = 0; ks < CS; ++ks) {
+          if (!tri(ks)) continue;                    // T' is lower triangular
+          tv[0] = mfma16(op.th[ks], vth[ks], tv[0]);
+          tv[1] = mfma16(op.tl[ks], vth[ks], tv[1]);
+          if (SPLIT) tv[1] = mfma16(op.th[ks], vtl[ks], tv[1]);
+        }
+        if (hf == 0) group(1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u[(ks & 1) * 2] = mfma16(op.wn[ks], sh[ks], u[(ks & 1) * 2]);
+          u[(ks & 1) * 2 + 1] = mfma16(op.wn[ks], slo[ks], u[(ks & 1) * 2 + 1]);
+          if (SPLIT) u[(ks & 1) * 2 + 1] = mfma16(op.wnl[ks], sh[ks], u[(ks & 1) * 2 + 1]);
+        }
+        if (hf == 0) group(2);
+        float uv[4];                                 // rows 16 I + 4 (lane / 16) .. + 3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uv[i] = ((u[0][i] + u[2][i]) + (u[1][i] + u[3][i])) - (tv[0][i] + tv[1][i]);
+        const int at = (kVT * hf + lane % 16) * CB + 16 * I + 4 * (lane / 16);
+        store_split4(uv, &s_U[0][at], &s_U[1][at]);
+      } else if (hf == 0) {
+        group(1); group(2);
       }
-      group(2);
-      float uv[4];                                   // rows 16 I + 4 (lane / 16) .. + 3
-#pragma unroll
-      for (int i = 0; i < 4; ++i) uv[i] = ((u[0][i] + u[2][i]) + (u[1][i] + u[3][i])) - (tv[0][i] + tv[1][i]);
-      const int at = (lane % 16) * CB + 16 * I + 4 * (lane / 16);
-      store_split4(uv, &s_U[0][at], &s_U[1][at]);
-      group(3);
-    } else {
-      group(1); group(2); group(3);
     }
+    group(3);
     wait_lgkm();
     wg_barrier();                                    // U in LDS; S and V^T reads done
-    bf16x8 uh[CS], ul[CS];
-    read_u(uh, ul);
-    group(4);
     // ---- S = Diag(Gam_last) S + Kh^T U  (the chain that carries to the next chunk)
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-      const int M = wave + 4 * m;
-      if (!srow(M)) continue;
-      f32x4 a0 = zero4(), a1 = zero4();
+    for (int hf = 0; hf < NH; ++hf) {
+      bf16x8 uh[CS], ul[CS];
+      read_u(hf, uh, ul);
+      if (hf == 0) group(4);
 #pragma unroll
-      for (int ks = 0; ks < CS; ++ks) {
-        a0 = mfma16(op.kh[m][ks], uh[ks], a0);
-        a1 = mfma16(op.kh[m][ks], ul[ks], a1);
-        if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
+      for (int m = 0; m < SPW; ++m) {
+        const int M = wave + 4 * m;
+        if (!srow(M)) continue;
+        f32x4 a0 = zero4(), a1 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < CS; ++ks) {
+          a0 = mfma16(op.kh[m][ks], uh[ks], a0);
+          a1 = mfma16(op.kh[m][ks], ul[ks], a1);
+          if (SPLIT) a1 = mfma16(op.khl[m][ks], uh[ks], a1);
+        }
+        const float gg[4] = {gam[m].x, gam[m].y, gam[m].z, gam[m].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[hf][m][i] = gg[i] * S[hf][m][i] + (a0[i] + a1[i]);
       }
-      const float gg[4] = {gam[m].x, gam[m].y, gam[m].z, gam[m].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) S[m][i] = gg[i] * S[m][i] + (a0[i] + a1[i]);
     }
     group(5);
     publish_state();
@@ -1389,8 +1423,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if ((size_t)(C + 1) * a.H * a.dv * 4 > 0xffffffffull) return hipErrorInvalidValue;   // 32-bit output offsets
   const bool varlen = a.cu_seqlens != nullptr;
   const int NC = (int)prefill_chunks(a.B, a.T, a.chunk, varlen);
-  const int NT = a.dv / kVT;
   const int nbh = a.B * a.H;
+  // 32-column scan tiles (bf16, dv = 128) once there are enough (b, h) pairs for one such
+  // workgroup per CU: each streams the chunk operands once for twice the columns
+  constexpr bool kWideOk = (DT == 0 && V == 128);
+  const bool wide = kWideOk && nbh >= 64;
+  const int NT = a.dv / (wide ? 2 * kVT : kVT);
   const size_t chunks_bytes = (size_t)(varlen ? a.H : nbh) * NC * WsLayout<K, V, C, DT == 1>::kElems * 2;
   int2* span = nullptr;
   int4* seq = nullptr;
@@ -1419,7 +1457,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
                 ckpt ? a.chunk_states : nullptr, ckpt ? a.state_interval / a.chunk : 0, ckpt ? a.num_states : 0,
                 a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
   const int groups = (nbh + 7) / 8;
-  hipLaunchKernelGGL((scan_kernel<DT, K, V, C>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);
+  if constexpr (kWideOk) {
+    if (wide) {
+      hipLaunchKernelGGL((scan_kernel<DT, K, V, C, 2 * kVT>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((scan_kernel<DT, K, V, C, kVT>), dim3(groups * 8 * NT), dim3(kScanThreads), 0, st, sp);
   return hipGetLastError();
 }
 

@@ -256,3 +256,28 @@ def test_long_prefill_sampled_heads(oracle):
     for i, h in enumerate(heads):
         check(f"long o h{h}", host(o[:, :, h]), ro[:, :, i], "bf16")
         check(f"long state h{h}", host(s[:, h]), rs[:, i], "bf16")
+
+
+@pytest.mark.parametrize("chunk", [64, 32])
+def test_wide_scan_tiles_equal_narrow(chunk):
+    """With 64 or more (b, h) pairs and dv = 128 in bf16 the scan takes 32 dv columns per
+    workgroup instead of 16; every column sees the same operations in the same order, so a
+    batch that takes that path equals each of its rows run alone (16-column path) bit for
+    bit, padding mask, initial state and L2 norm included."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv = 4, 300, 16, 128, 128
+    say(f"[case] 32-column scan tiles vs 16 chunk={chunk}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=40)
+    s0 = D.np_state(B, H, dk, dv, 0.1, seed=40)
+    mask = np.ones((B, T), np.uint8)
+    mask[1, 250:] = 0
+    mask[3, :37] = 0
+    o, s = _run(inp, "bf16", dev, chunk, mask=mask, s0=s0, l2norm=True)
+    for b in range(B):
+        ob, sb = _run({n: x[b:b + 1] for n, x in inp.items()}, "bf16", dev, chunk, mask=mask[b:b + 1],
+                      s0=s0[b:b + 1], l2norm=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[b:b + 1], ob), f"o of row {b}"
+        assert torch.equal(s[b:b + 1], sb), f"state of row {b}"
