@@ -349,3 +349,40 @@ def test_prefill_calls_in_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(out, o_e) and torch.equal(fs, s_e) and torch.equal(ck, c_e), f"packed, replay {r}"
         assert torch.equal(ob, ob_e) and torch.equal(fb, fb_e), f"batch, replay {r}"
+
+
+@pytest.mark.parametrize("scalar", [False, True])
+def test_varlen_wide_tiles_equal_narrow_with_checkpoints(scalar):
+    """16 packed sequences x 4 heads (64 pairs) run on 32-column scan tiles; the same
+    sequences split into four packed calls of 4 (16 pairs, 16-column tiles) give the same
+    outputs, final states and checkpoints bit for bit, with L2 norm, initial states and
+    the per-head gate."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    H, dk, dv, interval = 4, 128, 128, 128
+    r = np.random.default_rng(41)
+    lengths = [int(x) for x in r.integers(0, 700, 16)]
+    lengths[3] = 0
+    lengths[5] = 2 * interval
+    N = len(lengths)
+    say(f"[case] varlen wide vs narrow scalar={scalar} lengths={lengths}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, "bf16", seed=41, scalar=scalar)
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=41), dev=dev)
+    d = _dev(inp, "bf16", dev)
+    o, sN, ck = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                         initial_state=s0, l2norm_qk=True, scalar_gate=scalar,
+                                         state_interval=interval)
+    k = 0
+    for g0 in range(0, N, 4):
+        a, b = int(cu[g0]), int(cu[g0 + 4])
+        cu_g = (cu[g0:g0 + 5] - cu[g0]).astype(np.int32)
+        og, sg, cg = kda.chunk_prefill_varlen(*(d[n][a:b].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                              to_dev(cu_g, dev=dev), initial_state=s0[g0:g0 + 4].contiguous(),
+                                              l2norm_qk=True, scalar_gate=scalar, state_interval=interval)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], og), f"o of sequences {g0}..{g0 + 3}"
+        assert torch.equal(sN[g0:g0 + 4], sg), f"states of sequences {g0}..{g0 + 3}"
+        assert torch.equal(ck[k:k + cg.shape[0]], cg), f"checkpoints of sequences {g0}..{g0 + 3}"
+        k += cg.shape[0]
+    assert k == ck.shape[0]
