@@ -146,9 +146,16 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  *   beta        [T,H]        fp32 in [0,1]
  *   cu_seqlens  [N+1]        int32 device array, cu_seqlens[0] = 0,
  *                            non-decreasing, cu_seqlens[N] = T
- *   init_state  [N,H,dk,dv]  fp32, NULL = zeros
+ *   init_state  [N,H,dk,dv]  fp32, NULL = zeros ([num_slots,H,dk,dv] with slot)
  *   o           [T,H,dv]     dtype, written
  *   final_state [N,H,dk,dv]  fp32, written; may be the same pointer as init_state
+ *                            ([num_slots,H,dk,dv] with slot)
+ *   slot        [N]          int32 device array, or NULL: with it init_state and
+ *                            final_state are a pool of num_slots states (usually one
+ *                            pointer, as for kda_decode_step_fused) and sequence i
+ *                            reads and writes entry slot[i].  A slot outside
+ *                            [0, num_slots) starts from zero and keeps no final state.
+ *                            Two sequences must not share a slot (they would race).
  *   chunk_states [M,H,dk,dv] fp32, written, or NULL: state checkpoints for prefix
  *                            caching (remio.ai page, software-stack section: prefix
  *                            caching and the state at chunk boundaries are named among
@@ -172,11 +179,12 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  * as num_states bounds them).  Supported: as
  * kda_chunk_prefill with B = N (N <= 65535), and H times (ceil(T/chunk) + N)
  * < 2^31.  16-byte aligned: q, k, v, and log_alpha unless KDA_FLAG_SCALAR_GATE
- * is set; chunk_states 4-byte aligned.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
+ * is set; chunk_states and slot 4-byte aligned.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
  */
 int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, const int32_t* cu_seqlens,
                              const float* init_state, void* o, float* final_state,
+                             const int32_t* slot, int num_slots,
                              float* chunk_states, int num_states, int state_interval,
                              int N, int T, int H, int dk, int dv, int chunk, int dtype,
                              unsigned flags, void* workspace, size_t workspace_bytes, void* stream);

@@ -58,8 +58,8 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
 // and the packed layout (B sequences of T tokens in total, cu_seqlens given).
 static int prefill_entry(const void* q, const void* k, const void* v, const float* log_alpha,
                          const float* beta, const uint8_t* mask, const int32_t* cu_seqlens, bool varlen,
-                         const float* init_state, void* o, float* final_state, float* chunk_states,
-                         int num_states, int state_interval, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                         const float* init_state, void* o, float* final_state, const int32_t* slot,
+                         int num_slots, float* chunk_states, int num_states, int state_interval, int B, int T, int H, int dk, int dv, int chunk, int dtype,
                          unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
@@ -71,6 +71,7 @@ static int prefill_entry(const void* q, const void* k, const void* v, const floa
     if (final_state == nullptr || !aligned(final_state, 4)) return KDA_ERR_INVALID_ARG;
     if (init_state != nullptr && !aligned(init_state, 4)) return KDA_ERR_INVALID_ARG;
     if (varlen && (cu_seqlens == nullptr || !aligned(cu_seqlens, 4))) return KDA_ERR_INVALID_ARG;
+    if (slot != nullptr && (!aligned(slot, 4) || num_slots < 0)) return KDA_ERR_INVALID_ARG;
     if (chunk_states != nullptr && (!aligned(chunk_states, 4) || num_states < 0 || state_interval <= 0 ||
                                     state_interval % chunk != 0))
       return KDA_ERR_INVALID_ARG;
@@ -93,7 +94,7 @@ static int prefill_entry(const void* q, const void* k, const void* v, const floa
                      B, T, H, dk, dv, chunk, dtype, (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0,
                      (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, workspace, workspace_bytes, stream,
                      varlen ? cu_seqlens : nullptr, chunk_states, chunk_states != nullptr ? num_states : 0,
-                     chunk_states != nullptr ? state_interval : 0};
+                     chunk_states != nullptr ? state_interval : 0, slot, slot != nullptr ? num_slots : 0};
   return hip_status(kda::launch_prefill(a));
 }
 
@@ -101,17 +102,17 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
                       const float* beta, const uint8_t* mask, const float* init_state, void* o,
                       float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, o, final_state, nullptr, 0, 0,
+  return prefill_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, o, final_state, nullptr, 0, nullptr, 0, 0,
                        B, T, H, dk, dv, chunk, dtype, flags, workspace, workspace_bytes, stream);
 }
 
 int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
                              const float* beta, const int32_t* cu_seqlens, const float* init_state,
-                             void* o, float* final_state, float* chunk_states, int num_states,
-                             int state_interval, int N, int T, int H, int dk, int dv, int chunk, int dtype, unsigned flags,
+                             void* o, float* final_state, const int32_t* slot, int num_slots,
+                             float* chunk_states, int num_states, int state_interval, int N, int T, int H, int dk, int dv, int chunk, int dtype, unsigned flags,
                              void* workspace, size_t workspace_bytes, void* stream) {
   return prefill_entry(q, k, v, log_alpha, beta, nullptr, cu_seqlens, true, init_state, o, final_state,
-                       chunk_states, num_states, state_interval, N, T, H, dk, dv, chunk, dtype, flags, workspace,
+                       slot, num_slots, chunk_states, num_states, state_interval, N, T, H, dk, dv, chunk, dtype, flags, workspace,
                        workspace_bytes, stream);
 }
 

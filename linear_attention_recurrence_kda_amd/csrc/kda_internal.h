@@ -58,6 +58,8 @@ struct PrefillArgs {
   float* chunk_states;                     // packed only: the state every state_interval tokens, or null
   int num_states;                          // entries chunk_states holds
   int state_interval;                      // a multiple of chunk
+  const int32_t* slot;                     // packed only: each sequence's slot in a state pool, or null
+  int num_slots;                           // slots in the pool
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

@@ -105,6 +105,8 @@ struct ScanParams {
   const int32_t* first;                    // varlen: each sequence's first chunk (N + 1 entries)
   float* ckpt;                             // varlen: states saved every ck_every chunks, or null
   int ck_every, ck_cap;                    // ck_cap: entries ckpt holds
+  const int32_t* slot;                     // varlen: state slot of each sequence in a pool of S, or null
+  int S;
   int B, T, H, dk, dv, chunk, NC, NT, nbh;
 };
 
@@ -845,6 +847,13 @@ scan_kernel(ScanParams p) {
   }
   const uint16_t* wsh = p.ws + ws_chunk0 * L::kElems;
   const int last = NCs - 1;
+  // where this (sequence, head) keeps its state: its own row, or its slot of a pool (a
+  // slot outside the pool: no state is read or kept, the sequence starts from zero)
+  int sbh = bh;
+  if (p.slot != nullptr) {
+    const int sl = p.slot[b];
+    sbh = (sl >= 0 && sl < p.S) ? sl * p.H + h : -1;
+  }
   // tokens are H * dv elements apart in q, k, v and o; byte offsets inside a chunk stay
   // below 2^32 (checked on the host)
   const size_t row_bytes = (size_t)p.H * dv * sizeof(Tv);
@@ -1132,8 +1141,8 @@ scan_kernel(ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * M + 4 * (lane / 16) + i, col = v0 + kVT * hf + (lane % 16);
-        S[hf][m][i] = (M < SRT && row < dk && p.init_state != nullptr)
-                          ? p.init_state[((size_t)bh * dk + row) * dv + col] : 0.f;
+        S[hf][m][i] = (M < SRT && row < dk && p.init_state != nullptr && sbh >= 0)
+                          ? p.init_state[((size_t)sbh * dk + row) * dv + col] : 0.f;
       }
     }
   }
@@ -1308,7 +1317,7 @@ scan_kernel(ScanParams p) {
   asm volatile("" :: "v"(warmA), "v"(warmB));
   __builtin_amdgcn_s_waitcnt(0);
 
-  store_state(p.final_state + (size_t)bh * dk * dv);
+  if (sbh >= 0) store_state(p.final_state + (size_t)sbh * dk * dv);
 }
 
 // ================================================================ packed sequences
@@ -1455,7 +1464,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   ScanParams sp{a.v, a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
                 NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr, seq, first,
                 ckpt ? a.chunk_states : nullptr, ckpt ? a.state_interval / a.chunk : 0, ckpt ? a.num_states : 0,
-                a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
+                varlen ? a.slot : nullptr, a.num_slots, a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
   const int groups = (nbh + 7) / 8;
   if constexpr (kWideOk) {
     if (wide) {

@@ -67,7 +67,7 @@ def load():
     lib.kda_chunk_prefill_varlen_workspace_size.restype = sz
     lib.kda_chunk_prefill_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.kda_chunk_prefill_varlen.restype = i
-    lib.kda_chunk_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp, fp, i, i,
+    lib.kda_chunk_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, i, fp, i, i,
                                              i, i, i, i, i, i, i, u, vp, sz, vp]
     _lib = lib
     return lib
@@ -171,7 +171,7 @@ def num_checkpoints(cu_seqlens, state_interval) -> int:
 
 def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=None, chunk_size=64,
                          l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False,
-                         state_interval=0, chunk_states=None):
+                         state_interval=0, chunk_states=None, slot=None):
     """KDA prefill of N sequences packed end to end.  q,k [T,H,dk], v [T,H,dv] (bf16 or fp32),
     log_alpha [T,H,dk] fp32 ([T,H] with scalar_gate), beta [T,H] fp32, cu_seqlens [N+1] int32
     on the GPU (sequence i = tokens cu_seqlens[i] .. cu_seqlens[i+1]-1), initial_state
@@ -179,7 +179,9 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     With state_interval > 0 it also saves each sequence's state after every state_interval
     tokens (a multiple of chunk_size) and returns (o, final_state, chunk_states [M,H,dk,dv]),
     sequence by sequence in order; chunk_states is allocated when not given (M from
-    cu_seqlens, copied to the host)."""
+    cu_seqlens, copied to the host).  With slot ([N] int32 on the GPU), initial_state and
+    final_state are a pool [S,H,dk,dv] (pass the same tensor to update it in place) and
+    sequence i uses entry slot[i]; final_state must then be given."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -194,14 +196,21 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
     N = cu_seqlens.numel() - 1
+    n_slots = 0
+    if slot is not None:
+        _req(slot, "slot", torch.int32, (N,))
+        if final_state is None:
+            raise ValueError("with slot, final_state (the state pool) must be given")
+        n_slots = final_state.shape[0]
+    rows = n_slots if slot is not None else N
     if initial_state is not None:
-        _req(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+        _req(initial_state, "initial_state", torch.float32, (rows, H, dk, dv))
     if out is None:
         out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     _req(out, "out", q.dtype, (T, H, dv))
     if final_state is None:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    _req(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    _req(final_state, "final_state", torch.float32, (rows, H, dk, dv))
     n_states = 0
     if state_interval:
         if chunk_states is None:
@@ -219,6 +228,7 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_chunk_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                       _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                      _ptr(slot), n_slots,
                                       _ptr(chunk_states) if state_interval else None, n_states,
                                       int(state_interval),
                                       N, T, H, dk, dv, int(chunk_size), dt,

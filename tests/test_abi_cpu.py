@@ -148,12 +148,13 @@ def test_workspace_size_query(lib):
 
 
 def _varlen(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, cu=FAKE, s0=None, o=FAKE, sT=FAKE, ck=None,
-             nck=0, every=0, N=3, T=200, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0, ws=FAKE,
-             wsb=1 << 40)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, cu=FAKE, s0=None, o=FAKE, sT=FAKE, slot=None,
+             nslot=0, ck=None, nck=0, every=0, N=3, T=200, H=2, dk=128, dv=128, chunk=64, dtype=0, flags=0,
+             ws=FAKE, wsb=1 << 40)
     a.update(kw)
     return lib.kda_chunk_prefill_varlen(a["q"], a["k"], a["v"], a["la"], a["beta"], a["cu"], a["s0"],
-                                        a["o"], a["sT"], a["ck"], a["nck"], a["every"], a["N"], a["T"],
+                                        a["o"], a["sT"], a["slot"], a["nslot"], a["ck"], a["nck"], a["every"],
+                                        a["N"], a["T"],
                                         a["H"], a["dk"], a["dv"],
                                         a["chunk"], a["dtype"], a["flags"], a["ws"], a["wsb"], None)
 
@@ -180,6 +181,9 @@ def test_prefill_varlen_validation(lib):
     assert _varlen(lib, ck=ctypes.c_void_p(0x10002), nck=4, every=128) == INVALID
     assert _varlen(lib, ck=FAKE, nck=4, every=128, wsb=64) == WORKSPACE
     assert _varlen(lib, ck=None, nck=-5, every=-1, wsb=64) == WORKSPACE   # ignored without an array
+    assert _varlen(lib, slot=ctypes.c_void_p(0x10002), nslot=4) == INVALID
+    assert _varlen(lib, slot=FAKE, nslot=-1) == INVALID
+    assert _varlen(lib, slot=FAKE, nslot=8, wsb=64) == WORKSPACE   # a valid slot pool
     assert _varlen(lib, wsb=64) == WORKSPACE
     assert _varlen(lib, ws=None) == WORKSPACE
     assert _varlen(lib, N=0, cu=None, ws=None, wsb=0) == OK   # no sequence: nothing to do

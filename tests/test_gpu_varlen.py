@@ -386,3 +386,36 @@ def test_varlen_wide_tiles_equal_narrow_with_checkpoints(scalar):
         assert torch.equal(ck[k:k + cg.shape[0]], cg), f"checkpoints of sequences {g0}..{g0 + 3}"
         k += cg.shape[0]
     assert k == ck.shape[0]
+
+
+@pytest.mark.parametrize("heads", [2, 16])
+def test_varlen_state_slots(heads):
+    """States from a pool (in place): sequence i starts from pool[slot[i]] and leaves its
+    final state there; other entries are untouched; a slot outside the pool starts from
+    zero and keeps nothing.  Outputs equal the packed call on the gathered states bit for
+    bit; with 16 heads the 80 (sequence, head) pairs take the 32-column scan tiles."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    H, dk, dv, S = heads, 128, 128, 12
+    lengths = [100, 0, 65, 200, 30]
+    slot = np.array([7, 2, -1, 4, 12], np.int32)
+    N = len(lengths)
+    say(f"[case] varlen state slots H={H}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, "bf16", seed=42)
+    d = _dev(inp, "bf16", dev)
+    pool = to_dev(np.concatenate([D.np_state(1, H, dk, dv, 0.1, seed=200 + i) for i in range(S)]), dev=dev)
+    before = pool.clone()
+    valid = (slot >= 0) & (slot < S)
+    gathered = torch.stack([before[int(s)] if ok else torch.zeros_like(before[0]) for s, ok in zip(slot, valid)])
+    o_ref, s_ref = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                            initial_state=gathered.contiguous(), l2norm_qk=True)
+    o, _ = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                    initial_state=pool, final_state=pool, slot=to_dev(slot, dev=dev), l2norm_qk=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for i in range(N):
+        if valid[i]:
+            assert torch.equal(pool[int(slot[i])], s_ref[i]), f"slot {slot[i]} of sequence {i}"
+    for j in sorted(set(range(S)) - set(int(x) for x in slot[valid])):
+        assert torch.equal(pool[j], before[j]), f"slot {j} changed"
