@@ -20,7 +20,7 @@
 //   prep_kernel: one workgroup per (b, h, chunk), fully parallel; writes Wn, Qt and
 //     Kh^T, the lower-triangular fragments of P and -T' (bf16, MFMA operand order),
 //     Gam_last and the validity bits of the chunk's rows to a workspace;
-//   scan_kernel: one workgroup per (b, h, 16-column dv tile); a loop over the
+//   scan_kernel: one workgroup per (b, h, 16- or 32-column dv tile); a loop over the
 //     chunks in order with the fp32 state tile in registers.  Each chunk's operands
 //     are loaded into registers one chunk ahead of their use, and T' V for the next
 //     chunk is formed from V read straight from the input.
@@ -683,7 +683,8 @@ prep_kernel(PrepParams p) {
 }
 
 // ================================================================ scan kernel
-// One workgroup per (b, h, 16-column dv tile), eight waves in two roles.
+// One workgroup per (b, h, dv tile of 16 columns, or of 32 as two 16-column halves),
+// eight waves in two roles.
 //   Waves 0-3 carry the state: wave w owns state row tiles w, w+4, ... and row tile w of
 //   U.  Per chunk: T' V and U = T' V + Wn S, U exchanged through LDS, then
 //   S <- Diag(Gam_last) S + Kh^T U, published to LDS for the next chunk.
