@@ -419,3 +419,37 @@ def test_varlen_state_slots(heads):
             assert torch.equal(pool[int(slot[i])], s_ref[i]), f"slot {slot[i]} of sequence {i}"
     for j in sorted(set(range(S)) - set(int(x) for x in slot[valid])):
         assert torch.equal(pool[j], before[j]), f"slot {j} changed"
+
+
+def test_varlen_many_sequences_chunk_table():
+    """2500 packed sequences: the chunk table is built in several passes of the setup
+    workgroup (1024 sequences each), carrying chunk and checkpoint counts from pass to
+    pass.  The result equals the same sequences packed in calls of at most 1000 (one pass
+    each) bit for bit, outputs, final states and checkpoints."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    H, dk, dv, chunk, interval = 2, 64, 64, 32, 32
+    r = np.random.default_rng(43)
+    lengths = [int(x) for x in r.integers(0, 100, 2500)]
+    N = len(lengths)
+    say(f"[case] varlen N={N} T={sum(lengths)}")
+    inp, cu = _packed_inputs(lengths, H, dk, dv, "bf16", seed=43)
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=43), dev=dev)
+    d = _dev(inp, "bf16", dev)
+    o, sN, ck = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                         initial_state=s0, chunk_size=chunk, state_interval=interval)
+    k = 0
+    for g0 in range(0, N, 1000):
+        g1 = min(N, g0 + 1000)
+        a, b = int(cu[g0]), int(cu[g1])
+        cu_g = (cu[g0:g1 + 1] - cu[g0]).astype(np.int32)
+        og, sg, cg = kda.chunk_prefill_varlen(*(d[n][a:b].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                              to_dev(cu_g, dev=dev), initial_state=s0[g0:g1].contiguous(),
+                                              chunk_size=chunk, state_interval=interval)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], og), f"o of sequences {g0}..{g1 - 1}"
+        assert torch.equal(sN[g0:g1], sg), f"states of sequences {g0}..{g1 - 1}"
+        assert torch.equal(ck[k:k + cg.shape[0]], cg), f"checkpoints of sequences {g0}..{g1 - 1}"
+        k += cg.shape[0]
+    assert k == ck.shape[0] == sum(L // interval for L in lengths)
