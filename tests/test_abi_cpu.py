@@ -236,3 +236,18 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         kda.short_conv(x, torch.zeros(8, 4))
+    q = torch.zeros(8, 2, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.chunk_prefill_varlen(q, q, q, torch.zeros(8, 2, 16), torch.zeros(8, 2),
+                                 torch.tensor([0, 8], dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.chunk_prefill(q[None], q[None], q[None], torch.zeros(1, 8, 2, 16), torch.zeros(1, 8, 2))
+
+
+def test_checkpoint_count():
+    """Entries of the packed prefill's state checkpoints: floor(length / interval) per
+    sequence (host-side helper of the binding)."""
+    pytest.importorskip("torch")
+    assert kda.num_checkpoints([0, 5, 70, 70, 200], 32) == 0 + 2 + 0 + 4
+    assert kda.num_checkpoints([0, 64, 128], 64) == 2
+    assert kda.num_checkpoints([0], 16) == 0
