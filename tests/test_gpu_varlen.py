@@ -453,3 +453,32 @@ def test_varlen_many_sequences_chunk_table():
         assert torch.equal(ck[k:k + cg.shape[0]], cg), f"checkpoints of sequences {g0}..{g1 - 1}"
         k += cg.shape[0]
     assert k == ck.shape[0] == sum(L // interval for L in lengths)
+
+
+def test_varlen_all_empty_and_no_sequences():
+    """Edge cases: every packed sequence empty (T = 0) copies each initial state to its
+    final state (and to its slot); no sequences at all is a no-op."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    N, H, dk, dv = 3, 2, 64, 128
+    say("[case] varlen all-empty, N = 0")
+    e = lambda *shape: torch.empty(*shape, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    s0 = to_dev(D.np_state(N, H, dk, dv, 0.1, seed=44), dev=dev)
+    cu = torch.zeros(N + 1, dtype=torch.int32, device=dev)
+    la = torch.empty(0, H, dk, dtype=torch.float32, device=dev)
+    beta = torch.empty(0, H, dtype=torch.float32, device=dev)
+    o, sN = kda.chunk_prefill_varlen(e(0, H, dk), e(0, H, dk), e(0, H, dv), la, beta, cu, initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, dv) and torch.equal(sN, s0)
+    pool = to_dev(D.np_state(5, H, dk, dv, 0.1, seed=45), dev=dev)
+    before = pool.clone()
+    slot = torch.tensor([4, -1, 0], dtype=torch.int32, device=dev)
+    kda.chunk_prefill_varlen(e(0, H, dk), e(0, H, dk), e(0, H, dv), la, beta, cu, initial_state=pool,
+                             final_state=pool, slot=slot)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, before)                   # each used slot rewritten with itself
+    o0, s00 = kda.chunk_prefill_varlen(e(0, H, dk), e(0, H, dk), e(0, H, dv), la, beta,
+                                       torch.zeros(1, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert s00.shape == (0, H, dk, dv)
