@@ -176,10 +176,11 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  * read on the device, not on the host: entries outside [0, T] are clamped
  * into it and a decreasing entry gives an empty sequence, so a malformed
  * array gives wrong results but no out-of-bounds access (checkpoints included,
- * as num_states bounds them).  Supported: as
+ * as num_states bounds them; slots, as num_slots bounds them).  Supported: as
  * kda_chunk_prefill with B = N (N <= 65535), and H times (ceil(T/chunk) + N)
  * < 2^31.  16-byte aligned: q, k, v, and log_alpha unless KDA_FLAG_SCALAR_GATE
- * is set; chunk_states and slot 4-byte aligned.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
+ * is set; chunk_states and slot 4-byte aligned.  `flags` may hold
+ * KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
  */
 int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, const int32_t* cu_seqlens,
