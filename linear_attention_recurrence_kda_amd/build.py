@@ -1,9 +1,15 @@
-"""Build libkda.so (hand-written HIP for gfx950 + the C ABI) in-tree with hipcc."""
+"""Build libkda.so (hand-written HIP for gfx950 + the C ABI) in-tree with hipcc.
+
+Each source is compiled to an object in its own hipcc process (in parallel), then the
+objects are linked into the shared library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -11,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_prefill.hip"]
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators in VGPRs: results feed VALU code directly, no accumulator-register copies
@@ -20,19 +26,34 @@ FLAGS = [
 ]
 
 
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops" not in l)
+
+
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    with tempfile.TemporaryDirectory(prefix="kda_build_") as tmpd:
+        def compile_one(src):
+            obj = os.path.join(tmpd, os.path.splitext(src)[0] + ".o")
+            cmd = [hipcc, *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            return src, obj, r.returncode, _clean(r.stderr)
+
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        for src, _, rc, errs in results:
+            if rc != 0:
+                raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{errs}")
+            if verbose and errs.strip():
+                print(errs, file=sys.stderr)
+        tmp = LIB + ".tmp"
+        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o, _, _ in results], "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed ({r.returncode}):\n{_clean(r.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 
