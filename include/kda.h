@@ -25,7 +25,8 @@
  *     the caller, and aligned to their element size; the tensors each entry
  *     point reads with 16-byte vector accesses (listed there) must be 16-byte
  *     aligned.  The library allocates nothing, keeps no pointer after
- *     returning, and holds no global state.
+ *     returning, and holds no global state, except the per-GPU scratch array
+ *     of kda_chunk_prefill_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it; nothing synchronises the host.
  *   - Arguments are validated on the host before any HIP call.  A failing call
@@ -118,6 +119,30 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       const float* init_state, void* o, float* final_state,
                       int B, int T, int H, int dk, int dv, int chunk, int dtype,
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Arguments,
+ * results and supported sizes are those of kda_chunk_prefill, without the workspace:
+ * the call uses a scratch array that the library holds on each GPU (allocated with the
+ * library's code on that device, kept until the process ends) and calls no allocating
+ * routine.  Its size is kda_noalloc_scratch_bytes() (256 MiB); a call whose
+ * kda_chunk_prefill_workspace_size(...) exceeds it returns KDA_ERR_WORKSPACE before any
+ * HIP call.  The first call on a device looks the array's address up
+ * (hipGetSymbolAddress, no allocation); make that first call outside graph capture.
+ * Every call on one GPU shares that GPU's array: calls that can overlap on one GPU
+ * (different streams, or different host threads without ordering) race and must not be
+ * issued; calls in order on one stream are fine.  Nothing in the array needs clearing
+ * between calls (every byte a call reads there was written earlier in that call).
+ */
+int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v,
+                              const float* log_alpha, const float* beta, const uint8_t* mask,
+                              const float* init_state, void* o, float* final_state,
+                              int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                              unsigned flags, void* stream);
+
+/* Bytes of the per-GPU scratch array of kda_chunk_prefill_noalloc. */
+size_t kda_noalloc_scratch_bytes(void);
 
 /*
  * Bytes of device workspace kda_chunk_prefill_varlen needs for N packed

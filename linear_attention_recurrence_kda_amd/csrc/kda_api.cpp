@@ -60,7 +60,8 @@ static int prefill_entry(const void* q, const void* k, const void* v, const floa
                          const float* beta, const uint8_t* mask, const int32_t* cu_seqlens, bool varlen,
                          const float* init_state, void* o, float* final_state, const int32_t* slot,
                          int num_slots, float* chunk_states, int num_states, int state_interval, int B, int T, int H, int dk, int dv, int chunk, int dtype,
-                         unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
+                         unsigned flags, void* workspace, size_t workspace_bytes, void* stream,
+                         bool use_scratch = false) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
   if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
@@ -87,6 +88,17 @@ static int prefill_entry(const void* q, const void* k, const void* v, const floa
     }
   }
   const size_t need = kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype, varlen);
+  if (use_scratch) {
+    // the library's per-device scratch array stands in for the workspace: no allocation
+    if (need > kda::kNoallocScratchBytes) return KDA_ERR_WORKSPACE;
+    if (need > 0 && work) {
+      void* p = nullptr;
+      const hipError_t e = kda::noalloc_scratch(&p);
+      if (e != hipSuccess) return hip_status(e);
+      workspace = p;
+      workspace_bytes = kda::kNoallocScratchBytes;
+    }
+  }
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return KDA_ERR_WORKSPACE;
   if (!work) return KDA_OK;
@@ -105,6 +117,16 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
   return prefill_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, o, final_state, nullptr, 0, nullptr, 0, 0,
                        B, T, H, dk, dv, chunk, dtype, flags, workspace, workspace_bytes, stream);
 }
+
+int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* beta, const uint8_t* mask, const float* init_state, void* o,
+                              float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                              unsigned flags, void* stream) {
+  return prefill_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, o, final_state, nullptr, 0, nullptr, 0, 0,
+                       B, T, H, dk, dv, chunk, dtype, flags, nullptr, 0, stream, true);
+}
+
+size_t kda_noalloc_scratch_bytes(void) { return kda::kNoallocScratchBytes; }
 
 int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const float* log_alpha,
                              const float* beta, const int32_t* cu_seqlens, const float* init_state,

@@ -66,6 +66,10 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
+// bytes of the per-device scratch array of kda_chunk_prefill_noalloc
+constexpr size_t kNoallocScratchBytes = (size_t)256 << 20;
+// the current device's scratch array (device address), resolved on first use per device
+hipError_t noalloc_scratch(void** ptr);
 // varlen: B packed sequences of T tokens in total (cu_seqlens given)
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen);
 bool prefill_supported(int dk, int dv, int chunk);

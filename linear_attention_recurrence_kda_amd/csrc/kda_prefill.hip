@@ -33,6 +33,8 @@
 // Precision: bf16 MFMA operands that are not exactly bf16 are split into a
 // bf16 high part and a bf16 residual where that matters (A, P, T', S, U);
 // with fp32 inputs every operand is split.
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -1485,6 +1487,36 @@ static hipError_t launch_prefill_dt(const PrefillArgs& a) {
   KDA_FOR_SHAPES(KDA_PF)
 #undef KDA_PF
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------- scratch for callers that cannot allocate
+// The workspace of kda_chunk_prefill_noalloc: one array per GPU, resident from the first
+// use of the library's code on that device until the process ends.  Host code never
+// passes the array's name to a kernel (on the host that name is only a stand-in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, resolved once per
+// device with that device current.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& args) {

@@ -21,7 +21,7 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
            "kda_chunk_prefill_workspace_size", "kda_chunk_prefill", "kda_decode_step",
            "kda_short_conv", "kda_decode_step_fused", "kda_chunk_prefill_varlen_workspace_size",
-           "kda_chunk_prefill_varlen")
+           "kda_chunk_prefill_varlen", "kda_chunk_prefill_noalloc", "kda_noalloc_scratch_bytes")
 
 _lib = None
 
@@ -69,6 +69,11 @@ def load():
     lib.kda_chunk_prefill_varlen.restype = i
     lib.kda_chunk_prefill_varlen.argtypes = [vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, i, fp, i, i,
                                              i, i, i, i, i, i, i, u, vp, sz, vp]
+    lib.kda_chunk_prefill_noalloc.restype = i
+    lib.kda_chunk_prefill_noalloc.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp,
+                                              i, i, i, i, i, i, i, u, vp]
+    lib.kda_noalloc_scratch_bytes.restype = sz
+    lib.kda_noalloc_scratch_bytes.argtypes = []
     _lib = lib
     return lib
 
@@ -153,6 +158,42 @@ def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk
                                (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
                                _ptr(workspace), wbytes, _stream())
     _check("kda_chunk_prefill", st)
+    return out, final_state
+
+
+def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
+                          l2norm_qk=False, out=None, final_state=None, scalar_gate=False):
+    """kda_chunk_prefill_noalloc: chunk_prefill without a workspace (the library's per-GPU
+    scratch array stands in for it).  out and final_state may be given so that the call
+    itself allocates nothing; otherwise they are allocated here, before the C call."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (B, T, H, dk))
+    _req(v, "v", q.dtype, (B, T, H, dv))
+    _req(log_alpha, "log_alpha", torch.float32, (B, T, H) if scalar_gate else (B, T, H, dk))
+    _req(beta, "beta", torch.float32, (B, T, H))
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        _req(mask, "mask", torch.uint8, (B, T))
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, (B, H, dk, dv))
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    _req(out, "out", q.dtype, (B, T, H, dv))
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _req(final_state, "final_state", torch.float32, (B, H, dk, dv))
+    st = lib.kda_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                                       _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                       B, T, H, dk, dv, int(chunk_size), dt,
+                                       (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
+                                       (KDA_FLAG_SCALAR_GATE if scalar_gate else 0), _stream())
+    _check("kda_chunk_prefill_noalloc", st)
     return out, final_state
 
 

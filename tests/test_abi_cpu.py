@@ -251,3 +251,26 @@ def test_checkpoint_count():
     assert kda.num_checkpoints([0, 5, 70, 70, 200], 32) == 0 + 2 + 0 + 4
     assert kda.num_checkpoints([0, 64, 128], 64) == 2
     assert kda.num_checkpoints([0], 16) == 0
+
+
+def test_noalloc_validation(lib):
+    """kda_chunk_prefill_noalloc checks its arguments as kda_chunk_prefill does, and rejects a
+    call whose workspace would not fit the scratch array, all before any HIP call."""
+    lim = lib.kda_noalloc_scratch_bytes()
+    assert lim == 256 << 20
+
+    def call(**kw):
+        a = dict(B=1, T=4096, H=4, dk=128, dv=128, chunk=64, dtype=0, flags=0, q=FAKE, o=FAKE)
+        a.update(kw)
+        return lib.kda_chunk_prefill_noalloc(a["q"], FAKE, FAKE, FAKE, FAKE, None, None, a["o"], FAKE,
+                                             a["B"], a["T"], a["H"], a["dk"], a["dv"], a["chunk"],
+                                             a["dtype"], a["flags"], None)
+    assert call(dk=7) == UNSUPPORTED
+    assert call(q=MISALIGNED) == INVALID
+    assert call(flags=8) == INVALID
+    assert call(o=None) == INVALID
+    big = 1
+    while lib.kda_chunk_prefill_workspace_size(1, big, 32, 128, 128, 64, 0) <= lim:
+        big *= 2
+    assert call(T=big, H=32) == WORKSPACE
+    assert call(B=0) == OK                   # nothing to do: no HIP call either
