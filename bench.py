@@ -30,9 +30,27 @@ DECODE_BYTES_PER_SH = 132612         # state read+write 8*K*V + q,k,v,o (1024) +
 # scaled by a known-size streaming kernel in the same run (factors 2.0 and 1.0 on this GPU).  A
 # figure is reported only while the kernel sources still hash to what was profiled.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "ed9eab2da7a64a5c", "bytes": 16.322e9},
+    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "824fa92e8af04dea", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "e4ebe6e233fa9d6f", "bytes": 1.087e9},
 }
+
+
+# MFMA counters of the 128k prefill call (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+# SQ_INSTS_VALU_MFMA_MOPS_BF16 ...; busy % = busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)),
+# reported only while the kernel sources hash to what was profiled.
+MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "824fa92e8af04dea",
+                 "prep_busy_pct": 8.1, "scan_busy_pct": 19.5, "call_busy_pct": 14.5, "issued_flop_per_call": 1.433e12}
+
+
+def measured_mfma(default_workload):
+    import hashlib
+    h = hashlib.sha256()
+    for name in MEASURED_MFMA["sources"]:
+        with open(os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if not (default_workload and h.hexdigest()[:16] == MEASURED_MFMA["sha"]):
+        return None
+    return {k: v for k, v in MEASURED_MFMA.items() if k not in ("sources", "sha")}
 
 
 def measured_traffic(key, default_workload):
@@ -89,8 +107,20 @@ def cpu_baseline(args):
         _, state = O.c_prefill(**inp, init_state=state, nthreads=threads)
     dt = time.perf_counter() - t0
     return {"value": seg * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"fp64 token loop, B=1 H=32 dk=dv=128: a {seg}-token segment chained "
                       f"{reps}x ({seg * reps} tokens), {dt:.1f} s wall"}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -297,6 +327,7 @@ def main():
                     "algorithmic_GBps": pre_gbs, "hbm_frac": pre_gbs / HBM_PEAK_GBS,
                     "hbm_frac_of_copy": pre_gbs / copy_gbs,
                     "model_tflops": pre_tflops, "mfma_frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
+                    "mfma_counters": measured_mfma(default_wl),
                     "roofline_frac": max(pre_gbs / HBM_PEAK_GBS, pre_tflops / MFMA_BF16_PEAK_TFLOPS)},
         "prefill_varlen": {"N": Nv, "T_total": T, "len_min": min(lens), "len_max": max(lens), "ms": varlen_ms,
                            "tokens_per_s": T / (varlen_ms * 1e-3),

@@ -105,8 +105,10 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  *   o           [B,T,H,dv]   dtype, written (0 at masked positions)
  *   final_state [B,H,dk,dv]  fp32, written; may be the same pointer as init_state
  *
- * Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64, 128, 256} (128
- * and 256 run as 64-token chunks); B, H <= 65535; H times the number of
+ * Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64} (128 and 256,
+ * the pages' 256-token chunks included, return KDA_ERR_UNSUPPORTED: their decay
+ * factors leave the fp32 range with this kernel's chunk-start factorisation and
+ * their inverse does not fit the LDS); B, H <= 65535; H times the number of
  * chunks < 2^31 (KDA_ERR_UNSUPPORTED otherwise);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
  * and log_alpha unless KDA_FLAG_SCALAR_GATE is set.  The ragged tail of the last chunk is handled as masked

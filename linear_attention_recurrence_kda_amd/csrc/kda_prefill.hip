@@ -1374,17 +1374,17 @@ varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCm
 }
 
 // ================================================================ host side
-// The chunk size only changes rounding (the result is the token recurrence for any
-// chunk), so chunks above 64 tokens run as 64-token chunks: a 128- or 256-token WY
-// block would not fit the LDS of a workgroup, and its decay factors would leave the fp32
-// range for ordinary gates.
-static int run_chunk(int chunk) { return chunk > 64 ? 64 : chunk; }
+// Chunks of 16, 32 and 64 tokens.  The pages' kernel uses 256-token chunks; this one does
+// not accept 128 or 256: with the chunk-start factorisation the decay factors of such a
+// chunk leave the fp32 range for ordinary gates, its fp32 C x C inverse alone would take
+// 64 KB (C = 128) or 256 KB (C = 256) of the 160 KB LDS, and the scan's per-token operand
+// stream (P and T' grow with C) would grow by a fifth at C = 128.
 static int tile_chunk(int chunk) { return chunk <= 32 ? 32 : 64; }
 static int pad_k(int dk) { return dk < 32 ? 32 : dk; }
 
 bool prefill_supported(int dk, int dv, int chunk) {
   (void)dk; (void)dv;
-  return chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128 || chunk == 256;
+  return chunk == 16 || chunk == 32 || chunk == 64;
 }
 
 // (padded dk, dv, tile chunk) instantiated
@@ -1408,7 +1408,7 @@ static size_t chunk_ws_elems(int K, int V, int C, int dtype) {
 // chunks the workspace holds: per batch row, or for N packed sequences the bound
 // T / chunk + N (each sequence adds at most one partial chunk)
 static long long prefill_chunks(int B, int T, int chunk, bool varlen) {
-  const int c = run_chunk(chunk);
+  const int c = chunk;
   const long long nc = T > 0 ? ((long long)T + c - 1) / c : 0;
   return varlen ? nc + B : nc;
 }
@@ -1422,7 +1422,7 @@ static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen) {
   if (B == 0 || H == 0 || (T == 0 && !varlen)) return 0;
   const long long NC = prefill_chunks(B, T, chunk, varlen);
-  const size_t per_chunk = chunk_ws_elems(pad_k(dk), dv, tile_chunk(run_chunk(chunk)), dtype) * 2;
+  const size_t per_chunk = chunk_ws_elems(pad_k(dk), dv, tile_chunk(chunk), dtype) * 2;
   if (!varlen) return (size_t)B * H * NC * per_chunk + kSinkBytes;
   // packed: H x NC chunks, the sink, then the chunk table (span, seq, first)
   return (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + (size_t)B * 16 +
@@ -1520,9 +1520,7 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& args) {
-  PrefillArgs a = args;
-  a.chunk = run_chunk(a.chunk);
-  return a.dtype == 0 ? launch_prefill_dt<0>(a) : launch_prefill_dt<1>(a);
+  return args.dtype == 0 ? launch_prefill_dt<0>(args) : launch_prefill_dt<1>(args);
 }
 
 }  // namespace kda

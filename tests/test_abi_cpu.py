@@ -142,8 +142,8 @@ def test_workspace_size_query(lib):
     assert f(1, 65, 1, 128, 128, 64, 0) == one + per_chunk   # ragged tail takes a whole chunk
     assert f(4, 4096, 32, 128, 128, 64, 0) == one + (4 * 32 * 64 - 1) * per_chunk
     assert f(1, 64, 1, 128, 128, 64, 1) > one            # fp32 inputs keep residual parts
-    for big in (128, 256):                               # run as 64-token chunks: same workspace
-        assert f(4, 4096, 32, 128, 128, big, 0) == f(4, 4096, 32, 128, 128, 64, 0)
+    for big in (128, 256):                               # outside the supported chunks
+        assert f(4, 4096, 32, 128, 128, big, 0) == 0
     assert f(1, 64, 1, 128, 128, 512, 0) == 0
 
 
@@ -274,3 +274,19 @@ def test_noalloc_validation(lib):
         big *= 2
     assert call(T=big, H=32) == WORKSPACE
     assert call(B=0) == OK                   # nothing to do: no HIP call either
+
+
+def test_large_chunks_are_rejected(lib):
+    """chunk 128 and 256 are outside the supported set: the size queries return 0 and the
+    calls return KDA_ERR_UNSUPPORTED before any HIP call (batch, packed and no-alloc)."""
+    for chunk in (128, 256, 48, 0, -64):
+        assert lib.kda_chunk_prefill_workspace_size(1, 1024, 4, 128, 128, chunk, 0) == 0
+        assert lib.kda_chunk_prefill_varlen_workspace_size(2, 1024, 4, 128, 128, chunk, 0) == 0
+        st = lib.kda_chunk_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                   1, 1024, 4, 128, 128, chunk, 0, 0, FAKE, 1 << 30, None)
+        assert st == UNSUPPORTED, (chunk, st)
+        st = lib.kda_chunk_prefill_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                           1, 1024, 4, 128, 128, chunk, 0, 0, None)
+        assert st == UNSUPPORTED, (chunk, st)
+    for chunk in (16, 32, 64):
+        assert lib.kda_chunk_prefill_workspace_size(1, 1024, 4, 128, 128, chunk, 0) > 0
