@@ -18,6 +18,9 @@ Contents
   "Two auditing norms": a clean verdict needs a positive control).
 * ``l2norm``: x / sqrt(sum x^2 + 1e-6), the reading taken for the configs'
   "L2-normalised per head".
+* ``np_prefill_backward``: the fp64 gradients of the token recurrence for the loss
+  sum_t <do_t, o_t> + <dfinal, S_T> (reverse-mode differentiation of the token loop),
+  pinned by central finite differences of the C forward in tests/test_oracle_grad.py.
 
 The recurrence (Kimi Linear summary page, recurrent-layers paragraph; the
 remio.ai page's section on KDA's recurrent memory): per (b, h), with rows of
@@ -182,6 +185,68 @@ def np_prefill(q, k, v, log_alpha, beta, mask=None, init_state=None, l2norm_qk=F
         o[sel, t] = np.einsum("bhij,bhi->bhj", Sn, qt)
         S[sel] = Sn
     return o, S
+
+
+def np_prefill_backward(q, k, v, log_alpha, beta, do, dfinal=None, mask=None, init_state=None):
+    """Gradients of the token recurrence (the blockwise training the remio.ai page names in
+    its KDA section needs them): for the loss L = sum_t <do_t, o_t> + <dfinal, S_T>, the
+    derivatives of L with respect to q, k, v, log_alpha, beta and the initial state, in fp64.
+
+    Reverse-mode differentiation of the token loop of np_prefill, written out step by step
+    (all per-token states are kept, so for small inputs only).  With S' = Diag(a) S_{t-1},
+    a = exp(log_alpha_t), r = v_t - S'^T k_t, u = beta_t r, S_t = S' + k_t u^T and
+    o_t = S_t^T q_t, and lam = dL/dS_t:
+        lam += q_t do_t^T;  dq_t = S_t do_t
+        du = lam^T k_t;  dk_t = lam u;  dbeta_t = du . r;  dv_t = beta_t du
+        dS' = lam - k_t (beta_t du)^T;  dk_t -= S' (beta_t du)
+        dlog_alpha_t = rowsum(dS' * S');  lam <- Diag(a) dS'
+    A masked position leaves lam alone and has zero gradients.  Returns a dict with dq, dk,
+    dv, dlog_alpha, dbeta, dinit_state (the last is returned even without an initial state:
+    it is the gradient with respect to the zero state)."""
+    q, k, v, la, beta, do = map(_f64, (q, k, v, log_alpha, beta, do))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S0 = np.zeros((B, H, dk, dv)) if init_state is None else np.array(_f64(init_state), copy=True)
+    m = np.ones((B, T), bool) if mask is None else (_u8(mask) != 0)
+    # forward, keeping every state
+    states = [S0]
+    S = S0.copy()
+    for t in range(T):
+        Sn = S.copy()
+        for b in range(B):
+            if not m[b, t]:
+                continue
+            for h in range(H):
+                Sp = np.exp(la[b, t, h])[:, None] * S[b, h]
+                u = beta[b, t, h] * (v[b, t, h] - Sp.T @ k[b, t, h])
+                Sn[b, h] = Sp + np.outer(k[b, t, h], u)
+        S = Sn
+        states.append(S)
+    lam = np.zeros((B, H, dk, dv)) if dfinal is None else np.array(_f64(dfinal), copy=True)
+    g = {n: np.zeros_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dlog_alpha", la), ("dbeta", beta))}
+    for t in range(T - 1, -1, -1):
+        for b in range(B):
+            if not m[b, t]:
+                continue
+            for h in range(H):
+                Sprev, St = states[t][b, h], states[t + 1][b, h]
+                a = np.exp(la[b, t, h])
+                Sp = a[:, None] * Sprev
+                kt, qt, vt, bt = k[b, t, h], q[b, t, h], v[b, t, h], beta[b, t, h]
+                r = vt - Sp.T @ kt
+                u = bt * r
+                L = lam[b, h] + np.outer(qt, do[b, t, h])
+                g["dq"][b, t, h] = St @ do[b, t, h]
+                du = L.T @ kt
+                g["dbeta"][b, t, h] = du @ r
+                dr = bt * du
+                g["dv"][b, t, h] = dr
+                g["dk"][b, t, h] = L @ u - Sp @ dr
+                dSp = L - np.outer(kt, dr)
+                g["dlog_alpha"][b, t, h] = np.sum(dSp * Sp, axis=1)
+                lam[b, h] = a[:, None] * dSp
+    g["dinit_state"] = lam
+    return g
 
 
 def np_decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False):
