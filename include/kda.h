@@ -218,6 +218,43 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
                              unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace kda_chunk_prefill_backward needs (0 when none is needed or
+ * the arguments would be rejected).
+ */
+size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv);
+
+/*
+ * Gradients of kda_chunk_prefill for training (remio.ai page, KDA section: the model is
+ * trained with a blockwise algorithm).  For the scalar loss
+ *     L = sum_t <d_o[t], o[t]> + <d_final_state, final_state>
+ * of one prefill with the same inputs, writes dL/dq, dL/dk, dL/dv, dL/dlog_alpha,
+ * dL/dbeta and dL/dinit_state.  Masked positions get zero gradients and pass the state's
+ * gradient through.  The arithmetic is fp32 throughout (state, its gradient, every sum).
+ *
+ *   q, k, v, log_alpha, beta, mask, init_state   as for kda_chunk_prefill (flags = 0)
+ *   d_o           [B,T,H,dv]   dtype
+ *   d_final_state [B,H,dk,dv]  fp32, or NULL (zero)
+ *   dq, dk        [B,T,H,dk]   fp32, written
+ *   dv            [B,T,H,dv]   fp32, written
+ *   d_log_alpha   [B,T,H,dk]   fp32, written
+ *   d_beta        [B,T,H]      fp32, written
+ *   d_init_state  [B,H,dk,dv]  fp32, written (also when init_state is NULL: the gradient
+ *                              with respect to the zero state)
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535; flags = 0 (the L2-norm and
+ * per-head-gate flags return KDA_ERR_UNSUPPORTED).  One workgroup per (b, h) runs the
+ * sequence forward (saving the state every 16 tokens in the workspace) and then backward
+ * 16 tokens at a time, recomputing each segment's states from its saved state; the
+ * workspace holds (ceil(T/16) + 16) states per (b, h).  Outputs must not overlap inputs.
+ */
+int kda_chunk_prefill_backward(const void* q, const void* k, const void* v,
+                               const float* log_alpha, const float* beta, const uint8_t* mask,
+                               const float* init_state, const void* d_o, const float* d_final_state,
+                               float* dq, float* dk, float* dv, float* d_log_alpha, float* d_beta,
+                               float* d_init_state, int B, int T, int H, int dk_, int dv_, int dtype,
+                               unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step: a single new token per sequence, state updated in place
  * (remio.ai page, decode section: KDA keeps a fixed-size state, so each
  * generated token reads and rewrites that state once).

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_prefill.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_prefill.hip", "kda_backward.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU instructions anywhere in the device code

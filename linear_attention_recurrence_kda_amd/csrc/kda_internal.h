@@ -62,7 +62,20 @@ struct PrefillArgs {
   int num_slots;                           // slots in the pool
 };
 
+// gradients of the prefill (see kda_backward.hip)
+struct BackwardArgs {
+  const void *q, *k, *v, *dout;
+  const float *log_alpha, *beta, *init_state, *dfinal;
+  const uint8_t* mask;
+  float *dq, *dk, *dv, *dla, *dbeta, *dinit;
+  int B, T, H, dk_, dv_, dtype;
+  void* workspace;
+  void* stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_backward(const BackwardArgs& a);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -21,7 +21,8 @@ STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
            "kda_chunk_prefill_workspace_size", "kda_chunk_prefill", "kda_decode_step",
            "kda_short_conv", "kda_decode_step_fused", "kda_chunk_prefill_varlen_workspace_size",
-           "kda_chunk_prefill_varlen", "kda_chunk_prefill_noalloc", "kda_noalloc_scratch_bytes")
+           "kda_chunk_prefill_varlen", "kda_chunk_prefill_noalloc", "kda_noalloc_scratch_bytes",
+           "kda_chunk_prefill_backward_workspace_size", "kda_chunk_prefill_backward")
 
 _lib = None
 
@@ -74,6 +75,11 @@ def load():
                                               i, i, i, i, i, i, i, u, vp]
     lib.kda_noalloc_scratch_bytes.restype = sz
     lib.kda_noalloc_scratch_bytes.argtypes = []
+    lib.kda_chunk_prefill_backward_workspace_size.restype = sz
+    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i]
+    lib.kda_chunk_prefill_backward.restype = i
+    lib.kda_chunk_prefill_backward.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+                                               i, i, i, i, i, i, u, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -195,6 +201,48 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
                                        (KDA_FLAG_SCALAR_GATE if scalar_gate else 0), _stream())
     _check("kda_chunk_prefill_noalloc", st)
     return out, final_state
+
+
+def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, mask=None,
+                           initial_state=None, workspace=None):
+    """Gradients of chunk_prefill for L = sum <d_o, o> + <d_final_state, final_state>.
+    Inputs as for chunk_prefill (no flags); d_o [B,T,H,dv] in q's dtype, d_final_state
+    [B,H,dk,dv] fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha,
+    dbeta (shapes of the inputs) and dinit_state [B,H,dk,dv]."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (B, T, H, dk))
+    _req(v, "v", q.dtype, (B, T, H, dv))
+    _req(d_o, "d_o", q.dtype, (B, T, H, dv))
+    _req(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _req(beta, "beta", torch.float32, (B, T, H))
+    if mask is not None:
+        if mask.dtype == torch.bool:
+            mask = mask.to(torch.uint8)
+        _req(mask, "mask", torch.uint8, (B, T))
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, (B, H, dk, dv))
+    if d_final_state is not None:
+        _req(d_final_state, "d_final_state", torch.float32, (B, H, dk, dv))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"dq": torch.empty(B, T, H, dk, **f32), "dk": torch.empty(B, T, H, dk, **f32),
+         "dv": torch.empty(B, T, H, dv, **f32), "dlog_alpha": torch.empty(B, T, H, dk, **f32),
+         "dbeta": torch.empty(B, T, H, **f32), "dinit_state": torch.empty(B, H, dk, dv, **f32)}
+    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                                        _ptr(initial_state), _ptr(d_o), _ptr(d_final_state),
+                                        _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
+                                        _ptr(g["dbeta"]), _ptr(g["dinit_state"]), B, T, H, dk, dv, dt, 0,
+                                        _ptr(workspace), wbytes, _stream())
+    _check("kda_chunk_prefill_backward", st)
+    return g
 
 
 def prefill_varlen_workspace_size(N, T, H, dk, dv, chunk, dtype_code) -> int:

@@ -290,3 +290,34 @@ def test_large_chunks_are_rejected(lib):
         assert st == UNSUPPORTED, (chunk, st)
     for chunk in (16, 32, 64):
         assert lib.kda_chunk_prefill_workspace_size(1, 1024, 4, 128, 128, chunk, 0) > 0
+
+
+def test_backward_validation(lib):
+    """kda_chunk_prefill_backward rejects bad arguments before any HIP call: flags other
+    than 0, unsupported head sizes, missing or misaligned pointers, a short workspace."""
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128) == 0
+    need = lib.kda_chunk_prefill_backward_workspace_size(2, 33, 3, 64, 32)
+    assert need == 2 * 3 * (3 + 16) * 64 * 32 * 4
+
+    def call(**kw):
+        a = dict(B=1, T=33, H=2, dk=64, dv=64, dtype=0, flags=0, q=FAKE, dq=FAKE, dinit=FAKE,
+                 ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.kda_chunk_prefill_backward(a["q"], FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                              a["dq"], FAKE, FAKE, FAKE, FAKE, a["dinit"],
+                                              a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
+                                              a["flags"], a["ws"], a["wsb"], None)
+    assert call(flags=1) == UNSUPPORTED       # L2 norm inside the call is forward-only
+    assert call(flags=2) == UNSUPPORTED       # so is the per-head scalar gate
+    assert call(dk=48) == UNSUPPORTED
+    assert call(dtype=5) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(q=None) == INVALID
+    odd = ctypes.c_void_p(0x10002)          # fp32 outputs need 4-byte alignment
+    assert call(dq=odd) == INVALID
+    assert call(q=ctypes.c_void_p(0x10001)) == INVALID
+    assert call(dinit=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(H=0) == OK                   # nothing to do: no HIP call either

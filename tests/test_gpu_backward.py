@@ -1,0 +1,147 @@
+"""GPU parity of kda_chunk_prefill_backward (through the C ABI) against the oracle's fp64
+gradient np_prefill_backward, itself pinned by finite differences on the CPU.
+
+Bar: the backward computes in fp32 from dtype-exact inputs (bf16 inputs are exact in fp32),
+so both input dtypes are held to fp32 rounding: rel-L2 <= 2e-5 per gradient and
+max-abs <= 1e-4 * max(1, max|ref|)."""
+import numpy as np
+import pytest
+
+from linear_attention_recurrence_kda_amd import datagen as D
+from tests.gpu_util import device, host, metrics, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinit_state")
+REL, ABS = 2e-5, 1e-4
+
+
+def _check(tag, got, ref):
+    for n in NAMES:
+        g, r = host(got[n]), np.asarray(ref[n], np.float64)
+        assert g.shape == r.shape, f"{tag} {n}: shape {g.shape} vs {r.shape}"
+        max_abs, rel = metrics(g, r)
+        scale = max(1.0, float(np.max(np.abs(r), initial=0.0)))
+        say(f"[parity] {tag} {n}: max_abs={max_abs:.3e} (scale {scale:.2e}) rel_l2={rel:.3e}")
+        assert np.all(np.isfinite(g)), f"{tag} {n}: non-finite values"
+        assert max_abs <= ABS * scale, f"{tag} {n}: max_abs {max_abs:.3e} > {ABS * scale:.3e}"
+        assert rel <= REL, f"{tag} {n}: rel_l2 {rel:.3e} > {REL}"
+
+
+def _cotangents(B, T, H, dk, dv, dtype, seed, with_final=True):
+    rng = np.random.default_rng(1000 + seed)
+    do = D.to_storage(rng.normal(0, 1, (B, T, H, dv)).astype(np.float32), dtype)
+    dfinal = rng.normal(0, 1, (B, H, dk, dv)).astype(np.float32) if with_final else None
+    return do, dfinal
+
+
+def _run(inp, do, dfinal, dtype, dev, mask=None, s0=None):
+    from linear_attention_recurrence_kda_amd import kda
+    return kda.chunk_prefill_backward(
+        to_dev(inp["q"], dtype, dev), to_dev(inp["k"], dtype, dev), to_dev(inp["v"], dtype, dev),
+        to_dev(inp["log_alpha"], dev=dev), to_dev(inp["beta"], dev=dev), to_dev(do, dtype, dev),
+        d_final_state=None if dfinal is None else to_dev(dfinal, dev=dev),
+        mask=None if mask is None else to_dev(mask, dev=dev),
+        initial_state=None if s0 is None else to_dev(s0, dev=dev))
+
+
+def _ref(oracle, inp, do, dfinal, mask=None, s0=None):
+    return oracle.np_prefill_backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do,
+                                      dfinal, mask=mask, init_state=s0)
+
+
+def test_backward_tiny_fp32(oracle):
+    """B=1, H=2, T=64, dk=dv=16, fp32, zero initial state, no final-state cotangent."""
+    dev = device()
+    say("[case] backward tiny fp32")
+    inp = D.np_kda_inputs(1, 64, 2, 16, 16, "fp32", seed=0)
+    do, _ = _cotangents(1, 64, 2, 16, 16, "fp32", 0, with_final=False)
+    _check("tiny", _run(inp, do, None, "fp32", dev), _ref(oracle, inp, do, None))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_masked_with_state(oracle, dtype):
+    """T=300 (18 full 16-token segments and a 12-token tail), masks at the start, middle and end."""
+    dev = device()
+    B, T, H, dk, dv = 2, 300, 3, 128, 128
+    say(f"[case] backward {dtype} T={T} masked+state+dfinal")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, dtype, seed=1)
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=1)
+    mask = np.ones((B, T), np.uint8)
+    mask[0, :37] = 0
+    mask[1, 250:] = 0
+    mask[1, 100:103] = 0
+    do, dfinal = _cotangents(B, T, H, dk, dv, dtype, 1)
+    got = _run(inp, do, dfinal, dtype, dev, mask, s0)
+    _check(f"masked {dtype}", got, _ref(oracle, inp, do, dfinal, mask, s0))
+    for n in ("dq", "dk", "dv", "dlog_alpha"):
+        assert np.all(host(got[n])[mask == 0] == 0.0), f"{n} nonzero at a masked position"
+    assert np.all(host(got["dbeta"])[mask == 0] == 0.0)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (64, 64), (128, 32), (16, 64), (128, 16)])
+def test_backward_head_sizes(oracle, dk, dv):
+    dev = device()
+    B, T, H = 2, 37, 2
+    say(f"[case] backward bf16 dk={dk} dv={dv}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=2)
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=2)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 2)
+    _check(f"dk{dk} dv{dv}", _run(inp, do, dfinal, "bf16", dev, s0=s0), _ref(oracle, inp, do, dfinal, s0=s0))
+
+
+@pytest.mark.parametrize("T", [0, 1, 15, 16, 17])
+def test_backward_short_sequences(oracle, T):
+    """No token (dinit = dfinal), one token, and lengths around one segment."""
+    dev = device()
+    B, H, dk, dv = 1, 2, 64, 64
+    say(f"[case] backward T={T}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "fp32", seed=3)
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=3)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "fp32", 3)
+    got = _run(inp, do, dfinal, "fp32", dev, s0=s0)
+    _check(f"T{T}", got, _ref(oracle, inp, do, dfinal, s0=s0))
+    if T == 0:
+        assert np.array_equal(host(got["dinit_state"]), dfinal.astype(np.float64))
+
+
+def test_backward_all_masked_passes_dfinal_through(oracle):
+    dev = device()
+    B, T, H, dk, dv = 2, 40, 2, 32, 32
+    say("[case] backward all masked")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=4)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 4)
+    mask = np.zeros((B, T), np.uint8)
+    got = _run(inp, do, dfinal, "bf16", dev, mask)
+    for n in ("dq", "dk", "dv", "dlog_alpha", "dbeta"):
+        assert np.all(host(got[n]) == 0.0), n
+    assert np.array_equal(host(got["dinit_state"]), dfinal.astype(np.float64))
+
+
+def test_backward_is_deterministic():
+    dev = device()
+    say("[case] backward determinism")
+    inp = D.np_kda_inputs(1, 100, 4, 128, 128, "bf16", seed=5)
+    do, dfinal = _cotangents(1, 100, 4, 128, 128, "bf16", 5)
+    a = _run(inp, do, dfinal, "bf16", dev)
+    b = _run(inp, do, dfinal, "bf16", dev)
+    for n in NAMES:
+        assert np.array_equal(host(a[n]), host(b[n])), n
+
+
+def test_backward_training_size_sampled_heads(oracle):
+    """B=4, H=32, T=4096, dk=dv=128, bf16 (the chunked-prefill shape): the whole batch on
+    the GPU, three (b, h) heads checked against the oracle run on those heads alone (the
+    recurrence of one head does not see the others)."""
+    dev = device()
+    B, T, H, dk, dv = 4, 4096, 32, 128, 128
+    say(f"[case] backward bf16 B={B} T={T} H={H} sampled heads")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=6)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 6)
+    got = _run(inp, do, dfinal, "bf16", dev)
+    for b, h in ((0, 0), (2, 17), (3, 31)):
+        one = {n: x[b:b + 1, :, h:h + 1] for n, x in inp.items()}
+        ref = _ref(oracle, one, do[b:b + 1, :, h:h + 1], dfinal[b:b + 1, h:h + 1])
+        sub = {n: (got[n][b:b + 1, h:h + 1] if n == "dinit_state" else got[n][b:b + 1, :, h:h + 1])
+               for n in NAMES}
+        _check(f"full b{b} h{h}", sub, ref)
