@@ -221,7 +221,7 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
  * Bytes of device workspace kda_chunk_prefill_backward needs (0 when none is needed or
  * the arguments would be rejected).
  */
-size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv);
+size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
 
 /*
  * Gradients of kda_chunk_prefill for training (remio.ai page, KDA section: the model is
@@ -229,7 +229,7 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  *     L = sum_t <d_o[t], o[t]> + <d_final_state, final_state>
  * of one prefill with the same inputs, writes dL/dq, dL/dk, dL/dv, dL/dlog_alpha,
  * dL/dbeta and dL/dinit_state.  Masked positions get zero gradients and pass the state's
- * gradient through.  The arithmetic is fp32 throughout (state, its gradient, every sum).
+ * gradient through.
  *
  *   q, k, v, log_alpha, beta, mask, init_state   as for kda_chunk_prefill (flags = 0)
  *   d_o           [B,T,H,dv]   dtype
@@ -241,11 +241,19 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  *   d_init_state  [B,H,dk,dv]  fp32, written (also when init_state is NULL: the gradient
  *                              with respect to the zero state)
  *
- * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535; flags = 0 (the L2-norm and
- * per-head-gate flags return KDA_ERR_UNSUPPORTED).  One workgroup per (b, h) runs the
- * sequence forward (saving the state every 16 tokens in the workspace) and then backward
- * 16 tokens at a time, recomputing each segment's states from its saved state; the
- * workspace holds (ceil(T/16) + 16) states per (b, h).  Outputs must not overlap inputs.
+ * It runs the forward again in 64-token chunks, keeping the state at each chunk end,
+ * then a reverse scan over the chunks carries dL/dS (the chunk recurrence differentiated)
+ * and chunk-parallel kernels form the gradients; every sum accumulates in fp32, with
+ * MFMA operands split into bf16 high and low parts (single bf16 for the reverse scan's
+ * key, query and W operands with bf16 inputs, as in the forward scan).  The workspace
+ * holds the forward's own workspace, the chunk-end states and about 250 KB of chunk
+ * operands per (b, h, chunk) at dk = dv = 128.
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535 and H ceil(T/64) < 2^31;
+ * flags = 0 (the L2-norm and per-head-gate flags return KDA_ERR_UNSUPPORTED).
+ * 16-byte aligned: q, k, v, log_alpha, d_o, init_state, dq, dk, dv, d_log_alpha;
+ * 4-byte: beta, d_beta, d_final_state, d_init_state; workspace 256-byte aligned.
+ * Outputs must not overlap inputs.
  */
 int kda_chunk_prefill_backward(const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, const uint8_t* mask,

@@ -138,9 +138,11 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const 
                        workspace_bytes, stream);
 }
 
-size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv) {
-  if (B < 0 || T < 0 || H < 0 || !head_dim_ok(dk) || !head_dim_ok(dv) || B > 65535 || H > 65535) return 0;
-  return kda::backward_workspace_bytes(B, T, H, dk, dv);
+size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype) || !head_dim_ok(dk) || !head_dim_ok(dv) || B > 65535 ||
+      H > 65535 || !kda::prefill_grid_ok(B, T, H, 64, false))
+    return 0;
+  return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype);
 }
 
 int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -152,23 +154,22 @@ int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, cons
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if (flags != 0) return KDA_ERR_UNSUPPORTED;
   if (!head_dim_ok(dk_) || !head_dim_ok(dv_) || B > 65535 || H > 65535) return KDA_ERR_UNSUPPORTED;
+  if (!kda::prefill_grid_ok(B, T, H, 64, false)) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
   if (d_init_state == nullptr || !aligned(d_init_state, 4)) return KDA_ERR_INVALID_ARG;
-  if (init_state != nullptr && !aligned(init_state, 4)) return KDA_ERR_INVALID_ARG;
+  if (init_state != nullptr && !aligned(init_state, 16)) return KDA_ERR_INVALID_ARG;
   if (d_final_state != nullptr && !aligned(d_final_state, 4)) return KDA_ERR_INVALID_ARG;
   if (T > 0) {
     const void* req[] = {q, k, v, log_alpha, beta, d_o, dq, dk, dv, d_log_alpha, d_beta};
     for (const void* ptr : req)
       if (ptr == nullptr) return KDA_ERR_INVALID_ARG;
-    const void* el[] = {q, k, v, d_o};
-    for (const void* ptr : el)
-      if (!aligned(ptr, elem_bytes(dtype))) return KDA_ERR_INVALID_ARG;
-    const void* f32[] = {log_alpha, beta, dq, dk, dv, d_log_alpha, d_beta};
-    for (const void* ptr : f32)
-      if (!aligned(ptr, 4)) return KDA_ERR_INVALID_ARG;
+    const void* a16[] = {q, k, v, log_alpha, d_o, dq, dk, dv, d_log_alpha};
+    for (const void* ptr : a16)
+      if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(beta, 4) || !aligned(d_beta, 4)) return KDA_ERR_INVALID_ARG;
   }
-  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4)))
+  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return KDA_ERR_WORKSPACE;
   kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, mask,
                       dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype,

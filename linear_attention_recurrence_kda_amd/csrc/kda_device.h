@@ -164,4 +164,24 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 __device__ __forceinline__ f32x4 zero4() { return (f32x4){0.f, 0.f, 0.f, 0.f}; }
 
+// Two 16x16 products computed transposed, so lane l holds columns 4 (l/16) .. +3 of row
+// l%16 of column tiles 2s (t0) and 2s + 1 (t1), become the A-operand fragment of k step s
+// (lane l: columns 32 s + 8 (l/16) .. +7 of row l%16) with two cross-lane swaps per
+// register: the 32-lane swap pairs the tiles' halves, the 16-lane swap interleaves them.
+__device__ __forceinline__ void pair_to_afrag(const f32x4& t0, const f32x4& t1, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0[i]), __float_as_uint(t1[i]), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+    out[i] = __uint_as_float(b[0]);
+    out[4 + i] = __uint_as_float(b[1]);
+  }
+}
+// x shifted down by n lanes inside each row of 16 lanes (lanes below n read 0)
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
+}
+
+
 }  // namespace kda

@@ -55,7 +55,8 @@ struct PrefillArgs {
   size_t workspace_bytes;
   void* stream;
   const int32_t* cu_seqlens;               // packed sequences (then B = their number), or null
-  float* chunk_states;                     // packed only: the state every state_interval tokens, or null
+  float* chunk_states;                     // the state every state_interval tokens, or null (the batch
+                                           // layout saves entry b * (T / state_interval) + j - 1)
   int num_states;                          // entries chunk_states holds
   int state_interval;                      // a multiple of chunk
   const int32_t* slot;                     // packed only: each sequence's slot in a state pool, or null
@@ -75,7 +76,7 @@ struct BackwardArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -105,7 +105,7 @@ struct ScanParams {
   void* sink;
   const int4* seq;                         // varlen: each sequence's first token, end, first checkpoint
   const int32_t* first;                    // varlen: each sequence's first chunk (N + 1 entries)
-  float* ckpt;                             // varlen: states saved every ck_every chunks, or null
+  float* ckpt;                             // states saved every ck_every chunks, or null
   int ck_every, ck_cap;                    // ck_cap: entries ckpt holds
   const int32_t* slot;                     // varlen: state slot of each sequence in a pool of S, or null
   int S;
@@ -138,19 +138,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-// Two 16x16 products computed transposed, so lane l holds columns 4 (l/16) .. +3 of row
-// l%16 of column tiles 2s (t0) and 2s + 1 (t1), become the A-operand fragment of k step s
-// (lane l: columns 32 s + 8 (l/16) .. +7 of row l%16) with two cross-lane swaps per
-// register: the 32-lane swap pairs the tiles' halves, the 16-lane swap interleaves them.
-__device__ __forceinline__ void pair_to_afrag(const f32x4& t0, const f32x4& t1, float* out) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0[i]), __float_as_uint(t1[i]), false, false);
-    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
-    out[i] = __uint_as_float(b[0]);
-    out[4 + i] = __uint_as_float(b[1]);
-  }
 }
 // Element (n, j) of an n-major LDS matrix with C bf16 per row and no padding: the
 // 16-byte blocks of row n are permuted by an XOR with bits of n, so 16 lanes that
@@ -205,12 +192,6 @@ __device__ __forceinline__ void ld8t(const float* m, int r, int c, float* out) {
   const float4 b = *reinterpret_cast<const float4*>(&m[swzf<C>(r, c + 4)]);
   out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-}
-
-// x shifted down by n lanes inside each row of 16 lanes (lanes below n read 0)
-template <int N>
-__device__ __forceinline__ float row_shr(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xf, 0xf, false));
 }
 
 // One workgroup per (chunk, head) and batch row; wave I owns rows 16 I .. 16 I + 15 of
@@ -840,6 +821,7 @@ scan_kernel(ScanParams p) {
   // the workspace and its number of chunks (row b of the batch, or packed sequence b)
   size_t seq_tok0 = (size_t)b * p.T, ws_chunk0 = (size_t)bh * p.NC;
   int seq_T = p.T, NCs = p.NC, ck0 = 0;
+  if (p.ckpt != nullptr && p.seq == nullptr) ck0 = b * (p.T / (p.chunk * p.ck_every));
   if (p.seq != nullptr) {
     const int4 sq = p.seq[b];
     seq_tok0 = (size_t)sq.x;
@@ -1445,7 +1427,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   int2* span = nullptr;
   int4* seq = nullptr;
   int32_t* first = nullptr;
-  const bool ckpt = varlen && a.chunk_states != nullptr;
+  const bool ckpt = a.chunk_states != nullptr;
   if (varlen) {
     unsigned char* tail = (unsigned char*)a.workspace + chunks_bytes + kSinkBytes;
     span = reinterpret_cast<int2*>(tail);

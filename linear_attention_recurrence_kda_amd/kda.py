@@ -76,7 +76,7 @@ def load():
     lib.kda_noalloc_scratch_bytes.restype = sz
     lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_chunk_prefill_backward_workspace_size.restype = sz
-    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i]
+    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_prefill_backward.restype = i
     lib.kda_chunk_prefill_backward.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp, fp, fp, fp, fp, fp, fp,
                                                i, i, i, i, i, i, u, vp, sz, vp]
@@ -232,7 +232,7 @@ def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, ma
     g = {"dq": torch.empty(B, T, H, dk, **f32), "dk": torch.empty(B, T, H, dk, **f32),
          "dv": torch.empty(B, T, H, dv, **f32), "dlog_alpha": torch.empty(B, T, H, dk, **f32),
          "dbeta": torch.empty(B, T, H, **f32), "dinit_state": torch.empty(B, H, dk, dv, **f32)}
-    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv))
+    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

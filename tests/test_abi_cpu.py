@@ -295,16 +295,20 @@ def test_large_chunks_are_rejected(lib):
 def test_backward_validation(lib):
     """kda_chunk_prefill_backward rejects bad arguments before any HIP call: flags other
     than 0, unsupported head sizes, missing or misaligned pointers, a short workspace."""
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128) == 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128) == 0
-    need = lib.kda_chunk_prefill_backward_workspace_size(2, 33, 3, 64, 32)
-    assert need == 2 * 3 * (3 + 16) * 64 * 32 * 4
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 64, 64, 7) == 0
+    bf = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0)
+    f32 = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 1)
+    assert 0 < bf < f32
+    # the chunk operands alone: 2 * 3 * 3 chunks of them
+    assert bf > 2 * 3 * 3 * (3 * 64 * 64 * 2 + 64 * 64 * 4 + 6 * 64 * 64 * 4 + 64 * 32 * 4 * 3)
 
     def call(**kw):
-        a = dict(B=1, T=33, H=2, dk=64, dv=64, dtype=0, flags=0, q=FAKE, dq=FAKE, dinit=FAKE,
+        a = dict(B=1, T=33, H=2, dk=64, dv=64, dtype=0, flags=0, q=FAKE, dq=FAKE, s0=None, dinit=FAKE,
                  ws=FAKE, wsb=1 << 30)
         a.update(kw)
-        return lib.kda_chunk_prefill_backward(a["q"], FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+        return lib.kda_chunk_prefill_backward(a["q"], FAKE, FAKE, FAKE, FAKE, None, a["s0"], FAKE, None,
                                               a["dq"], FAKE, FAKE, FAKE, FAKE, a["dinit"],
                                               a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
                                               a["flags"], a["ws"], a["wsb"], None)
@@ -314,10 +318,11 @@ def test_backward_validation(lib):
     assert call(dtype=5) == INVALID
     assert call(T=-1) == INVALID
     assert call(q=None) == INVALID
-    odd = ctypes.c_void_p(0x10002)          # fp32 outputs need 4-byte alignment
-    assert call(dq=odd) == INVALID
-    assert call(q=ctypes.c_void_p(0x10001)) == INVALID
+    assert call(q=MISALIGNED) == INVALID      # 16-byte alignment for the vector loads
+    assert call(dq=MISALIGNED) == INVALID
+    assert call(s0=MISALIGNED) == INVALID
     assert call(dinit=None) == INVALID
     assert call(ws=None) == WORKSPACE
     assert call(wsb=16) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE   # 256-byte alignment
     assert call(H=0) == OK                   # nothing to do: no HIP call either

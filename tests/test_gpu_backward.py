@@ -1,9 +1,9 @@
 """GPU parity of kda_chunk_prefill_backward (through the C ABI) against the oracle's fp64
 gradient np_prefill_backward, itself pinned by finite differences on the CPU.
 
-Bar: the backward computes in fp32 from dtype-exact inputs (bf16 inputs are exact in fp32),
-so both input dtypes are held to fp32 rounding: rel-L2 <= 2e-5 per gradient and
-max-abs <= 1e-4 * max(1, max|ref|)."""
+Bar, per gradient: the forward's bars applied relative to the gradient's scale
+(max(1, max|ref|)), since gradients are not O(1): bf16 inputs rel-L2 <= 5e-3 and
+max-abs <= 2e-2 * scale; fp32 inputs rel-L2 <= 1e-4 and max-abs <= 1e-4 * scale."""
 import numpy as np
 import pytest
 
@@ -13,10 +13,11 @@ from tests.gpu_util import device, host, metrics, say, to_dev
 pytestmark = pytest.mark.gpu
 
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dinit_state")
-REL, ABS = 2e-5, 1e-4
+TOL_G = {"bf16": (5e-3, 2e-2), "fp32": (1e-4, 1e-4)}     # (rel-L2, max-abs per unit scale)
 
 
-def _check(tag, got, ref):
+def _check(tag, got, ref, dtype):
+    REL, ABS = TOL_G[dtype]
     for n in NAMES:
         g, r = host(got[n]), np.asarray(ref[n], np.float64)
         assert g.shape == r.shape, f"{tag} {n}: shape {g.shape} vs {r.shape}"
@@ -56,7 +57,7 @@ def test_backward_tiny_fp32(oracle):
     say("[case] backward tiny fp32")
     inp = D.np_kda_inputs(1, 64, 2, 16, 16, "fp32", seed=0)
     do, _ = _cotangents(1, 64, 2, 16, 16, "fp32", 0, with_final=False)
-    _check("tiny", _run(inp, do, None, "fp32", dev), _ref(oracle, inp, do, None))
+    _check("tiny", _run(inp, do, None, "fp32", dev), _ref(oracle, inp, do, None), "fp32")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -73,7 +74,7 @@ def test_backward_masked_with_state(oracle, dtype):
     mask[1, 100:103] = 0
     do, dfinal = _cotangents(B, T, H, dk, dv, dtype, 1)
     got = _run(inp, do, dfinal, dtype, dev, mask, s0)
-    _check(f"masked {dtype}", got, _ref(oracle, inp, do, dfinal, mask, s0))
+    _check(f"masked {dtype}", got, _ref(oracle, inp, do, dfinal, mask, s0), dtype)
     for n in ("dq", "dk", "dv", "dlog_alpha"):
         assert np.all(host(got[n])[mask == 0] == 0.0), f"{n} nonzero at a masked position"
     assert np.all(host(got["dbeta"])[mask == 0] == 0.0)
@@ -82,17 +83,17 @@ def test_backward_masked_with_state(oracle, dtype):
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 128), (64, 64), (128, 32), (16, 64), (128, 16)])
 def test_backward_head_sizes(oracle, dk, dv):
     dev = device()
-    B, T, H = 2, 37, 2
+    B, T, H = 2, 137, 2
     say(f"[case] backward bf16 dk={dk} dv={dv}")
     inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=2)
     s0 = D.np_state(B, H, dk, dv, 0.05, seed=2)
     do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 2)
-    _check(f"dk{dk} dv{dv}", _run(inp, do, dfinal, "bf16", dev, s0=s0), _ref(oracle, inp, do, dfinal, s0=s0))
+    _check(f"dk{dk} dv{dv}", _run(inp, do, dfinal, "bf16", dev, s0=s0), _ref(oracle, inp, do, dfinal, s0=s0), "bf16")
 
 
-@pytest.mark.parametrize("T", [0, 1, 15, 16, 17])
+@pytest.mark.parametrize("T", [0, 1, 17, 63, 64, 65, 130])
 def test_backward_short_sequences(oracle, T):
-    """No token (dinit = dfinal), one token, and lengths around one segment."""
+    """No token (dinit = dfinal), one token, and lengths around one and two 64-token chunks."""
     dev = device()
     B, H, dk, dv = 1, 2, 64, 64
     say(f"[case] backward T={T}")
@@ -100,7 +101,7 @@ def test_backward_short_sequences(oracle, T):
     s0 = D.np_state(B, H, dk, dv, 0.05, seed=3)
     do, dfinal = _cotangents(B, T, H, dk, dv, "fp32", 3)
     got = _run(inp, do, dfinal, "fp32", dev, s0=s0)
-    _check(f"T{T}", got, _ref(oracle, inp, do, dfinal, s0=s0))
+    _check(f"T{T}", got, _ref(oracle, inp, do, dfinal, s0=s0), "fp32")
     if T == 0:
         assert np.array_equal(host(got["dinit_state"]), dfinal.astype(np.float64))
 
@@ -144,4 +145,30 @@ def test_backward_training_size_sampled_heads(oracle):
         ref = _ref(oracle, one, do[b:b + 1, :, h:h + 1], dfinal[b:b + 1, h:h + 1])
         sub = {n: (got[n][b:b + 1, h:h + 1] if n == "dinit_state" else got[n][b:b + 1, :, h:h + 1])
                for n in NAMES}
-        _check(f"full b{b} h{h}", sub, ref)
+        _check(f"full b{b} h{h}", sub, ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_extreme_decay_chunks(oracle, dtype):
+    """Chunks in which some channels decay below 2^-120 (log_alpha = -3 over 64 tokens) take
+    the entry-by-entry path; the chunks around them stay on the factorised one."""
+    dev = device()
+    B, T, H, dk, dv = 1, 200, 2, 64, 64
+    say(f"[case] backward {dtype} extreme decay")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, dtype, seed=7)
+    inp["log_alpha"][:, 64:128, 0, :5] = -3.0
+    inp["log_alpha"][:, 140:, 1, 40:] = -6.0
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=7)
+    do, dfinal = _cotangents(B, T, H, dk, dv, dtype, 7)
+    _check(f"extreme {dtype}", _run(inp, do, dfinal, dtype, dev, s0=s0), _ref(oracle, inp, do, dfinal, s0=s0), dtype)
+
+
+def test_backward_slow_gates(oracle):
+    """Slow gates (log_alpha = -softplus(z - 5), per-token decay about 0.993): the state keeps
+    hundreds of tokens, the regime where rounding in the reverse scan accumulates most."""
+    dev = device()
+    B, T, H, dk, dv = 1, 1024, 2, 128, 128
+    say("[case] backward bf16 slow gates")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=8, decay="slow")
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 8)
+    _check("slow gates", _run(inp, do, dfinal, "bf16", dev), _ref(oracle, inp, do, dfinal), "bf16")
