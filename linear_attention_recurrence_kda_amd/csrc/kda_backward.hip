@@ -35,6 +35,8 @@
 // bf16 with bf16 inputs (as the forward scan's Wn, Qt and Kh^T are).  A chunk in which some
 // channel decays below 2^-120 cannot use the factorised products (Gam and 1/Gam would leave
 // the fp32 range); it computes the decay-weighted C x C terms entry by entry instead.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -57,8 +59,11 @@ __device__ __forceinline__ size_t afrag(int rt, int ks, int lane, int kk) {
 struct Ws {
   uint16_t *kh, *wt, *qt, *pt;           // reverse-scan operands (fragments; high parts, then residuals)
   float *gam, *G, *M;                    // Gam_last [KP], G and M [C][C]
+  uint64_t* vbits;                       // bit r: row r of the chunk is valid (in range, unmasked)
   float *dS1, *dU;                       // dL/dS at the chunk end [KP][V], dL/dU [C][V]
-  float *U, *dP, *dPt, *dG, *dGt;        // U [C][V]; dP, dG and their transposes [C][C]
+  float *U, *dP, *dG;                    // U [C][V]; dP and dG [C][C]
+  float *Y, *ss;                         // dO S0^T, dR S0^T, U dS1^T [3][C][KP] (fragment order);
+                                         // rowsum(dS1 * S0) [KP]
   const float* ck;                       // forward states at chunk ends [B * NCf][H][K][V]
 };
 
@@ -92,6 +97,14 @@ __device__ __forceinline__ f32x4 mm3(const float* a, const float* b, f32x4 acc) 
   return mfma16(ah, bl, acc);
 }
 
+// D += A B, one k step, operands already split (three MFMAs; two when A is exact in bf16)
+template <bool A_EXACT>
+__device__ __forceinline__ f32x4 mma(const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl, f32x4 acc) {
+  acc = mfma16(ah, bh, acc);
+  if (!A_EXACT) acc = mfma16(al, bh, acc);
+  return mfma16(ah, bl, acc);
+}
+
 // four consecutive values as bf16 high parts and residuals, 8-byte writes to LDS
 __device__ __forceinline__ void split4_to_lds(const float* v, __bf16* hi, __bf16* lo) {
   float x[8] = {v[0], v[1], v[2], v[3], 0.f, 0.f, 0.f, 0.f};
@@ -111,44 +124,57 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// One lane's view of chunk n: row 16 w + l%16 (w = wave), channels 32 ks + 8 (l/16) .. +7
-// (the A-operand layout).  q, k and log_alpha of rows that are not valid (masked or past T)
-// and of channels past K are 0.  g becomes the inclusive cumulative sum of log2 decay over
-// the chunk's rows and s_gl the chunk's totals per channel.  Every thread must call it (it
-// holds two barriers).
-template <int DT, int KP>
+// One lane's view of chunk n: row 16 w + l%16 (w = wave), channels c_base + 32 ks + 8 (l/16)
+// .. +7 of a window of KW channels (the A-operand layout).  q, k and log_alpha of rows that
+// are not valid (masked or past T) and of channels past K are 0.  g becomes the inclusive
+// cumulative sum of log2 decay over the chunk's rows and s_gl the chunk's totals per channel
+// of the window.  Every thread must call it (it holds two barriers).
+template <int DT, int KW>
 struct Rows {
-  static constexpr int KS = KP / 32;
+  static constexpr int KS = KW / 32;
   float k[KS][8], q[KS][8], g[KS][8];
   float beta;
   bool ok;
 };
 
-template <int DT, int KP, bool WANT_Q>
-__device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, Rows<DT, KP>& R,
+template <int DT, int KW, bool WANT_Q>
+__device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, int c_base, Rows<DT, KW>& R,
                                           float* s_tot, float* s_gl) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  constexpr int KS = KP / 32;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int KS = KW / 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = 16 * w + (lane & 15), cg = 8 * (lane >> 4);
   const int t = n * kC + r;
   const int ts = t < p.T ? t : p.T - 1;
   const size_t tk = ((size_t)b * p.T + ts) * p.H + h;
-  R.ok = t < p.T && (p.mask == nullptr || p.mask[(size_t)b * p.T + ts] != 0);
-  R.beta = R.ok ? p.beta[tk] : 0.f;
+  // every load is issued unconditionally from an in-bounds row and channel; what is not
+  // valid is replaced by 0 with a select afterwards (a branch on the loaded mask would wait
+  // for it before issuing the rest)
+  const uint8_t mk = p.mask == nullptr ? (uint8_t)1 : p.mask[(size_t)b * p.T + ts];
+  const float bt = p.beta[tk];
+  Raw8<DT> kr[KS], qr[KS];
+  Raw8<1> lr[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int c0 = 32 * ks + cg;
-    if (R.ok && c0 < p.K) {
-      E::ld8((const Tp*)p.k, tk * p.K + c0, R.k[ks]);
-      if (WANT_Q) E::ld8((const Tp*)p.q, tk * p.K + c0, R.q[ks]);
-      Elem<1>::ld8(p.la, tk * p.K + c0, R.g[ks]);
-    } else {
+    const int c0 = c_base + 32 * ks + cg, cs = c0 < p.K ? c0 : 0;
+    kr[ks].load((const Tp*)p.k, tk * p.K + cs);
+    if (WANT_Q) qr[ks].load((const Tp*)p.q, tk * p.K + cs);
+    lr[ks].load(p.la, tk * p.K + cs);
+  }
+  R.ok = t < p.T && mk != 0;
+  R.beta = R.ok ? bt : 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { R.k[ks][e] = 0.f; R.q[ks][e] = 0.f; R.g[ks][e] = 0.f; }
-    }
-    if (!WANT_Q) {
+  for (int ks = 0; ks < KS; ++ks) {
+    const bool cok = R.ok && c_base + 32 * ks + cg < p.K;
+    kr[ks].keep(cok);
+    lr[ks].keep(cok);
+    kr[ks].to_float(R.k[ks]);
+    lr[ks].to_float(R.g[ks]);
+    if (WANT_Q) {
+      qr[ks].keep(cok);
+      qr[ks].to_float(R.q[ks]);
+    } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) R.q[ks][e] = 0.f;
     }
@@ -166,15 +192,15 @@ __device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, 
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_tot[w * KP + 32 * ks + cg + e] = R.g[ks][e];
+      for (int e = 0; e < 8; ++e) s_tot[w * KW + 32 * ks + cg + e] = R.g[ks][e];
   }
   __syncthreads();
-  if (tid < KP) {
+  if (tid < KW) {
     float run = 0.f;
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-      const float x = s_tot[J * KP + tid];
-      s_tot[J * KP + tid] = run;
+      const float x = s_tot[J * KW + tid];
+      s_tot[J * KW + tid] = run;
       run += x;
     }
     s_gl[tid] = run;
@@ -183,7 +209,7 @@ __device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, 
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) R.g[ks][e] += s_tot[w * KP + 32 * ks + cg + e];
+    for (int e = 0; e < 8; ++e) R.g[ks][e] += s_tot[w * KW + 32 * ks + cg + e];
 }
 
 // the chunk's entry state: the initial state for the first chunk, else the forward's
@@ -207,16 +233,24 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float s_A[kC * LC];
   __shared__ __attribute__((aligned(16))) float s_M[kC * LC];    // P, then M
   __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC];
+  __shared__ uint32_t s_vb[4];
 
   const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
   const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
 
   Rows<DT, KP> R;
-  load_rows<DT, KP, true>(p, b, h, n, R, s_tot, s_gl);
+  load_rows<DT, KP, true>(p, b, h, n, 0, R, s_tot, s_gl);
   if (lane < 16) { s_beta[r] = R.beta; s_ok[r] = R.ok ? 1.f : 0.f; }
+  {
+    // validity of the chunk's rows as one 64-bit word (wave w holds rows 16 w .. +15)
+    const unsigned long long bal = __ballot(R.ok) & 0xffffull;
+    if (lane == 0) s_vb[w] = (uint32_t)bal;
+  }
   const bool fast = __syncthreads_and(tid >= KP || s_gl[tid] >= kFastLimit);
+  if (tid == 0)
+    p.w.vbits[ch] = (uint64_t)s_vb[0] | ((uint64_t)s_vb[1] << 16) | ((uint64_t)s_vb[2] << 32) | ((uint64_t)s_vb[3] << 48);
 
   // ---- decayed rows: Kt, Qt (and Ki or g) to LDS, Kh fragments to the workspace
   uint16_t* kh = p.w.kh + ch * (size_t)(kC * KP * parts);
@@ -398,20 +432,72 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
 // Wave w holds state row tiles w and w + 4 of lam = dL/dS (rows 16 rt + 4 (l/16) .. +3,
 // column l%16 of the tile); per chunk: lam is saved as that chunk's dS1, dU's row tile w
 // is formed and exchanged through LDS, then lam <- Diag(Gam_last) lam + W^T dU + Qt^T dO.
+// A chunk's operands are loaded into registers while the chunk after it (in scan order:
+// the one before it in time) is processed; the loop is unrolled by two so that the
+// compiler's load waits are exact.
+template <int DT, int KP>
+struct ScanOps {
+  static constexpr bool SPLIT = DT == 1;
+  static constexpr int KS = KP / 32, MPW = (KP / 16 + 3) / 4, P = SPLIT ? 2 : 1;
+  bf16x8 kh[P][KS];                  // Kh, row tile w
+  bf16x8 pt[2][2];                   // P^T (high, residual), row tile w
+  bf16x8 wt[P][MPW][2], qt[P][MPW][2];
+  float4 gam[MPW];
+  typename std::conditional<DT == 1, float4, uint2>::type dor;   // dO as loaded: row tid / 4,
+                                                                 // columns 4 (tid % 4) .. +3
+  uint64_t vb;                       // the chunk's row-validity bits
+};
+
 template <int DT, int KP, int V>
 __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
+  using Ops = ScanOps<DT, KP>;
   constexpr bool SPLIT = DT == 1;
   constexpr int parts = SPLIT ? 2 : 1;
-  constexpr int RTK = KP / 16, MPW = (RTK + 3) / 4, KS = KP / 32, NT = V / 16;
-  __shared__ __attribute__((aligned(16))) __bf16 s_lam[2][16 * KP];   // [part][column][row]
-  __shared__ __attribute__((aligned(16))) __bf16 s_du[2][16 * kC];
-  __shared__ __attribute__((aligned(16))) __bf16 s_do[2][16 * kC];
+  constexpr int RTK = KP / 16, MPW = Ops::MPW, KS = KP / 32, NT = V / 16;
+  // [part][column][row], columns padded by 8 so the 16 columns a fragment read touches
+  // start in different banks
+  constexpr int LK = KP + 8, LR = kC + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 s_lam[2][16 * LK];
+  __shared__ __attribute__((aligned(16))) __bf16 s_du[2][16 * LR];
+  __shared__ __attribute__((aligned(16))) __bf16 s_do[2][16 * LR];
 
   const int vt = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, vc = 16 * vt + col;
+
+  auto load_ops = [&](int n, Ops& o) __attribute__((always_inline)) {
+    const size_t ch = (size_t)bh * p.NC + n;
+    const uint16_t* kh = p.w.kh + ch * (size_t)(kC * KP * parts);
+    const uint16_t* pt = p.w.pt + ch * (size_t)(2 * kC * kC);
+    const uint16_t* wt = p.w.wt + ch * (size_t)(kC * KP * parts);
+    const uint16_t* qt = p.w.qt + ch * (size_t)(kC * KP * parts);
+#pragma unroll
+    for (int q = 0; q < parts; ++q)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        o.kh[q][ks] = *reinterpret_cast<const bf16x8*>(kh + q * kC * KP + afrag(w, ks, lane, KP));
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) o.pt[q][s] = *reinterpret_cast<const bf16x8*>(pt + q * kC * kC + afrag(w, s, lane, kC));
+#pragma unroll
+    for (int m = 0; m < MPW; ++m) {
+      const int rt = w + 4 * m < RTK ? w + 4 * m : 0;
+#pragma unroll
+      for (int q = 0; q < parts; ++q)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          o.wt[q][m][s] = *reinterpret_cast<const bf16x8*>(wt + q * kC * KP + afrag(rt, s, lane, kC));
+          o.qt[q][m][s] = *reinterpret_cast<const bf16x8*>(qt + q * kC * KP + afrag(rt, s, lane, kC));
+        }
+      o.gam[m] = *reinterpret_cast<const float4*>(p.w.gam + ch * KP + 16 * rt + 4 * g4);
+    }
+    const int row = tid >> 2, c4 = 4 * (tid & 3), t = n * kC + row, ts = t < p.T ? t : p.T - 1;
+    o.dor = *reinterpret_cast<const decltype(o.dor)*>((const Tp*)p.dout + (((size_t)b * p.T + ts) * p.H + h) * V + 16 * vt + c4);
+    o.vb = p.w.vbits[ch];
+  };
 
   float lam[MPW][4];
 #pragma unroll
@@ -422,55 +508,59 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
       lam[m][i] = (rt < RTK && row < p.K && p.dfinal != nullptr) ? p.dfinal[((size_t)bh * p.K + row) * V + vc] : 0.f;
     }
 
-  for (int n = p.NC - 1; n >= 0; --n) {
+  auto step = [&](int n, const Ops& o) __attribute__((always_inline)) {
     const size_t ch = (size_t)bh * p.NC + n;
     float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
 #pragma unroll
     for (int m = 0; m < MPW; ++m) {
       const int rt = w + 4 * m;
-      if (rt >= RTK) continue;
+      if (RTK % 4 != 0 && rt >= RTK) continue;       // (never taken when every wave has rows)
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS1[(16 * rt + 4 * g4 + i) * V + vc] = lam[m][i];
-      split4_to_lds(lam[m], &s_lam[0][col * KP + 16 * rt + 4 * g4], &s_lam[1][col * KP + 16 * rt + 4 * g4]);
+      split4_to_lds(lam[m], &s_lam[0][col * LK + 16 * rt + 4 * g4], &s_lam[1][col * LK + 16 * rt + 4 * g4]);
     }
     {
-      // dO of the chunk's rows (0 where not valid), transposed into [column][row]
-      const int row = tid >> 2, c4 = 4 * (tid & 3), t = n * kC + row;
-      float vals[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < p.T && (p.mask == nullptr || p.mask[(size_t)b * p.T + t] != 0))
-        E::ld4((const Tp*)p.dout, (((size_t)b * p.T + t) * p.H + h) * V + 16 * vt + c4, vals);
+      const int row = tid >> 2, c4 = 4 * (tid & 3);
+      // row valid (in range and unmasked); the empty asm keeps the test here, after the
+      // loads of the next chunk have been issued, instead of right behind its own load
+      uint64_t vb = o.vb;
+      asm volatile("" : "+v"(vb));
+      const bool rv = ((vb >> row) & 1ull) != 0ull;
+      float dov[4];
+      if constexpr (DT == 1) {
+        dov[0] = o.dor.x; dov[1] = o.dor.y; dov[2] = o.dor.z; dov[3] = o.dor.w;
+      } else {
+        dov[0] = __uint_as_float(o.dor.x << 16); dov[1] = __uint_as_float(o.dor.x & 0xffff0000u);
+        dov[2] = __uint_as_float(o.dor.y << 16); dov[3] = __uint_as_float(o.dor.y & 0xffff0000u);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const __bf16 hi = (__bf16)vals[e];
-        s_do[0][(c4 + e) * kC + row] = hi;
-        if (SPLIT) s_do[1][(c4 + e) * kC + row] = (__bf16)(vals[e] - (float)hi);
+        const float x = rv ? dov[e] : 0.f;
+        const __bf16 hi = (__bf16)x;
+        s_do[0][(c4 + e) * LR + row] = hi;
+        if (SPLIT) s_do[1][(c4 + e) * LR + row] = (__bf16)(x - (float)hi);
       }
     }
     __syncthreads();
 
     // ---- dU, row tile w: Kh dS1 + P^T dO
     {
-      const uint16_t* kh = p.w.kh + ch * (size_t)(kC * KP * parts);
-      const uint16_t* pt = p.w.pt + ch * (size_t)(2 * kC * kC);
       f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(kh + afrag(w, ks, lane, KP));
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_lam[0][col * KP + 32 * ks + 8 * g4]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_lam[1][col * KP + 32 * ks + 8 * g4]);
-        a0 = mfma16(ah, bh, a0);
-        a1 = mfma16(ah, bl, a1);
-        if (SPLIT) a2 = mfma16(*reinterpret_cast<const bf16x8*>(kh + kC * KP + afrag(w, ks, lane, KP)), bh, a2);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_lam[0][col * LK + 32 * ks + 8 * g4]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_lam[1][col * LK + 32 * ks + 8 * g4]);
+        a0 = mfma16(o.kh[0][ks], bh, a0);
+        a1 = mfma16(o.kh[0][ks], bl, a1);
+        if (SPLIT) a2 = mfma16(o.kh[parts - 1][ks], bh, a2);
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (32 * s + 31 < 16 * w) continue;          // P^T is upper triangular
-        const bf16x8 ph = *reinterpret_cast<const bf16x8*>(pt + afrag(w, s, lane, kC));
-        const bf16x8 pl = *reinterpret_cast<const bf16x8*>(pt + kC * kC + afrag(w, s, lane, kC));
-        const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][col * kC + 32 * s + 8 * g4]);
-        a0 = mfma16(ph, dh, a0);
-        a1 = mfma16(pl, dh, a1);
-        if (SPLIT) a2 = mfma16(ph, *reinterpret_cast<const bf16x8*>(&s_do[1][col * kC + 32 * s + 8 * g4]), a2);
+        const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][col * LR + 32 * s + 8 * g4]);
+        a0 = mfma16(o.pt[0][s], dh, a0);
+        a1 = mfma16(o.pt[1][s], dh, a1);
+        if (SPLIT) a2 = mfma16(o.pt[0][s], *reinterpret_cast<const bf16x8*>(&s_do[1][col * LR + 32 * s + 8 * g4]), a2);
       }
       float du[4];
 #pragma unroll
@@ -478,46 +568,51 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
       float* dU = p.w.dU + ch * (size_t)(kC * V);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dU[(16 * w + 4 * g4 + i) * V + vc] = du[i];
-      split4_to_lds(du, &s_du[0][col * kC + 16 * w + 4 * g4], &s_du[1][col * kC + 16 * w + 4 * g4]);
+      split4_to_lds(du, &s_du[0][col * LR + 16 * w + 4 * g4], &s_du[1][col * LR + 16 * w + 4 * g4]);
     }
     __syncthreads();
 
     // ---- lam <- Diag(Gam_last) lam + W^T dU + Qt^T dO
-    {
-      const uint16_t* wt = p.w.wt + ch * (size_t)(kC * KP * parts);
-      const uint16_t* qt = p.w.qt + ch * (size_t)(kC * KP * parts);
-      const float* gam = p.w.gam + ch * KP;
 #pragma unroll
-      for (int m = 0; m < MPW; ++m) {
-        const int rt = w + 4 * m;
-        if (rt >= RTK) continue;
-        f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
+    for (int m = 0; m < MPW; ++m) {
+      const int rt = w + 4 * m;
+      if (RTK % 4 != 0 && rt >= RTK) continue;
+      f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const size_t fo = afrag(rt, s, lane, kC);
-          const bf16x8 wh = *reinterpret_cast<const bf16x8*>(wt + fo);
-          const bf16x8 qh = *reinterpret_cast<const bf16x8*>(qt + fo);
-          const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_du[0][col * kC + 32 * s + 8 * g4]);
-          const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_du[1][col * kC + 32 * s + 8 * g4]);
-          const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][col * kC + 32 * s + 8 * g4]);
-          a0 = mfma16(wh, uh, a0);
-          a1 = mfma16(wh, ul, a1);
-          a0 = mfma16(qh, dh, a0);
-          if (SPLIT) {
-            const bf16x8 dl = *reinterpret_cast<const bf16x8*>(&s_do[1][col * kC + 32 * s + 8 * g4]);
-            a2 = mfma16(*reinterpret_cast<const bf16x8*>(wt + kC * KP + fo), uh, a2);
-            a2 = mfma16(*reinterpret_cast<const bf16x8*>(qt + kC * KP + fo), dh, a2);
-            a1 = mfma16(qh, dl, a1);
-          }
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_du[0][col * LR + 32 * s + 8 * g4]);
+        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_du[1][col * LR + 32 * s + 8 * g4]);
+        const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][col * LR + 32 * s + 8 * g4]);
+        a0 = mfma16(o.wt[0][m][s], uh, a0);
+        a1 = mfma16(o.wt[0][m][s], ul, a1);
+        a0 = mfma16(o.qt[0][m][s], dh, a0);
+        if (SPLIT) {
+          const bf16x8 dl = *reinterpret_cast<const bf16x8*>(&s_do[1][col * LR + 32 * s + 8 * g4]);
+          a2 = mfma16(o.wt[parts - 1][m][s], uh, a2);
+          a2 = mfma16(o.qt[parts - 1][m][s], dh, a2);
+          a1 = mfma16(o.qt[0][m][s], dl, a1);
         }
-        const float4 gm = *reinterpret_cast<const float4*>(gam + 16 * rt + 4 * g4);
-        const float gg[4] = {gm.x, gm.y, gm.z, gm.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lam[m][i] = gg[i] * lam[m][i] + (a0[i] + (a1[i] + a2[i]));
       }
+      const float gg[4] = {o.gam[m].x, o.gam[m].y, o.gam[m].z, o.gam[m].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lam[m][i] = gg[i] * lam[m][i] + (a0[i] + (a1[i] + a2[i]));
     }
     __syncthreads();
+  };
+
+  // (loads are never conditional inside the loop, so every wait the compiler places on
+  // them counts exactly the memory operations issued since)
+  Ops A, B;
+  int n = p.NC - 1;
+  if (n >= 0) load_ops(n, A);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (; n >= 1; n -= 2) {
+    load_ops(n - 1, B);
+    step(n, A);
+    load_ops(n >= 2 ? n - 2 : 0, A);
+    step(n - 1, B);
   }
+  if (n == 0) step(0, A);
 #pragma unroll
   for (int m = 0; m < MPW; ++m)
 #pragma unroll
@@ -528,182 +623,212 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
 }
 
 // ================================================================ 4. C x C gradients
+// dv runs in slabs of 32 columns: per slab R = V - Kt S0 (wave w: row tile w, Kt rows as
+// A operands from registers), U = T' R and dR = T'^T dU, while dT' = dU R^T and
+// dP = dO U^T accumulate in registers over the slabs (wave w: row tile w).  Then
+// X = dT' Diag(beta) M^T and dA = -strict_lower(M^T X).  About 78 KB of LDS: two
+// workgroups share a CU.
 template <int DT, int KP, int V>
-__global__ void __launch_bounds__(kThreads) bwd_cc_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  constexpr int KS = KP / 32, LD = KP + 2, LV = V + 2, LC = kC + 2, VT = V / 16, VS = (V + 31) / 32;
-  constexpr int LB = LD > LV ? LD : LV;
-  __shared__ __attribute__((aligned(16))) float s_big[kC * LB];  // Kt (stride LD), then dU (stride LV)
-  __shared__ __attribute__((aligned(16))) float s_R[kC * LV];
-  __shared__ __attribute__((aligned(16))) float s_U[kC * LV];
+  constexpr int KS = KP / 32, LC = kC + 2, LS = 34, VS = (V + 31) / 32;
+  __shared__ __attribute__((aligned(16))) float s_R[kC * LS];    // one 32-column slab of R
+  __shared__ __attribute__((aligned(16))) float s_U[kC * LS];    // ... of U
+  __shared__ __attribute__((aligned(16))) float s_dU[kC * LS];   // ... of dU
   __shared__ __attribute__((aligned(16))) float s_M[kC * LC];
   __shared__ __attribute__((aligned(16))) float s_dT[kC * LC];
   __shared__ __attribute__((aligned(16))) float s_X[kC * LC];
   __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC], s_db[kC];
 
   const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
   const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
   auto tok = [&](int row) -> size_t { return ((size_t)b * p.T + n * kC + row) * p.H + h; };
+  // the same row clamped into the sequence: an in-bounds address for unconditional loads
+  auto tokc = [&](int row) -> size_t {
+    const int t = n * kC + row;
+    return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
+  };
 
   Rows<DT, KP> R;
-  load_rows<DT, KP, false>(p, b, h, n, R, s_tot, s_gl);
+  load_rows<DT, KP, false>(p, b, h, n, 0, R, s_tot, s_gl);
   if (lane < 16) { s_beta[r] = R.beta; s_ok[r] = R.ok ? 1.f : 0.f; }
+  // Kt of this lane's row: the A operand of R = V - Kt S0 for row tile w
+  bf16x8 kth[KS], ktl[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < KS; ++ks) {
+    float kt[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_big[r * LD + 32 * ks + cg + e] = R.k[ks][e] * exp2f(R.g[ks][e]);
-  const float* Mg = p.w.M + ch * (size_t)(kC * kC);
-  for (int idx = tid; idx < kC * kC; idx += kThreads) s_M[(idx / kC) * LC + idx % kC] = Mg[idx];
-  __syncthreads();
-
-  // ---- R = V - Kt S0: wave w takes column tiles w and w + 4, all row tiles
-  const float* S0 = entry_state(p, b, h, n);
+    for (int e = 0; e < 8; ++e) kt[e] = R.k[ks][e] * exp2f(R.g[ks][e]);
+    split8(kt, kth[ks], ktl[ks]);
+  }
+  {
+    const float4* Mg = reinterpret_cast<const float4*>(p.w.M + ch * (size_t)(kC * kC));
+    float4 mv[kC * kC / 4 / kThreads];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int vt = w + 4 * m;
-    if (vt >= VT) continue;
-    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int j = 0; j < kC * kC / 4 / kThreads; ++j) mv[j] = Mg[tid + j * kThreads];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      float bv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 32 * ks + cg + e;
-        bv[e] = (S0 != nullptr && c < p.K) ? S0[(size_t)c * V + 16 * vt + col] : 0.f;
-      }
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        float av[8];
-        lds8(&s_big[(16 * I + col) * LD + 32 * ks + cg], av);
-        acc[I] = mm3(av, bv, acc[I]);
-      }
+    for (int j = 0; j < kC * kC / 4 / kThreads; ++j) {
+      const int idx = 4 * (tid + j * kThreads), row = idx / kC, cl = idx % kC;
+      *reinterpret_cast<float2*>(&s_M[row * LC + cl]) = make_float2(mv[j].x, mv[j].y);
+      *reinterpret_cast<float2*>(&s_M[row * LC + cl + 2]) = make_float2(mv[j].z, mv[j].w);
     }
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * I + 4 * g4 + i;
-        const float vv = s_ok[row] != 0.f ? E::ld((const Tp*)p.v, tok(row) * V + 16 * vt + col) : 0.f;
-        s_R[row * LV + 16 * vt + col] = vv - acc[I][i];
-      }
   }
   __syncthreads();
 
-  // ---- U = T' R (to LDS and the workspace); dU of the chunk into s_big
-  {
-    float* Ug = p.w.U + ch * (size_t)(kC * V);
+  const float* S0 = entry_state(p, b, h, n);
+  const float* dUg = p.w.dU + ch * (size_t)(kC * V);
+  float* Ug = p.w.U + ch * (size_t)(kC * V);
+  const bool rok = s_ok[r] != 0.f;
+  f32x4 dT[4], dPa[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int vt = w + 4 * m;
-      if (vt >= VT) continue;
+  for (int J = 0; J < 4; ++J) { dT[J] = zero4(); dPa[J] = zero4(); }
+
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 acc = zero4();
+  for (int vs = 0; vs < VS; ++vs) {
+    // ---- loads of the slab: S0 columns (B operand of Kt S0), V, dU, dO rows
+    float sv[2][KS][8], vv[2][4], duv[2][4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (s > I / 2) continue;
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int vc = 32 * vs + 16 * t2 + col, vcs = vc < V ? vc : 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * ks + cg + e;
+          sv[t2][ks][e] = S0 != nullptr ? S0[(size_t)(c < p.K ? c : 0) * V + vcs] : 0.f;
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[t2][i] = E::ld((const Tp*)p.v, tokc(16 * w + 4 * g4 + i) * V + vcs);
+    }
+    {
+      // dU rows 2 (tid / 16) .. +1 ... : 64 x 32 values, eight per thread
+      const int row = tid >> 2, c8 = 8 * (tid & 3), vc = 32 * vs + c8;
+      float x[8];
+      gld8(dUg + row * V + (vc < V ? vc : 0), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) duv[e >> 2][e & 3] = vc < V ? x[e] : 0.f;
+    }
+    float dov[8];
+    E::ld8((const Tp*)p.dout, tokc(r) * V + (32 * vs + cg < V ? 32 * vs + cg : 0), dov);
+    // ---- R slab, row tile w
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int vc = 32 * vs + 16 * t2 + col;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sv[t2][ks][e] = (32 * ks + cg + e < p.K) ? sv[t2][ks][e] : 0.f;
+        bf16x8 bh, bl;
+        split8(sv[t2][ks], bh, bl);
+        acc = mma<false>(kth[ks], ktl[ks], bh, bl, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g4 + i;
+        const float vvv = (s_ok[row] != 0.f && vc < V) ? vv[t2][i] : 0.f;
+        s_R[row * LS + 16 * t2 + col] = vc < V ? vvv - acc[i] : 0.f;
+      }
+    }
+    {
+      const int row = tid >> 2, c8 = 8 * (tid & 3);
+      *reinterpret_cast<float2*>(&s_dU[row * LS + c8]) = make_float2(duv[0][0], duv[0][1]);
+      *reinterpret_cast<float2*>(&s_dU[row * LS + c8 + 2]) = make_float2(duv[0][2], duv[0][3]);
+      *reinterpret_cast<float2*>(&s_dU[row * LS + c8 + 4]) = make_float2(duv[1][0], duv[1][1]);
+      *reinterpret_cast<float2*>(&s_dU[row * LS + c8 + 6]) = make_float2(duv[1][2], duv[1][3]);
+    }
+    __syncthreads();
+    // ---- U = T' R and dR = T'^T dU for row tile w of the slab
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int vc = 32 * vs + 16 * t2 + col;
+      f32x4 au = zero4(), ad = zero4();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if (s2 <= w / 2) {                           // T' is lower triangular
           float av[8], bv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int j = 32 * s + cg + e;
-            av[e] = s_M[(16 * I + col) * LC + j] * s_beta[j];
-            bv[e] = s_R[j * LV + 16 * vt + col];
+            const int j = 32 * s2 + cg + e;
+            av[e] = s_M[r * LC + j] * s_beta[j];
+            bv[e] = s_R[j * LS + 16 * t2 + col];
           }
-          acc = mm3(av, bv, acc);
+          au = mm3(av, bv, au);
         }
+        if (32 * s2 + 31 >= 16 * w) {                // T'^T is upper triangular
+          float av[8], bv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * I + 4 * g4 + i;
-          s_U[row * LV + 16 * vt + col] = acc[i];
-          Ug[row * V + 16 * vt + col] = acc[i];
+          for (int e = 0; e < 8; ++e) {
+            const int rr = 32 * s2 + cg + e;
+            av[e] = s_M[rr * LC + r] * s_beta[r];
+            bv[e] = s_dU[rr * LS + 16 * t2 + col];
+          }
+          ad = mm3(av, bv, ad);
         }
-      }
-    }
-    const float* dUg = p.w.dU + ch * (size_t)(kC * V);
-    for (int idx = tid; idx < kC * V; idx += kThreads) s_big[(idx / V) * LV + idx % V] = dUg[idx];
-  }
-  __syncthreads();
-
-  // ---- dV = dR = T'^T dU
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int vt = w + 4 * m;
-    if (vt >= VT) continue;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (32 * s + 31 < 16 * I) continue;          // T'^T is upper triangular
-        float av[8], bv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int rr = 32 * s + cg + e;
-          av[e] = s_M[rr * LC + 16 * I + col] * s_beta[16 * I + col];
-          bv[e] = s_big[rr * LV + 16 * vt + col];
-        }
-        acc = mm3(av, bv, acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * I + 4 * g4 + i;
-        if (n * kC + row < p.T) p.dv[tok(row) * V + 16 * vt + col] = s_ok[row] != 0.f ? acc[i] : 0.f;
-      }
-    }
-  }
-  // ---- dT' = dU R^T (lower) and dP = lower(dO U^T): row tile w
-  {
-    float* dP = p.w.dP + ch * (size_t)(kC * kC);
-    float* dPt = p.w.dPt + ch * (size_t)(kC * kC);
-    float dov[VS][8];
-    const bool rok = s_ok[r] != 0.f;
-#pragma unroll
-    for (int vs = 0; vs < VS; ++vs) {
-      const int v0 = 32 * vs + cg;
-      if (rok && v0 < V) E::ld8((const Tp*)p.dout, tok(r) * V + v0, dov[vs]);
-      else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dov[vs][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      f32x4 at = zero4(), ap = zero4();
-      if (J <= w) {
-#pragma unroll
-        for (int vs = 0; vs < VS; ++vs) {
-          const int v0 = 32 * vs + cg;
-          float du[8], rv[8], uv[8];
-          if (v0 < V) {
-            lds8(&s_big[r * LV + v0], du);
-            lds8(&s_R[(16 * J + col) * LV + v0], rv);
-            lds8(&s_U[(16 * J + col) * LV + v0], uv);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { du[e] = 0.f; rv[e] = 0.f; uv[e] = 0.f; }
-          }
-          at = mm3(du, rv, at);
-          ap = mm3(dov[vs], uv, ap);
+        const int row = 16 * w + 4 * g4 + i;
+        s_U[row * LS + 16 * t2 + col] = au[i];
+        if (vc < V) {
+          Ug[row * V + vc] = au[i];
+          if (n * kC + row < p.T) p.dv[tok(row) * V + vc] = s_ok[row] != 0.f ? ad[i] : 0.f;
         }
       }
-      float pv[4];
+    }
+    __syncthreads();
+    // ---- dT' += dU R^T and dP += dO U^T over the slab's columns: row tile w
+    {
+      float du[8];
+      lds8(&s_dU[r * LS + cg], du);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dov[e] = (rok && 32 * vs + cg < V) ? dov[e] : 0.f;
+      bf16x8 duh, dul, doh, dol;
+      split8(du, duh, dul);
+      split8(dov, doh, dol);
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        if (J > w) continue;
+        float rv[8], uv[8];
+        lds8(&s_R[(16 * J + col) * LS + cg], rv);
+        lds8(&s_U[(16 * J + col) * LS + cg], uv);
+        bf16x8 bh, bl;
+        split8(rv, bh, bl);
+        dT[J] = mma<false>(duh, dul, bh, bl, dT[J]);
+        split8(uv, bh, bl);
+        dPa[J] = mma<DT == 0>(doh, dol, bh, bl, dPa[J]);
+      }
+    }
+    __syncthreads();
+  }
+  // ---- dT' (lower) to LDS, dP (lower) to the workspace
+  {
+    float* dP = p.w.dP + ch * (size_t)(kC * kC);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g4 + i, cl = 16 * J + col;
         const bool lo = J <= w && cl <= row;
-        s_dT[row * LC + cl] = lo ? at[i] : 0.f;
-        pv[i] = lo ? ap[i] : 0.f;
-        dP[row * kC + cl] = pv[i];
+        s_dT[row * LC + cl] = lo ? dT[J][i] : 0.f;
+        dP[row * kC + cl] = lo ? dPa[J][i] : 0.f;
       }
-      *reinterpret_cast<float4*>(&dPt[(16 * J + col) * kC + 16 * w + 4 * g4]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-    }
   }
   __syncthreads();
 
-  // ---- dbeta through T' (column sums of dT' * M) and X = dT' Diag(beta) M^T
+  // ---- dbeta through T' (column sums of dT' * M) and X = dT' Diag(beta) M^T; G of this
+  //      wave's rows is loaded now for the dA step
+  float gpre[4][4];
+  {
+    const float* Gg = p.w.G + ch * (size_t)(kC * kC);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gpre[J][i] = Gg[(16 * w + 4 * g4 + i) * kC + 16 * J + col];
+  }
   float db = 0.f;
   if (tid < kC)
     for (int rr = tid; rr < kC; ++rr) db += s_dT[rr * LC + tid] * s_M[rr * LC + tid];
@@ -711,12 +836,12 @@ __global__ void __launch_bounds__(kThreads) bwd_cc_kernel(Params p) {
   for (int J = 0; J < 4; ++J) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      if (s > w / 2 || s > J / 2) continue;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      if (s2 > w / 2 || s2 > J / 2) continue;
       float av[8], bv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int kk = 32 * s + cg + e;
+        const int kk = 32 * s2 + cg + e;
         av[e] = s_dT[r * LC + kk] * s_beta[kk];
         bv[e] = s_M[(16 * J + col) * LC + kk];
       }
@@ -729,37 +854,32 @@ __global__ void __launch_bounds__(kThreads) bwd_cc_kernel(Params p) {
 
   // ---- dA = -strict_lower(M^T X); dG = Diag(beta) dA; dbeta through A (row sums of dA * G)
   {
-    const float* Gg = p.w.G + ch * (size_t)(kC * kC);
     float* dG = p.w.dG + ch * (size_t)(kC * kC);
-    float* dGt = p.w.dGt + ch * (size_t)(kC * kC);
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       f32x4 acc = zero4();
       if (J <= w) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (32 * s + 31 < 16 * w) continue;        // M^T is upper triangular
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (32 * s2 + 31 < 16 * w) continue;       // M^T is upper triangular
           float av[8], bv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int rr = 32 * s + cg + e;
+            const int rr = 32 * s2 + cg + e;
             av[e] = s_M[rr * LC + r];
             bv[e] = s_X[rr * LC + 16 * J + col];
           }
           acc = mm3(av, bv, acc);
         }
       }
-      float gv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * w + 4 * g4 + i, cl = 16 * J + col;
         const float da = (J <= w && cl < row) ? -acc[i] : 0.f;
-        part[i] += da * Gg[row * kC + cl];
-        gv[i] = s_beta[row] * da;
-        dG[row * kC + cl] = gv[i];
+        part[i] += da * gpre[J][i];
+        dG[row * kC + cl] = s_beta[row] * da;
       }
-      *reinterpret_cast<float4*>(&dGt[(16 * J + col) * kC + 16 * w + 4 * g4]) = make_float4(gv[0], gv[1], gv[2], gv[3]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -771,236 +891,347 @@ __global__ void __launch_bounds__(kThreads) bwd_cc_kernel(Params p) {
   if (tid < kC && n * kC + tid < p.T) p.dbeta[tok(tid)] = s_ok[tid] != 0.f ? db + s_db[tid] : 0.f;
 }
 
-// ================================================================ 5. q, k and decay gradients
-// Wave w takes channel tiles w and w + 4 with all four row tiles, so each lane holds 16 rows
-// of one channel and the reverse sum over rows for dlog_alpha stays in registers and lane
-// shuffles.
+// ================================================================ 5. products over dv
+// Y1 = dO S0^T, Y2 = dR S0^T and Z = U dS1^T (C x KP each, contraction over dv) and
+// rowsum(dS1 * S0), with dv in 32-column slabs staged through LDS as split bf16 pairs:
+// wave w forms row tile w of all three products for every key-channel tile.  The products
+// are stored in fragment order (tile (I, ct): 64 lanes x 4 values) for bwd_ck_kernel.
 template <int DT, int KP, int V>
-__global__ void __launch_bounds__(kThreads) bwd_ck_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads, 2) bwd_cy_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  constexpr int KS = KP / 32, CT = KP / 16, LD = KP + 2, VS = (V + 31) / 32;
+  constexpr int CT = KP / 16, VS = (V + 31) / 32, LA = 40;   // slab rows padded to 40 bf16
+  constexpr int NB = (KP * 4 + kThreads - 1) / kThreads;      // B-slab items per thread
+  __shared__ __attribute__((aligned(16))) __bf16 s_a[3][2][kC * LA];   // dO, dR, U (high, residual)
+  __shared__ __attribute__((aligned(16))) __bf16 s_b[2][2][KP * LA];   // S0, dS1 rows (high, residual)
+
+  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g4 = lane >> 4;
+  const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
+  auto tokc = [&](int row) -> size_t {
+    const int t = n * kC + row;
+    return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
+  };
+  const uint64_t vb = p.w.vbits[ch];
+  const float* S0 = entry_state(p, b, h, n);
+  const float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
+  const float* Ug = p.w.U + ch * (size_t)(kC * V);
+
+  f32x4 acc[3][CT];
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[m][ct] = zero4();
+  float ssp[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) ssp[j] = 0.f;
+
+  for (int vs = 0; vs < VS; ++vs) {
+    // ---- the slab into LDS: A rows (one 8-column piece per thread), B rows (NB pieces)
+    {
+      const int row = tid >> 2, c8 = 8 * (tid & 3), v = 32 * vs + c8;
+      const bool vin = v < V, rok = vin && ((vb >> row) & 1ull) != 0ull;
+      const int vsafe = vin ? v : 0;
+      float a[3][8];
+      E::ld8((const Tp*)p.dout, tokc(row) * V + vsafe, a[0]);
+      gld8(p.dv + tokc(row) * V + vsafe, a[1]);
+      gld8(Ug + row * V + vsafe, a[2]);
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[m][e] = (m == 2 ? vin : rok) ? a[m][e] : 0.f;
+        bf16x8 hi, lo;
+        split8(a[m], hi, lo);
+        *reinterpret_cast<bf16x8*>(&s_a[m][0][row * LA + c8]) = hi;
+        *reinterpret_cast<bf16x8*>(&s_a[m][1][row * LA + c8]) = lo;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int idx = tid + j * kThreads;
+      if (idx >= KP * 4) continue;
+      const int row = idx >> 2, c8 = 8 * (idx & 3), v = 32 * vs + c8;
+      const bool vin = v < V, sin = vin && S0 != nullptr && row < p.K;
+      float sv[8], dv[8];
+      gld8(S0 != nullptr ? S0 + (size_t)(row < p.K ? row : 0) * V + (vin ? v : 0) : dS1, sv);
+      gld8(dS1 + (size_t)row * V + (vin ? v : 0), dv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sv[e] = sin ? sv[e] : 0.f;
+        dv[e] = vin ? dv[e] : 0.f;
+        ssp[j] += sv[e] * dv[e];
+      }
+      bf16x8 hi, lo;
+      split8(sv, hi, lo);
+      *reinterpret_cast<bf16x8*>(&s_b[0][0][row * LA + c8]) = hi;
+      *reinterpret_cast<bf16x8*>(&s_b[0][1][row * LA + c8]) = lo;
+      split8(dv, hi, lo);
+      *reinterpret_cast<bf16x8*>(&s_b[1][0][row * LA + c8]) = hi;
+      *reinterpret_cast<bf16x8*>(&s_b[1][1][row * LA + c8]) = lo;
+    }
+    __syncthreads();
+    // ---- row tile w of the three products over the slab
+    bf16x8 ah[3], al[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      ah[m] = *reinterpret_cast<const bf16x8*>(&s_a[m][0][(16 * w + col) * LA + 8 * g4]);
+      al[m] = *reinterpret_cast<const bf16x8*>(&s_a[m][1][(16 * w + col) * LA + 8 * g4]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int br = (16 * ct + col) * LA + 8 * g4;
+      const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&s_b[0][0][br]);
+      const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&s_b[0][1][br]);
+      const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_b[1][0][br]);
+      const bf16x8 dl = *reinterpret_cast<const bf16x8*>(&s_b[1][1][br]);
+      acc[0][ct] = mma<DT == 0>(ah[0], al[0], sh, sl, acc[0][ct]);
+      acc[1][ct] = mma<false>(ah[1], al[1], sh, sl, acc[1][ct]);
+      acc[2][ct] = mma<false>(ah[2], al[2], dh, dl, acc[2][ct]);
+    }
+    __syncthreads();
+  }
+  float* Y = p.w.Y + ch * (size_t)(3 * kC * KP);
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      *reinterpret_cast<float4*>(Y + (size_t)m * kC * KP + ((w * CT + ct) * 64 + lane) * 4) =
+          make_float4(acc[m][ct][0], acc[m][ct][1], acc[m][ct][2], acc[m][ct][3]);
+  // rowsum(dS1 * S0): the four threads of a row are neighbouring lanes
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float x = ssp[j];
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    const int idx = tid + j * kThreads;
+    if (idx < KP * 4 && (idx & 3) == 0) p.w.ss[ch * KP + (idx >> 2)] = x;
+  }
+}
+
+// ================================================================ 6. q, k and decay gradients
+// Every term here is separable by key channel, so a workgroup takes a slice of 32 channels
+// and wave w channel tile w%2 of it over rows 32 (w/2) .. +31 (two row tiles): each lane
+// holds the rows of one channel, and the reverse sum over rows for dlog_alpha is lane
+// shuffles plus one exchange between the two halves.  dP and dG are staged in LDS (their
+// transposes are read from there by column).  About 70 KB of LDS.
+constexpr int kCkSlice = 32;
+
+template <int DT, int KP, int V>
+__global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
+  using E = Elem<DT>;
+  using Tp = typename E::T;
+  constexpr int SW = kCkSlice, LD = SW + 2, LC = kC + 2, CT = KP / 16;
   __shared__ __attribute__((aligned(16))) float s_a[kC * LD];    // Kt, or k on the exact path
   __shared__ __attribute__((aligned(16))) float s_b[kC * LD];    // Ki (fast path)
   __shared__ __attribute__((aligned(16))) float s_c[kC * LD];    // Qt, or q on the exact path
   __shared__ __attribute__((aligned(16))) float s_g[kC * LD];    // g (log2)
-  __shared__ float s_tot[4 * KP], s_gl[KP], s_ok[kC];
+  __shared__ __attribute__((aligned(16))) float s_dP[kC * LC];
+  __shared__ __attribute__((aligned(16))) float s_dG[kC * LC];
+  __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW];
 
-  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y, c_base = SW * blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
   const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
   auto tok = [&](int row) -> size_t { return ((size_t)b * p.T + n * kC + row) * p.H + h; };
+  auto tokc = [&](int row) -> size_t {
+    const int t = n * kC + row;
+    return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
+  };
 
-  Rows<DT, KP> R;
-  load_rows<DT, KP, true>(p, b, h, n, R, s_tot, s_gl);
-  if (lane < 16) s_ok[r] = R.ok ? 1.f : 0.f;
-  const bool fast = __syncthreads_and(tid >= KP || s_gl[tid] >= kFastLimit);
+  {
+    // dP and dG into LDS (4096 values each, 16 per thread)
+    const float4* dPg = reinterpret_cast<const float4*>(p.w.dP + ch * (size_t)(kC * kC));
+    const float4* dGg = reinterpret_cast<const float4*>(p.w.dG + ch * (size_t)(kC * kC));
+    float4 pv[4], gv[4];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+    for (int j = 0; j < 4; ++j) { pv[j] = dPg[tid + j * kThreads]; gv[j] = dGg[tid + j * kThreads]; }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int at = r * LD + 32 * ks + cg + e;
-      const float gv = R.g[ks][e];
-      s_g[at] = gv;
-      if (fast) {
-        const float gam = exp2f(gv);
-        s_a[at] = R.k[ks][e] * gam;
-        s_b[at] = R.k[ks][e] * exp2f(-gv);
-        s_c[at] = R.q[ks][e] * gam;
-      } else {
-        s_a[at] = R.k[ks][e];
-        s_b[at] = 0.f;
-        s_c[at] = R.q[ks][e];
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int idx = 4 * (tid + j * kThreads), row = idx / kC, cl = idx % kC;
+      *reinterpret_cast<float2*>(&s_dP[row * LC + cl]) = make_float2(pv[j].x, pv[j].y);
+      *reinterpret_cast<float2*>(&s_dP[row * LC + cl + 2]) = make_float2(pv[j].z, pv[j].w);
+      *reinterpret_cast<float2*>(&s_dG[row * LC + cl]) = make_float2(gv[j].x, gv[j].y);
+      *reinterpret_cast<float2*>(&s_dG[row * LC + cl + 2]) = make_float2(gv[j].z, gv[j].w);
     }
+  }
+  Rows<DT, SW> R;
+  load_rows<DT, SW, true>(p, b, h, n, c_base, R, s_tot, s_gl);
+  if (lane < 16) s_ok[r] = R.ok ? 1.f : 0.f;
+  const bool fast = __syncthreads_and(tid >= SW || s_gl[tid] >= kFastLimit);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int at = r * LD + cg + e;
+    const float gv = R.g[0][e];
+    s_g[at] = gv;
+    if (fast) {
+      const float gam = exp2f(gv);
+      s_a[at] = R.k[0][e] * gam;
+      s_b[at] = R.k[0][e] * exp2f(-gv);
+      s_c[at] = R.q[0][e] * gam;
+    } else {
+      s_a[at] = R.k[0][e];
+      s_b[at] = 0.f;
+      s_c[at] = R.q[0][e];
+    }
+  }
   __syncthreads();
 
-  const float* S0 = entry_state(p, b, h, n);
-  const float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
-  const float* Ug = p.w.U + ch * (size_t)(kC * V);
-  const float* dP = p.w.dP + ch * (size_t)(kC * kC);
-  const float* dPt = p.w.dPt + ch * (size_t)(kC * kC);
-  const float* dG = p.w.dG + ch * (size_t)(kC * kC);
-  const float* dGt = p.w.dGt + ch * (size_t)(kC * kC);
+  const int hw = w >> 1, lc = 16 * (w & 1) + col, c = c_base + lc;   // row half; channel
+  const int ct = (c_base >> 4) + (w & 1);                              // channel tile
+  const bool cin = c < p.K;
+  const float* Y = p.w.Y + ch * (size_t)(3 * kC * KP);
+  const float ss = p.w.ss[ch * KP + c];
 
-  for (int m = 0; m < 2; ++m) {
-    const int ct = w + 4 * m;
-    if (ct >= CT) continue;
-    const int c = 16 * ct + col;                     // this lane's channel
-    // ---- Y1 = dO S0^T, Y2 = dR S0^T, Z = U dS1^T (contraction over dv), rowsum(dS1 * S0)
-    f32x4 y1[4], y2[4], z[4];
+  const float gl = s_gl[lc];
+  float dl[2][4];
+  float zk = 0.f;
 #pragma unroll
-    for (int I = 0; I < 4; ++I) { y1[I] = zero4(); y2[I] = zero4(); z[I] = zero4(); }
-    float ss = 0.f;
+  for (int ii = 0; ii < 2; ++ii) {
+    const int I = 2 * hw + ii;
+    // ---- the products over dv for tile (I, ct), and the raw k, q of the lane's rows
+    const size_t yo = ((size_t)(I * CT + ct) * 64 + lane) * 4;
+    const float4 y1v = *reinterpret_cast<const float4*>(Y + yo);
+    const float4 y2v = *reinterpret_cast<const float4*>(Y + (size_t)kC * KP + yo);
+    const float4 zv = *reinterpret_cast<const float4*>(Y + (size_t)2 * kC * KP + yo);
+    const float y1[4] = {y1v.x, y1v.y, y1v.z, y1v.w}, y2[4] = {y2v.x, y2v.y, y2v.z, y2v.w};
+    const float z[4] = {zv.x, zv.y, zv.z, zv.w};
+    float kr[4], qr[4];
 #pragma unroll
-    for (int vs = 0; vs < VS; ++vs) {
-      const int v0 = 32 * vs + cg;
-      float sb[8], db[8];
-      if (v0 < V) {
-        if (S0 != nullptr && c < p.K) gld8(S0 + (size_t)c * V + v0, sb);
-        else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sb[e] = 0.f;
-        }
-        gld8(dS1 + (size_t)c * V + v0, db);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { sb[e] = 0.f; db[e] = 0.f; }
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += sb[e] * db[e];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const int row = 16 * I + col;
-        float a1[8], a2[8], a3[8];
-        if (s_ok[row] != 0.f && v0 < V) {
-          E::ld8((const Tp*)p.dout, tok(row) * V + v0, a1);
-          gld8(p.dv + tok(row) * V + v0, a2);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { a1[e] = 0.f; a2[e] = 0.f; }
-        }
-        if (v0 < V) gld8(Ug + row * V + v0, a3);
-        else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a3[e] = 0.f;
-        }
-        y1[I] = mm3(a1, sb, y1[I]);
-        y2[I] = mm3(a2, sb, y2[I]);
-        z[I] = mm3(a3, db, z[I]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const size_t kat = tokc(16 * I + 4 * g4 + i) * p.K + (cin ? c : 0);
+      kr[i] = E::ld((const Tp*)p.k, kat);
+      qr[i] = E::ld((const Tp*)p.q, kat);
     }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-
-    // ---- the decay-weighted C x C terms, as Gam_i (dP Ki)_i, Gam_i (dG Ki)_i, (dP^T Qt)_j / Gam_j
-    //      and (dG^T Kt)_j / Gam_j
-    f32x4 xq[4], xk1[4], xk2[4], xk3[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) { xq[I] = zero4(); xk1[I] = zero4(); xk2[I] = zero4(); xk3[I] = zero4(); }
+    // ---- the decay-weighted C x C terms: Gam_i (dP Ki)_i, Gam_i (dG Ki)_i, (dP^T Qt)_j / Gam_j,
+    //      (dG^T Kt)_j / Gam_j
+    f32x4 xq = zero4(), xk1 = zero4(), xk2 = zero4(), xk3 = zero4();
     if (fast) {
+      const int ra = 16 * I + col;                   // A-operand row
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int k0 = 32 * s2 + cg;
+        if (s2 <= I / 2) {                           // columns j <= i
+          float ap[8], ag[8], bv[8];
+          lds8(&s_dP[ra * LC + k0], ap);
+          lds8(&s_dG[ra * LC + k0], ag);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int k0 = 32 * s + cg;
-          float bv[8];
-          if (s <= I / 2) {                          // columns j <= i
-            float ap[8], ag[8];
-            gld8(dP + (16 * I + col) * kC + k0, ap);
-            gld8(dG + (16 * I + col) * kC + k0, ag);
+          for (int e = 0; e < 8; ++e) bv[e] = s_b[(k0 + e) * LD + lc];
+          bf16x8 bh, bl, hh, ll;
+          split8(bv, bh, bl);
+          split8(ap, hh, ll);
+          xq = mma<false>(hh, ll, bh, bl, xq);
+          split8(ag, hh, ll);
+          xk3 = mma<false>(hh, ll, bh, bl, xk3);
+        }
+        if (32 * s2 + 31 >= 16 * I) {                // rows i >= j
+          float ap[8], ag[8], bq[8], bk[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bv[e] = s_b[(k0 + e) * LD + c];
-            xq[I] = mm3(ap, bv, xq[I]);
-            xk3[I] = mm3(ag, bv, xk3[I]);
+          for (int e = 0; e < 8; ++e) {
+            ap[e] = s_dP[(k0 + e) * LC + ra];
+            ag[e] = s_dG[(k0 + e) * LC + ra];
+            bq[e] = s_c[(k0 + e) * LD + lc];
+            bk[e] = s_a[(k0 + e) * LD + lc];
           }
-          if (32 * s + 31 >= 16 * I) {               // rows i >= j
-            float ap[8], ag[8], bq[8];
-            gld8(dPt + (16 * I + col) * kC + k0, ap);
-            gld8(dGt + (16 * I + col) * kC + k0, ag);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              bq[e] = s_c[(k0 + e) * LD + c];
-              bv[e] = s_a[(k0 + e) * LD + c];
-            }
-            xk1[I] = mm3(ap, bq, xk1[I]);
-            xk2[I] = mm3(ag, bv, xk2[I]);
-          }
+          bf16x8 bh, bl, hh, ll;
+          split8(bq, bh, bl);
+          split8(ap, hh, ll);
+          xk1 = mma<false>(hh, ll, bh, bl, xk1);
+          split8(bk, bh, bl);
+          split8(ag, hh, ll);
+          xk2 = mma<false>(hh, ll, bh, bl, xk2);
         }
       }
     }
-
     // ---- per element: dq, dk and the per-row decay gradient
-    const float gl = s_gl[c];
-    float dl[4][4];
-    float zk = 0.f;
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * I + 4 * g4 + i;
-        const float gv = s_g[row * LD + c];
-        const bool ok = s_ok[row] != 0.f && c < p.K;
-        float kr = 0.f, qr = 0.f;
-        if (ok) {
-          kr = E::ld((const Tp*)p.k, tok(row) * p.K + c);
-          qr = E::ld((const Tp*)p.q, tok(row) * p.K + c);
-        }
-        float Xq, Xk1, Xk2, Xk3;
-        if (fast) {
-          const float gm = exp2f(gv), gi = exp2f(-gv);
-          Xq = gm * xq[I][i];
-          Xk3 = gm * xk3[I][i];
-          Xk1 = gi * xk1[I][i];
-          Xk2 = gi * xk2[I][i];
-        } else {
-          Xq = 0.f; Xk1 = 0.f; Xk2 = 0.f; Xk3 = 0.f;
-          for (int j = 0; j < kC; ++j) {
-            const float gj = s_g[j * LD + c];
-            if (j <= row) {
-              const float wgt = s_a[j * LD + c] * exp2f(gv - gj);
-              Xq += dP[row * kC + j] * wgt;
-              Xk3 += dG[row * kC + j] * wgt;
-            }
-            if (j >= row) {
-              const float d = exp2f(gj - gv);
-              Xk1 += dPt[row * kC + j] * s_c[j * LD + c] * d;
-              Xk2 += dGt[row * kC + j] * s_a[j * LD + c] * d;
-            }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * I + 4 * g4 + i;
+      const float gv = s_g[row * LD + lc];
+      const bool ok = s_ok[row] != 0.f && cin;
+      const float kv = ok ? kr[i] : 0.f, qv = ok ? qr[i] : 0.f;
+      float Xq, Xk1, Xk2, Xk3;
+      if (fast) {
+        const float gm = exp2f(gv), gi = exp2f(-gv);
+        Xq = gm * xq[i];
+        Xk3 = gm * xk3[i];
+        Xk1 = gi * xk1[i];
+        Xk2 = gi * xk2[i];
+      } else {
+        Xq = 0.f; Xk1 = 0.f; Xk2 = 0.f; Xk3 = 0.f;
+        for (int j = 0; j < kC; ++j) {
+          const float gj = s_g[j * LD + lc];
+          if (j <= row) {
+            const float wgt = s_a[j * LD + lc] * exp2f(gv - gj);
+            Xq += s_dP[row * LC + j] * wgt;
+            Xk3 += s_dG[row * LC + j] * wgt;
+          }
+          if (j >= row) {
+            const float d = exp2f(gj - gv);
+            Xk1 += s_dP[j * LC + row] * s_c[j * LD + lc] * d;
+            Xk2 += s_dG[j * LC + row] * s_a[j * LD + lc] * d;
           }
         }
-        const float gm = exp2f(gv), ekh = exp2f(gl - gv);
-        const float a = Xk3 - gm * y2[I][i];           // Gam dKt
-        const float bb = Xk1 + Xk2;                    // dKi / Gam
-        const float dqv = gm * y1[I][i] + Xq;
-        const float dkv = a + bb + z[I][i] * ekh;
-        const float khv = kr * ekh;
-        dl[I][i] = ok ? kr * a - kr * bb + qr * dqv - z[I][i] * khv : 0.f;
-        zk += ok ? z[I][i] * khv : 0.f;
-        if (n * kC + row < p.T && c < p.K) {
-          p.dq[tok(row) * p.K + c] = ok ? dqv : 0.f;
-          p.dk[tok(row) * p.K + c] = ok ? dkv : 0.f;
-        }
       }
-    // ---- dlog_alpha: reverse sums over the rows, plus the Gam_last term
-    zk += __shfl_xor(zk, 16, 64);
-    zk += __shfl_xor(zk, 32, 64);
-    const float dlast = zk + exp2f(gl) * ss;
-    float tile[4], after[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) tile[I] = (dl[I][0] + dl[I][1]) + (dl[I][2] + dl[I][3]);
-    // sums of the lanes holding later rows of the same tile (same column, larger l/16)
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      float later = 0.f, total = 0.f;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float x = __shfl(tile[I], col + 16 * q4, 64);
-        total += x;
-        later += q4 > g4 ? x : 0.f;
+      const float gm = exp2f(gv), ekh = exp2f(gl - gv);
+      const float a = Xk3 - gm * y2[i];              // Gam dKt
+      const float bb = Xk1 + Xk2;                    // dKi / Gam
+      const float dqv = gm * y1[i] + Xq;
+      const float dkv = a + bb + z[i] * ekh;
+      const float khv = kv * ekh;
+      dl[ii][i] = ok ? kv * a - kv * bb + qv * dqv - z[i] * khv : 0.f;
+      zk += ok ? z[i] * khv : 0.f;
+      if (n * kC + row < p.T && cin) {
+        p.dq[tok(row) * p.K + c] = ok ? dqv : 0.f;
+        p.dk[tok(row) * p.K + c] = ok ? dkv : 0.f;
       }
-      after[I] = later;
-      tile[I] = total;
     }
-    float carry = dlast;
+  }
+  // ---- dlog_alpha: reverse sums over the rows, plus the Gam_last term; the two row halves
+  //      of a channel exchange their totals through LDS
+  zk += __shfl_xor(zk, 16, 64);
+  zk += __shfl_xor(zk, 32, 64);
+  float tile[2], after[2];
 #pragma unroll
-    for (int I = 3; I >= 0; --I) {
-      float run = carry + after[I];
+  for (int ii = 0; ii < 2; ++ii) tile[ii] = (dl[ii][0] + dl[ii][1]) + (dl[ii][2] + dl[ii][3]);
+  // sums of the lanes holding later rows of the same tile (same column, larger l/16)
 #pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        const int row = 16 * I + 4 * g4 + i;
-        run += dl[I][i];
-        if (n * kC + row < p.T && c < p.K) p.dla[tok(row) * p.K + c] = s_ok[row] != 0.f ? run : 0.f;
-      }
-      carry += tile[I];
+  for (int ii = 0; ii < 2; ++ii) {
+    float later = 0.f, total = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float x = __shfl(tile[ii], col + 16 * q4, 64);
+      total += x;
+      later += q4 > g4 ? x : 0.f;
     }
+    after[ii] = later;
+    tile[ii] = total;
+  }
+  if (g4 == 0) {
+    s_half[hw][0][lc] = tile[0] + tile[1];
+    s_half[hw][1][lc] = zk;
+  }
+  __syncthreads();
+  const float dlast = s_half[0][1][lc] + s_half[1][1][lc] + exp2f(gl) * (cin ? ss : 0.f);
+  float carry = dlast + (hw == 0 ? s_half[1][0][lc] : 0.f);
+#pragma unroll
+  for (int ii = 1; ii >= 0; --ii) {
+    const int I = 2 * hw + ii;
+    float run = carry + after[ii];
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      const int row = 16 * I + 4 * g4 + i;
+      run += dl[ii][i];
+      if (n * kC + row < p.T && cin) p.dla[tok(row) * p.K + c] = s_ok[row] != 0.f ? run : 0.f;
+    }
+    carry += tile[ii];
   }
 }
 
 // ---------------------------------------------------------------- host side
 struct Layout {
-  size_t fwd, o, fin, ck, kh, wt, qt, pt, gam, G, M, dS1, dU, U, dP, dPt, dG, dGt, total;
+  size_t fwd, o, fin, ck, kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, Y, ss, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1021,15 +1252,16 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype) {
   L.qt = take(nch * kC * KP * 2 * parts);
   L.pt = take(nch * kC * kC * 2 * 2);
   L.gam = take(nch * KP * 4);
+  L.vbits = take(nch * 8);
   L.G = take(nch * kC * kC * 4);
   L.M = take(nch * kC * kC * 4);
   L.dS1 = take(nch * KP * dv * 4);
   L.dU = take(nch * kC * dv * 4);
   L.U = take(nch * kC * dv * 4);
   L.dP = take(nch * kC * kC * 4);
-  L.dPt = take(nch * kC * kC * 4);
   L.dG = take(nch * kC * kC * 4);
-  L.dGt = take(nch * kC * kC * 4);
+  L.Y = take(nch * 3 * kC * KP * 4);
+  L.ss = take(nch * KP * 4);
   L.total = off;
   return L;
 }
@@ -1048,7 +1280,10 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_cc_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_ck_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((bwd_cy_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_ck_kernel<DT, KP, V>), dim3(p.NC * p.H, p.B, KP / kCkSlice), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1099,9 +1334,10 @@ hipError_t launch_backward(const BackwardArgs& a) {
     p.w.kh = (uint16_t*)(ws + L.kh); p.w.wt = (uint16_t*)(ws + L.wt); p.w.qt = (uint16_t*)(ws + L.qt);
     p.w.pt = (uint16_t*)(ws + L.pt);
     p.w.gam = (float*)(ws + L.gam); p.w.G = (float*)(ws + L.G); p.w.M = (float*)(ws + L.M);
+    p.w.vbits = (uint64_t*)(ws + L.vbits);
     p.w.dS1 = (float*)(ws + L.dS1); p.w.dU = (float*)(ws + L.dU); p.w.U = (float*)(ws + L.U);
-    p.w.dP = (float*)(ws + L.dP); p.w.dPt = (float*)(ws + L.dPt);
-    p.w.dG = (float*)(ws + L.dG); p.w.dGt = (float*)(ws + L.dGt);
+    p.w.dP = (float*)(ws + L.dP); p.w.dG = (float*)(ws + L.dG);
+    p.w.Y = (float*)(ws + L.Y); p.w.ss = (float*)(ws + L.ss);
     p.w.ck = (const float*)(ws + L.ck);
   }
   p.B = a.B; p.T = a.T; p.H = a.H; p.K = a.dk_; p.V = a.dv_; p.NC = NC; p.NCf = NCf;
