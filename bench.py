@@ -9,6 +9,8 @@ One step = one pass of the whole path on synthetic, seeded inputs resident in HB
     in-kernel L2 normalisation of q and k.
 `value` is prefill tokens/s; the decode state-update GB/s is reported beside it, and so is the
 same 128k tokens prefilled as 32 packed prompts of seeded lengths (kda_chunk_prefill_varlen).
+The training backward (kda_chunk_prefill_backward) is timed on the chunked-prefill training
+shape (B=4, H=32, T=4096) with the forward on the same inputs beside it.
 Prints one JSON line.
 """
 import argparse
@@ -24,6 +26,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_BYTES_PER_TH = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (512) + beta (4)
 DECODE_BYTES_PER_SH = 132612         # state read+write 8*K*V + q,k,v,o (1024) + log_alpha (512) + beta
+# backward per token-head: q, k, v, dO bf16 (4 x 256) + log_alpha (512) + beta (4) read;
+# dq, dk, dv, dlog_alpha fp32 (4 x 512) + dbeta (4) written
+BACKWARD_BYTES_PER_TH = 1024 + 512 + 4 + 2048 + 4
 
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on the default workload,
@@ -83,6 +88,8 @@ def parse():
     ap.add_argument("--cpu-repeats", type=int, default=16,
                     help="times the segment is chained through the oracle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-B", type=int, default=4, help="batch of the backward timing (0: skip)")
+    ap.add_argument("--bwd-T", type=int, default=4096, help="tokens per sequence of the backward timing")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a known-size kernel "
                          "that scales the FETCH_SIZE/WRITE_SIZE counters of a profiling run)")
@@ -110,6 +117,25 @@ def cpu_baseline(args):
             "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"fp64 token loop, B=1 H=32 dk=dv=128: a {seg}-token segment chained "
                       f"{reps}x ({seg * reps} tokens), {dt:.1f} s wall"}
+
+
+def cpu_backward_baseline(T=4096, heads=8):
+    """The oracle's fp64 gradient (np_prefill_backward, a NumPy token loop on one core) on a
+    bounded sample of the backward workload: `heads` heads of one T-token sequence, each run
+    on its own (the oracle keeps every state of the sequence)."""
+    import numpy as np
+    from linear_attention_recurrence_kda_amd import datagen as D
+    from oracle import oracle as O
+    inp = D.np_kda_inputs(1, T, heads, 128, 128, "bf16", seed=0)
+    do = np.random.default_rng(1).normal(0, 1, (1, T, heads, 128))
+    t0 = time.perf_counter()
+    for hh in range(heads):
+        one = {n: np.ascontiguousarray(x[:, :, hh:hh + 1]) for n, x in inp.items()}
+        O.np_prefill_backward(one["q"], one["k"], one["v"], one["log_alpha"], one["beta"], do[:, :, hh:hh + 1])
+    dt = time.perf_counter() - t0
+    return {"value": T * heads / 32 / dt, "unit": "tokens/s (32 heads)", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 reverse token loop (NumPy), B=1 T={T}, {heads} heads of dk=dv=128 one at a "
+                      f"time, {dt:.1f} s wall; token-heads/s divided by 32"}
 
 
 def host_cpu_model():
@@ -282,6 +308,58 @@ def main():
                      "algorithmic_GBps": long_gbs, "hbm_frac": long_gbs / HBM_PEAK_GBS}
         del xl, ol, wsl
 
+    # the training backward on the chunked-prefill training shape: dq, dk, dv, dlog_alpha, dbeta
+    # and dinit for L = <dO, o> + <dS_T, S_T>, beside the forward on the same inputs
+    bwd_line = None
+    if args.bwd_B > 0:
+        Bb, Tb = args.bwd_B, args.bwd_T
+        xb = D.torch_kda_inputs(Bb, Tb, H, dk, dv, dev, "bf16", seed=4)
+        gb = torch.Generator(device=dev)
+        gb.manual_seed(5)
+        dob = torch.randn(Bb, Tb, H, dv, device=dev, generator=gb).to(torch.bfloat16)
+        dfb = torch.randn(Bb, H, dk, dv, device=dev, generator=gb)
+        wsb = torch.empty(kda.backward_workspace_size(Bb, Tb, H, dk, dv, kda.KDA_BF16), dtype=torch.uint8,
+                          device=dev)
+        bargs = (xb["q"], xb["k"], xb["v"], xb["log_alpha"], xb["beta"], dob)
+
+        def backward():
+            return kda.chunk_prefill_backward(*bargs, d_final_state=dfb, workspace=wsb)
+        ob = torch.empty(Bb, Tb, H, dv, dtype=torch.bfloat16, device=dev)
+        fsb = torch.empty(Bb, H, dk, dv, dtype=torch.float32, device=dev)
+        wfb = torch.empty(kda.prefill_workspace_size(Bb, Tb, H, dk, dv, C, kda.KDA_BF16), dtype=torch.uint8,
+                          device=dev)
+
+        def forward():
+            kda.chunk_prefill(xb["q"], xb["k"], xb["v"], xb["log_alpha"], xb["beta"], chunk_size=C, out=ob,
+                              final_state=fsb, workspace=wfb)
+        backward()
+        forward()
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a_, b_ in bev:
+            a_.record()
+            backward()
+            b_.record()
+        fev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a_, b_ in fev2:
+            a_.record()
+            forward()
+            b_.record()
+        torch.cuda.synchronize()
+        bwd_ms = sum(a_.elapsed_time(b_) for a_, b_ in bev) / len(bev)
+        fwd_ms = sum(a_.elapsed_time(b_) for a_, b_ in fev2) / len(fev2)
+        bth = Bb * Tb * H
+        bwd_gbs = BACKWARD_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
+        bwd_line = {"B": Bb, "T": Tb, "H": H, "dk": dk, "dv": dv, "dtype": "bf16", "ms": bwd_ms,
+                    "tokens_per_s": Bb * Tb / (bwd_ms * 1e-3), "forward_ms_same_inputs": fwd_ms,
+                    "backward_over_forward": bwd_ms / fwd_ms,
+                    "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": None,
+                                 "algorithmic_bytes": BACKWARD_BYTES_PER_TH * bth,
+                                 "kernel": "kda_chunk_prefill_backward call (forward with chunk states, "
+                                           "bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck)"}}
+        del xb, dob, dfb, wsb, ob, fsb, wfb
+
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
     # (read 1 GiB, write 1 GiB), the reference point beside the nominal 8 TB/s
     cn = (1 << 30) // 4
@@ -334,6 +412,7 @@ def main():
                            "algorithmic_GBps": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9,
                            "hbm_frac": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "prefill_long": long_line,
+        "backward": bwd_line,
         "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms, "fused_step_graph_ms": graph_step_ms,
                    "fused_tokens_per_s": Bd / (fused_ms * 1e-3), "state_update_ms": dstep_ms,
                    "state_update_GBps": dec_gbs, "hbm_frac": dec_gbs / HBM_PEAK_GBS,
@@ -357,6 +436,8 @@ def main():
         line["calibration_copy_bytes"] = {"read": n * 4, "write": n * 4}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args)
+        if bwd_line is not None:
+            bwd_line["cpu_baseline"] = cpu_backward_baseline()
     print(json.dumps(line), flush=True)
 
 

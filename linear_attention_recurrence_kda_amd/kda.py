@@ -203,6 +203,11 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
     return out, final_state
 
 
+def backward_workspace_size(B, T, H, dk, dv, dtype_code):
+    """Bytes of workspace kda_chunk_prefill_backward needs."""
+    return int(load().kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dtype_code))
+
+
 def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, mask=None,
                            initial_state=None, workspace=None):
     """Gradients of chunk_prefill for L = sum <d_o, o> + <d_final_state, final_state>.
