@@ -26,8 +26,8 @@
 //   1. the forward prefill, saving the state at every chunk end (its own kernels);
 //   2. bwd_prep_kernel, one workgroup per (chunk, head): G, P, M = (I + A)^-1 and W, and the
 //      reverse scan's operands Kh, W^T, Qt^T and P^T as bf16 MFMA fragments;
-//   3. bwd_scan_kernel, one workgroup per (b, h, 16-column dv tile), over the chunks from the
-//      last: dS1 and dU of every chunk, and dinit;
+//   3. bwd_scan_kernel, one workgroup per (b, h, 16- or 32-column dv tile), over the chunks
+//      from the last: dS1 and dU of every chunk, and dinit;
 //   4. bwd_cc_kernel, one workgroup per (chunk, head): R, U, dv, dT', dbeta, dA, dG and dP;
 //   5. bwd_ck_kernel, one workgroup per (chunk, head): dq, dk and dlog_alpha.
 // Products run on the bf16 MFMA with fp32 operands split into a bf16 high part and residual
@@ -367,19 +367,16 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
   }
   __syncthreads();
 
-  // ---- M = (I + A)^-1 by forward substitution, one column per lane of wave 0 (fp32)
+  // ---- M = (I + A)^-1 by forward substitution, one column per lane of wave 0 (fp32; eight
+  //      partial sums per row keep the dependency chain short)
   if (w == 0) {
     float x[kC];
 #pragma unroll
     for (int i = 0; i < kC; ++i) {
-      float a0 = (i == lane) ? 1.f : 0.f, a1 = 0.f;
+      float a[8] = {(i == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s2 = 0; s2 < i; ++s2) {
-        const float av = s_A[i * LC + s2];
-        if (s2 & 1) a1 -= av * x[s2];
-        else a0 -= av * x[s2];
-      }
-      x[i] = a0 + a1;
+      for (int s2 = 0; s2 < i; ++s2) a[s2 & 7] -= s_A[i * LC + s2] * x[s2];
+      x[i] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
     float* Mg = p.w.M + ch * (size_t)(kC * kC);
 #pragma unroll
@@ -435,7 +432,7 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
 // A chunk's operands are loaded into registers while the chunk after it (in scan order:
 // the one before it in time) is processed; the loop is unrolled by two so that the
 // compiler's load waits are exact.
-template <int DT, int KP>
+template <int DT, int KP, int NH>
 struct ScanOps {
   static constexpr bool SPLIT = DT == 1;
   static constexpr int KS = KP / 32, MPW = (KP / 16 + 3) / 4, P = SPLIT ? 2 : 1;
@@ -443,29 +440,31 @@ struct ScanOps {
   bf16x8 pt[2][2];                   // P^T (high, residual), row tile w
   bf16x8 wt[P][MPW][2], qt[P][MPW][2];
   float4 gam[MPW];
-  typename std::conditional<DT == 1, float4, uint2>::type dor;   // dO as loaded: row tid / 4,
-                                                                 // columns 4 (tid % 4) .. +3
+  // dO as loaded: row tid / 4, 4 NH columns from 4 NH (tid % 4)
+  typename std::conditional<DT == 1, float4, typename std::conditional<NH == 2, uint4, uint2>::type>::type dor[DT == 1 ? NH : 1];
   uint64_t vb;                       // the chunk's row-validity bits
 };
 
-template <int DT, int KP, int V>
+// NH = 2: the workgroup takes 32 dv columns as two 16-column halves, so each chunk's
+// operands, the dominant per-step traffic of the CU, serve twice the columns
+template <int DT, int KP, int V, int NH>
 __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  using Ops = ScanOps<DT, KP>;
+  using Ops = ScanOps<DT, KP, NH>;
   constexpr bool SPLIT = DT == 1;
   constexpr int parts = SPLIT ? 2 : 1;
-  constexpr int RTK = KP / 16, MPW = Ops::MPW, KS = KP / 32, NT = V / 16;
+  constexpr int RTK = KP / 16, MPW = Ops::MPW, KS = KP / 32, NT = V / (16 * NH), TW = 16 * NH;
   // [part][column][row], columns padded by 8 so the 16 columns a fragment read touches
   // start in different banks
   constexpr int LK = KP + 8, LR = kC + 8;
-  __shared__ __attribute__((aligned(16))) __bf16 s_lam[2][16 * LK];
-  __shared__ __attribute__((aligned(16))) __bf16 s_du[2][16 * LR];
-  __shared__ __attribute__((aligned(16))) __bf16 s_do[2][16 * LR];
+  __shared__ __attribute__((aligned(16))) __bf16 s_lam[2][TW * LK];
+  __shared__ __attribute__((aligned(16))) __bf16 s_du[2][TW * LR];
+  __shared__ __attribute__((aligned(16))) __bf16 s_do[2][TW * LR];
 
   const int vt = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, g4 = lane >> 4, vc = 16 * vt + col;
+  const int col = lane & 15, g4 = lane >> 4, v0 = TW * vt;
 
   auto load_ops = [&](int n, Ops& o) __attribute__((always_inline)) {
     const size_t ch = (size_t)bh * p.NC + n;
@@ -494,47 +493,68 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
         }
       o.gam[m] = *reinterpret_cast<const float4*>(p.w.gam + ch * KP + 16 * rt + 4 * g4);
     }
-    const int row = tid >> 2, c4 = 4 * (tid & 3), t = n * kC + row, ts = t < p.T ? t : p.T - 1;
-    o.dor = *reinterpret_cast<const decltype(o.dor)*>((const Tp*)p.dout + (((size_t)b * p.T + ts) * p.H + h) * V + 16 * vt + c4);
+    const int row = tid >> 2, c4 = 4 * NH * (tid & 3), t = n * kC + row, ts = t < p.T ? t : p.T - 1;
+    const Tp* dp = (const Tp*)p.dout + (((size_t)b * p.T + ts) * p.H + h) * V + v0 + c4;
+#pragma unroll
+    for (int j = 0; j < (DT == 1 ? NH : 1); ++j)
+      o.dor[j] = *reinterpret_cast<const typename std::remove_reference<decltype(o.dor[0])>::type*>(dp + 4 * j);
     o.vb = p.w.vbits[ch];
   };
 
-  float lam[MPW][4];
+  float lam[NH][MPW][4];
 #pragma unroll
-  for (int m = 0; m < MPW; ++m)
+  for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rt = w + 4 * m, row = 16 * rt + 4 * g4 + i;
-      lam[m][i] = (rt < RTK && row < p.K && p.dfinal != nullptr) ? p.dfinal[((size_t)bh * p.K + row) * V + vc] : 0.f;
-    }
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rt = w + 4 * m, row = 16 * rt + 4 * g4 + i;
+        lam[hf][m][i] = (rt < RTK && row < p.K && p.dfinal != nullptr)
+                            ? p.dfinal[((size_t)bh * p.K + row) * V + v0 + 16 * hf + col] : 0.f;
+      }
 
   auto step = [&](int n, const Ops& o) __attribute__((always_inline)) {
     const size_t ch = (size_t)bh * p.NC + n;
     float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
 #pragma unroll
-    for (int m = 0; m < MPW; ++m) {
-      const int rt = w + 4 * m;
-      if (RTK % 4 != 0 && rt >= RTK) continue;       // (never taken when every wave has rows)
+    for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dS1[(16 * rt + 4 * g4 + i) * V + vc] = lam[m][i];
-      split4_to_lds(lam[m], &s_lam[0][col * LK + 16 * rt + 4 * g4], &s_lam[1][col * LK + 16 * rt + 4 * g4]);
-    }
+      for (int m = 0; m < MPW; ++m) {
+        const int rt = w + 4 * m;
+        if (RTK % 4 != 0 && rt >= RTK) continue;     // (never taken when every wave has rows)
+        const int cc = 16 * hf + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS1[(16 * rt + 4 * g4 + i) * V + v0 + cc] = lam[hf][m][i];
+        split4_to_lds(lam[hf][m], &s_lam[0][cc * LK + 16 * rt + 4 * g4], &s_lam[1][cc * LK + 16 * rt + 4 * g4]);
+      }
     {
-      const int row = tid >> 2, c4 = 4 * (tid & 3);
+      const int row = tid >> 2, c4 = 4 * NH * (tid & 3);
       // row valid (in range and unmasked); the empty asm keeps the test here, after the
       // loads of the next chunk have been issued, instead of right behind its own load
       uint64_t vb = o.vb;
       asm volatile("" : "+v"(vb));
       const bool rv = ((vb >> row) & 1ull) != 0ull;
-      float dov[4];
+      float dov[4 * NH];
       if constexpr (DT == 1) {
-        dov[0] = o.dor.x; dov[1] = o.dor.y; dov[2] = o.dor.z; dov[3] = o.dor.w;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          dov[4 * j] = o.dor[j].x; dov[4 * j + 1] = o.dor[j].y; dov[4 * j + 2] = o.dor[j].z; dov[4 * j + 3] = o.dor[j].w;
+        }
       } else {
-        dov[0] = __uint_as_float(o.dor.x << 16); dov[1] = __uint_as_float(o.dor.x & 0xffff0000u);
-        dov[2] = __uint_as_float(o.dor.y << 16); dov[3] = __uint_as_float(o.dor.y & 0xffff0000u);
+        uint32_t wd[2 * NH];
+        if constexpr (NH == 2) {
+          wd[0] = o.dor[0].x; wd[1] = o.dor[0].y; wd[2] = o.dor[0].z; wd[3] = o.dor[0].w;
+        } else {
+          wd[0] = o.dor[0].x; wd[1] = o.dor[0].y;
+        }
+#pragma unroll
+        for (int j = 0; j < 2 * NH; ++j) {
+          dov[2 * j] = __uint_as_float(wd[j] << 16);
+          dov[2 * j + 1] = __uint_as_float(wd[j] & 0xffff0000u);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4 * NH; ++e) {
         const float x = rv ? dov[e] : 0.f;
         const __bf16 hi = (__bf16)x;
         s_do[0][(c4 + e) * LR + row] = hi;
@@ -544,12 +564,14 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
     __syncthreads();
 
     // ---- dU, row tile w: Kh dS1 + P^T dO
-    {
+#pragma unroll
+    for (int hf = 0; hf < NH; ++hf) {
+      const int cc = 16 * hf + col;
       f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_lam[0][col * LK + 32 * ks + 8 * g4]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_lam[1][col * LK + 32 * ks + 8 * g4]);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_lam[0][cc * LK + 32 * ks + 8 * g4]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_lam[1][cc * LK + 32 * ks + 8 * g4]);
         a0 = mfma16(o.kh[0][ks], bh, a0);
         a1 = mfma16(o.kh[0][ks], bl, a1);
         if (SPLIT) a2 = mfma16(o.kh[parts - 1][ks], bh, a2);
@@ -557,18 +579,18 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (32 * s + 31 < 16 * w) continue;          // P^T is upper triangular
-        const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][col * LR + 32 * s + 8 * g4]);
+        const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][cc * LR + 32 * s + 8 * g4]);
         a0 = mfma16(o.pt[0][s], dh, a0);
         a1 = mfma16(o.pt[1][s], dh, a1);
-        if (SPLIT) a2 = mfma16(o.pt[0][s], *reinterpret_cast<const bf16x8*>(&s_do[1][col * LR + 32 * s + 8 * g4]), a2);
+        if (SPLIT) a2 = mfma16(o.pt[0][s], *reinterpret_cast<const bf16x8*>(&s_do[1][cc * LR + 32 * s + 8 * g4]), a2);
       }
       float du[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) du[i] = a0[i] + (a1[i] + a2[i]);
       float* dU = p.w.dU + ch * (size_t)(kC * V);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dU[(16 * w + 4 * g4 + i) * V + vc] = du[i];
-      split4_to_lds(du, &s_du[0][col * LR + 16 * w + 4 * g4], &s_du[1][col * LR + 16 * w + 4 * g4]);
+      for (int i = 0; i < 4; ++i) dU[(16 * w + 4 * g4 + i) * V + v0 + cc] = du[i];
+      split4_to_lds(du, &s_du[0][cc * LR + 16 * w + 4 * g4], &s_du[1][cc * LR + 16 * w + 4 * g4]);
     }
     __syncthreads();
 
@@ -577,25 +599,29 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
     for (int m = 0; m < MPW; ++m) {
       const int rt = w + 4 * m;
       if (RTK % 4 != 0 && rt >= RTK) continue;
-      f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_du[0][col * LR + 32 * s + 8 * g4]);
-        const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_du[1][col * LR + 32 * s + 8 * g4]);
-        const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][col * LR + 32 * s + 8 * g4]);
-        a0 = mfma16(o.wt[0][m][s], uh, a0);
-        a1 = mfma16(o.wt[0][m][s], ul, a1);
-        a0 = mfma16(o.qt[0][m][s], dh, a0);
-        if (SPLIT) {
-          const bf16x8 dl = *reinterpret_cast<const bf16x8*>(&s_do[1][col * LR + 32 * s + 8 * g4]);
-          a2 = mfma16(o.wt[parts - 1][m][s], uh, a2);
-          a2 = mfma16(o.qt[parts - 1][m][s], dh, a2);
-          a1 = mfma16(o.qt[0][m][s], dl, a1);
-        }
-      }
       const float gg[4] = {o.gam[m].x, o.gam[m].y, o.gam[m].z, o.gam[m].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lam[m][i] = gg[i] * lam[m][i] + (a0[i] + (a1[i] + a2[i]));
+      for (int hf = 0; hf < NH; ++hf) {
+        const int cc = 16 * hf + col;
+        f32x4 a0 = zero4(), a1 = zero4(), a2 = zero4();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 uh = *reinterpret_cast<const bf16x8*>(&s_du[0][cc * LR + 32 * s + 8 * g4]);
+          const bf16x8 ul = *reinterpret_cast<const bf16x8*>(&s_du[1][cc * LR + 32 * s + 8 * g4]);
+          const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_do[0][cc * LR + 32 * s + 8 * g4]);
+          a0 = mfma16(o.wt[0][m][s], uh, a0);
+          a1 = mfma16(o.wt[0][m][s], ul, a1);
+          a0 = mfma16(o.qt[0][m][s], dh, a0);
+          if (SPLIT) {
+            const bf16x8 dl = *reinterpret_cast<const bf16x8*>(&s_do[1][cc * LR + 32 * s + 8 * g4]);
+            a2 = mfma16(o.wt[parts - 1][m][s], uh, a2);
+            a2 = mfma16(o.qt[parts - 1][m][s], dh, a2);
+            a1 = mfma16(o.qt[0][m][s], dl, a1);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[hf][m][i] = gg[i] * lam[hf][m][i] + (a0[i] + (a1[i] + a2[i]));
+      }
     }
     __syncthreads();
   };
@@ -614,12 +640,14 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
   }
   if (n == 0) step(0, A);
 #pragma unroll
-  for (int m = 0; m < MPW; ++m)
+  for (int hf = 0; hf < NH; ++hf)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rt = w + 4 * m, row = 16 * rt + 4 * g4 + i;
-      if (rt < RTK && row < p.K) p.dinit[((size_t)bh * p.K + row) * V + vc] = lam[m][i];
-    }
+    for (int m = 0; m < MPW; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rt = w + 4 * m, row = 16 * rt + 4 * g4 + i;
+        if (rt < RTK && row < p.K) p.dinit[((size_t)bh * p.K + row) * V + v0 + 16 * hf + col] = lam[hf][m][i];
+      }
 }
 
 // ================================================================ 4. C x C gradients
@@ -1274,7 +1302,13 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V>), dim3(p.B * p.H * (V / 16)), dim3(kThreads), 0, st, p);
+  // 32-column scan workgroups (bf16) once there are enough (b, h) pairs to fill the chip with them
+  constexpr bool kWideOk = DT == 0 && V >= 32;
+  if (kWideOk && p.B * p.H >= 64)
+    hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V, kWideOk ? 2 : 1>), dim3(p.B * p.H * (V / 32)), dim3(kThreads), 0,
+                       st, p);
+  else
+    hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V, 1>), dim3(p.B * p.H * (V / 16)), dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.NC == 0) return e;
   hipLaunchKernelGGL((bwd_cc_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);

@@ -172,3 +172,25 @@ def test_backward_slow_gates(oracle):
     inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=8, decay="slow")
     do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 8)
     _check("slow gates", _run(inp, do, dfinal, "bf16", dev), _ref(oracle, inp, do, dfinal), "bf16")
+
+
+def test_backward_wide_scan_tiles_equal_narrow():
+    """With 64 or more (b, h) pairs and bf16 the reverse scan takes 32 dv columns per
+    workgroup; every column sees the same operations in the same order as with 16, so
+    one call over 64 pairs equals two calls over 32 pairs each, bit for bit."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv = 2, 200, 32, 128, 128
+    say("[case] backward wide vs narrow scan tiles")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=9)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 9)
+    mask = np.ones((B, T), np.uint8)
+    mask[1, 150:] = 0
+    full = _run(inp, do, dfinal, "bf16", dev, mask)
+    for b in range(B):
+        one = {n: x[b:b + 1] for n, x in inp.items()}
+        part = _run(one, do[b:b + 1], dfinal[b:b + 1], "bf16", dev, mask[b:b + 1])
+        for n in NAMES:
+            got = full[n][b:b + 1]
+            assert torch.equal(got, part[n]), f"{n} differs for batch row {b}"
