@@ -116,6 +116,14 @@ __device__ __forceinline__ void split4_to_lds(const float* v, __bf16* hi, __bf16
   *reinterpret_cast<uint2*>(lo) = make_uint2(lu[0], lu[1]);
 }
 
+// LDS written by this wave is visible to its other lanes after this point: a wave's LDS
+// operations execute in order, so the compiler only must not move accesses across it
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1, 64);
   x += __shfl_xor(x, 2, 64);
@@ -220,20 +228,26 @@ __device__ __forceinline__ const float* entry_state(const Params& p, int b, int 
 }
 
 // ================================================================ 2. prep
+// One workgroup per (chunk, head); wave w holds rows 16 w .. +15 of the chunk in the
+// A-operand layout.  One LDS region of C x (KP + 4) floats is reused, phase by phase, for Qt
+// (to transpose it into Qt^T fragments), Ki (the B operand of G and P), A and P (the
+// inverse and the P^T fragments), and Kt (the B operand of W = -T' Kt); with M and a small
+// staging area that is about 58 KB, so two workgroups share a CU.
 template <int DT, int KP>
-__global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads, 2) bwd_prep_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  constexpr int KS = KP / 32, CT = KP / 16, LD = KP + 2, LC = kC + 2;
+  constexpr int KS = KP / 32, CT = KP / 16, LD = KP + 4, LC = kC + 2;
   constexpr bool SPLIT = DT == 1;
   constexpr int parts = SPLIT ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) float s_kt[kC * LD];   // Kt
-  __shared__ __attribute__((aligned(16))) float s_qt[kC * LD];   // Qt
-  __shared__ __attribute__((aligned(16))) float s_x[kC * LD];    // Ki, or g on the exact path
-  __shared__ __attribute__((aligned(16))) float s_A[kC * LC];
-  __shared__ __attribute__((aligned(16))) float s_M[kC * LC];    // P, then M
+  constexpr int RS = LD > 2 * LC ? LD : 2 * LC;                   // region floats per row
+  __shared__ __attribute__((aligned(16))) float s_x[kC * RS];    // Qt; Ki or g; A and P; Kt
+  __shared__ __attribute__((aligned(16))) float s_M[kC * LC];
+  __shared__ __attribute__((aligned(16))) float s_stage[4 * 256];
   __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC];
   __shared__ uint32_t s_vb[4];
+  float* s_A = s_x;                                              // after G and P are formed
+  float* s_P = s_x + kC * LC;
 
   const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -252,24 +266,23 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
   if (tid == 0)
     p.w.vbits[ch] = (uint64_t)s_vb[0] | ((uint64_t)s_vb[1] << 16) | ((uint64_t)s_vb[2] << 32) | ((uint64_t)s_vb[3] << 48);
 
-  // ---- decayed rows: Kt, Qt (and Ki or g) to LDS, Kh fragments to the workspace
+  // ---- decayed rows in registers; Kh fragments to the workspace; Qt to LDS
   uint16_t* kh = p.w.kh + ch * (size_t)(kC * KP * parts);
+  float kt[KS][8];
   bf16x8 kth[KS], ktl[KS], qth[KS], qtl[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    float kt[8], qt[8], khv[8];
+    float qt[8], khv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int c = 32 * ks + cg + e;
       const float gv = R.g[ks][e], gam = exp2f(gv);
-      kt[e] = R.k[ks][e] * gam;
+      kt[ks][e] = R.k[ks][e] * gam;
       qt[e] = R.q[ks][e] * gam;
       khv[e] = R.k[ks][e] * exp2f(s_gl[c] - gv);
-      s_kt[r * LD + c] = kt[e];
-      s_qt[r * LD + c] = qt[e];
-      s_x[r * LD + c] = fast ? R.k[ks][e] * exp2f(-gv) : gv;
+      s_x[r * LD + c] = qt[e];
     }
-    split8(kt, kth[ks], ktl[ks]);
+    split8(kt[ks], kth[ks], ktl[ks]);
     split8(qt, qth[ks], qtl[ks]);
     bf16x8 hi, lo;
     split8(khv, hi, lo);
@@ -277,76 +290,8 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
     if (SPLIT) *reinterpret_cast<bf16x8*>(kh + kC * KP + afrag(w, ks, lane, KP)) = lo;
   }
   __syncthreads();
-
-  // ---- G (strictly lower), A = Diag(beta) G and P (lower, staged in s_M): wave w, row tile w
-  float* Gg = p.w.G + ch * (size_t)(kC * kC);
-  if (fast) {
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      f32x4 ga = zero4(), pa = zero4();
-      if (J <= w) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          float bv[8];
-          lds8(&s_x[(16 * J + col) * LD + 32 * ks + cg], bv);
-          bf16x8 bh, bl;
-          split8(bv, bh, bl);
-          ga = mfma16(kth[ks], bh, ga);
-          ga = mfma16(ktl[ks], bh, ga);
-          ga = mfma16(kth[ks], bl, ga);
-          pa = mfma16(qth[ks], bh, pa);
-          pa = mfma16(qtl[ks], bh, pa);
-          pa = mfma16(qth[ks], bl, pa);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * w + 4 * g4 + i, cl = 16 * J + col;
-        const float gv = (J <= w && cl < row) ? ga[i] : 0.f;
-        const float pv = (J <= w && cl <= row) ? pa[i] : 0.f;
-        s_A[row * LC + cl] = s_beta[row] * gv;
-        s_M[row * LC + cl] = pv;
-        Gg[row * kC + cl] = gv;
-      }
-    }
-  } else {
-    // exact pairwise decays exp2(g_i - g_j) <= 1, entry by entry
-    const Tp* kg = (const Tp*)p.k;
-    const Tp* qg = (const Tp*)p.q;
-    for (int idx = tid; idx < kC * kC; idx += kThreads) {
-      const int i = idx / kC, j = idx % kC;
-      float gs = 0.f, ps = 0.f;
-      if (j <= i && s_ok[i] != 0.f && s_ok[j] != 0.f) {
-        const size_t ti = (((size_t)b * p.T + n * kC + i) * p.H + h) * p.K;
-        const size_t tj = (((size_t)b * p.T + n * kC + j) * p.H + h) * p.K;
-        for (int c = 0; c < p.K; ++c) {
-          const float d = exp2f(s_x[i * LD + c] - s_x[j * LD + c]);
-          const float kj = E::ld(kg, tj + c) * d;
-          gs += E::ld(kg, ti + c) * kj;
-          ps += E::ld(qg, ti + c) * kj;
-        }
-      }
-      gs = j < i ? gs : 0.f;
-      s_A[i * LC + j] = s_beta[i] * gs;
-      s_M[i * LC + j] = ps;
-      Gg[i * kC + j] = gs;
-    }
-  }
-  __syncthreads();
-
-  // ---- P^T and Qt^T fragments (rows of P^T / channels, contraction over chunk rows), Gam_last
+  // ---- Qt^T fragments (rows: channels, contraction over chunk rows) and Gam_last
   {
-    uint16_t* pt = p.w.pt + ch * (size_t)(2 * kC * kC);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = s_M[(32 * s + cg + e) * LC + 16 * w + col];
-      bf16x8 hi, lo;
-      split8(pv, hi, lo);
-      *reinterpret_cast<bf16x8*>(pt + afrag(w, s, lane, kC)) = hi;
-      *reinterpret_cast<bf16x8*>(pt + kC * kC + afrag(w, s, lane, kC)) = lo;
-    }
     uint16_t* qtw = p.w.qt + ch * (size_t)(kC * KP * parts);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -356,7 +301,7 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
       for (int s = 0; s < 2; ++s) {
         float qv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = s_qt[(32 * s + cg + e) * LD + 16 * ct + col];
+        for (int e = 0; e < 8; ++e) qv[e] = s_x[(32 * s + cg + e) * LD + 16 * ct + col];
         bf16x8 hi, lo;
         split8(qv, hi, lo);
         *reinterpret_cast<bf16x8*>(qtw + afrag(ct, s, lane, kC)) = hi;
@@ -366,28 +311,158 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
     if (tid < KP) p.w.gam[ch * KP + tid] = exp2f(s_gl[tid]);
   }
   __syncthreads();
+  // ---- Ki (factorised path) or g (exact path) to LDS
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      s_x[r * LD + 32 * ks + cg + e] = fast ? R.k[ks][e] * exp2f(-R.g[ks][e]) : R.g[ks][e];
+  __syncthreads();
 
-  // ---- M = (I + A)^-1 by forward substitution, one column per lane of wave 0 (fp32; eight
-  //      partial sums per row keep the dependency chain short)
-  if (w == 0) {
-    float x[kC];
+  // ---- G (strictly lower) and P (lower) for row tile w, in registers in the D layout
+  //      (lane: rows 16 w + 4 (l/16) .. +3, column 16 J + l%16)
+  f32x4 gt[4], ptl[4];
 #pragma unroll
-    for (int i = 0; i < kC; ++i) {
-      float a[8] = {(i == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int J = 0; J < 4; ++J) { gt[J] = zero4(); ptl[J] = zero4(); }
+  if (fast) {
 #pragma unroll
-      for (int s2 = 0; s2 < i; ++s2) a[s2 & 7] -= s_A[i * LC + s2] * x[s2];
-      x[i] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    for (int J = 0; J < 4; ++J) {
+      if (J > w) continue;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float bv[8];
+        lds8(&s_x[(16 * J + col) * LD + 32 * ks + cg], bv);
+        bf16x8 bh, bl;
+        split8(bv, bh, bl);
+        gt[J] = mfma16(kth[ks], bh, gt[J]);
+        gt[J] = mfma16(ktl[ks], bh, gt[J]);
+        gt[J] = mfma16(kth[ks], bl, gt[J]);
+        ptl[J] = mfma16(qth[ks], bh, ptl[J]);
+        ptl[J] = mfma16(qtl[ks], bh, ptl[J]);
+        ptl[J] = mfma16(qth[ks], bl, ptl[J]);
+      }
     }
-    float* Mg = p.w.M + ch * (size_t)(kC * kC);
+  } else {
+    // exact pairwise decays exp2(g_i - g_j) <= 1, entry by entry for the lane's D positions
+    const Tp* kg = (const Tp*)p.k;
+    const Tp* qg = (const Tp*)p.q;
+    for (int J = 0; J <= w; ++J)
 #pragma unroll
-    for (int i = 0; i < kC; ++i) {
-      s_M[i * LC + lane] = x[i];
-      Mg[i * kC + lane] = x[i];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int ii = 16 * w + 4 * g4 + i, jj = 16 * J + col;
+        float gs = 0.f, ps = 0.f;
+        if (jj <= ii && s_ok[ii] != 0.f && s_ok[jj] != 0.f) {
+          const size_t ti = (((size_t)b * p.T + n * kC + ii) * p.H + h) * p.K;
+          const size_t tj = (((size_t)b * p.T + n * kC + jj) * p.H + h) * p.K;
+          for (int c = 0; c < p.K; ++c) {
+            const float d = exp2f(s_x[ii * LD + c] - s_x[jj * LD + c]);
+            const float kj = E::ld(kg, tj + c) * d;
+            gs += E::ld(kg, ti + c) * kj;
+            ps += E::ld(qg, ti + c) * kj;
+          }
+        }
+        gt[J][i] = gs;
+        ptl[J][i] = ps;
+      }
+  }
+  __syncthreads();                                   // Ki / g read: the region takes A and P
+  {
+    float* Gg = p.w.G + ch * (size_t)(kC * kC);
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g4 + i, cl = 16 * J + col;
+        const float gv = (J <= w && cl < row) ? gt[J][i] : 0.f;
+        s_A[row * LC + cl] = s_beta[row] * gv;
+        s_P[row * LC + cl] = (J <= w && cl <= row) ? ptl[J][i] : 0.f;
+        Gg[row * kC + cl] = gv;
+      }
   }
   __syncthreads();
 
-  // ---- W = -T' Kt, computed per channel tile and turned into W^T fragments by lane swaps
+  // ---- P^T fragments (rows: P's columns, contraction over P's rows)
+  {
+    uint16_t* pt = p.w.pt + ch * (size_t)(2 * kC * kC);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = s_P[(32 * s + cg + e) * LC + 16 * w + col];
+      bf16x8 hi, lo;
+      split8(pv, hi, lo);
+      *reinterpret_cast<bf16x8*>(pt + afrag(w, s, lane, kC)) = hi;
+      *reinterpret_cast<bf16x8*>(pt + kC * kC + afrag(w, s, lane, kC)) = lo;
+    }
+  }
+
+  // ---- M = (I + A)^-1, blocked by 16 rows, fp32: wave I inverts diagonal block I by forward
+  //      substitution (one column per lane of its first 16 lanes) and clears the blocks right
+  //      of it; then the blocks below the diagonal by distance d, M_IJ = -M_II sum_{L=J}^{I-1}
+  //      A_IL M_LJ with I = J + d (wave J, four values per lane, through a 16 x 16 staging tile)
+  {
+    const int I = w;
+    if (lane < 16) {
+      float x[16];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        float a0 = (rr == lane) ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < rr; ++jj) {
+          const float av = s_A[(16 * I + rr) * LC + 16 * I + jj];
+          if (jj & 1) a1 -= av * x[jj];
+          else a0 -= av * x[jj];
+        }
+        x[rr] = a0 + a1;
+      }
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) s_M[(16 * I + rr) * LC + 16 * I + lane] = x[rr];
+    }
+    for (int idx = lane; idx < (3 - I) * 256; idx += 64) {
+      const int J = I + 1 + idx / 256, rr = (idx % 256) / 16, cc = idx % 16;
+      s_M[(16 * I + rr) * LC + 16 * J + cc] = 0.f;
+    }
+    __syncthreads();
+    float* stage = s_stage + w * 256;
+    const int rr = lane >> 2, c0 = 4 * (lane & 3);
+    for (int d = 1; d < 4; ++d) {
+      const int J = w, Ib = J + d;
+      if (Ib < 4) {
+        float xv[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int L = J; L < Ib; ++L) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const float av = s_A[(16 * Ib + rr) * LC + 16 * L + t];
+            const float2 m0 = *reinterpret_cast<const float2*>(&s_M[(16 * L + t) * LC + 16 * J + c0]);
+            const float2 m1 = *reinterpret_cast<const float2*>(&s_M[(16 * L + t) * LC + 16 * J + c0 + 2]);
+            xv[0] += av * m0.x; xv[1] += av * m0.y; xv[2] += av * m1.x; xv[3] += av * m1.y;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) stage[rr * 16 + c0 + e] = xv[e];
+        wave_lds_fence();
+        float yv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float mv = s_M[(16 * Ib + rr) * LC + 16 * Ib + t];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yv[e] -= mv * stage[t * 16 + c0 + e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_M[(16 * Ib + rr) * LC + 16 * J + c0 + e] = yv[e];
+      }
+      __syncthreads();                               // (the last one also ends the reads of A and P)
+    }
+    float* Mg = p.w.M + ch * (size_t)(kC * kC);
+    for (int idx = tid; idx < kC * kC; idx += kThreads) Mg[idx] = s_M[(idx / kC) * LC + idx % kC];
+  }
+
+  // ---- Kt to LDS, then W = -T' Kt per channel tile, turned into W^T fragments by lane swaps
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_x[r * LD + 32 * ks + cg + e] = kt[ks][e];
+  __syncthreads();
   {
     uint16_t* wt = p.w.wt + ch * (size_t)(kC * KP * parts);
 #pragma unroll
@@ -406,7 +481,7 @@ __global__ void __launch_bounds__(kThreads) bwd_prep_kernel(Params p) {
           for (int e = 0; e < 8; ++e) {
             const int j = 32 * s + cg + e;
             av[e] = s_M[(16 * I + col) * LC + j] * s_beta[j];
-            bv[e] = s_kt[j * LD + 16 * ct + col];
+            bv[e] = s_x[j * LD + 16 * ct + col];
           }
           acc = mm3(av, bv, acc);
         }
