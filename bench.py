@@ -10,7 +10,9 @@ One step = one pass of the whole path on synthetic, seeded inputs resident in HB
 `value` is prefill tokens/s; the decode state-update GB/s is reported beside it, and so is the
 same 128k tokens prefilled as 32 packed prompts of seeded lengths (kda_chunk_prefill_varlen).
 The training backward (kda_chunk_prefill_backward) is timed on the chunked-prefill training
-shape (B=4, H=32, T=4096) with the forward on the same inputs beside it.
+shape (B=4, H=32, T=4096): fed with the chunk-end states that the training forward
+(kda_chunk_prefill_states) saves, and as the self-contained call that runs the forward again,
+with the plain forward on the same inputs beside them.
 Prints one JSON line.
 """
 import argparse
@@ -27,8 +29,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_BYTES_PER_TH = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (512) + beta (4)
 DECODE_BYTES_PER_SH = 132612         # state read+write 8*K*V + q,k,v,o (1024) + log_alpha (512) + beta
 # backward per token-head: q, k, v, dO bf16 (4 x 256) + log_alpha (512) + beta (4) read;
-# dq, dk, dv, dlog_alpha fp32 (4 x 512) + dbeta (4) written
+# dq, dk, dv, dlog_alpha fp32 (4 x 512) + dbeta (4) written; with the chunk-end states
+# handed in, those are read too (K x V fp32 per 64 tokens: 1024)
 BACKWARD_BYTES_PER_TH = 1024 + 512 + 4 + 2048 + 4
+BACKWARD_STATES_BYTES_PER_TH = BACKWARD_BYTES_PER_TH + 128 * 128 * 4 // 64
 
 
 # HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on the default workload,
@@ -309,7 +313,9 @@ def main():
         del xl, ol, wsl
 
     # the training backward on the chunked-prefill training shape: dq, dk, dv, dlog_alpha, dbeta
-    # and dinit for L = <dO, o> + <dS_T, S_T>, beside the forward on the same inputs
+    # and dinit for L = <dO, o> + <dS_T, S_T>.  A training step runs the forward that saves the
+    # chunk-end states, then the backward that takes them; the backward that runs the forward
+    # again, and the plain forward, are timed beside it
     bwd_line = None
     if args.bwd_B > 0:
         Bb, Tb = args.bwd_B, args.bwd_T
@@ -318,47 +324,61 @@ def main():
         gb.manual_seed(5)
         dob = torch.randn(Bb, Tb, H, dv, device=dev, generator=gb).to(torch.bfloat16)
         dfb = torch.randn(Bb, H, dk, dv, device=dev, generator=gb)
-        wsb = torch.empty(kda.backward_workspace_size(Bb, Tb, H, dk, dv, kda.KDA_BF16), dtype=torch.uint8,
-                          device=dev)
-        bargs = (xb["q"], xb["k"], xb["v"], xb["log_alpha"], xb["beta"], dob)
-
-        def backward():
-            return kda.chunk_prefill_backward(*bargs, d_final_state=dfb, workspace=wsb)
+        fargs = (xb["q"], xb["k"], xb["v"], xb["log_alpha"], xb["beta"])
+        bargs = fargs + (dob,)
         ob = torch.empty(Bb, Tb, H, dv, dtype=torch.bfloat16, device=dev)
         fsb = torch.empty(Bb, H, dk, dv, dtype=torch.float32, device=dev)
-        wfb = torch.empty(kda.prefill_workspace_size(Bb, Tb, H, dk, dv, C, kda.KDA_BF16), dtype=torch.uint8,
+        ckb = torch.empty(Bb * (Tb // 64), H, dk, dv, dtype=torch.float32, device=dev)
+        wfb = torch.empty(max(kda.prefill_workspace_size(Bb, Tb, H, dk, dv, c, kda.KDA_BF16) for c in (64, C)),
+                          dtype=torch.uint8, device=dev)
+        wsg = torch.empty(kda.backward_workspace_size(Bb, Tb, H, dk, dv, kda.KDA_BF16, states_given=True),
+                          dtype=torch.uint8, device=dev)
+        wsr = torch.empty(kda.backward_workspace_size(Bb, Tb, H, dk, dv, kda.KDA_BF16), dtype=torch.uint8,
                           device=dev)
 
+        def forward_states():
+            kda.chunk_prefill_states(*fargs, chunk_size=64, state_interval=64, chunk_states=ckb, out=ob,
+                                     final_state=fsb, workspace=wfb)
+
+        def backward():
+            return kda.chunk_prefill_backward(*bargs, d_final_state=dfb, workspace=wsg, chunk_states=ckb)
+
+        def backward_recompute():
+            return kda.chunk_prefill_backward(*bargs, d_final_state=dfb, workspace=wsr)
+
         def forward():
-            kda.chunk_prefill(xb["q"], xb["k"], xb["v"], xb["log_alpha"], xb["beta"], chunk_size=C, out=ob,
-                              final_state=fsb, workspace=wfb)
-        backward()
-        forward()
-        torch.cuda.synchronize()
-        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for a_, b_ in bev:
-            a_.record()
-            backward()
-            b_.record()
-        fev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for a_, b_ in fev2:
-            a_.record()
-            forward()
-            b_.record()
-        torch.cuda.synchronize()
-        bwd_ms = sum(a_.elapsed_time(b_) for a_, b_ in bev) / len(bev)
-        fwd_ms = sum(a_.elapsed_time(b_) for a_, b_ in fev2) / len(fev2)
+            kda.chunk_prefill(*fargs, chunk_size=C, out=ob, final_state=fsb, workspace=wfb)
+
+        def timed(fn, n=5):
+            fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for a_, b_ in ev:
+                a_.record()
+                fn()
+                b_.record()
+            torch.cuda.synchronize()
+            return sum(a_.elapsed_time(b_) for a_, b_ in ev) / n
+        fst_ms = timed(forward_states)
+        bwd_ms = timed(backward)                 # reads the states forward_states left in ckb
+        rec_ms = timed(backward_recompute)
+        fwd_ms = timed(forward)
         bth = Bb * Tb * H
-        bwd_gbs = BACKWARD_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
-        bwd_line = {"B": Bb, "T": Tb, "H": H, "dk": dk, "dv": dv, "dtype": "bf16", "ms": bwd_ms,
-                    "tokens_per_s": Bb * Tb / (bwd_ms * 1e-3), "forward_ms_same_inputs": fwd_ms,
+        bwd_gbs = BACKWARD_STATES_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
+        bwd_line = {"B": Bb, "T": Tb, "H": H, "dk": dk, "dv": dv, "dtype": "bf16",
+                    "ms": bwd_ms, "tokens_per_s": Bb * Tb / (bwd_ms * 1e-3),
+                    "forward_states_ms": fst_ms,
+                    "training_step_ms": fst_ms + bwd_ms,
+                    "training_step_tokens_per_s": Bb * Tb / ((fst_ms + bwd_ms) * 1e-3),
+                    "ms_recompute": rec_ms,
+                    "forward_ms_same_inputs": fwd_ms,
                     "backward_over_forward": bwd_ms / fwd_ms,
                     "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": None,
-                                 "algorithmic_bytes": BACKWARD_BYTES_PER_TH * bth,
-                                 "kernel": "kda_chunk_prefill_backward call (forward with chunk states, "
-                                           "bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck)"}}
-        del xb, dob, dfb, wsb, ob, fsb, wfb
+                                 "algorithmic_bytes": BACKWARD_STATES_BYTES_PER_TH * bth,
+                                 "kernel": "kda_chunk_prefill_backward call with the chunk-end states given "
+                                           "(bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck)"}}
+        del xb, dob, dfb, ob, fsb, ckb, wfb, wsg, wsr
 
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
     # (read 1 GiB, write 1 GiB), the reference point beside the nominal 8 TB/s

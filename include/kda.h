@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -109,7 +109,8 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * the pages' 256-token chunks included, return KDA_ERR_UNSUPPORTED: their decay
  * factors leave the fp32 range with this kernel's chunk-start factorisation and
  * their inverse does not fit the LDS); B, H <= 65535; H times the number of
- * chunks < 2^31 (KDA_ERR_UNSUPPORTED otherwise);
+ * chunks < 2^24 and B*H <= 2^20 - 8, so every launch's extent in threads fits 32
+ * bits (KDA_ERR_UNSUPPORTED otherwise, and a workspace size of 0);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
  * and log_alpha unless KDA_FLAG_SCALAR_GATE is set.  The ragged tail of the last chunk is handled as masked
  * positions.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
@@ -121,6 +122,33 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
                       const float* init_state, void* o, float* final_state,
                       int B, int T, int H, int dk, int dv, int chunk, int dtype,
                       unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_prefill that also saves the state every state_interval tokens of each row,
+ * for prefix caching in the batch layout and for training: with state_interval = 64 these
+ * are the chunk-end states kda_chunk_prefill_backward takes instead of running the
+ * forward again (the state recurrence of the Kimi Linear summary page, read at chunk
+ * boundaries).  Arguments, results, supported sizes and the workspace are those of
+ * kda_chunk_prefill (kda_chunk_prefill_workspace_size), plus:
+ *
+ *   chunk_states [M,H,dk,dv] fp32, written, or NULL (then the call is kda_chunk_prefill):
+ *                            row b's state after its first j * state_interval tokens,
+ *                            j = 1 .. floor(T / state_interval), at entry
+ *                            b * floor(T / state_interval) + j - 1; masked positions leave
+ *                            the state as it is, so the saved states count them as tokens
+ *   num_states               entries chunk_states holds (>= 0); entries past it are not
+ *                            written (M = B * floor(T / state_interval) holds them all)
+ *   state_interval           a positive multiple of chunk
+ *
+ * chunk_states 4-byte aligned (16-byte when handed to kda_chunk_prefill_backward);
+ * KDA_ERR_INVALID_ARG for a bad interval or a negative num_states.
+ */
+int kda_chunk_prefill_states(const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, const uint8_t* mask,
+                             const float* init_state, void* o, float* final_state,
+                             float* chunk_states, int num_states, int state_interval,
+                             int B, int T, int H, int dk, int dv, int chunk, int dtype,
+                             unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_chunk_prefill for callers that cannot allocate device memory: code under HIP
@@ -204,8 +232,8 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  * into it and a decreasing entry gives an empty sequence, so a malformed
  * array gives wrong results but no out-of-bounds access (checkpoints included,
  * as num_states bounds them; slots, as num_slots bounds them).  Supported: as
- * kda_chunk_prefill with B = N (N <= 65535), and H times (ceil(T/chunk) + N)
- * < 2^31.  16-byte aligned: q, k, v, and log_alpha unless KDA_FLAG_SCALAR_GATE
+ * kda_chunk_prefill with B = N (N <= 65535), H times (ceil(T/chunk) + N)
+ * < 2^24 and N*H <= 2^20 - 8.  16-byte aligned: q, k, v, and log_alpha unless KDA_FLAG_SCALAR_GATE
  * is set; chunk_states and slot 4-byte aligned.  `flags` may hold
  * KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
  */
@@ -219,9 +247,11 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace kda_chunk_prefill_backward needs (0 when none is needed or
- * the arguments would be rejected).
+ * the arguments would be rejected): states_given != 0 for calls that pass chunk_states
+ * (the forward's workspace, outputs and states are then not needed).
  */
-size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
+                                                 int states_given);
 
 /*
  * Gradients of kda_chunk_prefill for training (remio.ai page, KDA section: the model is
@@ -232,6 +262,11 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  * gradient through.
  *
  *   q, k, v, log_alpha, beta, mask, init_state   as for kda_chunk_prefill (flags = 0)
+ *   chunk_states  [B*floor(T/64),H,dk,dv]  fp32, or NULL: the state at every 64-token
+ *                              boundary as kda_chunk_prefill_states writes it with
+ *                              state_interval = 64 on the same inputs (any chunk; with
+ *                              chunk = 64 the gradients equal those of a NULL call bit for
+ *                              bit).  NULL: the call runs the forward again to form them.
  *   d_o           [B,T,H,dv]   dtype
  *   d_final_state [B,H,dk,dv]  fp32, or NULL (zero)
  *   dq, dk        [B,T,H,dk]   fp32, written
@@ -241,23 +276,27 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  *   d_init_state  [B,H,dk,dv]  fp32, written (also when init_state is NULL: the gradient
  *                              with respect to the zero state)
  *
- * It runs the forward again in 64-token chunks, keeping the state at each chunk end,
- * then a reverse scan over the chunks carries dL/dS (the chunk recurrence differentiated)
+ * Without chunk_states it runs the forward again in 64-token chunks, keeping the state at
+ * each chunk end; then a reverse scan over the chunks carries dL/dS (the chunk recurrence
+ * differentiated)
  * and chunk-parallel kernels form the gradients; every sum accumulates in fp32, with
  * MFMA operands split into bf16 high and low parts (single bf16 for the reverse scan's
  * key, query and W operands with bf16 inputs, as in the forward scan).  The workspace
- * holds the forward's own workspace, the chunk-end states and about 250 KB of chunk
- * operands per (b, h, chunk) at dk = dv = 128.
+ * holds about 250 KB of chunk operands per (b, h, chunk) at dk = dv = 128 and, without
+ * chunk_states, the forward's own workspace, outputs and chunk-end states.
  *
- * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535 and H ceil(T/64) < 2^31;
+ * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535, H ceil(T/64) < 2^24, B*H <= 2^20 - 8
+ * and B*H*ceil(T/64) <= 2^22 - 8 (launch extents in threads fit 32 bits);
  * flags = 0 (the L2-norm and per-head-gate flags return KDA_ERR_UNSUPPORTED).
- * 16-byte aligned: q, k, v, log_alpha, d_o, init_state, dq, dk, dv, d_log_alpha;
- * 4-byte: beta, d_beta, d_final_state, d_init_state; workspace 256-byte aligned.
+ * 16-byte aligned: q, k, v, log_alpha, d_o, init_state, chunk_states, dq, dk, dv,
+ * d_log_alpha; 4-byte: beta, d_beta, d_final_state, d_init_state; workspace 256-byte
+ * aligned.
  * Outputs must not overlap inputs.
  */
 int kda_chunk_prefill_backward(const void* q, const void* k, const void* v,
                                const float* log_alpha, const float* beta, const uint8_t* mask,
-                               const float* init_state, const void* d_o, const float* d_final_state,
+                               const float* init_state, const float* chunk_states,
+                               const void* d_o, const float* d_final_state,
                                float* dq, float* dk, float* dv, float* d_log_alpha, float* d_beta,
                                float* d_init_state, int B, int T, int H, int dk_, int dv_, int dtype,
                                unsigned flags, void* workspace, size_t workspace_bytes, void* stream);

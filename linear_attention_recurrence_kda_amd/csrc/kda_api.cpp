@@ -44,13 +44,17 @@ int kda_last_hip_error(void) { return g_last_hip_error; }
 
 size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return 0;
-  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535) return 0;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
+      !kda::prefill_grid_ok(B, T, H, chunk, false))
+    return 0;
   return kda::prefill_workspace_bytes(B, T, H, dk, dv, chunk, dtype, false);
 }
 
 size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int dv, int chunk, int dtype) {
   if (N < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return 0;
-  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || N > 65535) return 0;
+  if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || N > 65535 ||
+      !kda::prefill_grid_ok(N, T, H, chunk, true))
+    return 0;
   return kda::prefill_workspace_bytes(N, T, H, dk, dv, chunk, dtype, true);
 }
 
@@ -118,6 +122,16 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const float* 
                        B, T, H, dk, dv, chunk, dtype, flags, workspace, workspace_bytes, stream);
 }
 
+int kda_chunk_prefill_states(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, const uint8_t* mask, const float* init_state, void* o,
+                             float* final_state, float* chunk_states, int num_states, int state_interval,
+                             int B, int T, int H, int dk, int dv, int chunk, int dtype, unsigned flags,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, o, final_state, nullptr, 0,
+                       chunk_states, num_states, state_interval, B, T, H, dk, dv, chunk, dtype, flags, workspace,
+                       workspace_bytes, stream);
+}
+
 int kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
                               const float* beta, const uint8_t* mask, const float* init_state, void* o,
                               float* final_state, int B, int T, int H, int dk, int dv, int chunk, int dtype,
@@ -138,23 +152,24 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const 
                        workspace_bytes, stream);
 }
 
-size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
+                                                 int states_given) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype) || !head_dim_ok(dk) || !head_dim_ok(dv) || B > 65535 ||
-      H > 65535 || !kda::prefill_grid_ok(B, T, H, 64, false))
+      H > 65535 || !kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H))
     return 0;
-  return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype);
+  return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype, states_given != 0);
 }
 
 int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
                                const float* beta, const uint8_t* mask, const float* init_state,
-                               const void* d_o, const float* d_final_state, float* dq, float* dk,
+                               const float* chunk_states, const void* d_o, const float* d_final_state, float* dq, float* dk,
                                float* dv, float* d_log_alpha, float* d_beta, float* d_init_state,
                                int B, int T, int H, int dk_, int dv_, int dtype, unsigned flags,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if (flags != 0) return KDA_ERR_UNSUPPORTED;
   if (!head_dim_ok(dk_) || !head_dim_ok(dv_) || B > 65535 || H > 65535) return KDA_ERR_UNSUPPORTED;
-  if (!kda::prefill_grid_ok(B, T, H, 64, false)) return KDA_ERR_UNSUPPORTED;
+  if (!kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H)) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
   if (d_init_state == nullptr || !aligned(d_init_state, 4)) return KDA_ERR_INVALID_ARG;
   if (init_state != nullptr && !aligned(init_state, 16)) return KDA_ERR_INVALID_ARG;
@@ -167,11 +182,13 @@ int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, cons
     for (const void* ptr : a16)
       if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
     if (!aligned(beta, 4) || !aligned(d_beta, 4)) return KDA_ERR_INVALID_ARG;
+    // the chunk-end states are read with 16-byte vector loads
+    if (chunk_states != nullptr && !aligned(chunk_states, 16)) return KDA_ERR_INVALID_ARG;
   }
-  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype);
+  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return KDA_ERR_WORKSPACE;
-  kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, mask,
+  kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, mask, chunk_states,
                       dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype,
                       workspace, stream};
   return hip_status(kda::launch_backward(a));

@@ -521,9 +521,13 @@ struct ScanOps {
 };
 
 // NH = 2: the workgroup takes 32 dv columns as two 16-column halves, so each chunk's
-// operands, the dominant per-step traffic of the CU, serve twice the columns
+// operands, the dominant per-step traffic of the CU, serve twice the columns.  At
+// dk = dv = 128 (bf16) that instance is held to 256 registers so that two workgroups share
+// a CU (a 4-register spill outside the chunk loop; the other shapes spill far more under
+// that bound and keep the compiler's choice)
 template <int DT, int KP, int V, int NH>
-__global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads, (DT == 0 && KP == 128 && V == 128 && NH == 2) ? 2 : 1)
+    bwd_scan_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
   using Ops = ScanOps<DT, KP, NH>;
@@ -537,7 +541,12 @@ __global__ void __launch_bounds__(kThreads) bwd_scan_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) __bf16 s_du[2][TW * LR];
   __shared__ __attribute__((aligned(16))) __bf16 s_do[2][TW * LR];
 
-  const int vt = blockIdx.x % NT, bh = blockIdx.x / NT, b = bh / p.H, h = bh % p.H;
+  // XCD-aware mapping: the NT column tiles of one (b, h) share blockIdx.x % 8, so they run
+  // on one XCD and read each chunk's operands through one L2
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int bh = (slot / NT) * 8 + xcd, vt = slot % NT;
+  if (bh >= p.B * p.H) return;
+  const int b = bh / p.H, h = bh % p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, v0 = TW * vt;
 
@@ -1133,7 +1142,14 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float s_dG[kC * LC];
   __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW];
 
-  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y, c_base = SW * blockIdx.z;
+  // XCD-aware mapping: the KP / SW channel slices of one chunk share blockIdx.x % 8 and are
+  // dispatched 8 blocks apart, so dP, dG and the row data come from one L2
+  constexpr int NS = KP / SW;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const long long cid = (long long)(slot / NS) * 8 + xcd;       // (b * NC + n) * H + h
+  if (cid >= (long long)p.B * p.NC * p.H) return;
+  const int bn = (int)(cid / p.H), h = (int)(cid % p.H), b = bn / p.NC, n = bn % p.NC;
+  const int c_base = SW * (slot % NS);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
   const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
@@ -1333,8 +1349,11 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- host side
+// The chunk operands and gradients first, then what running the forward again needs (its
+// workspace, its discarded outputs and the chunk-end states): `own` bytes suffice when the
+// caller hands the states in.
 struct Layout {
-  size_t fwd, o, fin, ck, kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, Y, ss, total;
+  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, Y, ss, own, fwd, o, fin, ck, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1346,10 +1365,6 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype) {
   const size_t nch = (size_t)B * H * NC, parts = dtype == 1 ? 2 : 1, es = dtype == 1 ? 4 : 2;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
-  L.fwd = take(prefill_workspace_bytes(B, T, H, dk, dv, kC, dtype, false));
-  L.o = take((size_t)B * T * H * dv * es);
-  L.fin = take((size_t)B * H * dk * dv * 4);
-  L.ck = take((size_t)B * NCf * H * dk * dv * 4);
   L.kh = take(nch * kC * KP * 2 * parts);
   L.wt = take(nch * kC * KP * 2 * parts);
   L.qt = take(nch * kC * KP * 2 * parts);
@@ -1365,6 +1380,11 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype) {
   L.dG = take(nch * kC * kC * 4);
   L.Y = take(nch * 3 * kC * KP * 4);
   L.ss = take(nch * KP * 4);
+  L.own = off;
+  L.fwd = take(prefill_workspace_bytes(B, T, H, dk, dv, kC, dtype, false));
+  L.o = take((size_t)B * T * H * dv * es);
+  L.fin = take((size_t)B * H * dk * dv * 4);
+  L.ck = take((size_t)B * NCf * H * dk * dv * 4);
   L.total = off;
   return L;
 }
@@ -1379,11 +1399,12 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   }
   // 32-column scan workgroups (bf16) once there are enough (b, h) pairs to fill the chip with them
   constexpr bool kWideOk = DT == 0 && V >= 32;
+  const int groups = (p.B * p.H + 7) / 8;
   if (kWideOk && p.B * p.H >= 64)
-    hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V, kWideOk ? 2 : 1>), dim3(p.B * p.H * (V / 32)), dim3(kThreads), 0,
-                       st, p);
+    hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V, kWideOk ? 2 : 1>), dim3(groups * 8 * (V / 32)), dim3(kThreads),
+                       0, st, p);
   else
-    hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V, 1>), dim3(p.B * p.H * (V / 16)), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((bwd_scan_kernel<DT, KP, V, 1>), dim3(groups * 8 * (V / 16)), dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.NC == 0) return e;
   hipLaunchKernelGGL((bwd_cc_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
@@ -1392,7 +1413,9 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_cy_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_ck_kernel<DT, KP, V>), dim3(p.NC * p.H, p.B, KP / kCkSlice), dim3(kThreads), 0, st, p);
+  const long long cgroups = ((long long)p.B * p.NC * p.H + 7) / 8;
+  hipLaunchKernelGGL((bwd_ck_kernel<DT, KP, V>), dim3((unsigned)(cgroups * 8 * (KP / kCkSlice))), dim3(kThreads), 0,
+                     st, p);
   return hipGetLastError();
 }
 
@@ -1410,15 +1433,27 @@ hipError_t launch_dt(const Params& p, hipStream_t st) {
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype) {
-  return layout(B, T, H, dk, dv, dtype).total;
+// the x extent of every backward launch in threads fits 32 bits (the forward's own grids are
+// checked by prefill_grid_ok): the chunk-local grid (H ceil(T/64) workgroups), the scan
+// (B H rounded up to 8, times up to 8 column tiles) and the channel-slice grid (B H ceil(T/64)
+// rounded up to 8, times up to 4 slices)
+bool backward_grid_ok(int B, int T, int H) {
+  const long long kMax = 0xffffffffll, NC = T > 0 ? ((long long)T + kC - 1) / kC : 0;
+  const long long nbh = (long long)B * H, chunks = nbh * NC;
+  return NC * H * kThreads <= kMax && (nbh + 7) / 8 * 8 * 8 * kThreads <= kMax &&
+         (chunks + 7) / 8 * 8 * (128 / kCkSlice) * kThreads <= kMax;
+}
+
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given) {
+  const Layout L = layout(B, T, H, dk, dv, dtype);
+  return states_given ? L.own : L.total;
 }
 
 hipError_t launch_backward(const BackwardArgs& a) {
   const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype);
   unsigned char* ws = (unsigned char*)a.workspace;
   const int NC = a.T > 0 ? (a.T + kC - 1) / kC : 0, NCf = a.T / kC;
-  if (a.T > 0) {
+  if (a.T > 0 && a.chunk_states == nullptr) {
     // the forward pass again, keeping the state at every chunk end
     PrefillArgs f{};
     f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.beta = a.beta; f.mask = a.mask;
@@ -1447,7 +1482,7 @@ hipError_t launch_backward(const BackwardArgs& a) {
     p.w.dS1 = (float*)(ws + L.dS1); p.w.dU = (float*)(ws + L.dU); p.w.U = (float*)(ws + L.U);
     p.w.dP = (float*)(ws + L.dP); p.w.dG = (float*)(ws + L.dG);
     p.w.Y = (float*)(ws + L.Y); p.w.ss = (float*)(ws + L.ss);
-    p.w.ck = (const float*)(ws + L.ck);
+    p.w.ck = a.chunk_states != nullptr ? a.chunk_states : (const float*)(ws + L.ck);
   }
   p.B = a.B; p.T = a.T; p.H = a.H; p.K = a.dk_; p.V = a.dv_; p.NC = NC; p.NCf = NCf;
   hipStream_t st = (hipStream_t)a.stream;

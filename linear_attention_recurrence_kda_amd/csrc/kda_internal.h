@@ -68,6 +68,8 @@ struct BackwardArgs {
   const void *q, *k, *v, *dout;
   const float *log_alpha, *beta, *init_state, *dfinal;
   const uint8_t* mask;
+  const float* chunk_states;               // the forward's state at every 64-token chunk end, or
+                                           // null (the forward runs again inside the call)
   float *dq, *dk, *dv, *dla, *dbeta, *dinit;
   int B, T, H, dk_, dv_, dtype;
   void* workspace;
@@ -76,7 +78,9 @@ struct BackwardArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given);
+// every backward launch's grid fits (the forward inside it is checked by prefill_grid_ok)
+bool backward_grid_ok(int B, int T, int H);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
@@ -87,7 +91,7 @@ hipError_t noalloc_scratch(void** ptr);
 // varlen: B packed sequences of T tokens in total (cu_seqlens given)
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen);
 bool prefill_supported(int dk, int dv, int chunk);
-// the chunk-local kernel's grid: H times the number of chunks below 2^31
+// every prefill launch's grid fits: H times the chunks, and the scan's B*H workgroup rows
 bool prefill_grid_ok(int B, int T, int H, int chunk, bool varlen);
 
 }  // namespace kda

@@ -1395,8 +1395,13 @@ static long long prefill_chunks(int B, int T, int chunk, bool varlen) {
   return varlen ? nc + B : nc;
 }
 
+// a launch's x extent in threads is a 32-bit number: the chunk-local grid holds H times the
+// chunks workgroups, the scan (B*H rounded up to 8) times up to dv / 16 = 8 column tiles
 bool prefill_grid_ok(int B, int T, int H, int chunk, bool varlen) {
-  return prefill_chunks(B, T, chunk, varlen) * H <= 0x7fffffffll;
+  const long long kMax = 0xffffffffll;
+  const long long nbh = (long long)B * H;
+  return prefill_chunks(B, T, chunk, varlen) * H * kPrepThreads <= kMax &&
+         (nbh + 7) / 8 * 8 * 8 * kScanThreads <= kMax;
 }
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }

@@ -22,7 +22,8 @@ EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
            "kda_chunk_prefill_workspace_size", "kda_chunk_prefill", "kda_decode_step",
            "kda_short_conv", "kda_decode_step_fused", "kda_chunk_prefill_varlen_workspace_size",
            "kda_chunk_prefill_varlen", "kda_chunk_prefill_noalloc", "kda_noalloc_scratch_bytes",
-           "kda_chunk_prefill_backward_workspace_size", "kda_chunk_prefill_backward")
+           "kda_chunk_prefill_backward_workspace_size", "kda_chunk_prefill_backward",
+           "kda_chunk_prefill_states")
 
 _lib = None
 
@@ -76,10 +77,13 @@ def load():
     lib.kda_noalloc_scratch_bytes.restype = sz
     lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_chunk_prefill_backward_workspace_size.restype = sz
-    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.kda_chunk_prefill_backward.restype = i
-    lib.kda_chunk_prefill_backward.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+    lib.kda_chunk_prefill_backward.argtypes = [vp, vp, vp, fp, fp, up, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
                                                i, i, i, i, i, i, u, vp, sz, vp]
+    lib.kda_chunk_prefill_states.restype = i
+    lib.kda_chunk_prefill_states.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp, fp, i, i,
+                                             i, i, i, i, i, i, i, u, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -131,6 +135,37 @@ def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk
     """KDA prefill.  q,k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32), log_alpha [B,T,H,dk] fp32,
     beta [B,T,H] fp32, mask [B,T] uint8/bool or None, initial_state [B,H,dk,dv] fp32 or None.
     Returns (o [B,T,H,dv] in q's dtype, final_state [B,H,dk,dv] fp32)."""
+    o, fin, _ = _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2norm_qk,
+                               out, final_state, workspace, scalar_gate, None, 0)
+    return o, fin
+
+
+def chunk_prefill_states(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
+                         state_interval=64, chunk_states=None, l2norm_qk=False, out=None,
+                         final_state=None, workspace=None, scalar_gate=False):
+    """kda_chunk_prefill_states: chunk_prefill that also returns the state after every
+    state_interval tokens of each row, chunk_states [B * (T // state_interval), H, dk, dv] fp32
+    (row b's j-th state at entry b * (T // state_interval) + j - 1; a given array with fewer
+    entries receives those that fit).  With state_interval = 64
+    these are the chunk-end states chunk_prefill_backward takes.  Returns (o, final_state,
+    chunk_states)."""
+    import torch
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if state_interval <= 0:
+        raise ValueError("state_interval must be positive")
+    n = B * (T // state_interval)
+    if chunk_states is None:
+        chunk_states = torch.empty((n, H, dk, dv), dtype=torch.float32, device=q.device)
+    _req(chunk_states, "chunk_states", torch.float32)
+    if chunk_states.dim() != 4 or tuple(chunk_states.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"chunk_states must be [M,{H},{dk},{dv}], got {tuple(chunk_states.shape)}")
+    return _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2norm_qk, out,
+                          final_state, workspace, scalar_gate, chunk_states, int(state_interval))
+
+
+def _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2norm_qk, out,
+                   final_state, workspace, scalar_gate, chunk_states, state_interval):
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -157,14 +192,21 @@ def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
-                               _ptr(initial_state), _ptr(out), _ptr(final_state),
-                               B, T, H, dk, dv, int(chunk_size), dt,
-                               (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
-                               (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
-                               _ptr(workspace), wbytes, _stream())
-    _check("kda_chunk_prefill", st)
-    return out, final_state
+    flags = (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_SCALAR_GATE if scalar_gate else 0)
+    if chunk_states is None:
+        st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                                   _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                   B, T, H, dk, dv, int(chunk_size), dt, flags,
+                                   _ptr(workspace), wbytes, _stream())
+        _check("kda_chunk_prefill", st)
+    else:
+        st = lib.kda_chunk_prefill_states(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
+                                          _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(chunk_states),
+                                          chunk_states.shape[0], state_interval,
+                                          B, T, H, dk, dv, int(chunk_size), dt, flags,
+                                          _ptr(workspace), wbytes, _stream())
+        _check("kda_chunk_prefill_states", st)
+    return out, final_state, chunk_states
 
 
 def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
@@ -203,17 +245,21 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
     return out, final_state
 
 
-def backward_workspace_size(B, T, H, dk, dv, dtype_code):
-    """Bytes of workspace kda_chunk_prefill_backward needs."""
-    return int(load().kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dtype_code))
+def backward_workspace_size(B, T, H, dk, dv, dtype_code, states_given=False):
+    """Bytes of workspace kda_chunk_prefill_backward needs (less when the chunk-end states
+    are given)."""
+    return int(load().kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dtype_code,
+                                                                int(bool(states_given))))
 
 
 def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, mask=None,
-                           initial_state=None, workspace=None):
+                           initial_state=None, workspace=None, chunk_states=None):
     """Gradients of chunk_prefill for L = sum <d_o, o> + <d_final_state, final_state>.
     Inputs as for chunk_prefill (no flags); d_o [B,T,H,dv] in q's dtype, d_final_state
-    [B,H,dk,dv] fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha,
-    dbeta (shapes of the inputs) and dinit_state [B,H,dk,dv]."""
+    [B,H,dk,dv] fp32 or None.  chunk_states: the states chunk_prefill_states wrote for the
+    same inputs with state_interval = 64, or None (the forward then runs again inside the
+    call).  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, dbeta (shapes of the
+    inputs) and dinit_state [B,H,dk,dv]."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -233,16 +279,18 @@ def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, ma
         _req(initial_state, "initial_state", torch.float32, (B, H, dk, dv))
     if d_final_state is not None:
         _req(d_final_state, "d_final_state", torch.float32, (B, H, dk, dv))
+    if chunk_states is not None:
+        _req(chunk_states, "chunk_states", torch.float32, (B * (T // 64), H, dk, dv))
     f32 = dict(dtype=torch.float32, device=q.device)
     g = {"dq": torch.empty(B, T, H, dk, **f32), "dk": torch.empty(B, T, H, dk, **f32),
          "dv": torch.empty(B, T, H, dv, **f32), "dlog_alpha": torch.empty(B, T, H, dk, **f32),
          "dbeta": torch.empty(B, T, H, **f32), "dinit_state": torch.empty(B, H, dk, dv, **f32)}
-    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt))
+    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt, int(chunk_states is not None)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
-                                        _ptr(initial_state), _ptr(d_o), _ptr(d_final_state),
+                                        _ptr(initial_state), _ptr(chunk_states), _ptr(d_o), _ptr(d_final_state),
                                         _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
                                         _ptr(g["dbeta"]), _ptr(g["dinit_state"]), B, T, H, dk, dv, dt, 0,
                                         _ptr(workspace), wbytes, _stream())

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert lib.kda_status_string(code).decode().startswith(kda.STATUS[code])
     assert lib.kda_status_string(17) == b"unknown kda_status"
@@ -111,8 +111,16 @@ def test_prefill_validation(lib):
     assert _prefill(lib, dk=100) == UNSUPPORTED
     assert _prefill(lib, H=65536) == UNSUPPORTED
     assert _prefill(lib, B=65536) == UNSUPPORTED
-    # the chunk-local grid holds H x chunks workgroups: at most 2^31 - 1
+    # launch extents in threads fit 32 bits: H x chunks workgroups of 256 threads (< 2^24),
+    # and the scan's B*H rows rounded up to 8 times 8 tiles of 512 threads (B*H <= 2^20 - 8)
     assert _prefill(lib, T=1 << 30, H=256, chunk=64) == UNSUPPORTED
+    # (no workspace given: a supported size stops at the workspace check, before any HIP call)
+    assert _prefill(lib, T=64 * ((1 << 19) - 1), H=32, ws=None) == WORKSPACE
+    assert _prefill(lib, T=64 * (1 << 19), H=32, ws=None) == UNSUPPORTED
+    assert lib.kda_chunk_prefill_workspace_size(1, 64 * ((1 << 19) - 1), 32, 128, 128, 64, 0) > 0
+    assert lib.kda_chunk_prefill_workspace_size(1, 64 * (1 << 19), 32, 128, 128, 64, 0) == 0
+    assert _prefill(lib, B=32767, H=32, ws=None) == WORKSPACE
+    assert _prefill(lib, B=32768, H=32, ws=None) == UNSUPPORTED
     assert _prefill(lib, T=-3) == INVALID
     assert _prefill(lib, dtype=2) == INVALID
     assert _prefill(lib, flags=2) == INVALID            # SILU belongs to the short conv
@@ -159,11 +167,35 @@ def _varlen(lib, **kw):
                                         a["chunk"], a["dtype"], a["flags"], a["ws"], a["wsb"], None)
 
 
+def test_prefill_states_validation(lib):
+    """kda_chunk_prefill_states: the batch prefill's checks plus those of the state
+    checkpoints (a positive multiple of chunk, a 4-byte aligned array, a capacity >= 0); each
+    valid case stops at the short workspace, before any HIP call."""
+    def call(**kw):
+        a = dict(ck=FAKE, nck=4, every=64, B=1, T=256, H=2, chunk=64, wsb=64, flags=0)
+        a.update(kw)
+        return lib.kda_chunk_prefill_states(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                                            a["ck"], a["nck"], a["every"], a["B"], a["T"], a["H"],
+                                            128, 128, a["chunk"], 0, a["flags"], FAKE, a["wsb"], None)
+    assert call() == WORKSPACE
+    assert call(ck=None) == WORKSPACE                   # no checkpoints: the plain prefill
+    assert call(every=0) == INVALID
+    assert call(every=96) == INVALID
+    assert call(every=48, chunk=32) == INVALID
+    assert call(every=96, chunk=32) == WORKSPACE
+    assert call(nck=-1) == INVALID
+    assert call(ck=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(chunk=128) == UNSUPPORTED
+    assert call(flags=2) == INVALID
+    assert call(B=0) == OK
+
+
 def test_prefill_varlen_validation(lib):
     assert _varlen(lib, chunk=48) == UNSUPPORTED
     assert _varlen(lib, dv=8) == UNSUPPORTED
     assert _varlen(lib, N=65536) == UNSUPPORTED
-    # H x (ceil(T / chunk) + N) chunk workgroups must stay below 2^31
+    # H x (ceil(T / chunk) + N) chunk workgroups of 256 threads must stay below 2^24
+    assert lib.kda_chunk_prefill_varlen_workspace_size(1000, 64 * ((1 << 19) - 1000), 32, 128, 128, 64, 0) == 0
     assert _varlen(lib, T=(1 << 29) - 64 * 1000, N=1000, H=256, chunk=64) == UNSUPPORTED
     assert _varlen(lib, N=-1) == INVALID
     assert _varlen(lib, T=-1) == INVALID
@@ -295,20 +327,24 @@ def test_large_chunks_are_rejected(lib):
 def test_backward_validation(lib):
     """kda_chunk_prefill_backward rejects bad arguments before any HIP call: flags other
     than 0, unsupported head sizes, missing or misaligned pointers, a short workspace."""
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128, 0) == 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128, 0) == 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 64, 64, 7) == 0
-    bf = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0)
-    f32 = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 1)
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128, 0, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128, 0, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 64, 64, 7, 0) == 0
+    bf = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0)
+    f32 = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 1, 0)
     assert 0 < bf < f32
+    # with the chunk-end states given, the forward's workspace, outputs and states drop out
+    bf_s = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 1)
+    fwd = lib.kda_chunk_prefill_workspace_size(2, 130, 3, 64, 32, 64, 0)
+    assert 0 < bf_s <= bf - fwd - 2 * 130 * 3 * 32 * 2 - 2 * 3 * 64 * 32 * 4 - 2 * 2 * 3 * 64 * 32 * 4
     # the chunk operands alone: 2 * 3 * 3 chunks of them
     assert bf > 2 * 3 * 3 * (3 * 64 * 64 * 2 + 64 * 64 * 4 + 6 * 64 * 64 * 4 + 64 * 32 * 4 * 3)
 
     def call(**kw):
         a = dict(B=1, T=33, H=2, dk=64, dv=64, dtype=0, flags=0, q=FAKE, dq=FAKE, s0=None, dinit=FAKE,
-                 ws=FAKE, wsb=1 << 30)
+                 ws=FAKE, wsb=1 << 30, cs=None)
         a.update(kw)
-        return lib.kda_chunk_prefill_backward(a["q"], FAKE, FAKE, FAKE, FAKE, None, a["s0"], FAKE, None,
+        return lib.kda_chunk_prefill_backward(a["q"], FAKE, FAKE, FAKE, FAKE, None, a["s0"], a["cs"], FAKE, None,
                                               a["dq"], FAKE, FAKE, FAKE, FAKE, a["dinit"],
                                               a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
                                               a["flags"], a["ws"], a["wsb"], None)
@@ -322,7 +358,16 @@ def test_backward_validation(lib):
     assert call(dq=MISALIGNED) == INVALID
     assert call(s0=MISALIGNED) == INVALID
     assert call(dinit=None) == INVALID
+    assert call(cs=MISALIGNED) == INVALID     # chunk-end states: 16-byte vector loads
+    assert call(cs=ctypes.c_void_p(0x10008)) == INVALID
+    assert call(cs=FAKE, ws=None) == WORKSPACE
     assert call(ws=None) == WORKSPACE
     assert call(wsb=16) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE   # 256-byte alignment
     assert call(H=0) == OK                   # nothing to do: no HIP call either
+    # launch extents in threads fit 32 bits: B*H*ceil(T/64) <= 2^22 - 8 for the channel-slice grid
+    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1023, 64, 128, 128, 0, 0) > 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 1) == 0
+    assert call(B=64, T=64 * 1023, H=64, ws=None) == WORKSPACE
+    assert call(B=64, T=64 * 1024, H=64, ws=None) == UNSUPPORTED
