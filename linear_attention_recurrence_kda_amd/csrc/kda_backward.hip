@@ -749,8 +749,16 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float s_U[kC * LS];    // ... of U
   __shared__ __attribute__((aligned(16))) float s_dU[kC * LS];   // ... of dU
   __shared__ __attribute__((aligned(16))) float s_M[kC * LC];
-  __shared__ __attribute__((aligned(16))) float s_dT[kC * LC];
-  __shared__ __attribute__((aligned(16))) float s_X[kC * LC];
+  // dT' and X (after the slab loop); during the loop the same bytes hold the slab of S0 as
+  // split bf16 pairs, column-major ([column][k], k padded by 8): staged once per workgroup
+  // with 16-byte loads and read as MFMA B operands by every wave
+  constexpr int LK = KP + 8;
+  static_assert(2 * 32 * LK * 2 <= 2 * kC * LC * 4, "the S0 slab does not fit the dT'/X region");
+  __shared__ __attribute__((aligned(16))) float s_tx[2 * kC * LC];
+  float* const s_dT = s_tx;
+  float* const s_X = s_tx + kC * LC;
+  __bf16* const s_Sh = reinterpret_cast<__bf16*>(s_tx);
+  __bf16* const s_Sl = s_Sh + 32 * LK;
   __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC], s_db[kC];
 
   const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
@@ -798,20 +806,25 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
 #pragma unroll
   for (int J = 0; J < 4; ++J) { dT[J] = zero4(); dPa[J] = zero4(); }
 
+  constexpr int SQ = KP * 8 / kThreads;           // float4 loads per thread of one S0 slab
 #pragma unroll
   for (int vs = 0; vs < VS; ++vs) {
-    // ---- loads of the slab: S0 columns (B operand of Kt S0), V, dU, dO rows
-    float sv[2][KS][8], vv[2][4], duv[2][4];
+    // ---- loads of the slab: S0 rows (KP x 32, 8 float4 per row), V, dU, dO rows; the
+    //      addresses are clamped in range and the values selected, so no load is conditional
+    float4 s4[SQ];
+    float vv[2][4], duv[2][4];
+#pragma unroll
+    for (int j = 0; j < SQ; ++j) {
+      const int idx = tid + kThreads * j, row = idx >> 3, vc = 32 * vs + 4 * (idx & 7);
+      const int vcc = vc < V ? vc : 0;
+      const float* src = S0 != nullptr ? S0 + (size_t)(row < p.K ? row : 0) * V + vcc : dUg + vcc;
+      const float4 x = *reinterpret_cast<const float4*>(src);
+      const bool ok = S0 != nullptr && row < p.K && vc < V;
+      s4[j] = ok ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int vc = 32 * vs + 16 * t2 + col, vcs = vc < V ? vc : 0;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = 32 * ks + cg + e;
-          sv[t2][ks][e] = S0 != nullptr ? S0[(size_t)(c < p.K ? c : 0) * V + vcs] : 0.f;
-        }
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[t2][i] = E::ld((const Tp*)p.v, tokc(16 * w + 4 * g4 + i) * V + vcs);
     }
@@ -825,6 +838,20 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
     }
     float dov[8];
     E::ld8((const Tp*)p.dout, tokc(r) * V + (32 * vs + cg < V ? 32 * vs + cg : 0), dov);
+    // ---- the S0 slab split into LDS (the previous slab's readers passed the loop's last barrier)
+#pragma unroll
+    for (int j = 0; j < SQ; ++j) {
+      const int idx = tid + kThreads * j, row = idx >> 3, c4 = 4 * (idx & 7);
+      float x[8] = {s4[j].x, s4[j].y, s4[j].z, s4[j].w, 0.f, 0.f, 0.f, 0.f};
+      bf16x8 hv, lv;
+      split8(x, hv, lv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s_Sh[(c4 + e) * LK + row] = hv[e];
+        s_Sl[(c4 + e) * LK + row] = lv[e];
+      }
+    }
+    __syncthreads();
     // ---- R slab, row tile w
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
@@ -832,10 +859,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sv[t2][ks][e] = (32 * ks + cg + e < p.K) ? sv[t2][ks][e] : 0.f;
-        bf16x8 bh, bl;
-        split8(sv[t2][ks], bh, bl);
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&s_Sh[(16 * t2 + col) * LK + 32 * ks + cg]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&s_Sl[(16 * t2 + col) * LK + 32 * ks + cg]);
         acc = mma<false>(kth[ks], ktl[ks], bh, bl, acc);
       }
 #pragma unroll
@@ -1125,21 +1150,25 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cy_kernel(Params p) {
 // Every term here is separable by key channel, so a workgroup takes a slice of 32 channels
 // and wave w channel tile w%2 of it over rows 32 (w/2) .. +31 (two row tiles): each lane
 // holds the rows of one channel, and the reverse sum over rows for dlog_alpha is lane
-// shuffles plus one exchange between the two halves.  dP and dG are staged in LDS (their
-// transposes are read from there by column).  About 70 KB of LDS.
+// shuffles plus one exchange between the two halves.  dP and dG are staged in LDS as packed
+// lower triangles (both are zero above the diagonal; their transposes are read from there by
+// column): about 53 KB of LDS, three workgroups per CU.
 constexpr int kCkSlice = 32;
+constexpr int kTri = kC * (kC + 1) / 2;
+// entry (i, j), j <= i, of a packed lower-triangular C x C matrix
+__device__ __forceinline__ int tix(int i, int j) { return i * (i + 1) / 2 + j; }
 
 template <int DT, int KP, int V>
-__global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
+__global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  constexpr int SW = kCkSlice, LD = SW + 2, LC = kC + 2, CT = KP / 16;
+  constexpr int SW = kCkSlice, LD = SW + 2, CT = KP / 16;
   __shared__ __attribute__((aligned(16))) float s_a[kC * LD];    // Kt, or k on the exact path
   __shared__ __attribute__((aligned(16))) float s_b[kC * LD];    // Ki (fast path)
   __shared__ __attribute__((aligned(16))) float s_c[kC * LD];    // Qt, or q on the exact path
   __shared__ __attribute__((aligned(16))) float s_g[kC * LD];    // g (log2)
-  __shared__ __attribute__((aligned(16))) float s_dP[kC * LC];
-  __shared__ __attribute__((aligned(16))) float s_dG[kC * LC];
+  __shared__ __attribute__((aligned(16))) float s_dP[kTri];
+  __shared__ __attribute__((aligned(16))) float s_dG[kTri];
   __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW];
 
   // XCD-aware mapping: the KP / SW channel slices of one chunk share blockIdx.x % 8 and are
@@ -1160,7 +1189,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
   };
 
   {
-    // dP and dG into LDS (4096 values each, 16 per thread)
+    // dP and dG into LDS (4096 values each, 16 per thread; the lower triangles kept)
     const float4* dPg = reinterpret_cast<const float4*>(p.w.dP + ch * (size_t)(kC * kC));
     const float4* dGg = reinterpret_cast<const float4*>(p.w.dG + ch * (size_t)(kC * kC));
     float4 pv[4], gv[4];
@@ -1169,10 +1198,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int idx = 4 * (tid + j * kThreads), row = idx / kC, cl = idx % kC;
-      *reinterpret_cast<float2*>(&s_dP[row * LC + cl]) = make_float2(pv[j].x, pv[j].y);
-      *reinterpret_cast<float2*>(&s_dP[row * LC + cl + 2]) = make_float2(pv[j].z, pv[j].w);
-      *reinterpret_cast<float2*>(&s_dG[row * LC + cl]) = make_float2(gv[j].x, gv[j].y);
-      *reinterpret_cast<float2*>(&s_dG[row * LC + cl + 2]) = make_float2(gv[j].z, gv[j].w);
+      const float pe[4] = {pv[j].x, pv[j].y, pv[j].z, pv[j].w}, ge[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (cl + e <= row) {
+          s_dP[tix(row, cl + e)] = pe[e];
+          s_dG[tix(row, cl + e)] = ge[e];
+        }
     }
   }
   Rows<DT, SW> R;
@@ -1233,10 +1265,14 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
         const int k0 = 32 * s2 + cg;
         if (s2 <= I / 2) {                           // columns j <= i
           float ap[8], ag[8], bv[8];
-          lds8(&s_dP[ra * LC + k0], ap);
-          lds8(&s_dG[ra * LC + k0], ag);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bv[e] = s_b[(k0 + e) * LD + lc];
+          for (int e = 0; e < 8; ++e) {
+            const bool lo = k0 + e <= ra;
+            const int at = tix(ra, lo ? k0 + e : 0);
+            ap[e] = lo ? s_dP[at] : 0.f;
+            ag[e] = lo ? s_dG[at] : 0.f;
+            bv[e] = s_b[(k0 + e) * LD + lc];
+          }
           bf16x8 bh, bl, hh, ll;
           split8(bv, bh, bl);
           split8(ap, hh, ll);
@@ -1248,8 +1284,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
           float ap[8], ag[8], bq[8], bk[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            ap[e] = s_dP[(k0 + e) * LC + ra];
-            ag[e] = s_dG[(k0 + e) * LC + ra];
+            const bool lo = k0 + e >= ra;
+            const int at = lo ? tix(k0 + e, ra) : 0;
+            ap[e] = lo ? s_dP[at] : 0.f;
+            ag[e] = lo ? s_dG[at] : 0.f;
             bq[e] = s_c[(k0 + e) * LD + lc];
             bk[e] = s_a[(k0 + e) * LD + lc];
           }
@@ -1283,13 +1321,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_ck_kernel(Params p) {
           const float gj = s_g[j * LD + lc];
           if (j <= row) {
             const float wgt = s_a[j * LD + lc] * exp2f(gv - gj);
-            Xq += s_dP[row * LC + j] * wgt;
-            Xk3 += s_dG[row * LC + j] * wgt;
+            Xq += s_dP[tix(row, j)] * wgt;
+            Xk3 += s_dG[tix(row, j)] * wgt;
           }
           if (j >= row) {
             const float d = exp2f(gj - gv);
-            Xk1 += s_dP[j * LC + row] * s_c[j * LD + lc] * d;
-            Xk2 += s_dG[j * LC + row] * s_a[j * LD + lc] * d;
+            Xk1 += s_dP[tix(j, row)] * s_c[j * LD + lc] * d;
+            Xk2 += s_dG[tix(j, row)] * s_a[j * LD + lc] * d;
           }
         }
       }
