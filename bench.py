@@ -39,15 +39,17 @@ BACKWARD_STATES_BYTES_PER_TH = BACKWARD_BYTES_PER_TH + 128 * 128 * 4 // 64
 # scaled by a known-size streaming kernel in the same run (factors 2.0 and 1.0 on this GPU).  A
 # figure is reported only while the kernel sources still hash to what was profiled.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "824fa92e8af04dea", "bytes": 16.322e9},
-    "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "e4ebe6e233fa9d6f", "bytes": 1.087e9},
+    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433", "bytes": 16.322e9},
+    "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
+    # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "15074ac000e6913e", "bytes": 10.574e9},
 }
 
 
 # MFMA counters of the 128k prefill call (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 ...; busy % = busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)),
 # reported only while the kernel sources hash to what was profiled.
-MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "824fa92e8af04dea",
+MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433",
                  "prep_busy_pct": 8.1, "scan_busy_pct": 19.5, "call_busy_pct": 14.5, "issued_flop_per_call": 1.433e12}
 
 
@@ -365,6 +367,7 @@ def main():
         fwd_ms = timed(forward)
         bth = Bb * Tb * H
         bwd_gbs = BACKWARD_STATES_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
+        default_bwd = (Bb == 4 and Tb == 4096)    # the shape the measured traffic was taken on
         bwd_line = {"B": Bb, "T": Tb, "H": H, "dk": dk, "dv": dv, "dtype": "bf16",
                     "ms": bwd_ms, "tokens_per_s": Bb * Tb / (bwd_ms * 1e-3),
                     "forward_states_ms": fst_ms,
@@ -374,7 +377,8 @@ def main():
                     "forward_ms_same_inputs": fwd_ms,
                     "backward_over_forward": bwd_ms / fwd_ms,
                     "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": bwd_gbs / HBM_PEAK_GBS, "traffic": None,
+                                 "frac": bwd_gbs / HBM_PEAK_GBS,
+                                 "traffic": measured_traffic("backward", default_bwd),
                                  "algorithmic_bytes": BACKWARD_STATES_BYTES_PER_TH * bth,
                                  "kernel": "kda_chunk_prefill_backward call with the chunk-end states given "
                                            "(bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck)"}}
