@@ -22,14 +22,15 @@
 // rows at or after t.  Padded and masked rows enter as zero (an identity step) and get zero
 // gradients.
 //
-// The pass runs as five launches on the caller's stream:
-//   1. the forward prefill, saving the state at every chunk end (its own kernels);
-//   2. bwd_prep_kernel, one workgroup per (chunk, head): G, P, M = (I + A)^-1 and W, and the
+// The pass runs as four launches on the caller's stream, after the forward prefill that saves
+// the state at every chunk end (its own kernels) unless the caller hands those states in:
+//   1. bwd_prep_kernel, one workgroup per (chunk, head): G, P, M = (I + A)^-1 and W, and the
 //      reverse scan's operands Kh, W^T, Qt^T and P^T as bf16 MFMA fragments;
-//   3. bwd_scan_kernel, one workgroup per (b, h, 16- or 32-column dv tile), over the chunks
+//   2. bwd_scan_kernel, one workgroup per (b, h, 16- or 32-column dv tile), over the chunks
 //      from the last: dS1 and dU of every chunk, and dinit;
-//   4. bwd_cc_kernel, one workgroup per (chunk, head): R, U, dv, dT', dbeta, dA, dG and dP;
-//   5. bwd_ck_kernel, one workgroup per (chunk, head): dq, dk and dlog_alpha.
+//   3. bwd_cc_kernel, one workgroup per (chunk, head): R, U, dv, dT', dbeta, dA, dG and dP;
+//   4. bwd_ck_kernel, one workgroup per (chunk, head, 32 key channels): the products over dv
+//      (dO S0^T, dR S0^T, U dS1^T) for its channels, then dq, dk and dlog_alpha.
 // Products run on the bf16 MFMA with fp32 operands split into a bf16 high part and residual
 // (three MFMAs per product), except the reverse scan's Kh, W^T and Qt^T, which are single
 // bf16 with bf16 inputs (as the forward scan's Wn, Qt and Kh^T are).  A chunk in which some
@@ -62,8 +63,6 @@ struct Ws {
   uint64_t* vbits;                       // bit r: row r of the chunk is valid (in range, unmasked)
   float *dS1, *dU;                       // dL/dS at the chunk end [KP][V], dL/dU [C][V]
   float *U, *dP, *dG;                    // U [C][V]; dP and dG [C][C]
-  float *Y, *ss;                         // dO S0^T, dR S0^T, U dS1^T [3][C][KP] (fragment order);
-                                         // rowsum(dS1 * S0) [KP]
   const float* ck;                       // forward states at chunk ends [B * NCf][H][K][V]
 };
 
@@ -1028,125 +1027,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
   if (tid < kC && n * kC + tid < p.T) p.dbeta[tok(tid)] = s_ok[tid] != 0.f ? db + s_db[tid] : 0.f;
 }
 
-// ================================================================ 5. products over dv
-// Y1 = dO S0^T, Y2 = dR S0^T and Z = U dS1^T (C x KP each, contraction over dv) and
-// rowsum(dS1 * S0), with dv in 32-column slabs staged through LDS as split bf16 pairs:
-// wave w forms row tile w of all three products for every key-channel tile.  The products
-// are stored in fragment order (tile (I, ct): 64 lanes x 4 values) for bwd_ck_kernel.
-template <int DT, int KP, int V>
-__global__ void __launch_bounds__(kThreads, 2) bwd_cy_kernel(Params p) {
-  using E = Elem<DT>;
-  using Tp = typename E::T;
-  constexpr int CT = KP / 16, VS = (V + 31) / 32, LA = 40;   // slab rows padded to 40 bf16
-  constexpr int NB = (KP * 4 + kThreads - 1) / kThreads;      // B-slab items per thread
-  __shared__ __attribute__((aligned(16))) __bf16 s_a[3][2][kC * LA];   // dO, dR, U (high, residual)
-  __shared__ __attribute__((aligned(16))) __bf16 s_b[2][2][KP * LA];   // S0, dS1 rows (high, residual)
-
-  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 15, g4 = lane >> 4;
-  const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
-  auto tokc = [&](int row) -> size_t {
-    const int t = n * kC + row;
-    return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
-  };
-  const uint64_t vb = p.w.vbits[ch];
-  const float* S0 = entry_state(p, b, h, n);
-  const float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
-  const float* Ug = p.w.U + ch * (size_t)(kC * V);
-
-  f32x4 acc[3][CT];
-#pragma unroll
-  for (int m = 0; m < 3; ++m)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) acc[m][ct] = zero4();
-  float ssp[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) ssp[j] = 0.f;
-
-  for (int vs = 0; vs < VS; ++vs) {
-    // ---- the slab into LDS: A rows (one 8-column piece per thread), B rows (NB pieces)
-    {
-      const int row = tid >> 2, c8 = 8 * (tid & 3), v = 32 * vs + c8;
-      const bool vin = v < V, rok = vin && ((vb >> row) & 1ull) != 0ull;
-      const int vsafe = vin ? v : 0;
-      float a[3][8];
-      E::ld8((const Tp*)p.dout, tokc(row) * V + vsafe, a[0]);
-      gld8(p.dv + tokc(row) * V + vsafe, a[1]);
-      gld8(Ug + row * V + vsafe, a[2]);
-#pragma unroll
-      for (int m = 0; m < 3; ++m) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[m][e] = (m == 2 ? vin : rok) ? a[m][e] : 0.f;
-        bf16x8 hi, lo;
-        split8(a[m], hi, lo);
-        *reinterpret_cast<bf16x8*>(&s_a[m][0][row * LA + c8]) = hi;
-        *reinterpret_cast<bf16x8*>(&s_a[m][1][row * LA + c8]) = lo;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int idx = tid + j * kThreads;
-      if (idx >= KP * 4) continue;
-      const int row = idx >> 2, c8 = 8 * (idx & 3), v = 32 * vs + c8;
-      const bool vin = v < V, sin = vin && S0 != nullptr && row < p.K;
-      float sv[8], dv[8];
-      gld8(S0 != nullptr ? S0 + (size_t)(row < p.K ? row : 0) * V + (vin ? v : 0) : dS1, sv);
-      gld8(dS1 + (size_t)row * V + (vin ? v : 0), dv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = sin ? sv[e] : 0.f;
-        dv[e] = vin ? dv[e] : 0.f;
-        ssp[j] += sv[e] * dv[e];
-      }
-      bf16x8 hi, lo;
-      split8(sv, hi, lo);
-      *reinterpret_cast<bf16x8*>(&s_b[0][0][row * LA + c8]) = hi;
-      *reinterpret_cast<bf16x8*>(&s_b[0][1][row * LA + c8]) = lo;
-      split8(dv, hi, lo);
-      *reinterpret_cast<bf16x8*>(&s_b[1][0][row * LA + c8]) = hi;
-      *reinterpret_cast<bf16x8*>(&s_b[1][1][row * LA + c8]) = lo;
-    }
-    __syncthreads();
-    // ---- row tile w of the three products over the slab
-    bf16x8 ah[3], al[3];
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      ah[m] = *reinterpret_cast<const bf16x8*>(&s_a[m][0][(16 * w + col) * LA + 8 * g4]);
-      al[m] = *reinterpret_cast<const bf16x8*>(&s_a[m][1][(16 * w + col) * LA + 8 * g4]);
-    }
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int br = (16 * ct + col) * LA + 8 * g4;
-      const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&s_b[0][0][br]);
-      const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&s_b[0][1][br]);
-      const bf16x8 dh = *reinterpret_cast<const bf16x8*>(&s_b[1][0][br]);
-      const bf16x8 dl = *reinterpret_cast<const bf16x8*>(&s_b[1][1][br]);
-      acc[0][ct] = mma<DT == 0>(ah[0], al[0], sh, sl, acc[0][ct]);
-      acc[1][ct] = mma<false>(ah[1], al[1], sh, sl, acc[1][ct]);
-      acc[2][ct] = mma<false>(ah[2], al[2], dh, dl, acc[2][ct]);
-    }
-    __syncthreads();
-  }
-  float* Y = p.w.Y + ch * (size_t)(3 * kC * KP);
-#pragma unroll
-  for (int m = 0; m < 3; ++m)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-      *reinterpret_cast<float4*>(Y + (size_t)m * kC * KP + ((w * CT + ct) * 64 + lane) * 4) =
-          make_float4(acc[m][ct][0], acc[m][ct][1], acc[m][ct][2], acc[m][ct][3]);
-  // rowsum(dS1 * S0): the four threads of a row are neighbouring lanes
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    float x = ssp[j];
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    const int idx = tid + j * kThreads;
-    if (idx < KP * 4 && (idx & 3) == 0) p.w.ss[ch * KP + (idx >> 2)] = x;
-  }
-}
-
-// ================================================================ 6. q, k and decay gradients
+// ================================================================ 5. q, k and decay gradients
 // Every term here is separable by key channel, so a workgroup takes a slice of 32 channels
 // and wave w channel tile w%2 of it over rows 32 (w/2) .. +31 (two row tiles): each lane
 // holds the rows of one channel, and the reverse sum over rows for dlog_alpha is lane
@@ -1162,17 +1043,26 @@ template <int DT, int KP, int V>
 __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  constexpr int SW = kCkSlice, LD = SW + 2, CT = KP / 16;
-  __shared__ __attribute__((aligned(16))) float s_a[kC * LD];    // Kt, or k on the exact path
-  __shared__ __attribute__((aligned(16))) float s_b[kC * LD];    // Ki (fast path)
-  __shared__ __attribute__((aligned(16))) float s_c[kC * LD];    // Qt, or q on the exact path
-  __shared__ __attribute__((aligned(16))) float s_g[kC * LD];    // g (log2)
-  __shared__ __attribute__((aligned(16))) float s_dP[kTri];
-  __shared__ __attribute__((aligned(16))) float s_dG[kTri];
-  __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW];
+  constexpr int SW = kCkSlice, LD = SW + 2, VS = (V + 31) / 32, LA = 40;
+  // One LDS region used twice: first for the dv slabs of the products (split bf16 rows of
+  // dO, dR and U, and of S0 and dS1 for this slice's channels, rows padded to LA), then for
+  // Kt, Ki, Qt, g and the packed dP and dG.
+  constexpr int kX = 4 * kC * LD + 2 * kTri;                   // floats
+  constexpr int kYA = kC * LA, kYB = SW * LA;                  // bf16 per part
+  static_assert((3 * 2 * kYA + 2 * 2 * kYB) * 2 <= kX * 4, "the dv slabs do not fit the region");
+  __shared__ __attribute__((aligned(16))) float s_x[kX];
+  float* const s_a = s_x;                  // Kt, or k on the exact path
+  float* const s_b = s_a + kC * LD;        // Ki (fast path)
+  float* const s_c = s_b + kC * LD;        // Qt, or q on the exact path
+  float* const s_g = s_c + kC * LD;        // g (log2)
+  float* const s_dP = s_g + kC * LD;
+  float* const s_dG = s_dP + kTri;
+  __bf16* const s_ya = reinterpret_cast<__bf16*>(s_x);   // [dO, dR, U][high, residual][row][v]
+  __bf16* const s_yb = s_ya + 3 * 2 * kYA;                // [S0, dS1][high, residual][channel][v]
+  __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW], s_ss[SW];
 
   // XCD-aware mapping: the KP / SW channel slices of one chunk share blockIdx.x % 8 and are
-  // dispatched 8 blocks apart, so dP, dG and the row data come from one L2
+  // dispatched 8 blocks apart, so the rows every slice reads (dO, dR, U, dP, dG) come from one L2
   constexpr int NS = KP / SW;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const long long cid = (long long)(slot / NS) * 8 + xcd;       // (b * NC + n) * H + h
@@ -1187,6 +1077,107 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
     const int t = n * kC + row;
     return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
   };
+  const int hw = w >> 1, lc = 16 * (w & 1) + col, c = c_base + lc;   // row half; channel
+  const bool cin = c < p.K;
+
+  // ---- the products over dv for this wave's tiles (rows 32 hw .. +31, channels
+  //      c_base + 16 (w & 1) .. +15), kept in registers in MFMA output order:
+  //      Y1 = dO S0^T, Y2 = dR S0^T and Z = U dS1^T; and rowsum(dS1 * S0) of the slice
+  f32x4 y1a[2], y2a[2], za[2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii) { y1a[ii] = zero4(); y2a[ii] = zero4(); za[ii] = zero4(); }
+  const int bch = tid >> 3, bc = c_base + bch;           // B piece: channel, 4 columns
+  float ssp = 0.f;
+  {
+    const uint64_t vb = p.w.vbits[ch];
+    const float* S0 = entry_state(p, b, h, n);
+    const float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
+    const float* Ug = p.w.U + ch * (size_t)(kC * V);
+    const int arow = tid >> 2, ac8 = 8 * (tid & 3), bc4 = 4 * (tid & 7);   // A piece: row, 8 columns
+    const bool arv = ((vb >> arow) & 1ull) != 0ull;
+    // one slab's loads as they arrive, from addresses clamped in range (no load is
+    // conditional); the next slab's are issued before this one is split into LDS
+    struct Slab {
+      Raw8<DT> dor;
+      float4 dr[2], u[2], sv, dsv;
+    };
+    auto load_slab = [&](int vs, Slab& L) __attribute__((always_inline)) {
+      const int va = 32 * vs + ac8, vas = va < V ? va : 0;
+      L.dor.load((const Tp*)p.dout, tokc(arow) * V + vas);
+      const float4* dr = reinterpret_cast<const float4*>(p.dv + tokc(arow) * V + vas);
+      const float4* u = reinterpret_cast<const float4*>(Ug + arow * V + vas);
+      L.dr[0] = dr[0]; L.dr[1] = dr[1];
+      L.u[0] = u[0]; L.u[1] = u[1];
+      const int vb4 = 32 * vs + bc4, vbs = vb4 < V ? vb4 : 0;
+      L.sv = *reinterpret_cast<const float4*>(S0 != nullptr ? S0 + (size_t)(bc < p.K ? bc : 0) * V + vbs : dS1 + vbs);
+      L.dsv = *reinterpret_cast<const float4*>(dS1 + (size_t)bc * V + vbs);
+    };
+    Slab cur, nxt;
+    load_slab(0, cur);
+#pragma unroll
+    for (int vs = 0; vs < VS; ++vs) {
+      if (vs + 1 < VS) load_slab(vs + 1, nxt);
+      {
+        const int v = 32 * vs + ac8;
+        const bool vin = v < V, rok = vin && arv;
+        float a[3][8];
+        cur.dor.to_float(a[0]);
+        const float4 q4[4] = {cur.dr[0], cur.dr[1], cur.u[0], cur.u[1]};
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          a[1 + m][0] = q4[2 * m].x; a[1 + m][1] = q4[2 * m].y; a[1 + m][2] = q4[2 * m].z; a[1 + m][3] = q4[2 * m].w;
+          a[1 + m][4] = q4[2 * m + 1].x; a[1 + m][5] = q4[2 * m + 1].y;
+          a[1 + m][6] = q4[2 * m + 1].z; a[1 + m][7] = q4[2 * m + 1].w;
+        }
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[m][e] = (m == 2 ? vin : rok) ? a[m][e] : 0.f;
+          bf16x8 hi, lo;
+          split8(a[m], hi, lo);
+          *reinterpret_cast<bf16x8*>(&s_ya[(2 * m) * kYA + arow * LA + ac8]) = hi;
+          *reinterpret_cast<bf16x8*>(&s_ya[(2 * m + 1) * kYA + arow * LA + ac8]) = lo;
+        }
+      }
+      {
+        const int v = 32 * vs + bc4;
+        const bool vin = v < V, sin = vin && S0 != nullptr && bc < p.K;
+        const float4 s4 = cur.sv, d4 = cur.dsv;
+        const float sv[4] = {sin ? s4.x : 0.f, sin ? s4.y : 0.f, sin ? s4.z : 0.f, sin ? s4.w : 0.f};
+        const float dv[4] = {vin ? d4.x : 0.f, vin ? d4.y : 0.f, vin ? d4.z : 0.f, vin ? d4.w : 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ssp += sv[e] * dv[e];
+        split4_to_lds(sv, &s_yb[0 * kYB + bch * LA + bc4], &s_yb[1 * kYB + bch * LA + bc4]);
+        split4_to_lds(dv, &s_yb[2 * kYB + bch * LA + bc4], &s_yb[3 * kYB + bch * LA + bc4]);
+      }
+      __syncthreads();
+      const int br = (16 * (w & 1) + col) * LA + cg;
+      const bf16x8 sh = *reinterpret_cast<const bf16x8*>(&s_yb[0 * kYB + br]);
+      const bf16x8 sl = *reinterpret_cast<const bf16x8*>(&s_yb[1 * kYB + br]);
+      const bf16x8 dsh = *reinterpret_cast<const bf16x8*>(&s_yb[2 * kYB + br]);
+      const bf16x8 dsl = *reinterpret_cast<const bf16x8*>(&s_yb[3 * kYB + br]);
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int ar = (16 * (2 * hw + ii) + col) * LA + cg;
+        bf16x8 ah[3], al[3];
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+          ah[m] = *reinterpret_cast<const bf16x8*>(&s_ya[(2 * m) * kYA + ar]);
+          al[m] = *reinterpret_cast<const bf16x8*>(&s_ya[(2 * m + 1) * kYA + ar]);
+        }
+        y1a[ii] = mma<DT == 0>(ah[0], al[0], sh, sl, y1a[ii]);
+        y2a[ii] = mma<false>(ah[1], al[1], sh, sl, y2a[ii]);
+        za[ii] = mma<false>(ah[2], al[2], dsh, dsl, za[ii]);
+      }
+      __syncthreads();
+      if (vs + 1 < VS) cur = nxt;
+    }
+  }
+  // rowsum(dS1 * S0): the eight threads of a channel are neighbouring lanes
+  ssp += __shfl_xor(ssp, 1, 64);
+  ssp += __shfl_xor(ssp, 2, 64);
+  ssp += __shfl_xor(ssp, 4, 64);
+  if ((tid & 7) == 0) s_ss[bch] = ssp;
 
   {
     // dP and dG into LDS (4096 values each, 16 per thread; the lower triangles kept)
@@ -1228,12 +1219,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
     }
   }
   __syncthreads();
-
-  const int hw = w >> 1, lc = 16 * (w & 1) + col, c = c_base + lc;   // row half; channel
-  const int ct = (c_base >> 4) + (w & 1);                              // channel tile
-  const bool cin = c < p.K;
-  const float* Y = p.w.Y + ch * (size_t)(3 * kC * KP);
-  const float ss = p.w.ss[ch * KP + c];
+  const float ss = s_ss[lc];
 
   const float gl = s_gl[lc];
   float dl[2][4];
@@ -1241,13 +1227,10 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii) {
     const int I = 2 * hw + ii;
-    // ---- the products over dv for tile (I, ct), and the raw k, q of the lane's rows
-    const size_t yo = ((size_t)(I * CT + ct) * 64 + lane) * 4;
-    const float4 y1v = *reinterpret_cast<const float4*>(Y + yo);
-    const float4 y2v = *reinterpret_cast<const float4*>(Y + (size_t)kC * KP + yo);
-    const float4 zv = *reinterpret_cast<const float4*>(Y + (size_t)2 * kC * KP + yo);
-    const float y1[4] = {y1v.x, y1v.y, y1v.z, y1v.w}, y2[4] = {y2v.x, y2v.y, y2v.z, y2v.w};
-    const float z[4] = {zv.x, zv.y, zv.z, zv.w};
+    // ---- the products over dv for tile I, and the raw k, q of the lane's rows
+    const float y1[4] = {y1a[ii][0], y1a[ii][1], y1a[ii][2], y1a[ii][3]};
+    const float y2[4] = {y2a[ii][0], y2a[ii][1], y2a[ii][2], y2a[ii][3]};
+    const float z[4] = {za[ii][0], za[ii][1], za[ii][2], za[ii][3]};
     float kr[4], qr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1391,7 +1374,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
 // workspace, its discarded outputs and the chunk-end states): `own` bytes suffice when the
 // caller hands the states in.
 struct Layout {
-  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, Y, ss, own, fwd, o, fin, ck, total;
+  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, own, fwd, o, fin, ck, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1416,8 +1399,6 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype) {
   L.U = take(nch * kC * dv * 4);
   L.dP = take(nch * kC * kC * 4);
   L.dG = take(nch * kC * kC * 4);
-  L.Y = take(nch * 3 * kC * KP * 4);
-  L.ss = take(nch * KP * 4);
   L.own = off;
   L.fwd = take(prefill_workspace_bytes(B, T, H, dk, dv, kC, dtype, false));
   L.o = take((size_t)B * T * H * dv * es);
@@ -1446,9 +1427,6 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.NC == 0) return e;
   hipLaunchKernelGGL((bwd_cc_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_cy_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long cgroups = ((long long)p.B * p.NC * p.H + 7) / 8;
@@ -1519,7 +1497,6 @@ hipError_t launch_backward(const BackwardArgs& a) {
     p.w.vbits = (uint64_t*)(ws + L.vbits);
     p.w.dS1 = (float*)(ws + L.dS1); p.w.dU = (float*)(ws + L.dU); p.w.U = (float*)(ws + L.U);
     p.w.dP = (float*)(ws + L.dP); p.w.dG = (float*)(ws + L.dG);
-    p.w.Y = (float*)(ws + L.Y); p.w.ss = (float*)(ws + L.ss);
     p.w.ck = a.chunk_states != nullptr ? a.chunk_states : (const float*)(ws + L.ck);
   }
   p.B = a.B; p.T = a.T; p.H = a.H; p.K = a.dk_; p.V = a.dv_; p.NC = NC; p.NCf = NCf;
