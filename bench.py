@@ -41,8 +41,8 @@ BACKWARD_STATES_BYTES_PER_TH = BACKWARD_BYTES_PER_TH + 128 * 128 * 4 // 64
 MEASURED_TRAFFIC = {
     "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
-    # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck
-    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "15074ac000e6913e", "bytes": 10.574e9},
+    # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "802988d6c52fdc61", "bytes": 8.881e9},
 }
 
 
@@ -381,7 +381,7 @@ def main():
                                  "traffic": measured_traffic("backward", default_bwd),
                                  "algorithmic_bytes": BACKWARD_STATES_BYTES_PER_TH * bth,
                                  "kernel": "kda_chunk_prefill_backward call with the chunk-end states given "
-                                           "(bwd_prep, bwd_scan, bwd_cc, bwd_cy, bwd_ck)"}}
+                                           "(bwd_prep, bwd_scan, bwd_cc, bwd_ck)"}}
         del xb, dob, dfb, ob, fsb, ckb, wfb, wsg, wsr
 
     # achievable streaming bandwidth on this GPU: a plain elementwise kernel over 1 GiB
