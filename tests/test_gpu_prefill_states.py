@@ -146,3 +146,31 @@ def test_backward_with_states_of_another_chunk_size(oracle):
     got = kda.chunk_prefill_backward(*args, to_dev(do, "bf16", dev), d_final_state=to_dev(dfinal, dev=dev),
                                      chunk_states=ck)
     _check("chunk-32 states", got, _ref(oracle, inp, do, dfinal), "bf16")
+
+
+@pytest.mark.parametrize("l2,scalar", [(True, False), (False, True)])
+def test_prefill_states_equal_prefix_runs_with_flags(l2, scalar):
+    """With the L2-norm flag or the per-head gate, checkpoint j of each row is bit for bit the
+    final state of kda_chunk_prefill over that row's first j * interval tokens (the chunk
+    boundaries of the prefix and of the whole row coincide)."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv, interval = 2, 320, 2, 64, 64, 128
+    say(f"[case] prefill states vs prefix runs, l2={l2} scalar_gate={scalar}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=46)
+    if scalar:
+        inp["log_alpha"] = np.ascontiguousarray(inp["log_alpha"][..., 0])
+    d = _dev(inp, "bf16", dev)
+    s0 = to_dev(D.np_state(B, H, dk, dv, 0.05, seed=46), dev=dev)
+    _, fin, ck = kda.chunk_prefill_states(*(d[n] for n in INPUTS), initial_state=s0, chunk_size=32,
+                                          state_interval=interval, l2norm_qk=l2, scalar_gate=scalar)
+    per = T // interval
+    for j in range(1, per + 1):
+        L = j * interval
+        pre = {n: x[:, :L].contiguous() for n, x in d.items()}
+        _, sj = kda.chunk_prefill(*(pre[n] for n in INPUTS), initial_state=s0, chunk_size=32,
+                                  l2norm_qk=l2, scalar_gate=scalar)
+        torch.cuda.synchronize()
+        for b in range(B):
+            assert torch.equal(ck[b * per + j - 1], sj[b]), f"row {b} checkpoint {j}"
