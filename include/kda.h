@@ -247,11 +247,11 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v,
 
 /*
  * Bytes of device workspace kda_chunk_prefill_backward needs (0 when none is needed or
- * the arguments would be rejected): states_given != 0 for calls that pass chunk_states
- * (the forward's workspace, outputs and states are then not needed).
+ * the arguments would be rejected): flags as for the call; states_given != 0 for calls that
+ * pass chunk_states (the forward's workspace, outputs and states are then not needed).
  */
 size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
-                                                 int states_given);
+                                                 unsigned flags, int states_given);
 
 /*
  * Gradients of kda_chunk_prefill for training (remio.ai page, KDA section: the model is
@@ -261,7 +261,7 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  * dL/dbeta and dL/dinit_state.  Masked positions get zero gradients and pass the state's
  * gradient through.
  *
- *   q, k, v, log_alpha, beta, mask, init_state   as for kda_chunk_prefill (flags = 0)
+ *   q, k, v, log_alpha, beta, mask, init_state   as for kda_chunk_prefill
  *   chunk_states  [B*floor(T/64),H,dk,dv]  fp32, or NULL: the state at every 64-token
  *                              boundary as kda_chunk_prefill_states writes it with
  *                              state_interval = 64 on the same inputs (any chunk; with
@@ -271,7 +271,7 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  *   d_final_state [B,H,dk,dv]  fp32, or NULL (zero)
  *   dq, dk        [B,T,H,dk]   fp32, written
  *   dv            [B,T,H,dv]   fp32, written
- *   d_log_alpha   [B,T,H,dk]   fp32, written
+ *   d_log_alpha   [B,T,H,dk]   fp32, written ([B,T,H] with KDA_FLAG_SCALAR_GATE)
  *   d_beta        [B,T,H]      fp32, written
  *   d_init_state  [B,H,dk,dv]  fp32, written (also when init_state is NULL: the gradient
  *                              with respect to the zero state)
@@ -282,15 +282,21 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  * and chunk-parallel kernels form the gradients; every sum accumulates in fp32, with
  * MFMA operands split into bf16 high and low parts (single bf16 for the reverse scan's
  * key, query and W operands with bf16 inputs, as in the forward scan).  The workspace
- * holds about 250 KB of chunk operands per (b, h, chunk) at dk = dv = 128 and, without
- * chunk_states, the forward's own workspace, outputs and chunk-end states.
+ * holds about 250 KB of chunk operands per (b, h, chunk) at dk = dv = 128; without
+ * chunk_states, the forward's own workspace, outputs and chunk-end states; with
+ * KDA_FLAG_SCALAR_GATE, the gate on every channel and its per-channel gradient (dk floats
+ * each per token and head).
  *
  * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535, H ceil(T/64) < 2^24, B*H <= 2^20 - 8
  * and B*H*ceil(T/64) <= 2^22 - 8 (launch extents in threads fit 32 bits);
- * flags = 0 (the L2-norm and per-head-gate flags return KDA_ERR_UNSUPPORTED).
- * 16-byte aligned: q, k, v, log_alpha, d_o, init_state, chunk_states, dq, dk, dv,
- * d_log_alpha; 4-byte: beta, d_beta, d_final_state, d_init_state; workspace 256-byte
- * aligned.
+ * flags may hold KDA_FLAG_SCALAR_GATE (Gated DeltaNet's gate, one value per (token, head):
+ * the gate is applied to every channel and its gradient is the sum over the channels, so
+ * the other gradients equal those of a per-channel call fed the broadcast gate bit for bit);
+ * KDA_FLAG_L2NORM_QK returns KDA_ERR_UNSUPPORTED (normalise q and k before the call and
+ * let the caller's autodiff take that step), other bits KDA_ERR_INVALID_ARG.
+ * 16-byte aligned: q, k, v, d_o, init_state, chunk_states, dq, dk, dv, and log_alpha and
+ * d_log_alpha unless KDA_FLAG_SCALAR_GATE is set (then 4-byte); 4-byte: beta, d_beta,
+ * d_final_state, d_init_state; workspace 256-byte aligned.
  * Outputs must not overlap inputs.
  */
 int kda_chunk_prefill_backward(const void* q, const void* k, const void* v,

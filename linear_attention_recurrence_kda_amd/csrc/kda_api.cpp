@@ -153,11 +153,13 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const 
 }
 
 size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
-                                                 int states_given) {
+                                                 unsigned flags, int states_given) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype) || !head_dim_ok(dk) || !head_dim_ok(dv) || B > 65535 ||
-      H > 65535 || !kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H))
+      H > 65535 || !kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H) ||
+      (flags & ~(unsigned)KDA_FLAG_SCALAR_GATE) != 0)
     return 0;
-  return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype, states_given != 0);
+  return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype, states_given != 0,
+                                       (flags & KDA_FLAG_SCALAR_GATE) != 0);
 }
 
 int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -167,7 +169,9 @@ int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, cons
                                int B, int T, int H, int dk_, int dv_, int dtype, unsigned flags,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
-  if (flags != 0) return KDA_ERR_UNSUPPORTED;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
+  if (flags & KDA_FLAG_L2NORM_QK) return KDA_ERR_UNSUPPORTED;      // normalise q and k before the call
+  const bool sg = (flags & KDA_FLAG_SCALAR_GATE) != 0;
   if (!head_dim_ok(dk_) || !head_dim_ok(dv_) || B > 65535 || H > 65535) return KDA_ERR_UNSUPPORTED;
   if (!kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H)) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
@@ -178,18 +182,20 @@ int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, cons
     const void* req[] = {q, k, v, log_alpha, beta, d_o, dq, dk, dv, d_log_alpha, d_beta};
     for (const void* ptr : req)
       if (ptr == nullptr) return KDA_ERR_INVALID_ARG;
-    const void* a16[] = {q, k, v, log_alpha, d_o, dq, dk, dv, d_log_alpha};
+    const void* a16[] = {q, k, v, d_o, dq, dk, dv};
     for (const void* ptr : a16)
       if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    // the per-channel gate and its gradient move in 16-byte vectors; one per head, as scalars
+    if (!aligned(log_alpha, sg ? 4 : 16) || !aligned(d_log_alpha, sg ? 4 : 16)) return KDA_ERR_INVALID_ARG;
     if (!aligned(beta, 4) || !aligned(d_beta, 4)) return KDA_ERR_INVALID_ARG;
     // the chunk-end states are read with 16-byte vector loads
     if (chunk_states != nullptr && !aligned(chunk_states, 16)) return KDA_ERR_INVALID_ARG;
   }
-  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr);
+  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr, sg);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return KDA_ERR_WORKSPACE;
   kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, mask, chunk_states,
-                      dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype,
+                      dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype, sg ? 1 : 0,
                       workspace, stream};
   return hip_status(kda::launch_backward(a));
 }

@@ -1369,17 +1369,61 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------- per-head gate (Gated DeltaNet)
+// With one gate per (token, head) every channel decays alike: the gate is written to every
+// channel, the per-channel pass runs unchanged, and the gate's gradient is the sum of the
+// per-channel ones (the chain rule through the broadcast), taken in a fixed order.
+constexpr int kGateThreads = 256;
+constexpr unsigned kGateMaxBlocks = 1u << 16;     // grid-stride loops past this
+
+__global__ void __launch_bounds__(kGateThreads)
+gate_broadcast_kernel(const float* __restrict__ la, float* __restrict__ out, size_t rows, int K) {
+  const size_t per = (size_t)K / 4, n = rows * per;                       // 4 channels per item
+  for (size_t i = (size_t)blockIdx.x * kGateThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kGateThreads) {
+    const float x = la[i / per];
+    *reinterpret_cast<float4*>(out + 4 * i) = make_float4(x, x, x, x);
+  }
+}
+
+// four threads per row (neighbouring lanes), each summing K/4 channels, then two shuffles;
+// every lane of a wave runs the same number of iterations, so the shuffles stay uniform
+__global__ void __launch_bounds__(kGateThreads)
+gate_reduce_kernel(const float* __restrict__ dla_pc, float* __restrict__ dla, size_t rows, int K) {
+  const int q = K / 4;
+  const size_t stride = (size_t)gridDim.x * kGateThreads;
+  for (size_t base = (size_t)blockIdx.x * kGateThreads; base < rows * 4; base += stride) {
+    const size_t g = base + threadIdx.x, row = g / 4;
+    const int part = (int)(g % 4);
+    float s = 0.f;
+    if (row < rows) {
+      const float* src = dla_pc + row * K + part * q;
+      for (int c = 0; c < q; c += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + c);
+        s += (v.x + v.y) + (v.z + v.w);
+      }
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (row < rows && part == 0) dla[row] = s;
+  }
+}
+
+static unsigned gate_blocks(size_t items) {
+  const size_t b = (items + kGateThreads - 1) / kGateThreads;
+  return (unsigned)(b < kGateMaxBlocks ? b : kGateMaxBlocks);
+}
+
 // ---------------------------------------------------------------- host side
 // The chunk operands and gradients first, then what running the forward again needs (its
 // workspace, its discarded outputs and the chunk-end states): `own` bytes suffice when the
 // caller hands the states in.
 struct Layout {
-  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, own, fwd, o, fin, ck, total;
+  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, lab, dlab, own, fwd, o, fin, ck, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(int B, int T, int H, int dk, int dv, int dtype) {
+Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate) {
   Layout L{};
   if (T <= 0 || B == 0 || H == 0) return L;
   const int KP = kpad(dk), NC = (T + kC - 1) / kC, NCf = T / kC;
@@ -1399,6 +1443,10 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype) {
   L.U = take(nch * kC * dv * 4);
   L.dP = take(nch * kC * kC * 4);
   L.dG = take(nch * kC * kC * 4);
+  if (scalar_gate) {                        // the gate on every channel, and its per-channel gradient
+    L.lab = take((size_t)B * T * H * dk * 4);
+    L.dlab = take((size_t)B * T * H * dk * 4);
+  }
   L.own = off;
   L.fwd = take(prefill_workspace_bytes(B, T, H, dk, dv, kC, dtype, false));
   L.o = take((size_t)B * T * H * dv * es);
@@ -1460,19 +1508,34 @@ bool backward_grid_ok(int B, int T, int H) {
          (chunks + 7) / 8 * 8 * (128 / kCkSlice) * kThreads <= kMax;
 }
 
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given) {
-  const Layout L = layout(B, T, H, dk, dv, dtype);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given,
+                                bool scalar_gate) {
+  const Layout L = layout(B, T, H, dk, dv, dtype, scalar_gate);
   return states_given ? L.own : L.total;
 }
 
 hipError_t launch_backward(const BackwardArgs& a) {
-  const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype);
+  const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype, a.scalar_gate != 0);
   unsigned char* ws = (unsigned char*)a.workspace;
+  hipStream_t st = (hipStream_t)a.stream;
   const int NC = a.T > 0 ? (a.T + kC - 1) / kC : 0, NCf = a.T / kC;
+  const size_t rows = (size_t)a.B * a.T * a.H;
+  // the per-channel gate and dlog_alpha the pass works with
+  const float* la = a.log_alpha;
+  float* dla = a.dla;
+  if (a.scalar_gate && rows > 0) {
+    la = (const float*)(ws + L.lab);
+    dla = (float*)(ws + L.dlab);
+    const size_t n4 = rows * (size_t)(a.dk_ / 4);
+    hipLaunchKernelGGL(gate_broadcast_kernel, dim3(gate_blocks(n4)), dim3(kGateThreads), 0, st, a.log_alpha,
+                       (float*)(ws + L.lab), rows, a.dk_);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (a.T > 0 && a.chunk_states == nullptr) {
     // the forward pass again, keeping the state at every chunk end
     PrefillArgs f{};
-    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.beta = a.beta; f.mask = a.mask;
+    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = la; f.beta = a.beta; f.mask = a.mask;
     f.init_state = a.init_state;
     f.o = ws + L.o;
     f.final_state = (float*)(ws + L.fin);
@@ -1488,8 +1551,8 @@ hipError_t launch_backward(const BackwardArgs& a) {
   }
   Params p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout;
-  p.la = a.log_alpha; p.beta = a.beta; p.init = a.init_state; p.dfinal = a.dfinal; p.mask = a.mask;
-  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = a.dla; p.dbeta = a.dbeta; p.dinit = a.dinit;
+  p.la = la; p.beta = a.beta; p.init = a.init_state; p.dfinal = a.dfinal; p.mask = a.mask;
+  p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = dla; p.dbeta = a.dbeta; p.dinit = a.dinit;
   if (a.T > 0) {
     p.w.kh = (uint16_t*)(ws + L.kh); p.w.wt = (uint16_t*)(ws + L.wt); p.w.qt = (uint16_t*)(ws + L.qt);
     p.w.pt = (uint16_t*)(ws + L.pt);
@@ -1500,8 +1563,11 @@ hipError_t launch_backward(const BackwardArgs& a) {
     p.w.ck = a.chunk_states != nullptr ? a.chunk_states : (const float*)(ws + L.ck);
   }
   p.B = a.B; p.T = a.T; p.H = a.H; p.K = a.dk_; p.V = a.dv_; p.NC = NC; p.NCf = NCf;
-  hipStream_t st = (hipStream_t)a.stream;
-  return a.dtype == 0 ? launch_dt<0>(p, st) : launch_dt<1>(p, st);
+  hipError_t e = a.dtype == 0 ? launch_dt<0>(p, st) : launch_dt<1>(p, st);
+  if (e != hipSuccess || !a.scalar_gate || rows == 0) return e;
+  hipLaunchKernelGGL(gate_reduce_kernel, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st,
+                     (const float*)dla, a.dla, rows, a.dk_);
+  return hipGetLastError();
 }
 
 }  // namespace kda

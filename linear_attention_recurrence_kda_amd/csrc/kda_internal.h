@@ -72,13 +72,15 @@ struct BackwardArgs {
                                            // null (the forward runs again inside the call)
   float *dq, *dk, *dv, *dla, *dbeta, *dinit;
   int B, T, H, dk_, dv_, dtype;
+  int scalar_gate;                         // log_alpha and dla are [B,T,H]: one gate per head
   void* workspace;
   void* stream;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
-size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given);
+size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given,
+                                bool scalar_gate);
 // every backward launch's grid fits (the forward inside it is checked by prefill_grid_ok)
 bool backward_grid_ok(int B, int T, int H);
 hipError_t launch_short_conv(const ConvArgs& a);

@@ -77,7 +77,7 @@ def load():
     lib.kda_noalloc_scratch_bytes.restype = sz
     lib.kda_noalloc_scratch_bytes.argtypes = []
     lib.kda_chunk_prefill_backward_workspace_size.restype = sz
-    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.kda_chunk_prefill_backward_workspace_size.argtypes = [i, i, i, i, i, i, u, i]
     lib.kda_chunk_prefill_backward.restype = i
     lib.kda_chunk_prefill_backward.argtypes = [vp, vp, vp, fp, fp, up, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
                                                i, i, i, i, i, i, u, vp, sz, vp]
@@ -245,20 +245,21 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
     return out, final_state
 
 
-def backward_workspace_size(B, T, H, dk, dv, dtype_code, states_given=False):
+def backward_workspace_size(B, T, H, dk, dv, dtype_code, states_given=False, scalar_gate=False):
     """Bytes of workspace kda_chunk_prefill_backward needs (less when the chunk-end states
-    are given)."""
-    return int(load().kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dtype_code,
-                                                                int(bool(states_given))))
+    are given, more with the per-head gate)."""
+    return int(load().kda_chunk_prefill_backward_workspace_size(
+        B, T, H, dk, dv, dtype_code, KDA_FLAG_SCALAR_GATE if scalar_gate else 0, int(bool(states_given))))
 
 
 def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, mask=None,
-                           initial_state=None, workspace=None, chunk_states=None):
+                           initial_state=None, workspace=None, chunk_states=None, scalar_gate=False):
     """Gradients of chunk_prefill for L = sum <d_o, o> + <d_final_state, final_state>.
     Inputs as for chunk_prefill (no flags); d_o [B,T,H,dv] in q's dtype, d_final_state
     [B,H,dk,dv] fp32 or None.  chunk_states: the states chunk_prefill_states wrote for the
     same inputs with state_interval = 64, or None (the forward then runs again inside the
-    call).  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, dbeta (shapes of the
+    call).  scalar_gate: log_alpha is one gate per (token, head), [B,T,H], and so is its
+    gradient.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, dbeta (shapes of the
     inputs) and dinit_state [B,H,dk,dv]."""
     import torch
     lib = load()
@@ -269,7 +270,7 @@ def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, ma
     _req(k, "k", q.dtype, (B, T, H, dk))
     _req(v, "v", q.dtype, (B, T, H, dv))
     _req(d_o, "d_o", q.dtype, (B, T, H, dv))
-    _req(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _req(log_alpha, "log_alpha", torch.float32, (B, T, H) if scalar_gate else (B, T, H, dk))
     _req(beta, "beta", torch.float32, (B, T, H))
     if mask is not None:
         if mask.dtype == torch.bool:
@@ -283,16 +284,18 @@ def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, ma
         _req(chunk_states, "chunk_states", torch.float32, (B * (T // 64), H, dk, dv))
     f32 = dict(dtype=torch.float32, device=q.device)
     g = {"dq": torch.empty(B, T, H, dk, **f32), "dk": torch.empty(B, T, H, dk, **f32),
-         "dv": torch.empty(B, T, H, dv, **f32), "dlog_alpha": torch.empty(B, T, H, dk, **f32),
+         "dv": torch.empty(B, T, H, dv, **f32),
+         "dlog_alpha": torch.empty(*((B, T, H) if scalar_gate else (B, T, H, dk)), **f32),
          "dbeta": torch.empty(B, T, H, **f32), "dinit_state": torch.empty(B, H, dk, dv, **f32)}
-    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt, int(chunk_states is not None)))
+    flags = KDA_FLAG_SCALAR_GATE if scalar_gate else 0
+    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt, flags, int(chunk_states is not None)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.kda_chunk_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
                                         _ptr(initial_state), _ptr(chunk_states), _ptr(d_o), _ptr(d_final_state),
                                         _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
-                                        _ptr(g["dbeta"]), _ptr(g["dinit_state"]), B, T, H, dk, dv, dt, 0,
+                                        _ptr(g["dbeta"]), _ptr(g["dinit_state"]), B, T, H, dk, dv, dt, flags,
                                         _ptr(workspace), wbytes, _stream())
     _check("kda_chunk_prefill_backward", st)
     return g

@@ -327,14 +327,14 @@ def test_large_chunks_are_rejected(lib):
 def test_backward_validation(lib):
     """kda_chunk_prefill_backward rejects bad arguments before any HIP call: flags other
     than 0, unsupported head sizes, missing or misaligned pointers, a short workspace."""
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128, 0, 0) == 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128, 0, 0) == 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 64, 64, 7, 0) == 0
-    bf = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0)
-    f32 = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 1, 0)
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128, 0, 0, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128, 0, 0, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 64, 64, 7, 0, 0) == 0
+    bf = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0)
+    f32 = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 1, 0, 0)
     assert 0 < bf < f32
     # with the chunk-end states given, the forward's workspace, outputs and states drop out
-    bf_s = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 1)
+    bf_s = lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 1)
     fwd = lib.kda_chunk_prefill_workspace_size(2, 130, 3, 64, 32, 64, 0)
     assert 0 < bf_s <= bf - fwd - 2 * 130 * 3 * 32 * 2 - 2 * 3 * 64 * 32 * 4 - 2 * 2 * 3 * 64 * 32 * 4
     # the chunk operands alone (scan fragments, P^T, G, M, dP, dG, dS1, dU, U): 2 * 3 * 3 chunks
@@ -349,7 +349,13 @@ def test_backward_validation(lib):
                                               a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
                                               a["flags"], a["ws"], a["wsb"], None)
     assert call(flags=1) == UNSUPPORTED       # L2 norm inside the call is forward-only
-    assert call(flags=2) == UNSUPPORTED       # so is the per-head scalar gate
+    assert call(flags=2) == INVALID           # SILU belongs to the short conv
+    assert call(flags=8) == INVALID
+    assert call(flags=4, ws=None) == WORKSPACE   # the per-head gate: accepted
+    # the per-head gate needs its broadcast and per-channel gradient in the workspace
+    assert (lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 4, 0)
+            == lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0) + 2 * 2 * 130 * 3 * 64 * 4)
+    assert lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 1, 0) == 0
     assert call(dk=48) == UNSUPPORTED
     assert call(dtype=5) == INVALID
     assert call(T=-1) == INVALID
@@ -366,8 +372,8 @@ def test_backward_validation(lib):
     assert call(ws=ctypes.c_void_p(0x10010)) == WORKSPACE   # 256-byte alignment
     assert call(H=0) == OK                   # nothing to do: no HIP call either
     # launch extents in threads fit 32 bits: B*H*ceil(T/64) <= 2^22 - 8 for the channel-slice grid
-    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1023, 64, 128, 128, 0, 0) > 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 0) == 0
-    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 1) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1023, 64, 128, 128, 0, 0, 0) > 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 0, 0) == 0
+    assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 0, 1) == 0
     assert call(B=64, T=64 * 1023, H=64, ws=None) == WORKSPACE
     assert call(B=64, T=64 * 1024, H=64, ws=None) == UNSUPPORTED

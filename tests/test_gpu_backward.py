@@ -194,3 +194,60 @@ def test_backward_wide_scan_tiles_equal_narrow():
         for n in NAMES:
             got = full[n][b:b + 1]
             assert torch.equal(got, part[n]), f"{n} differs for batch row {b}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_scalar_gate_equals_broadcast(dtype):
+    """KDA_FLAG_SCALAR_GATE (one gate per token and head): dq, dk, dv, dbeta and dinit equal
+    those of the per-channel call fed the broadcast gate bit for bit, and the gate's gradient is
+    that call's per-channel dlog_alpha summed over the channels."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv = 2, 200, 3, 64, 128
+    say(f"[case] backward scalar gate = broadcast gate, {dtype}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, dtype, seed=11)
+    la1 = np.ascontiguousarray(inp["log_alpha"][..., 0])
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=11)
+    mask = np.ones((B, T), np.uint8)
+    mask[1, :30] = 0
+    do, dfinal = _cotangents(B, T, H, dk, dv, dtype, 11)
+    q, k, v = (to_dev(inp[n], dtype, dev) for n in ("q", "k", "v"))
+    beta, dm, ds0 = to_dev(inp["beta"], dev=dev), to_dev(mask, dev=dev), to_dev(s0, dev=dev)
+    ddo, dfin = to_dev(do, dtype, dev), to_dev(dfinal, dev=dev)
+    la_s = to_dev(la1, dev=dev)
+    la_b = la_s.unsqueeze(-1).expand(B, T, H, dk).contiguous()
+    got = kda.chunk_prefill_backward(q, k, v, la_s, beta, ddo, d_final_state=dfin, mask=dm, initial_state=ds0,
+                                     scalar_gate=True)
+    ref = kda.chunk_prefill_backward(q, k, v, la_b, beta, ddo, d_final_state=dfin, mask=dm, initial_state=ds0)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "dbeta", "dinit_state"):
+        assert torch.equal(got[n], ref[n]), n
+    assert got["dlog_alpha"].shape == (B, T, H)
+    summed = ref["dlog_alpha"].double().sum(-1)
+    err = (got["dlog_alpha"].double() - summed).abs().max().item()
+    assert err <= 1e-5 * max(1.0, summed.abs().max().item()), err
+    assert torch.all(got["dlog_alpha"][1, :30] == 0)
+
+
+def test_backward_scalar_gate_vs_oracle(oracle):
+    """The per-head gate's gradients against the oracle's gradient with the gate broadcast to
+    every channel (its dlog_alpha summed over the channels: the chain rule through the
+    broadcast), with the states of a scalar-gate training forward handed in."""
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv = 1, 300, 2, 128, 128
+    say("[case] backward scalar gate vs oracle")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=12)
+    la1 = np.ascontiguousarray(inp["log_alpha"][..., 0])
+    one = dict(inp, log_alpha=np.ascontiguousarray(np.broadcast_to(la1[..., None], inp["log_alpha"].shape)))
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=12)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 12)
+    q, k, v = (to_dev(inp[n], "bf16", dev) for n in ("q", "k", "v"))
+    la_s, beta, ds0 = to_dev(la1, dev=dev), to_dev(inp["beta"], dev=dev), to_dev(s0, dev=dev)
+    _, _, ck = kda.chunk_prefill_states(q, k, v, la_s, beta, initial_state=ds0, state_interval=64, scalar_gate=True)
+    got = kda.chunk_prefill_backward(q, k, v, la_s, beta, to_dev(do, "bf16", dev), d_final_state=to_dev(dfinal, dev=dev),
+                                     initial_state=ds0, chunk_states=ck, scalar_gate=True)
+    ref = _ref(oracle, one, do, dfinal, s0=s0)
+    ref = dict(ref, dlog_alpha=np.asarray(ref["dlog_alpha"]).sum(-1))
+    _check("scalar gate", got, ref, "bf16")
