@@ -251,3 +251,19 @@ def test_backward_scalar_gate_vs_oracle(oracle):
     ref = _ref(oracle, one, do, dfinal, s0=s0)
     ref = dict(ref, dlog_alpha=np.asarray(ref["dlog_alpha"]).sum(-1))
     _check("scalar gate", got, ref, "bf16")
+
+
+def test_backward_128k_sampled_head(oracle):
+    """One 131072-token sequence (2048 chunk steps of the reverse scan), bf16, 2 heads on the
+    GPU; head 1 against the oracle's fp64 gradient over the whole sequence."""
+    dev = device()
+    B, T, H, dk, dv = 1, 131072, 2, 128, 128
+    say(f"[case] backward bf16 T={T} sampled head")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=13)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 13)
+    got = _run(inp, do, dfinal, "bf16", dev)
+    h = 1
+    one = {n: x[:, :, h:h + 1] for n, x in inp.items()}
+    ref = _ref(oracle, one, do[:, :, h:h + 1], dfinal[:, h:h + 1])
+    sub = {n: (got[n][:, h:h + 1] if n == "dinit_state" else got[n][:, :, h:h + 1]) for n in NAMES}
+    _check(f"128k h{h}", sub, ref, "bf16")
