@@ -42,7 +42,7 @@ MEASURED_TRAFFIC = {
     "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
     # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
-    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "802988d6c52fdc61", "bytes": 8.881e9},
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "e9d879d30a82ea56", "bytes": 8.880e9},
 }
 
 
