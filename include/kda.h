@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -306,6 +306,62 @@ int kda_chunk_prefill_backward(const void* q, const void* k, const void* v,
                                float* dq, float* dk, float* dv, float* d_log_alpha, float* d_beta,
                                float* d_init_state, int B, int T, int H, int dk_, int dv_, int dtype,
                                unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace kda_chunk_prefill_varlen_backward needs for N packed sequences of
+ * T tokens in total (0 when none is needed or the arguments would be rejected); flags and
+ * states_given as for kda_chunk_prefill_backward_workspace_size.  It depends on N and T only,
+ * not on how the tokens are split between the sequences.
+ */
+size_t kda_chunk_prefill_varlen_backward_workspace_size(int N, int T, int H, int dk, int dv, int dtype,
+                                                        unsigned flags, int states_given);
+
+/*
+ * Gradients of kda_chunk_prefill_varlen (without slots) for training on packed sequences: the
+ * backward above for N sequences of different lengths packed end to end (the remio.ai page
+ * names continuous batching among what a serving and training stack must support for KDA;
+ * its KDA section, the blockwise training algorithm).  For the loss
+ *     L = sum_t <d_o[t], o[t]> + sum_i <d_final_state[i], final_state[i]>
+ * sequence i's gradients depend on its own tokens, d_o rows and d_final_state[i] only, and
+ * equal those of kda_chunk_prefill_backward on that sequence alone (B = 1, same inputs) bit for
+ * bit: each sequence's 64-token chunks start at its first token.
+ *
+ *   q, k, v, log_alpha, beta, cu_seqlens, init_state   as for kda_chunk_prefill_varlen
+ *                              ([T,H,...] packed; init_state [N,H,dk,dv] or NULL)
+ *   chunk_states  [M,H,dk,dv]  fp32, or NULL: the checkpoints kda_chunk_prefill_varlen writes
+ *                              with state_interval = 64 on the same inputs (sequence i's state
+ *                              after each of its first j * 64 tokens at entry
+ *                              sum_{i' < i} floor(L_i' / 64) + j - 1).  NULL: the call runs the
+ *                              forward again to form them.
+ *   num_states                 entries chunk_states holds (>= M; ignored when it is NULL); an
+ *                              entry past it is read as a zero state
+ *   d_o           [T,H,dv]     dtype
+ *   d_final_state [N,H,dk,dv]  fp32, or NULL (zero)
+ *   dq, dk        [T,H,dk]     fp32, written
+ *   dv            [T,H,dv]     fp32, written
+ *   d_log_alpha   [T,H,dk]     fp32, written ([T,H] with KDA_FLAG_SCALAR_GATE)
+ *   d_beta        [T,H]        fp32, written
+ *   d_init_state  [N,H,dk,dv]  fp32, written
+ *
+ * A sequence of length 0 gets d_init_state[i] = d_final_state[i].  cu_seqlens is read on the
+ * device: entries are clamped as for kda_chunk_prefill_varlen, so a malformed array gives
+ * wrong (or unwritten) gradients but no access outside a buffer.  The workspace adds to that
+ * of kda_chunk_prefill_backward a sequence table (16 bytes per sequence) and a chunk table
+ * (8 bytes per chunk slot), and holds ceil(T/64) + N chunk slots per head.
+ * Supported: as kda_chunk_prefill_backward with B = N (N <= 65535, N*H <= 2^20 - 8) and
+ * H (ceil(T/64) + N) <= 2^22 - 8 in place of its chunk bounds; flags and alignment as there,
+ * cu_seqlens 4-byte aligned.
+ * Outputs must not overlap inputs.
+ */
+int kda_chunk_prefill_varlen_backward(const void* q, const void* k, const void* v,
+                                      const float* log_alpha, const float* beta,
+                                      const int32_t* cu_seqlens, const float* init_state,
+                                      const float* chunk_states, int num_states,
+                                      const void* d_o, const float* d_final_state,
+                                      float* dq, float* dk, float* dv, float* d_log_alpha,
+                                      float* d_beta, float* d_init_state, int N, int T, int H,
+                                      int dk_, int dv_, int dtype, unsigned flags,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One decode step: a single new token per sequence, state updated in place

@@ -152,32 +152,39 @@ int kda_chunk_prefill_varlen(const void* q, const void* k, const void* v, const 
                        workspace_bytes, stream);
 }
 
-size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
-                                                 unsigned flags, int states_given) {
-  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype) || !head_dim_ok(dk) || !head_dim_ok(dv) || B > 65535 ||
-      H > 65535 || !kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H) ||
+// the batch and packed backward calls: the same checks, the packed one with cu_seqlens
+// (B = sequences, T = packed tokens, no mask) and the count of the checkpoints it is given
+static bool backward_shape_ok(int B, int T, int H, int dk, int dv, bool varlen) {
+  return head_dim_ok(dk) && head_dim_ok(dv) && B <= 65535 && H <= 65535 &&
+         kda::prefill_grid_ok(B, T, H, 64, varlen) && kda::backward_grid_ok(B, T, H, varlen);
+}
+
+static size_t backward_size(int B, int T, int H, int dk, int dv, int dtype, unsigned flags, int states_given,
+                            bool varlen) {
+  if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype) || !backward_shape_ok(B, T, H, dk, dv, varlen) ||
       (flags & ~(unsigned)KDA_FLAG_SCALAR_GATE) != 0)
     return 0;
   return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype, states_given != 0,
-                                       (flags & KDA_FLAG_SCALAR_GATE) != 0);
+                                       (flags & KDA_FLAG_SCALAR_GATE) != 0, varlen);
 }
 
-int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
-                               const float* beta, const uint8_t* mask, const float* init_state,
-                               const float* chunk_states, const void* d_o, const float* d_final_state, float* dq, float* dk,
-                               float* dv, float* d_log_alpha, float* d_beta, float* d_init_state,
-                               int B, int T, int H, int dk_, int dv_, int dtype, unsigned flags,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+static int backward_entry(const void* q, const void* k, const void* v, const float* log_alpha,
+                          const float* beta, const uint8_t* mask, const int32_t* cu_seqlens, bool varlen,
+                          const float* init_state, const float* chunk_states, int num_states, const void* d_o,
+                          const float* d_final_state, float* dq, float* dk, float* dv, float* d_log_alpha,
+                          float* d_beta, float* d_init_state, int B, int T, int H, int dk_, int dv_, int dtype,
+                          unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
   if (flags & KDA_FLAG_L2NORM_QK) return KDA_ERR_UNSUPPORTED;      // normalise q and k before the call
   const bool sg = (flags & KDA_FLAG_SCALAR_GATE) != 0;
-  if (!head_dim_ok(dk_) || !head_dim_ok(dv_) || B > 65535 || H > 65535) return KDA_ERR_UNSUPPORTED;
-  if (!kda::prefill_grid_ok(B, T, H, 64, false) || !kda::backward_grid_ok(B, T, H)) return KDA_ERR_UNSUPPORTED;
+  if (!backward_shape_ok(B, T, H, dk_, dv_, varlen)) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
   if (d_init_state == nullptr || !aligned(d_init_state, 4)) return KDA_ERR_INVALID_ARG;
   if (init_state != nullptr && !aligned(init_state, 16)) return KDA_ERR_INVALID_ARG;
   if (d_final_state != nullptr && !aligned(d_final_state, 4)) return KDA_ERR_INVALID_ARG;
+  if (varlen && (cu_seqlens == nullptr || !aligned(cu_seqlens, 4))) return KDA_ERR_INVALID_ARG;
+  if (varlen && chunk_states != nullptr && num_states < 0) return KDA_ERR_INVALID_ARG;
   if (T > 0) {
     const void* req[] = {q, k, v, log_alpha, beta, d_o, dq, dk, dv, d_log_alpha, d_beta};
     for (const void* ptr : req)
@@ -191,13 +198,46 @@ int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, cons
     // the chunk-end states are read with 16-byte vector loads
     if (chunk_states != nullptr && !aligned(chunk_states, 16)) return KDA_ERR_INVALID_ARG;
   }
-  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr, sg);
+  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr, sg, varlen);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return KDA_ERR_WORKSPACE;
-  kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, mask, chunk_states,
-                      dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype, sg ? 1 : 0,
-                      workspace, stream};
+  kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, varlen ? nullptr : mask,
+                      chunk_states, dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype,
+                      sg ? 1 : 0, workspace, stream, varlen ? cu_seqlens : nullptr, num_states};
   return hip_status(kda::launch_backward(a));
+}
+
+size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
+                                                 unsigned flags, int states_given) {
+  return backward_size(B, T, H, dk, dv, dtype, flags, states_given, false);
+}
+
+int kda_chunk_prefill_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta, const uint8_t* mask, const float* init_state,
+                               const float* chunk_states, const void* d_o, const float* d_final_state, float* dq, float* dk,
+                               float* dv, float* d_log_alpha, float* d_beta, float* d_init_state,
+                               int B, int T, int H, int dk_, int dv_, int dtype, unsigned flags,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_entry(q, k, v, log_alpha, beta, mask, nullptr, false, init_state, chunk_states, 0, d_o,
+                        d_final_state, dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype,
+                        flags, workspace, workspace_bytes, stream);
+}
+
+size_t kda_chunk_prefill_varlen_backward_workspace_size(int N, int T, int H, int dk, int dv, int dtype,
+                                                        unsigned flags, int states_given) {
+  return backward_size(N, T, H, dk, dv, dtype, flags, states_given, true);
+}
+
+int kda_chunk_prefill_varlen_backward(const void* q, const void* k, const void* v, const float* log_alpha,
+                                      const float* beta, const int32_t* cu_seqlens, const float* init_state,
+                                      const float* chunk_states, int num_states, const void* d_o,
+                                      const float* d_final_state, float* dq, float* dk, float* dv,
+                                      float* d_log_alpha, float* d_beta, float* d_init_state, int N, int T, int H,
+                                      int dk_, int dv_, int dtype, unsigned flags, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return backward_entry(q, k, v, log_alpha, beta, nullptr, cu_seqlens, true, init_state, chunk_states, num_states,
+                        d_o, d_final_state, dq, dk, dv, d_log_alpha, d_beta, d_init_state, N, T, H, dk_, dv_,
+                        dtype, flags, workspace, workspace_bytes, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -72,8 +72,57 @@ struct Params {
   const uint8_t* mask;
   float *dq, *dk, *dv, *dla, *dbeta, *dinit;
   Ws w;
-  int B, T, H, K, V, NC, NCf;
+  // packed sequences: per sequence (start, end, first checkpoint, first chunk) and per chunk
+  // (sequence, chunk within it), (-1, -1) past the last; both null for a padded batch
+  const int4* seqs;
+  const int2* cmap;
+  int B, T, H, K, V, NC, NCf;              // packed: B = sequences, T = tokens, NC = chunk slots
+  int num_states;                          // checkpoints ck holds (entries past it read as zero)
 };
+
+// Where sequence s lies for head h.  A padded batch: row s of [B, T], its chunks consecutive
+// in the workspace.  Packed sequences: tokens [start, end) of the packed arrays, its chunks at
+// consecutive entries of the chunk table, the workspace holding each entry's heads together.
+struct SeqLoc {
+  size_t t0;       // token (row of the [tokens][H] arrays) at the sequence's start
+  int len, nc;     // tokens and chunks
+  size_t ch0, chs; // workspace index of chunk 0 and the step between chunks
+  long long ck0;   // checkpoint entry holding the state after the first chunk
+};
+
+__device__ __forceinline__ SeqLoc seq_loc(const Params& p, int s, int h) {
+  if (p.seqs == nullptr)
+    return {(size_t)s * p.T, p.T, p.NC, ((size_t)s * p.H + h) * p.NC, 1, (long long)s * p.NCf};
+  const int4 q = p.seqs[s];
+  const int len = q.y - q.x;
+  return {(size_t)q.x, len, (len + kC - 1) / kC, (size_t)q.w * p.H + h, (size_t)p.H, q.z};
+}
+
+// chunk n of a sequence: its first token, the rows in range (1 .. 64) and its workspace index
+struct ChunkLoc {
+  size_t t0;
+  int rows;
+  size_t ch;
+};
+
+__device__ __forceinline__ ChunkLoc chunk_loc(const SeqLoc& S, int n) {
+  const int left = S.len - n * kC;
+  return {S.t0 + (size_t)n * kC, left < kC ? left : kC, S.ch0 + (size_t)n * S.chs};
+}
+
+// the (sequence, chunk) of a chunk-parallel workgroup: row b's chunk n in a padded batch, entry
+// n of the chunk table for packed sequences (b = 0), where false means past the last chunk
+__device__ __forceinline__ bool find_chunk(const Params& p, int b, int n, int& s, int& j) {
+  if (p.cmap == nullptr) {
+    s = b;
+    j = n;
+    return true;
+  }
+  const int2 m = p.cmap[n];
+  s = m.x;
+  j = m.y;
+  return m.x >= 0;
+}
 
 // 8 consecutive floats from 8-byte aligned LDS
 __device__ __forceinline__ void lds8(const float* src, float* out) {
@@ -131,9 +180,9 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
-// One lane's view of chunk n: row 16 w + l%16 (w = wave), channels c_base + 32 ks + 8 (l/16)
+// One lane's view of a chunk: row 16 w + l%16 (w = wave), channels c_base + 32 ks + 8 (l/16)
 // .. +7 of a window of KW channels (the A-operand layout).  q, k and log_alpha of rows that
-// are not valid (masked or past T) and of channels past K are 0.  g becomes the inclusive
+// are not valid (masked or past the sequence) and of channels past K are 0.  g becomes the inclusive
 // cumulative sum of log2 decay over the chunk's rows and s_gl the chunk's totals per channel
 // of the window.  Every thread must call it (it holds two barriers).
 template <int DT, int KW>
@@ -145,20 +194,19 @@ struct Rows {
 };
 
 template <int DT, int KW, bool WANT_Q>
-__device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, int c_base, Rows<DT, KW>& R,
+__device__ __forceinline__ void load_rows(const Params& p, const ChunkLoc& L, int h, int c_base, Rows<DT, KW>& R,
                                           float* s_tot, float* s_gl) {
   using E = Elem<DT>;
   using Tp = typename E::T;
   constexpr int KS = KW / 32;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = 16 * w + (lane & 15), cg = 8 * (lane >> 4);
-  const int t = n * kC + r;
-  const int ts = t < p.T ? t : p.T - 1;
-  const size_t tk = ((size_t)b * p.T + ts) * p.H + h;
+  const int rs = r < L.rows ? r : L.rows - 1;
+  const size_t tk = (L.t0 + rs) * p.H + h;
   // every load is issued unconditionally from an in-bounds row and channel; what is not
   // valid is replaced by 0 with a select afterwards (a branch on the loaded mask would wait
   // for it before issuing the rest)
-  const uint8_t mk = p.mask == nullptr ? (uint8_t)1 : p.mask[(size_t)b * p.T + ts];
+  const uint8_t mk = p.mask == nullptr ? (uint8_t)1 : p.mask[L.t0 + rs];
   const float bt = p.beta[tk];
   Raw8<DT> kr[KS], qr[KS];
   Raw8<1> lr[KS];
@@ -169,7 +217,7 @@ __device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, 
     if (WANT_Q) qr[ks].load((const Tp*)p.q, tk * p.K + cs);
     lr[ks].load(p.la, tk * p.K + cs);
   }
-  R.ok = t < p.T && mk != 0;
+  R.ok = r < L.rows && mk != 0;
   R.beta = R.ok ? bt : 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -219,11 +267,13 @@ __device__ __forceinline__ void load_rows(const Params& p, int b, int h, int n, 
     for (int e = 0; e < 8; ++e) R.g[ks][e] += s_tot[w * KW + 32 * ks + cg + e];
 }
 
-// the chunk's entry state: the initial state for the first chunk, else the forward's
-// state at the end of the chunk before (null: zero)
-__device__ __forceinline__ const float* entry_state(const Params& p, int b, int h, int n) {
-  if (n == 0) return p.init == nullptr ? nullptr : p.init + ((size_t)b * p.H + h) * p.K * p.V;
-  return p.w.ck + (((size_t)b * p.NCf + n - 1) * p.H + h) * p.K * p.V;
+// the entry state of chunk n of sequence s: the initial state for the first chunk, else the
+// forward's state at the end of the chunk before (null: zero)
+__device__ __forceinline__ const float* entry_state(const Params& p, const SeqLoc& S, int s, int h, int n) {
+  if (n == 0) return p.init == nullptr ? nullptr : p.init + ((size_t)s * p.H + h) * p.K * p.V;
+  const long long e = S.ck0 + n - 1;
+  if (e < 0 || e >= p.num_states) return nullptr;
+  return p.w.ck + ((size_t)e * p.H + h) * p.K * p.V;
 }
 
 // ================================================================ 2. prep
@@ -248,13 +298,16 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_prep_kernel(Params p) {
   float* s_A = s_x;                                              // after G and P are formed
   float* s_P = s_x + kC * LC;
 
-  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
+  const int h = blockIdx.x % p.H;
+  int s, n;
+  if (!find_chunk(p, blockIdx.y, blockIdx.x / p.H, s, n)) return;
+  const ChunkLoc L = chunk_loc(seq_loc(p, s, h), n);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
-  const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
+  const size_t ch = L.ch;
 
   Rows<DT, KP> R;
-  load_rows<DT, KP, true>(p, b, h, n, 0, R, s_tot, s_gl);
+  load_rows<DT, KP, true>(p, L, h, 0, R, s_tot, s_gl);
   if (lane < 16) { s_beta[r] = R.beta; s_ok[r] = R.ok ? 1.f : 0.f; }
   {
     // validity of the chunk's rows as one 64-bit word (wave w holds rows 16 w .. +15)
@@ -351,8 +404,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_prep_kernel(Params p) {
         const int ii = 16 * w + 4 * g4 + i, jj = 16 * J + col;
         float gs = 0.f, ps = 0.f;
         if (jj <= ii && s_ok[ii] != 0.f && s_ok[jj] != 0.f) {
-          const size_t ti = (((size_t)b * p.T + n * kC + ii) * p.H + h) * p.K;
-          const size_t tj = (((size_t)b * p.T + n * kC + jj) * p.H + h) * p.K;
+          const size_t ti = ((L.t0 + ii) * p.H + h) * p.K;
+          const size_t tj = ((L.t0 + jj) * p.H + h) * p.K;
           for (int c = 0; c < p.K; ++c) {
             const float d = exp2f(s_x[ii * LD + c] - s_x[jj * LD + c]);
             const float kj = E::ld(kg, tj + c) * d;
@@ -545,12 +598,14 @@ __global__ void __launch_bounds__(kThreads, (DT == 0 && KP == 128 && V == 128 &&
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int bh = (slot / NT) * 8 + xcd, vt = slot % NT;
   if (bh >= p.B * p.H) return;
-  const int b = bh / p.H, h = bh % p.H;
+  const int h = bh % p.H;
+  const SeqLoc S = seq_loc(p, bh / p.H, h);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, v0 = TW * vt;
 
   auto load_ops = [&](int n, Ops& o) __attribute__((always_inline)) {
-    const size_t ch = (size_t)bh * p.NC + n;
+    const ChunkLoc L = chunk_loc(S, n);
+    const size_t ch = L.ch;
     const uint16_t* kh = p.w.kh + ch * (size_t)(kC * KP * parts);
     const uint16_t* pt = p.w.pt + ch * (size_t)(2 * kC * kC);
     const uint16_t* wt = p.w.wt + ch * (size_t)(kC * KP * parts);
@@ -576,8 +631,8 @@ __global__ void __launch_bounds__(kThreads, (DT == 0 && KP == 128 && V == 128 &&
         }
       o.gam[m] = *reinterpret_cast<const float4*>(p.w.gam + ch * KP + 16 * rt + 4 * g4);
     }
-    const int row = tid >> 2, c4 = 4 * NH * (tid & 3), t = n * kC + row, ts = t < p.T ? t : p.T - 1;
-    const Tp* dp = (const Tp*)p.dout + (((size_t)b * p.T + ts) * p.H + h) * V + v0 + c4;
+    const int row = tid >> 2, c4 = 4 * NH * (tid & 3), rs = row < L.rows ? row : L.rows - 1;
+    const Tp* dp = (const Tp*)p.dout + ((L.t0 + rs) * p.H + h) * V + v0 + c4;
 #pragma unroll
     for (int j = 0; j < (DT == 1 ? NH : 1); ++j)
       o.dor[j] = *reinterpret_cast<const typename std::remove_reference<decltype(o.dor[0])>::type*>(dp + 4 * j);
@@ -597,7 +652,7 @@ __global__ void __launch_bounds__(kThreads, (DT == 0 && KP == 128 && V == 128 &&
       }
 
   auto step = [&](int n, const Ops& o) __attribute__((always_inline)) {
-    const size_t ch = (size_t)bh * p.NC + n;
+    const size_t ch = S.ch0 + (size_t)n * S.chs;
     float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
 #pragma unroll
     for (int hf = 0; hf < NH; ++hf)
@@ -712,7 +767,7 @@ __global__ void __launch_bounds__(kThreads, (DT == 0 && KP == 128 && V == 128 &&
   // (loads are never conditional inside the loop, so every wait the compiler places on
   // them counts exactly the memory operations issued since)
   Ops A, B;
-  int n = p.NC - 1;
+  int n = S.nc - 1;
   if (n >= 0) load_ops(n, A);
   __builtin_amdgcn_s_waitcnt(0);
   for (; n >= 1; n -= 2) {
@@ -760,19 +815,20 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
   __bf16* const s_Sl = s_Sh + 32 * LK;
   __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC], s_db[kC];
 
-  const int n = blockIdx.x / p.H, h = blockIdx.x % p.H, b = blockIdx.y;
+  const int h = blockIdx.x % p.H;
+  int s, n;
+  if (!find_chunk(p, blockIdx.y, blockIdx.x / p.H, s, n)) return;
+  const SeqLoc S = seq_loc(p, s, h);
+  const ChunkLoc L = chunk_loc(S, n);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
-  const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
-  auto tok = [&](int row) -> size_t { return ((size_t)b * p.T + n * kC + row) * p.H + h; };
+  const size_t ch = L.ch;
+  auto tok = [&](int row) -> size_t { return (L.t0 + row) * p.H + h; };
   // the same row clamped into the sequence: an in-bounds address for unconditional loads
-  auto tokc = [&](int row) -> size_t {
-    const int t = n * kC + row;
-    return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
-  };
+  auto tokc = [&](int row) -> size_t { return (L.t0 + (row < L.rows ? row : L.rows - 1)) * p.H + h; };
 
   Rows<DT, KP> R;
-  load_rows<DT, KP, false>(p, b, h, n, 0, R, s_tot, s_gl);
+  load_rows<DT, KP, false>(p, L, h, 0, R, s_tot, s_gl);
   if (lane < 16) { s_beta[r] = R.beta; s_ok[r] = R.ok ? 1.f : 0.f; }
   // Kt of this lane's row: the A operand of R = V - Kt S0 for row tile w
   bf16x8 kth[KS], ktl[KS];
@@ -797,7 +853,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
   }
   __syncthreads();
 
-  const float* S0 = entry_state(p, b, h, n);
+  const float* S0 = entry_state(p, S, s, h, n);
   const float* dUg = p.w.dU + ch * (size_t)(kC * V);
   float* Ug = p.w.U + ch * (size_t)(kC * V);
   const bool rok = s_ok[r] != 0.f;
@@ -911,7 +967,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
         s_U[row * LS + 16 * t2 + col] = au[i];
         if (vc < V) {
           Ug[row * V + vc] = au[i];
-          if (n * kC + row < p.T) p.dv[tok(row) * V + vc] = s_ok[row] != 0.f ? ad[i] : 0.f;
+          if (row < L.rows) p.dv[tok(row) * V + vc] = s_ok[row] != 0.f ? ad[i] : 0.f;
         }
       }
     }
@@ -1024,7 +1080,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_cc_kernel(Params p) {
     }
   }
   __syncthreads();
-  if (tid < kC && n * kC + tid < p.T) p.dbeta[tok(tid)] = s_ok[tid] != 0.f ? db + s_db[tid] : 0.f;
+  if (tid < L.rows) p.dbeta[tok(tid)] = s_ok[tid] != 0.f ? db + s_db[tid] : 0.f;
 }
 
 // ================================================================ 5. q, k and decay gradients
@@ -1066,17 +1122,19 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   constexpr int NS = KP / SW;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const long long cid = (long long)(slot / NS) * 8 + xcd;       // (b * NC + n) * H + h
-  if (cid >= (long long)p.B * p.NC * p.H) return;
-  const int bn = (int)(cid / p.H), h = (int)(cid % p.H), b = bn / p.NC, n = bn % p.NC;
+  const int rows_b = p.cmap == nullptr ? p.B : 1;                // packed: one row of NC slots
+  if (cid >= (long long)rows_b * p.NC * p.H) return;
+  const int bn = (int)(cid / p.H), h = (int)(cid % p.H);
+  int s, n;
+  if (!find_chunk(p, bn / p.NC, bn % p.NC, s, n)) return;
+  const SeqLoc S = seq_loc(p, s, h);
+  const ChunkLoc L = chunk_loc(S, n);
   const int c_base = SW * (slot % NS);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, r = 16 * w + col, cg = 8 * g4;
-  const size_t ch = ((size_t)b * p.H + h) * p.NC + n;
-  auto tok = [&](int row) -> size_t { return ((size_t)b * p.T + n * kC + row) * p.H + h; };
-  auto tokc = [&](int row) -> size_t {
-    const int t = n * kC + row;
-    return ((size_t)b * p.T + (t < p.T ? t : p.T - 1)) * p.H + h;
-  };
+  const size_t ch = L.ch;
+  auto tok = [&](int row) -> size_t { return (L.t0 + row) * p.H + h; };
+  auto tokc = [&](int row) -> size_t { return (L.t0 + (row < L.rows ? row : L.rows - 1)) * p.H + h; };
   const int hw = w >> 1, lc = 16 * (w & 1) + col, c = c_base + lc;   // row half; channel
   const bool cin = c < p.K;
 
@@ -1090,7 +1148,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   float ssp = 0.f;
   {
     const uint64_t vb = p.w.vbits[ch];
-    const float* S0 = entry_state(p, b, h, n);
+    const float* S0 = entry_state(p, S, s, h, n);
     const float* dS1 = p.w.dS1 + ch * (size_t)(KP * V);
     const float* Ug = p.w.U + ch * (size_t)(kC * V);
     const int arow = tid >> 2, ac8 = 8 * (tid & 3), bc4 = 4 * (tid & 7);   // A piece: row, 8 columns
@@ -1199,7 +1257,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
     }
   }
   Rows<DT, SW> R;
-  load_rows<DT, SW, true>(p, b, h, n, c_base, R, s_tot, s_gl);
+  load_rows<DT, SW, true>(p, L, h, c_base, R, s_tot, s_gl);
   if (lane < 16) s_ok[r] = R.ok ? 1.f : 0.f;
   const bool fast = __syncthreads_and(tid >= SW || s_gl[tid] >= kFastLimit);
 #pragma unroll
@@ -1322,7 +1380,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
       const float khv = kv * ekh;
       dl[ii][i] = ok ? kv * a - kv * bb + qv * dqv - z[i] * khv : 0.f;
       zk += ok ? z[i] * khv : 0.f;
-      if (n * kC + row < p.T && cin) {
+      if (row < L.rows && cin) {
         p.dq[tok(row) * p.K + c] = ok ? dqv : 0.f;
         p.dk[tok(row) * p.K + c] = ok ? dkv : 0.f;
       }
@@ -1363,7 +1421,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
     for (int i = 3; i >= 0; --i) {
       const int row = 16 * I + 4 * g4 + i;
       run += dl[ii][i];
-      if (n * kC + row < p.T && cin) p.dla[tok(row) * p.K + c] = s_ok[row] != 0.f ? run : 0.f;
+      if (row < L.rows && cin) p.dla[tok(row) * p.K + c] = s_ok[row] != 0.f ? run : 0.f;
     }
     carry += tile[ii];
   }
@@ -1413,21 +1471,80 @@ static unsigned gate_blocks(size_t items) {
   return (unsigned)(b < kGateMaxBlocks ? b : kGateMaxBlocks);
 }
 
+// ---------------------------------------------------------------- packed sequences
+// The sequence table (start, end, first checkpoint, first chunk) and the chunk table
+// (sequence, chunk within it) from cu_seqlens: one workgroup scans the chunk counts and the
+// 64-token checkpoint counts together (low and high 32 bits of one 64-bit sum).  Token bounds
+// are clamped into [0, T]; a sequence whose chunks would pass the NC slots of the workspace is
+// cut short, so a malformed cu_seqlens gives wrong results but no access outside a buffer.
+constexpr int kSetupThreads = 1024;
+__global__ void __launch_bounds__(kSetupThreads)
+bwd_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int NC, int4* __restrict__ seqs,
+                 int2* __restrict__ cmap) {
+  __shared__ long long s_scan[kSetupThreads];
+  __shared__ long long s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += kSetupThreads) {
+    const int i = base + tid;
+    int start = 0, end = 0, nc = 0, nk = 0;
+    if (i < N) {
+      start = min(max(cu[i], 0), T);
+      end = min(max(cu[i + 1], start), T);
+      nc = (end - start + kC - 1) / kC;
+      nk = (end - start) / kC;
+    }
+    const long long mine = ((long long)nk << 32) | (unsigned)nc;
+    s_scan[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kSetupThreads; off <<= 1) {      // inclusive scan of the counts
+      const long long v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const long long before = s_carry + s_scan[tid] - mine;
+    const int first = (int)min(before & 0xffffffffll, (long long)NC);
+    const int fit = min(nc, NC - first);
+    if (i < N) {
+      seqs[i] = make_int4(start, fit < nc ? start + fit * kC : end, (int)(before >> 32), first);
+      for (int j = 0; j < fit; ++j) cmap[first + j] = make_int2(i, j);
+    }
+    __syncthreads();
+    if (tid == kSetupThreads - 1) s_carry += s_scan[tid];
+    __syncthreads();
+  }
+  for (int g = (int)min(s_carry & 0xffffffffll, (long long)NC) + tid; g < NC; g += kSetupThreads)
+    cmap[g] = make_int2(-1, -1);
+}
+
 // ---------------------------------------------------------------- host side
 // The chunk operands and gradients first, then what running the forward again needs (its
 // workspace, its discarded outputs and the chunk-end states): `own` bytes suffice when the
 // caller hands the states in.
 struct Layout {
-  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, lab, dlab, own, fwd, o, fin, ck, total;
+  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, lab, dlab, seqs, cmap, own, fwd, o, fin, ck, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate) {
+// chunk slots of the workspace per head: ceil(T / 64) per batch row, or for B packed
+// sequences the bound ceil(T / 64) + B (each sequence adds at most one partial chunk)
+long long chunk_slots(int B, int T, bool varlen) {
+  const long long nc = T > 0 ? ((long long)T + kC - 1) / kC : 0;
+  return varlen && T > 0 ? nc + B : nc;
+}
+
+Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate, bool varlen) {
   Layout L{};
-  if (T <= 0 || B == 0 || H == 0) return L;
-  const int KP = kpad(dk), NC = (T + kC - 1) / kC, NCf = T / kC;
-  const size_t nch = (size_t)B * H * NC, parts = dtype == 1 ? 2 : 1, es = dtype == 1 ? 4 : 2;
+  if (B == 0 || H == 0 || (T <= 0 && !varlen)) return L;
+  const int KP = kpad(dk);
+  const long long NC = chunk_slots(B, T, varlen);
+  const size_t rows_b = varlen ? 1 : B, tokens = rows_b * (size_t)T;
+  const size_t nch = rows_b * H * NC, parts = dtype == 1 ? 2 : 1, es = dtype == 1 ? 4 : 2;
+  // checkpoints: B floor(T / 64) for a batch, at most floor(T / 64) for packed sequences
+  const size_t nck = varlen ? (size_t)(T / kC) : (size_t)B * (T / kC);
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align256(bytes); return at; };
   L.kh = take(nch * kC * KP * 2 * parts);
@@ -1444,21 +1561,26 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate) 
   L.dP = take(nch * kC * kC * 4);
   L.dG = take(nch * kC * kC * 4);
   if (scalar_gate) {                        // the gate on every channel, and its per-channel gradient
-    L.lab = take((size_t)B * T * H * dk * 4);
-    L.dlab = take((size_t)B * T * H * dk * 4);
+    L.lab = take(tokens * H * dk * 4);
+    L.dlab = take(tokens * H * dk * 4);
+  }
+  if (varlen) {
+    L.seqs = take((size_t)B * 16);
+    L.cmap = take((size_t)NC * 8);
   }
   L.own = off;
-  L.fwd = take(prefill_workspace_bytes(B, T, H, dk, dv, kC, dtype, false));
-  L.o = take((size_t)B * T * H * dv * es);
+  L.fwd = take(T > 0 ? prefill_workspace_bytes(B, T, H, dk, dv, kC, dtype, varlen) : 0);
+  L.o = take(tokens * H * dv * es);
   L.fin = take((size_t)B * H * dk * dv * 4);
-  L.ck = take((size_t)B * NCf * H * dk * dv * 4);
+  L.ck = take(nck * H * dk * dv * 4);
   L.total = off;
   return L;
 }
 
 template <int DT, int KP, int V>
 hipError_t launch_t(const Params& p, hipStream_t st) {
-  const dim3 cgrid(p.NC * p.H, p.B);
+  const int rows_b = p.cmap != nullptr ? 1 : p.B;     // packed: one row of chunk slots
+  const dim3 cgrid(p.NC * p.H, rows_b);
   if (p.NC > 0) {
     hipLaunchKernelGGL((bwd_prep_kernel<DT, KP>), cgrid, dim3(kThreads), 0, st, p);
     hipError_t e = hipGetLastError();
@@ -1477,7 +1599,7 @@ hipError_t launch_t(const Params& p, hipStream_t st) {
   hipLaunchKernelGGL((bwd_cc_kernel<DT, KP, V>), cgrid, dim3(kThreads), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long cgroups = ((long long)p.B * p.NC * p.H + 7) / 8;
+  const long long cgroups = ((long long)rows_b * p.NC * p.H + 7) / 8;
   hipLaunchKernelGGL((bwd_ck_kernel<DT, KP, V>), dim3((unsigned)(cgroups * 8 * (KP / kCkSlice))), dim3(kThreads), 0,
                      st, p);
   return hipGetLastError();
@@ -1498,28 +1620,35 @@ hipError_t launch_dt(const Params& p, hipStream_t st) {
 }  // namespace
 
 // the x extent of every backward launch in threads fits 32 bits (the forward's own grids are
-// checked by prefill_grid_ok): the chunk-local grid (H ceil(T/64) workgroups), the scan
-// (B H rounded up to 8, times up to 8 column tiles) and the channel-slice grid (B H ceil(T/64)
-// rounded up to 8, times up to 4 slices)
-bool backward_grid_ok(int B, int T, int H) {
-  const long long kMax = 0xffffffffll, NC = T > 0 ? ((long long)T + kC - 1) / kC : 0;
-  const long long nbh = (long long)B * H, chunks = nbh * NC;
+// checked by prefill_grid_ok): the chunk-local grid (H times the chunk slots workgroups), the
+// scan (B H rounded up to 8, times up to 8 column tiles) and the channel-slice grid (the
+// chunk-local workgroups rounded up to 8, times up to 4 slices)
+bool backward_grid_ok(int B, int T, int H, bool varlen) {
+  const long long kMax = 0xffffffffll, NC = chunk_slots(B, T, varlen);
+  const long long nbh = (long long)B * H, chunks = (varlen ? 1 : B) * NC * H;
   return NC * H * kThreads <= kMax && (nbh + 7) / 8 * 8 * 8 * kThreads <= kMax &&
          (chunks + 7) / 8 * 8 * (128 / kCkSlice) * kThreads <= kMax;
 }
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given,
-                                bool scalar_gate) {
-  const Layout L = layout(B, T, H, dk, dv, dtype, scalar_gate);
+                                bool scalar_gate, bool varlen) {
+  const Layout L = layout(B, T, H, dk, dv, dtype, scalar_gate, varlen);
   return states_given ? L.own : L.total;
 }
 
 hipError_t launch_backward(const BackwardArgs& a) {
-  const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype, a.scalar_gate != 0);
+  const bool varlen = a.cu_seqlens != nullptr;
+  const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype, a.scalar_gate != 0, varlen);
   unsigned char* ws = (unsigned char*)a.workspace;
   hipStream_t st = (hipStream_t)a.stream;
-  const int NC = a.T > 0 ? (a.T + kC - 1) / kC : 0, NCf = a.T / kC;
-  const size_t rows = (size_t)a.B * a.T * a.H;
+  const int NC = (int)chunk_slots(a.B, a.T, varlen), NCf = a.T / kC;
+  const size_t rows = (size_t)(varlen ? 1 : a.B) * a.T * a.H;
+  if (varlen) {
+    hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.cu_seqlens, a.B, a.T, NC,
+                       (int4*)(ws + L.seqs), (int2*)(ws + L.cmap));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // the per-channel gate and dlog_alpha the pass works with
   const float* la = a.log_alpha;
   float* dla = a.dla;
@@ -1532,6 +1661,8 @@ hipError_t launch_backward(const BackwardArgs& a) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // checkpoints the pass may read: the caller's count, or what the forward below writes
+  const int own_states = varlen ? NCf : a.B * NCf;
   if (a.T > 0 && a.chunk_states == nullptr) {
     // the forward pass again, keeping the state at every chunk end
     PrefillArgs f{};
@@ -1543,8 +1674,9 @@ hipError_t launch_backward(const BackwardArgs& a) {
     f.workspace = ws + L.fwd;
     f.workspace_bytes = L.o - L.fwd;
     f.stream = a.stream;
-    f.chunk_states = NCf > 0 ? (float*)(ws + L.ck) : nullptr;
-    f.num_states = a.B * NCf;
+    f.cu_seqlens = a.cu_seqlens;
+    f.chunk_states = own_states > 0 ? (float*)(ws + L.ck) : nullptr;
+    f.num_states = own_states;
     f.state_interval = kC;
     const hipError_t e = launch_prefill(f);
     if (e != hipSuccess) return e;
@@ -1562,6 +1694,11 @@ hipError_t launch_backward(const BackwardArgs& a) {
     p.w.dP = (float*)(ws + L.dP); p.w.dG = (float*)(ws + L.dG);
     p.w.ck = a.chunk_states != nullptr ? a.chunk_states : (const float*)(ws + L.ck);
   }
+  if (varlen) {
+    p.seqs = (const int4*)(ws + L.seqs);
+    p.cmap = (const int2*)(ws + L.cmap);
+  }
+  p.num_states = a.chunk_states != nullptr ? (varlen ? a.num_states : a.B * NCf) : own_states;
   p.B = a.B; p.T = a.T; p.H = a.H; p.K = a.dk_; p.V = a.dv_; p.NC = NC; p.NCf = NCf;
   hipError_t e = a.dtype == 0 ? launch_dt<0>(p, st) : launch_dt<1>(p, st);
   if (e != hipSuccess || !a.scalar_gate || rows == 0) return e;

@@ -75,14 +75,17 @@ struct BackwardArgs {
   int scalar_gate;                         // log_alpha and dla are [B,T,H]: one gate per head
   void* workspace;
   void* stream;
+  const int32_t* cu_seqlens;               // packed sequences (then B = their number, no mask), or null
+  int num_states;                          // packed: entries chunk_states holds
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
+// varlen: B packed sequences of T tokens in total
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given,
-                                bool scalar_gate);
+                                bool scalar_gate, bool varlen);
 // every backward launch's grid fits (the forward inside it is checked by prefill_grid_ok)
-bool backward_grid_ok(int B, int T, int H);
+bool backward_grid_ok(int B, int T, int H, bool varlen);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -23,7 +23,8 @@ EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
            "kda_short_conv", "kda_decode_step_fused", "kda_chunk_prefill_varlen_workspace_size",
            "kda_chunk_prefill_varlen", "kda_chunk_prefill_noalloc", "kda_noalloc_scratch_bytes",
            "kda_chunk_prefill_backward_workspace_size", "kda_chunk_prefill_backward",
-           "kda_chunk_prefill_states")
+           "kda_chunk_prefill_states", "kda_chunk_prefill_varlen_backward_workspace_size",
+           "kda_chunk_prefill_varlen_backward")
 
 _lib = None
 
@@ -84,6 +85,11 @@ def load():
     lib.kda_chunk_prefill_states.restype = i
     lib.kda_chunk_prefill_states.argtypes = [vp, vp, vp, fp, fp, up, fp, vp, fp, fp, i, i,
                                              i, i, i, i, i, i, i, u, vp, sz, vp]
+    lib.kda_chunk_prefill_varlen_backward_workspace_size.restype = sz
+    lib.kda_chunk_prefill_varlen_backward_workspace_size.argtypes = [i, i, i, i, i, i, u, i]
+    lib.kda_chunk_prefill_varlen_backward.restype = i
+    lib.kda_chunk_prefill_varlen_backward.argtypes = [vp, vp, vp, fp, fp, vp, fp, fp, i, vp, fp, fp, fp, fp, fp,
+                                                      fp, fp, i, i, i, i, i, i, u, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -384,6 +390,69 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     if state_interval:
         return out, final_state, chunk_states
     return out, final_state
+
+
+def varlen_backward_workspace_size(N, T, H, dk, dv, dtype_code, states_given=False, scalar_gate=False):
+    """Bytes of workspace kda_chunk_prefill_varlen_backward needs."""
+    return int(load().kda_chunk_prefill_varlen_backward_workspace_size(
+        N, T, H, dk, dv, dtype_code, KDA_FLAG_SCALAR_GATE if scalar_gate else 0, int(bool(states_given))))
+
+
+def chunk_prefill_varlen_backward(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_final_state=None,
+                                  initial_state=None, chunk_states=None, workspace=None, scalar_gate=False):
+    """Gradients of chunk_prefill_varlen (no slots, no L2 flag) for
+    L = sum <d_o, o> + sum_i <d_final_state[i], final_state[i]>.  Inputs as for
+    chunk_prefill_varlen: q,k [T,H,dk], v [T,H,dv], log_alpha [T,H,dk] ([T,H] with
+    scalar_gate), beta [T,H], cu_seqlens [N+1] int32 on the GPU, initial_state [N,H,dk,dv] or
+    None; d_o [T,H,dv] in q's dtype, d_final_state [N,H,dk,dv] fp32 or None.  chunk_states:
+    the checkpoints chunk_prefill_varlen wrote for the same inputs with state_interval = 64
+    ([M,H,dk,dv]), or None (the forward then runs again inside the call).  Returns a dict of
+    fp32 tensors dq, dk, dv, dlog_alpha, dbeta (shapes of the inputs) and dinit_state
+    [N,H,dk,dv]."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    _req(q, "q")
+    _req(k, "k", q.dtype, (T, H, dk))
+    _req(v, "v", q.dtype, (T, H, dv))
+    _req(d_o, "d_o", q.dtype, (T, H, dv))
+    _req(log_alpha, "log_alpha", torch.float32, (T, H) if scalar_gate else (T, H, dk))
+    _req(beta, "beta", torch.float32, (T, H))
+    _req(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _req(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if d_final_state is not None:
+        _req(d_final_state, "d_final_state", torch.float32, (N, H, dk, dv))
+    n_states = 0
+    if chunk_states is not None:
+        _req(chunk_states, "chunk_states", torch.float32)
+        if chunk_states.dim() != 4 or tuple(chunk_states.shape[1:]) != (H, dk, dv):
+            raise ValueError(f"chunk_states must be [M,{H},{dk},{dv}], got {tuple(chunk_states.shape)}")
+        n_states = chunk_states.shape[0]
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"dq": torch.empty(T, H, dk, **f32), "dk": torch.empty(T, H, dk, **f32),
+         "dv": torch.empty(T, H, dv, **f32),
+         "dlog_alpha": torch.empty(*((T, H) if scalar_gate else (T, H, dk)), **f32),
+         "dbeta": torch.empty(T, H, **f32), "dinit_state": torch.empty(N, H, dk, dv, **f32)}
+    flags = KDA_FLAG_SCALAR_GATE if scalar_gate else 0
+    need = int(lib.kda_chunk_prefill_varlen_backward_workspace_size(N, T, H, dk, dv, dt, flags,
+                                                                    int(chunk_states is not None)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_prefill_varlen_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                               _ptr(cu_seqlens), _ptr(initial_state), _ptr(chunk_states),
+                                               n_states, _ptr(d_o), _ptr(d_final_state), _ptr(g["dq"]),
+                                               _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_alpha"]),
+                                               _ptr(g["dbeta"]), _ptr(g["dinit_state"]), N, T, H, dk, dv, dt,
+                                               flags, _ptr(workspace), wbytes, _stream())
+    _check("kda_chunk_prefill_varlen_backward", st)
+    return g
 
 
 def decode_step(q, k, v, log_alpha, beta, state, mask=None, l2norm_qk=False, out=None,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert lib.kda_status_string(code).decode().startswith(kda.STATUS[code])
     assert lib.kda_status_string(17) == b"unknown kda_status"
@@ -377,3 +377,55 @@ def test_backward_validation(lib):
     assert lib.kda_chunk_prefill_backward_workspace_size(64, 64 * 1024, 64, 128, 128, 0, 0, 1) == 0
     assert call(B=64, T=64 * 1023, H=64, ws=None) == WORKSPACE
     assert call(B=64, T=64 * 1024, H=64, ws=None) == UNSUPPORTED
+
+
+def test_varlen_backward_validation(lib):
+    """kda_chunk_prefill_varlen_backward: the backward's checks plus cu_seqlens, and a
+    workspace of ceil(T/64) + N chunk slots per head (with the states given, that of a batch
+    row of as many chunks plus the sequence and chunk tables)."""
+    size = lib.kda_chunk_prefill_varlen_backward_workspace_size
+    bsize = lib.kda_chunk_prefill_backward_workspace_size
+    # 3 sequences, 130 tokens: 3 + 3 = 6 slots per head, as a 384-token batch row; tables of
+    # 3 x 16 and 6 x 8 bytes, each rounded up to 256
+    assert size(3, 130, 2, 64, 64, 0, 0, 1) == bsize(1, 384, 2, 64, 64, 0, 0, 1) + 256 + 256
+    assert size(3, 130, 2, 64, 64, 1, 4, 1) == bsize(1, 384, 2, 64, 64, 1, 0, 1) + 512 + 2 * 130 * 2 * 64 * 4
+    # without the states, the packed forward's workspace, outputs and checkpoints come in
+    assert size(3, 130, 2, 64, 64, 0, 0, 0) > size(3, 130, 2, 64, 64, 0, 0, 1) + \
+        lib.kda_chunk_prefill_varlen_workspace_size(3, 130, 2, 64, 64, 64, 0)
+    assert size(3, 0, 2, 64, 64, 0, 0, 1) > 0              # the sequence table: d_init = d_final
+    assert size(3, 130, 2, 64, 64, 0, 1, 0) == 0           # L2 flag: unsupported
+    assert size(3, 130, 2, 48, 64, 0, 0, 0) == 0
+    assert size(70000, 130, 2, 64, 64, 0, 0, 0) == 0       # N <= 65535
+    # launch extents: H (ceil(T/64) + N) <= 2^22 - 8
+    assert size(15, 64 * 65520, 64, 128, 128, 0, 0, 1) > 0
+    assert size(15, 64 * 65521, 64, 128, 128, 0, 0, 1) == 0
+    cu = FAKE
+
+    def call(**kw):
+        a = dict(N=2, T=100, H=2, dk=64, dv=64, dtype=0, flags=0, q=FAKE, dq=FAKE, s0=None, dinit=FAKE,
+                 ws=FAKE, wsb=1 << 30, cs=None, ns=0, cu=cu)
+        a.update(kw)
+        return lib.kda_chunk_prefill_varlen_backward(a["q"], FAKE, FAKE, FAKE, FAKE, a["cu"], a["s0"], a["cs"],
+                                                     a["ns"], FAKE, None, a["dq"], FAKE, FAKE, FAKE, FAKE,
+                                                     a["dinit"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                                     a["dtype"], a["flags"], a["ws"], a["wsb"], None)
+    assert call(flags=1) == UNSUPPORTED
+    assert call(flags=2) == INVALID
+    assert call(flags=4, ws=None) == WORKSPACE
+    assert call(cu=None) == INVALID
+    assert call(cu=ctypes.c_void_p(0x10002)) == INVALID      # int32 offsets
+    assert call(cs=FAKE, ns=-1) == INVALID
+    assert call(cs=MISALIGNED, ns=1) == INVALID
+    assert call(cs=FAKE, ns=1, ws=None) == WORKSPACE
+    assert call(q=None) == INVALID
+    assert call(dq=MISALIGNED) == INVALID
+    assert call(dinit=None) == INVALID
+    assert call(s0=MISALIGNED) == INVALID
+    assert call(dk=48) == UNSUPPORTED
+    assert call(N=-1) == INVALID
+    assert call(N=70000) == UNSUPPORTED
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(N=0) == OK                      # nothing to do
+    assert call(H=0) == OK
+    assert call(N=15, T=64 * 65521, H=64, dk=128, dv=128, ws=None) == UNSUPPORTED
