@@ -12,7 +12,8 @@ same 128k tokens prefilled as 32 packed prompts of seeded lengths (kda_chunk_pre
 The training backward (kda_chunk_prefill_backward) is timed on the chunked-prefill training
 shape (B=4, H=32, T=4096): fed with the chunk-end states that the training forward
 (kda_chunk_prefill_states) saves, and as the self-contained call that runs the forward again,
-with the plain forward on the same inputs beside them.
+with the plain forward on the same inputs beside them; the same tokens as 12 packed documents
+(kda_chunk_prefill_varlen with 64-token checkpoints, then kda_chunk_prefill_varlen_backward).
 Prints one JSON line.
 """
 import argparse
@@ -42,7 +43,7 @@ MEASURED_TRAFFIC = {
     "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
     # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
-    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "e9d879d30a82ea56", "bytes": 8.880e9},
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "d0b285d86bdb6480", "bytes": 8.878e9},
 }
 
 
@@ -161,6 +162,7 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path would shard over heads/sequences, see the design notes)", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     from linear_attention_recurrence_kda_amd import datagen as D
     from linear_attention_recurrence_kda_amd import kda
@@ -365,6 +367,37 @@ def main():
         bwd_ms = timed(backward)                 # reads the states forward_states left in ckb
         rec_ms = timed(backward_recompute)
         fwd_ms = timed(forward)
+
+        # the same tokens as 12 documents packed end to end (seeded cut points): the packed
+        # training forward with 64-token checkpoints, then the packed backward fed with them
+        NP = 12
+        cuts = np.sort(np.random.default_rng(6).choice(np.arange(1, Bb * Tb), NP - 1, replace=False))
+        cu_np = np.concatenate([[0], cuts, [Bb * Tb]]).astype(np.int32)
+        plen = np.diff(cu_np)
+        cup = torch.from_numpy(cu_np).to(dev)
+        pk = tuple(x.view(Bb * Tb, *x.shape[2:]) for x in fargs)
+        dop = dob.view(Bb * Tb, H, dv)
+        dfp = torch.randn(NP, H, dk, dv, device=dev, generator=gb)
+        ckp = torch.empty(int((plen // 64).sum()), H, dk, dv, dtype=torch.float32, device=dev)
+        fsp = torch.empty(NP, H, dk, dv, dtype=torch.float32, device=dev)
+        wfp = torch.empty(kda.prefill_varlen_workspace_size(NP, Bb * Tb, H, dk, dv, 64, kda.KDA_BF16),
+                          dtype=torch.uint8, device=dev)
+        wsp = torch.empty(kda.varlen_backward_workspace_size(NP, Bb * Tb, H, dk, dv, kda.KDA_BF16, states_given=True),
+                          dtype=torch.uint8, device=dev)
+
+        def forward_states_packed():
+            kda.chunk_prefill_varlen(*pk, cup, chunk_size=64, state_interval=64, chunk_states=ckp,
+                                     out=ob.view(Bb * Tb, H, dv), final_state=fsp, workspace=wfp)
+
+        def backward_packed():
+            return kda.chunk_prefill_varlen_backward(*pk, cup, dop, d_final_state=dfp, chunk_states=ckp,
+                                                     workspace=wsp)
+        pfst_ms = timed(forward_states_packed)
+        pbwd_ms = timed(backward_packed)
+        packed_line = {"documents": NP, "len_min": int(plen.min()), "len_max": int(plen.max()),
+                       "forward_states_ms": pfst_ms, "ms": pbwd_ms, "training_step_ms": pfst_ms + pbwd_ms,
+                       "training_step_tokens_per_s": Bb * Tb / ((pfst_ms + pbwd_ms) * 1e-3)}
+        del ckp, fsp, wfp, wsp, dfp
         bth = Bb * Tb * H
         bwd_gbs = BACKWARD_STATES_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
         default_bwd = (Bb == 4 and Tb == 4096)    # the shape the measured traffic was taken on
@@ -376,6 +409,7 @@ def main():
                     "ms_recompute": rec_ms,
                     "forward_ms_same_inputs": fwd_ms,
                     "backward_over_forward": bwd_ms / fwd_ms,
+                    "packed": packed_line,
                     "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": bwd_gbs / HBM_PEAK_GBS,
                                  "traffic": measured_traffic("backward", default_bwd),
