@@ -43,7 +43,7 @@ MEASURED_TRAFFIC = {
     "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
     # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
-    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "d0b285d86bdb6480", "bytes": 8.878e9},
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "8e0849c7b94542d6", "bytes": 8.878e9},
 }
 
 

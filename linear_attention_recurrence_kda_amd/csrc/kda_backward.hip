@@ -31,6 +31,9 @@
 //   3. bwd_cc_kernel, one workgroup per (chunk, head): R, U, dv, dT', dbeta, dA, dG and dP;
 //   4. bwd_ck_kernel, one workgroup per (chunk, head, 32 key channels): the products over dv
 //      (dO S0^T, dR S0^T, U dS1^T) for its channels, then dq, dk and dlog_alpha.
+// For sequences packed end to end (cu_seqlens) a one-workgroup setup kernel first writes a
+// sequence table and a chunk table; each sequence's chunks start at its own first token, and
+// the same four kernels find their rows, entry states and workspace slots through them.
 // Products run on the bf16 MFMA with fp32 operands split into a bf16 high part and residual
 // (three MFMAs per product), except the reverse scan's Kh, W^T and Qt^T, which are single
 // bf16 with bf16 inputs (as the forward scan's Wn, Qt and Kh^T are).  A chunk in which some
@@ -182,9 +185,9 @@ __device__ __forceinline__ float sum16(float x) {
 
 // One lane's view of a chunk: row 16 w + l%16 (w = wave), channels c_base + 32 ks + 8 (l/16)
 // .. +7 of a window of KW channels (the A-operand layout).  q, k and log_alpha of rows that
-// are not valid (masked or past the sequence) and of channels past K are 0.  g becomes the inclusive
-// cumulative sum of log2 decay over the chunk's rows and s_gl the chunk's totals per channel
-// of the window.  Every thread must call it (it holds two barriers).
+// are not valid (masked or past the sequence) and of channels past K are 0.  g becomes the
+// inclusive cumulative sum of log2 decay over the chunk's rows and s_gl the chunk's totals
+// per channel of the window.  Every thread must call it (it holds two barriers).
 template <int DT, int KW>
 struct Rows {
   static constexpr int KS = KW / 32;
