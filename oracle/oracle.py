@@ -19,8 +19,9 @@ Contents
 * ``l2norm``: x / sqrt(sum x^2 + 1e-6), the reading taken for the configs'
   "L2-normalised per head".
 * ``np_prefill_backward``: the fp64 gradients of the token recurrence for the loss
-  sum_t <do_t, o_t> + <dfinal, S_T> (reverse-mode differentiation of the token loop),
-  pinned by central finite differences of the C forward in tests/test_oracle_grad.py.
+  sum_t <do_t, o_t> + <dfinal, S_T> (reverse-mode differentiation of the token loop; with
+  l2norm_qk, through the q/k normalisation as well), pinned by central finite differences
+  of the C forward in tests/test_oracle_grad.py.
 
 The recurrence (Kimi Linear summary page, recurrent-layers paragraph; the
 remio.ai page's section on KDA's recurrent memory): per (b, h), with rows of
@@ -187,7 +188,8 @@ def np_prefill(q, k, v, log_alpha, beta, mask=None, init_state=None, l2norm_qk=F
     return o, S
 
 
-def np_prefill_backward(q, k, v, log_alpha, beta, do, dfinal=None, mask=None, init_state=None):
+def np_prefill_backward(q, k, v, log_alpha, beta, do, dfinal=None, mask=None, init_state=None,
+                        l2norm_qk=False):
     """Gradients of the token recurrence (the blockwise training the remio.ai page names in
     its KDA section needs them): for the loss L = sum_t <do_t, o_t> + <dfinal, S_T>, the
     derivatives of L with respect to q, k, v, log_alpha, beta and the initial state, in fp64.
@@ -200,10 +202,17 @@ def np_prefill_backward(q, k, v, log_alpha, beta, do, dfinal=None, mask=None, in
         du = lam^T k_t;  dk_t = lam u;  dbeta_t = du . r;  dv_t = beta_t du
         dS' = lam - k_t (beta_t du)^T;  dk_t -= S' (beta_t du)
         dlog_alpha_t = rowsum(dS' * S');  lam <- Diag(a) dS'
-    A masked position leaves lam alone and has zero gradients.  Returns a dict with dq, dk,
-    dv, dlog_alpha, dbeta, dinit_state (the last is returned even without an initial state:
-    it is the gradient with respect to the zero state)."""
+    A masked position leaves lam alone and has zero gradients.  With l2norm_qk the loop runs
+    on q and k normalised as in np_prefill, x_hat = s x with s = (|x|^2 + eps)^(-1/2), and dq,
+    dk are taken back to the raw rows by the chain rule through that map:
+        dx = s dx_hat - s^3 x (x . dx_hat).
+    Returns a dict with dq, dk, dv, dlog_alpha, dbeta, dinit_state (the last is returned even
+    without an initial state: it is the gradient with respect to the zero state)."""
     q, k, v, la, beta, do = map(_f64, (q, k, v, log_alpha, beta, do))
+    raw = None
+    if l2norm_qk:
+        raw = {"dq": q, "dk": k}
+        q, k = l2norm(q), l2norm(k)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     S0 = np.zeros((B, H, dk, dv)) if init_state is None else np.array(_f64(init_state), copy=True)
@@ -246,6 +255,11 @@ def np_prefill_backward(q, k, v, log_alpha, beta, do, dfinal=None, mask=None, in
                 g["dlog_alpha"][b, t, h] = np.sum(dSp * Sp, axis=1)
                 lam[b, h] = a[:, None] * dSp
     g["dinit_state"] = lam
+    if raw is not None:
+        for n, x in raw.items():
+            sc = 1.0 / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2_EPS)
+            gx = g[n]
+            g[n] = sc * gx - sc ** 3 * x * np.sum(x * gx, axis=-1, keepdims=True)
     return g
 
 

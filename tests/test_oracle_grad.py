@@ -9,9 +9,9 @@ import pytest
 from linear_attention_recurrence_kda_amd import datagen as D
 
 
-def _loss(O, inp, do, dfinal, mask, s0):
+def _loss(O, inp, do, dfinal, mask, s0, l2=False):
     o, s = O.c_prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], mask=mask,
-                       init_state=s0, nthreads=1)
+                       init_state=s0, l2norm_qk=l2, nthreads=1)
     return float(np.sum(o * do) + np.sum(s * dfinal))
 
 
@@ -31,11 +31,13 @@ def _case(seed, B=2, T=9, H=2, dk=3, dv=4, masked=True):
     return inp, s0, do, dfinal, mask
 
 
-@pytest.mark.parametrize("masked", [False, True])
-def test_gradient_matches_central_differences(oracle, masked):
+@pytest.mark.parametrize("masked,l2", [(False, False), (True, False), (True, True)])
+def test_gradient_matches_central_differences(oracle, masked, l2):
+    """With l2, the C forward normalises q and k itself (its own code, pinned against the NumPy
+    twin), so the differences also pin the chain rule through the normalisation."""
     inp, s0, do, dfinal, mask = _case(3, masked=masked)
     g = oracle.np_prefill_backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do, dfinal,
-                                   mask=mask, init_state=s0)
+                                   mask=mask, init_state=s0, l2norm_qk=l2)
     eps = 1e-6
     names = {"q": "dq", "k": "dk", "v": "dv", "log_alpha": "dlog_alpha", "beta": "dbeta"}
     for n, gn in list(names.items()) + [("s0", "dinit_state")]:
@@ -44,9 +46,9 @@ def test_gradient_matches_central_differences(oracle, masked):
         for idx in np.ndindex(base.shape):
             keep = base[idx]
             base[idx] = keep + eps
-            lp = _loss(oracle, inp, do, dfinal, mask, s0)
+            lp = _loss(oracle, inp, do, dfinal, mask, s0, l2)
             base[idx] = keep - eps
-            lm = _loss(oracle, inp, do, dfinal, mask, s0)
+            lm = _loss(oracle, inp, do, dfinal, mask, s0, l2)
             base[idx] = keep
             fd[idx] = (lp - lm) / (2 * eps)
         err = np.max(np.abs(fd - g[gn]))
@@ -81,3 +83,19 @@ def test_gradient_is_linear_in_the_cotangents(oracle):
     for n in g1:
         assert np.allclose(g2[n], 2.0 * g1[n], rtol=1e-12, atol=1e-12), n
         assert np.all(g0[n] == 0), n
+
+
+def test_gradient_l2_radial_direction_is_null(oracle):
+    """Scaling a row of q or k leaves its normalised row unchanged (up to the eps), so with
+    the norm inside the call the raw gradient has no radial part: x . dx ~ 0 for every row,
+    while without the norm it does not vanish."""
+    inp, s0, do, dfinal, mask = _case(11, masked=False)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do, dfinal)
+    g = oracle.np_prefill_backward(*args, init_state=s0, l2norm_qk=True)
+    g0 = oracle.np_prefill_backward(*args, init_state=s0)
+    for n, x in (("dq", inp["q"]), ("dk", inp["k"])):
+        radial = np.abs(np.sum(x * g[n], axis=-1))
+        scale = np.linalg.norm(x, axis=-1) * np.linalg.norm(g[n], axis=-1)
+        # the eps leaves a radial part of relative size eps / |x|^2
+        assert np.all(radial <= 1e-5 * scale + 1e-12), n
+        assert np.max(np.abs(np.sum(x * g0[n], axis=-1))) > 1e-3, n
