@@ -291,9 +291,13 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  * and B*H*ceil(T/64) <= 2^22 - 8 (launch extents in threads fit 32 bits);
  * flags may hold KDA_FLAG_SCALAR_GATE (Gated DeltaNet's gate, one value per (token, head):
  * the gate is applied to every channel and its gradient is the sum over the channels, so
- * the other gradients equal those of a per-channel call fed the broadcast gate bit for bit);
- * KDA_FLAG_L2NORM_QK returns KDA_ERR_UNSUPPORTED (normalise q and k before the call and
- * let the caller's autodiff take that step), other bits KDA_ERR_INVALID_ARG.
+ * the other gradients equal those of a per-channel call fed the broadcast gate bit for bit)
+ * and KDA_FLAG_L2NORM_QK (the gradients of the prefill that normalises q and k with that
+ * flag: the pass runs on the normalised rows, formed as the forward forms them, and dq, dk
+ * are taken back to the raw rows at the end, dx = s dx_hat - s^3 x (x . dx_hat) with
+ * s = (|x|^2 + 1e-6)^-1/2; the workspace holds the two row scales, 8 bytes per token and
+ * head; chunk_states must then come from a forward with the flag); other bits
+ * KDA_ERR_INVALID_ARG.
  * 16-byte aligned: q, k, v, d_o, init_state, chunk_states, dq, dk, dv, and log_alpha and
  * d_log_alpha unless KDA_FLAG_SCALAR_GATE is set (then 4-byte); 4-byte: beta, d_beta,
  * d_final_state, d_init_state; workspace 256-byte aligned.

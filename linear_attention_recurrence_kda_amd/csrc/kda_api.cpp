@@ -162,10 +162,11 @@ static bool backward_shape_ok(int B, int T, int H, int dk, int dv, bool varlen) 
 static size_t backward_size(int B, int T, int H, int dk, int dv, int dtype, unsigned flags, int states_given,
                             bool varlen) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype) || !backward_shape_ok(B, T, H, dk, dv, varlen) ||
-      (flags & ~(unsigned)KDA_FLAG_SCALAR_GATE) != 0)
+      (flags & ~(unsigned)(KDA_FLAG_SCALAR_GATE | KDA_FLAG_L2NORM_QK)) != 0)
     return 0;
   return kda::backward_workspace_bytes(B, T, H, dk, dv, dtype, states_given != 0,
-                                       (flags & KDA_FLAG_SCALAR_GATE) != 0, varlen);
+                                       (flags & KDA_FLAG_SCALAR_GATE) != 0, varlen,
+                                       (flags & KDA_FLAG_L2NORM_QK) != 0);
 }
 
 static int backward_entry(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -176,8 +177,7 @@ static int backward_entry(const void* q, const void* k, const void* v, const flo
                           unsigned flags, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
   if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
-  if (flags & KDA_FLAG_L2NORM_QK) return KDA_ERR_UNSUPPORTED;      // normalise q and k before the call
-  const bool sg = (flags & KDA_FLAG_SCALAR_GATE) != 0;
+  const bool sg = (flags & KDA_FLAG_SCALAR_GATE) != 0, l2 = (flags & KDA_FLAG_L2NORM_QK) != 0;
   if (!backward_shape_ok(B, T, H, dk_, dv_, varlen)) return KDA_ERR_UNSUPPORTED;
   if ((size_t)B * H == 0) return KDA_OK;
   if (d_init_state == nullptr || !aligned(d_init_state, 4)) return KDA_ERR_INVALID_ARG;
@@ -198,12 +198,13 @@ static int backward_entry(const void* q, const void* k, const void* v, const flo
     // the chunk-end states are read with 16-byte vector loads
     if (chunk_states != nullptr && !aligned(chunk_states, 16)) return KDA_ERR_INVALID_ARG;
   }
-  const size_t need = kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr, sg, varlen);
+  const size_t need =
+      kda::backward_workspace_bytes(B, T, H, dk_, dv_, dtype, chunk_states != nullptr, sg, varlen, l2);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
     return KDA_ERR_WORKSPACE;
   kda::BackwardArgs a{q, k, v, d_o, log_alpha, beta, init_state, d_final_state, varlen ? nullptr : mask,
                       chunk_states, dq, dk, dv, d_log_alpha, d_beta, d_init_state, B, T, H, dk_, dv_, dtype,
-                      sg ? 1 : 0, workspace, stream, varlen ? cu_seqlens : nullptr, num_states};
+                      sg ? 1 : 0, workspace, stream, varlen ? cu_seqlens : nullptr, num_states, l2 ? 1 : 0};
   return hip_status(kda::launch_backward(a));
 }
 

@@ -79,6 +79,9 @@ struct Params {
   // (sequence, chunk within it), (-1, -1) past the last; both null for a padded batch
   const int4* seqs;
   const int2* cmap;
+  // with the q/k L2 norm: per token and head the row scales (q, k) = (|x|^2 + 1e-6)^-1/2,
+  // written by the prep, (0, 0) where the row is not valid; null without the norm
+  float2* qks;
   int B, T, H, K, V, NC, NCf;              // packed: B = sequences, T = tokens, NC = chunk slots
   int num_states;                          // checkpoints ck holds (entries past it read as zero)
 };
@@ -193,10 +196,14 @@ struct Rows {
   static constexpr int KS = KW / 32;
   float k[KS][8], q[KS][8], g[KS][8];
   float beta;
+  float qsc, ksc;                          // the row's L2 scales (1 without the norm)
   bool ok;
 };
 
-template <int DT, int KW, bool WANT_Q>
+// With the q/k L2 norm, OWN_SCALE (the full channel window, q loaded) forms the row scales
+// as the forward prep does (the same per-lane sums in the same order, so the same values)
+// and stores them; the other callers read them.
+template <int DT, int KW, bool WANT_Q, bool OWN_SCALE = false>
 __device__ __forceinline__ void load_rows(const Params& p, const ChunkLoc& L, int h, int c_base, Rows<DT, KW>& R,
                                           float* s_tot, float* s_gl) {
   using E = Elem<DT>;
@@ -222,6 +229,10 @@ __device__ __forceinline__ void load_rows(const Params& p, const ChunkLoc& L, in
   }
   R.ok = r < L.rows && mk != 0;
   R.beta = R.ok ? bt : 0.f;
+  R.qsc = 1.f;
+  R.ksc = 1.f;
+  float2 sc = make_float2(1.f, 1.f);
+  if (!OWN_SCALE && p.qks != nullptr) sc = p.qks[tk];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const bool cok = R.ok && c_base + 32 * ks + cg < p.K;
@@ -236,6 +247,28 @@ __device__ __forceinline__ void load_rows(const Params& p, const ChunkLoc& L, in
 #pragma unroll
       for (int e = 0; e < 8; ++e) R.q[ks][e] = 0.f;
     }
+  }
+  if (p.qks != nullptr) {
+    if constexpr (OWN_SCALE) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { sq += R.q[ks][e] * R.q[ks][e]; sk += R.k[ks][e] * R.k[ks][e]; }
+      sq += __shfl_xor(sq, 16, 64); sk += __shfl_xor(sk, 16, 64);
+      sq += __shfl_xor(sq, 32, 64); sk += __shfl_xor(sk, 32, 64);
+      sc = make_float2(rsqrtf(sq + 1e-6f), rsqrtf(sk + 1e-6f));
+      if (lane < 16 && r < L.rows) p.qks[tk] = R.ok ? sc : make_float2(0.f, 0.f);
+    }
+    R.qsc = R.ok ? sc.x : 0.f;
+    R.ksc = R.ok ? sc.y : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { R.k[ks][e] *= R.ksc; R.q[ks][e] *= R.qsc; }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = R.g[ks][e] * kLog2e;
@@ -296,7 +329,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_prep_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) float s_x[kC * RS];    // Qt; Ki or g; A and P; Kt
   __shared__ __attribute__((aligned(16))) float s_M[kC * LC];
   __shared__ __attribute__((aligned(16))) float s_stage[4 * 256];
-  __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC];
+  __shared__ float s_tot[4 * KP], s_gl[KP], s_beta[kC], s_ok[kC], s_qsc[kC], s_ksc[kC];
   __shared__ uint32_t s_vb[4];
   float* s_A = s_x;                                              // after G and P are formed
   float* s_P = s_x + kC * LC;
@@ -310,8 +343,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_prep_kernel(Params p) {
   const size_t ch = L.ch;
 
   Rows<DT, KP> R;
-  load_rows<DT, KP, true>(p, L, h, 0, R, s_tot, s_gl);
-  if (lane < 16) { s_beta[r] = R.beta; s_ok[r] = R.ok ? 1.f : 0.f; }
+  load_rows<DT, KP, true, true>(p, L, h, 0, R, s_tot, s_gl);
+  if (lane < 16) { s_beta[r] = R.beta; s_ok[r] = R.ok ? 1.f : 0.f; s_qsc[r] = R.qsc; s_ksc[r] = R.ksc; }
   {
     // validity of the chunk's rows as one 64-bit word (wave w holds rows 16 w .. +15)
     const unsigned long long bal = __ballot(R.ok) & 0xffffull;
@@ -409,11 +442,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_prep_kernel(Params p) {
         if (jj <= ii && s_ok[ii] != 0.f && s_ok[jj] != 0.f) {
           const size_t ti = ((L.t0 + ii) * p.H + h) * p.K;
           const size_t tj = ((L.t0 + jj) * p.H + h) * p.K;
+          // the L2 scales are 1 without the norm (an exact product)
+          const float ski = s_ksc[ii], sqi = s_qsc[ii], skj = s_ksc[jj];
           for (int c = 0; c < p.K; ++c) {
             const float d = exp2f(s_x[ii * LD + c] - s_x[jj * LD + c]);
-            const float kj = E::ld(kg, tj + c) * d;
-            gs += E::ld(kg, ti + c) * kj;
-            ps += E::ld(qg, ti + c) * kj;
+            const float kj = E::ld(kg, tj + c) * skj * d;
+            gs += E::ld(kg, ti + c) * ski * kj;
+            ps += E::ld(qg, ti + c) * sqi * kj;
           }
         }
         gt[J][i] = gs;
@@ -1118,7 +1153,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   float* const s_dG = s_dP + kTri;
   __bf16* const s_ya = reinterpret_cast<__bf16*>(s_x);   // [dO, dR, U][high, residual][row][v]
   __bf16* const s_yb = s_ya + 3 * 2 * kYA;                // [S0, dS1][high, residual][channel][v]
-  __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW], s_ss[SW];
+  __shared__ float s_tot[4 * SW], s_gl[SW], s_ok[kC], s_half[2][2][SW], s_ss[SW], s_qsc[kC], s_ksc[kC];
 
   // XCD-aware mapping: the KP / SW channel slices of one chunk share blockIdx.x % 8 and are
   // dispatched 8 blocks apart, so the rows every slice reads (dO, dR, U, dP, dG) come from one L2
@@ -1261,7 +1296,7 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
   }
   Rows<DT, SW> R;
   load_rows<DT, SW, true>(p, L, h, c_base, R, s_tot, s_gl);
-  if (lane < 16) s_ok[r] = R.ok ? 1.f : 0.f;
+  if (lane < 16) { s_ok[r] = R.ok ? 1.f : 0.f; s_qsc[r] = R.qsc; s_ksc[r] = R.ksc; }
   const bool fast = __syncthreads_and(tid >= SW || s_gl[tid] >= kFastLimit);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -1351,7 +1386,11 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
       const int row = 16 * I + 4 * g4 + i;
       const float gv = s_g[row * LD + lc];
       const bool ok = s_ok[row] != 0.f && cin;
-      const float kv = ok ? kr[i] : 0.f, qv = ok ? qr[i] : 0.f;
+      float kv = ok ? kr[i] : 0.f, qv = ok ? qr[i] : 0.f;
+      if (p.qks != nullptr) {                        // the normalised rows
+        kv *= s_ksc[row];
+        qv *= s_qsc[row];
+      }
       float Xq, Xk1, Xk2, Xk3;
       if (fast) {
         const float gm = exp2f(gv), gi = exp2f(-gv);
@@ -1469,6 +1508,53 @@ gate_reduce_kernel(const float* __restrict__ dla_pc, float* __restrict__ dla, si
   }
 }
 
+// ---------------------------------------------------------------- q/k L2 norm
+// With the norm inside the call the pass differentiates with respect to the normalised rows
+// x_hat = s x, s = (|x|^2 + 1e-6)^-1/2; this maps each row's gradient back to the raw row,
+// in place: dx = s dx_hat - s^3 x (x . dx_hat).  Four threads per row as above, K/4 channels
+// each (a multiple of 4); a row whose scale is 0 (not valid) gets 0.
+template <int DT>
+__global__ void __launch_bounds__(kGateThreads)
+l2_grad_kernel(const void* __restrict__ q, const void* __restrict__ k, const float2* __restrict__ qks,
+               float* __restrict__ dq, float* __restrict__ dk, size_t rows, int K) {
+  using E = Elem<DT>;
+  using Tp = typename E::T;
+  const int per = K / 4;
+  const size_t stride = (size_t)gridDim.x * kGateThreads;
+  for (size_t base = (size_t)blockIdx.x * kGateThreads; base < rows * 4; base += stride) {
+    const size_t g = base + threadIdx.x, row = g / 4;
+    const bool in = row < rows;
+    const size_t off = (in ? row : 0) * K + (size_t)(g % 4) * per;
+    const float2 sc = qks[in ? row : 0];
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const Tp* x = (const Tp*)(which == 0 ? q : k);
+      float* d = which == 0 ? dq : dk;
+      const float s = which == 0 ? sc.x : sc.y;
+      float dot = 0.f;
+      for (int c = 0; c < per; c += 4) {
+        float xv[4];
+        E::ld4(x, off + c, xv);
+        const float4 dv = *reinterpret_cast<const float4*>(d + off + c);
+        dot += (xv[0] * dv.x + xv[1] * dv.y) + (xv[2] * dv.z + xv[3] * dv.w);
+      }
+      dot += __shfl_xor(dot, 1, 64);
+      dot += __shfl_xor(dot, 2, 64);
+      const float t = s * s * s * dot;
+      if (!in) continue;
+      for (int c = 0; c < per; c += 4) {
+        float xv[4];
+        E::ld4(x, off + c, xv);
+        float4 dv = *reinterpret_cast<const float4*>(d + off + c);
+        dv = s != 0.f ? make_float4(s * dv.x - t * xv[0], s * dv.y - t * xv[1], s * dv.z - t * xv[2],
+                                    s * dv.w - t * xv[3])
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(d + off + c) = dv;
+      }
+    }
+  }
+}
+
 static unsigned gate_blocks(size_t items) {
   const size_t b = (items + kGateThreads - 1) / kGateThreads;
   return (unsigned)(b < kGateMaxBlocks ? b : kGateMaxBlocks);
@@ -1527,7 +1613,7 @@ bwd_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int NC, int4* __r
 // workspace, its discarded outputs and the chunk-end states): `own` bytes suffice when the
 // caller hands the states in.
 struct Layout {
-  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, lab, dlab, seqs, cmap, own, fwd, o, fin, ck, total;
+  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, lab, dlab, qks, seqs, cmap, own, fwd, o, fin, ck, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1539,7 +1625,7 @@ long long chunk_slots(int B, int T, bool varlen) {
   return varlen && T > 0 ? nc + B : nc;
 }
 
-Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate, bool varlen) {
+Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate, bool varlen, bool l2) {
   Layout L{};
   if (B == 0 || H == 0 || (T <= 0 && !varlen)) return L;
   const int KP = kpad(dk);
@@ -1567,6 +1653,7 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate, 
     L.lab = take(tokens * H * dk * 4);
     L.dlab = take(tokens * H * dk * 4);
   }
+  if (l2) L.qks = take(tokens * H * 8);     // the row scales of q and k
   if (varlen) {
     L.seqs = take((size_t)B * 16);
     L.cmap = take((size_t)NC * 8);
@@ -1634,14 +1721,15 @@ bool backward_grid_ok(int B, int T, int H, bool varlen) {
 }
 
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given,
-                                bool scalar_gate, bool varlen) {
-  const Layout L = layout(B, T, H, dk, dv, dtype, scalar_gate, varlen);
+                                bool scalar_gate, bool varlen, bool l2) {
+  const Layout L = layout(B, T, H, dk, dv, dtype, scalar_gate, varlen, l2);
   return states_given ? L.own : L.total;
 }
 
 hipError_t launch_backward(const BackwardArgs& a) {
   const bool varlen = a.cu_seqlens != nullptr;
-  const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype, a.scalar_gate != 0, varlen);
+  const bool l2 = a.l2norm != 0;
+  const Layout L = layout(a.B, a.T, a.H, a.dk_, a.dv_, a.dtype, a.scalar_gate != 0, varlen, l2);
   unsigned char* ws = (unsigned char*)a.workspace;
   hipStream_t st = (hipStream_t)a.stream;
   const int NC = (int)chunk_slots(a.B, a.T, varlen), NCf = a.T / kC;
@@ -1678,6 +1766,7 @@ hipError_t launch_backward(const BackwardArgs& a) {
     f.workspace_bytes = L.o - L.fwd;
     f.stream = a.stream;
     f.cu_seqlens = a.cu_seqlens;
+    f.l2norm = l2 ? 1 : 0;
     f.chunk_states = own_states > 0 ? (float*)(ws + L.ck) : nullptr;
     f.num_states = own_states;
     f.state_interval = kC;
@@ -1701,10 +1790,23 @@ hipError_t launch_backward(const BackwardArgs& a) {
     p.seqs = (const int4*)(ws + L.seqs);
     p.cmap = (const int2*)(ws + L.cmap);
   }
+  if (l2 && rows > 0) p.qks = (float2*)(ws + L.qks);
   p.num_states = a.chunk_states != nullptr ? (varlen ? a.num_states : a.B * NCf) : own_states;
   p.B = a.B; p.T = a.T; p.H = a.H; p.K = a.dk_; p.V = a.dv_; p.NC = NC; p.NCf = NCf;
   hipError_t e = a.dtype == 0 ? launch_dt<0>(p, st) : launch_dt<1>(p, st);
-  if (e != hipSuccess || !a.scalar_gate || rows == 0) return e;
+  if (e != hipSuccess || rows == 0) return e;
+  if (l2) {
+    // dq and dk so far are with respect to the normalised rows
+    if (a.dtype == 0)
+      hipLaunchKernelGGL(l2_grad_kernel<0>, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st, a.q, a.k,
+                         (const float2*)p.qks, a.dq, a.dk, rows, a.dk_);
+    else
+      hipLaunchKernelGGL(l2_grad_kernel<1>, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st, a.q, a.k,
+                         (const float2*)p.qks, a.dq, a.dk, rows, a.dk_);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!a.scalar_gate) return hipSuccess;
   hipLaunchKernelGGL(gate_reduce_kernel, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st,
                      (const float*)dla, a.dla, rows, a.dk_);
   return hipGetLastError();

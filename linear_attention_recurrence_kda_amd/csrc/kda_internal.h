@@ -77,13 +77,14 @@ struct BackwardArgs {
   void* stream;
   const int32_t* cu_seqlens;               // packed sequences (then B = their number, no mask), or null
   int num_states;                          // packed: entries chunk_states holds
+  int l2norm;                              // q and k normalised inside the call (as the forward's flag)
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 // varlen: B packed sequences of T tokens in total
 size_t backward_workspace_bytes(int B, int T, int H, int dk, int dv, int dtype, bool states_given,
-                                bool scalar_gate, bool varlen);
+                                bool scalar_gate, bool varlen, bool l2);
 // every backward launch's grid fits (the forward inside it is checked by prefill_grid_ok)
 bool backward_grid_ok(int B, int T, int H, bool varlen);
 hipError_t launch_short_conv(const ConvArgs& a);

@@ -251,22 +251,29 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
     return out, final_state
 
 
-def backward_workspace_size(B, T, H, dk, dv, dtype_code, states_given=False, scalar_gate=False):
+def _bwd_flags(scalar_gate, l2norm_qk):
+    return (KDA_FLAG_SCALAR_GATE if scalar_gate else 0) | (KDA_FLAG_L2NORM_QK if l2norm_qk else 0)
+
+
+def backward_workspace_size(B, T, H, dk, dv, dtype_code, states_given=False, scalar_gate=False,
+                            l2norm_qk=False):
     """Bytes of workspace kda_chunk_prefill_backward needs (less when the chunk-end states
-    are given, more with the per-head gate)."""
+    are given, more with the per-head gate or the q/k norm)."""
     return int(load().kda_chunk_prefill_backward_workspace_size(
-        B, T, H, dk, dv, dtype_code, KDA_FLAG_SCALAR_GATE if scalar_gate else 0, int(bool(states_given))))
+        B, T, H, dk, dv, dtype_code, _bwd_flags(scalar_gate, l2norm_qk), int(bool(states_given))))
 
 
 def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, mask=None,
-                           initial_state=None, workspace=None, chunk_states=None, scalar_gate=False):
+                           initial_state=None, workspace=None, chunk_states=None, scalar_gate=False,
+                           l2norm_qk=False):
     """Gradients of chunk_prefill for L = sum <d_o, o> + <d_final_state, final_state>.
     Inputs as for chunk_prefill (no flags); d_o [B,T,H,dv] in q's dtype, d_final_state
     [B,H,dk,dv] fp32 or None.  chunk_states: the states chunk_prefill_states wrote for the
     same inputs with state_interval = 64, or None (the forward then runs again inside the
     call).  scalar_gate: log_alpha is one gate per (token, head), [B,T,H], and so is its
-    gradient.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha, dbeta (shapes of the
-    inputs) and dinit_state [B,H,dk,dv]."""
+    gradient.  l2norm_qk: the forward normalised q and k (chunk_prefill's flag); dq and dk are
+    then the gradients with respect to the raw q and k.  Returns a dict of fp32 tensors dq,
+    dk, dv, dlog_alpha, dbeta (shapes of the inputs) and dinit_state [B,H,dk,dv]."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -293,7 +300,7 @@ def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, ma
          "dv": torch.empty(B, T, H, dv, **f32),
          "dlog_alpha": torch.empty(*((B, T, H) if scalar_gate else (B, T, H, dk)), **f32),
          "dbeta": torch.empty(B, T, H, **f32), "dinit_state": torch.empty(B, H, dk, dv, **f32)}
-    flags = KDA_FLAG_SCALAR_GATE if scalar_gate else 0
+    flags = _bwd_flags(scalar_gate, l2norm_qk)
     need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt, flags, int(chunk_states is not None)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -392,23 +399,25 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     return out, final_state
 
 
-def varlen_backward_workspace_size(N, T, H, dk, dv, dtype_code, states_given=False, scalar_gate=False):
+def varlen_backward_workspace_size(N, T, H, dk, dv, dtype_code, states_given=False, scalar_gate=False,
+                                   l2norm_qk=False):
     """Bytes of workspace kda_chunk_prefill_varlen_backward needs."""
     return int(load().kda_chunk_prefill_varlen_backward_workspace_size(
-        N, T, H, dk, dv, dtype_code, KDA_FLAG_SCALAR_GATE if scalar_gate else 0, int(bool(states_given))))
+        N, T, H, dk, dv, dtype_code, _bwd_flags(scalar_gate, l2norm_qk), int(bool(states_given))))
 
 
 def chunk_prefill_varlen_backward(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_final_state=None,
-                                  initial_state=None, chunk_states=None, workspace=None, scalar_gate=False):
-    """Gradients of chunk_prefill_varlen (no slots, no L2 flag) for
+                                  initial_state=None, chunk_states=None, workspace=None, scalar_gate=False,
+                                  l2norm_qk=False):
+    """Gradients of chunk_prefill_varlen (no slots) for
     L = sum <d_o, o> + sum_i <d_final_state[i], final_state[i]>.  Inputs as for
     chunk_prefill_varlen: q,k [T,H,dk], v [T,H,dv], log_alpha [T,H,dk] ([T,H] with
     scalar_gate), beta [T,H], cu_seqlens [N+1] int32 on the GPU, initial_state [N,H,dk,dv] or
     None; d_o [T,H,dv] in q's dtype, d_final_state [N,H,dk,dv] fp32 or None.  chunk_states:
     the checkpoints chunk_prefill_varlen wrote for the same inputs with state_interval = 64
-    ([M,H,dk,dv]), or None (the forward then runs again inside the call).  Returns a dict of
-    fp32 tensors dq, dk, dv, dlog_alpha, dbeta (shapes of the inputs) and dinit_state
-    [N,H,dk,dv]."""
+    ([M,H,dk,dv]), or None (the forward then runs again inside the call).  scalar_gate and
+    l2norm_qk as for chunk_prefill_backward.  Returns a dict of fp32 tensors dq, dk, dv,
+    dlog_alpha, dbeta (shapes of the inputs) and dinit_state [N,H,dk,dv]."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -439,7 +448,7 @@ def chunk_prefill_varlen_backward(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_f
          "dv": torch.empty(T, H, dv, **f32),
          "dlog_alpha": torch.empty(*((T, H) if scalar_gate else (T, H, dk)), **f32),
          "dbeta": torch.empty(T, H, **f32), "dinit_state": torch.empty(N, H, dk, dv, **f32)}
-    flags = KDA_FLAG_SCALAR_GATE if scalar_gate else 0
+    flags = _bwd_flags(scalar_gate, l2norm_qk)
     need = int(lib.kda_chunk_prefill_varlen_backward_workspace_size(N, T, H, dk, dv, dt, flags,
                                                                     int(chunk_states is not None)))
     if workspace is None and need > 0:

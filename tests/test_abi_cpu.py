@@ -325,8 +325,9 @@ def test_large_chunks_are_rejected(lib):
 
 
 def test_backward_validation(lib):
-    """kda_chunk_prefill_backward rejects bad arguments before any HIP call: flags other
-    than 0, unsupported head sizes, missing or misaligned pointers, a short workspace."""
+    """kda_chunk_prefill_backward rejects bad arguments before any HIP call: flags other than
+    the per-head gate and the q/k norm, unsupported head sizes, missing or misaligned
+    pointers, a short workspace."""
     assert lib.kda_chunk_prefill_backward_workspace_size(1, 0, 4, 128, 128, 0, 0, 0) == 0
     assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 24, 128, 0, 0, 0) == 0
     assert lib.kda_chunk_prefill_backward_workspace_size(1, 16, 4, 64, 64, 7, 0, 0) == 0
@@ -348,14 +349,18 @@ def test_backward_validation(lib):
                                               a["dq"], FAKE, FAKE, FAKE, FAKE, a["dinit"],
                                               a["B"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"],
                                               a["flags"], a["ws"], a["wsb"], None)
-    assert call(flags=1) == UNSUPPORTED       # L2 norm inside the call is forward-only
+    assert call(flags=1, ws=None) == WORKSPACE   # the q/k L2 norm: accepted
+    assert call(flags=5, ws=None) == WORKSPACE
     assert call(flags=2) == INVALID           # SILU belongs to the short conv
     assert call(flags=8) == INVALID
     assert call(flags=4, ws=None) == WORKSPACE   # the per-head gate: accepted
     # the per-head gate needs its broadcast and per-channel gradient in the workspace
     assert (lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 4, 0)
             == lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0) + 2 * 2 * 130 * 3 * 64 * 4)
-    assert lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 1, 0) == 0
+    # the q/k norm adds the two row scales per token and head (rounded up to 256 bytes)
+    assert (lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 1, 0)
+            == lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0) + 6400)
+    assert lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 2, 0) == 0
     assert call(dk=48) == UNSUPPORTED
     assert call(dtype=5) == INVALID
     assert call(T=-1) == INVALID
@@ -393,7 +398,8 @@ def test_varlen_backward_validation(lib):
     assert size(3, 130, 2, 64, 64, 0, 0, 0) > size(3, 130, 2, 64, 64, 0, 0, 1) + \
         lib.kda_chunk_prefill_varlen_workspace_size(3, 130, 2, 64, 64, 64, 0)
     assert size(3, 0, 2, 64, 64, 0, 0, 1) > 0              # the sequence table: d_init = d_final
-    assert size(3, 130, 2, 64, 64, 0, 1, 0) == 0           # L2 flag: unsupported
+    assert size(3, 130, 2, 64, 64, 0, 1, 1) == size(3, 130, 2, 64, 64, 0, 0, 1) + 2304   # q/k norm scales
+    assert size(3, 130, 2, 64, 64, 0, 2, 0) == 0           # SILU: not a backward flag
     assert size(3, 130, 2, 48, 64, 0, 0, 0) == 0
     assert size(70000, 130, 2, 64, 64, 0, 0, 0) == 0       # N <= 65535
     # launch extents: H (ceil(T/64) + N) <= 2^22 - 8
@@ -409,7 +415,7 @@ def test_varlen_backward_validation(lib):
                                                      a["ns"], FAKE, None, a["dq"], FAKE, FAKE, FAKE, FAKE,
                                                      a["dinit"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
                                                      a["dtype"], a["flags"], a["ws"], a["wsb"], None)
-    assert call(flags=1) == UNSUPPORTED
+    assert call(flags=1, ws=None) == WORKSPACE
     assert call(flags=2) == INVALID
     assert call(flags=4, ws=None) == WORKSPACE
     assert call(cu=None) == INVALID

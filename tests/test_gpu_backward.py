@@ -46,9 +46,9 @@ def _run(inp, do, dfinal, dtype, dev, mask=None, s0=None):
         initial_state=None if s0 is None else to_dev(s0, dev=dev))
 
 
-def _ref(oracle, inp, do, dfinal, mask=None, s0=None):
+def _ref(oracle, inp, do, dfinal, mask=None, s0=None, l2=False):
     return oracle.np_prefill_backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do,
-                                      dfinal, mask=mask, init_state=s0)
+                                      dfinal, mask=mask, init_state=s0, l2norm_qk=l2)
 
 
 def test_backward_tiny_fp32(oracle):
@@ -267,3 +267,66 @@ def test_backward_128k_sampled_head(oracle):
     ref = _ref(oracle, one, do[:, :, h:h + 1], dfinal[:, h:h + 1])
     sub = {n: (got[n][:, h:h + 1] if n == "dinit_state" else got[n][:, :, h:h + 1]) for n in NAMES}
     _check(f"128k h{h}", sub, ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype,dk,dv", [("bf16", 128, 128), ("fp32", 64, 32), ("bf16", 16, 64)])
+def test_backward_l2norm_vs_oracle(oracle, dtype, dk, dv):
+    """With the q/k L2-norm flag the call differentiates the prefill that normalises q and k
+    itself: raw N(0,1) rows (norms near sqrt(dk)), masks, an initial state and a final-state
+    cotangent, against the oracle's gradient with the norm.  NaN in q and k at masked
+    positions gives the same gradients as zeros there, bit for bit, and zero gradients."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H = 2, 300, 2
+    say(f"[case] backward l2 norm {dtype} dk={dk} dv={dv}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, dtype, seed=61, unit_qk=False)
+    s0 = D.np_state(B, H, dk, dv, 0.05, seed=61)
+    mask = np.ones((B, T), np.uint8)
+    mask[0, :21] = 0
+    mask[1, 150:170] = 0
+    do, dfinal = _cotangents(B, T, H, dk, dv, dtype, 61)
+    zeroed = {n: x.copy() for n, x in inp.items()}
+    for n in ("q", "k"):
+        zeroed[n][mask == 0] = 0.0
+    ref = _ref(oracle, zeroed, do, dfinal, mask, s0, l2=True)
+
+    def run(src):
+        return kda.chunk_prefill_backward(
+            *(to_dev(src[n], dtype if n in "qkv" else None, dev) for n in ("q", "k", "v", "log_alpha", "beta")),
+            to_dev(do, dtype, dev), d_final_state=to_dev(dfinal, dev=dev), mask=to_dev(mask, dev=dev),
+            initial_state=to_dev(s0, dev=dev), l2norm_qk=True)
+    got = run(zeroed)
+    _check(f"l2 {dtype}", got, ref, dtype)
+    poisoned = {n: x.copy() for n, x in zeroed.items()}
+    for n in ("q", "k"):
+        poisoned[n][mask == 0] = np.nan
+    bad = run(poisoned)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(bad[n], got[n]), f"NaN at masked positions changed {n}"
+    for n in ("dq", "dk"):
+        assert np.all(host(got[n])[mask == 0] == 0.0), n
+
+
+def test_backward_l2norm_given_states_equals_recompute():
+    """States saved by kda_chunk_prefill_states with the L2-norm flag, handed to the backward
+    with the flag, give the gradients of the call that runs that forward again, bit for bit."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H, dk, dv = 2, 260, 3, 128, 128
+    say("[case] backward l2 norm, given states vs recompute")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=62, unit_qk=False)
+    do, dfinal = _cotangents(B, T, H, dk, dv, "bf16", 62)
+    args = tuple(to_dev(inp[n], "bf16" if n in "qkv" else None, dev) for n in ("q", "k", "v", "log_alpha", "beta"))
+    ddo, dfin = to_dev(do, "bf16", dev), to_dev(dfinal, dev=dev)
+    _, _, ck = kda.chunk_prefill_states(*args, chunk_size=64, state_interval=64, l2norm_qk=True)
+    got = kda.chunk_prefill_backward(*args, ddo, d_final_state=dfin, chunk_states=ck, l2norm_qk=True)
+    ref = kda.chunk_prefill_backward(*args, ddo, d_final_state=dfin, l2norm_qk=True)
+    plain = kda.chunk_prefill_backward(*args, ddo, d_final_state=dfin)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(got[n], ref[n]), n
+    # the flag matters for rows that are not unit-norm
+    assert not torch.equal(got["dq"], plain["dq"])

@@ -19,11 +19,11 @@ INPUTS = ("q", "k", "v", "log_alpha", "beta")
 TOKEN_GRADS = ("dq", "dk", "dv", "dlog_alpha", "dbeta")
 
 
-def _packed(lengths, H, dk, dv, dtype, seed, scalar=False):
+def _packed(lengths, H, dk, dv, dtype, seed, scalar=False, unit_qk=True):
     """Packed inputs, initial states and cotangents for the given lengths (numpy)."""
     T = int(sum(lengths))
     N = len(lengths)
-    inp = {n: x[0] for n, x in D.np_kda_inputs(1, max(T, 1), H, dk, dv, dtype, seed=seed).items()}
+    inp = {n: x[0] for n, x in D.np_kda_inputs(1, max(T, 1), H, dk, dv, dtype, seed=seed, unit_qk=unit_qk).items()}
     inp = {n: np.ascontiguousarray(x[:T]) for n, x in inp.items()}
     if scalar:
         inp["log_alpha"] = np.ascontiguousarray(inp["log_alpha"][..., 0])
@@ -35,22 +35,22 @@ def _packed(lengths, H, dk, dv, dtype, seed, scalar=False):
     return inp, do, dfinal, s0, cu
 
 
-def _lone(kda, d, ddo, dfin, ds0, cu, i, scalar):
+def _lone(kda, d, ddo, dfin, ds0, cu, i, scalar, l2=False):
     """kda_chunk_prefill_backward on sequence i alone (B = 1)."""
     a, b = int(cu[i]), int(cu[i + 1])
     one = {n: x[a:b].unsqueeze(0).contiguous() for n, x in d.items()}
     return kda.chunk_prefill_backward(*(one[n] for n in INPUTS), ddo[a:b].unsqueeze(0).contiguous(),
                                       d_final_state=dfin[i:i + 1].contiguous(),
-                                      initial_state=ds0[i:i + 1].contiguous(), scalar_gate=scalar)
+                                      initial_state=ds0[i:i + 1].contiguous(), scalar_gate=scalar, l2norm_qk=l2)
 
 
-def _compare_with_lone_runs(kda, got, d, ddo, dfin, ds0, cu, lengths, scalar, tag):
+def _compare_with_lone_runs(kda, got, d, ddo, dfin, ds0, cu, lengths, scalar, tag, l2=False):
     import torch
     for i, L in enumerate(lengths):
         if L == 0:
             assert torch.equal(got["dinit_state"][i], dfin[i]), f"{tag}: empty sequence {i}"
             continue
-        ref = _lone(kda, d, ddo, dfin, ds0, cu, i, scalar)
+        ref = _lone(kda, d, ddo, dfin, ds0, cu, i, scalar, l2)
         torch.cuda.synchronize()
         a, b = int(cu[i]), int(cu[i + 1])
         for n in TOKEN_GRADS:
@@ -58,31 +58,36 @@ def _compare_with_lone_runs(kda, got, d, ddo, dfin, ds0, cu, lengths, scalar, ta
         assert torch.equal(got["dinit_state"][i], ref["dinit_state"][0]), f"{tag}: dinit of sequence {i}"
 
 
-@pytest.mark.parametrize("dtype,H,dk,dv,scalar", [("bf16", 2, 128, 128, False), ("fp32", 3, 64, 32, False),
-                                                  ("bf16", 16, 128, 128, False), ("bf16", 2, 64, 64, True)])
-def test_varlen_backward_equals_lone_sequences(dtype, H, dk, dv, scalar):
+@pytest.mark.parametrize("dtype,H,dk,dv,scalar,l2", [("bf16", 2, 128, 128, False, False),
+                                                     ("fp32", 3, 64, 32, False, False),
+                                                     ("bf16", 16, 128, 128, False, False),
+                                                     ("bf16", 2, 64, 64, True, False),
+                                                     ("bf16", 2, 128, 128, False, True)])
+def test_varlen_backward_equals_lone_sequences(dtype, H, dk, dv, scalar, l2):
     """Lengths with empty sequences, single tokens, exact and ragged chunks: every gradient
     equals the lone sequence's backward bit for bit, with the states recomputed and with the
-    packed forward's checkpoints handed in.  H = 16 puts N*H past 64 (the 32-column scan tiles)."""
+    packed forward's checkpoints handed in.  H = 16 puts N*H past 64 (the 32-column scan tiles);
+    l2: the q/k norm inside the call, on raw rows that are not unit-norm."""
     import torch
     from linear_attention_recurrence_kda_amd import kda
     dev = device()
     lengths = [0, 1, 63, 64, 65, 200, 130, 0, 17]
-    say(f"[case] varlen backward vs lone runs {dtype} H={H} dk={dk} dv={dv} scalar={scalar} lengths={lengths}")
-    inp, do, dfinal, s0, cu = _packed(lengths, H, dk, dv, dtype, seed=51, scalar=scalar)
+    say(f"[case] varlen backward vs lone runs {dtype} H={H} dk={dk} dv={dv} scalar={scalar} l2={l2} "
+        f"lengths={lengths}")
+    inp, do, dfinal, s0, cu = _packed(lengths, H, dk, dv, dtype, seed=51, scalar=scalar, unit_qk=not l2)
     d = {n: to_dev(x, dtype if n in "qkv" else None, dev) for n, x in inp.items()}
     ddo, dfin, ds0, dcu = to_dev(do, dtype, dev), to_dev(dfinal, dev=dev), to_dev(s0, dev=dev), to_dev(cu, dev=dev)
     args = tuple(d[n] for n in INPUTS)
     got = kda.chunk_prefill_varlen_backward(*args, dcu, ddo, d_final_state=dfin, initial_state=ds0,
-                                            scalar_gate=scalar)
+                                            scalar_gate=scalar, l2norm_qk=l2)
     _, _, ck = kda.chunk_prefill_varlen(*args, dcu, initial_state=ds0, chunk_size=64, state_interval=64,
-                                        scalar_gate=scalar)
+                                        scalar_gate=scalar, l2norm_qk=l2)
     given = kda.chunk_prefill_varlen_backward(*args, dcu, ddo, d_final_state=dfin, initial_state=ds0,
-                                              chunk_states=ck, scalar_gate=scalar)
+                                              chunk_states=ck, scalar_gate=scalar, l2norm_qk=l2)
     torch.cuda.synchronize()
     for n in got:
         assert torch.equal(got[n], given[n]), f"states given vs recomputed: {n}"
-    _compare_with_lone_runs(kda, got, d, ddo, dfin, ds0, cu, lengths, scalar, f"{dtype} H={H}")
+    _compare_with_lone_runs(kda, got, d, ddo, dfin, ds0, cu, lengths, scalar, f"{dtype} H={H}", l2)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
