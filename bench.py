@@ -7,8 +7,9 @@ One step = one pass of the whole path on synthetic, seeded inputs resident in HB
   * one batched decode step: 256 sequences x 32 heads, fp32 128x128 states ~ N(0, 0.02),
     raw bf16 activations -> width-4 short conv with cache (q, k, v) -> decode step with
     in-kernel L2 normalisation of q and k.
-`value` is prefill tokens/s; the decode state-update GB/s is reported beside it, and so is the
-same 128k tokens prefilled as 32 packed prompts of seeded lengths (kda_chunk_prefill_varlen).
+`value` is prefill tokens/s; the decode state-update GB/s is reported beside it, and so are the
+same 128k tokens prefilled as 32 packed prompts of seeded lengths (kda_chunk_prefill_varlen)
+and with Gated DeltaNet's per-head gate (KDA_FLAG_SCALAR_GATE).
 The training backward (kda_chunk_prefill_backward) is timed on the chunked-prefill training
 shape (B=4, H=32, T=4096): fed with the chunk-end states that the training forward
 (kda_chunk_prefill_states) saves, and as the self-contained call that runs the forward again,
@@ -28,6 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_BYTES_PER_TH = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (512) + beta (4)
+PREFILL_GDN_BYTES_PER_TH = 1032      # the same with one gate per (token, head): log_alpha fp32 (4)
 DECODE_BYTES_PER_SH = 132612         # state read+write 8*K*V + q,k,v,o (1024) + log_alpha (512) + beta
 # backward per token-head: q, k, v, dO bf16 (4 x 256) + log_alpha (512) + beta (4) read;
 # dq, dk, dv, dlog_alpha fp32 (4 x 512) + dbeta (4) written; with the chunk-end states
@@ -289,6 +291,23 @@ def main():
     varlen_ms = sum(a_.elapsed_time(b_) for a_, b_ in vev) / reps
     del wsv
 
+    # Gated DeltaNet's per-head gate on the same tokens (kda_chunk_prefill with
+    # KDA_FLAG_SCALAR_GATE): log_alpha [1, T, H], the first channel's gate
+    la_h = x["log_alpha"][..., 0].contiguous()
+
+    def prefill_gdn():
+        kda.chunk_prefill(x["q"], x["k"], x["v"], la_h, x["beta"], chunk_size=C, out=o, final_state=fs,
+                          workspace=ws, scalar_gate=True)
+    prefill_gdn()
+    gdn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a_, b_ in gdn_ev:
+        a_.record()
+        prefill_gdn()
+        b_.record()
+    torch.cuda.synchronize()
+    gdn_ms = sum(a_.elapsed_time(b_) for a_, b_ in gdn_ev) / reps
+    del la_h
+
     # the long-context end of the pages' range: one 512k-token sequence, 32 heads, timed
     # after the headline workload (its inputs replace the 128k ones in HBM)
     long_line = None
@@ -469,6 +488,9 @@ def main():
                            "tokens_per_s": T / (varlen_ms * 1e-3),
                            "algorithmic_GBps": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9,
                            "hbm_frac": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "prefill_scalar_gate": {"ms": gdn_ms, "tokens_per_s": T / (gdn_ms * 1e-3),
+                                "algorithmic_GBps": PREFILL_GDN_BYTES_PER_TH * th / (gdn_ms * 1e-3) / 1e9,
+                                "hbm_frac": PREFILL_GDN_BYTES_PER_TH * th / (gdn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "prefill_long": long_line,
         "backward": bwd_line,
         "decode": {"step_ms_with_conv": dec_avg, "fused_step_ms": fused_ms, "fused_step_graph_ms": graph_step_ms,

@@ -68,7 +68,11 @@ enum {
   /* Gated DeltaNet's gate: one log forget gate per (token, head), applied to every key
    * channel; log_alpha is then [B,T,H] in a prefill and [B,H] in a decode step (Kimi
    * Linear summary page, recurrent-layers paragraph: earlier variants gate whole heads,
-   * KDA each channel; remio.ai page, KDA section: KDA extends Gated DeltaNet) */
+   * KDA each channel; remio.ai page, KDA section: KDA extends Gated DeltaNet).  With bf16
+   * inputs the prefill forms the chunk's decay-weighted products as Gram products of the
+   * raw rows times a per-row decay mask, so its results differ from those of the
+   * per-channel call fed the broadcast gate by rounding; with fp32 inputs, and in the decode
+   * steps, they are the same bit for bit. */
   KDA_FLAG_SCALAR_GATE = 4u
 };
 
@@ -291,7 +295,8 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  * and B*H*ceil(T/64) <= 2^22 - 8 (launch extents in threads fit 32 bits);
  * flags may hold KDA_FLAG_SCALAR_GATE (Gated DeltaNet's gate, one value per (token, head):
  * the gate is applied to every channel and its gradient is the sum over the channels, so
- * the other gradients equal those of a per-channel call fed the broadcast gate bit for bit)
+ * given the same chunk_states the other gradients equal those of a per-channel call fed the
+ * broadcast gate bit for bit; without them the call runs the per-head prefill)
  * and KDA_FLAG_L2NORM_QK (the gradients of the prefill that normalises q and k with that
  * flag: the pass runs on the normalised rows, formed as the forward forms them, and dq, dk
  * are taken back to the raw rows at the end, dx = s dx_hat - s^3 x (x . dx_hat) with

@@ -1471,8 +1471,9 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
 
 // ---------------------------------------------------------------- per-head gate (Gated DeltaNet)
 // With one gate per (token, head) every channel decays alike: the gate is written to every
-// channel, the per-channel pass runs unchanged, and the gate's gradient is the sum of the
-// per-channel ones (the chain rule through the broadcast), taken in a fixed order.
+// channel, the per-channel pass runs unchanged on it (the forward that forms the chunk-end
+// states runs the per-head prefill), and the gate's gradient is the sum of the per-channel
+// ones (the chain rule through the broadcast), taken in a fixed order.
 constexpr int kGateThreads = 256;
 constexpr unsigned kGateMaxBlocks = 1u << 16;     // grid-stride loops past this
 
@@ -1757,7 +1758,10 @@ hipError_t launch_backward(const BackwardArgs& a) {
   if (a.T > 0 && a.chunk_states == nullptr) {
     // the forward pass again, keeping the state at every chunk end
     PrefillArgs f{};
-    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = la; f.beta = a.beta; f.mask = a.mask;
+    // (with the per-head gate, the per-head forward the caller runs: its chunk-end states
+    // are the ones that call saves, bit for bit)
+    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.scalar_gate = a.scalar_gate;
+    f.beta = a.beta; f.mask = a.mask;
     f.init_state = a.init_state;
     f.o = ws + L.o;
     f.final_state = (float*)(ws + L.fin);

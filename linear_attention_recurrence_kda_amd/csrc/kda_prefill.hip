@@ -167,11 +167,11 @@ struct PrepLds {
   static constexpr int kT = C * C * 4;                   // bytes of T
   static constexpr int r1 = cmax(cmax(2 * C * K * 2, C * K * 4), kT + kParts * K * C * 2);
   static constexpr int r3 = cmax(kParts * K * C * 2, C * C * 4);
-  // R4 in floats: s_tot [RT][K], s_gc [K], s_gce [K], 8 zeros, 8 ones, s_ks [C]
+  // R4 in floats: s_tot [RT][K], s_gc [K], s_gce [K], 8 zeros, 8 ones, s_ks [C], s_grow [C]
   static constexpr int off_gc = RT * K, off_gce = off_gc + K, off_zero = off_gce + K, off_one = off_zero + 8;
-  static constexpr int off_ks = off_one + 8;
+  static constexpr int off_ks = off_one + 8, off_grow = off_ks + C;
   static constexpr int kStage = 16 * 17;
-  static constexpr int r4 = cmax(off_ks + C, cmax(RT - 1, 1) * kStage);
+  static constexpr int r4 = cmax(off_grow + C, cmax(RT - 1, 1) * kStage);
 };
 
 // Element (r, c) of an r-major bf16 matrix with K per row: 16-byte blocks permuted by
@@ -200,7 +200,11 @@ __device__ __forceinline__ void ld8t(const float* m, int r, int c, float* out) {
 // registers on their way into A and P.  All global loads are issued up front,
 // unconditionally, from in-bounds rows; validity (mask, ragged tail) is applied by
 // select afterwards.
-template <int DT, int K, int V, int C>
+// SGP: one gate per (token, head) with bf16 inputs.  Every channel of a row then decays
+// alike, so the decay factors are per row, and A and P are Gram products of the raw bf16
+// rows (exact MFMA operands, one product per k step instead of three) times the scalar
+// mask exp2(g_i - g_j) <= 1: no 1/Gam factor, and so no exact path.
+template <int DT, int K, int V, int C, bool SGP = false>
 __global__ void __launch_bounds__(kPrepThreads, DT == 0 ? 3 : 1)
 prep_kernel(PrepParams p) {
   using E = Elem<DT>;
@@ -230,6 +234,7 @@ prep_kernel(PrepParams p) {
   float* s_zero = s_r4 + Lds::off_zero;                              // 8 x 0
   float* s_one = s_r4 + Lds::off_one;                                // 8 x 1
   float* s_ks = s_r4 + Lds::off_ks;                                  // key row scales, 0: row not valid
+  float* s_grow = s_r4 + Lds::off_grow;                              // SGP: g of each row (log2)
   float* s_scratch = s_r4;                                           // staging tiles, in the inversion
 
   // heads vary fastest across workgroups, so the ones running together read whole token
@@ -351,7 +356,13 @@ prep_kernel(PrepParams p) {
     reinterpret_cast<float*>(wsb + L::off_gam)[tid] = ge;
     ch_fast = run >= kFastLimit;
   }
-  const bool fast = __syncthreads_and(ch_fast);
+  bool fast = true;
+  if constexpr (SGP) {
+    static_assert(DT == 0, "the per-head specialisation takes bf16 rows as exact MFMA operands");
+    __syncthreads();
+  } else {
+    fast = __syncthreads_and(ch_fast);
+  }
 
   // ---- decay factors for this lane's row.  On the fast path every factor lies in
   //      [2^-120, 2^120], so the bare hardware exp2 is exact enough, and
@@ -361,6 +372,16 @@ prep_kernel(PrepParams p) {
   // used there).  X and the factor after it are read from Gc / Gam_last or from blocks
   // of eight zeros / ones, chosen per k step, so the elementwise work has no selects.
   bf16x8 kth[KS], ktl[KS], qth[KS], qtl[KS];
+  // SGP: the row's factors Gam and Gam_last / Gam, from this lane's first channel (a channel
+  // past dk holds g = 0 there, and its k and q are 0 as well); lanes 0-15 hold channel 0
+  // and publish the row's g for the mask of A and P
+  float gam_r = 1.f, khf_r = 1.f;
+  if constexpr (SGP) {
+    const float g0 = g_r[0][0] + s_tot[(rows ? I : 0) * K + cg];
+    gam_r = exp2f(g0);
+    khf_r = exp2f(s_gc[cg] - g0);
+    if (rows && lane < 16) s_grow[rq] = g0;
+  }
   {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -379,15 +400,23 @@ prep_kernel(PrepParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         g[e] = g_r[ks][e] + pre[e];
-        const float gam = __builtin_amdgcn_exp2f(g[e]);
-        kt[e] = kv[e] * gam;
-        qt[e] = qv[e] * gam;
-        ki[e] = kv[e] * __builtin_amdgcn_exp2f(xv[e] - g[e]);
-        kh[e] = ki[e] * mv[e];
+        if constexpr (SGP) {
+          kt[e] = kv[e] * gam_r;
+          qt[e] = qv[e] * gam_r;
+          ki[e] = 0.f;
+          kh[e] = kv[e] * khf_r;
+        } else {
+          const float gam = __builtin_amdgcn_exp2f(g[e]);
+          kt[e] = kv[e] * gam;
+          qt[e] = qv[e] * gam;
+          ki[e] = kv[e] * __builtin_amdgcn_exp2f(xv[e] - g[e]);
+          kh[e] = ki[e] * mv[e];
+        }
       }
       split8(kt, kth[ks], ktl[ks]);
       split8(qt, qth[ks], qtl[ks]);
-      pin8(kth[ks]); pin8(ktl[ks]); pin8(qth[ks]); pin8(qtl[ks]);
+      pin8(kth[ks]); pin8(ktl[ks]); pin8(qth[ks]);
+      if constexpr (!SGP) pin8(qtl[ks]);                          // (SGP: P takes the raw q rows)
       if (rows) {
         // Qt rows to the workspace (invalid rows are 0)
         const size_t off = frag_off(I, ks, lane, K);
@@ -400,7 +429,10 @@ prep_kernel(PrepParams p) {
           s_khs[swz<C>(c0 + e, rq)] = hi[e];
           if (SPLIT) s_khs[K * C + swz<C>(c0 + e, rq)] = lo[e];
         }
-        if (fast) {
+        if constexpr (SGP) {
+          // the raw k row (bf16, exact) is the A operand of the Gram products
+          *reinterpret_cast<bf16x8*>(&s_ki[swzk<K>(rq, c0)]) = __builtin_bit_cast(bf16x8, k_r[ks].u);
+        } else if (fast) {
           split8(ki, hi, lo);
           *reinterpret_cast<bf16x8*>(&s_ki[swzk<K>(rq, c0)]) = hi;
           *reinterpret_cast<bf16x8*>(&s_ki[C * K + swzk<K>(rq, c0)]) = lo;
@@ -435,7 +467,44 @@ prep_kernel(PrepParams p) {
   bf16x8 ph[CS], pl[CS];
 #pragma unroll
   for (int ks = 0; ks < CS; ++ks) { ph[ks] = zero8(); pl[ks] = zero8(); }
-  if (fast) {
+  if constexpr (SGP) {
+    if (rows) {
+      // Gram products of the raw rows (A operand: k rows of column tile J from LDS; B: this
+      // lane's raw k and q rows), then per entry the decay mask exp2(g_i - g_j) <= 1 and
+      // the rows' L2 scales (s_ks is 0 for a row that is not valid)
+      const float beta_row = s_beta[rq], g_i = s_grow[rq];
+#pragma unroll
+      for (int s2 = 0; s2 < CS; ++s2) {
+        f32x4 pt[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int J = 2 * s2 + t;
+          f32x4 accA = zero4(), accP = zero4();
+          if (J <= I) {
+            const int j = 16 * J + (lane % 16);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              const bf16x8 kj = *reinterpret_cast<const bf16x8*>(&s_ki[swzk<K>(j, 32 * ks + cg)]);
+              accA = mfma16(kj, __builtin_bit_cast(bf16x8, k_r[ks].u), accA);
+              accP = mfma16(kj, __builtin_bit_cast(bf16x8, q_r[ks].u), accP);
+            }
+          }
+          float av[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int jj = 16 * J + 4 * (lane / 16) + i;
+            const float d = exp2f(fminf(g_i - s_grow[jj], 0.f)) * s_ks[jj];
+            av[i] = (jj < rq) ? beta_row * (accA[i] * (d * ksc)) : 0.f;
+            pt[t][i] = (jj <= rq) ? accP[i] * (d * qs) : 0.f;
+          }
+          *reinterpret_cast<float4*>(&s_A[swzf<C>(rq, 16 * J + 4 * (lane / 16))]) = make_float4(av[0], av[1], av[2], av[3]);
+        }
+        float pv[8];
+        pair_to_afrag(pt[0], pt[1], pv);
+        split8(pv, ph[s2], pl[s2]);
+      }
+    }
+  } else if (fast) {
     if (rows) {
       // transposed products: A-operand rows are Ki rows of column tile J (LDS), B-operand
       // columns are this wave's Kt and Qt rows (registers); lane (g, r) gets columns
@@ -1446,8 +1515,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if (NC > 0) {
     PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace, span,
                   a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate};
-    hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), dim3(NC * a.H, varlen ? 1 : a.B), dim3(kPrepThreads), 0,
-                       st, pp);
+    const dim3 pgrid(NC * a.H, varlen ? 1 : a.B);
+    if (DT == 0 && a.scalar_gate)
+      hipLaunchKernelGGL((prep_kernel<DT, K, V, C, DT == 0>), pgrid, dim3(kPrepThreads), 0, st, pp);
+    else
+      hipLaunchKernelGGL((prep_kernel<DT, K, V, C>), pgrid, dim3(kPrepThreads), 0, st, pp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -198,9 +198,11 @@ def test_backward_wide_scan_tiles_equal_narrow():
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_backward_scalar_gate_equals_broadcast(dtype):
-    """KDA_FLAG_SCALAR_GATE (one gate per token and head): dq, dk, dv, dbeta and dinit equal
-    those of the per-channel call fed the broadcast gate bit for bit, and the gate's gradient is
-    that call's per-channel dlog_alpha summed over the channels."""
+    """KDA_FLAG_SCALAR_GATE (one gate per token and head), fed the chunk-end states of the
+    per-head training forward: dq, dk, dv, dbeta and dinit equal those of the per-channel call
+    fed the broadcast gate and the same states bit for bit, and the gate's gradient is that
+    call's per-channel dlog_alpha summed over the channels.  Without the states the call runs
+    the per-head forward itself and gives the same gradients bit for bit."""
     import torch
     from linear_attention_recurrence_kda_amd import kda
     dev = device()
@@ -217,10 +219,17 @@ def test_backward_scalar_gate_equals_broadcast(dtype):
     ddo, dfin = to_dev(do, dtype, dev), to_dev(dfinal, dev=dev)
     la_s = to_dev(la1, dev=dev)
     la_b = la_s.unsqueeze(-1).expand(B, T, H, dk).contiguous()
+    _, _, ck = kda.chunk_prefill_states(q, k, v, la_s, beta, mask=dm, initial_state=ds0, chunk_size=64,
+                                        state_interval=64, scalar_gate=True)
     got = kda.chunk_prefill_backward(q, k, v, la_s, beta, ddo, d_final_state=dfin, mask=dm, initial_state=ds0,
+                                     chunk_states=ck, scalar_gate=True)
+    rec = kda.chunk_prefill_backward(q, k, v, la_s, beta, ddo, d_final_state=dfin, mask=dm, initial_state=ds0,
                                      scalar_gate=True)
-    ref = kda.chunk_prefill_backward(q, k, v, la_b, beta, ddo, d_final_state=dfin, mask=dm, initial_state=ds0)
+    ref = kda.chunk_prefill_backward(q, k, v, la_b, beta, ddo, d_final_state=dfin, mask=dm, initial_state=ds0,
+                                     chunk_states=ck)
     torch.cuda.synchronize()
+    for n in got:
+        assert torch.equal(got[n], rec[n]), f"given states vs recompute: {n}"
     for n in ("dq", "dk", "dv", "dbeta", "dinit_state"):
         assert torch.equal(got[n], ref[n]), n
     assert got["dlog_alpha"].shape == (B, T, H)

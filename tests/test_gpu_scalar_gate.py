@@ -1,6 +1,9 @@
 """Gated DeltaNet's gate (KDA_FLAG_SCALAR_GATE): one log forget gate per (token, head).
-It is KDA with that gate on every key channel, so the scalar-gate path must give bit for
-bit what the per-channel path gives for the broadcast gate, and match the fp64 oracle fed
+It is KDA with that gate on every key channel.  With fp32 rows (and in the decode kernels)
+the scalar-gate path runs the per-channel arithmetic on the one value, so it gives bit for
+bit what the per-channel path gives for the broadcast gate.  With bf16 rows the prefill
+takes its own prep (A and P as Gram products of the raw rows times the scalar decay mask),
+which differs from the broadcast path by rounding only; it is held to the fp64 oracle fed
 the broadcast gate."""
 import numpy as np
 import pytest
@@ -11,35 +14,53 @@ from tests.gpu_util import check, device, host, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(kda, inp, dtype, dev, chunk, la, scalar, mask=None, s0=None):
+def _run(kda, inp, dtype, dev, chunk, la, scalar, mask=None, s0=None, l2=False):
     d = {n: to_dev(inp[n], dtype if n in "qkv" else None, dev) for n in ("q", "k", "v", "beta")}
     return kda.chunk_prefill(d["q"], d["k"], d["v"], to_dev(la, dev=dev), d["beta"],
                              mask=None if mask is None else to_dev(mask, dev=dev),
                              initial_state=None if s0 is None else to_dev(s0, dev=dev),
-                             chunk_size=chunk, scalar_gate=scalar)
+                             chunk_size=chunk, scalar_gate=scalar, l2norm_qk=l2)
 
 
-@pytest.mark.parametrize("dtype,chunk,decay", [("bf16", 64, "default"), ("fp32", 32, "default"),
-                                               ("bf16", 64, "strong")])
-def test_prefill_scalar_gate_equals_broadcast(dtype, chunk, decay):
+@pytest.mark.parametrize("dtype,chunk,decay,dk,l2", [("bf16", 64, "default", 128, False),
+                                                     ("fp32", 32, "default", 128, False),
+                                                     ("fp32", 64, "strong", 64, True),
+                                                     ("bf16", 64, "strong", 128, False),
+                                                     ("bf16", 32, "default", 16, True),
+                                                     ("bf16", 16, "strong", 64, True)])
+def test_prefill_scalar_gate_vs_broadcast(oracle, dtype, chunk, decay, dk, l2):
+    """Masks, an initial state, head sizes down to 16, the q/k norm, and chunks whose decay
+    passes 2^-120 (where the per-channel path takes its exact pairwise branch): fp32 bit for
+    bit equal to the broadcast gate; both paths within the bar of the oracle."""
     import torch
     from linear_attention_recurrence_kda_amd import kda
     dev = device()
-    B, T, H, dk, dv = 2, 203, 3, 128, 64
-    say(f"[case] prefill scalar gate {dtype} chunk={chunk} decay={decay}")
-    inp = D.np_kda_inputs(B, T, H, dk, dv, dtype, seed=21)
+    B, T, H, dv = 2, 203, 3, 64
+    say(f"[case] prefill scalar gate {dtype} chunk={chunk} decay={decay} dk={dk} l2={l2}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, dtype, seed=21, unit_qk=not l2)
     g = np.ascontiguousarray(inp["log_alpha"][..., 0])                       # [B,T,H]
-    if decay == "strong":          # a chunk whose decay passes 2^-120: the exact pairwise path
+    if decay == "strong":
         g[:, 70:74] = -40.0
     gb = np.ascontiguousarray(np.repeat(g[..., None], dk, axis=-1))          # [B,T,H,dk]
     s0 = D.np_state(B, H, dk, dv, 0.1, seed=21)
     mask = np.ones((B, T), np.uint8)
     mask[1, 150:] = 0
-    o1, s1 = _run(kda, inp, dtype, dev, chunk, g, True, mask, s0)
-    o2, s2 = _run(kda, inp, dtype, dev, chunk, gb, False, mask, s0)
+    mask[0, :5] = 0
+    o1, s1 = _run(kda, inp, dtype, dev, chunk, g, True, mask, s0, l2)
+    o2, s2 = _run(kda, inp, dtype, dev, chunk, gb, False, mask, s0, l2)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2)
-    assert torch.equal(s1, s2)
+    if dtype == "fp32":
+        assert torch.equal(o1, o2)
+        assert torch.equal(s1, s2)
+    else:                                   # the per-head prep ran (other roundings)
+        assert not torch.equal(s1, s2)
+    ref = dict(inp)
+    ref["log_alpha"] = gb
+    ro, rs = oracle.c_prefill(**ref, mask=mask, init_state=s0, l2norm_qk=l2)
+    check(f"gate per head o ({dtype})", host(o1), ro, dtype)
+    check(f"gate per head state ({dtype})", host(s1), rs, dtype)
+    check(f"broadcast gate o ({dtype})", host(o2), ro, dtype)
+    check(f"broadcast gate state ({dtype})", host(s2), rs, dtype)
 
 
 def test_prefill_scalar_gate_matches_oracle(oracle):
