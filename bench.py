@@ -42,18 +42,18 @@ BACKWARD_STATES_BYTES_PER_TH = BACKWARD_BYTES_PER_TH + 128 * 128 * 4 // 64
 # scaled by a known-size streaming kernel in the same run (factors 2.0 and 1.0 on this GPU).  A
 # figure is reported only while the kernel sources still hash to what was profiled.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433", "bytes": 16.322e9},
+    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "89fb885d5c0fc5f7", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
     # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
-    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "8e0849c7b94542d6", "bytes": 8.878e9},
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "9e886c2ffc25b477", "bytes": 8.898e9},
 }
 
 
 # MFMA counters of the 128k prefill call (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 ...; busy % = busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)),
 # reported only while the kernel sources hash to what was profiled.
-MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "f6886cb59768f433",
-                 "prep_busy_pct": 8.1, "scan_busy_pct": 19.5, "call_busy_pct": 14.5, "issued_flop_per_call": 1.433e12}
+MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "89fb885d5c0fc5f7",
+                 "prep_busy_pct": 8.1, "scan_busy_pct": 18.8, "call_busy_pct": 14.2, "issued_flop_per_call": 1.433e12}
 
 
 def measured_mfma(default_workload):
