@@ -251,6 +251,12 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
     return out, final_state
 
 
+def _given(t):
+    """A tensor passed as chunk_states reaches the library as a pointer; an empty one (no
+    64-token boundary to hold a state) as NULL, so the workspace is sized from that."""
+    return t is not None and t.data_ptr() != 0
+
+
 def _bwd_flags(scalar_gate, l2norm_qk):
     return (KDA_FLAG_SCALAR_GATE if scalar_gate else 0) | (KDA_FLAG_L2NORM_QK if l2norm_qk else 0)
 
@@ -301,7 +307,7 @@ def chunk_prefill_backward(q, k, v, log_alpha, beta, d_o, d_final_state=None, ma
          "dlog_alpha": torch.empty(*((B, T, H) if scalar_gate else (B, T, H, dk)), **f32),
          "dbeta": torch.empty(B, T, H, **f32), "dinit_state": torch.empty(B, H, dk, dv, **f32)}
     flags = _bwd_flags(scalar_gate, l2norm_qk)
-    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt, flags, int(chunk_states is not None)))
+    need = int(lib.kda_chunk_prefill_backward_workspace_size(B, T, H, dk, dv, dt, flags, int(_given(chunk_states))))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -450,7 +456,7 @@ def chunk_prefill_varlen_backward(q, k, v, log_alpha, beta, cu_seqlens, d_o, d_f
          "dbeta": torch.empty(T, H, **f32), "dinit_state": torch.empty(N, H, dk, dv, **f32)}
     flags = _bwd_flags(scalar_gate, l2norm_qk)
     need = int(lib.kda_chunk_prefill_varlen_backward_workspace_size(N, T, H, dk, dv, dt, flags,
-                                                                    int(chunk_states is not None)))
+                                                                    int(_given(chunk_states))))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

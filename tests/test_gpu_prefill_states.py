@@ -174,3 +174,35 @@ def test_prefill_states_equal_prefix_runs_with_flags(l2, scalar):
         torch.cuda.synchronize()
         for b in range(B):
             assert torch.equal(ck[b * per + j - 1], sj[b]), f"row {b} checkpoint {j}"
+
+
+@pytest.mark.parametrize("T", [1, 40, 63])
+def test_backward_with_no_state_boundary(T):
+    """Sequences shorter than 64 tokens: the training forward saves no state (an empty tensor,
+    which reaches the library as NULL); the backward handed it equals the recomputing call bit
+    for bit, in the batch and the packed layouts."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, H, dk, dv = 2, 2, 64, 64
+    say(f"[case] backward with no 64-token boundary, T={T}")
+    inp = D.np_kda_inputs(B, T, H, dk, dv, "bf16", seed=47)
+    rng = np.random.default_rng(47)
+    do = to_dev(D.to_storage(rng.normal(0, 1, (B, T, H, dv)).astype(np.float32), "bf16"), "bf16", dev)
+    dfin = to_dev(rng.normal(0, 1, (B, H, dk, dv)).astype(np.float32), dev=dev)
+    d = _dev(inp, "bf16", dev)
+    args = tuple(d[n] for n in INPUTS)
+    _, _, ck = kda.chunk_prefill_states(*args, chunk_size=64, state_interval=64)
+    assert ck.shape[0] == 0
+    got = kda.chunk_prefill_backward(*args, do, d_final_state=dfin, chunk_states=ck)
+    ref = kda.chunk_prefill_backward(*args, do, d_final_state=dfin)
+    cu = to_dev(np.array([0, T, 2 * T], np.int32), dev=dev)
+    flat = tuple(x.reshape(B * T, *x.shape[2:]).contiguous() for x in args)
+    _, _, ckp = kda.chunk_prefill_varlen(*flat, cu, chunk_size=64, state_interval=64)
+    gp = kda.chunk_prefill_varlen_backward(*flat, cu, do.reshape(B * T, H, dv).contiguous(), d_final_state=dfin,
+                                           chunk_states=ckp)
+    torch.cuda.synchronize()
+    for n in GRADS:
+        assert torch.equal(got[n], ref[n]), n
+        want = ref[n] if n == "dinit_state" else ref[n].reshape(B * T, *ref[n].shape[2:])
+        assert torch.equal(gp[n], want), f"packed {n}"
