@@ -14,7 +14,8 @@ The training backward (kda_chunk_prefill_backward) is timed on the chunked-prefi
 shape (B=4, H=32, T=4096): fed with the chunk-end states that the training forward
 (kda_chunk_prefill_states) saves, and as the self-contained call that runs the forward again,
 with the plain forward on the same inputs beside them; the same tokens as 12 packed documents
-(kda_chunk_prefill_varlen with 64-token checkpoints, then kda_chunk_prefill_varlen_backward).
+(kda_chunk_prefill_varlen with 64-token checkpoints, then kda_chunk_prefill_varlen_backward);
+and the training step with the per-head gate and with the q/k L2 norm.
 Prints one JSON line.
 """
 import argparse
@@ -417,6 +418,26 @@ def main():
                        "forward_states_ms": pfst_ms, "ms": pbwd_ms, "training_step_ms": pfst_ms + pbwd_ms,
                        "training_step_tokens_per_s": Bb * Tb / ((pfst_ms + pbwd_ms) * 1e-3)}
         del ckp, fsp, wfp, wsp, dfp
+
+        # the same training step with each forward flag: Gated DeltaNet's per-head gate
+        # (log_alpha [B,T,H]) and the q/k L2 norm inside the calls (raw rows)
+        def flagged_step(flags, la):
+            args_f = (xb["q"], xb["k"], xb["v"], la, xb["beta"])
+            wsf = torch.empty(kda.backward_workspace_size(Bb, Tb, H, dk, dv, kda.KDA_BF16, states_given=True,
+                                                          **flags), dtype=torch.uint8, device=dev)
+
+            def fwd():
+                kda.chunk_prefill_states(*args_f, chunk_size=64, state_interval=64, chunk_states=ckb, out=ob,
+                                         final_state=fsb, workspace=wfb, **flags)
+
+            def bwd():
+                return kda.chunk_prefill_backward(*args_f, dob, d_final_state=dfb, workspace=wsf, chunk_states=ckb,
+                                                  **flags)
+            f_ms, b_ms = timed(fwd), timed(bwd)
+            return {"forward_states_ms": f_ms, "ms": b_ms, "training_step_ms": f_ms + b_ms,
+                    "training_step_tokens_per_s": Bb * Tb / ((f_ms + b_ms) * 1e-3)}
+        gate_line = flagged_step({"scalar_gate": True}, xb["log_alpha"][..., 0].contiguous())
+        l2_line = flagged_step({"l2norm_qk": True}, xb["log_alpha"])
         bth = Bb * Tb * H
         bwd_gbs = BACKWARD_STATES_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
         default_bwd = (Bb == 4 and Tb == 4096)    # the shape the measured traffic was taken on
@@ -429,6 +450,8 @@ def main():
                     "forward_ms_same_inputs": fwd_ms,
                     "backward_over_forward": bwd_ms / fwd_ms,
                     "packed": packed_line,
+                    "per_head_gate": gate_line,
+                    "l2norm_qk": l2_line,
                     "roofline": {"bound": "hbm", "achieved": bwd_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": bwd_gbs / HBM_PEAK_GBS,
                                  "traffic": measured_traffic("backward", default_bwd),

@@ -1486,25 +1486,23 @@ gate_broadcast_kernel(const float* __restrict__ la, float* __restrict__ out, siz
   }
 }
 
-// four threads per row (neighbouring lanes), each summing K/4 channels, then two shuffles;
-// every lane of a wave runs the same number of iterations, so the shuffles stay uniform
+// K/8 neighbouring lanes per row, eight channels each (contiguous across the lanes of a
+// row), then a butterfly over those lanes; every lane of a wave runs the same iterations, so
+// the shuffles stay uniform, and the order of the sum is fixed
 __global__ void __launch_bounds__(kGateThreads)
 gate_reduce_kernel(const float* __restrict__ dla_pc, float* __restrict__ dla, size_t rows, int K) {
-  const int q = K / 4;
+  const int lpr = K / 8;
   const size_t stride = (size_t)gridDim.x * kGateThreads;
-  for (size_t base = (size_t)blockIdx.x * kGateThreads; base < rows * 4; base += stride) {
-    const size_t g = base + threadIdx.x, row = g / 4;
-    const int part = (int)(g % 4);
+  for (size_t base = (size_t)blockIdx.x * kGateThreads; base < rows * lpr; base += stride) {
+    const size_t g = base + threadIdx.x, row = g / lpr;
+    const int part = (int)(g % lpr);
     float s = 0.f;
     if (row < rows) {
-      const float* src = dla_pc + row * K + part * q;
-      for (int c = 0; c < q; c += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + c);
-        s += (v.x + v.y) + (v.z + v.w);
-      }
+      const float4* src = reinterpret_cast<const float4*>(dla_pc + row * K + part * 8);
+      const float4 a = src[0], b = src[1];
+      s = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
     }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
+    for (int o = 1; o < lpr; o <<= 1) s += __shfl_xor(s, o, 64);
     if (row < rows && part == 0) dla[row] = s;
   }
 }
@@ -1512,46 +1510,40 @@ gate_reduce_kernel(const float* __restrict__ dla_pc, float* __restrict__ dla, si
 // ---------------------------------------------------------------- q/k L2 norm
 // With the norm inside the call the pass differentiates with respect to the normalised rows
 // x_hat = s x, s = (|x|^2 + 1e-6)^-1/2; this maps each row's gradient back to the raw row,
-// in place: dx = s dx_hat - s^3 x (x . dx_hat).  Four threads per row as above, K/4 channels
-// each (a multiple of 4); a row whose scale is 0 (not valid) gets 0.
+// in place: dx = s dx_hat - s^3 x (x . dx_hat).  A row is spread over K/8 neighbouring
+// lanes, eight channels each, so every load and store is contiguous across the lanes of a
+// row and the row is read once; the dot product is a butterfly over those lanes (every lane
+// of a wave runs the same iterations).  A row whose scale is 0 (not valid) gets 0.
 template <int DT>
 __global__ void __launch_bounds__(kGateThreads)
 l2_grad_kernel(const void* __restrict__ q, const void* __restrict__ k, const float2* __restrict__ qks,
                float* __restrict__ dq, float* __restrict__ dk, size_t rows, int K) {
   using E = Elem<DT>;
   using Tp = typename E::T;
-  const int per = K / 4;
+  const int lpr = K / 8;                                    // lanes per row: 2, 4, 8 or 16
   const size_t stride = (size_t)gridDim.x * kGateThreads;
-  for (size_t base = (size_t)blockIdx.x * kGateThreads; base < rows * 4; base += stride) {
-    const size_t g = base + threadIdx.x, row = g / 4;
+  for (size_t base = (size_t)blockIdx.x * kGateThreads; base < rows * lpr; base += stride) {
+    const size_t g = base + threadIdx.x, row = g / lpr;
     const bool in = row < rows;
-    const size_t off = (in ? row : 0) * K + (size_t)(g % 4) * per;
+    const size_t off = (in ? row : 0) * K + (size_t)(g % lpr) * 8;
     const float2 sc = qks[in ? row : 0];
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       const Tp* x = (const Tp*)(which == 0 ? q : k);
       float* d = which == 0 ? dq : dk;
       const float s = which == 0 ? sc.x : sc.y;
+      float xv[8], gv[8];
+      E::ld8(x, off, xv);
+      Elem<1>::ld8(d, off, gv);
       float dot = 0.f;
-      for (int c = 0; c < per; c += 4) {
-        float xv[4];
-        E::ld4(x, off + c, xv);
-        const float4 dv = *reinterpret_cast<const float4*>(d + off + c);
-        dot += (xv[0] * dv.x + xv[1] * dv.y) + (xv[2] * dv.z + xv[3] * dv.w);
-      }
-      dot += __shfl_xor(dot, 1, 64);
-      dot += __shfl_xor(dot, 2, 64);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot += xv[e] * gv[e];
+      for (int o = 1; o < lpr; o <<= 1) dot += __shfl_xor(dot, o, 64);
       const float t = s * s * s * dot;
-      if (!in) continue;
-      for (int c = 0; c < per; c += 4) {
-        float xv[4];
-        E::ld4(x, off + c, xv);
-        float4 dv = *reinterpret_cast<const float4*>(d + off + c);
-        dv = s != 0.f ? make_float4(s * dv.x - t * xv[0], s * dv.y - t * xv[1], s * dv.z - t * xv[2],
-                                    s * dv.w - t * xv[3])
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(d + off + c) = dv;
-      }
+      float out[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = s != 0.f ? s * gv[e] - t * xv[e] : 0.f;
+      if (in) Elem<1>::st8(d, off, out);
     }
   }
 }
@@ -1802,16 +1794,16 @@ hipError_t launch_backward(const BackwardArgs& a) {
   if (l2) {
     // dq and dk so far are with respect to the normalised rows
     if (a.dtype == 0)
-      hipLaunchKernelGGL(l2_grad_kernel<0>, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st, a.q, a.k,
-                         (const float2*)p.qks, a.dq, a.dk, rows, a.dk_);
+      hipLaunchKernelGGL(l2_grad_kernel<0>, dim3(gate_blocks(rows * (a.dk_ / 8))), dim3(kGateThreads), 0, st, a.q,
+                         a.k, (const float2*)p.qks, a.dq, a.dk, rows, a.dk_);
     else
-      hipLaunchKernelGGL(l2_grad_kernel<1>, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st, a.q, a.k,
-                         (const float2*)p.qks, a.dq, a.dk, rows, a.dk_);
+      hipLaunchKernelGGL(l2_grad_kernel<1>, dim3(gate_blocks(rows * (a.dk_ / 8))), dim3(kGateThreads), 0, st, a.q,
+                         a.k, (const float2*)p.qks, a.dq, a.dk, rows, a.dk_);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (!a.scalar_gate) return hipSuccess;
-  hipLaunchKernelGGL(gate_reduce_kernel, dim3(gate_blocks(rows * 4)), dim3(kGateThreads), 0, st,
+  hipLaunchKernelGGL(gate_reduce_kernel, dim3(gate_blocks(rows * (a.dk_ / 8))), dim3(kGateThreads), 0, st,
                      (const float*)dla, a.dla, rows, a.dk_);
   return hipGetLastError();
 }
