@@ -288,8 +288,8 @@ size_t kda_chunk_prefill_backward_workspace_size(int B, int T, int H, int dk, in
  * key, query and W operands with bf16 inputs, as in the forward scan).  The workspace
  * holds about 250 KB of chunk operands per (b, h, chunk) at dk = dv = 128; without
  * chunk_states, the forward's own workspace, outputs and chunk-end states; with
- * KDA_FLAG_SCALAR_GATE, the gate on every channel and its per-channel gradient (dk floats
- * each per token and head).
+ * KDA_FLAG_SCALAR_GATE, the gate's per-channel gradient before the sum over the channels
+ * (dk floats per token and head).
  *
  * Supported: dk, dv in {16, 32, 64, 128}; B, H <= 65535, H ceil(T/64) < 2^24, B*H <= 2^20 - 8
  * and B*H*ceil(T/64) <= 2^22 - 8 (launch extents in threads fit 32 bits);

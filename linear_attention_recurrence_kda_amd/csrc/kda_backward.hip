@@ -82,6 +82,7 @@ struct Params {
   // with the q/k L2 norm: per token and head the row scales (q, k) = (|x|^2 + 1e-6)^-1/2,
   // written by the prep, (0, 0) where the row is not valid; null without the norm
   float2* qks;
+  int sgate;                               // la holds one gate per (token, head), read into every channel
   int B, T, H, K, V, NC, NCf;              // packed: B = sequences, T = tokens, NC = chunk slots
   int num_states;                          // checkpoints ck holds (entries past it read as zero)
 };
@@ -225,7 +226,8 @@ __device__ __forceinline__ void load_rows(const Params& p, const ChunkLoc& L, in
     const int c0 = c_base + 32 * ks + cg, cs = c0 < p.K ? c0 : 0;
     kr[ks].load((const Tp*)p.k, tk * p.K + cs);
     if (WANT_Q) qr[ks].load((const Tp*)p.q, tk * p.K + cs);
-    lr[ks].load(p.la, tk * p.K + cs);
+    if (p.sgate) lr[ks].fill(p.la[tk]);   // one gate per (t, h), the same in every channel
+    else lr[ks].load(p.la, tk * p.K + cs);
   }
   R.ok = r < L.rows && mk != 0;
   R.beta = R.ok ? bt : 0.f;
@@ -1470,21 +1472,12 @@ __global__ void __launch_bounds__(kThreads, 3) bwd_ck_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------- per-head gate (Gated DeltaNet)
-// With one gate per (token, head) every channel decays alike: the gate is written to every
-// channel, the per-channel pass runs unchanged on it (the forward that forms the chunk-end
-// states runs the per-head prefill), and the gate's gradient is the sum of the per-channel
-// ones (the chain rule through the broadcast), taken in a fixed order.
+// With one gate per (token, head) every channel decays alike: the kernels read the one value
+// into every channel's registers, the per-channel pass runs unchanged on it (the forward that
+// forms the chunk-end states runs the per-head prefill), and the gate's gradient is the sum
+// of the per-channel ones (the chain rule through the broadcast), taken in a fixed order.
 constexpr int kGateThreads = 256;
 constexpr unsigned kGateMaxBlocks = 1u << 16;     // grid-stride loops past this
-
-__global__ void __launch_bounds__(kGateThreads)
-gate_broadcast_kernel(const float* __restrict__ la, float* __restrict__ out, size_t rows, int K) {
-  const size_t per = (size_t)K / 4, n = rows * per;                       // 4 channels per item
-  for (size_t i = (size_t)blockIdx.x * kGateThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kGateThreads) {
-    const float x = la[i / per];
-    *reinterpret_cast<float4*>(out + 4 * i) = make_float4(x, x, x, x);
-  }
-}
 
 // K/8 neighbouring lanes per row, eight channels each (contiguous across the lanes of a
 // row), then a butterfly over those lanes; every lane of a wave runs the same iterations, so
@@ -1606,7 +1599,7 @@ bwd_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int NC, int4* __r
 // workspace, its discarded outputs and the chunk-end states): `own` bytes suffice when the
 // caller hands the states in.
 struct Layout {
-  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, lab, dlab, qks, seqs, cmap, own, fwd, o, fin, ck, total;
+  size_t kh, wt, qt, pt, gam, vbits, G, M, dS1, dU, U, dP, dG, dlab, qks, seqs, cmap, own, fwd, o, fin, ck, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1643,7 +1636,6 @@ Layout layout(int B, int T, int H, int dk, int dv, int dtype, bool scalar_gate, 
   L.dP = take(nch * kC * kC * 4);
   L.dG = take(nch * kC * kC * 4);
   if (scalar_gate) {                        // the gate on every channel, and its per-channel gradient
-    L.lab = take(tokens * H * dk * 4);
     L.dlab = take(tokens * H * dk * 4);
   }
   if (l2) L.qks = take(tokens * H * 8);     // the row scales of q and k
@@ -1733,18 +1725,10 @@ hipError_t launch_backward(const BackwardArgs& a) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // the per-channel gate and dlog_alpha the pass works with
+  // the per-head gate's per-channel gradient goes to the workspace, then is summed
   const float* la = a.log_alpha;
   float* dla = a.dla;
-  if (a.scalar_gate && rows > 0) {
-    la = (const float*)(ws + L.lab);
-    dla = (float*)(ws + L.dlab);
-    const size_t n4 = rows * (size_t)(a.dk_ / 4);
-    hipLaunchKernelGGL(gate_broadcast_kernel, dim3(gate_blocks(n4)), dim3(kGateThreads), 0, st, a.log_alpha,
-                       (float*)(ws + L.lab), rows, a.dk_);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (a.scalar_gate && rows > 0) dla = (float*)(ws + L.dlab);
   // checkpoints the pass may read: the caller's count, or what the forward below writes
   const int own_states = varlen ? NCf : a.B * NCf;
   if (a.T > 0 && a.chunk_states == nullptr) {
@@ -1772,6 +1756,7 @@ hipError_t launch_backward(const BackwardArgs& a) {
   Params p{};
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout;
   p.la = la; p.beta = a.beta; p.init = a.init_state; p.dfinal = a.dfinal; p.mask = a.mask;
+  p.sgate = a.scalar_gate != 0;
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dla = dla; p.dbeta = a.dbeta; p.dinit = a.dinit;
   if (a.T > 0) {
     p.w.kh = (uint16_t*)(ws + L.kh); p.w.wt = (uint16_t*)(ws + L.wt); p.w.qt = (uint16_t*)(ws + L.qt);

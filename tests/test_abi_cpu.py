@@ -354,9 +354,9 @@ def test_backward_validation(lib):
     assert call(flags=2) == INVALID           # SILU belongs to the short conv
     assert call(flags=8) == INVALID
     assert call(flags=4, ws=None) == WORKSPACE   # the per-head gate: accepted
-    # the per-head gate needs its broadcast and per-channel gradient in the workspace
+    # the per-head gate needs its per-channel gradient in the workspace (the sum comes after)
     assert (lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 4, 0)
-            == lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0) + 2 * 2 * 130 * 3 * 64 * 4)
+            == lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0) + 2 * 130 * 3 * 64 * 4)
     # the q/k norm adds the two row scales per token and head (rounded up to 256 bytes)
     assert (lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 1, 0)
             == lib.kda_chunk_prefill_backward_workspace_size(2, 130, 3, 64, 32, 0, 0, 0) + 6400)
@@ -393,7 +393,7 @@ def test_varlen_backward_validation(lib):
     # 3 sequences, 130 tokens: 3 + 3 = 6 slots per head, as a 384-token batch row; tables of
     # 3 x 16 and 6 x 8 bytes, each rounded up to 256
     assert size(3, 130, 2, 64, 64, 0, 0, 1) == bsize(1, 384, 2, 64, 64, 0, 0, 1) + 256 + 256
-    assert size(3, 130, 2, 64, 64, 1, 4, 1) == bsize(1, 384, 2, 64, 64, 1, 0, 1) + 512 + 2 * 130 * 2 * 64 * 4
+    assert size(3, 130, 2, 64, 64, 1, 4, 1) == bsize(1, 384, 2, 64, 64, 1, 0, 1) + 512 + 130 * 2 * 64 * 4
     # without the states, the packed forward's workspace, outputs and checkpoints come in
     assert size(3, 130, 2, 64, 64, 0, 0, 0) > size(3, 130, 2, 64, 64, 0, 0, 1) + \
         lib.kda_chunk_prefill_varlen_workspace_size(3, 130, 2, 64, 64, 64, 0)
