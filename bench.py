@@ -46,7 +46,7 @@ MEASURED_TRAFFIC = {
     "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "89fb885d5c0fc5f7", "bytes": 16.322e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
     # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
-    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "9e886c2ffc25b477", "bytes": 8.898e9},
+    "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "82437ce0d51abfed", "bytes": 8.877e9},
 }
 
 
@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 ...; busy % = busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)),
 # reported only while the kernel sources hash to what was profiled.
 MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "89fb885d5c0fc5f7",
-                 "prep_busy_pct": 8.1, "scan_busy_pct": 18.8, "call_busy_pct": 14.2, "issued_flop_per_call": 1.433e12}
+                 "prep_busy_pct": 8.0, "scan_busy_pct": 18.7, "call_busy_pct": 14.1, "issued_flop_per_call": 1.433e12}
 
 
 def measured_mfma(default_workload):
@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--T", type=int, default=131072)
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--decode-batch", type=int, default=256)
+    ap.add_argument("--flagged-steps", type=int, default=1,
+                    help="also time the training step with the per-head gate and with the q/k L2 norm "
+                         "(0 skips them, so that a profile's backward rows hold the default call only)")
     ap.add_argument("--long-T", type=int, default=524288,
                     help="tokens of the long single-sequence prefill timed beside the headline (0: skip)")
     ap.add_argument("--cpu-segment", type=int, default=8192,
@@ -436,8 +439,10 @@ def main():
             f_ms, b_ms = timed(fwd), timed(bwd)
             return {"forward_states_ms": f_ms, "ms": b_ms, "training_step_ms": f_ms + b_ms,
                     "training_step_tokens_per_s": Bb * Tb / ((f_ms + b_ms) * 1e-3)}
-        gate_line = flagged_step({"scalar_gate": True}, xb["log_alpha"][..., 0].contiguous())
-        l2_line = flagged_step({"l2norm_qk": True}, xb["log_alpha"])
+        gate_line = l2_line = None
+        if args.flagged_steps:
+            gate_line = flagged_step({"scalar_gate": True}, xb["log_alpha"][..., 0].contiguous())
+            l2_line = flagged_step({"l2norm_qk": True}, xb["log_alpha"])
         bth = Bb * Tb * H
         bwd_gbs = BACKWARD_STATES_BYTES_PER_TH * bth / (bwd_ms * 1e-3) / 1e9
         default_bwd = (Bb == 4 and Tb == 4096)    # the shape the measured traffic was taken on
