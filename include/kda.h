@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -73,7 +73,10 @@ enum {
    * raw rows times a per-row decay mask, so its results differ from those of the
    * per-channel call fed the broadcast gate by rounding; with fp32 inputs, and in the decode
    * steps, they are the same bit for bit. */
-  KDA_FLAG_SCALAR_GATE = 4u
+  KDA_FLAG_SCALAR_GATE = 4u,
+  /* prefill: scan each (b, h) as one chain of chunks, never in segments (see
+   * kda_chunk_prefill); the packed, state-saving and backward calls always do */
+  KDA_FLAG_SERIAL_SCAN = 8u
 };
 
 /* KDA_ABI_VERSION of the built library. */
@@ -117,7 +120,19 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * bits (KDA_ERR_UNSUPPORTED otherwise, and a workspace size of 0);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
  * and log_alpha unless KDA_FLAG_SCALAR_GATE is set.  The ragged tail of the last chunk is handled as masked
- * positions.  `flags` may hold KDA_FLAG_L2NORM_QK and KDA_FLAG_SCALAR_GATE.
+ * positions.  `flags` may hold KDA_FLAG_L2NORM_QK, KDA_FLAG_SCALAR_GATE and KDA_FLAG_SERIAL_SCAN.
+ *
+ * Segmented scan.  With bf16 inputs, dv = 128 and fewer than 64 (b, h) pairs, a long
+ * enough sequence (at least 128 chunks) is scanned as G = 2, 4, ... segments side by side
+ * when its gates forget fast enough: the state entering segment g is taken as the run from a
+ * zero state over the shortest tail of chunks before it whose per-token contraction bounds
+ * (max over the key channels of alpha, times max(1, |1 - beta |k|^2|): the norm of one
+ * step's state map) multiply to at most 2^-100, which changes that state by at most 2^-100
+ * of its norm.  A head for which some boundary has no such tail inside the segment before
+ * it is scanned as one chain, so every input gets a result within rounding of the token
+ * recurrence; the segmented one differs from the single chain's by rounding only.  The
+ * call stays asynchronous (the choice is made on the device).  KDA_FLAG_SERIAL_SCAN turns
+ * it off, e.g. to get results equal bit for bit to the packed and state-saving calls.
  * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
  * bytes of device memory (may be NULL when that size is 0).
  */

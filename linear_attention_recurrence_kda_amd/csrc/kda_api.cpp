@@ -67,7 +67,8 @@ static int prefill_entry(const void* q, const void* k, const void* v, const floa
                          unsigned flags, void* workspace, size_t workspace_bytes, void* stream,
                          bool use_scratch = false) {
   if (B < 0 || T < 0 || H < 0 || !dtype_ok(dtype)) return KDA_ERR_INVALID_ARG;
-  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE)) != 0) return KDA_ERR_INVALID_ARG;
+  if ((flags & ~(unsigned)(KDA_FLAG_L2NORM_QK | KDA_FLAG_SCALAR_GATE | KDA_FLAG_SERIAL_SCAN)) != 0)
+    return KDA_ERR_INVALID_ARG;
   if (!head_dim_ok(dk) || !head_dim_ok(dv) || !kda::prefill_supported(dk, dv, chunk) || H > 65535 || B > 65535 ||
       !kda::prefill_grid_ok(B, T, H, chunk, varlen))
     return KDA_ERR_UNSUPPORTED;
@@ -110,7 +111,8 @@ static int prefill_entry(const void* q, const void* k, const void* v, const floa
                      B, T, H, dk, dv, chunk, dtype, (flags & KDA_FLAG_L2NORM_QK) ? 1 : 0,
                      (flags & KDA_FLAG_SCALAR_GATE) ? 1 : 0, workspace, workspace_bytes, stream,
                      varlen ? cu_seqlens : nullptr, chunk_states, chunk_states != nullptr ? num_states : 0,
-                     chunk_states != nullptr ? state_interval : 0, slot, slot != nullptr ? num_slots : 0};
+                     chunk_states != nullptr ? state_interval : 0, slot, slot != nullptr ? num_slots : 0,
+                     (flags & KDA_FLAG_SERIAL_SCAN) ? 1 : 0};
   return hip_status(kda::launch_prefill(a));
 }
 

@@ -1750,6 +1750,7 @@ hipError_t launch_backward(const BackwardArgs& a) {
     f.chunk_states = own_states > 0 ? (float*)(ws + L.ck) : nullptr;
     f.num_states = own_states;
     f.state_interval = kC;
+    f.serial_scan = 1;
     const hipError_t e = launch_prefill(f);
     if (e != hipSuccess) return e;
   }

@@ -61,6 +61,7 @@ struct PrefillArgs {
   int state_interval;                      // a multiple of chunk
   const int32_t* slot;                     // packed only: each sequence's slot in a state pool, or null
   int num_slots;                           // slots in the pool
+  int serial_scan;                         // 1: each (b, h) as one chain, never segmented
 };
 
 // gradients of the prefill (see kda_backward.hip)

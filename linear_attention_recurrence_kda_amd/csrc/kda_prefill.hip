@@ -71,7 +71,8 @@ struct WsLayout {
   static constexpr size_t off_p = off_kh + kSplitCK;     // P   hi, lo      packed
   static constexpr size_t off_tn = off_p + 2 * kPF;      // -T' hi, lo      packed
   static constexpr size_t off_gam = off_tn + 2 * kPF;    // Gam_last        [K] fp32
-  static constexpr size_t off_valid = off_gam + 2 * (size_t)K;   // 4 x 16 row-valid bits
+  static constexpr size_t off_valid = off_gam + 2 * (size_t)K;   // 4 x 16 row-valid bits, then
+                                                                 // the contraction bound (fp32)
   static constexpr size_t kElems = off_valid + 8;
 };
 
@@ -110,6 +111,14 @@ struct ScanParams {
   const int32_t* slot;                     // varlen: state slot of each sequence in a pool of S, or null
   int S;
   int B, T, H, dk, dv, chunk, NC, NT, nbh;
+  // Segmented scan (batch layout): each (b, h) cut into G segments of seg_nc chunks.
+  // plan[(b H + h) G + g]: g = 0 the head's flag (1: every boundary has a forgetting tail),
+  // g >= 1 the first chunk of boundary g's tail.  seg_states [B H][G][dk][dv]: segment g's
+  // entry state (g = 0: a copy of the initial state).  pass 1: the tails (and the copies),
+  // pass 2: the segments, pass 0: every head that is not segmented, as one chain.
+  const int32_t* plan;
+  float* seg_states;
+  int G, seg_nc, pass;
 };
 
 __device__ __forceinline__ void store_frag(uint16_t* dst, const bf16x8& v) {
@@ -221,6 +230,7 @@ prep_kernel(PrepParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_r3[Lds::r3];
   __shared__ __attribute__((aligned(16))) float s_r4[Lds::r4];
   __shared__ float s_beta[C];
+  __shared__ float s_bnd[4];                                         // per wave: bound over its rows
   __bf16* s_ki = reinterpret_cast<__bf16*>(s_r1);                    // [hi, lo][C][K] swzk (fast path)
   float* s_G = reinterpret_cast<float*>(s_r1);                       // [C][K] (other path)
   float* s_T = reinterpret_cast<float*>(s_r1);                       // [C][C] swzf
@@ -287,10 +297,11 @@ prep_kernel(PrepParams p) {
     q_r[ks].keep(cok);
   }
 
-  // ---- row scales of the optional L2 normalisation
-  float qs = 1.f, ksc = 1.f;
-  if (p.l2norm) {
-    float sq = 0.f, sk = 0.f;
+  // ---- row scales of the optional L2 normalisation, and the key row's squared norm (it
+  //      also enters the chunk's contraction bound below)
+  float qs = 1.f, ksc = 1.f, sk = 0.f;
+  {
+    float sq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float qf[8], kf[8];
@@ -301,8 +312,10 @@ prep_kernel(PrepParams p) {
     }
     sq += __shfl_xor(sq, 16, 64); sk += __shfl_xor(sk, 16, 64);
     sq += __shfl_xor(sq, 32, 64); sk += __shfl_xor(sk, 32, 64);
-    qs = rsqrtf(sq + 1e-6f);
-    ksc = rsqrtf(sk + 1e-6f);
+    if (p.l2norm) {
+      qs = rsqrtf(sq + 1e-6f);
+      ksc = rsqrtf(sk + 1e-6f);
+    }
   }
   if (tid < 8) { s_zero[tid] = 0.f; s_one[tid] = 1.f; }
   if (rows && lane < 16) {
@@ -313,6 +326,7 @@ prep_kernel(PrepParams p) {
   // ---- inclusive cumulative sum of log2 decay over the tile's 16 rows (DPP row scan);
   //      invalid rows and channels past dk contribute 0
   float g_r[KS][8];
+  float lmax = -INFINITY, lchk = 0.f;                                // for the contraction bound
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const bool cok = rok && 32 * ks + cg < dk;
@@ -321,12 +335,35 @@ prep_kernel(PrepParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = cok ? laf[e] * kLog2e : 0.f;
+      lmax = fmaxf(lmax, cok ? x : -INFINITY);
+      lchk += x;
       x += row_shr<1>(x);
       x += row_shr<2>(x);
       x += row_shr<4>(x);
       x += row_shr<8>(x);
       g_r[ks][e] = x;
     }
+  }
+  // ---- the chunk's contraction bound, log2 of an upper bound on the spectral norm of the
+  //      state transition over the chunk's valid rows.  A row's step S -> (I - b k k^T)
+  //      Diag(alpha) S + ... has norm at most max_c alpha_c times max(1, |1 - b |k|^2|)
+  //      (the projection is symmetric with eigenvalues 1 and 1 - b |k|^2), and a chunk's
+  //      transition is the product of its rows'.  A row that is not valid is the identity
+  //      (0).  A non-finite input gives a NaN bound, which no test below accepts.
+  {
+    float lm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
+    lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
+    float lc = lchk + __shfl_xor(lchk, 16, 64);
+    lc += __shfl_xor(lc, 32, 64);
+    const float kk = ksc * ksc * sk;
+    float f = fabsf(1.f - beta_r * kk);
+    f = f <= 1.f ? 1.f : f;                                          // (a NaN stays NaN)
+    float l = rok ? lm + __log2f(f) + 0.f * lc : 0.f;
+    l += __shfl_xor(l, 1, 64);                                       // lanes 0-15: the tile's rows
+    l += __shfl_xor(l, 2, 64);
+    l += __shfl_xor(l, 4, 64);
+    l += __shfl_xor(l, 8, 64);
+    if (lane == 0) s_bnd[I] = rows ? l : 0.f;
   }
   if (rows && (lane % 16) == 15) {
 #pragma unroll
@@ -451,6 +488,8 @@ prep_kernel(PrepParams p) {
     if (lane == 0) wsb[L::off_valid + I] = rows ? (uint16_t)(bal & 0xffffu) : (uint16_t)0;
   }
   __syncthreads();
+  if (tid == 0)                                                      // after the valid bits
+    *reinterpret_cast<float*>(wsb + L::off_valid + 4) = (s_bnd[0] + s_bnd[1]) + (s_bnd[2] + s_bnd[3]);
 
   // ---- Kh^T fragments: row c, contraction over rows 8*oct .. +7
   for (int idx = tid; idx < K * (C / 8); idx += kPrepThreads) {
@@ -872,8 +911,11 @@ scan_kernel(ScanParams p) {
   // XCD-aware mapping: all dv tiles of one head share blockIdx.x % 8 (one L2)
   const int L_id = blockIdx.x;
   const int xcd = L_id % 8, slot = L_id / 8;
-  const int bh = (slot / p.NT) * 8 + xcd, tile = slot % p.NT;
-  if (bh >= p.nbh) return;
+  const int vbh = (slot / p.NT) * 8 + xcd, tile = slot % p.NT;
+  if (vbh >= p.nbh) return;
+  // passes 1 and 2 of a segmented scan run one chain per (b, h, segment)
+  const bool seg_pass = p.plan != nullptr && p.pass != 0;
+  const int bh = seg_pass ? vbh / p.G : vbh, seg = seg_pass ? vbh % p.G : 0;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = tile * TW;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -899,8 +941,6 @@ scan_kernel(ScanParams p) {
     ws_chunk0 = (size_t)h * p.NC + p.first[b];
     NCs = p.first[b + 1] - p.first[b];
   }
-  const uint16_t* wsh = p.ws + ws_chunk0 * L::kElems;
-  const int last = NCs - 1;
   // where this (sequence, head) keeps its state: its own row, or its slot of a pool (a
   // slot outside the pool: no state is read or kept, the sequence starts from zero)
   int sbh = bh;
@@ -908,6 +948,38 @@ scan_kernel(ScanParams p) {
     const int sl = p.slot[b];
     sbh = (sl >= 0 && sl < p.S) ? sl * p.H + h : -1;
   }
+  const size_t mat = (size_t)dk * dv;
+  const float* init_ptr = (p.init_state != nullptr && sbh >= 0) ? p.init_state + (size_t)sbh * mat : nullptr;
+  float* fin_ptr = (p.final_state != nullptr && sbh >= 0) ? p.final_state + (size_t)sbh * mat : nullptr;
+  bool outputs = true;
+  if (p.plan != nullptr) {
+    // segmented scan: this chain's chunks [c0, c1), where its state comes from and goes to
+    const int32_t* pl = p.plan + (size_t)bh * p.G;
+    const bool seg_ok = pl[0] != 0;
+    if (seg_ok != seg_pass) return;                  // pass 0 takes the heads passes 1, 2 leave
+    int c0 = 0, c1 = p.NC;
+    float* st = p.seg_states + ((size_t)bh * p.G + seg) * mat;
+    if (p.pass == 1) {
+      // segment 0: the initial state copied (no chunk), so that pass 2 may write the final
+      // state over it; segment g: boundary g's tail from zero, its end state kept, no output
+      c1 = seg == 0 ? 0 : seg * p.seg_nc;
+      c0 = seg == 0 ? 0 : min(max(pl[seg], 0), c1);
+      if (seg > 0) init_ptr = nullptr;
+      fin_ptr = st;
+      outputs = false;
+    } else if (p.pass == 2) {
+      c0 = seg * p.seg_nc;
+      c1 = min(c0 + p.seg_nc, p.NC);
+      init_ptr = st;
+      if (seg + 1 < p.G) fin_ptr = nullptr;
+    }
+    seq_tok0 += (size_t)c0 * p.chunk;
+    ws_chunk0 += (size_t)c0;
+    seq_T = min(p.T - c0 * p.chunk, (c1 - c0) * p.chunk);
+    NCs = c1 - c0;
+  }
+  const uint16_t* wsh = p.ws + ws_chunk0 * L::kElems;
+  const int last = NCs - 1;
   // tokens are H * dv elements apart in q, k, v and o; byte offsets inside a chunk stay
   // below 2^32 (checked on the host)
   const size_t row_bytes = (size_t)p.H * dv * sizeof(Tv);
@@ -1030,7 +1102,8 @@ scan_kernel(ScanParams p) {
           for (int i = 0; i < kStores; ++i) {
             const int rr = 16 * I + 4 * (lane / 16) + i;
             Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i] + kVT * hf * (uint32_t)sizeof(Tv));
-            if (!full && !(rr < p.chunk && t0 + rr < seq_T)) dst = sink + 64 * hf + 16 * i + (lane % 16);
+            if (!outputs || (!full && !(rr < p.chunk && t0 + rr < seq_T)))
+              dst = sink + 64 * hf + 16 * i + (lane % 16);
             E::st(dst, 0, o4[hf][0][i] + o4[hf][1][i]);
           }
         }
@@ -1195,8 +1268,7 @@ scan_kernel(ScanParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * M + 4 * (lane / 16) + i, col = v0 + kVT * hf + (lane % 16);
-        S[hf][m][i] = (M < SRT && row < dk && p.init_state != nullptr && sbh >= 0)
-                          ? p.init_state[((size_t)sbh * dk + row) * dv + col] : 0.f;
+        S[hf][m][i] = (M < SRT && row < dk && init_ptr != nullptr) ? init_ptr[(size_t)row * dv + col] : 0.f;
       }
     }
   }
@@ -1371,7 +1443,47 @@ scan_kernel(ScanParams p) {
   asm volatile("" :: "v"(warmA), "v"(warmB));
   __builtin_amdgcn_s_waitcnt(0);
 
-  if (sbh >= 0) store_state(p.final_state + (size_t)sbh * dk * dv);
+  if (fin_ptr != nullptr) store_state(fin_ptr);
+}
+
+// ================================================================ segmented scan plan
+// One workgroup per (b, h).  Thread g - 1 takes boundary g (chunk g * seg_nc): walking back
+// over the segment before it, it looks for the shortest tail of chunks ending at the
+// boundary whose contraction bounds sum to at most kForgetLog2.  The exact map from the
+// state entering the tail to the state at the boundary then has spectral norm at most
+// 2^kForgetLog2, so the tail run from a zero state gives the boundary state to within
+// 2^-100 of the state's own norm, far below fp32 rounding.  A head is segmented only if
+// every boundary has such a tail; the others run as one chain, as without a plan.
+constexpr float kForgetLog2 = -100.f;
+constexpr int kPlanThreads = 64;                    // boundaries per (b, h): G - 1 <= 63
+
+template <int K, int V, int C, bool SPLIT>
+__global__ void __launch_bounds__(kPlanThreads)
+seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int32_t* __restrict__ plan) {
+  using L = WsLayout<K, V, C, SPLIT>;
+  const int bh = blockIdx.x, g = threadIdx.x + 1;
+  int start = -1;
+  if (g < G) {
+    const int end = g * seg_nc, lo = end - seg_nc;
+    const uint16_t* base = ws + (size_t)bh * NC * L::kElems + L::off_valid + 4;
+    float acc = 0.f;
+    for (int j0 = end - 1; j0 >= lo && start < 0; j0 -= 8) {
+      float bnd[8];                                  // eight loads in flight, then the walk
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        bnd[u] = j0 - u >= lo ? *reinterpret_cast<const float*>(base + (size_t)(j0 - u) * L::kElems) : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (start < 0 && j0 - u >= lo) {
+          acc += bnd[u];
+          if (acc <= kForgetLog2) start = j0 - u;      // a NaN bound never passes
+        }
+      }
+    }
+  }
+  const bool ok = __syncthreads_and(g >= G || start >= 0);
+  if (g < G) plan[(size_t)bh * G + g] = start;
+  if (threadIdx.x == 0) plan[(size_t)bh * G] = ok ? 1 : 0;
 }
 
 // ================================================================ packed sequences
@@ -1474,12 +1586,32 @@ bool prefill_grid_ok(int B, int T, int H, int chunk, bool varlen) {
 }
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Segments per (b, h) of a segmented scan (1: none).  It pays where the 32-column scan
+// tiles (bf16, dv = 128) would not otherwise fill the chip, i.e. with fewer than 64 (b, h)
+// pairs: segments double until there are 64 chains, each of at least kMinSegChunks chunks
+// (the tails that precede the boundaries stay a small fraction of the work).
+constexpr int kMinSegChunks = 64;
+static int seg_count(int nbh, long long NC, int dv, int dtype) {
+  if (dtype != 0 || dv != 128 || nbh <= 0) return 1;
+  int G = 1;
+  while ((long long)nbh * G < 64 && NC / (2LL * G) >= kMinSegChunks) G *= 2;
+  return G;
+}
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen) {
   if (B == 0 || H == 0 || (T == 0 && !varlen)) return 0;
   const long long NC = prefill_chunks(B, T, chunk, varlen);
   const size_t per_chunk = chunk_ws_elems(pad_k(dk), dv, tile_chunk(chunk), dtype) * 2;
-  if (!varlen) return (size_t)B * H * NC * per_chunk + kSinkBytes;
+  if (!varlen) {
+    // a segmented scan adds the segments' entry states and the plan after the sink
+    const size_t base = (size_t)B * H * NC * per_chunk + kSinkBytes;
+    const int G = seg_count(B * H, NC, dv, dtype);
+    if (G == 1) return base;
+    const size_t chains = (size_t)B * H * G;
+    return align256(base) + chains * dk * dv * 4 + chains * 4;
+  }
   // packed: H x NC chunks, the sink, then the chunk table (span, seq, first)
   return (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + (size_t)B * 16 +
          align16((size_t)(B + 1) * 4);
@@ -1526,7 +1658,41 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   ScanParams sp{a.v, a.init_state, a.final_state, a.o, (const uint16_t*)a.workspace,
                 NC > 0 ? (void*)((unsigned char*)a.workspace + chunks_bytes) : nullptr, seq, first,
                 ckpt ? a.chunk_states : nullptr, ckpt ? a.state_interval / a.chunk : 0, ckpt ? a.num_states : 0,
-                varlen ? a.slot : nullptr, a.num_slots, a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh};
+                varlen ? a.slot : nullptr, a.num_slots, a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh,
+                nullptr, nullptr, 1, NC, 0};
+  if constexpr (kWideOk) {
+    // segmented scan: plan, then the tails (pass 1) and the segments (pass 2) as chains of
+    // 32-column tiles, then the heads without a plan as single chains (pass 0)
+    const int G = (varlen || ckpt || a.serial_scan) ? 1 : seg_count(nbh, NC, a.dv, DT);
+    if (G > 1) {
+      const size_t chains = (size_t)nbh * G;
+      unsigned char* tail = (unsigned char*)a.workspace + align256(chunks_bytes + kSinkBytes);
+      sp.seg_states = reinterpret_cast<float*>(tail);
+      sp.plan = reinterpret_cast<const int32_t*>(tail + chains * a.dk * a.dv * 4);
+      sp.G = G;
+      sp.seg_nc = (NC + G - 1) / G;
+      hipLaunchKernelGGL((seg_plan_kernel<K, V, C, DT == 1>), dim3(nbh), dim3(kPlanThreads), 0, st,
+                         (const uint16_t*)a.workspace, NC, G, sp.seg_nc, const_cast<int32_t*>(sp.plan));
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      ScanParams sw = sp;
+      sw.nbh = (int)chains;
+      sw.NT = a.dv / (2 * kVT);
+      const int wgroups = ((int)chains + 7) / 8;
+      for (int pass = 1; pass <= 2; ++pass) {
+        sw.pass = pass;
+        hipLaunchKernelGGL((scan_kernel<DT, K, V, C, 2 * kVT>), dim3(wgroups * 8 * sw.NT), dim3(kScanThreads), 0,
+                           st, sw);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      sp.pass = 0;                                   // then the heads left to a single chain
+      sp.NT = a.dv / kVT;
+      hipLaunchKernelGGL((scan_kernel<DT, K, V, C, kVT>), dim3((nbh + 7) / 8 * 8 * sp.NT), dim3(kScanThreads), 0,
+                         st, sp);
+      return hipGetLastError();
+    }
+  }
   const int groups = (nbh + 7) / 8;
   if constexpr (kWideOk) {
     if (wide) {

@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_BF16, KDA_F32 = 0, 1
-KDA_FLAG_L2NORM_QK, KDA_FLAG_SILU, KDA_FLAG_SCALAR_GATE = 1, 2, 4
+KDA_FLAG_L2NORM_QK, KDA_FLAG_SILU, KDA_FLAG_SCALAR_GATE, KDA_FLAG_SERIAL_SCAN = 1, 2, 4, 8
 STATUS = {0: "KDA_OK", -1: "KDA_ERR_INVALID_ARG", -2: "KDA_ERR_UNSUPPORTED",
           -3: "KDA_ERR_WORKSPACE", -4: "KDA_ERR_HIP"}
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_last_hip_error",
@@ -137,12 +137,14 @@ def prefill_workspace_size(B, T, H, dk, dv, chunk, dtype_code) -> int:
 
 
 def chunk_prefill(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
-                  l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False):
+                  l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False,
+                  serial_scan=False):
     """KDA prefill.  q,k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32), log_alpha [B,T,H,dk] fp32,
     beta [B,T,H] fp32, mask [B,T] uint8/bool or None, initial_state [B,H,dk,dv] fp32 or None.
+    serial_scan: KDA_FLAG_SERIAL_SCAN (each (b, h) scanned as one chain, never in segments).
     Returns (o [B,T,H,dv] in q's dtype, final_state [B,H,dk,dv] fp32)."""
     o, fin, _ = _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2norm_qk,
-                               out, final_state, workspace, scalar_gate, None, 0)
+                               out, final_state, workspace, scalar_gate, None, 0, serial_scan)
     return o, fin
 
 
@@ -171,7 +173,7 @@ def chunk_prefill_states(q, k, v, log_alpha, beta, mask=None, initial_state=None
 
 
 def _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2norm_qk, out,
-                   final_state, workspace, scalar_gate, chunk_states, state_interval):
+                   final_state, workspace, scalar_gate, chunk_states, state_interval, serial_scan=False):
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -198,7 +200,8 @@ def _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    flags = (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_SCALAR_GATE if scalar_gate else 0)
+    flags = ((KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_SCALAR_GATE if scalar_gate else 0) |
+             (KDA_FLAG_SERIAL_SCAN if serial_scan else 0))
     if chunk_states is None:
         st = lib.kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(mask),
                                    _ptr(initial_state), _ptr(out), _ptr(final_state),
@@ -216,7 +219,8 @@ def _prefill_batch(q, k, v, log_alpha, beta, mask, initial_state, chunk_size, l2
 
 
 def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=None, chunk_size=64,
-                          l2norm_qk=False, out=None, final_state=None, scalar_gate=False):
+                          l2norm_qk=False, out=None, final_state=None, scalar_gate=False,
+                          serial_scan=False):
     """kda_chunk_prefill_noalloc: chunk_prefill without a workspace (the library's per-GPU
     scratch array stands in for it).  out and final_state may be given so that the call
     itself allocates nothing; otherwise they are allocated here, before the C call."""
@@ -246,7 +250,8 @@ def chunk_prefill_noalloc(q, k, v, log_alpha, beta, mask=None, initial_state=Non
                                        _ptr(initial_state), _ptr(out), _ptr(final_state),
                                        B, T, H, dk, dv, int(chunk_size), dt,
                                        (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
-                                       (KDA_FLAG_SCALAR_GATE if scalar_gate else 0), _stream())
+                                       (KDA_FLAG_SCALAR_GATE if scalar_gate else 0) |
+                                       (KDA_FLAG_SERIAL_SCAN if serial_scan else 0), _stream())
     _check("kda_chunk_prefill_noalloc", st)
     return out, final_state
 

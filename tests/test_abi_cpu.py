@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert lib.kda_status_string(code).decode().startswith(kda.STATUS[code])
     assert lib.kda_status_string(17) == b"unknown kda_status"
@@ -124,6 +124,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, T=-3) == INVALID
     assert _prefill(lib, dtype=2) == INVALID
     assert _prefill(lib, flags=2) == INVALID            # SILU belongs to the short conv
+    assert _prefill(lib, flags=16) == INVALID           # no such flag
+    assert _prefill(lib, flags=8, ws=None) == WORKSPACE  # KDA_FLAG_SERIAL_SCAN is accepted
     assert _prefill(lib, v=None) == INVALID
     assert _prefill(lib, sT=None) == INVALID
     assert _prefill(lib, s0=ctypes.c_void_p(0x10002)) == INVALID
@@ -299,7 +301,7 @@ def test_noalloc_validation(lib):
                                              a["dtype"], a["flags"], None)
     assert call(dk=7) == UNSUPPORTED
     assert call(q=MISALIGNED) == INVALID
-    assert call(flags=8) == INVALID
+    assert call(flags=16) == INVALID
     assert call(o=None) == INVALID
     big = 1
     while lib.kda_chunk_prefill_workspace_size(1, big, 32, 128, 128, 64, 0) <= lim:

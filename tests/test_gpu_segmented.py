@@ -1,0 +1,154 @@
+"""GPU tests of the segmented scan of kda_chunk_prefill (through the C ABI).
+
+With bf16 inputs, dv = 128, fewer than 64 (b, h) pairs and at least 128 chunks, the call
+cuts each head's sequence into G segments scanned side by side; the state entering segment g
+is the run from a zero state over a tail of chunks whose per-token contraction bounds
+multiply to at most 2^-100, and a head with a boundary lacking such a tail is scanned as one
+chain.  The tests check the results against the fp64 oracle (every position, final state),
+the fallback bit for bit against KDA_FLAG_SERIAL_SCAN, and which heads were segmented by
+reading the plan the call leaves at the end of its workspace.
+"""
+import numpy as np
+import pytest
+
+from linear_attention_recurrence_kda_amd import datagen as D
+from tests.gpu_util import check, device, host, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DK = DV = 128
+
+
+def _segments(nbh, NC):
+    """The segment count the library chooses (mirrors its rule: double while there are
+    fewer than 64 chains and every segment keeps at least 64 chunks)."""
+    G = 1
+    while nbh * G < 64 and NC // (2 * G) >= 64:
+        G *= 2
+    return G
+
+
+def _run(inp, dev, mask=None, s0=None, l2norm=False, serial=False, scalar_gate=False, inplace=False):
+    """Returns (o, final_state, plan or None): the plan is read from the workspace tail."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    B, T, H, _ = inp["q"].shape
+    d = dict(q=to_dev(inp["q"], "bf16", dev), k=to_dev(inp["k"], "bf16", dev), v=to_dev(inp["v"], "bf16", dev),
+             log_alpha=to_dev(inp["log_alpha"], dev=dev), beta=to_dev(inp["beta"], dev=dev))
+    need = kda.prefill_workspace_size(B, T, H, DK, DV, 64, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    init = None if s0 is None else to_dev(s0, dev=dev)
+    fin = init if inplace else None
+    o, s = kda.chunk_prefill(**d, mask=None if mask is None else to_dev(mask, dev=dev), initial_state=init,
+                             chunk_size=64, l2norm_qk=l2norm, workspace=ws, scalar_gate=scalar_gate,
+                             serial_scan=serial, final_state=fin)
+    torch.cuda.synchronize()
+    G = _segments(B * H, (T + 63) // 64)
+    plan = None
+    if G > 1 and not serial:
+        plan = ws[need - B * H * G * 4:need].view(torch.int32).cpu().numpy().reshape(B * H, G)
+    return o, s, plan
+
+
+def _check_all(name, o, s, ro, rs):
+    check(f"{name} o", host(o), ro, "bf16")
+    check(f"{name} state", host(s), rs, "bf16")
+
+
+@pytest.mark.parametrize("T", [8192, 16384 + 37])
+def test_segmented_fast_gates_vs_oracle(oracle, T):
+    """Default gates forget within a few chunks: every head is segmented (G = 2 at 8192
+    tokens, 4 at 16421 with two heads); o at every position and the final state against the
+    oracle, and against the single-chain call within the same bar."""
+    dev = device()
+    B, H = 1, 2
+    say(f"[case] segmented fast gates T={T}")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=51)
+    s0 = D.np_state(B, H, DK, DV, 0.1, seed=51)
+    o, s, plan = _run(inp, dev, s0=s0)
+    assert plan is not None and plan.shape[1] == _segments(B * H, (T + 63) // 64)
+    say(f"[plan] {plan.tolist()}")
+    assert np.all(plan[:, 0] == 1), "every head should be segmented"
+    G = plan.shape[1]
+    seg_nc = -(-((T + 63) // 64) // G)
+    for g in range(1, G):
+        assert np.all((plan[:, g] >= (g - 1) * seg_nc) & (plan[:, g] < g * seg_nc)), "tail inside the segment before"
+    ro, rs = oracle.c_prefill(**inp, init_state=s0)
+    _check_all("segmented", o, s, ro, rs)
+    os_, ss, _ = _run(inp, dev, s0=s0, serial=True)
+    _check_all("serial", os_, ss, ro, rs)
+
+
+def test_segmented_slow_gates_fall_back_bitwise():
+    """Slow gates (the state lives for thousands of tokens): no boundary has a forgetting
+    tail, so every head runs as one chain, bit for bit the KDA_FLAG_SERIAL_SCAN call."""
+    import torch
+    dev = device()
+    B, T, H = 1, 8192 + 5, 3
+    say("[case] segmented slow gates fall back")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=52, decay="slow")
+    s0 = D.np_state(B, H, DK, DV, 0.1, seed=52)
+    o, s, plan = _run(inp, dev, s0=s0)
+    assert plan is not None and np.all(plan[:, 0] == 0), f"no head should be segmented: {plan[:, 0]}"
+    os_, ss, _ = _run(inp, dev, s0=s0, serial=True)
+    assert torch.equal(o, os_) and torch.equal(s, ss)
+
+
+def test_segmented_mixed_heads(oracle):
+    """Heads 0 and 2 forget fast, head 1 has one slow channel: heads 0 and 2 are segmented,
+    head 1 runs as one chain and equals its single-chain run bit for bit; all three against
+    the oracle, with a padding mask (left padding and a hole) and an initial state."""
+    import torch
+    dev = device()
+    B, T, H = 1, 8192 + 100, 3
+    say("[case] segmented mixed heads")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=53)
+    inp["log_alpha"][0, :, 1, 5] = -1e-4                  # one channel that almost never decays
+    mask = np.ones((B, T), np.uint8)
+    mask[0, :300] = 0
+    mask[0, 5000:5400] = 0
+    s0 = D.np_state(B, H, DK, DV, 0.1, seed=53)
+    o, s, plan = _run(inp, dev, mask=mask, s0=s0)
+    assert plan[:, 0].tolist() == [1, 0, 1], plan[:, 0]
+    os_, ss, _ = _run(inp, dev, mask=mask, s0=s0, serial=True)
+    assert torch.equal(o[:, :, 1], os_[:, :, 1]) and torch.equal(s[:, 1], ss[:, 1])
+    assert torch.all(o[0, :300] == 0) and torch.all(o[0, 5000:5400] == 0), "masked positions give o = 0"
+    ro, rs = oracle.c_prefill(**inp, mask=mask, init_state=s0)
+    _check_all("mixed", o, s, ro, rs)
+
+
+def test_segmented_flags_and_inplace(oracle):
+    """The q/k L2-norm flag on raw rows and the per-head gate, each with the final state
+    written over the initial state (pass 1 copies it before pass 2 overwrites it), and a
+    ragged tail; against the oracle."""
+    dev = device()
+    B, T, H = 1, 8192 + 63, 2
+    s0 = D.np_state(B, H, DK, DV, 0.1, seed=54)
+    say("[case] segmented l2norm in place")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=54, unit_qk=False)
+    o, s, plan = _run(inp, dev, s0=s0, l2norm=True, inplace=True)
+    assert np.all(plan[:, 0] == 1)
+    ro, rs = oracle.c_prefill(**inp, init_state=s0, l2norm_qk=True)
+    _check_all("l2norm", o, s, ro, rs)
+    say("[case] segmented per-head gate in place")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=55)
+    gate = np.ascontiguousarray(inp["log_alpha"][..., 0])                    # [B,T,H]
+    run = dict(inp, log_alpha=gate)
+    o, s, plan = _run(run, dev, s0=s0, scalar_gate=True, inplace=True)
+    assert np.all(plan[:, 0] == 1)
+    ro, rs = oracle.c_prefill(**dict(inp, log_alpha=np.repeat(gate[..., None], DK, axis=-1)), init_state=s0)
+    _check_all("per-head gate", o, s, ro, rs)
+
+
+def test_segmented_deterministic():
+    """Two calls on the same inputs give the same bits (the plan is made on the device from
+    the inputs alone)."""
+    import torch
+    dev = device()
+    B, T, H = 2, 8192, 4
+    say("[case] segmented determinism")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=56)
+    o1, s1, p1 = _run(inp, dev)
+    o2, s2, p2 = _run(inp, dev)
+    assert np.all(p1[:, 0] == 1)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2) and np.array_equal(p1, p2)
