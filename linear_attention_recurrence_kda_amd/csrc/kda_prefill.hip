@@ -133,6 +133,15 @@ __device__ __forceinline__ void pin8(bf16x8& v) {
   asm volatile("" : "+v"(u));
   v = __builtin_bit_cast(bf16x8, u);
 }
+// The raw words of a row slice, hidden from the optimiser (no value computed from them is
+// shared with a later conversion of the same words)
+__device__ __forceinline__ void opaque(Raw8<0>& r) {
+  asm volatile("" : "+v"(r.u.x), "+v"(r.u.y), "+v"(r.u.z), "+v"(r.u.w));
+}
+__device__ __forceinline__ void opaque(Raw8<1>& r) {
+  asm volatile("" : "+v"(r.a.x), "+v"(r.a.y), "+v"(r.a.z), "+v"(r.a.w));
+  asm volatile("" : "+v"(r.b.x), "+v"(r.b.y), "+v"(r.b.z), "+v"(r.b.w));
+}
 // 8 consecutive floats from 16-byte aligned LDS
 __device__ __forceinline__ void ld8f(const float* src, float* out) {
   const float4 a = reinterpret_cast<const float4*>(src)[0];
@@ -297,25 +306,79 @@ prep_kernel(PrepParams p) {
     q_r[ks].keep(cok);
   }
 
-  // ---- row scales of the optional L2 normalisation, and the key row's squared norm (it
-  //      also enters the chunk's contraction bound below)
-  float qs = 1.f, ksc = 1.f, sk = 0.f;
-  {
+  // ---- the key row's squared norm (for the contraction bound below, and the L2 norm);
+  //      converted from an opaque copy of the raw words, so that the compiler does not keep
+  //      these floats alive until the decay pass converts the same words again
+  float sk = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    Raw8<DT> kc = k_r[ks];
+    opaque(kc);
+    float kf[8];
+    kc.to_float(kf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sk += kf[e] * kf[e];
+  }
+  sk += __shfl_xor(sk, 16, 64);
+  sk += __shfl_xor(sk, 32, 64);
+  // ---- row scales of the optional L2 normalisation
+  float qs = 1.f, ksc = 1.f;
+  if (p.l2norm) {
     float sq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      float qf[8], kf[8];
+      float qf[8];
       q_r[ks].to_float(qf);
-      k_r[ks].to_float(kf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { sq += qf[e] * qf[e]; sk += kf[e] * kf[e]; }
+      for (int e = 0; e < 8; ++e) sq += qf[e] * qf[e];
     }
-    sq += __shfl_xor(sq, 16, 64); sk += __shfl_xor(sk, 16, 64);
-    sq += __shfl_xor(sq, 32, 64); sk += __shfl_xor(sk, 32, 64);
-    if (p.l2norm) {
-      qs = rsqrtf(sq + 1e-6f);
-      ksc = rsqrtf(sk + 1e-6f);
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    qs = rsqrtf(sq + 1e-6f);
+    ksc = rsqrtf(sk + 1e-6f);
+  }
+  // ---- the chunk's contraction bound, log2 of an upper bound on the spectral norm of the
+  //      state transition over the chunk's valid rows.  A row's step S -> (I - b k k^T)
+  //      Diag(alpha) S + ... has norm at most max_c alpha_c times max(1, |1 - b |k|^2|)
+  //      (the projection is symmetric with eigenvalues 1 and 1 - b |k|^2), and a chunk's
+  //      transition is the product of its rows'.  A row that is not valid is the identity
+  //      (0).  A non-finite input gives a NaN bound, which no test of it accepts.
+  {
+    float lm, lc;                                                    // max and sum of log2 alpha
+    if constexpr (SGP) {
+      float laf[8];
+      la_r[0].to_float(laf);                                         // the row's one gate
+      lm = laf[0] * kLog2e;
+      lc = lm;
+    } else {
+      lm = -INFINITY;
+      lc = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bool cin = 32 * ks + cg < dk;
+        float laf[8];
+        la_r[ks].to_float(laf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = cin ? laf[e] * kLog2e : 0.f;
+          lm = fmaxf(lm, cin ? x : -INFINITY);
+          lc += x;
+        }
+      }
+      lm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+      lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
+      lc += __shfl_xor(lc, 16, 64);
+      lc += __shfl_xor(lc, 32, 64);
     }
+    const float kk = ksc * ksc * sk;
+    float f = fabsf(1.f - beta_r * kk);
+    f = f <= 1.f ? 1.f : f;                                          // (a NaN stays NaN)
+    float l = rok ? lm + __log2f(f) + 0.f * lc : 0.f;
+    l += __shfl_xor(l, 1, 64);                                       // lanes 0-15: the tile's rows
+    l += __shfl_xor(l, 2, 64);
+    l += __shfl_xor(l, 4, 64);
+    l += __shfl_xor(l, 8, 64);
+    if (lane == 0) s_bnd[I] = rows ? l : 0.f;
   }
   if (tid < 8) { s_zero[tid] = 0.f; s_one[tid] = 1.f; }
   if (rows && lane < 16) {
@@ -326,7 +389,6 @@ prep_kernel(PrepParams p) {
   // ---- inclusive cumulative sum of log2 decay over the tile's 16 rows (DPP row scan);
   //      invalid rows and channels past dk contribute 0
   float g_r[KS][8];
-  float lmax = -INFINITY, lchk = 0.f;                                // for the contraction bound
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const bool cok = rok && 32 * ks + cg < dk;
@@ -335,35 +397,12 @@ prep_kernel(PrepParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = cok ? laf[e] * kLog2e : 0.f;
-      lmax = fmaxf(lmax, cok ? x : -INFINITY);
-      lchk += x;
       x += row_shr<1>(x);
       x += row_shr<2>(x);
       x += row_shr<4>(x);
       x += row_shr<8>(x);
       g_r[ks][e] = x;
     }
-  }
-  // ---- the chunk's contraction bound, log2 of an upper bound on the spectral norm of the
-  //      state transition over the chunk's valid rows.  A row's step S -> (I - b k k^T)
-  //      Diag(alpha) S + ... has norm at most max_c alpha_c times max(1, |1 - b |k|^2|)
-  //      (the projection is symmetric with eigenvalues 1 and 1 - b |k|^2), and a chunk's
-  //      transition is the product of its rows'.  A row that is not valid is the identity
-  //      (0).  A non-finite input gives a NaN bound, which no test below accepts.
-  {
-    float lm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));
-    lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
-    float lc = lchk + __shfl_xor(lchk, 16, 64);
-    lc += __shfl_xor(lc, 32, 64);
-    const float kk = ksc * ksc * sk;
-    float f = fabsf(1.f - beta_r * kk);
-    f = f <= 1.f ? 1.f : f;                                          // (a NaN stays NaN)
-    float l = rok ? lm + __log2f(f) + 0.f * lc : 0.f;
-    l += __shfl_xor(l, 1, 64);                                       // lanes 0-15: the tile's rows
-    l += __shfl_xor(l, 2, 64);
-    l += __shfl_xor(l, 4, 64);
-    l += __shfl_xor(l, 8, 64);
-    if (lane == 0) s_bnd[I] = rows ? l : 0.f;
   }
   if (rows && (lane % 16) == 15) {
 #pragma unroll
