@@ -437,3 +437,23 @@ def test_varlen_backward_validation(lib):
     assert call(N=0) == OK                      # nothing to do
     assert call(H=0) == OK
     assert call(N=15, T=64 * 65521, H=64, dk=128, dv=128, ws=None) == UNSUPPORTED
+
+
+def test_segmented_workspace_size(lib):
+    """A batch prefill that may run as a segmented scan (bf16, dv = 128, B*H < 64, at least 128
+    chunks) needs, after the chunks and the 16 KB sink (rounded up to 256 bytes), one fp32
+    dk x dv entry state and one int per (b, h, segment); otherwise only chunks and sink."""
+    def size(B, T, H, dk=128, dv=128, chunk=64, dtype=0):
+        return lib.kda_chunk_prefill_workspace_size(B, T, H, dk, dv, chunk, dtype)
+    per_chunk = (size(1, 64, 1) - 16384)                    # one (b, h) chunk
+    assert per_chunk > 0
+    plain = lambda B, T, H: B * H * ((T + 63) // 64) * per_chunk + 16384
+    assert size(1, 8128, 2) == plain(1, 8128, 2)            # 127 chunks: one chain
+    for B, T, H, G in ((1, 8192, 2, 2), (1, 16421, 2, 4), (1, 131072, 32, 2), (2, 8192, 4, 2)):
+        base = plain(B, T, H)
+        want = (base + 255) // 256 * 256 + B * H * G * (128 * 128 * 4 + 4)
+        assert size(B, T, H) == want, (B, T, H)
+    assert size(1, 8192, 64) == plain(1, 8192, 64)          # 64 (b, h) pairs: never segmented
+    assert size(1, 8192, 2, dv=64) == (lambda pc: 2 * 128 * pc + 16384)(size(1, 64, 1, dv=64) - 16384)
+    fp = size(1, 8192, 2, dtype=1)                          # fp32: never segmented
+    assert fp == 2 * 128 * (size(1, 64, 1, dtype=1) - 16384) + 16384

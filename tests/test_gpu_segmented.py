@@ -152,3 +152,47 @@ def test_segmented_deterministic():
     o2, s2, p2 = _run(inp, dev)
     assert np.all(p1[:, 0] == 1)
     assert torch.equal(o1, o2) and torch.equal(s1, s2) and np.array_equal(p1, p2)
+
+
+@pytest.mark.parametrize("dk,chunk", [(64, 64), (128, 32), (32, 16)])
+def test_segmented_other_shapes(oracle, dk, chunk):
+    """Segmentation depends only on bf16, dv = 128, B*H < 64 and the chunk count: key sizes 64
+    and 32 and 32- and 16-token chunks (run inside the 32-row chunk kernels) segment too;
+    two batch rows with their own initial states, against the oracle."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, H = 2, 2
+    T = 128 * chunk + 21                                  # at least 128 chunks: segmented
+    say(f"[case] segmented dk={dk} chunk={chunk} T={T}")
+    inp = D.np_kda_inputs(B, T, H, dk, DV, "bf16", seed=57)
+    s0 = D.np_state(B, H, dk, DV, 0.1, seed=57)
+    d = dict(q=to_dev(inp["q"], "bf16", dev), k=to_dev(inp["k"], "bf16", dev), v=to_dev(inp["v"], "bf16", dev),
+             log_alpha=to_dev(inp["log_alpha"], dev=dev), beta=to_dev(inp["beta"], dev=dev))
+    need = kda.prefill_workspace_size(B, T, H, dk, DV, chunk, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    o, s = kda.chunk_prefill(**d, initial_state=to_dev(s0, dev=dev), chunk_size=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    G = _segments(B * H, (T + chunk - 1) // chunk)
+    assert G >= 2
+    plan = ws[need - B * H * G * 4:need].view(torch.int32).cpu().numpy().reshape(B * H, G)
+    assert np.all(plan[:, 0] == 1), plan
+    ro, rs = oracle.c_prefill(**inp, init_state=s0)
+    _check_all(f"dk{dk} chunk{chunk}", o, s, ro, rs)
+
+
+def test_segmented_noalloc_equals_workspace_call():
+    """kda_chunk_prefill_noalloc takes the same segmented path from its static scratch: bit
+    for bit the workspace call, twice in a row (the second call smaller but still segmented)."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    for T, H in ((16384 + 3, 2), (8192, 1)):
+        say(f"[case] segmented noalloc T={T} H={H}")
+        inp = D.np_kda_inputs(1, T, H, DK, DV, "bf16", seed=58)
+        d = dict(q=to_dev(inp["q"], "bf16", dev), k=to_dev(inp["k"], "bf16", dev), v=to_dev(inp["v"], "bf16", dev),
+                 log_alpha=to_dev(inp["log_alpha"], dev=dev), beta=to_dev(inp["beta"], dev=dev))
+        o1, s1 = kda.chunk_prefill(**d, chunk_size=64)
+        o2, s2 = kda.chunk_prefill_noalloc(**d, chunk_size=64)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
