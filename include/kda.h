@@ -127,8 +127,9 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * when its gates forget fast enough: the state entering segment g is taken as the run from a
  * zero state over the shortest tail of chunks before it whose per-token contraction bounds
  * (max over the key channels of alpha, times max(1, |1 - beta |k|^2|): the norm of one
- * step's state map) multiply to at most 2^-100, which changes that state by at most 2^-100
- * of its norm.  A head for which some boundary has no such tail inside the segment before
+ * step's state map) multiply to at most 2^-160, which changes that state by at most 2^-160
+ * of the norm of the state entering the tail, below 2^-25 in absolute value for any finite
+ * fp32 state.  A head for which some boundary has no such tail inside the segment before
  * it is scanned as one chain, so every input gets a result within rounding of the token
  * recurrence; the segmented one differs from the single chain's by rounding only.  The
  * call stays asynchronous (the choice is made on the device).  KDA_FLAG_SERIAL_SCAN turns

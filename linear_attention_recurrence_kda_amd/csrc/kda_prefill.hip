@@ -1490,10 +1490,12 @@ scan_kernel(ScanParams p) {
 // over the segment before it, it looks for the shortest tail of chunks ending at the
 // boundary whose contraction bounds sum to at most kForgetLog2.  The exact map from the
 // state entering the tail to the state at the boundary then has spectral norm at most
-// 2^kForgetLog2, so the tail run from a zero state gives the boundary state to within
-// 2^-100 of the state's own norm, far below fp32 rounding.  A head is segmented only if
-// every boundary has such a tail; the others run as one chain, as without a plan.
-constexpr float kForgetLog2 = -100.f;
+// 2^-160, so the tail run from a zero state gives the boundary state to within 2^-160 of the
+// Frobenius norm of the state entering the tail; that state is finite fp32 (norm below
+// 2^135), so the difference is below 2^-25 in absolute value whatever the inputs.  A head
+// is segmented only if every boundary has such a tail; the others run as one chain, as
+// without a plan.
+constexpr float kForgetLog2 = -160.f;
 constexpr int kPlanThreads = 64;                    // boundaries per (b, h): G - 1 <= 63
 
 template <int K, int V, int C, bool SPLIT>

@@ -3,7 +3,7 @@
 With bf16 inputs, dv = 128, fewer than 64 (b, h) pairs and at least 128 chunks, the call
 cuts each head's sequence into G segments scanned side by side; the state entering segment g
 is the run from a zero state over a tail of chunks whose per-token contraction bounds
-multiply to at most 2^-100, and a head with a boundary lacking such a tail is scanned as one
+multiply to at most 2^-160, and a head with a boundary lacking such a tail is scanned as one
 chain.  The tests check the results against the fp64 oracle (every position, final state),
 the fallback bit for bit against KDA_FLAG_SERIAL_SCAN, and which heads were segmented by
 reading the plan the call leaves at the end of its workspace.
