@@ -95,6 +95,7 @@ struct PrepParams {
   uint16_t* ws;
   const int2* span;                        // varlen chunk spans, or null (batch layout)
   int B, T, H, dk, dv, chunk, NC, l2norm, scalar_gate;
+  int bound;                               // 1: store each chunk's contraction bound (segmented scan)
 };
 
 struct ScanParams {
@@ -310,17 +311,19 @@ prep_kernel(PrepParams p) {
   //      converted from an opaque copy of the raw words, so that the compiler does not keep
   //      these floats alive until the decay pass converts the same words again
   float sk = 0.f;
+  if (p.l2norm || p.bound) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    Raw8<DT> kc = k_r[ks];
-    opaque(kc);
-    float kf[8];
-    kc.to_float(kf);
+    for (int ks = 0; ks < KS; ++ks) {
+      Raw8<DT> kc = k_r[ks];
+      opaque(kc);
+      float kf[8];
+      kc.to_float(kf);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sk += kf[e] * kf[e];
+      for (int e = 0; e < 8; ++e) sk += kf[e] * kf[e];
+    }
+    sk += __shfl_xor(sk, 16, 64);
+    sk += __shfl_xor(sk, 32, 64);
   }
-  sk += __shfl_xor(sk, 16, 64);
-  sk += __shfl_xor(sk, 32, 64);
   // ---- row scales of the optional L2 normalisation
   float qs = 1.f, ksc = 1.f;
   if (p.l2norm) {
@@ -342,8 +345,9 @@ prep_kernel(PrepParams p) {
   //      Diag(alpha) S + ... has norm at most max_c alpha_c times max(1, |1 - b |k|^2|)
   //      (the projection is symmetric with eigenvalues 1 and 1 - b |k|^2), and a chunk's
   //      transition is the product of its rows'.  A row that is not valid is the identity
-  //      (0).  A non-finite input gives a NaN bound, which no test of it accepts.
-  {
+  //      (0).  A non-finite input gives a NaN bound, which no test of it accepts.  Only a
+  //      launch whose scan is segmented reads it.
+  if (p.bound) {
     float lm, lc;                                                    // max and sum of log2 alpha
     if constexpr (SGP) {
       float laf[8];
@@ -527,7 +531,7 @@ prep_kernel(PrepParams p) {
     if (lane == 0) wsb[L::off_valid + I] = rows ? (uint16_t)(bal & 0xffffu) : (uint16_t)0;
   }
   __syncthreads();
-  if (tid == 0)                                                      // after the valid bits
+  if (p.bound && tid == 0)                                           // after the valid bits
     *reinterpret_cast<float*>(wsb + L::off_valid + 4) = (s_bnd[0] + s_bnd[1]) + (s_bnd[2] + s_bnd[3]);
 
   // ---- Kh^T fragments: row c, contraction over rows 8*oct .. +7
@@ -1685,9 +1689,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // segments per (b, h) of a segmented scan (1: one chain each)
+  const int G = (!kWideOk || varlen || ckpt || a.serial_scan) ? 1 : seg_count(nbh, NC, a.dv, DT);
   if (NC > 0) {
     PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace, span,
-                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate};
+                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate, G > 1 ? 1 : 0};
     const dim3 pgrid(NC * a.H, varlen ? 1 : a.B);
     if (DT == 0 && a.scalar_gate)
       hipLaunchKernelGGL((prep_kernel<DT, K, V, C, DT == 0>), pgrid, dim3(kPrepThreads), 0, st, pp);
@@ -1704,7 +1710,6 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if constexpr (kWideOk) {
     // segmented scan: plan, then the tails (pass 1) and the segments (pass 2) as chains of
     // 32-column tiles, then the heads without a plan as single chains (pass 0)
-    const int G = (varlen || ckpt || a.serial_scan) ? 1 : seg_count(nbh, NC, a.dv, DT);
     if (G > 1) {
       const size_t chains = (size_t)nbh * G;
       unsigned char* tail = (unsigned char*)a.workspace + align256(chunks_bytes + kSinkBytes);
