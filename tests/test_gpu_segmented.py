@@ -196,3 +196,72 @@ def test_segmented_noalloc_equals_workspace_call():
         o2, s2 = kda.chunk_prefill_noalloc(**d, chunk_size=64)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def _sweep_cases(n=10, seed=4242):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        chunk = int(r.choice([16, 32, 64]))
+        out.append(dict(dk=int(r.choice([32, 64, 128])), chunk=chunk, B=int(r.integers(1, 3)),
+                        H=int(r.choice([1, 2, 3])), T=int(r.integers(128 * chunk, 160 * chunk + 64)),
+                        mask=str(r.choice(["none", "left", "right", "holes"])), s0=bool(r.integers(0, 2)),
+                        l2=bool(r.integers(0, 2)), scalar=bool(r.integers(0, 2)),
+                        slow_head=bool(r.random() < 0.3), seed=300 + i))
+    return out
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("case", SWEEP, ids=[f"s{i}" for i in range(len(SWEEP))])
+def test_segmented_sweep(oracle, case):
+    """Seeded sweep over shapes that take the segmented path (bf16, dv = 128, B*H < 64, at
+    least 128 chunks): key size, chunk, batch, heads, length, mask pattern, initial state, the
+    two flags, and sometimes one head with a slow channel (which then runs as one chain); o and
+    the final state against the oracle, and the plan's per-head decision checked against which
+    head was made slow."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    c = case
+    B, T, H, dk, chunk = c["B"], c["T"], c["H"], c["dk"], c["chunk"]
+    say(f"[case] segmented sweep {c}")
+    inp = D.np_kda_inputs(B, T, H, dk, DV, "bf16", seed=c["seed"], unit_qk=not c["l2"])
+    if c["slow_head"]:
+        inp["log_alpha"][0, :, 0, :] *= 1e-3                   # (b 0, h 0) forgets too slowly
+    ref_la = inp["log_alpha"]
+    if c["scalar"]:
+        inp["log_alpha"] = np.ascontiguousarray(inp["log_alpha"][..., 0])
+        ref_la = np.repeat(inp["log_alpha"][..., None], dk, axis=-1)
+    mask = None
+    if c["mask"] != "none":
+        r = np.random.default_rng(c["seed"])
+        mask = np.ones((B, T), np.uint8)
+        for b in range(B):
+            cut = int(r.integers(0, T // 4))
+            if c["mask"] == "left":
+                mask[b, :cut] = 0
+            elif c["mask"] == "right":
+                mask[b, T - cut:] = 0
+            else:
+                mask[b, r.random(T) < 0.15] = 0
+    s0 = D.np_state(B, H, dk, DV, 0.1, seed=c["seed"]) if c["s0"] else None
+    d = dict(q=to_dev(inp["q"], "bf16", dev), k=to_dev(inp["k"], "bf16", dev), v=to_dev(inp["v"], "bf16", dev),
+             log_alpha=to_dev(inp["log_alpha"], dev=dev), beta=to_dev(inp["beta"], dev=dev))
+    need = kda.prefill_workspace_size(B, T, H, dk, DV, chunk, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    o, s = kda.chunk_prefill(**d, mask=None if mask is None else to_dev(mask, dev=dev),
+                             initial_state=None if s0 is None else to_dev(s0, dev=dev), chunk_size=chunk,
+                             l2norm_qk=c["l2"], scalar_gate=c["scalar"], workspace=ws)
+    torch.cuda.synchronize()
+    G = _segments(B * H, (T + chunk - 1) // chunk)
+    assert G >= 2
+    plan = ws[need - B * H * G * 4:need].view(torch.int32).cpu().numpy().reshape(B * H, G)
+    want = np.ones(B * H, np.int32)
+    if c["slow_head"]:
+        want[0] = 0
+    assert np.array_equal(plan[:, 0], want), plan[:, 0]
+    ro, rs = oracle.c_prefill(q=inp["q"], k=inp["k"], v=inp["v"], log_alpha=ref_la, beta=inp["beta"], mask=mask,
+                              init_state=s0, l2norm_qk=c["l2"])
+    _check_all("sweep", o, s, ro, rs)
