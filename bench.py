@@ -268,6 +268,31 @@ def main():
     graph_step_ms = sum(a_.elapsed_time(b_) for a_, b_ in gev) / (5 * 8)
     del graph
 
+    # how the headline call scanned: the plan its segmented scan left at the end of the
+    # workspace (segments per head by the library's rule; heads whose boundaries all had a
+    # forgetting tail), and the same call as single chains (KDA_FLAG_SERIAL_SCAN) beside it
+    G = 1
+    while H * G < 64 and ((T + C - 1) // C) // (2 * G) >= 64:
+        G *= 2
+    seg_heads = 0
+    if G > 1:
+        plan = ws[ws.numel() - H * G * 4:].view(torch.int32).view(H, G).cpu()
+        seg_heads = int((plan[:, 0] == 1).sum())
+
+    def prefill_serial():
+        kda.chunk_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], chunk_size=C,
+                          out=o, final_state=fs, workspace=ws, serial_scan=True)
+    prefill_serial()
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a_, b_ in sev:
+        a_.record()
+        prefill_serial()
+        b_.record()
+    torch.cuda.synchronize()
+    serial_ms = sum(a_.elapsed_time(b_) for a_, b_ in sev) / reps
+    scan_line = {"segments_per_head": G, "segmented_heads": seg_heads, "heads": H,
+                 "single_chain_ms": serial_ms, "single_chain_tokens_per_s": T / (serial_ms * 1e-3)}
+
     # the same 128k tokens served as 32 prompts packed end to end (kda_chunk_prefill_varlen):
     # seeded cut points, so lengths vary from a few tokens to several thousand
     Nv = 32
@@ -511,7 +536,8 @@ def main():
                     "hbm_frac_of_copy": pre_gbs / copy_gbs,
                     "model_tflops": pre_tflops, "mfma_frac": pre_tflops / MFMA_BF16_PEAK_TFLOPS,
                     "mfma_counters": measured_mfma(default_wl),
-                    "roofline_frac": max(pre_gbs / HBM_PEAK_GBS, pre_tflops / MFMA_BF16_PEAK_TFLOPS)},
+                    "roofline_frac": max(pre_gbs / HBM_PEAK_GBS, pre_tflops / MFMA_BF16_PEAK_TFLOPS),
+                    "scan": scan_line},
         "prefill_varlen": {"N": Nv, "T_total": T, "len_min": min(lens), "len_max": max(lens), "ms": varlen_ms,
                            "tokens_per_s": T / (varlen_ms * 1e-3),
                            "algorithmic_GBps": PREFILL_BYTES_PER_TH * th / (varlen_ms * 1e-3) / 1e9,
