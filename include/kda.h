@@ -149,7 +149,8 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v,
  * are the chunk-end states kda_chunk_prefill_backward takes instead of running the
  * forward again (the state recurrence of the Kimi Linear summary page, read at chunk
  * boundaries).  Arguments, results, supported sizes and the workspace are those of
- * kda_chunk_prefill (kda_chunk_prefill_workspace_size), plus:
+ * kda_chunk_prefill (kda_chunk_prefill_workspace_size), with each (b, h) scanned as one
+ * chain (as with KDA_FLAG_SERIAL_SCAN), plus:
  *
  *   chunk_states [M,H,dk,dv] fp32, written, or NULL (then the call is kda_chunk_prefill):
  *                            row b's state after its first j * state_interval tokens,
@@ -213,7 +214,9 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  * output crosses a boundary (dev.to prefix-invariance page: the output at a
  * position depends on its own prefix and nothing else).  Each sequence's
  * chunks start at its first token, so its results equal those of
- * kda_chunk_prefill on that sequence alone with the same chunk, bit for bit.
+ * kda_chunk_prefill on that sequence alone with the same chunk, bit for bit, when that
+ * call scans it as one chain (always with KDA_FLAG_SERIAL_SCAN; see the segmented scan
+ * of kda_chunk_prefill).  The packed call never segments its scan.
  *
  *   q, k        [T,H,dk]     dtype (T = total tokens)
  *   v           [T,H,dv]     dtype
