@@ -830,6 +830,9 @@ prep_kernel(PrepParams p) {
 // step from L2, and a wave that issues a burst of loads waits for room in the load
 // queue), with an L2 warm-up two chunks ahead.  Each step has two barriers, which all
 // eight waves join: one when U is in LDS, one when the next state and V^T are.
+// With a segment plan (ScanParams::plan) the same kernel runs a chain per (b, h, segment):
+// pass 1 the boundary tails from a zero state with the output sent to the sink, pass 2
+// the segments from their entry states, pass 0 the heads the plan left to one chain.
 template <int K, int C, bool SPLIT>
 struct ChainOps {
   static constexpr int KS = K / 32, CS = C / 32, SPW = (K / 16 + 3) / 4;
