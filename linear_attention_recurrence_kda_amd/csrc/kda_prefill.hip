@@ -359,20 +359,21 @@ prep_kernel(PrepParams p) {
       lc = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bool cin = 32 * ks + cg < dk;
+        // channels past dk exist only in the 32-channel tile of dk = 16
+        const bool cin = (K > 32) || (32 * ks + cg < dk);
         float laf[8];
         la_r[ks].to_float(laf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = cin ? laf[e] * kLog2e : 0.f;
-          lm = fmaxf(lm, cin ? x : -INFINITY);
-          lc += x;
+          lm = fmaxf(lm, cin ? laf[e] : -INFINITY);
+          lc += cin ? laf[e] : 0.f;
         }
       }
       lm = fmaxf(lm, __shfl_xor(lm, 16, 64));
       lm = fmaxf(lm, __shfl_xor(lm, 32, 64));
       lc += __shfl_xor(lc, 16, 64);
       lc += __shfl_xor(lc, 32, 64);
+      lm *= kLog2e;
     }
     const float kk = ksc * ksc * sk;
     float f = fabsf(1.f - beta_r * kk);
