@@ -265,3 +265,29 @@ def test_segmented_sweep(oracle, case):
     ro, rs = oracle.c_prefill(q=inp["q"], k=inp["k"], v=inp["v"], log_alpha=ref_la, beta=inp["beta"], mask=mask,
                               init_state=s0, l2norm_qk=c["l2"])
     _check_all("sweep", o, s, ro, rs)
+
+
+@pytest.mark.parametrize("B,H,dk", [(1, 40, 128), (7, 9, 128), (2, 3, 16)])
+def test_segmented_chain_counts(oracle, B, H, dk):
+    """Between 33 and 63 (b, h) pairs the call still segments (G = 2: 80 and 126 chains, not
+    multiples of the eight chains an XCD group takes), and a 16-channel key runs inside the
+    32-channel kernels; sampled (b, h) pairs against the oracle over every position."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    T = 8192 + 77
+    say(f"[case] segmented chain counts B={B} H={H} dk={dk} T={T}")
+    x = D.torch_kda_inputs(B, T, H, dk, DV, dev, "bf16", seed=59)
+    need = kda.prefill_workspace_size(B, T, H, dk, DV, 64, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    o, s = kda.chunk_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], chunk_size=64, workspace=ws)
+    torch.cuda.synchronize()
+    G = _segments(B * H, (T + 63) // 64)
+    assert G == 2 if B * H < 64 else G == 1
+    plan = ws[need - B * H * G * 4:need].view(torch.int32).cpu().numpy().reshape(B * H, G)
+    assert np.all(plan[:, 0] == 1), plan[:, 0]
+    picks = sorted({(0, 0), (B - 1, H - 1), (B // 2, H // 2)})
+    for b, h in picks:
+        one = {n: host(t[b:b + 1, :, h:h + 1]) for n, t in x.items()}
+        ro, rs = oracle.c_prefill(**one)
+        _check_all(f"b{b}h{h}", o[b:b + 1, :, h:h + 1], s[b:b + 1, h:h + 1], ro, rs)
