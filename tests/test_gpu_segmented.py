@@ -291,3 +291,30 @@ def test_segmented_chain_counts(oracle, B, H, dk):
         one = {n: host(t[b:b + 1, :, h:h + 1]) for n, t in x.items()}
         ro, rs = oracle.c_prefill(**one)
         _check_all(f"b{b}h{h}", o[b:b + 1, :, h:h + 1], s[b:b + 1, h:h + 1], ro, rs)
+
+
+def test_segmented_headline_128k(oracle):
+    """The benchmarked call itself: B=1, H=32, T=131072, dk=dv=128, bf16, chunk 64, zero
+    state, in the launch configuration bench.py times (two segments per head, 64 chains of
+    32-column tiles); three heads against the oracle over every position and the final
+    state, and every head segmented."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    B, T, H = 1, 131072, 32
+    say("[case] segmented headline 1x131072x32, sampled heads")
+    x = D.torch_kda_inputs(B, T, H, DK, DV, dev, "bf16", seed=0)
+    need = kda.prefill_workspace_size(B, T, H, DK, DV, 64, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    o, s = kda.chunk_prefill(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], chunk_size=64, workspace=ws)
+    torch.cuda.synchronize()
+    G = _segments(B * H, T // 64)
+    assert G == 2
+    plan = ws[need - H * G * 4:need].view(torch.int32).cpu().numpy().reshape(H, G)
+    assert np.all(plan[:, 0] == 1), plan[:, 0]
+    say(f"[plan] tails start at chunks {sorted(set(plan[:, 1].tolist()))} (boundary 1024)")
+    heads = [0, 13, 31]
+    one = {n: host(t[:, :, heads]) for n, t in x.items()}
+    ro, rs = oracle.c_prefill(**one)
+    for i, h in enumerate(heads):
+        _check_all(f"128k h{h}", o[:, :, h], s[:, h], ro[:, :, i], rs[:, i])
