@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 ...; busy % = busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)),
 # reported only while the kernel sources hash to what was profiled.
 MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "781111c40d521698",
-                 "prep_busy_pct": 8.0, "scan_busy_pct": 24.2, "call_busy_pct": 16.0, "issued_flop_per_call": 1.441e12}
+                 "prep_busy_pct": 8.1, "scan_busy_pct": 25.2, "call_busy_pct": 16.4, "issued_flop_per_call": 1.441e12}
 
 
 def measured_mfma(default_workload):

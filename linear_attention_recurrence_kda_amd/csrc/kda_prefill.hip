@@ -1725,21 +1725,17 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
                          (const uint16_t*)a.workspace, NC, G, sp.seg_nc, const_cast<int32_t*>(sp.plan));
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      // pass 1 in 16-column tiles (its tails are short, and half its chains only copy a
-      // state: more workgroups spread them over the chip), pass 2 in 32-column tiles
       ScanParams sw = sp;
       sw.nbh = (int)chains;
-      const int wgroups = ((int)chains + 7) / 8;
-      sw.pass = 1;
-      sw.NT = a.dv / kVT;
-      hipLaunchKernelGGL((scan_kernel<DT, K, V, C, kVT>), dim3(wgroups * 8 * sw.NT), dim3(kScanThreads), 0, st, sw);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      sw.pass = 2;
       sw.NT = a.dv / (2 * kVT);
-      hipLaunchKernelGGL((scan_kernel<DT, K, V, C, 2 * kVT>), dim3(wgroups * 8 * sw.NT), dim3(kScanThreads), 0, st, sw);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
+      const int wgroups = ((int)chains + 7) / 8;
+      for (int pass = 1; pass <= 2; ++pass) {
+        sw.pass = pass;
+        hipLaunchKernelGGL((scan_kernel<DT, K, V, C, 2 * kVT>), dim3(wgroups * 8 * sw.NT), dim3(kScanThreads), 0,
+                           st, sw);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
       sp.pass = 0;                                   // then the heads left to a single chain
       sp.NT = a.dv / kVT;
       hipLaunchKernelGGL((scan_kernel<DT, K, V, C, kVT>), dim3((nbh + 7) / 8 * 8 * sp.NT), dim3(kScanThreads), 0,
