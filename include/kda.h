@@ -74,8 +74,8 @@ enum {
    * per-channel call fed the broadcast gate by rounding; with fp32 inputs, and in the decode
    * steps, they are the same bit for bit. */
   KDA_FLAG_SCALAR_GATE = 4u,
-  /* prefill: scan each (b, h) as one chain of chunks, never in segments (see
-   * kda_chunk_prefill); the packed, state-saving and backward calls always do */
+  /* prefill: scan each (b, h) or packed sequence as one chain of chunks, never in
+   * segments (see kda_chunk_prefill); calls that save states, and the backward, always do */
   KDA_FLAG_SERIAL_SCAN = 8u
 };
 
@@ -133,7 +133,7 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * it is scanned as one chain, so every input gets a result within rounding of the token
  * recurrence; the segmented one differs from the single chain's by rounding only.  The
  * call stays asynchronous (the choice is made on the device).  KDA_FLAG_SERIAL_SCAN turns
- * it off, e.g. to get results equal bit for bit to the packed and state-saving calls.
+ * it off, e.g. to get results equal bit for bit to the state-saving calls.
  * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
  * bytes of device memory (may be NULL when that size is 0).
  */
@@ -213,10 +213,12 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  * the recurrence above from init_state[i] over those tokens only: no state or
  * output crosses a boundary (dev.to prefix-invariance page: the output at a
  * position depends on its own prefix and nothing else).  Each sequence's
- * chunks start at its first token, so its results equal those of
- * kda_chunk_prefill on that sequence alone with the same chunk, bit for bit, when that
- * call scans it as one chain (always with KDA_FLAG_SERIAL_SCAN; see the segmented scan
- * of kda_chunk_prefill).  The packed call never segments its scan.
+ * chunks start at its first token, and a long sequence is cut into segments exactly as
+ * kda_chunk_prefill would cut it run alone (the same rule on its chunk count and H, the
+ * same plan from its own inputs; see the segmented scan of kda_chunk_prefill), so its
+ * results equal those of kda_chunk_prefill on that sequence alone with the same chunk and
+ * flags, bit for bit.  With checkpoints (state_interval > 0) or KDA_FLAG_SERIAL_SCAN every
+ * sequence is scanned as one chain, equal to its lone run with KDA_FLAG_SERIAL_SCAN.
  *
  *   q, k        [T,H,dk]     dtype (T = total tokens)
  *   v           [T,H,dv]     dtype

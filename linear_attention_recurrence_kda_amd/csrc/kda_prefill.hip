@@ -960,9 +960,30 @@ scan_kernel(ScanParams p) {
   const int xcd = L_id % 8, slot = L_id / 8;
   const int vbh = (slot / p.NT) * 8 + xcd, tile = slot % p.NT;
   if (vbh >= p.nbh) return;
-  // passes 1 and 2 of a segmented scan run one chain per (b, h, segment)
+  // passes 1 and 2 of a segmented scan run one chain per (b, h, segment): in the batch
+  // layout G per (b, h); packed, sequence b has seq[b].w segments (0: too short for any)
+  // and its (head, segment) jobs start at H * seq[b].z
   const bool seg_pass = p.plan != nullptr && p.pass != 0;
-  const int bh = seg_pass ? vbh / p.G : vbh, seg = seg_pass ? vbh % p.G : 0;
+  int bh = vbh, seg = 0, Gb = p.G;
+  if (seg_pass) {
+    if (p.seq == nullptr) {
+      bh = vbh / p.G;
+      seg = vbh % p.G;
+    } else {
+      int lo = 0, hi = p.B - 1;                      // the last sequence whose jobs start at or before vbh
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((long long)p.seq[mid].z * p.H <= vbh) lo = mid;
+        else hi = mid - 1;
+      }
+      const int4 sq = p.seq[lo];
+      if ((long long)(sq.z + sq.w) * p.H <= vbh) return;   // past the last job
+      Gb = sq.w;
+      const int r = vbh - sq.z * p.H;
+      bh = lo * p.H + r / Gb;
+      seg = r % Gb;
+    }
+  }
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = tile * TW;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -999,31 +1020,38 @@ scan_kernel(ScanParams p) {
   const float* init_ptr = (p.init_state != nullptr && sbh >= 0) ? p.init_state + (size_t)sbh * mat : nullptr;
   float* fin_ptr = (p.final_state != nullptr && sbh >= 0) ? p.final_state + (size_t)sbh * mat : nullptr;
   bool outputs = true;
-  if (p.plan != nullptr) {
-    // segmented scan: this chain's chunks [c0, c1), where its state comes from and goes to
-    const int32_t* pl = p.plan + (size_t)bh * p.G;
+  // a packed sequence too short for segments has no plan (pass 0 runs it)
+  if (p.plan != nullptr && p.seq != nullptr && !seg_pass) Gb = p.seq[b].w;
+  if (p.plan != nullptr && Gb > 0) {
+    // segmented scan: this chain's chunks [c0, c1), where its state comes from and goes to;
+    // the (b, h)'s plan and entry states start at pbase
+    const size_t pbase = p.seq == nullptr ? (size_t)bh * Gb : ((size_t)p.seq[b].z * p.H + (size_t)h * Gb);
+    const int32_t* pl = p.plan + pbase;
     const bool seg_ok = pl[0] != 0;
     if (seg_ok != seg_pass) return;                  // pass 0 takes the heads passes 1, 2 leave
-    int c0 = 0, c1 = p.NC;
-    float* st = p.seg_states + ((size_t)bh * p.G + seg) * mat;
+    const int seg_nc = (NCs + Gb - 1) / Gb;
+    int c0 = 0, c1 = NCs;
+    float* st = p.seg_states + (pbase + seg) * mat;
     if (p.pass == 1) {
       // segment 0: the initial state copied (no chunk), so that pass 2 may write the final
       // state over it; segment g: boundary g's tail from zero, its end state kept, no output
-      c1 = seg == 0 ? 0 : seg * p.seg_nc;
+      c1 = seg == 0 ? 0 : seg * seg_nc;
       c0 = seg == 0 ? 0 : min(max(pl[seg], 0), c1);
       if (seg > 0) init_ptr = nullptr;
       fin_ptr = st;
       outputs = false;
     } else if (p.pass == 2) {
-      c0 = seg * p.seg_nc;
-      c1 = min(c0 + p.seg_nc, p.NC);
+      c0 = seg * seg_nc;
+      c1 = min(c0 + seg_nc, NCs);
       init_ptr = st;
-      if (seg + 1 < p.G) fin_ptr = nullptr;
+      if (seg + 1 < Gb) fin_ptr = nullptr;
     }
     seq_tok0 += (size_t)c0 * p.chunk;
     ws_chunk0 += (size_t)c0;
-    seq_T = min(p.T - c0 * p.chunk, (c1 - c0) * p.chunk);
+    seq_T = min(seq_T - c0 * p.chunk, (c1 - c0) * p.chunk);
     NCs = c1 - c0;
+  } else if (seg_pass) {
+    return;
   }
   const uint16_t* wsh = p.ws + ws_chunk0 * L::kElems;
   const int last = NCs - 1;
@@ -1504,17 +1532,33 @@ scan_kernel(ScanParams p) {
 // is segmented only if every boundary has such a tail; the others run as one chain, as
 // without a plan.
 constexpr float kForgetLog2 = -160.f;
+constexpr int kMinSegChunks = 64;                   // chunks per segment, at least
 constexpr int kPlanThreads = 64;                    // boundaries per (b, h): G - 1 <= 63
 
+// Packed sequences (seq, first given): one workgroup per (sequence, head); a sequence with
+// seq[b].w = G segments has its boundaries in its own chunks (head h's run of the packed
+// workspace) and its plan at H seq[b].z + h G.
 template <int K, int V, int C, bool SPLIT>
 __global__ void __launch_bounds__(kPlanThreads)
-seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int32_t* __restrict__ plan) {
+seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int32_t* __restrict__ plan,
+                int H, const int4* __restrict__ seq, const int32_t* __restrict__ first) {
   using L = WsLayout<K, V, C, SPLIT>;
-  const int bh = blockIdx.x, g = threadIdx.x + 1;
+  const int g = threadIdx.x + 1;
+  size_t chunk0 = (size_t)blockIdx.x * NC, pbase = (size_t)blockIdx.x * G;
+  if (seq != nullptr) {
+    const int b = blockIdx.x / H, h = blockIdx.x % H;
+    const int4 sq = seq[b];
+    G = sq.w;
+    if (G == 0) return;                              // too short for segments
+    const int ncb = first[b + 1] - first[b];
+    seg_nc = (ncb + G - 1) / G;
+    chunk0 = (size_t)h * NC + first[b];
+    pbase = (size_t)sq.z * H + (size_t)h * G;
+  }
   int start = -1;
   if (g < G) {
     const int end = g * seg_nc, lo = end - seg_nc;
-    const uint16_t* base = ws + (size_t)bh * NC * L::kElems + L::off_valid + 4;
+    const uint16_t* base = ws + chunk0 * L::kElems + L::off_valid + 4;
     float acc = 0.f;
     for (int j0 = end - 1; j0 >= lo && start < 0; j0 -= 8) {
       float bnd[8];                                  // eight loads in flight, then the walk
@@ -1531,8 +1575,8 @@ seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int3
     }
   }
   const bool ok = __syncthreads_and(g >= G || start >= 0);
-  if (g < G) plan[(size_t)bh * G + g] = start;
-  if (threadIdx.x == 0) plan[(size_t)bh * G] = ok ? 1 : 0;
+  if (g < G) plan[pbase + g] = start;
+  if (threadIdx.x == 0) plan[pbase] = ok ? 1 : 0;
 }
 
 // ================================================================ packed sequences
@@ -1546,9 +1590,13 @@ seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int3
 constexpr int kSetupThreads = 1024;
 __global__ void __launch_bounds__(kSetupThreads)
 varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCmax, int interval,
-                    int2* __restrict__ span, int4* __restrict__ seq, int32_t* __restrict__ first) {
+                    int2* __restrict__ span, int4* __restrict__ seq, int32_t* __restrict__ first, int seg_H) {
   // chunk counts in the low 32 bits, checkpoint counts in the high ones: both totals stay
-  // below 2^31, so one 64-bit scan carries the two
+  // below 2^31, so one 64-bit scan carries the two.  With seg_H > 0 (a segmented scan, which
+  // saves no checkpoints) the high half counts each sequence's segments instead, by the rule
+  // a lone run of the sequence with seg_H heads follows (0 for a sequence too short to cut):
+  // seq[i].z is then the first (head, segment) job of the sequence over H and seq[i].w its
+  // segment count.
   __shared__ long long s_scan[kSetupThreads];
   __shared__ long long s_carry;
   const int tid = threadIdx.x;
@@ -1562,6 +1610,11 @@ varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCm
       end = min(max(cu[i + 1], start), T);
       nc = (end - start + C - 1) / C;
       ck = interval > 0 ? (end - start) / interval : 0;
+      if (seg_H > 0) {
+        int G = 1;
+        while (seg_H * G < 64 && nc / (2 * G) >= kMinSegChunks) G *= 2;
+        ck = G > 1 ? G : 0;
+      }
     }
     const long long mine = ((long long)ck << 32) | (unsigned)nc;
     s_scan[tid] = mine;
@@ -1574,7 +1627,7 @@ varlen_setup_kernel(const int32_t* __restrict__ cu, int N, int T, int C, int NCm
     }
     const long long before = s_carry + s_scan[tid] - mine;
     const int excl = min((int)(before & 0xffffffffll), NCmax);
-    if (i < N) seq[i] = make_int4(start, end, (int)(before >> 32), 0);
+    if (i < N) seq[i] = make_int4(start, end, (int)(before >> 32), seg_H > 0 ? ck : 0);
     if (i <= N) first[i] = excl;
     for (int j = 0; j < nc && excl + j < NCmax; ++j) span[excl + j] = make_int2(start + j * C, end);
     __syncthreads();
@@ -1641,13 +1694,20 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // tiles (bf16, dv = 128) would not otherwise fill the chip, i.e. with fewer than 64 (b, h)
 // pairs: segments double until there are 64 chains, each of at least kMinSegChunks chunks
 // (the tails that precede the boundaries stay a small fraction of the work).
-constexpr int kMinSegChunks = 64;
 static int seg_count(int nbh, long long NC, int dv, int dtype) {
   if (dtype != 0 || dv != 128 || nbh <= 0) return 1;
   int G = 1;
   while ((long long)nbh * G < 64 && NC / (2LL * G) >= kMinSegChunks) G *= 2;
   return G;
 }
+
+// Packed sequences are segmented one by one, each as a lone run of it would be (so a packed
+// sequence still equals that run bit for bit): possible with fewer than 64 heads once some
+// sequence can hold 128 chunks.
+static bool varlen_may_segment(int H, long long NC, int dv, int dtype) {
+  return dtype == 0 && dv == 128 && H > 0 && H < 64 && NC >= 2 * kMinSegChunks;
+}
+static size_t varlen_jobs(int H, long long NC) { return (size_t)H * (size_t)(NC / kMinSegChunks); }
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen) {
   if (B == 0 || H == 0 || (T == 0 && !varlen)) return 0;
@@ -1661,9 +1721,14 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, i
     const size_t chains = (size_t)B * H * G;
     return align256(base) + chains * dk * dv * 4 + chains * 4;
   }
-  // packed: H x NC chunks, the sink, then the chunk table (span, seq, first)
-  return (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + (size_t)B * 16 +
-         align16((size_t)(B + 1) * 4);
+  // packed: H x NC chunks, the sink, then the chunk table (span, seq, first); a segmented
+  // scan then adds entry states and plan entries for at most H * (NC / 64) (head, segment)
+  // jobs (a sequence of n chunks has at most n / 64 segments)
+  const size_t base = (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + (size_t)B * 16 +
+                      align16((size_t)(B + 1) * 4);
+  if (!varlen_may_segment(H, NC, dv, dtype)) return base;
+  const size_t jobs = varlen_jobs(H, NC);
+  return align256(base) + jobs * dk * dv * 4 + jobs * 4;
 }
 
 template <int DT, int K, int V, int C>
@@ -1688,16 +1753,20 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     span = reinterpret_cast<int2*>(tail);
     seq = reinterpret_cast<int4*>(tail + align16((size_t)NC * 8));
     first = reinterpret_cast<int32_t*>(tail + align16((size_t)NC * 8) + (size_t)a.B * 16);
+  }
+  // segments per (b, h) of a segmented scan (1: one chain each); packed sequences are
+  // segmented one by one on the device (vseg), never when checkpoints are saved
+  const int G = (!kWideOk || varlen || ckpt || a.serial_scan) ? 1 : seg_count(nbh, NC, a.dv, DT);
+  const bool vseg = kWideOk && varlen && !ckpt && !a.serial_scan && varlen_may_segment(a.H, NC, a.dv, DT);
+  if (varlen) {
     hipLaunchKernelGGL(varlen_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.cu_seqlens, a.B, a.T,
-                       a.chunk, NC, ckpt ? a.state_interval : 0, span, seq, first);
+                       a.chunk, NC, ckpt ? a.state_interval : 0, span, seq, first, vseg ? a.H : 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // segments per (b, h) of a segmented scan (1: one chain each)
-  const int G = (!kWideOk || varlen || ckpt || a.serial_scan) ? 1 : seg_count(nbh, NC, a.dv, DT);
   if (NC > 0) {
     PrepParams pp{a.q, a.k, a.v, a.log_alpha, a.beta, a.mask, (uint16_t*)a.workspace, span,
-                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate, G > 1 ? 1 : 0};
+                  a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, a.l2norm, a.scalar_gate, (G > 1 || vseg) ? 1 : 0};
     const dim3 pgrid(NC * a.H, varlen ? 1 : a.B);
     if (DT == 0 && a.scalar_gate)
       hipLaunchKernelGGL((prep_kernel<DT, K, V, C, DT == 0>), pgrid, dim3(kPrepThreads), 0, st, pp);
@@ -1713,16 +1782,22 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
                 nullptr, nullptr, 1, NC, 0};
   if constexpr (kWideOk) {
     // segmented scan: plan, then the tails (pass 1) and the segments (pass 2) as chains of
-    // 32-column tiles, then the heads without a plan as single chains (pass 0)
-    if (G > 1) {
-      const size_t chains = (size_t)nbh * G;
-      unsigned char* tail = (unsigned char*)a.workspace + align256(chunks_bytes + kSinkBytes);
+    // 32-column tiles, then (below, pass 0) the heads without a plan as single chains
+    if (G > 1 || vseg) {
+      // chains of passes 1 and 2: every (b, h, segment), or packed an upper bound on the
+      // (sequence, head, segment) jobs, past which workgroups exit
+      const size_t chains = vseg ? varlen_jobs(a.H, NC) : (size_t)nbh * G;
+      const size_t base = vseg ? chunks_bytes + kSinkBytes + align16((size_t)NC * 8) + (size_t)a.B * 16 +
+                                     align16((size_t)(a.B + 1) * 4)
+                               : chunks_bytes + kSinkBytes;
+      unsigned char* tail = (unsigned char*)a.workspace + align256(base);
       sp.seg_states = reinterpret_cast<float*>(tail);
       sp.plan = reinterpret_cast<const int32_t*>(tail + chains * a.dk * a.dv * 4);
-      sp.G = G;
-      sp.seg_nc = (NC + G - 1) / G;
+      sp.G = vseg ? 0 : G;
+      sp.seg_nc = vseg ? 0 : (NC + G - 1) / G;
       hipLaunchKernelGGL((seg_plan_kernel<K, V, C, DT == 1>), dim3(nbh), dim3(kPlanThreads), 0, st,
-                         (const uint16_t*)a.workspace, NC, G, sp.seg_nc, const_cast<int32_t*>(sp.plan));
+                         (const uint16_t*)a.workspace, NC, sp.G, sp.seg_nc, const_cast<int32_t*>(sp.plan), a.H,
+                         vseg ? seq : nullptr, vseg ? first : nullptr);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       ScanParams sw = sp;
@@ -1736,11 +1811,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
       }
-      sp.pass = 0;                                   // then the heads left to a single chain
-      sp.NT = a.dv / kVT;
-      hipLaunchKernelGGL((scan_kernel<DT, K, V, C, kVT>), dim3((nbh + 7) / 8 * 8 * sp.NT), dim3(kScanThreads), 0,
-                         st, sp);
-      return hipGetLastError();
+      sp.pass = 0;
     }
   }
   const int groups = (nbh + 7) / 8;

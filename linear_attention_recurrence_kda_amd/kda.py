@@ -340,7 +340,7 @@ def num_checkpoints(cu_seqlens, state_interval) -> int:
 
 def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=None, chunk_size=64,
                          l2norm_qk=False, out=None, final_state=None, workspace=None, scalar_gate=False,
-                         state_interval=0, chunk_states=None, slot=None):
+                         state_interval=0, chunk_states=None, slot=None, serial_scan=False):
     """KDA prefill of N sequences packed end to end.  q,k [T,H,dk], v [T,H,dv] (bf16 or fp32),
     log_alpha [T,H,dk] fp32 ([T,H] with scalar_gate), beta [T,H] fp32, cu_seqlens [N+1] int32
     on the GPU (sequence i = tokens cu_seqlens[i] .. cu_seqlens[i+1]-1), initial_state
@@ -350,7 +350,8 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
     sequence by sequence in order; chunk_states is allocated when not given (M from
     cu_seqlens, copied to the host).  With slot ([N] int32 on the GPU), initial_state and
     final_state are a pool [S,H,dk,dv] (pass the same tensor to update it in place) and
-    sequence i uses entry slot[i]; final_state must then be given."""
+    sequence i uses entry slot[i]; final_state must then be given.  serial_scan:
+    KDA_FLAG_SERIAL_SCAN (every sequence scanned as one chain, never in segments)."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -402,7 +403,8 @@ def chunk_prefill_varlen(q, k, v, log_alpha, beta, cu_seqlens, initial_state=Non
                                       int(state_interval),
                                       N, T, H, dk, dv, int(chunk_size), dt,
                                       (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) |
-                                      (KDA_FLAG_SCALAR_GATE if scalar_gate else 0),
+                                      (KDA_FLAG_SCALAR_GATE if scalar_gate else 0) |
+                                      (KDA_FLAG_SERIAL_SCAN if serial_scan else 0),
                                       _ptr(workspace), wbytes, _stream())
     _check("kda_chunk_prefill_varlen", st)
     if state_interval:

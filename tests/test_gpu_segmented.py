@@ -318,3 +318,104 @@ def test_segmented_headline_128k(oracle):
     ro, rs = oracle.c_prefill(**one)
     for i, h in enumerate(heads):
         _check_all(f"128k h{h}", o[:, :, h], s[:, h], ro[:, :, i], rs[:, i])
+
+
+# ---------------------------------------------------------------- packed sequences
+def _packed(lengths, H, dk, seed, decay="default"):
+    T = int(sum(lengths))
+    inp = {n: np.ascontiguousarray(x[0]) for n, x in D.np_kda_inputs(1, T, H, dk, DV, "bf16", seed=seed,
+                                                                        decay=decay).items()}
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return inp, cu
+
+
+def _dev_packed(inp, dev):
+    return {n: to_dev(x, "bf16" if n in "qkv" else None, dev) for n, x in inp.items()}
+
+
+@pytest.mark.parametrize("H", [2, 40])
+def test_varlen_segments_like_lone_runs(oracle, H):
+    """Packed sequences are segmented one by one, each as its lone kda_chunk_prefill run is
+    (per-sequence rule on the chunk count and the head count): long ones (9000 and 8256
+    tokens) among short and empty ones, with initial states, equal their lone runs bit for
+    bit, whatever the number of packed sequences; the long ones against the oracle too."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    lengths = [9000, 300, 0, 8256, 17, 1]
+    N = len(lengths)
+    say(f"[case] varlen segmented H={H} lengths={lengths}")
+    inp, cu = _packed(lengths, H, DK, seed=61)
+    d = _dev_packed(inp, dev)
+    s0 = to_dev(D.np_state(N, H, DK, DV, 0.1, seed=61), dev=dev)
+    o, sN = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], to_dev(cu, dev=dev),
+                                     initial_state=s0, chunk_size=64)
+    torch.cuda.synchronize()
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        oi, si = kda.chunk_prefill(*(d[n][a:b].unsqueeze(0).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
+                                   initial_state=s0[i:i + 1].contiguous(), chunk_size=64)
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:b], oi[0]), f"o of sequence {i} (length {b - a}) differs from its lone run"
+        assert torch.equal(sN[i], si[0]), f"state of sequence {i} differs from its lone run"
+    heads = [0, H - 1]
+    for i in (0, 3):
+        a, b = int(cu[i]), int(cu[i + 1])
+        one = {n: x[a:b][None][:, :, heads] for n, x in inp.items()}
+        ro, rs = oracle.c_prefill(**one, init_state=host(s0[i:i + 1, heads]))
+        _check_all(f"seq{i}", o[a:b][None][:, :, heads], sN[i:i + 1, heads], ro, rs)
+
+
+def test_varlen_segmented_slots_checkpoints_serial():
+    """With state slots (the pool updated in place) the segmented packed call equals the
+    lone runs bit for bit; with checkpoints, or with KDA_FLAG_SERIAL_SCAN, it scans each
+    sequence as one chain and equals the single-chain lone runs bit for bit; a sequence with
+    slow gates falls back to one chain."""
+    import torch
+    from linear_attention_recurrence_kda_amd import kda
+    dev = device()
+    H = 2
+    lengths = [8192 + 40, 500, 8192 + 64]
+    N = len(lengths)
+    say(f"[case] varlen segmented slots/checkpoints/serial lengths={lengths}")
+    inp, cu = _packed(lengths, H, DK, seed=62)
+    inp["log_alpha"][int(cu[2]):int(cu[3])] *= 1e-3          # sequence 2: slow gates
+    d = _dev_packed(inp, dev)
+    cu_d = to_dev(cu, dev=dev)
+    s0 = to_dev(D.np_state(N, H, DK, DV, 0.1, seed=62), dev=dev)
+    lone, lone_serial, flags = [], [], []
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        args = [d[n][a:b].unsqueeze(0).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+        need = kda.prefill_workspace_size(1, b - a, H, DK, DV, 64, 0)
+        ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        lone.append(kda.chunk_prefill(*args, initial_state=s0[i:i + 1].contiguous(), chunk_size=64, workspace=ws))
+        lone_serial.append(kda.chunk_prefill(*args, initial_state=s0[i:i + 1].contiguous(), chunk_size=64,
+                                             serial_scan=True))
+        G = _segments(H, (b - a + 63) // 64)
+        flags.append(ws[need - H * G * 4:need].view(torch.int32).cpu().numpy().reshape(H, G)[:, 0].tolist()
+                     if G > 1 else None)
+    torch.cuda.synchronize()
+    assert flags == [[1, 1], None, [0, 0]], flags      # 0 segmented, 1 too short, 2 slow gates
+    assert torch.equal(lone[2][0], lone_serial[2][0]) and torch.equal(lone[2][1], lone_serial[2][1])
+    # slots: sequence i in slot 3 - i of a pool of 4, updated in place
+    pool = torch.zeros(4, H, DK, DV, dtype=torch.float32, device=dev)
+    for i in range(N):
+        pool[3 - i] = s0[i]
+    slot = torch.tensor([3 - i for i in range(N)], dtype=torch.int32, device=dev)
+    o, _ = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], cu_d, initial_state=pool,
+                                    final_state=pool, slot=slot, chunk_size=64)
+    torch.cuda.synchronize()
+    for i in range(N):
+        a, b = int(cu[i]), int(cu[i + 1])
+        assert torch.equal(o[a:b], lone[i][0][0]) and torch.equal(pool[3 - i], lone[i][1][0]), f"slots: sequence {i}"
+    # checkpoints and the serial flag: single chains
+    for kw in (dict(state_interval=64), dict(serial_scan=True)):
+        res = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], cu_d, initial_state=s0,
+                                       chunk_size=64, **kw)
+        torch.cuda.synchronize()
+        o, sN = res[0], res[1]
+        for i in range(N):
+            a, b = int(cu[i]), int(cu[i + 1])
+            assert torch.equal(o[a:b], lone_serial[i][0][0]) and torch.equal(sN[i], lone_serial[i][1][0]), \
+                f"{kw}: sequence {i}"
