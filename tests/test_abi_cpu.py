@@ -457,3 +457,23 @@ def test_segmented_workspace_size(lib):
     assert size(1, 8192, 2, dv=64) == (lambda pc: 2 * 128 * pc + 16384)(size(1, 64, 1, dv=64) - 16384)
     fp = size(1, 8192, 2, dtype=1)                          # fp32: never segmented
     assert fp == 2 * 128 * (size(1, 64, 1, dtype=1) - 16384) + 16384
+
+
+def test_segmented_varlen_workspace_size(lib):
+    """The packed prefill reserves, for sequences it may segment (bf16, dv = 128, fewer than 64
+    heads, at least 128 chunks in the bound), one fp32 dk x dv entry state and one int for
+    each of at most H * (chunks / 64) (sequence, head, segment) jobs after its chunk table."""
+    def size(N, T, H, dk=128, dv=128, dtype=0):
+        return lib.kda_chunk_prefill_varlen_workspace_size(N, T, H, dk, dv, 64, dtype)
+    def a16(x):
+        return (x + 15) // 16 * 16
+    per_chunk = lib.kda_chunk_prefill_workspace_size(1, 64, 1, 128, 128, 64, 0) - 16384
+    def base(N, T, H):
+        nc = (T + 63) // 64 + N
+        return H * nc * per_chunk + 16384 + a16(nc * 8) + N * 16 + a16((N + 1) * 4)
+    for N, T, H in ((3, 8000, 2), (6, 17766, 2), (32, 131072, 32)):
+        nc = (T + 63) // 64 + N
+        want = (base(N, T, H) + 255) // 256 * 256 + H * (nc // 64) * (128 * 128 * 4 + 4)
+        assert nc >= 128 and size(N, T, H) == want, (N, T, H)
+    assert size(2, 8000, 64) == base(2, 8000, 64)          # 64 heads: never segmented
+    assert size(2, 64 * 100, 2) == base(2, 64 * 100, 2)    # 102 chunks: too short
