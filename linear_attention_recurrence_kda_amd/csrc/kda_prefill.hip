@@ -115,8 +115,9 @@ struct ScanParams {
   // Segmented scan (batch layout): each (b, h) cut into G segments of seg_nc chunks.
   // plan[(b H + h) G + g]: g = 0 the head's flag (1: every boundary has a forgetting tail),
   // g >= 1 the first chunk of boundary g's tail.  seg_states [B H][G][dk][dv]: segment g's
-  // entry state (g = 0: a copy of the initial state).  pass 1: the tails (and the copies),
-  // pass 2: the segments, pass 0: every head that is not segmented, as one chain.
+  // entry state (only g = 0 is used: a copy of the initial state).  pass 2: the segments,
+  // each from the start of its boundary's tail; pass 0: every head that is not segmented,
+  // as one chain.
   const int32_t* plan;
   float* seg_states;
   int G, seg_nc, pass;
@@ -832,8 +833,9 @@ prep_kernel(PrepParams p) {
 // queue), with an L2 warm-up two chunks ahead.  Each step has two barriers, which all
 // eight waves join: one when U is in LDS, one when the next state and V^T are.
 // With a segment plan (ScanParams::plan) the same kernel runs a chain per (b, h, segment):
-// pass 1 the boundary tails from a zero state with the output sent to the sink, pass 2
-// the segments from their entry states, pass 0 the heads the plan left to one chain.
+// pass 2 a segment from a zero state at the start of its boundary's tail, with the output
+// of the tail's chunks sent to the sink (segment 0 from the initial state), pass 0 the
+// heads the plan left to one chain.
 template <int K, int C, bool SPLIT>
 struct ChainOps {
   static constexpr int KS = K / 32, CS = C / 32, SPW = (K / 16 + 3) / 4;
@@ -960,16 +962,20 @@ scan_kernel(ScanParams p) {
   const int xcd = L_id % 8, slot = L_id / 8;
   const int vbh = (slot / p.NT) * 8 + xcd, tile = slot % p.NT;
   if (vbh >= p.nbh) return;
+  const int pass = p.pass;
   // passes 1 and 2 of a segmented scan run one chain per (b, h, segment): in the batch
   // layout G per (b, h); packed, sequence b has seq[b].w segments (0: too short for any)
   // and its (head, segment) jobs start at H * seq[b].z
-  const bool seg_pass = p.plan != nullptr && p.pass != 0;
+  const bool seg_pass = p.plan != nullptr && pass != 0;
   int bh = vbh, seg = 0, Gb = p.G;
   if (seg_pass) {
     if (p.seq == nullptr) {
       bh = vbh / p.G;
       seg = vbh % p.G;
     } else {
+      // past the last job (the grid is an upper bound): leave after one load
+      const int4 sl = p.seq[p.B - 1];
+      if ((long long)(sl.z + sl.w) * p.H <= vbh) return;
       int lo = 0, hi = p.B - 1;                      // the last sequence whose jobs start at or before vbh
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -1019,37 +1025,31 @@ scan_kernel(ScanParams p) {
   const size_t mat = (size_t)dk * dv;
   const float* init_ptr = (p.init_state != nullptr && sbh >= 0) ? p.init_state + (size_t)sbh * mat : nullptr;
   float* fin_ptr = (p.final_state != nullptr && sbh >= 0) ? p.final_state + (size_t)sbh * mat : nullptr;
-  bool outputs = true;
+  int out0 = 0;                                      // the chain's first chunk with output
   // a packed sequence too short for segments has no plan (pass 0 runs it)
   if (p.plan != nullptr && p.seq != nullptr && !seg_pass) Gb = p.seq[b].w;
   if (p.plan != nullptr && Gb > 0) {
     // segmented scan: this chain's chunks [c0, c1), where its state comes from and goes to;
-    // the (b, h)'s plan and entry states start at pbase
+    // the (b, h)'s plan and segment-0 entry state (the initial state, copied by the plan
+    // kernel so that the last segment may write the final state over it) are at pbase
     const size_t pbase = p.seq == nullptr ? (size_t)bh * Gb : ((size_t)p.seq[b].z * p.H + (size_t)h * Gb);
     const int32_t* pl = p.plan + pbase;
     const bool seg_ok = pl[0] != 0;
-    if (seg_ok != seg_pass) return;                  // pass 0 takes the heads passes 1, 2 leave
-    const int seg_nc = (NCs + Gb - 1) / Gb;
-    int c0 = 0, c1 = NCs;
-    float* st = p.seg_states + (pbase + seg) * mat;
-    if (p.pass == 1) {
-      // segment 0: the initial state copied (no chunk), so that pass 2 may write the final
-      // state over it; segment g: boundary g's tail from zero, its end state kept, no output
-      c1 = seg == 0 ? 0 : seg * seg_nc;
-      c0 = seg == 0 ? 0 : min(max(pl[seg], 0), c1);
-      if (seg > 0) init_ptr = nullptr;
-      fin_ptr = st;
-      outputs = false;
-    } else if (p.pass == 2) {
-      c0 = seg * seg_nc;
-      c1 = min(c0 + seg_nc, NCs);
-      init_ptr = st;
+    if (seg_ok != seg_pass) return;                  // pass 0 takes the heads pass 2 leaves
+    if (seg_pass) {
+      // segment 0 from the initial state; segment g from a zero state at the first chunk of
+      // boundary g's tail, with output from the segment's first chunk on
+      const int seg_nc = (NCs + Gb - 1) / Gb;
+      const int s0 = seg * seg_nc, c1 = min(s0 + seg_nc, NCs);
+      const int c0 = seg == 0 ? 0 : min(max(pl[seg], 0), s0);
+      init_ptr = seg == 0 ? p.seg_states + pbase * mat : nullptr;
       if (seg + 1 < Gb) fin_ptr = nullptr;
+      out0 = s0 - c0;
+      seq_tok0 += (size_t)c0 * p.chunk;
+      ws_chunk0 += (size_t)c0;
+      seq_T = min(seq_T - c0 * p.chunk, (c1 - c0) * p.chunk);
+      NCs = c1 - c0;
     }
-    seq_tok0 += (size_t)c0 * p.chunk;
-    ws_chunk0 += (size_t)c0;
-    seq_T = min(seq_T - c0 * p.chunk, (c1 - c0) * p.chunk);
-    NCs = c1 - c0;
   } else if (seg_pass) {
     return;
   }
@@ -1177,7 +1177,7 @@ scan_kernel(ScanParams p) {
           for (int i = 0; i < kStores; ++i) {
             const int rr = 16 * I + 4 * (lane / 16) + i;
             Tv* dst = reinterpret_cast<Tv*>(ochunk + o_lane[i] + kVT * hf * (uint32_t)sizeof(Tv));
-            if (!outputs || (!full && !(rr < p.chunk && t0 + rr < seq_T)))
+            if (n < out0 || (!full && !(rr < p.chunk && t0 + rr < seq_T)))
               dst = sink + 64 * hf + 16 * i + (lane % 16);
             E::st(dst, 0, o4[hf][0][i] + o4[hf][1][i]);
           }
@@ -1533,7 +1533,7 @@ scan_kernel(ScanParams p) {
 // without a plan.
 constexpr float kForgetLog2 = -160.f;
 constexpr int kMinSegChunks = 64;                   // chunks per segment, at least
-constexpr int kPlanThreads = 64;                    // boundaries per (b, h): G - 1 <= 63
+constexpr int kPlanThreads = 256;                   // boundaries per (b, h): G - 1 <= 63
 
 // Packed sequences (seq, first given): one workgroup per (sequence, head); a sequence with
 // seq[b].w = G segments has its boundaries in its own chunks (head h's run of the packed
@@ -1541,12 +1541,14 @@ constexpr int kPlanThreads = 64;                    // boundaries per (b, h): G 
 template <int K, int V, int C, bool SPLIT>
 __global__ void __launch_bounds__(kPlanThreads)
 seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int32_t* __restrict__ plan,
-                int H, const int4* __restrict__ seq, const int32_t* __restrict__ first) {
+                int H, const int4* __restrict__ seq, const int32_t* __restrict__ first,
+                const float* __restrict__ init, const int32_t* __restrict__ slot, int S, int mat,
+                float* __restrict__ seg_states) {
   using L = WsLayout<K, V, C, SPLIT>;
   const int g = threadIdx.x + 1;
+  const int b = blockIdx.x / H, h = blockIdx.x % H;
   size_t chunk0 = (size_t)blockIdx.x * NC, pbase = (size_t)blockIdx.x * G;
   if (seq != nullptr) {
-    const int b = blockIdx.x / H, h = blockIdx.x % H;
     const int4 sq = seq[b];
     G = sq.w;
     if (G == 0) return;                              // too short for segments
@@ -1577,6 +1579,17 @@ seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int3
   const bool ok = __syncthreads_and(g >= G || start >= 0);
   if (g < G) plan[pbase + g] = start;
   if (threadIdx.x == 0) plan[pbase] = ok ? 1 : 0;
+  // a segmented (b, h): its initial state (the row, or its slot of a pool; zeros without
+  // one) copied to the segment-0 entry, so that the last segment may overwrite it in place
+  if (!ok) return;
+  int row = blockIdx.x;
+  if (slot != nullptr) {
+    const int sl = slot[b];
+    row = (sl >= 0 && sl < S) ? sl * H + h : -1;
+  }
+  const float* src = (init != nullptr && row >= 0) ? init + (size_t)row * mat : nullptr;   // 4-byte aligned
+  float* dst = seg_states + pbase * mat;
+  for (int i = threadIdx.x; i < mat; i += kPlanThreads) dst[i] = src != nullptr ? src[i] : 0.f;
 }
 
 // ================================================================ packed sequences
@@ -1701,13 +1714,21 @@ static int seg_count(int nbh, long long NC, int dv, int dtype) {
   return G;
 }
 
-// Packed sequences are segmented one by one, each as a lone run of it would be (so a packed
-// sequence still equals that run bit for bit): possible with fewer than 64 heads once some
-// sequence can hold 128 chunks.
-static bool varlen_may_segment(int H, long long NC, int dv, int dtype) {
-  return dtype == 0 && dv == 128 && H > 0 && H < 64 && NC >= 2 * kMinSegChunks;
+// Packed sequences are segmented one by one, each as a lone run of it would be (so such a
+// packed sequence equals that run bit for bit), when the call has fewer than 64 (sequence,
+// head) pairs, as the batch call needs fewer than 64 (b, h) pairs: with more the chip is
+// full of single chains already.  Possible once some sequence can hold 128 chunks.
+static bool varlen_may_segment(int N, int H, long long NC, int dv, int dtype) {
+  return dtype == 0 && dv == 128 && H > 0 && (long long)N * H < 64 && NC >= 2 * kMinSegChunks;
 }
-static size_t varlen_jobs(int H, long long NC) { return (size_t)H * (size_t)(NC / kMinSegChunks); }
+// at most H * (NC / 64) (head, segment) jobs (a sequence of n chunks has at most n / 64
+// segments), and at most N * H * Gmax (a sequence has at most Gmax segments with H heads)
+static size_t varlen_jobs(int N, int H, long long NC) {
+  long long gmax = 1;
+  while ((long long)H * gmax < 64) gmax *= 2;
+  const long long a = NC / kMinSegChunks, b = (long long)N * gmax;
+  return (size_t)H * (size_t)(a < b ? a : b);
+}
 
 size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int dtype, bool varlen) {
   if (B == 0 || H == 0 || (T == 0 && !varlen)) return 0;
@@ -1722,12 +1743,11 @@ size_t prefill_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, i
     return align256(base) + chains * dk * dv * 4 + chains * 4;
   }
   // packed: H x NC chunks, the sink, then the chunk table (span, seq, first); a segmented
-  // scan then adds entry states and plan entries for at most H * (NC / 64) (head, segment)
-  // jobs (a sequence of n chunks has at most n / 64 segments)
+  // scan then adds entry states and plan entries for its (sequence, head, segment) jobs
   const size_t base = (size_t)H * NC * per_chunk + kSinkBytes + align16((size_t)NC * 8) + (size_t)B * 16 +
                       align16((size_t)(B + 1) * 4);
-  if (!varlen_may_segment(H, NC, dv, dtype)) return base;
-  const size_t jobs = varlen_jobs(H, NC);
+  if (!varlen_may_segment(B, H, NC, dv, dtype)) return base;
+  const size_t jobs = varlen_jobs(B, H, NC);
   return align256(base) + jobs * dk * dv * 4 + jobs * 4;
 }
 
@@ -1757,7 +1777,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   // segments per (b, h) of a segmented scan (1: one chain each); packed sequences are
   // segmented one by one on the device (vseg), never when checkpoints are saved
   const int G = (!kWideOk || varlen || ckpt || a.serial_scan) ? 1 : seg_count(nbh, NC, a.dv, DT);
-  const bool vseg = kWideOk && varlen && !ckpt && !a.serial_scan && varlen_may_segment(a.H, NC, a.dv, DT);
+  const bool vseg = kWideOk && varlen && !ckpt && !a.serial_scan && varlen_may_segment(a.B, a.H, NC, a.dv, DT);
   if (varlen) {
     hipLaunchKernelGGL(varlen_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.cu_seqlens, a.B, a.T,
                        a.chunk, NC, ckpt ? a.state_interval : 0, span, seq, first, vseg ? a.H : 0);
@@ -1781,12 +1801,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
                 varlen ? a.slot : nullptr, a.num_slots, a.B, a.T, a.H, a.dk, a.dv, a.chunk, NC, NT, nbh,
                 nullptr, nullptr, 1, NC, 0};
   if constexpr (kWideOk) {
-    // segmented scan: plan, then the tails (pass 1) and the segments (pass 2) as chains of
-    // 32-column tiles, then (below, pass 0) the heads without a plan as single chains
+    // segmented scan: plan (and the copies of the initial states), then the segments
+    // (pass 2) as chains of 32-column tiles, then (below, pass 0) the heads without a plan
+    // as single chains
     if (G > 1 || vseg) {
       // chains of passes 1 and 2: every (b, h, segment), or packed an upper bound on the
       // (sequence, head, segment) jobs, past which workgroups exit
-      const size_t chains = vseg ? varlen_jobs(a.H, NC) : (size_t)nbh * G;
+      const size_t chains = vseg ? varlen_jobs(a.B, a.H, NC) : (size_t)nbh * G;
       const size_t base = vseg ? chunks_bytes + kSinkBytes + align16((size_t)NC * 8) + (size_t)a.B * 16 +
                                      align16((size_t)(a.B + 1) * 4)
                                : chunks_bytes + kSinkBytes;
@@ -1797,20 +1818,19 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       sp.seg_nc = vseg ? 0 : (NC + G - 1) / G;
       hipLaunchKernelGGL((seg_plan_kernel<K, V, C, DT == 1>), dim3(nbh), dim3(kPlanThreads), 0, st,
                          (const uint16_t*)a.workspace, NC, sp.G, sp.seg_nc, const_cast<int32_t*>(sp.plan), a.H,
-                         vseg ? seq : nullptr, vseg ? first : nullptr);
+                         vseg ? seq : nullptr, vseg ? first : nullptr, a.init_state, varlen ? a.slot : nullptr,
+                         a.num_slots, a.dk * a.dv, sp.seg_states);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
+      // the segments, each after its boundary's tail, as chains of 32-column tiles
       ScanParams sw = sp;
-      sw.nbh = (int)chains;
       sw.NT = a.dv / (2 * kVT);
-      const int wgroups = ((int)chains + 7) / 8;
-      for (int pass = 1; pass <= 2; ++pass) {
-        sw.pass = pass;
-        hipLaunchKernelGGL((scan_kernel<DT, K, V, C, 2 * kVT>), dim3(wgroups * 8 * sw.NT), dim3(kScanThreads), 0,
-                           st, sw);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
+      sw.pass = 2;
+      sw.nbh = (int)chains;
+      hipLaunchKernelGGL((scan_kernel<DT, K, V, C, 2 * kVT>), dim3(((int)chains + 7) / 8 * 8 * sw.NT),
+                         dim3(kScanThreads), 0, st, sw);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
       sp.pass = 0;
     }
   }

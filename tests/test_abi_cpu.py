@@ -460,9 +460,10 @@ def test_segmented_workspace_size(lib):
 
 
 def test_segmented_varlen_workspace_size(lib):
-    """The packed prefill reserves, for sequences it may segment (bf16, dv = 128, fewer than 64
-    heads, at least 128 chunks in the bound), one fp32 dk x dv entry state and one int for
-    each of at most H * (chunks / 64) (sequence, head, segment) jobs after its chunk table."""
+    """The packed prefill reserves, when it may segment (bf16, dv = 128, fewer than 64
+    (sequence, head) pairs, at least 128 chunks in the bound), one fp32 dk x dv entry state
+    and one int for each of its at most H * min(chunks / 64, N * Gmax) (sequence, head,
+    segment) jobs after its chunk table (Gmax: the most segments H heads allow)."""
     def size(N, T, H, dk=128, dv=128, dtype=0):
         return lib.kda_chunk_prefill_varlen_workspace_size(N, T, H, dk, dv, 64, dtype)
     def a16(x):
@@ -471,9 +472,16 @@ def test_segmented_varlen_workspace_size(lib):
     def base(N, T, H):
         nc = (T + 63) // 64 + N
         return H * nc * per_chunk + 16384 + a16(nc * 8) + N * 16 + a16((N + 1) * 4)
-    for N, T, H in ((3, 8000, 2), (6, 17766, 2), (32, 131072, 32)):
+    def gmax(H):
+        g = 1
+        while H * g < 64:
+            g *= 2
+        return g
+    for N, T, H in ((3, 8000, 2), (6, 17766, 2), (1, 1 << 20, 32), (1, 131072, 32)):
         nc = (T + 63) // 64 + N
-        want = (base(N, T, H) + 255) // 256 * 256 + H * (nc // 64) * (128 * 128 * 4 + 4)
+        jobs = H * min(nc // 64, N * gmax(H))
+        want = (base(N, T, H) + 255) // 256 * 256 + jobs * (128 * 128 * 4 + 4)
         assert nc >= 128 and size(N, T, H) == want, (N, T, H)
+    assert size(32, 131072, 32) == base(32, 131072, 32)    # 1024 (sequence, head) pairs: never
     assert size(2, 8000, 64) == base(2, 8000, 64)          # 64 heads: never segmented
     assert size(2, 64 * 100, 2) == base(2, 64 * 100, 2)    # 102 chunks: too short

@@ -335,10 +335,12 @@ def _dev_packed(inp, dev):
 
 @pytest.mark.parametrize("H", [2, 40])
 def test_varlen_segments_like_lone_runs(oracle, H):
-    """Packed sequences are segmented one by one, each as its lone kda_chunk_prefill run is
-    (per-sequence rule on the chunk count and the head count): long ones (9000 and 8256
-    tokens) among short and empty ones, with initial states, equal their lone runs bit for
-    bit, whatever the number of packed sequences; the long ones against the oracle too."""
+    """With fewer than 64 (sequence, head) pairs (H = 2) packed sequences are segmented one
+    by one, each as its lone kda_chunk_prefill run is (the same rule on its chunk count and
+    the head count): long ones (9000 and 8256 tokens) among short and empty ones, with
+    initial states, equal their lone runs bit for bit.  With more pairs (H = 40: 240) the
+    chip is full of single chains and every sequence equals its lone run with
+    KDA_FLAG_SERIAL_SCAN.  The long ones against the oracle too."""
     import torch
     from linear_attention_recurrence_kda_amd import kda
     dev = device()
@@ -354,7 +356,8 @@ def test_varlen_segments_like_lone_runs(oracle, H):
     for i in range(N):
         a, b = int(cu[i]), int(cu[i + 1])
         oi, si = kda.chunk_prefill(*(d[n][a:b].unsqueeze(0).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")),
-                                   initial_state=s0[i:i + 1].contiguous(), chunk_size=64)
+                                   initial_state=s0[i:i + 1].contiguous(), chunk_size=64,
+                                   serial_scan=N * H >= 64)
         torch.cuda.synchronize()
         assert torch.equal(o[a:b], oi[0]), f"o of sequence {i} (length {b - a}) differs from its lone run"
         assert torch.equal(sN[i], si[0]), f"state of sequence {i} differs from its lone run"
