@@ -213,12 +213,13 @@ size_t kda_chunk_prefill_varlen_workspace_size(int N, int T, int H, int dk, int 
  * the recurrence above from init_state[i] over those tokens only: no state or
  * output crosses a boundary (dev.to prefix-invariance page: the output at a
  * position depends on its own prefix and nothing else).  Each sequence's
- * chunks start at its first token, and a long sequence is cut into segments exactly as
- * kda_chunk_prefill would cut it run alone (the same rule on its chunk count and H, the
- * same plan from its own inputs; see the segmented scan of kda_chunk_prefill), so its
- * results equal those of kda_chunk_prefill on that sequence alone with the same chunk and
- * flags, bit for bit.  With checkpoints (state_interval > 0) or KDA_FLAG_SERIAL_SCAN every
- * sequence is scanned as one chain, equal to its lone run with KDA_FLAG_SERIAL_SCAN.
+ * chunks start at its first token.  With fewer than 64 (sequence, head) pairs a long
+ * sequence is cut into segments exactly as kda_chunk_prefill would cut it run alone (the
+ * same rule on its chunk count and H, the same plan from its own inputs; see the segmented
+ * scan of kda_chunk_prefill), so its results equal those of kda_chunk_prefill on that
+ * sequence alone with the same chunk and flags, bit for bit.  With 64 pairs or more, with
+ * checkpoints (state_interval > 0) or with KDA_FLAG_SERIAL_SCAN every sequence is scanned as
+ * one chain, equal to its lone run with KDA_FLAG_SERIAL_SCAN.
  *
  *   q, k        [T,H,dk]     dtype (T = total tokens)
  *   v           [T,H,dv]     dtype
