@@ -131,8 +131,13 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * of the norm of the state entering the tail, below 2^-25 in absolute value for any finite
  * fp32 state.  A head for which some boundary has no such tail inside the segment before
  * it is scanned as one chain, so every input gets a result within rounding of the token
- * recurrence; the segmented one differs from the single chain's by rounding only.  The
- * call stays asynchronous (the choice is made on the device).  KDA_FLAG_SERIAL_SCAN turns
+ * recurrence; the segmented one differs from the single chain's by rounding only.  A
+ * non-finite value at a valid position (outside this contract) turns the single chain's
+ * state into NaN from that token on, while a later segment whose tail does not reach it
+ * starts from zero and stays finite: callers that detect bad inputs through the final
+ * state set KDA_FLAG_SERIAL_SCAN.  Masked positions count as the identity in the bound and
+ * their values are never read.  The call stays asynchronous (the choice is made on the
+ * device).  KDA_FLAG_SERIAL_SCAN turns
  * it off, e.g. to get results equal bit for bit to the state-saving calls.
  * workspace/workspace_bytes: at least kda_chunk_prefill_workspace_size(...)
  * bytes of device memory (may be NULL when that size is 0).

@@ -117,10 +117,61 @@ def test_segmented_mixed_heads(oracle):
     _check_all("mixed", o, s, ro, rs)
 
 
+def _poison(a, m):
+    """Copy of a with NaN / +Inf / -Inf cycling over the masked positions (mask m [B,T])."""
+    out = a.copy()
+    bad = np.array([np.nan, np.inf, -np.inf], np.float32)
+    for i, (b, t) in enumerate(np.argwhere(m == 0)):
+        out[b, t] = bad[i % 3]
+    return out
+
+
+def test_segmented_masked_garbage_and_padding(oracle):
+    """Masked positions never enter the contraction bound or the scan: with NaN, +Inf and
+    -Inf at every masked position of q, k, v, log_alpha and beta (left padding, a hole across
+    the segment boundary and its tail, right padding) the segmented call equals, bit for bit,
+    the call with zeros there, which is checked against the oracle.  A masked run counts as
+    the identity in the bound, so padding longer than the first segment leaves the boundary
+    without a forgetting tail (the state entering it is the initial state, not forgotten):
+    that head must fall back to one chain, bit for bit the serial call."""
+    import torch
+    dev = device()
+    B, T, H = 1, 8192 + 77, 2
+    NC = (T + 63) // 64
+    seg_nc = -(-NC // _segments(B * H, NC))
+    say("[case] segmented masked garbage")
+    inp = D.np_kda_inputs(B, T, H, DK, DV, "bf16", seed=56)
+    s0 = D.np_state(B, H, DK, DV, 0.1, seed=56)
+    mask = np.ones((B, T), np.uint8)
+    mask[0, :200] = 0
+    mask[0, 64 * seg_nc - 700:64 * seg_nc + 300] = 0       # over the boundary and its tail
+    mask[0, T - 150:] = 0
+    zero = {n: a.copy() for n, a in inp.items()}
+    for a in zero.values():
+        a[mask == 0] = 0.0
+    bad = {n: _poison(a, mask) for n, a in inp.items()}
+    oz, sz, pz = _run(zero, dev, mask=mask, s0=s0)
+    ob, sb, pb = _run(bad, dev, mask=mask, s0=s0)
+    assert np.all(pz[:, 0] == 1) and np.array_equal(pz, pb), (pz.tolist(), pb.tolist())
+    assert torch.equal(oz, ob) and torch.equal(sz, sb), "masked NaN/Inf changed the segmented result"
+    ro, rs = oracle.c_prefill(**zero, mask=mask, init_state=s0)
+    _check_all("masked garbage", oz, sz, ro, rs)
+
+    say("[case] segmented padding past the first segment falls back")
+    mask2 = np.ones((B, T), np.uint8)
+    mask2[0, :64 * seg_nc + 10] = 0
+    bad2 = {n: _poison(a, mask2) for n, a in inp.items()}
+    o2, s2, p2 = _run(bad2, dev, mask=mask2, s0=s0)
+    assert np.all(p2[:, 0] == 0), p2.tolist()
+    os2, ss2, _ = _run(bad2, dev, mask=mask2, s0=s0, serial=True)
+    assert torch.equal(o2, os2) and torch.equal(s2, ss2)
+    assert torch.all(o2[0, :64 * seg_nc + 10] == 0)
+
+
 def test_segmented_flags_and_inplace(oracle):
     """The q/k L2-norm flag on raw rows and the per-head gate, each with the final state
-    written over the initial state (pass 1 copies it before pass 2 overwrites it), and a
-    ragged tail; against the oracle."""
+    written over the initial state (the plan kernel copies it before pass 2 overwrites it),
+    and a ragged tail; against the oracle."""
     dev = device()
     B, T, H = 1, 8192 + 63, 2
     s0 = D.np_state(B, H, DK, DV, 0.1, seed=54)
