@@ -115,7 +115,9 @@ size_t kda_chunk_prefill_workspace_size(int B, int T, int H, int dk, int dv, int
  * Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64} (128 and 256,
  * the pages' 256-token chunks included, return KDA_ERR_UNSUPPORTED: their decay
  * factors leave the fp32 range with this kernel's chunk-start factorisation and
- * their inverse does not fit the LDS); B, H <= 65535; H times the number of
+ * their inverse does not fit the LDS; chunk 16 runs its 16-token chunks in the
+ * 32-row tiles of chunk 32, the upper rows masked, so it costs a chunk-32 step per
+ * 16 tokens and exists for chunk-size audits rather than speed); B, H <= 65535; H times the number of
  * chunks < 2^24 and B*H <= 2^20 - 8, so every launch's extent in threads fits 32
  * bits (KDA_ERR_UNSUPPORTED otherwise, and a workspace size of 0);
  * T >= 0 (T = 0 copies init_state to final_state).  16-byte aligned: q, k, v,
