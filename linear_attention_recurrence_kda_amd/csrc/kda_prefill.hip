@@ -963,7 +963,7 @@ scan_kernel(ScanParams p) {
   const int vbh = (slot / p.NT) * 8 + xcd, tile = slot % p.NT;
   if (vbh >= p.nbh) return;
   const int pass = p.pass;
-  // passes 1 and 2 of a segmented scan run one chain per (b, h, segment): in the batch
+  // pass 2 of a segmented scan runs one chain per (b, h, segment): in the batch
   // layout G per (b, h); packed, sequence b has seq[b].w segments (0: too short for any)
   // and its (head, segment) jobs start at H * seq[b].z
   const bool seg_pass = p.plan != nullptr && pass != 0;
@@ -1805,7 +1805,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     // (pass 2) as chains of 32-column tiles, then (below, pass 0) the heads without a plan
     // as single chains
     if (G > 1 || vseg) {
-      // chains of passes 1 and 2: every (b, h, segment), or packed an upper bound on the
+      // chains of pass 2: every (b, h, segment), or packed an upper bound on the
       // (sequence, head, segment) jobs, past which workgroups exit
       const size_t chains = vseg ? varlen_jobs(a.B, a.H, NC) : (size_t)nbh * G;
       const size_t base = vseg ? chunks_bytes + kSinkBytes + align16((size_t)NC * 8) + (size_t)a.B * 16 +
