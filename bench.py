@@ -43,7 +43,7 @@ BACKWARD_STATES_BYTES_PER_TH = BACKWARD_BYTES_PER_TH + 128 * 128 * 4 // 64
 # scaled by a known-size streaming kernel in the same run (factors 2.0 and 1.0 on this GPU).  A
 # figure is reported only while the kernel sources still hash to what was profiled.
 MEASURED_TRAFFIC = {
-    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "e3f636fa3abeffb2", "bytes": 16.394e9},
+    "prefill": {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "a4ab46f5ccfff747", "bytes": 16.389e9},
     "decode": {"sources": ("kda_decode.hip", "kda_device.h"), "sha": "7bca8c2b29273684", "bytes": 1.087e9},
     # the backward call with the chunk-end states given: bwd_prep, bwd_scan, bwd_cc, bwd_ck
     "backward": {"sources": ("kda_backward.hip", "kda_device.h"), "sha": "28d1e459b9f0f3e9", "bytes": 8.877e9},
@@ -53,8 +53,8 @@ MEASURED_TRAFFIC = {
 # MFMA counters of the 128k prefill call (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
 # SQ_INSTS_VALU_MFMA_MOPS_BF16 ...; busy % = busy cycles / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)),
 # reported only while the kernel sources hash to what was profiled.
-MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "e3f636fa3abeffb2",
-                 "prep_busy_pct": 8.0, "scan_busy_pct": 24.1, "call_busy_pct": 16.0, "issued_flop_per_call": 1.441e12}
+MEASURED_MFMA = {"sources": ("kda_prefill.hip", "kda_device.h"), "sha": "a4ab46f5ccfff747",
+                 "prep_busy_pct": 8.1, "scan_busy_pct": 24.1, "call_busy_pct": 16.1, "issued_flop_per_call": 1.441e12}
 
 
 def measured_mfma(default_workload):

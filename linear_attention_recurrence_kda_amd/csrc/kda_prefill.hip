@@ -1030,8 +1030,9 @@ scan_kernel(ScanParams p) {
   if (p.plan != nullptr && p.seq != nullptr && !seg_pass) Gb = p.seq[b].w;
   if (p.plan != nullptr && Gb > 0) {
     // segmented scan: this chain's chunks [c0, c1), where its state comes from and goes to;
-    // the (b, h)'s plan and segment-0 entry state (the initial state, copied by the plan
-    // kernel so that the last segment may write the final state over it) are at pbase
+    // the (b, h)'s plan and segment-0 entry state (the initial state when there is one,
+    // copied by the plan kernel so that the last segment may write the final state over
+    // it) are at pbase
     const size_t pbase = p.seq == nullptr ? (size_t)bh * Gb : ((size_t)p.seq[b].z * p.H + (size_t)h * Gb);
     const int32_t* pl = p.plan + pbase;
     const bool seg_ok = pl[0] != 0;
@@ -1042,7 +1043,7 @@ scan_kernel(ScanParams p) {
       const int seg_nc = (NCs + Gb - 1) / Gb;
       const int s0 = seg * seg_nc, c1 = min(s0 + seg_nc, NCs);
       const int c0 = seg == 0 ? 0 : min(max(pl[seg], 0), s0);
-      init_ptr = seg == 0 ? p.seg_states + pbase * mat : nullptr;
+      init_ptr = (seg == 0 && init_ptr != nullptr) ? p.seg_states + pbase * mat : nullptr;
       if (seg + 1 < Gb) fin_ptr = nullptr;
       out0 = s0 - c0;
       seq_tok0 += (size_t)c0 * p.chunk;
@@ -1579,17 +1580,19 @@ seg_plan_kernel(const uint16_t* __restrict__ ws, int NC, int G, int seg_nc, int3
   const bool ok = __syncthreads_and(g >= G || start >= 0);
   if (g < G) plan[pbase + g] = start;
   if (threadIdx.x == 0) plan[pbase] = ok ? 1 : 0;
-  // a segmented (b, h): its initial state (the row, or its slot of a pool; zeros without
-  // one) copied to the segment-0 entry, so that the last segment may overwrite it in place
+  // a segmented (b, h) with an initial state (its row, or its slot of a pool): that state
+  // copied to the segment-0 entry, so that the last segment may overwrite it in place
+  // (without one, segment 0 starts from zero and the entry is not used)
   if (!ok) return;
   int row = blockIdx.x;
   if (slot != nullptr) {
     const int sl = slot[b];
     row = (sl >= 0 && sl < S) ? sl * H + h : -1;
   }
-  const float* src = (init != nullptr && row >= 0) ? init + (size_t)row * mat : nullptr;   // 4-byte aligned
+  if (init == nullptr || row < 0) return;
+  const float* src = init + (size_t)row * mat;
   float* dst = seg_states + pbase * mat;
-  for (int i = threadIdx.x; i < mat; i += kPlanThreads) dst[i] = src != nullptr ? src[i] : 0.f;
+  for (int i = threadIdx.x; i < mat; i += kPlanThreads) dst[i] = src[i];
 }
 
 // ================================================================ packed sequences
