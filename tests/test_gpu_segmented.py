@@ -463,6 +463,25 @@ def test_varlen_segmented_slots_checkpoints_serial():
     for i in range(N):
         a, b = int(cu[i]), int(cu[i + 1])
         assert torch.equal(o[a:b], lone[i][0][0]) and torch.equal(pool[3 - i], lone[i][1][0]), f"slots: sequence {i}"
+    # a slot outside the pool: the segmented sequence 0 starts from zero (no entry state is
+    # copied for it) and keeps no state; it equals its lone run without an initial state
+    a0, b0 = int(cu[0]), int(cu[1])
+    args0 = [d[n][a0:b0].unsqueeze(0).contiguous() for n in ("q", "k", "v", "log_alpha", "beta")]
+    o_zero, s_zero = kda.chunk_prefill(*args0, chunk_size=64)
+    pool2 = pool.clone()
+    before = pool2.clone()
+    slot2 = torch.tensor([-1, 1, 0], dtype=torch.int32, device=dev)
+    o2, _ = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], cu_d, initial_state=pool2,
+                                     final_state=pool2, slot=slot2, chunk_size=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o2[a0:b0], o_zero[0]), "slot outside the pool: sequence 0 from zero"
+    assert torch.equal(pool2[2], before[2]) and torch.equal(pool2[3], before[3]), "no state kept for slot -1"
+    for i in (1, 2):
+        a, b = int(cu[i]), int(cu[i + 1])
+        assert torch.equal(o2[a:b], kda.chunk_prefill(*[d[n][a:b].unsqueeze(0).contiguous() for n in
+                                                        ("q", "k", "v", "log_alpha", "beta")],
+                                                      initial_state=before[2 - i:3 - i].contiguous(),
+                                                      chunk_size=64)[0][0]), f"slot {2 - i}: sequence {i}"
     # checkpoints and the serial flag: single chains
     for kw in (dict(state_interval=64), dict(serial_scan=True)):
         res = kda.chunk_prefill_varlen(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], cu_d, initial_state=s0,
